@@ -1,0 +1,177 @@
+/*
+ * ssm_tree.h - C ABI of libssm_tree.so: verifying a speculative draft-token
+ * tree through Mamba2 selective-SSM layers on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (from the pages that describe the method):
+ *   SpecMamba page, "FPGA加速Mamba推理：SpecMamba方案与优化实践"
+ *   (jsqmd.com/news/939380):
+ *     sec. 2.1  rejecting draft tokens needs the hidden state of the last
+ *               accepted token, and keeping every intermediate state is too
+ *               costly;
+ *     sec. 3.1  draft side stores only the per-token Delta, A, B, X; the
+ *               target recomputes only the affected path;
+ *     sec. 3.2  the candidate tree is flattened breadth-first and verified
+ *               with a FIFO of live states, each child state formed from its
+ *               parent's, a state released once its children are done;
+ *     sec. 5.2  trees of branching 2-3, depth 4-5, 12-16 predicted tokens.
+ *   LightMamba part of "FPGA accelerator part 2"
+ *   (pinghaoyang.com.cn/aigc/posts/fpga-accelerator-part-2/), "why Mamba is
+ *   hard to accelerate": in_proj yields X, B, C, Delta, Z; X passes conv1d,
+ *   the SSM keeps h_t and emits Y; the recurrence fragments read
+ *   h_t = Abar (.) h_{t-1} + Bbar (.) X_t.
+ *
+ * Per (layer l, sequence b, node v, head h, headdim row p, state index n),
+ * with g = h / (H / G) and c = h * P + p:
+ *   dt_v[h]  = softplus(dt_raw_v[h] + dt_bias[h])   (softplus(z) = z, z > 20)
+ *   dA_v[h]  = exp(dt_v[h] * A[h])
+ *   x~_v[c]  = act(conv_b[c] + sum_{j<W} conv_w[c][W-1-j] * u_j[c])
+ *              u_0 = x_v, u_j = x of the j-th ancestor of v, continuing into
+ *              the conv window newest row first once past the tree root;
+ *              act = identity, or SiLU with SSM_TREE_CONV_SILU
+ *   h_v      = dA_v[h] * h_parent(v) + (dt_v[h] * x~_v[c]) * B_v[g][n]
+ *              (h_parent = root state for parent -1)
+ *   y_v[c]   = sum_n C_v[g][n] * h_v[h][p][n] + D[h] * x~_v[c]
+ *
+ * Memory: every tensor argument is a DEVICE pointer to contiguous row-major
+ * data, 16-byte aligned, allocated and owned by the caller.  The library
+ * allocates nothing, keeps no mutable global state and is reentrant; it
+ * enqueues work on `hip_stream` (a hipStream_t, NULL = default stream) and
+ * returns without synchronising.  Structs are read on the host during the
+ * call only.
+ *
+ * Errors: the return value is SSM_TREE_OK or a negative code for problems
+ * detectable on the host (nothing is enqueued then).  Problems that depend
+ * on device data (an invalid parent[] or path) are reported per sequence in
+ * seq_status[b] once the stream reaches the work; other sequences are
+ * processed normally.
+ */
+#ifndef SSM_TREE_H
+#define SSM_TREE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSM_TREE_ABI_VERSION 1
+
+/* input element types for x, B, C, dt_raw and the conv window */
+#define SSM_TREE_F32 0
+#define SSM_TREE_BF16 1
+
+/* dims.flags */
+#define SSM_TREE_CONV_SILU 1 /* SiLU after the conv (Mamba2 checkpoints use it; the pages name no activation) */
+
+/* return / status codes */
+#define SSM_TREE_OK 0
+#define SSM_TREE_E_NULL (-1)   /* a required pointer is NULL */
+#define SSM_TREE_E_ALIGN (-2)  /* a tensor pointer is not 16-byte aligned */
+#define SSM_TREE_E_DIMS (-3)   /* unsupported or inconsistent dimensions */
+#define SSM_TREE_E_DTYPE (-4)  /* unknown in_dtype */
+#define SSM_TREE_E_ALIAS (-5)  /* an output overlaps an input (other than an allowed exact in-place) */
+#define SSM_TREE_E_HIP (-6)    /* a HIP launch failed */
+#define SSM_TREE_E_FLAGS (-7)  /* unknown bits in dims.flags */
+#define SSM_TREE_E_TREE (-10)  /* seq_status: parent[] is not a BFS labelling */
+#define SSM_TREE_E_PATH (-11)  /* seq_status: path is not a root-to-node path of the tree */
+
+/* Dimensions.  Supported: 0 <= n_nodes <= 64; d_state in {16,32,64,128,256};
+ * 1 <= conv_width <= 4; nheads % ngroups == 0; nheads*headdim a multiple of
+ * 64 and (nheads*headdim/ngroups) a multiple of 64. */
+typedef struct ssm_tree_dims {
+  int32_t n_layers;   /* L   : independent layer instances in this call */
+  int32_t batch;      /* Bsz : sequences, each with its own tree */
+  int32_t n_nodes;    /* T   : nodes per tree */
+  int32_t nheads;     /* H */
+  int32_t headdim;    /* P */
+  int32_t d_state;    /* N */
+  int32_t ngroups;    /* G : B and C are shared by H/G consecutive heads */
+  int32_t conv_width; /* W */
+  int32_t in_dtype;   /* SSM_TREE_F32 or SSM_TREE_BF16 */
+  int32_t flags;      /* 0 or SSM_TREE_CONV_SILU */
+} ssm_tree_dims;
+
+/* Per-layer parameters, float32 device pointers. */
+typedef struct ssm_tree_params {
+  const float* A;       /* [L][H]        decay rate per head (negative in Mamba2) */
+  const float* D;       /* [L][H]        skip weight per head */
+  const float* dt_bias; /* [L][H] */
+  const float* conv_w;  /* [L][H*P][W]   depthwise conv weights, tap W-1 = current token */
+  const float* conv_b;  /* [L][H*P]      or NULL for no conv bias */
+} ssm_tree_params;
+
+/*
+ * ssm_tree_verify: every node's output y for every layer and sequence.
+ *
+ * parent      [Bsz][T] int32.  BFS labelling: parent[0] = -1,
+ *             -1 <= parent[i] < i, parent[] non-decreasing (children of a
+ *             node are a contiguous index range).  -1 = child of the root
+ *             state.  Shared by all layers.
+ * x           [L][Bsz][T][H*P]   in_dtype   per-node conv input
+ * B, C        [L][Bsz][T][G][N]  in_dtype
+ * dt_raw      [L][Bsz][T][H]     in_dtype   step size before bias/softplus
+ * conv_window [L][Bsz][W-1][H*P] in_dtype   raw x of the last W-1 committed
+ *             tokens, oldest row first (may be NULL when W == 1)
+ * state       [L][Bsz][H][P][N]  float32    root SSM state (read only)
+ * y           [L][Bsz][T][H][P]  float32    out; must not overlap any input
+ * seq_status  [Bsz] int32 out, or NULL.  SSM_TREE_OK or SSM_TREE_E_TREE;
+ *             a sequence with an invalid tree gets NaN in all its y.
+ *
+ * Child states are never written to memory: the root state is read once.
+ */
+int ssm_tree_verify(const ssm_tree_dims* dims, const ssm_tree_params* params, const int32_t* parent,
+                    const void* x, const void* B, const void* C, const void* dt_raw, const void* conv_window,
+                    const float* state, float* y, int32_t* seq_status, void* hip_stream);
+
+/*
+ * ssm_tree_commit: advance the root state and conv window along the
+ * accepted path (SpecMamba page sec. 3.1: recompute the accepted path from
+ * the stored per-token dt, B and x instead of storing per-node states).
+ *
+ * path        [Bsz][T] int32: path[b][0..len) = root-level node, its child,
+ *             ... (entries past len are ignored)
+ * path_len    [Bsz] int32, 0 <= len <= T (0 = keep state and window)
+ * x, B, dt_raw, conv_window_in, state_in: as for ssm_tree_verify
+ * conv_window_out [L][Bsz][W-1][H*P] in_dtype: last W-1 rows of
+ *             (old window, x of each path node), copied bit for bit
+ * state_out   [L][Bsz][H][P][N] float32: state of the last path node
+ * Outputs may equal the matching input exactly (in place); any other
+ * overlap is SSM_TREE_E_ALIAS.
+ * seq_status  [Bsz] or NULL: SSM_TREE_OK, SSM_TREE_E_TREE or SSM_TREE_E_PATH;
+ *             a failed sequence's outputs are left unwritten.
+ */
+int ssm_tree_commit(const ssm_tree_dims* dims, const ssm_tree_params* params, const int32_t* parent,
+                    const int32_t* path, const int32_t* path_len, const void* x, const void* B, const void* dt_raw,
+                    const void* conv_window_in, const float* state_in, void* conv_window_out, float* state_out,
+                    int32_t* seq_status, void* hip_stream);
+
+/*
+ * ssm_tree_plan: the tree plan the kernels derive from parent[] (SpecMamba
+ * page sec. 3.2: breadth-first flattening, FIFO of live states), exported
+ * so that its integer bookkeeping can be compared exactly.
+ *
+ * plan_out [Bsz][SSM_TREE_PLAN_HEADER + T * SSM_TREE_PLAN_STRIDE] int32:
+ *   header: status, peak FIFO occupancy (internal nodes pushed and not yet
+ *           popped), maximum depth, number of internal nodes;
+ *   per node: depth (root-level = 1), parent, first child (-1 if none),
+ *           child count, FIFO rank (order among internal nodes, -1 for a
+ *           leaf), conv inputs for taps 1..3 (node index, or -(1 + r) for
+ *           window row r, SSM_TREE_PLAN_UNUSED beyond W-1).
+ * An invalid tree yields the status and zeros elsewhere.  Only dims.batch,
+ * n_nodes and conv_width are read.
+ */
+#define SSM_TREE_PLAN_HEADER 4
+#define SSM_TREE_PLAN_STRIDE 8
+#define SSM_TREE_PLAN_UNUSED (-32768)
+int ssm_tree_plan(const ssm_tree_dims* dims, const int32_t* parent, int32_t* plan_out, void* hip_stream);
+
+/* Static text for a status code (never NULL). */
+const char* ssm_tree_status_string(int status);
+
+/* SSM_TREE_ABI_VERSION of the loaded library. */
+int ssm_tree_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SSM_TREE_H */

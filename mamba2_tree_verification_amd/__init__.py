@@ -1,0 +1,175 @@
+"""Python binding of libssm_tree.so (argument marshalling only).
+
+The functions ``ssm_tree_verify``, ``ssm_tree_commit``, ``ssm_tree_plan``,
+``ssm_tree_status_string`` and ``ssm_tree_abi_version`` mirror the C ABI in
+``include/ssm_tree.h`` one to one and take raw device addresses.  The
+``verify`` / ``commit`` / ``plan`` helpers accept torch tensors on the GPU,
+check their dtypes and contiguity, pass ``data_ptr()`` and the current HIP
+stream, and raise ``SsmTreeError`` on a nonzero return.  Every step of the
+computation runs in the HIP kernels; there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libssm_tree.so")
+
+SSM_TREE_ABI_VERSION = 1
+SSM_TREE_F32, SSM_TREE_BF16 = 0, 1
+SSM_TREE_CONV_SILU = 1
+OK, E_NULL, E_ALIGN, E_DIMS, E_DTYPE, E_ALIAS, E_HIP, E_FLAGS = 0, -1, -2, -3, -4, -5, -6, -7
+E_TREE, E_PATH = -10, -11
+PLAN_HEADER, PLAN_STRIDE, PLAN_UNUSED = 4, 8, -32768
+
+
+class SsmTreeError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        super().__init__("%s failed: %s (%d)" % (where, ssm_tree_status_string(code), code))
+        self.code = code
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [(k, ctypes.c_int32) for k in ("n_layers", "batch", "n_nodes", "nheads", "headdim", "d_state",
+                                               "ngroups", "conv_width", "in_dtype", "flags")]
+
+
+class Params(ctypes.Structure):
+    _fields_ = [(k, ctypes.c_void_p) for k in ("A", "D", "dt_bias", "conv_w", "conv_b")]
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def lib_path() -> str:
+    return LIB_PATH
+
+
+def load():
+    """Load the built library; raise if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libssm_tree.so is not built: run __graft_entry__.build() (hipcc, gfx950)")
+        L = ctypes.CDLL(LIB_PATH)
+        p, i = ctypes.c_void_p, ctypes.c_int
+        L.ssm_tree_verify.argtypes = [p] * 12
+        L.ssm_tree_verify.restype = i
+        L.ssm_tree_commit.argtypes = [p] * 14
+        L.ssm_tree_commit.restype = i
+        L.ssm_tree_plan.argtypes = [p] * 4
+        L.ssm_tree_plan.restype = i
+        L.ssm_tree_status_string.argtypes = [i]
+        L.ssm_tree_status_string.restype = ctypes.c_char_p
+        L.ssm_tree_abi_version.argtypes = []
+        L.ssm_tree_abi_version.restype = i
+        if L.ssm_tree_abi_version() != SSM_TREE_ABI_VERSION:
+            raise RuntimeError("libssm_tree.so ABI version mismatch")
+        _lib = L
+        return L
+
+
+# ---------------------------------------------------------------------------
+# one-to-one wrappers of the C entry points (raw addresses, ints or None)
+# ---------------------------------------------------------------------------
+
+def ssm_tree_verify(dims: Dims, params: Params, parent, x, B, C, dt_raw, conv_window, state, y, seq_status,
+                    hip_stream) -> int:
+    return load().ssm_tree_verify(ctypes.byref(dims), ctypes.byref(params), parent, x, B, C, dt_raw, conv_window,
+                                  state, y, seq_status, hip_stream)
+
+
+def ssm_tree_commit(dims: Dims, params: Params, parent, path, path_len, x, B, dt_raw, conv_window_in, state_in,
+                    conv_window_out, state_out, seq_status, hip_stream) -> int:
+    return load().ssm_tree_commit(ctypes.byref(dims), ctypes.byref(params), parent, path, path_len, x, B, dt_raw,
+                                  conv_window_in, state_in, conv_window_out, state_out, seq_status, hip_stream)
+
+
+def ssm_tree_plan(dims: Dims, parent, plan_out, hip_stream) -> int:
+    return load().ssm_tree_plan(ctypes.byref(dims), parent, plan_out, hip_stream)
+
+
+def ssm_tree_status_string(code: int) -> str:
+    try:
+        return load().ssm_tree_status_string(code).decode()
+    except RuntimeError:
+        return "status %d" % code
+
+
+def ssm_tree_abi_version() -> int:
+    return load().ssm_tree_abi_version()
+
+
+# ---------------------------------------------------------------------------
+# torch tensor helpers
+# ---------------------------------------------------------------------------
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def make_dims(L, Bsz, T, H, P, N, G, W, bf16: bool, silu: bool = False) -> Dims:
+    return Dims(L, Bsz, T, H, P, N, G, W, SSM_TREE_BF16 if bf16 else SSM_TREE_F32,
+                SSM_TREE_CONV_SILU if silu else 0)
+
+
+def make_params(A, D, dt_bias, conv_w, conv_b=None) -> Params:
+    for t in (A, D, dt_bias, conv_w, conv_b):
+        _check(t, "float32")
+    return Params(_ptr(A), _ptr(D), _ptr(dt_bias), _ptr(conv_w), _ptr(conv_b))
+
+
+def _check(t, kind):
+    if t is None:
+        return
+    import torch
+    if not t.is_cuda:
+        raise ValueError("tensor must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    want = {"float32": (torch.float32,), "int32": (torch.int32,), "in": (torch.float32, torch.bfloat16)}[kind]
+    if t.dtype not in want:
+        raise ValueError("unexpected dtype %s" % t.dtype)
+
+
+def verify(dims: Dims, params: Params, parent, x, B, C, dt_raw, conv_window, state, y, seq_status=None,
+           stream=None):
+    for t, k in ((parent, "int32"), (x, "in"), (B, "in"), (C, "in"), (dt_raw, "in"), (conv_window, "in"),
+                 (state, "float32"), (y, "float32"), (seq_status, "int32")):
+        _check(t, k)
+    rc = ssm_tree_verify(dims, params, _ptr(parent), _ptr(x), _ptr(B), _ptr(C), _ptr(dt_raw), _ptr(conv_window),
+                         _ptr(state), _ptr(y), _ptr(seq_status), _stream(stream))
+    if rc != OK:
+        raise SsmTreeError(rc, "ssm_tree_verify")
+
+
+def commit(dims: Dims, params: Params, parent, path, path_len, x, B, dt_raw, conv_window_in, state_in,
+           conv_window_out, state_out, seq_status=None, stream=None):
+    for t, k in ((parent, "int32"), (path, "int32"), (path_len, "int32"), (x, "in"), (B, "in"), (dt_raw, "in"),
+                 (conv_window_in, "in"), (state_in, "float32"), (conv_window_out, "in"), (state_out, "float32"),
+                 (seq_status, "int32")):
+        _check(t, k)
+    rc = ssm_tree_commit(dims, params, _ptr(parent), _ptr(path), _ptr(path_len), _ptr(x), _ptr(B), _ptr(dt_raw),
+                         _ptr(conv_window_in), _ptr(state_in), _ptr(conv_window_out), _ptr(state_out),
+                         _ptr(seq_status), _stream(stream))
+    if rc != OK:
+        raise SsmTreeError(rc, "ssm_tree_commit")
+
+
+def plan(dims: Dims, parent, plan_out, stream=None):
+    _check(parent, "int32")
+    _check(plan_out, "int32")
+    rc = ssm_tree_plan(dims, _ptr(parent), _ptr(plan_out), _stream(stream))
+    if rc != OK:
+        raise SsmTreeError(rc, "ssm_tree_plan")

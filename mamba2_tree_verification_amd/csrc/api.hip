@@ -1,0 +1,207 @@
+// api.hip - the extern "C" entry points of libssm_tree.so: argument
+// checks on the host, then kernel launches on the caller's stream.
+#include <stdint.h>
+#include <string.h>
+
+#include "common.h"
+
+namespace ssmt {
+int launch_verify(const VerifyArgs& a, bool bf16, hipStream_t s);  // status code
+hipError_t launch_commit(const CommitArgs& a, bool bf16, hipStream_t s);
+hipError_t launch_plan(const int32_t* parent, int Bsz, int T, int W, int32_t* out, hipStream_t s);
+hipError_t launch_status(int32_t* seq_status, int Bsz, int value, hipStream_t s);
+}  // namespace ssmt
+
+using namespace ssmt;
+
+namespace {
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range range_of(const void* p, int64_t bytes) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return Range{a, a + (uintptr_t)(bytes > 0 ? bytes : 0)};
+}
+
+bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.hi > a.lo && b.hi > b.lo; }
+
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+int check_dims(const ssm_tree_dims* dm, Dims* out) {
+  if (!dm) return SSM_TREE_E_NULL;
+  const ssm_tree_dims& d = *dm;
+  if (d.in_dtype != SSM_TREE_F32 && d.in_dtype != SSM_TREE_BF16) return SSM_TREE_E_DTYPE;
+  if (d.flags & ~SSM_TREE_CONV_SILU) return SSM_TREE_E_FLAGS;
+  if (d.n_layers < 0 || d.batch < 0 || d.n_nodes < 0 || d.n_nodes > kMaxNodes) return SSM_TREE_E_DIMS;
+  if (d.nheads < 1 || d.headdim < 1 || d.ngroups < 1 || d.nheads % d.ngroups) return SSM_TREE_E_DIMS;
+  if (d.conv_width < 1 || d.conv_width > 4) return SSM_TREE_E_DIMS;
+  if (d.d_state != 16 && d.d_state != 32 && d.d_state != 64 && d.d_state != 128 && d.d_state != 256)
+    return SSM_TREE_E_DIMS;
+  const int64_t di = (int64_t)d.nheads * d.headdim;
+  if (di % kWave || di > (1 << 20) || (di / d.ngroups) % kWave) return SSM_TREE_E_DIMS;
+  const int64_t units = (int64_t)d.n_layers * d.batch;
+  if (d.batch > 65535 || d.n_layers > 65535 || units * di * d.d_state > ((int64_t)1 << 40)) return SSM_TREE_E_DIMS;
+  *out = Dims{d.n_layers, d.batch, d.n_nodes, d.nheads, d.headdim, d.d_state, d.ngroups, d.conv_width,
+              (d.flags & SSM_TREE_CONV_SILU) ? 1 : 0, (int32_t)di};
+  return SSM_TREE_OK;
+}
+
+int check_params(const ssm_tree_params* p) {
+  if (!p || !p->A || !p->D || !p->dt_bias || !p->conv_w) return SSM_TREE_E_NULL;
+  if (misaligned(p->A) || misaligned(p->D) || misaligned(p->dt_bias) || misaligned(p->conv_w) ||
+      (p->conv_b && misaligned(p->conv_b)))
+    return SSM_TREE_E_ALIGN;
+  return SSM_TREE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ssm_tree_abi_version(void) { return SSM_TREE_ABI_VERSION; }
+
+const char* ssm_tree_status_string(int status) {
+  switch (status) {
+    case SSM_TREE_OK: return "ok";
+    case SSM_TREE_E_NULL: return "a required pointer is NULL";
+    case SSM_TREE_E_ALIGN: return "a tensor pointer is not 16-byte aligned";
+    case SSM_TREE_E_DIMS: return "unsupported or inconsistent dimensions";
+    case SSM_TREE_E_DTYPE: return "unknown input dtype";
+    case SSM_TREE_E_ALIAS: return "an output overlaps an input";
+    case SSM_TREE_E_HIP: return "HIP kernel launch failed";
+    case SSM_TREE_E_FLAGS: return "unknown flag bits";
+    case SSM_TREE_E_TREE: return "parent[] is not a BFS-ordered tree";
+    case SSM_TREE_E_PATH: return "path is not a root-to-node path of the tree";
+    default: return "unknown status";
+  }
+}
+
+int ssm_tree_verify(const ssm_tree_dims* dims, const ssm_tree_params* params, const int32_t* parent,
+                    const void* x, const void* B, const void* C, const void* dt_raw, const void* conv_window,
+                    const float* state, float* y, int32_t* seq_status, void* hip_stream) {
+  Dims d;
+  int st = check_dims(dims, &d);
+  if (st) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
+  if (d.L == 0 || d.Bsz == 0) return SSM_TREE_OK;
+  if (d.T == 0) {
+    if (seq_status) return launch_status(seq_status, d.Bsz, SSM_TREE_OK, s) == hipSuccess ? SSM_TREE_OK : SSM_TREE_E_HIP;
+    return SSM_TREE_OK;
+  }
+  if ((st = check_params(params))) return st;
+  if (!parent || !x || !B || !C || !dt_raw || !state || !y || (d.W > 1 && !conv_window)) return SSM_TREE_E_NULL;
+  const void* ptrs[] = {parent, x, B, C, dt_raw, state, y, seq_status, d.W > 1 ? conv_window : nullptr};
+  for (const void* p : ptrs)
+    if (p && misaligned(p)) return SSM_TREE_E_ALIGN;
+  const int64_t e = dims->in_dtype == SSM_TREE_BF16 ? 2 : 4;
+  const int64_t U = (int64_t)d.L * d.Bsz, T = d.T, DI = d.d_in;
+  const Range ry = range_of(y, U * T * DI * 4);
+  const Range ins[] = {range_of(parent, (int64_t)d.Bsz * T * 4), range_of(x, U * T * DI * e),
+                       range_of(B, U * T * d.G * d.N * e), range_of(C, U * T * d.G * d.N * e),
+                       range_of(dt_raw, U * T * d.H * e), range_of(state, U * DI * d.N * 4),
+                       range_of(conv_window, d.W > 1 ? U * (d.W - 1) * DI * e : 0),
+                       range_of(params->A, d.L * (int64_t)d.H * 4), range_of(params->D, d.L * (int64_t)d.H * 4),
+                       range_of(params->dt_bias, d.L * (int64_t)d.H * 4),
+                       range_of(params->conv_w, d.L * DI * d.W * 4),
+                       range_of(params->conv_b, params->conv_b ? d.L * DI * 4 : 0)};
+  for (const Range& r : ins)
+    if (overlaps(ry, r)) return SSM_TREE_E_ALIAS;
+  if (seq_status) {
+    const Range rs = range_of(seq_status, (int64_t)d.Bsz * 4);
+    if (overlaps(rs, ry)) return SSM_TREE_E_ALIAS;
+    for (const Range& r : ins)
+      if (overlaps(rs, r)) return SSM_TREE_E_ALIAS;
+  }
+  VerifyArgs a;
+  a.d = d;
+  a.prm = Params{params->A, params->D, params->dt_bias, params->conv_w, params->conv_b};
+  a.parent = parent;
+  a.x = x;
+  a.B = B;
+  a.C = C;
+  a.dt_raw = dt_raw;
+  a.window = conv_window;
+  a.state = state;
+  a.y = y;
+  a.seq_status = seq_status;
+  return launch_verify(a, dims->in_dtype == SSM_TREE_BF16, s);
+}
+
+int ssm_tree_commit(const ssm_tree_dims* dims, const ssm_tree_params* params, const int32_t* parent,
+                    const int32_t* path, const int32_t* path_len, const void* x, const void* B, const void* dt_raw,
+                    const void* conv_window_in, const float* state_in, void* conv_window_out, float* state_out,
+                    int32_t* seq_status, void* hip_stream) {
+  Dims d;
+  int st = check_dims(dims, &d);
+  if (st) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
+  if (d.L == 0 || d.Bsz == 0) return SSM_TREE_OK;
+  if ((st = check_params(params))) return st;
+  if (!path_len || !state_in || !state_out) return SSM_TREE_E_NULL;
+  if (d.T > 0 && (!parent || !path || !x || !B || !dt_raw)) return SSM_TREE_E_NULL;
+  if (d.W > 1 && (!conv_window_in || !conv_window_out)) return SSM_TREE_E_NULL;
+  const void* ptrs[] = {parent, path, path_len, x, B, dt_raw, state_in, state_out, seq_status,
+                        d.W > 1 ? conv_window_in : nullptr, d.W > 1 ? conv_window_out : nullptr};
+  for (const void* p : ptrs)
+    if (p && misaligned(p)) return SSM_TREE_E_ALIGN;
+  const int64_t e = dims->in_dtype == SSM_TREE_BF16 ? 2 : 4;
+  const int64_t U = (int64_t)d.L * d.Bsz, T = d.T, DI = d.d_in;
+  const int64_t wbytes = d.W > 1 ? U * (d.W - 1) * DI * e : 0;
+  const Range rso = range_of(state_out, U * DI * d.N * 4), rsi = range_of(state_in, U * DI * d.N * 4);
+  const Range rwo = range_of(conv_window_out, wbytes), rwi = range_of(conv_window_in, wbytes);
+  const Range others[] = {range_of(parent, (int64_t)d.Bsz * T * 4), range_of(path, (int64_t)d.Bsz * T * 4),
+                          range_of(path_len, (int64_t)d.Bsz * 4), range_of(x, U * T * DI * e),
+                          range_of(B, U * T * d.G * d.N * e), range_of(dt_raw, U * T * d.H * e),
+                          range_of(params->A, d.L * (int64_t)d.H * 4), range_of(params->D, d.L * (int64_t)d.H * 4),
+                          range_of(params->dt_bias, d.L * (int64_t)d.H * 4),
+                          range_of(params->conv_w, d.L * DI * d.W * 4),
+                          range_of(params->conv_b, params->conv_b ? d.L * DI * 4 : 0)};
+  // outputs: exact in-place allowed, any other overlap rejected
+  if (state_out != state_in && overlaps(rso, rsi)) return SSM_TREE_E_ALIAS;
+  if (d.W > 1 && conv_window_out != conv_window_in && overlaps(rwo, rwi)) return SSM_TREE_E_ALIAS;
+  if (overlaps(rso, rwo) || overlaps(rso, rwi) || overlaps(rwo, rsi)) return SSM_TREE_E_ALIAS;
+  for (const Range& r : others)
+    if (overlaps(rso, r) || overlaps(rwo, r)) return SSM_TREE_E_ALIAS;
+  if (seq_status) {
+    const Range rs = range_of(seq_status, (int64_t)d.Bsz * 4);
+    if (overlaps(rs, rso) || overlaps(rs, rwo) || overlaps(rs, rsi) || overlaps(rs, rwi)) return SSM_TREE_E_ALIAS;
+    for (const Range& r : others)
+      if (overlaps(rs, r)) return SSM_TREE_E_ALIAS;
+  }
+  CommitArgs a;
+  a.d = d;
+  a.prm = Params{params->A, params->D, params->dt_bias, params->conv_w, params->conv_b};
+  a.parent = parent;
+  a.path = path;
+  a.path_len = path_len;
+  a.x = x;
+  a.B = B;
+  a.dt_raw = dt_raw;
+  a.window_in = conv_window_in;
+  a.state_in = state_in;
+  a.window_out = conv_window_out;
+  a.state_out = state_out;
+  a.seq_status = seq_status;
+  return launch_commit(a, dims->in_dtype == SSM_TREE_BF16, s) == hipSuccess ? SSM_TREE_OK : SSM_TREE_E_HIP;
+}
+
+int ssm_tree_plan(const ssm_tree_dims* dims, const int32_t* parent, int32_t* plan_out, void* hip_stream) {
+  if (!dims) return SSM_TREE_E_NULL;
+  if (dims->batch < 0 || dims->n_nodes < 0 || dims->n_nodes > kMaxNodes || dims->conv_width < 1 ||
+      dims->conv_width > 4 || dims->batch > 65535)
+    return SSM_TREE_E_DIMS;
+  if (dims->batch == 0) return SSM_TREE_OK;
+  if (!plan_out || (dims->n_nodes > 0 && !parent)) return SSM_TREE_E_NULL;
+  if (misaligned(plan_out) || (parent && misaligned(parent))) return SSM_TREE_E_ALIGN;
+  const int64_t nb = (int64_t)dims->batch * (SSM_TREE_PLAN_HEADER + dims->n_nodes * SSM_TREE_PLAN_STRIDE) * 4;
+  if (parent && overlaps(range_of(plan_out, nb), range_of(parent, (int64_t)dims->batch * dims->n_nodes * 4)))
+    return SSM_TREE_E_ALIAS;
+  return launch_plan(parent, dims->batch, dims->n_nodes, dims->conv_width, plan_out,
+                     reinterpret_cast<hipStream_t>(hip_stream)) == hipSuccess
+             ? SSM_TREE_OK
+             : SSM_TREE_E_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,189 @@
+// commit.hip - ssm_tree_commit kernel for gfx950.
+//
+// SpecMamba page sec. 3.1: after verification the root state is advanced
+// along the accepted path by recomputing the recurrence from the stored
+// per-token dt, B and x (no per-node state is kept between verify and
+// commit).  For path nodes u_0 .. u_{m-1}:
+//   h <- dA_{u_k} h + (dt_{u_k} x~_{u_k}) B_{u_k}^T     k = 0 .. m-1
+// and the conv window becomes the last W-1 rows of (old window, x_{u_0..}),
+// copied bit for bit.
+//
+// The state update is elementwise, so the kernel is a coalesced HBM stream:
+// a workgroup owns 64 channels (rows) of one (layer, sequence); its threads
+// issue all their 16-byte state loads first, prepare the per-path scalars,
+// the conv outputs and the fp32 B rows in LDS, then update and store.
+#include "common.h"
+
+namespace ssmt {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kCommitRows = 64;
+constexpr int kCommitThreads = 256;
+
+template <typename TIn, int QPT>
+__global__ void __launch_bounds__(kCommitThreads) commit_kernel(CommitArgs a, int HWMAX) {
+  const Dims d = a.d;
+  const int T = d.T, N = d.N, P = d.P, H = d.H, W = d.W, DI = d.d_in;
+  const int b = blockIdx.y, l = blockIdx.z;
+  const int64_t unit = (int64_t)l * d.Bsz + b;
+  const int c0 = blockIdx.x * kCommitRows;
+  const int g = c0 / (DI / d.G);
+  const int h_lo = c0 / P;
+  const int qpr = N / 4;  // float4 quads per row
+
+  extern __shared__ __align__(16) unsigned char smem[];
+  int32_t* s_parent = reinterpret_cast<int32_t*>(smem);
+  int32_t* s_path = s_parent + kMaxNodes;
+  int32_t* s_misc = s_path + kMaxNodes;  // [0] = len, [1] = valid status
+  float* s_dA = reinterpret_cast<float*>(s_misc + 4);      // [T][HWMAX]
+  float* s_dtx = s_dA + kMaxNodes * HWMAX;                 // [T][64]
+  float* s_B = s_dtx + kMaxNodes * kCommitRows;            // [T][N]
+
+  // ---- issue the state loads first (QPT quads per thread) ----
+  const float* sin = a.state_in + (unit * DI + c0) * (int64_t)N;
+  f32x4 hq[QPT];
+#pragma unroll
+  for (int it = 0; it < QPT; ++it) {
+    const int qi = threadIdx.x + it * kCommitThreads;
+    hq[it] = reinterpret_cast<const f32x4*>(sin)[qi];
+  }
+
+  // ---- validate tree and path ----
+  for (int i = threadIdx.x; i < T; i += blockDim.x) {
+    s_parent[i] = a.parent[(int64_t)b * T + i];
+    s_path[i] = a.path[(int64_t)b * T + i];
+  }
+  __syncthreads();
+  const bool tree_ok = tree_is_valid(s_parent, T);
+  if (threadIdx.x == 0) {
+    int st = tree_ok ? SSM_TREE_OK : SSM_TREE_E_TREE;
+    const int len = a.path_len[b];
+    if (st == SSM_TREE_OK) {
+      if (len < 0 || len > T) st = SSM_TREE_E_PATH;
+      for (int k = 0; st == SSM_TREE_OK && k < len; ++k) {
+        const int v = s_path[k];
+        if (v < 0 || v >= T || s_parent[v] != (k == 0 ? -1 : s_path[k - 1])) st = SSM_TREE_E_PATH;
+      }
+    }
+    s_misc[0] = st == SSM_TREE_OK ? len : 0;
+    s_misc[1] = st;
+    if (blockIdx.x == 0 && l == 0 && a.seq_status) a.seq_status[b] = st;
+  }
+  __syncthreads();
+  if (s_misc[1] != SSM_TREE_OK) return;  // outputs of a failed sequence stay unwritten
+  const int len = s_misc[0];
+
+  // ---- per-path scalars, conv outputs, B rows ----
+  const int HW = (c0 + kCommitRows - 1) / P - h_lo + 1;
+  const TIn* dtr = reinterpret_cast<const TIn*>(a.dt_raw) + unit * T * H;
+  for (int i = threadIdx.x; i < len * HW; i += blockDim.x) {
+    const int k = i / HW, hh = i % HW, h = h_lo + hh;
+    const float z = load_in(dtr, (int64_t)s_path[k] * H + h) + a.prm.dt_bias[(int64_t)l * H + h];
+    const float dt = softplus_f32(z);
+    s_dA[k * HWMAX + hh] = expf(dt * a.prm.A[(int64_t)l * H + h]);
+  }
+  const TIn* xin = reinterpret_cast<const TIn*>(a.x) + unit * T * DI;
+  const TIn* Bg = reinterpret_cast<const TIn*>(a.B) + (unit * T * d.G + g) * (int64_t)N;
+  for (int i = threadIdx.x; i < len * N; i += blockDim.x) {
+    const int k = i / N, n = i % N;
+    s_B[k * N + n] = load_in(Bg + (int64_t)s_path[k] * d.G * N, n);
+  }
+  if (threadIdx.x < kCommitRows) {
+    const int c = c0 + threadIdx.x, h = c / P;
+    const TIn* win_in = reinterpret_cast<const TIn*>(a.window_in) + unit * (W - 1) * (int64_t)DI;
+    // wj[jj] weighs conv input jj (0 = the token itself, jj = the jj-th previous token)
+    float wj[4];
+    const float* cw = a.prm.conv_w + ((int64_t)l * DI + c) * W;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) wj[jj] = (jj < W) ? cw[W - 1 - jj] : 0.0f;
+    const float cb = a.prm.conv_b ? a.prm.conv_b[(int64_t)l * DI + c] : 0.0f;
+    // sliding window of raw inputs, hist[0] = newest
+    float hist[3];
+#pragma unroll
+    for (int r = 0; r < 3; ++r) hist[r] = (r < W - 1) ? load_in(win_in, (int64_t)(W - 2 - r) * DI + c) : 0.0f;
+    // new window row r (oldest first) is element len + r of the sequence
+    // (old window rows, x of the path nodes); read every source before any
+    // write so that an in-place window is safe
+    TIn nw[3];
+#pragma unroll
+    for (int r = 0; r < 3; ++r) {
+      if (r < W - 1) {
+        const int e = len + r;
+        nw[r] = (e < W - 1) ? win_in[(int64_t)e * DI + c] : xin[(int64_t)s_path[e - (W - 1)] * DI + c];
+      }
+    }
+    for (int k = 0; k < len; ++k) {
+      const int v = s_path[k];
+      const float xv = load_in(xin, (int64_t)v * DI + c);
+      float z = fmaf(wj[0], xv, cb);
+#pragma unroll
+      for (int jj = 1; jj < 4; ++jj)
+        if (jj < W) z = fmaf(wj[jj], hist[jj - 1], z);
+      const float xt = d.silu ? silu_f32(z) : z;
+      const float zdt = load_in(dtr, (int64_t)v * H + h) + a.prm.dt_bias[(int64_t)l * H + h];
+      s_dtx[k * kCommitRows + threadIdx.x] = softplus_f32(zdt) * xt;
+      hist[2] = hist[1];
+      hist[1] = hist[0];
+      hist[0] = xv;
+    }
+    if (W > 1) {
+      TIn* win_out = reinterpret_cast<TIn*>(a.window_out) + unit * (W - 1) * (int64_t)DI;
+#pragma unroll
+      for (int r = 0; r < 3; ++r)
+        if (r < W - 1) win_out[(int64_t)r * DI + c] = nw[r];
+    }
+  }
+  __syncthreads();
+
+  // ---- state update along the path ----
+  float* sout = a.state_out + (unit * DI + c0) * (int64_t)N;
+#pragma unroll
+  for (int it = 0; it < QPT; ++it) {
+    const int qi = threadIdx.x + it * kCommitThreads;
+    const int row = qi / qpr, n = (qi % qpr) * 4;
+    const int hh = (c0 + row) / P - h_lo;
+    f32x4 h = hq[it];
+    for (int k = 0; k < len; ++k) {
+      const float dA = s_dA[k * HWMAX + hh];
+      const float cx = s_dtx[k * kCommitRows + row];
+      const f32x4 bq = *reinterpret_cast<const f32x4*>(s_B + k * N + n);
+      h.x = fmaf(dA, h.x, cx * bq.x);
+      h.y = fmaf(dA, h.y, cx * bq.y);
+      h.z = fmaf(dA, h.z, cx * bq.z);
+      h.w = fmaf(dA, h.w, cx * bq.w);
+    }
+    reinterpret_cast<f32x4*>(sout)[qi] = h;
+  }
+}
+
+template <typename TIn, int QPT>
+static hipError_t launch_c(const CommitArgs& a, hipStream_t s) {
+  const int HWMAX = ((kCommitRows + a.d.P - 1) / a.d.P + 1 + 3) & ~3;
+  const size_t lds = sizeof(int32_t) * (2 * kMaxNodes + 4) +
+                     sizeof(float) * ((size_t)kMaxNodes * HWMAX + kMaxNodes * kCommitRows + (size_t)a.d.T * a.d.N);
+  dim3 grid(a.d.d_in / kCommitRows, a.d.Bsz, a.d.L);
+  hipError_t e = allow_lds(commit_kernel<TIn, QPT>, lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((commit_kernel<TIn, QPT>), grid, dim3(kCommitThreads), lds, s, a, HWMAX);
+  return hipGetLastError();
+}
+
+template <typename TIn>
+static hipError_t launch_cin(const CommitArgs& a, hipStream_t s) {
+  // quads per thread = 64 rows * N / 4 / 256 threads = N / 16
+  switch (a.d.N) {
+    case 16: return launch_c<TIn, 1>(a, s);
+    case 32: return launch_c<TIn, 2>(a, s);
+    case 64: return launch_c<TIn, 4>(a, s);
+    case 128: return launch_c<TIn, 8>(a, s);
+    case 256: return launch_c<TIn, 16>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_commit(const CommitArgs& a, bool bf16, hipStream_t s) {
+  return bf16 ? launch_cin<bf16_t>(a, s) : launch_cin<float>(a, s);
+}
+
+}  // namespace ssmt

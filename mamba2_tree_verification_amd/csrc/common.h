@@ -1,0 +1,142 @@
+// common.h - device helpers and launch argument blocks shared by the HIP
+// kernels of libssm_tree.so (gfx950 only; wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/ssm_tree.h"
+
+namespace ssmt {
+
+constexpr int kWave = 64;
+constexpr int kMaxNodes = 64;
+
+// ---------------------------------------------------------------------------
+// element access
+// ---------------------------------------------------------------------------
+
+struct bf16_t {
+  uint16_t bits;
+};
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t b) { return __uint_as_float(b << 16); }
+
+template <typename TIn>
+__device__ __forceinline__ float load_in(const TIn* p, int64_t i);
+
+template <>
+__device__ __forceinline__ float load_in<float>(const float* p, int64_t i) {
+  return p[i];
+}
+
+template <>
+__device__ __forceinline__ float load_in<bf16_t>(const bf16_t* p, int64_t i) {
+  return bf16_bits_to_float(p[i].bits);
+}
+
+// softplus with the large-argument cut-over used by Mamba2 (z for z > 20)
+__device__ __forceinline__ float softplus_f32(float z) { return z > 20.0f ? z : log1pf(expf(z)); }
+
+__device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + expf(-z)); }
+
+// ---------------------------------------------------------------------------
+// launch argument blocks (passed by value)
+// ---------------------------------------------------------------------------
+
+struct Dims {
+  int32_t L, Bsz, T, H, P, N, G, W, silu;
+  int32_t d_in;  // H * P
+};
+
+struct Params {
+  const float* A;
+  const float* D;
+  const float* dt_bias;
+  const float* conv_w;
+  const float* conv_b;
+};
+
+struct VerifyArgs {
+  Dims d;
+  Params prm;
+  const int32_t* parent;
+  const void* x;
+  const void* B;
+  const void* C;
+  const void* dt_raw;
+  const void* window;
+  const float* state;
+  float* y;
+  int32_t* seq_status;
+};
+
+struct CommitArgs {
+  Dims d;
+  Params prm;
+  const int32_t* parent;
+  const int32_t* path;
+  const int32_t* path_len;
+  const void* x;
+  const void* B;
+  const void* dt_raw;
+  const void* window_in;
+  const float* state_in;
+  void* window_out;
+  float* state_out;
+  int32_t* seq_status;
+};
+
+// Allow a kernel more than the default 64 KiB of dynamic LDS (gfx950 has
+// 160 KiB per CU).
+template <typename K>
+inline hipError_t allow_lds(K* kernel, size_t bytes) {
+  if (bytes <= 65536) return hipSuccess;
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                             (int)bytes);
+}
+
+// ---------------------------------------------------------------------------
+// tree bookkeeping in LDS (one workgroup, T <= 64)
+// ---------------------------------------------------------------------------
+
+// BFS labelling check: parent[0] = -1, -1 <= parent[i] < i, non-decreasing.
+// Every thread of the workgroup must call it (it contains a barrier).
+__device__ __forceinline__ bool tree_is_valid(const int32_t* s_parent, int T) {
+  int bad = 0;
+  for (int i = threadIdx.x; i < T; i += blockDim.x) {
+    const int p = s_parent[i];
+    if (i == 0)
+      bad |= (p != -1);
+    else
+      bad |= (p < -1) | (p >= i) | (p < s_parent[i - 1]);
+  }
+  return __syncthreads_or(bad) == 0;
+}
+
+// Code of conv input j (1 = parent) of node v: node index, or -(1 + r) for
+// row r of the committed window (row W-2 newest).
+__device__ __forceinline__ int conv_input_code(const int32_t* s_parent, int v, int j, int W) {
+  int u = v;
+  int k = 0;
+  while (k < j && u >= 0) {
+    u = s_parent[u];
+    ++k;
+  }
+  if (u >= 0) return u;
+  return -(1 + (W - 2) - (j - k));
+}
+
+// Per node: depth and the root path (top first) as uint8 node ids,
+// path row stride kMaxNodes.  Threads split the nodes.
+__device__ __forceinline__ void build_paths(const int32_t* s_parent, int T, int32_t* s_depth, uint8_t* s_path) {
+  for (int v = threadIdx.x; v < T; v += blockDim.x) {
+    int d = 0;
+    for (int u = v; u >= 0; u = s_parent[u]) ++d;
+    s_depth[v] = d;
+    int k = d - 1;
+    for (int u = v; u >= 0; u = s_parent[u]) s_path[v * kMaxNodes + (k--)] = (uint8_t)u;
+  }
+}
+
+}  // namespace ssmt

@@ -48,6 +48,7 @@ class Config:
     state_std: float
     tree: str
     silu: bool = False
+    conv_bias: bool = False
 
     @property
     def d_in(self) -> int:
@@ -205,12 +206,39 @@ def make_trees(cfg: Config, rng: np.random.Generator):
                 dd = int(rng.integers(dmin, 9))
                 par = random_tree(rng, T, bb, dd, spine=dd)
             pth = _random_depth_path(rng, par)
+        elif kind == "forest":
+            par = random_forest(rng, T)
+            pth = random_prefix_path(rng, par)
+        elif kind == "chain_or_star":
+            par = chain(T) if b % 2 == 0 else star(T)
+            pth = random_prefix_path(rng, par)
         else:
             raise ValueError(kind)
         parent[b] = par
         plen[b] = len(pth)
         path[b, : len(pth)] = pth
     return parent, path, plen
+
+
+def random_forest(rng: np.random.Generator, T: int) -> np.ndarray:
+    """Random BFS labelling, possibly several root-level nodes: each parent is
+    drawn between the previous node's parent and i - 1."""
+    if T == 0:
+        return np.zeros(0, dtype=np.int32)
+    p = [-1]
+    for i in range(1, T):
+        p.append(int(rng.integers(p[-1], i)))
+    return np.array(p, dtype=np.int32)
+
+
+def random_prefix_path(rng, par):
+    """A prefix of the root path of a uniformly random node (length 0 allowed)."""
+    T = len(par)
+    if T == 0:
+        return []
+    v = int(rng.integers(T))
+    full = root_path(par, v)
+    return full[: int(rng.integers(0, len(full) + 1))]
 
 
 def _random_depth_path(rng, par):
@@ -251,7 +279,7 @@ def tensor_shapes(cfg: Config) -> dict:
     L, Bsz, T, H, P, N, G, W, d = cfg.L, cfg.Bsz, cfg.T, cfg.H, cfg.P, cfg.N, cfg.G, cfg.W, cfg.d_in
     return dict(x=(L, Bsz, T, d), B=(L, Bsz, T, G, N), C=(L, Bsz, T, G, N), dt_raw=(L, Bsz, T, H),
                 window=(L, Bsz, W - 1, d), state=(L, Bsz, H, P, N), A=(L, H), D=(L, H), dt_bias=(L, H),
-                conv_w=(L, d, W))
+                conv_w=(L, d, W), conv_b=(L, d))
 
 
 # (stream, dist, a, b, is_input_dtype)
@@ -267,6 +295,7 @@ def _specs(cfg: Config) -> dict:
         D=(S_D, DIST_NORMAL, 0.0, 1.0, False),
         dt_bias=(S_DTB, DIST_UNIFORM, -4.0, -2.0, False),
         conv_w=(S_CONVW, DIST_NORMAL, 0.0, 0.5, False),
+        conv_b=(S_CONVB, DIST_NORMAL, 0.0, 0.5, False),
     )
 
 
@@ -279,6 +308,7 @@ def draw(cfg: Config, name: str, shape=None, offset: int = 0, nthreads=None) -> 
 def make_inputs(cfg: Config, nthreads=None, skip=()) -> Inputs:
     rng = np.random.Generator(np.random.PCG64(cfg.seed))
     parent, path, plen = make_trees(cfg, rng)
+    skip = set(skip) | (set() if cfg.conv_bias else {"conv_b"})
     t = {k: (None if k in skip else draw(cfg, k, nthreads=nthreads)) for k in tensor_shapes(cfg)}
     return Inputs(cfg=cfg, parent=parent, path=path, path_len=plen, **t)
 
@@ -288,13 +318,13 @@ def unit_offsets(cfg: Config, l: int, b: int) -> dict:
     L, Bsz, T, H, P, N, G, W, d = cfg.L, cfg.Bsz, cfg.T, cfg.H, cfg.P, cfg.N, cfg.G, cfg.W, cfg.d_in
     u = l * Bsz + b
     return dict(x=u * T * d, B=u * T * G * N, C=u * T * G * N, dt_raw=u * T * H, window=u * (W - 1) * d,
-                state=u * H * P * N, A=l * H, D=l * H, dt_bias=l * H, conv_w=l * d * W)
+                state=u * H * P * N, A=l * H, D=l * H, dt_bias=l * H, conv_w=l * d * W, conv_b=l * d)
 
 
 def unit_shapes(cfg: Config) -> dict:
     T, H, P, N, G, W, d = cfg.T, cfg.H, cfg.P, cfg.N, cfg.G, cfg.W, cfg.d_in
     return dict(x=(T, d), B=(T, G, N), C=(T, G, N), dt_raw=(T, H), window=(W - 1, d), state=(H, P, N),
-                A=(H,), D=(H,), dt_bias=(H,), conv_w=(d, W))
+                A=(H,), D=(H,), dt_bias=(H,), conv_w=(d, W), conv_b=(d,))
 
 
 def unit_f64(cfg: Config, l: int, b: int, inputs: Inputs | None = None) -> dict:
@@ -304,12 +334,14 @@ def unit_f64(cfg: Config, l: int, b: int, inputs: Inputs | None = None) -> dict:
     (bit-identical either way).
     """
     offs, shp = unit_offsets(cfg, l, b), unit_shapes(cfg)
-    out = {}
+    out = {"conv_b": None}
     for k in shp:
+        if k == "conv_b" and not cfg.conv_bias:
+            continue
         is_in = _specs(cfg)[k][4]
         if inputs is not None:
             full = getattr(inputs, k)
-            if k in ("A", "D", "dt_bias", "conv_w"):
+            if k in ("A", "D", "dt_bias", "conv_w", "conv_b"):
                 arr = full[l]
             else:
                 arr = full[l, b]

@@ -89,8 +89,42 @@ typedef struct {
   int bf16;
 } tg_job;
 
+/* normal draws two at a time: one log/sqrt and one sin/cos pair per pair
+ * index k gives elements 2k and 2k+1 (same values as tg_normal) */
+static void tg_normal_run(const tg_job* j) {
+  int64_t i = j->lo;
+  while (i < j->hi) {
+    uint64_t gi = (uint64_t)(j->offset + i);
+    if ((gi & 1) == 0 && i + 1 < j->hi) {
+      uint64_t k = gi >> 1;
+      double u1 = tg_u01(j->key, 2 * k), u2 = tg_u01(j->key, 2 * k + 1);
+      double r = sqrt(-2.0 * log(u1)), t = TG_TWO_PI * u2;
+      double z0 = j->a + j->b * (r * cos(t)), z1 = j->a + j->b * (r * sin(t));
+      if (j->bf16) {
+        ((uint16_t*)j->out)[i] = tg_f32_to_bf16((float)z0);
+        ((uint16_t*)j->out)[i + 1] = tg_f32_to_bf16((float)z1);
+      } else {
+        ((float*)j->out)[i] = (float)z0;
+        ((float*)j->out)[i + 1] = (float)z1;
+      }
+      i += 2;
+    } else {
+      double z = tg_value(j->key, gi, 0, j->a, j->b);
+      if (j->bf16)
+        ((uint16_t*)j->out)[i] = tg_f32_to_bf16((float)z);
+      else
+        ((float*)j->out)[i] = (float)z;
+      i += 1;
+    }
+  }
+}
+
 static void* tg_worker(void* p) {
   tg_job* j = (tg_job*)p;
+  if (j->dist == 0) {
+    tg_normal_run(j);
+    return NULL;
+  }
   if (j->bf16) {
     uint16_t* o = (uint16_t*)j->out;
     for (int64_t i = j->lo; i < j->hi; ++i)
