@@ -25,6 +25,10 @@
 // C_v . B_u do not depend on N.  Child states are never materialised, so y
 // is the only output.
 //
+// Trees of at most 16 nodes whose heads are a multiple of 16 channels wide
+// take the matrix-core kernel in verify_mfma.hip (same formula, both sums as
+// MFMA contractions); this file's VALU kernel serves every other shape.
+//
 // Mapping.  A workgroup of NW waves owns one (layer, sequence) and NBLK
 // consecutive blocks of NW*R*64 channels (rows of the root state) inside one
 // B/C group; the tree prologue (paths, step sizes, C.B dots) runs once per
@@ -88,6 +92,16 @@ struct CRow<bf16_t> {
     return __uint_as_float((i & 1) ? (w[i >> 1] & 0xFFFF0000u) : (w[i >> 1] << 16));
   }
 };
+
+// One input element as raw bits (loaded early, widened when used).
+template <typename TIn>
+__device__ __forceinline__ uint32_t load_bits(const TIn* p, int64_t i);
+template <>
+__device__ __forceinline__ uint32_t load_bits<float>(const float* p, int64_t i) { return __float_as_uint(p[i]); }
+template <>
+__device__ __forceinline__ uint32_t load_bits<bf16_t>(const bf16_t* p, int64_t i) { return p[i].bits; }
+template <typename TIn>
+__device__ __forceinline__ float widen_bits(uint32_t b) { return sizeof(TIn) == 2 ? __uint_as_float(b << 16) : __uint_as_float(b); }
 
 // Raw 4-element loads converted to float later, so that a thread can issue
 // several before waiting on any.
@@ -191,21 +205,22 @@ template <int R, int TMAX, bool DENSE>
 struct VerifyLds {
   static constexpr int kPairs = TMAX * (TMAX + 1) / 2;
   static constexpr int kWaveScratch = (R * kWave * kChunk > (TMAX + 3) * kWave) ? R * kWave * kChunk : (TMAX + 3) * kWave;
-  int parent, depth, cidx, path, dt, lg, Dh, cb, pair, a, dA, M, dyn, total;
+  int parent, depth, cidx, path, onk, dt, S, Dh, cb, pair, a, dA, M, dyn, total;
   __host__ __device__ VerifyLds(const VerifyGeom& g) {
     int o = 0;
     parent = o; o += 4 * kMaxNodes;
     depth = o; o += 4 * kMaxNodes;
     cidx = o; o += 4 * kMaxNodes;
     path = o; o += (TMAX * TMAX + 15) & ~15;
+    onk = o; o += (TMAX * TMAX + 15) & ~15;
     dt = o; o += 4 * TMAX * g.HWG;
-    lg = o; o += 4 * TMAX * g.HWG;
+    S = o; o += 4 * TMAX * g.HWG;
     Dh = o; o += 4 * ((g.HWG + 3) & ~3);
     cb = o; o += 4 * TMAX * TMAX;
     pair = o; o += (2 * kPairs + 15) & ~15;
-    a = o; o += 4 * TMAX * g.HB;
-    dA = o; o += DENSE ? 0 : 4 * TMAX * g.HB;
-    M = o; o += DENSE ? 4 * g.HB * TMAX * TMAX : 0;
+    a = o; o += 3 * 4 * TMAX * g.HB;                           // three blocks in flight
+    dA = o; o += DENSE ? 0 : 3 * 4 * TMAX * g.HB;
+    M = o; o += DENSE ? 3 * 4 * g.HB * TMAX * TMAX : 0;
     dyn = o;
     const int stage = 2 * TMAX * (g.NC + 4);
     o += 4 * (g.NW * kWaveScratch > stage ? g.NW * kWaveScratch : stage);
@@ -236,14 +251,17 @@ __global__ void __launch_bounds__(kThreads) verify_proj_kernel(VerifyArgs a, Ver
   int32_t* s_depth = reinterpret_cast<int32_t*>(smem + lo.depth);
   int32_t* s_cidx = reinterpret_cast<int32_t*>(smem + lo.cidx);   // xs rows of conv inputs 1..3, 8 bits each
   uint8_t* s_path = smem + lo.path;                                // [TMAX][TMAX] root path, top first
+  uint8_t* s_onk = smem + lo.onk;                                  // [TMAX][TMAX] k + 1 if u = path(v)[k], else 0
   float* s_dt = reinterpret_cast<float*>(smem + lo.dt);            // [TMAX][HWG] dt
-  float* s_lg = reinterpret_cast<float*>(smem + lo.lg);            // [TMAX][HWG] dt * A
+  float* s_S = reinterpret_cast<float*>(smem + lo.S);              // [TMAX][HWG] sum of dt * A over the root path
   float* s_D = reinterpret_cast<float*>(smem + lo.Dh);             // [HWG]
   float* s_cb = reinterpret_cast<float*>(smem + lo.cb);            // [TMAX][TMAX] C_v . B_(k-th path node)
   uint16_t* s_pair = reinterpret_cast<uint16_t*>(smem + lo.pair);  // (v << 8 | k)
-  float* s_a = reinterpret_cast<float*>(smem + lo.a);              // [TMAX][HB] decay of the root state
-  float* s_dA = reinterpret_cast<float*>(smem + lo.dA);            // [TMAX][HB] (path-walk epilogue)
-  float* s_M = reinterpret_cast<float*>(smem + lo.M);              // [HB][TMAX][TMAX] (dense epilogue)
+  // per-block coefficients, buffer blk % 3: block k+1's are written during block
+  // k's stream while block k's are read by its epilogue
+  float* s_a = reinterpret_cast<float*>(smem + lo.a);              // [3][TMAX][HB] decay of the root state
+  float* s_dA = reinterpret_cast<float*>(smem + lo.dA);            // [3][TMAX][HB] (path-walk epilogue)
+  float* s_M = reinterpret_cast<float*>(smem + lo.M);              // [3][HB][TMAX][TMAX] (dense epilogue)
   float* s_dyn = reinterpret_cast<float*>(smem + lo.dyn);          // prologue staging, then per wave
   float* s_mine = s_dyn + wave * Lds::kWaveScratch;
 
@@ -340,11 +358,18 @@ __global__ void __launch_bounds__(kThreads) verify_proj_kernel(VerifyArgs a, Ver
     const int v = i / HWG, hh = i % HWG, h = h_wg + hh;
     const float dt = softplus_f32(load_in(dtr, (int64_t)v * H + h) + a.prm.dt_bias[(int64_t)l * H + h]);
     s_dt[v * HWG + hh] = dt;
-    s_lg[v * HWG + hh] = dt * a.prm.A[(int64_t)l * H + h];
+    s_S[v * HWG + hh] = dt * a.prm.A[(int64_t)l * H + h];  // this node's own term for now
   }
+  for (int i = tid; i < TMAX * TMAX; i += nthr) s_onk[i] = 0;
   for (int i = tid; i < HWG; i += nthr) s_D[i] = a.prm.D[(int64_t)l * H + h_wg + i];
   stage_store(0);
   __syncthreads();
+  // cumulative log-decay along each root path (parents precede children)
+  for (int hh = tid; hh < HWG; hh += nthr)
+    for (int v = 0; v < T; ++v)
+      if (s_parent[v] >= 0) s_S[v * HWG + hh] += s_S[s_parent[v] * HWG + hh];
+  for (int v = tid; v < T; v += nthr)
+    for (int k = 0; k < s_depth[v]; ++k) s_onk[v * TMAX + s_path[v * TMAX + k]] = (uint8_t)(k + 1);
   // (node, ancestor) pairs: node v owns slots [sum of earlier depths, + depth(v))
   for (int v = tid; v < T; v += nthr) {
     int off = 0;
@@ -385,31 +410,39 @@ __global__ void __launch_bounds__(kThreads) verify_proj_kernel(VerifyArgs a, Ver
   const TIn* win = reinterpret_cast<const TIn*>(a.window) + unit * (W - 1) * (int64_t)DI;
   f32x4* lds4 = reinterpret_cast<f32x4*>(s_mine);
   float acc[R][TMAX];
+  uint32_t xr[R][TMAX + 3];  // the block's raw x (nodes, then window rows), in flight during the stream
+  float wt[R][5];            // the block's conv weights (input jj = jj-th ancestor) and bias, likewise
 
-  // Per-block coefficients: a_v, and M_h[v][u] (dense) or dA (path walk).
-  auto block_coeffs = [&](int blk) {
+  // Per-block coefficients a_v, and M_h[v][u] (dense) or dA (path walk):
+  // slice `part` of `nparts` of them, so that they can be spread over a
+  // block's chunks.
+  auto block_coeffs = [&](int blk, int part, int nparts) {
     const int c0 = c_wg + blk * BC;
     const int hb0 = c0 / P - h_wg;  // first head of the block, workgroup-relative
     const int HBk = (c0 + BC - 1) / P - c0 / P + 1;
-    for (int i = tid; i < T * HBk; i += nthr) {
+    const int buf = blk % 3;
+    float* sa = s_a + buf * TMAX * geo.HB;
+    for (int i = tid + part * nthr; i < T * HBk; i += nparts * nthr) {
       const int v = i / HBk, hb = i % HBk;
-      float sum = 0.0f;
-      for (int w = v; w >= 0; w = s_parent[w]) sum += s_lg[w * HWG + hb0 + hb];
-      s_a[v * geo.HB + hb] = expf(sum);
-      if constexpr (!DENSE) s_dA[v * geo.HB + hb] = expf(s_lg[v * HWG + hb0 + hb]);
+      const float Sv = s_S[v * HWG + hb0 + hb];
+      sa[v * geo.HB + hb] = expf(Sv);
+      if constexpr (!DENSE) {
+        const int p = s_parent[v];
+        s_dA[buf * TMAX * geo.HB + v * geo.HB + hb] = expf(p >= 0 ? Sv - s_S[p * HWG + hb0 + hb] : Sv);
+      }
     }
     if constexpr (DENSE) {
-      for (int i = tid; i < HBk * T * T; i += nthr) {
+      float* sm = s_M + buf * geo.HB * TMAX * TMAX;
+      for (int i = tid + part * nthr; i < HBk * T * T; i += nparts * nthr) {
         const int hb = i / (T * T), v = (i / T) % T, u = i % T;
-        const int du = s_depth[u];
+        const int k1 = s_onk[v * TMAX + u];
         float val = 0.0f;
-        if (du <= s_depth[v] && s_path[v * TMAX + du - 1] == u) {
-          float sum = 0.0f;
-          for (int w = v; w != u; w = s_parent[w]) sum += s_lg[w * HWG + hb0 + hb];
-          val = expf(sum) * s_dt[u * HWG + hb0 + hb] * s_cb[v * TMAX + du - 1];
-          if (u == v) val += s_D[hb0 + hb];
+        if (k1) {
+          const int hw = hb0 + hb;
+          val = expf(s_S[v * HWG + hw] - s_S[u * HWG + hw]) * s_dt[u * HWG + hw] * s_cb[v * TMAX + k1 - 1];
+          if (u == v) val += s_D[hw];
         }
-        s_M[(hb * TMAX + v) * TMAX + u] = val;
+        sm[(hb * TMAX + v) * TMAX + u] = val;
       }
     }
   };
@@ -424,24 +457,13 @@ __global__ void __launch_bounds__(kThreads) verify_proj_kernel(VerifyArgs a, Ver
       const int c = c_row0 + j * kWave + lane;
       const int hb = c / P - c_blk / P;  // block-relative head
       const int hw = c / P - h_wg;       // workgroup-relative head
-      // raw x of every node and the window rows, 16 loads in flight at a time
-      for (int v0 = 0; v0 < T + W - 1; v0 += 16) {
-        float xr[16];
+      // raw x of every node and the window rows, prefetched at block start
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int v = (v0 + i < T + W - 1) ? v0 + i : T + W - 2;
-          xr[i] = v < T ? load_in(xin, (int64_t)v * DI + c) : load_in(win, (int64_t)(v - T) * DI + c);
-        }
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (v0 + i < T + W - 1) xs[(v0 + i) * kWave + lane] = xr[i];
-      }
-      // wj[jj] weighs conv input jj (0 = the node itself, jj = its jj-th ancestor)
-      float wj[4];
-      const float* cw = a.prm.conv_w + ((int64_t)l * DI + c) * W;
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) wj[jj] = (jj < W) ? cw[W - 1 - jj] : 0.0f;
-      const float cbias = a.prm.conv_b ? a.prm.conv_b[(int64_t)l * DI + c] : 0.0f;
+      for (int v = 0; v < TMAX + 3; ++v)
+        if (v < T + W - 1) xs[v * kWave + lane] = widen_bits<TIn>(xr[j][v]);
+      const float* wj = wt[j];  // prefetched: wj[jj] weighs conv input jj (0 = the node itself)
+      const float cbias = wt[j][4];
+      const float* sa = s_a + (blk % 3) * TMAX * geo.HB;
       float* yo = a.y + unit * T * DI + c;
       if constexpr (DENSE) {
         // conv outputs of every node in registers; the input rows are wave-uniform
@@ -464,10 +486,11 @@ __global__ void __launch_bounds__(kThreads) verify_proj_kernel(VerifyArgs a, Ver
         float* accs = xs;
 #pragma unroll
         for (int v = 0; v < TMAX; ++v) accs[v * kWave + lane] = acc[j][v];
-        const float* Mh = s_M + hb * TMAX * TMAX;
+        const float* Mh = s_M + ((blk % 3) * geo.HB + hb) * TMAX * TMAX;
+#pragma unroll 4
         for (int v = 0; v < T; ++v) {
           const f32x4* Mrow = reinterpret_cast<const f32x4*>(Mh + v * TMAX);
-          float yv = s_a[v * geo.HB + hb] * accs[v * kWave + lane];
+          float yv = sa[v * geo.HB + hb] * accs[v * kWave + lane];
 #pragma unroll
           for (int u4 = 0; u4 < TMAX / 4; ++u4) {
             const f32x4 m = Mrow[u4];
@@ -497,9 +520,10 @@ __global__ void __launch_bounds__(kThreads) verify_proj_kernel(VerifyArgs a, Ver
             float S = 0.0f;
             for (int k = 0; k < m; ++k) {
               const int u = s_path[v * TMAX + k];
-              S = fmaf(S, s_dA[u * geo.HB + hb], (s_dt[u * HWG + hw] * s_cb[v * TMAX + k]) * xs[u * kWave + lane]);
+              S = fmaf(S, s_dA[(blk % 3) * TMAX * geo.HB + u * geo.HB + hb],
+                       (s_dt[u * HWG + hw] * s_cb[v * TMAX + k]) * xs[u * kWave + lane]);
             }
-            yo[(int64_t)v * DI] = fmaf(s_a[v * geo.HB + hb], acc[j][v], S) + Dh * xs[v * kWave + lane];
+            yo[(int64_t)v * DI] = fmaf(sa[v * geo.HB + hb], acc[j][v], S) + Dh * xs[v * kWave + lane];
           }
         }
       }
@@ -515,29 +539,47 @@ __global__ void __launch_bounds__(kThreads) verify_proj_kernel(VerifyArgs a, Ver
                                  (uint32_t)(T * d.G * N * (int)sizeof(TIn)));
   const int c_goff = g * N * (int)sizeof(TIn);
   const int c_stride = d.G * N * (int)sizeof(TIn);
+  block_coeffs(0, 0, 1);
   for (int blk = 0; blk < NBLK; ++blk) {
-    __syncthreads();  // the previous block's epilogue no longer reads the coefficients
-    block_coeffs(blk);
 #pragma unroll
-    for (int j = 0; j < R; ++j)
+    for (int j = 0; j < R; ++j) {
+      const int c = c_wg + blk * BC + wave * R * kWave + j * kWave + lane;
+#pragma unroll
+      for (int v = 0; v < TMAX + 3; ++v) {
+        const int vv = v < T + W - 1 ? v : T + W - 2;  // clamped: every load is in bounds
+        const TIn* src = vv < T ? xin + (int64_t)vv * DI : win + (int64_t)(vv - T) * DI;
+        xr[j][v] = load_bits(src, c);
+      }
+      const float* cw = a.prm.conv_w + ((int64_t)l * DI + c) * W;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) wt[j][jj] = cw[jj < W ? W - 1 - jj : 0] * (jj < W ? 1.0f : 0.0f);
+      wt[j][4] = a.prm.conv_b ? a.prm.conv_b[(int64_t)l * DI + c] : 0.0f;
 #pragma unroll
       for (int v = 0; v < TMAX; ++v) acc[j][v] = 0.0f;
+    }
+    const bool more = blk + 1 < NBLK;
     if (two) {
       for (int ch = 0; ch < NCH; ch += 2) {
         const int s = blk * NCH + ch;
         stream_chunk<TIn, R, TMAX>(gA, chunk_src(min(s + 2, total - 1)), row_step, lds4, lane, c_rsrc,
                                    c_goff + ch * kChunk * (int)sizeof(TIn), c_stride, T, acc);
+        if (more) block_coeffs(blk + 1, ch, NCH);
         stream_chunk<TIn, R, TMAX>(gB, chunk_src(min(s + 3, total - 1)), row_step, lds4, lane, c_rsrc,
                                    c_goff + (ch + 1) * kChunk * (int)sizeof(TIn), c_stride, T, acc);
+        if (more) block_coeffs(blk + 1, ch + 1, NCH);
       }
     } else {
       for (int ch = 0; ch < NCH; ++ch) {
         const int s = blk * NCH + ch;
         stream_chunk<TIn, R, TMAX>(gA, chunk_src(min(s + 1, total - 1)), row_step, lds4, lane, c_rsrc,
                                    c_goff + ch * kChunk * (int)sizeof(TIn), c_stride, T, acc);
+        if (more) block_coeffs(blk + 1, ch, NCH);
       }
     }
-    __syncthreads();  // the block's coefficients are complete
+    // this block's coefficients (written during the previous block) are
+    // complete, and every wave is past the epilogue whose buffer the next
+    // block's coefficients reuse
+    __syncthreads();
     block_epilogue(blk);
   }
 }
@@ -549,7 +591,7 @@ __global__ void __launch_bounds__(kThreads) verify_proj_kernel(VerifyArgs a, Ver
 namespace {
 
 constexpr size_t kLdsCap = 160 * 1024;
-constexpr size_t kLdsDenseCap = 64 * 1024;
+constexpr size_t kLdsDenseCap = 80 * 1024;  // two workgroups per CU
 
 // heads that a range of `ch` channels starting at a multiple of `ch` can touch
 int heads_of_range(int ch, int P) { return (ch % P == 0) ? ch / P : (P % ch == 0 ? 1 : ch / P + 2); }
@@ -564,7 +606,7 @@ int launch_t(const VerifyArgs& a, const VerifyGeom& geo, size_t lds, hipStream_t
 
 template <int R, int TMAX, bool DENSE>
 size_t lds_bytes(VerifyGeom& geo) {
-  while (geo.NC > 16 && (size_t)VerifyLds<R, TMAX, DENSE>(geo).total > 56 * 1024) geo.NC /= 2;
+  while (geo.NC > 16 && (size_t)VerifyLds<R, TMAX, DENSE>(geo).total > 72 * 1024) geo.NC /= 2;
   return (size_t)VerifyLds<R, TMAX, DENSE>(geo).total;
 }
 
@@ -612,7 +654,11 @@ int launch_in(const VerifyArgs& a, hipStream_t s) {
 
 }  // namespace
 
+bool mfma_verify_applies(const Dims& d);
+int launch_verify_mfma(const VerifyArgs& a, bool bf16, hipStream_t s);
+
 int launch_verify(const VerifyArgs& a, bool bf16, hipStream_t s) {
+  if (mfma_verify_applies(a.d)) return launch_verify_mfma(a, bf16, s);
   return bf16 ? launch_in<bf16_t>(a, s) : launch_in<float>(a, s);
 }
 

@@ -1,0 +1,443 @@
+// verify_mfma.hip - ssm_tree_verify for trees of at most 16 nodes, on the
+// gfx950 matrix cores.
+//
+// Same arithmetic as the root projection in verify.hip (SpecMamba page
+// sec. 3.2 recurrence, unrolled along each root path):
+//   y_v[c] = a_v(h) (C_v . h0[c]) + sum_u M_h[v][u] x~_u[c],
+//   M_h[v][u] = exp(S_v - S_u) dt_u (C_v . B_u) for u on v's root path
+//               (u = v included), plus D_h when u = v;  a_v = exp(S_v),
+//   S_v = sum of dt * A over v's root path.
+// Both sums are dense contractions once the tree is padded to 16 nodes:
+//   Y1 = C (16 x N) . h0^T (N x channels)        -- the HBM-bound stream
+//   Y  = diag(a) Y1 + M_h (16 x 16) . X~ (16 x channels)
+// and both run on v_mfma_f32_16x16x4_f32 (fp32 in, fp32 accumulate).
+//
+// MFMA operand layout (16x16x4, one block): lane l holds A[l % 16][l / 16]
+// and B[l / 16][l % 16]; the 16x16 result D[i][j] sits in lane j + 16 (i / 4),
+// element i % 4.  The contraction index may be permuted freely as long as A
+// and B agree, so for state columns n = 16 gg + 4 k + t a lane (j + 16 k)
+// takes the four consecutive columns 16 gg + 4 k .. + 3 of channel j with one
+// 16-byte load and feeds them to four MFMAs (t = 0..3): the root state goes
+// from HBM to the matrix cores with no LDS transpose, and two loads of a wave
+// (gg and gg + 1) cover whole 128-byte lines.
+//
+// Work split.  A work item is one (layer, sequence, 64-channel slab); every
+// wave owns a contiguous range of items and runs on its own (no workgroup
+// barrier anywhere).  The root state of its range is one flat stream of
+// 1 KiB pieces (16 channels x 16 columns) kept RD pieces ahead in registers,
+// across tile, slab and sequence boundaries.  Per item the wave computes the
+// conv outputs of its 64 channels and S, dt of its heads; per (layer,
+// sequence) and B/C group it loads C into MFMA operand registers and forms
+// the 16 x 16 dots C_v . B_u with 32 more MFMAs.
+#include "common.h"
+
+namespace ssmt {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kTile = 16;            // node rows of an MFMA tile
+constexpr int kSlab = 64;            // channels per work item
+constexpr int kXRows = kTile + 3;    // conv input rows: nodes, then window rows
+
+// per-wave LDS region (byte offsets)
+struct WaveLds {
+  static constexpr int xs = 0;                         // [kXRows + 1][64] raw x; then conv outputs [64][16] (swizzled); C.B transpose
+  static constexpr int parent = xs + (kXRows + 1) * kSlab * 4;
+  static constexpr int anc = parent + 4 * kTile;       // bit u of anc[v]: u is on v's root path (v included)
+  static constexpr int cidx = anc + 4 * kTile;         // conv input rows 1..3 of node v, 8 bits each
+  static constexpr int S = cidx + 4 * kTile;           // [4 heads][16] cumulative dt * A
+  static constexpr int dt = S + 4 * 4 * kTile;         // [4 heads][16]
+  static constexpr int D = dt + 4 * 4 * kTile;         // [4 heads]
+  static constexpr int bytes = D + 16;
+};
+
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// four consecutive input elements widened to float
+template <typename TIn>
+__device__ __forceinline__ f32x4 load4(const TIn* p);
+template <>
+__device__ __forceinline__ f32x4 load4<float>(const float* p) {
+  return *reinterpret_cast<const f32x4*>(p);
+}
+template <>
+__device__ __forceinline__ f32x4 load4<bf16_t>(const bf16_t* p) {
+  const uint2 w = *reinterpret_cast<const uint2*>(p);
+  f32x4 r;
+  r.x = __uint_as_float(w.x << 16);
+  r.y = __uint_as_float(w.x & 0xFFFF0000u);
+  r.z = __uint_as_float(w.y << 16);
+  r.w = __uint_as_float(w.y & 0xFFFF0000u);
+  return r;
+}
+
+template <typename TIn>
+__device__ __forceinline__ uint32_t raw_bits(const TIn* p);
+template <>
+__device__ __forceinline__ uint32_t raw_bits<float>(const float* p) { return __float_as_uint(*p); }
+template <>
+__device__ __forceinline__ uint32_t raw_bits<bf16_t>(const bf16_t* p) { return p->bits; }
+template <typename TIn>
+__device__ __forceinline__ float from_bits(uint32_t b) { return sizeof(TIn) == 2 ? __uint_as_float(b << 16) : __uint_as_float(b); }
+
+// two consecutive input elements, raw
+template <typename TIn>
+struct Pair;
+template <>
+struct Pair<float> {
+  typedef uint2 type;
+  static __device__ __forceinline__ float get(const float* s, int i) { return s[i]; }
+};
+template <>
+struct Pair<bf16_t> {
+  typedef uint32_t type;
+  static __device__ __forceinline__ float get(const bf16_t* s, int i) { return __uint_as_float((uint32_t)s[i].bits << 16); }
+};
+
+// An opaque copy of a wave-uniform value: derived addresses are recomputed
+// where they are used instead of being hoisted (and spilled) out of the loop.
+__device__ __forceinline__ int opaque(int v) {
+  asm volatile("" : "+s"(v));
+  return v;
+}
+__device__ __forceinline__ int opaque_lane() {
+  int v = threadIdx.x;
+  asm volatile("" : "+v"(v));
+  return v & 63;
+}
+
+}  // namespace
+
+// NG = N / 16 column groups per state row; RD = pieces kept in flight.
+template <typename TIn, int NG, int RD>
+__global__ void __launch_bounds__(256) verify_mfma_kernel(VerifyArgs a, int items_per_wave) {
+  constexpr int N = 16 * NG;
+  static_assert(RD % NG == 0 || NG % RD == 0, "ring depth and column groups must nest");
+  const Dims d = a.d;
+  const int T = d.T, P = d.P, H = d.H, W = d.W, DI = d.d_in, G = d.G;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int NS = DI / kSlab;                        // slabs per (layer, sequence)
+  const int total = d.L * d.Bsz * NS;  // work items (the host keeps this below 2^31)
+  const int it0 = (blockIdx.x * (blockDim.x / kWave) + wave) * items_per_wave;
+  if (it0 >= total) return;
+  const int nit = min(items_per_wave, total - it0);
+  const int ntiles = nit * 4;
+  const int np = ntiles * NG;  // pieces of this wave's stream
+  const int j = lane & 15, k = lane >> 4;
+
+  extern __shared__ __align__(16) unsigned char smem[];
+  unsigned char* ws = smem + wave * WaveLds::bytes;
+  float* s_xs = reinterpret_cast<float*>(ws + WaveLds::xs);
+  int32_t* s_par = reinterpret_cast<int32_t*>(ws + WaveLds::parent);
+  int32_t* s_anc = reinterpret_cast<int32_t*>(ws + WaveLds::anc);
+  int32_t* s_cidx = reinterpret_cast<int32_t*>(ws + WaveLds::cidx);
+  float* s_S = reinterpret_cast<float*>(ws + WaveLds::S);
+  float* s_dt = reinterpret_cast<float*>(ws + WaveLds::dt);
+  float* s_D = reinterpret_cast<float*>(ws + WaveLds::D);
+
+  // ---- the state stream: piece p = (tile p / NG, columns 16 (p % NG) ..) ----
+  // tile t of the wave = channels 16 t .. 16 t + 15 counted from the range start
+  const float* sbase = a.state + ((int64_t)it0 * kSlab + j) * N + 4 * k;
+  auto piece = [&](int p) {
+    const unsigned q = p < np ? p : np - 1;  // past the end: the last piece again (branch-free)
+    return *reinterpret_cast<const f32x4*>(sbase + (int64_t)(q / NG) * (16 * N) + (q % NG) * 16);
+  };
+  f32x4 ring[RD];
+#pragma unroll
+  for (int i = 0; i < RD; ++i) ring[i] = piece(i);
+
+  // ---- per-item inputs, loaded one item ahead ----
+  const TIn* xg = reinterpret_cast<const TIn*>(a.x);
+  const TIn* wg = reinterpret_cast<const TIn*>(a.window);
+  const TIn* dtr = reinterpret_cast<const TIn*>(a.dt_raw);
+  const int HS = P >= kSlab ? 1 : kSlab / P;  // heads touched by a slab
+  // raw x rows (nodes, then window rows) of the slab: lanes 0..31 hold rows
+  // 2 m, lanes 32..63 rows 2 m + 1, two channels per lane
+  typename Pair<TIn>::type xr[(kXRows + 1) / 2];
+  float wt[5];                                // conv taps (0 = the node itself) and bias
+  uint32_t dtr_raw;                           // lane (head hl, node v): dt_raw
+  float p_bias, p_A, p_D;                     // lane (hl, v): that head's parameters
+  auto prefetch = [&](int it) {
+    it = it < nit ? it : nit - 1;
+    const int item = it0 + it;
+    const int unit = item / NS;
+    const int slab = item - unit * NS;
+    const int l = unit / d.Bsz;
+    const int ln = opaque_lane();
+    const int c = slab * kSlab + ln;
+    {
+      const int Tq = opaque(T), DIq = opaque(DI), last = Tq + opaque(W) - 2;
+      const TIn* xu = xg + (int64_t)unit * Tq * DIq + slab * kSlab + 2 * (ln & 31);
+      const TIn* wu = wg + ((int64_t)unit * (W - 1) - Tq) * DIq + slab * kSlab + 2 * (ln & 31);  // row r >= T at r * DI
+#pragma unroll
+      for (int m = 0; m < (kXRows + 1) / 2; ++m) {
+        int r = 2 * m + (ln >> 5);
+        r = r < last ? r : last;  // clamped: every load is in bounds
+        xr[m] = *reinterpret_cast<const typename Pair<TIn>::type*>((r < Tq ? xu : wu) + (int64_t)r * DIq);
+      }
+    }
+    const float* cw = a.prm.conv_w + ((int64_t)l * DI + c) * W;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) wt[jj] = cw[jj < W ? W - 1 - jj : 0] * (jj < W ? 1.0f : 0.0f);
+    wt[4] = a.prm.conv_b ? a.prm.conv_b[(int64_t)l * DI + c] : 0.0f;
+    const int hl = ln >> 4, v = ln & 15;
+    const int hh = min(slab * kSlab / P + (hl < HS ? hl : 0), H - 1);
+    dtr_raw = raw_bits<TIn>(dtr + ((int64_t)unit * T + (v < T ? v : T - 1)) * H + hh);
+    p_bias = a.prm.dt_bias[(int64_t)l * H + hh];
+    p_A = a.prm.A[(int64_t)l * H + hh];
+    p_D = a.prm.D[(int64_t)l * H + hh];
+  };
+  prefetch(0);
+
+  // ---- per (layer, sequence) and group state ----
+  int cur_unit = -1;
+  int cur_group = -1;
+  bool ok = false;
+  f32x4 cop[NG];  // lane (i + 16 k): C_i[16 gg + 4 k .. + 3], zero for i >= T
+  f32x4 cbop;     // lane (i + 16 k): C_i . B_(4 k + t), zero off i's root path
+  int ancm = 0;   // anc[i]
+#pragma unroll
+  for (int gg = 0; gg < NG; ++gg) cop[gg] = f32x4{0.f, 0.f, 0.f, 0.f};
+  cbop = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // start of item it: tree bookkeeping on a new (layer, sequence), C operands
+  // and C.B dots on a new group, conv outputs and S, dt of the slab's heads
+  auto item_start = [&](int it) {
+    const int lane = opaque_lane();  // recomputed here rather than kept live across the stream
+    const int j = lane & 15, k = lane >> 4;
+    const int item = it0 + it;
+    const int unit = item / NS;
+    const int slab = item - unit * NS;
+    const int l = unit / d.Bsz, b = unit - l * d.Bsz;
+    const int g = slab * kSlab / (DI / G);
+    const bool new_unit = unit != cur_unit;
+    if (new_unit) {
+      cur_unit = unit;
+      const int par = a.parent[(int64_t)b * T + (lane < T ? lane : T - 1)];
+      const int prev = __shfl_up(par, 1);
+      const bool bad = lane < T && (lane == 0 ? par != -1 : (par < -1 || par >= lane || par < prev));
+      ok = __ballot(bad) == 0;
+      if (ok) {
+        if (lane < T) s_par[lane] = par;
+        wave_sync();
+        if (lane < kTile) {
+          int m = 0, packed = 0;
+          if (lane < T) {
+            for (int u = lane; u >= 0; u = s_par[u]) m |= 1 << u;
+            for (int jj = 1; jj < W; ++jj) {
+              const int code = conv_input_code(s_par, lane, jj, W);
+              packed |= (code >= 0 ? code : T + (-1 - code)) << (8 * (jj - 1));
+            }
+          }
+          s_anc[lane] = m;  // zero for the padding rows
+          s_cidx[lane] = packed;
+        }
+        wave_sync();
+      }
+    }
+    if (slab == 0 && l == 0 && lane == 0 && a.seq_status) a.seq_status[b] = ok ? SSM_TREE_OK : SSM_TREE_E_TREE;
+    if (!ok) {
+      prefetch(it + 1);
+      return;
+    }
+    if (new_unit || g != cur_group) {
+      cur_group = g;
+      const int i = lane & 15;
+      const int ic = i < T ? i : T - 1;
+      const float keep = i < T ? 1.0f : 0.0f;
+      const TIn* cg = reinterpret_cast<const TIn*>(a.C) + (((int64_t)unit * T + ic) * G + g) * N + 4 * k;
+      const TIn* bg = reinterpret_cast<const TIn*>(a.B) + (((int64_t)unit * T + ic) * G + g) * N + 4 * k;
+      f32x4 bop[NG];
+#pragma unroll
+      for (int gg = 0; gg < NG; ++gg) {
+        cop[gg] = load4<TIn>(cg + 16 * gg) * keep;
+        bop[gg] = load4<TIn>(bg + 16 * gg) * keep;
+      }
+      // CB[v][u] = C_v . B_u: A = C rows, B = B rows (lane j + 16 k holds B_j)
+      f32x4 cb = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int gg = 0; gg < NG; ++gg) {
+        cb = mfma4(cop[gg].x, bop[gg].x, cb);
+        cb = mfma4(cop[gg].y, bop[gg].y, cb);
+        cb = mfma4(cop[gg].z, bop[gg].z, cb);
+        cb = mfma4(cop[gg].w, bop[gg].w, cb);
+      }
+      // result layout: lane (u + 16 q) holds CB[4 q + r][u]; transpose through LDS
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s_xs[(4 * k + r) * 16 + j] = cb[r];
+      wave_sync();
+      const f32x4 row = *reinterpret_cast<const f32x4*>(s_xs + i * 16 + 4 * k);
+      ancm = s_anc[i];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) cbop[t] = ((ancm >> (4 * k + t)) & 1) ? row[t] : 0.0f;
+      wave_sync();
+    }
+    // conv outputs of the slab's 64 channels (lane = channel), nodes in registers
+    TIn* s_xr = reinterpret_cast<TIn*>(s_xs);  // [kXRows + 1][64] raw
+#pragma unroll
+    for (int m = 0; m < (kXRows + 1) / 2; ++m)
+      *reinterpret_cast<typename Pair<TIn>::type*>(s_xr + (2 * m + (lane >> 5)) * kSlab + 2 * (lane & 31)) = xr[m];
+    wave_sync();
+    float xt[kTile];
+#pragma unroll
+    for (int v = 0; v < kTile; ++v) {
+      xt[v] = 0.0f;
+      if (v < T) {
+        const int ci = __builtin_amdgcn_readfirstlane(s_cidx[v]);
+        float z = fmaf(wt[0], Pair<TIn>::get(s_xr, v * kSlab + lane), wt[4]);
+#pragma unroll
+        for (int jj = 1; jj < 4; ++jj)
+          if (jj < W) z = fmaf(wt[jj], Pair<TIn>::get(s_xr, ((ci >> (8 * (jj - 1))) & 255) * kSlab + lane), z);
+        xt[v] = d.silu ? silu_f32(z) : z;
+      }
+    }
+    // S and dt of the slab's heads: lane (hl, v)
+    {
+      const int hl = lane >> 4, v = lane & 15;
+      const float dt = v < T ? softplus_f32(from_bits<TIn>(dtr_raw) + p_bias) : 0.0f;
+      wave_sync();
+      // conv outputs as the MFMA B operand: channel c's quad q at c * 16 + 4 (q ^ ((c >> 2) & 3))
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<f32x4*>(s_xs + lane * 16 + 4 * (q ^ ((lane >> 2) & 3))) =
+            f32x4{xt[4 * q], xt[4 * q + 1], xt[4 * q + 2], xt[4 * q + 3]};
+      if (hl < HS) s_S[hl * 16 + v] = dt * p_A;
+      wave_sync();
+      float S = 0.0f;
+      if (hl < HS && v < T) {
+        const int m = s_anc[v];
+        for (int u = 0; u <= v; ++u)
+          if ((m >> u) & 1) S += s_S[hl * 16 + u];
+      }
+      wave_sync();
+      if (hl < HS) {
+        s_S[hl * 16 + v] = S;
+        s_dt[hl * 16 + v] = dt;
+        if (v == 0) s_D[hl] = p_D;
+      }
+      wave_sync();
+    }
+    prefetch(it + 1);
+  };
+
+  // tile epilogue: y = diag(a) Y1 + M_h X~ for 16 channels
+  auto tile_end = [&](int tile, f32x4 acc) {
+    const int lane = opaque_lane();
+    const int j = lane & 15, k = lane >> 4;
+    const int it = tile >> 2, tl = tile & 3;
+    const int item = it0 + it;
+    const int unit = item / NS;
+    const int slab = item - unit * NS;
+    const int c0 = slab * kSlab + tl * 16;
+    float* yo = a.y + (int64_t)unit * T * DI + c0 + j;
+    if (!ok) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (4 * k + r < T) yo[(int64_t)(4 * k + r) * DI] = __builtin_nanf("");
+      return;
+    }
+    const int hl = c0 / P - slab * kSlab / P;
+    const int i = lane & 15;
+    const float Sv = s_S[hl * 16 + i];
+    const f32x4 Sq = *reinterpret_cast<const f32x4*>(s_S + hl * 16 + 4 * k);
+    const f32x4 dq = *reinterpret_cast<const f32x4*>(s_dt + hl * 16 + 4 * k);
+    const float Dh = s_D[hl];
+    f32x4 mop, y;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const float m = ((ancm >> (4 * k + t)) & 1) ? expf(Sv - Sq[t]) * dq[t] * cbop[t] : 0.0f;
+      mop[t] = (4 * k + t == i) ? m + Dh : m;
+      y[t] = expf(Sq[t]) * acc[t];  // lane (c + 16 k) holds nodes 4 k + t
+    }
+    const int cl = tl * 16 + j;
+    const f32x4 xq = *reinterpret_cast<const f32x4*>(s_xs + cl * 16 + 4 * (k ^ ((cl >> 2) & 3)));
+    y = mfma4(mop.x, xq.x, y);
+    y = mfma4(mop.y, xq.y, y);
+    y = mfma4(mop.z, xq.z, y);
+    y = mfma4(mop.w, xq.w, y);
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (4 * k + r < T) yo[(int64_t)(4 * k + r) * DI] = y[r];
+  };
+
+  // ---- main loop: RD pieces per pass, ring slots static ----
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int pb = 0; pb < np; pb += RD) {
+#pragma clang loop unroll(full)
+    for (int i = 0; i < RD; ++i) {
+      const int p = pb + i;
+      const int gg = i % NG;
+      const int tile = p / NG;
+      if (gg == 0) {
+        if ((tile & 3) == 0 && tile < ntiles) item_start(tile >> 2);
+        acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+      const f32x4 h = ring[i];
+      acc = mfma4(cop[gg].x, h.x, acc);
+      acc = mfma4(cop[gg].y, h.y, acc);
+      acc = mfma4(cop[gg].z, h.z, acc);
+      acc = mfma4(cop[gg].w, h.w, acc);
+      ring[i] = piece(p + RD);
+      if (gg == NG - 1 && tile < ntiles) tile_end(tile, acc);
+    }
+  }
+}
+
+namespace {
+
+template <typename TIn, int NG, int RD>
+int launch_mfma_t(const VerifyArgs& a, hipStream_t s) {
+  auto kern = verify_mfma_kernel<TIn, NG, RD>;
+  constexpr int kWaves = 4;
+  const size_t lds = (size_t)kWaves * WaveLds::bytes;
+  static int resident = 0;  // workgroups per CU, from the occupancy calculator
+  static int n_cu = 0;
+  if (!resident) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return SSM_TREE_E_HIP;
+    if (hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return SSM_TREE_E_HIP;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&resident, reinterpret_cast<const void*>(kern), kWaves * kWave,
+                                                     lds) != hipSuccess || resident < 1)
+      return SSM_TREE_E_HIP;
+  }
+  const int64_t items = (int64_t)a.d.L * a.d.Bsz * (a.d.d_in / kSlab);
+  if (items >= ((int64_t)1 << 30)) return SSM_TREE_E_DIMS;  // item indices are 32-bit in the kernel
+  const int64_t waves = (int64_t)resident * n_cu * kWaves;
+  const int64_t ipw = (items + waves - 1) / waves;
+  const int64_t wgs = ((items + ipw - 1) / ipw + kWaves - 1) / kWaves;
+  hipLaunchKernelGGL(kern, dim3((unsigned)wgs), dim3(kWaves * kWave), lds, s, a, (int)ipw);
+  return hipGetLastError() == hipSuccess ? SSM_TREE_OK : SSM_TREE_E_HIP;
+}
+
+template <typename TIn>
+int launch_mfma_in(const VerifyArgs& a, hipStream_t s) {
+  switch (a.d.N) {
+    case 16: return launch_mfma_t<TIn, 1, 16>(a, s);
+    case 32: return launch_mfma_t<TIn, 2, 16>(a, s);
+    case 64: return launch_mfma_t<TIn, 4, 16>(a, s);
+    case 128: return launch_mfma_t<TIn, 8, 16>(a, s);
+    case 256: return launch_mfma_t<TIn, 16, 16>(a, s);
+    default: return SSM_TREE_E_DIMS;
+  }
+}
+
+}  // namespace
+
+// Trees of at most 16 nodes with heads of a multiple of 16 channels.
+bool mfma_verify_applies(const Dims& d) { return d.T >= 1 && d.T <= kTile && d.P % 16 == 0 && d.d_in % kSlab == 0; }
+
+int launch_verify_mfma(const VerifyArgs& a, bool bf16, hipStream_t s) {
+  return bf16 ? launch_mfma_in<bf16_t>(a, s) : launch_mfma_in<float>(a, s);
+}
+
+}  // namespace ssmt
