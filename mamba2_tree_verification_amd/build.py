@@ -2,7 +2,9 @@
 
 Packed-FP32 VALU instructions are disabled for every device translation
 unit (``-target-feature -packed-fp32-ops``): the kernels are written with
-scalar float arithmetic only.
+scalar float arithmetic only.  Matrix-core results are allocated in
+ordinary VGPRs (``-amdgpu-mfma-vgpr-form``) rather than AccVGPRs, which
+keeps the streaming verify kernel at four waves per SIMD.
 """
 from __future__ import annotations
 
@@ -25,6 +27,7 @@ def hipcc() -> str:
 def command(out: str, extra=()) -> list:
     return [hipcc(), "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-shared",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-mllvm", "-amdgpu-mfma-vgpr-form",
             "-Wno-unused-command-line-argument", *extra, "-o", out,
             *[os.path.join(CSRC, s) for s in SOURCES]]
 

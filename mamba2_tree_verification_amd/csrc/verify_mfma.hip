@@ -41,15 +41,20 @@ constexpr int kSlab = 64;            // channels per work item
 constexpr int kXRows = kTile + 3;    // conv input rows: nodes, then window rows
 
 // per-wave LDS region (byte offsets)
+template <int E>  // input element size
 struct WaveLds {
-  static constexpr int xs = 0;                         // [kXRows + 1][64] raw x; then conv outputs [64][16] (swizzled); C.B transpose
-  static constexpr int parent = xs + (kXRows + 1) * kSlab * 4;
+  // two buffers (item parity): [kXRows + 1][64] raw x, then the item's conv
+  // outputs [64][16] (swizzled) in place
+  static constexpr int xs = 0;
+  static constexpr int xs_bytes = (kXRows + 1) * kSlab * E > kSlab * kTile * 4 ? (kXRows + 1) * kSlab * E : kSlab * kTile * 4;
+  static constexpr int parent = xs + 2 * xs_bytes;
   static constexpr int anc = parent + 4 * kTile;       // bit u of anc[v]: u is on v's root path (v included)
   static constexpr int cidx = anc + 4 * kTile;         // conv input rows 1..3 of node v, 8 bits each
-  static constexpr int S = cidx + 4 * kTile;           // [4 heads][16] cumulative dt * A
+  static constexpr int S = cidx + 4 * kTile;           // [4 heads][16] cumulative dt * A, times log2(e)
   static constexpr int dt = S + 4 * 4 * kTile;         // [4 heads][16]
   static constexpr int D = dt + 4 * 4 * kTile;         // [4 heads]
-  static constexpr int bytes = D + 16;
+  static constexpr int cb = D + 16;                    // [16][16] C.B transpose
+  static constexpr int bytes = cb + 4 * kTile * kTile;
 };
 
 __device__ __forceinline__ void wave_sync() {
@@ -117,44 +122,62 @@ __device__ __forceinline__ int opaque_lane() {
 
 }  // namespace
 
-// NG = N / 16 column groups per state row; RD = pieces kept in flight.
-template <typename TIn, int NG, int RD>
-__global__ void __launch_bounds__(256) verify_mfma_kernel(VerifyArgs a, int items_per_wave) {
+// NG = N / 16 column groups per state row; RD = pieces kept in flight; WPG
+// waves per workgroup (one workgroup per CU).  ILV (heads a multiple of 64
+// channels wide): tile tl of an item holds channels 4 j + tl, so that across
+// its four tiles a lane owns four adjacent channels and y leaves in 16-byte
+// stores of whole 256-byte row segments; otherwise tile tl holds channels
+// 16 tl + j (one head per tile) and y leaves per tile.
+template <typename TIn, int NG, int RD, int WPG, bool ILV>
+__global__ void __launch_bounds__(WPG * 64) verify_mfma_kernel(VerifyArgs a, int items_per_wg) {
   constexpr int N = 16 * NG;
-  static_assert(RD % NG == 0 || NG % RD == 0, "ring depth and column groups must nest");
+  typedef WaveLds<sizeof(TIn)> Lw;
+  static_assert(RD <= 4 * NG && (4 * NG) % RD == 0, "an item's pieces must fill whole ring cycles");
   const Dims d = a.d;
   const int T = d.T, P = d.P, H = d.H, W = d.W, DI = d.d_in, G = d.G;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int NS = DI / kSlab;                        // slabs per (layer, sequence)
   const int total = d.L * d.Bsz * NS;  // work items (the host keeps this below 2^31)
-  const int it0 = (blockIdx.x * (blockDim.x / kWave) + wave) * items_per_wave;
-  if (it0 >= total) return;
-  const int nit = min(items_per_wave, total - it0);
-  const int ntiles = nit * 4;
-  const int np = ntiles * NG;  // pieces of this wave's stream
+  const int wg_begin = blockIdx.x * items_per_wg;
+  const int wg_end = min(total, wg_begin + items_per_wg);
   const int j = lane & 15, k = lane >> 4;
 
   extern __shared__ __align__(16) unsigned char smem[];
-  unsigned char* ws = smem + wave * WaveLds::bytes;
-  float* s_xs = reinterpret_cast<float*>(ws + WaveLds::xs);
-  int32_t* s_par = reinterpret_cast<int32_t*>(ws + WaveLds::parent);
-  int32_t* s_anc = reinterpret_cast<int32_t*>(ws + WaveLds::anc);
-  int32_t* s_cidx = reinterpret_cast<int32_t*>(ws + WaveLds::cidx);
-  float* s_S = reinterpret_cast<float*>(ws + WaveLds::S);
-  float* s_dt = reinterpret_cast<float*>(ws + WaveLds::dt);
-  float* s_D = reinterpret_cast<float*>(ws + WaveLds::D);
+  // The workgroup's items are handed out one at a time from an LDS counter:
+  // the hardware issues the oldest waves first, so equal static shares would
+  // leave the youngest waves finishing long after the others.
+  int* s_next = reinterpret_cast<int*>(smem + WPG * Lw::bytes);
+  if (threadIdx.x == 0) *s_next = wg_begin;
+  __syncthreads();
+  auto grab = [&]() {
+    int v = 0;
+    if (lane == 0) v = atomicAdd(s_next, 1);
+    return __builtin_amdgcn_readlane(v, 0);
+  };
+  unsigned char* ws = smem + wave * Lw::bytes;
+  auto xs_buf = [&](int it) { return reinterpret_cast<float*>(ws + Lw::xs + (it & 1) * Lw::xs_bytes); };
+  int32_t* s_par = reinterpret_cast<int32_t*>(ws + Lw::parent);
+  int32_t* s_anc = reinterpret_cast<int32_t*>(ws + Lw::anc);
+  int32_t* s_cidx = reinterpret_cast<int32_t*>(ws + Lw::cidx);
+  float* s_S = reinterpret_cast<float*>(ws + Lw::S);
+  float* s_dt = reinterpret_cast<float*>(ws + Lw::dt);
+  float* s_D = reinterpret_cast<float*>(ws + Lw::D);
+  float* s_cbt = reinterpret_cast<float*>(ws + Lw::cb);
 
-  // ---- the state stream: piece p = (tile p / NG, columns 16 (p % NG) ..) ----
-  // tile t of the wave = channels 16 t .. 16 t + 15 counted from the range start
-  const float* sbase = a.state + ((int64_t)it0 * kSlab + j) * N + 4 * k;
-  auto piece = [&](int p) {
-    const unsigned q = p < np ? p : np - 1;  // past the end: the last piece again (branch-free)
-    return *reinterpret_cast<const f32x4*>(sbase + (int64_t)(q / NG) * (16 * N) + (q % NG) * 16);
+  int cur = grab();
+  if (cur >= wg_end) return;
+  int nxt = grab();
+
+  // ---- the state stream: piece i of an item = (tile i / NG, columns 16 (i % NG) ..) ----
+  const float* sbase = a.state + (int64_t)(ILV ? 4 * j : j) * N + 4 * k;
+  auto piece = [&](int item, int i) {
+    return *reinterpret_cast<const f32x4*>(sbase + ((int64_t)item * kSlab + (i / NG) * (ILV ? 1 : 16)) * N +
+                                           (i % NG) * 16);
   };
   f32x4 ring[RD];
 #pragma unroll
-  for (int i = 0; i < RD; ++i) ring[i] = piece(i);
+  for (int i = 0; i < RD; ++i) ring[i] = piece(cur, i);
 
   // ---- per-item inputs, loaded one item ahead ----
   const TIn* xg = reinterpret_cast<const TIn*>(a.x);
@@ -164,12 +187,12 @@ __global__ void __launch_bounds__(256) verify_mfma_kernel(VerifyArgs a, int item
   // raw x rows (nodes, then window rows) of the slab: lanes 0..31 hold rows
   // 2 m, lanes 32..63 rows 2 m + 1, two channels per lane
   typename Pair<TIn>::type xr[(kXRows + 1) / 2];
-  float wt[5];                                // conv taps (0 = the node itself) and bias
+  // conv taps (0 = the node itself; taps >= W unused) and bias, raw: any
+  // arithmetic on a prefetched value here would wait for the load at once
+  float wt[5];
   uint32_t dtr_raw;                           // lane (head hl, node v): dt_raw
   float p_bias, p_A, p_D;                     // lane (hl, v): that head's parameters
-  auto prefetch = [&](int it) {
-    it = it < nit ? it : nit - 1;
-    const int item = it0 + it;
+  auto prefetch = [&](int item) {
     const int unit = item / NS;
     const int slab = item - unit * NS;
     const int l = unit / d.Bsz;
@@ -188,8 +211,8 @@ __global__ void __launch_bounds__(256) verify_mfma_kernel(VerifyArgs a, int item
     }
     const float* cw = a.prm.conv_w + ((int64_t)l * DI + c) * W;
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) wt[jj] = cw[jj < W ? W - 1 - jj : 0] * (jj < W ? 1.0f : 0.0f);
-    wt[4] = a.prm.conv_b ? a.prm.conv_b[(int64_t)l * DI + c] : 0.0f;
+    for (int jj = 0; jj < 4; ++jj) wt[jj] = cw[jj < W ? W - 1 - jj : 0];
+    wt[4] = *(a.prm.conv_b ? a.prm.conv_b + (int64_t)l * DI + c : cw);  // no bias: replaced by 0 at use
     const int hl = ln >> 4, v = ln & 15;
     const int hh = min(slab * kSlab / P + (hl < HS ? hl : 0), H - 1);
     dtr_raw = raw_bits<TIn>(dtr + ((int64_t)unit * T + (v < T ? v : T - 1)) * H + hh);
@@ -197,7 +220,22 @@ __global__ void __launch_bounds__(256) verify_mfma_kernel(VerifyArgs a, int item
     p_A = a.prm.A[(int64_t)l * H + hh];
     p_D = a.prm.D[(int64_t)l * H + hh];
   };
-  prefetch(0);
+  // Take delivery of item it's prefetched inputs: raw x into its LDS buffer,
+  // the rest marked as arrived.  Placed in straight-line code a fixed number
+  // of memory operations after the prefetch, so that the compiler's wait is
+  // exact (a wait after a branch join degrades to draining the stream).
+  auto deliver = [&](int par) {
+    const int ln = opaque_lane();
+    TIn* s_xr = reinterpret_cast<TIn*>(xs_buf(par));
+#pragma unroll
+    for (int m = 0; m < (kXRows + 1) / 2; ++m)
+      *reinterpret_cast<typename Pair<TIn>::type*>(s_xr + (2 * m + (ln >> 5)) * kSlab + 2 * (ln & 31)) = xr[m];
+#pragma unroll
+    for (int q = 0; q < 5; ++q) asm volatile("" : "+v"(wt[q]));
+    asm volatile("" : "+v"(dtr_raw), "+v"(p_bias), "+v"(p_A), "+v"(p_D));
+  };
+  prefetch(cur);
+  deliver(0);
 
   // ---- per (layer, sequence) and group state ----
   int cur_unit = -1;
@@ -212,14 +250,15 @@ __global__ void __launch_bounds__(256) verify_mfma_kernel(VerifyArgs a, int item
 
   // start of item it: tree bookkeeping on a new (layer, sequence), C operands
   // and C.B dots on a new group, conv outputs and S, dt of the slab's heads
-  auto item_start = [&](int it) {
+  auto item_start = [&](int item, int par) {
     const int lane = opaque_lane();  // recomputed here rather than kept live across the stream
     const int j = lane & 15, k = lane >> 4;
-    const int item = it0 + it;
     const int unit = item / NS;
     const int slab = item - unit * NS;
     const int l = unit / d.Bsz, b = unit - l * d.Bsz;
     const int g = slab * kSlab / (DI / G);
+    float* s_xs = xs_buf(par);
+    const TIn* s_xr = reinterpret_cast<const TIn*>(s_xs);  // [kXRows + 1][64] raw, delivered
     const bool new_unit = unit != cur_unit;
     if (new_unit) {
       cur_unit = unit;
@@ -246,10 +285,7 @@ __global__ void __launch_bounds__(256) verify_mfma_kernel(VerifyArgs a, int item
       }
     }
     if (slab == 0 && l == 0 && lane == 0 && a.seq_status) a.seq_status[b] = ok ? SSM_TREE_OK : SSM_TREE_E_TREE;
-    if (!ok) {
-      prefetch(it + 1);
-      return;
-    }
+    if (!ok) return;
     if (new_unit || g != cur_group) {
       cur_group = g;
       const int i = lane & 15;
@@ -274,31 +310,31 @@ __global__ void __launch_bounds__(256) verify_mfma_kernel(VerifyArgs a, int item
       }
       // result layout: lane (u + 16 q) holds CB[4 q + r][u]; transpose through LDS
 #pragma unroll
-      for (int r = 0; r < 4; ++r) s_xs[(4 * k + r) * 16 + j] = cb[r];
+      for (int r = 0; r < 4; ++r) s_cbt[(4 * k + r) * 16 + j] = cb[r];
       wave_sync();
-      const f32x4 row = *reinterpret_cast<const f32x4*>(s_xs + i * 16 + 4 * k);
+      const f32x4 row = *reinterpret_cast<const f32x4*>(s_cbt + i * 16 + 4 * k);
       ancm = s_anc[i];
 #pragma unroll
       for (int t = 0; t < 4; ++t) cbop[t] = ((ancm >> (4 * k + t)) & 1) ? row[t] : 0.0f;
       wave_sync();
     }
     // conv outputs of the slab's 64 channels (lane = channel), nodes in registers
-    TIn* s_xr = reinterpret_cast<TIn*>(s_xs);  // [kXRows + 1][64] raw
-#pragma unroll
-    for (int m = 0; m < (kXRows + 1) / 2; ++m)
-      *reinterpret_cast<typename Pair<TIn>::type*>(s_xr + (2 * m + (lane >> 5)) * kSlab + 2 * (lane & 31)) = xr[m];
     wave_sync();
+    int4 cq[4];  // every node's conv input rows, read at once
+#pragma unroll
+    for (int q = 0; q < 4; ++q) cq[q] = *reinterpret_cast<const int4*>(s_cidx + 4 * q);
     float xt[kTile];
 #pragma unroll
     for (int v = 0; v < kTile; ++v) {
       xt[v] = 0.0f;
       if (v < T) {
-        const int ci = __builtin_amdgcn_readfirstlane(s_cidx[v]);
-        float z = fmaf(wt[0], Pair<TIn>::get(s_xr, v * kSlab + lane), wt[4]);
+        const int ci = __builtin_amdgcn_readfirstlane(v % 4 == 0 ? cq[v / 4].x : v % 4 == 1 ? cq[v / 4].y
+                                                                  : v % 4 == 2 ? cq[v / 4].z : cq[v / 4].w);
+        float z = fmaf(wt[0], Pair<TIn>::get(s_xr, v * kSlab + lane), a.prm.conv_b ? wt[4] : 0.0f);
 #pragma unroll
         for (int jj = 1; jj < 4; ++jj)
           if (jj < W) z = fmaf(wt[jj], Pair<TIn>::get(s_xr, ((ci >> (8 * (jj - 1))) & 255) * kSlab + lane), z);
-        xt[v] = d.silu ? silu_f32(z) : z;
+        xt[v] = d.silu ? z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)) : z;
       }
     }
     // S and dt of the slab's heads: lane (hl, v)
@@ -306,47 +342,45 @@ __global__ void __launch_bounds__(256) verify_mfma_kernel(VerifyArgs a, int item
       const int hl = lane >> 4, v = lane & 15;
       const float dt = v < T ? softplus_f32(from_bits<TIn>(dtr_raw) + p_bias) : 0.0f;
       wave_sync();
-      // conv outputs as the MFMA B operand: channel c's quad q at c * 16 + 4 (q ^ ((c >> 2) & 3))
+      // conv outputs as the MFMA B operand: the channel in column j of tile tl
+      // sits in row p = 16 tl + j, its quad q at p * 16 + 4 (q ^ ((p >> 2) & 3))
+      const int p = ILV ? (lane & 3) * 16 + (lane >> 2) : lane;
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        *reinterpret_cast<f32x4*>(s_xs + lane * 16 + 4 * (q ^ ((lane >> 2) & 3))) =
+        *reinterpret_cast<f32x4*>(s_xs + p * 16 + 4 * (q ^ ((p >> 2) & 3))) =
             f32x4{xt[4 * q], xt[4 * q + 1], xt[4 * q + 2], xt[4 * q + 3]};
       if (hl < HS) s_S[hl * 16 + v] = dt * p_A;
       wave_sync();
+      // S_v = sum of dt * A over v's root path, root first (zero terms skipped
+      // in effect: adding +0 leaves the sum unchanged)
+      const int hr = hl < HS ? hl : 0;
+      f32x4 dq[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) dq[q] = *reinterpret_cast<const f32x4*>(s_S + hr * 16 + 4 * q);
+      const int m = v < T ? s_anc[v] : 0;
       float S = 0.0f;
-      if (hl < HS && v < T) {
-        const int m = s_anc[v];
-        for (int u = 0; u <= v; ++u)
-          if ((m >> u) & 1) S += s_S[hl * 16 + u];
-      }
+#pragma unroll
+      for (int u = 0; u < kTile; ++u) S += ((m >> u) & 1) ? dq[u / 4][u % 4] : 0.0f;
       wave_sync();
       if (hl < HS) {
-        s_S[hl * 16 + v] = S;
+        // stored in base-2 units: exp(S_v - S_u) = exp2(S2_v - S2_u)
+        s_S[hl * 16 + v] = S * 1.4426950408889634f;
         s_dt[hl * 16 + v] = dt;
         if (v == 0) s_D[hl] = p_D;
       }
       wave_sync();
     }
-    prefetch(it + 1);
   };
 
-  // tile epilogue: y = diag(a) Y1 + M_h X~ for 16 channels
-  auto tile_end = [&](int tile, f32x4 acc) {
+  // tile epilogue: y = diag(a) Y1 + M_h X~ for 16 channels; lane (c + 16 k)
+  // returns nodes 4 k .. 4 k + 3 of its channel (NaN for an invalid tree)
+  auto tile_end = [&](int item, int par, int tl, f32x4 acc) {
     const int lane = opaque_lane();
     const int j = lane & 15, k = lane >> 4;
-    const int it = tile >> 2, tl = tile & 3;
-    const int item = it0 + it;
     const int unit = item / NS;
     const int slab = item - unit * NS;
-    const int c0 = slab * kSlab + tl * 16;
-    float* yo = a.y + (int64_t)unit * T * DI + c0 + j;
-    if (!ok) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (4 * k + r < T) yo[(int64_t)(4 * k + r) * DI] = __builtin_nanf("");
-      return;
-    }
-    const int hl = c0 / P - slab * kSlab / P;
+    const float* s_xs = xs_buf(par);
+    const int hl = ILV ? 0 : (slab * kSlab + tl * 16) / P - slab * kSlab / P;
     const int i = lane & 15;
     const float Sv = s_S[hl * 16 + i];
     const f32x4 Sq = *reinterpret_cast<const f32x4*>(s_S + hl * 16 + 4 * k);
@@ -355,9 +389,9 @@ __global__ void __launch_bounds__(256) verify_mfma_kernel(VerifyArgs a, int item
     f32x4 mop, y;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const float m = ((ancm >> (4 * k + t)) & 1) ? expf(Sv - Sq[t]) * dq[t] * cbop[t] : 0.0f;
+      const float m = ((ancm >> (4 * k + t)) & 1) ? __builtin_amdgcn_exp2f(Sv - Sq[t]) * dq[t] * cbop[t] : 0.0f;
       mop[t] = (4 * k + t == i) ? m + Dh : m;
-      y[t] = expf(Sq[t]) * acc[t];  // lane (c + 16 k) holds nodes 4 k + t
+      y[t] = __builtin_amdgcn_exp2f(Sq[t]) * acc[t];  // lane (c + 16 k) holds nodes 4 k + t
     }
     const int cl = tl * 16 + j;
     const f32x4 xq = *reinterpret_cast<const f32x4*>(s_xs + cl * 16 + 4 * (k ^ ((cl >> 2) & 3)));
@@ -365,70 +399,107 @@ __global__ void __launch_bounds__(256) verify_mfma_kernel(VerifyArgs a, int item
     y = mfma4(mop.y, xq.y, y);
     y = mfma4(mop.z, xq.z, y);
     y = mfma4(mop.w, xq.w, y);
+    // selected, not branched: the body stays straight-line
+#pragma unroll
+    for (int r = 0; r < 4; ++r) y[r] = ok ? y[r] : __builtin_nanf("");
+    return y;
+  };
+  // y of one tile (channels 16 tl + j)
+  auto store_tile = [&](int item, int tl, f32x4 y) {
+    const int lane = opaque_lane();
+    const int j = lane & 15, k = lane >> 4;
+    const int unit = item / NS;
+    float* yo = a.y + (int64_t)unit * T * DI + (item - unit * NS) * kSlab + tl * 16 + j;
 #pragma unroll
     for (int r = 0; r < 4; ++r)
       if (4 * k + r < T) yo[(int64_t)(4 * k + r) * DI] = y[r];
   };
+  // y of an interleaved item: lane (j + 16 k) holds channels 4 j .. 4 j + 3 of nodes 4 k + r
+  auto store_item = [&](int item, const f32x4 (&ys)[4]) {
+    const int lane = opaque_lane();
+    const int j = lane & 15, k = lane >> 4;
+    const int unit = item / NS;
+    float* yo = a.y + (int64_t)unit * T * DI + (item - unit * NS) * kSlab + 4 * j;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (4 * k + r < T)
+        *reinterpret_cast<f32x4*>(yo + (int64_t)(4 * k + r) * DI) = f32x4{ys[0][r], ys[1][r], ys[2][r], ys[3][r]};
+  };
 
-  // ---- main loop: RD pieces per pass, ring slots static ----
-  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int pb = 0; pb < np; pb += RD) {
-#pragma clang loop unroll(full)
-    for (int i = 0; i < RD; ++i) {
-      const int p = pb + i;
-      const int gg = i % NG;
-      const int tile = p / NG;
-      if (gg == 0) {
-        if ((tile & 3) == 0 && tile < ntiles) item_start(tile >> 2);
-        acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  // ---- main loop: one work item (4 tiles of NG pieces) per iteration ----
+  // After item_start the body is straight-line: the next item's inputs are
+  // requested, then delivered two tiles later; the ring runs on into the
+  // next item (the current one again when there is none).
+  for (int par = 0;; par ^= 1) {
+    const int after = grab();  // the item after next, known well before it is needed
+    item_start(cur, par);
+    const int nx = nxt < wg_end ? nxt : cur;
+    prefetch(nx);
+    f32x4 ys[4];
+#pragma unroll
+    for (int tl = 0; tl < 4; ++tl) {
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int gg = 0; gg < NG; ++gg) {
+        const int i = tl * NG + gg;  // static
+        const f32x4 h = ring[i % RD];
+        acc = mfma4(cop[gg].x, h.x, acc);
+        acc = mfma4(cop[gg].y, h.y, acc);
+        acc = mfma4(cop[gg].z, h.z, acc);
+        acc = mfma4(cop[gg].w, h.w, acc);
+        ring[i % RD] = i + RD < 4 * NG ? piece(cur, i + RD) : piece(nx, i + RD - 4 * NG);
       }
-      const f32x4 h = ring[i];
-      acc = mfma4(cop[gg].x, h.x, acc);
-      acc = mfma4(cop[gg].y, h.y, acc);
-      acc = mfma4(cop[gg].z, h.z, acc);
-      acc = mfma4(cop[gg].w, h.w, acc);
-      ring[i] = piece(p + RD);
-      if (gg == NG - 1 && tile < ntiles) tile_end(tile, acc);
+      ys[tl] = tile_end(cur, par, tl, acc);
+      if (!ILV) store_tile(cur, tl, ys[tl]);
+      if (tl == 1) deliver(par ^ 1);
     }
+    if (ILV) store_item(cur, ys);
+    if (nxt >= wg_end) break;
+    cur = nxt;
+    nxt = after;
   }
 }
 
 namespace {
 
-template <typename TIn, int NG, int RD>
+template <typename TIn, int NG, int RD, bool ILV>
 int launch_mfma_t(const VerifyArgs& a, hipStream_t s) {
-  auto kern = verify_mfma_kernel<TIn, NG, RD>;
-  constexpr int kWaves = 4;
-  const size_t lds = (size_t)kWaves * WaveLds::bytes;
-  static int resident = 0;  // workgroups per CU, from the occupancy calculator
-  static int n_cu = 0;
-  if (!resident) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return SSM_TREE_E_HIP;
-    if (hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return SSM_TREE_E_HIP;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&resident, reinterpret_cast<const void*>(kern), kWaves * kWave,
-                                                     lds) != hipSuccess || resident < 1)
-      return SSM_TREE_E_HIP;
-  }
+  // sixteen waves per CU where registers and LDS allow, else twelve
+  constexpr int kWpg = (sizeof(TIn) == 2 && NG <= 8) ? 16 : 12;
+  auto kern = verify_mfma_kernel<TIn, NG, RD, kWpg, ILV>;
+  const size_t lds = (size_t)kWpg * WaveLds<sizeof(TIn)>::bytes + 16;
+  if (allow_lds(kern, lds) != hipSuccess) return SSM_TREE_E_HIP;
+  int dev = 0, n_cu = 0, resident = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&resident, reinterpret_cast<const void*>(kern), kWpg * kWave, lds) !=
+          hipSuccess ||
+      resident < 1)
+    return SSM_TREE_E_HIP;
   const int64_t items = (int64_t)a.d.L * a.d.Bsz * (a.d.d_in / kSlab);
   if (items >= ((int64_t)1 << 30)) return SSM_TREE_E_DIMS;  // item indices are 32-bit in the kernel
-  const int64_t waves = (int64_t)resident * n_cu * kWaves;
-  const int64_t ipw = (items + waves - 1) / waves;
-  const int64_t wgs = ((items + ipw - 1) / ipw + kWaves - 1) / kWaves;
-  hipLaunchKernelGGL(kern, dim3((unsigned)wgs), dim3(kWaves * kWave), lds, s, a, (int)ipw);
+  const int64_t groups = (int64_t)resident * n_cu;
+  const int64_t ipg = (items + groups - 1) / groups;
+  const int64_t wgs = (items + ipg - 1) / ipg;
+  hipLaunchKernelGGL(kern, dim3((unsigned)wgs), dim3(kWpg * kWave), lds, s, a, (int)ipg);
   return hipGetLastError() == hipSuccess ? SSM_TREE_OK : SSM_TREE_E_HIP;
+}
+
+template <typename TIn, bool ILV>
+int launch_mfma_n(const VerifyArgs& a, hipStream_t s) {
+  switch (a.d.N) {
+    case 16: return launch_mfma_t<TIn, 1, 4, ILV>(a, s);
+    case 32: return launch_mfma_t<TIn, 2, 8, ILV>(a, s);
+    case 64: return launch_mfma_t<TIn, 4, 8, ILV>(a, s);
+    case 128: return launch_mfma_t<TIn, 8, 8, ILV>(a, s);
+    case 256: return launch_mfma_t<TIn, 16, 4, ILV>(a, s);
+    default: return SSM_TREE_E_DIMS;
+  }
 }
 
 template <typename TIn>
 int launch_mfma_in(const VerifyArgs& a, hipStream_t s) {
-  switch (a.d.N) {
-    case 16: return launch_mfma_t<TIn, 1, 16>(a, s);
-    case 32: return launch_mfma_t<TIn, 2, 16>(a, s);
-    case 64: return launch_mfma_t<TIn, 4, 16>(a, s);
-    case 128: return launch_mfma_t<TIn, 8, 16>(a, s);
-    case 256: return launch_mfma_t<TIn, 16, 16>(a, s);
-    default: return SSM_TREE_E_DIMS;
-  }
+  return a.d.P % kSlab == 0 ? launch_mfma_n<TIn, true>(a, s) : launch_mfma_n<TIn, false>(a, s);
 }
 
 }  // namespace
