@@ -270,6 +270,19 @@ def main(argv=None):
         print("bench: NaN in y", file=sys.stderr)
         return 1
 
+    # the page's own form (explicit FIFO walk, every child state materialised),
+    # timed apart for comparison; not part of the step
+    dims_fifo = m.make_dims(cfg.L, cfg.Bsz, cfg.T, cfg.H, cfg.P, cfg.N, cfg.G, cfg.W, cfg.bf16, cfg.silu, fifo=True)
+    fifo_ms = []
+    for k in range(4):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        m.verify(dims_fifo, prm, g.parent, g.x, g.B, g.C, g.dt_raw, window, state, y, st_v)
+        e1.record()
+        torch.cuda.synchronize()
+        if k:
+            fifo_ms.append(e0.elapsed_time(e1))
+
     vb, cb, pb = algorithmic_bytes(cfg, inp.path_len)
     v_avg = sum(ver_ms) / len(ver_ms)
     c_avg = sum(com_ms) / len(com_ms)
@@ -285,7 +298,9 @@ def main(argv=None):
                            node_layers_per_s=round(node_layers / (v_avg * 1e-3), 1),
                            roofline=roof("verify", vb, v_avg)),
             "commit": dict(ms=round(c_avg, 4), ms_min=round(min(com_ms), 4), bytes=cb,
-                           roofline=roof("commit", cb, c_avg))}
+                           roofline=roof("commit", cb, c_avg)),
+            "verify_fifo_walk": dict(ms=round(sum(fifo_ms) / len(fifo_ms), 4), bytes=vb,
+                                     note="SSM_TREE_VERIFY_FIFO, not in the step")}
     dominant = "verify" if v_avg >= c_avg else "commit"
     rec = {
         "metric": METRIC,

@@ -62,6 +62,11 @@ extern "C" {
 
 /* dims.flags */
 #define SSM_TREE_CONV_SILU 1 /* SiLU after the conv (Mamba2 checkpoints use it; the pages name no activation) */
+/* ssm_tree_verify computes every child state explicitly, walking the tree
+ * breadth-first with a FIFO of live states (SpecMamba page sec. 3.2), instead
+ * of the default root projection.  Same outputs up to fp32 rounding; slower.
+ * Ignored by ssm_tree_commit. */
+#define SSM_TREE_VERIFY_FIFO 2
 
 /* return / status codes */
 #define SSM_TREE_OK 0
@@ -88,7 +93,7 @@ typedef struct ssm_tree_dims {
   int32_t ngroups;    /* G : B and C are shared by H/G consecutive heads */
   int32_t conv_width; /* W */
   int32_t in_dtype;   /* SSM_TREE_F32 or SSM_TREE_BF16 */
-  int32_t flags;      /* 0 or SSM_TREE_CONV_SILU */
+  int32_t flags;      /* 0 or SSM_TREE_CONV_SILU | SSM_TREE_VERIFY_FIFO */
 } ssm_tree_dims;
 
 /* Per-layer parameters, float32 device pointers. */

@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(HERE, "libssm_tree.so")
 SSM_TREE_ABI_VERSION = 1
 SSM_TREE_F32, SSM_TREE_BF16 = 0, 1
 SSM_TREE_CONV_SILU = 1
+SSM_TREE_VERIFY_FIFO = 2
 OK, E_NULL, E_ALIGN, E_DIMS, E_DTYPE, E_ALIAS, E_HIP, E_FLAGS = 0, -1, -2, -3, -4, -5, -6, -7
 E_TREE, E_PATH = -10, -11
 PLAN_HEADER, PLAN_STRIDE, PLAN_UNUSED = 4, 8, -32768
@@ -119,9 +120,9 @@ def _stream(stream):
     return s.cuda_stream
 
 
-def make_dims(L, Bsz, T, H, P, N, G, W, bf16: bool, silu: bool = False) -> Dims:
+def make_dims(L, Bsz, T, H, P, N, G, W, bf16: bool, silu: bool = False, fifo: bool = False) -> Dims:
     return Dims(L, Bsz, T, H, P, N, G, W, SSM_TREE_BF16 if bf16 else SSM_TREE_F32,
-                SSM_TREE_CONV_SILU if silu else 0)
+                (SSM_TREE_CONV_SILU if silu else 0) | (SSM_TREE_VERIFY_FIFO if fifo else 0))
 
 
 def make_params(A, D, dt_bias, conv_w, conv_b=None) -> Params:

@@ -33,7 +33,7 @@ int check_dims(const ssm_tree_dims* dm, Dims* out) {
   if (!dm) return SSM_TREE_E_NULL;
   const ssm_tree_dims& d = *dm;
   if (d.in_dtype != SSM_TREE_F32 && d.in_dtype != SSM_TREE_BF16) return SSM_TREE_E_DTYPE;
-  if (d.flags & ~SSM_TREE_CONV_SILU) return SSM_TREE_E_FLAGS;
+  if (d.flags & ~(SSM_TREE_CONV_SILU | SSM_TREE_VERIFY_FIFO)) return SSM_TREE_E_FLAGS;
   if (d.n_layers < 0 || d.batch < 0 || d.n_nodes < 0 || d.n_nodes > kMaxNodes) return SSM_TREE_E_DIMS;
   if (d.nheads < 1 || d.headdim < 1 || d.ngroups < 1 || d.nheads % d.ngroups) return SSM_TREE_E_DIMS;
   if (d.conv_width < 1 || d.conv_width > 4) return SSM_TREE_E_DIMS;
@@ -44,7 +44,7 @@ int check_dims(const ssm_tree_dims* dm, Dims* out) {
   const int64_t units = (int64_t)d.n_layers * d.batch;
   if (d.batch > 65535 || d.n_layers > 65535 || units * di * d.d_state > ((int64_t)1 << 40)) return SSM_TREE_E_DIMS;
   *out = Dims{d.n_layers, d.batch, d.n_nodes, d.nheads, d.headdim, d.d_state, d.ngroups, d.conv_width,
-              (d.flags & SSM_TREE_CONV_SILU) ? 1 : 0, (int32_t)di};
+              (d.flags & SSM_TREE_CONV_SILU) ? 1 : 0, (int32_t)di, (d.flags & SSM_TREE_VERIFY_FIFO) ? 1 : 0};
   return SSM_TREE_OK;
 }
 

@@ -47,6 +47,7 @@ __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + expf(-z)
 struct Dims {
   int32_t L, Bsz, T, H, P, N, G, W, silu;
   int32_t d_in;  // H * P
+  int32_t fifo;  // verify by the explicit FIFO walk
 };
 
 struct Params {

@@ -657,7 +657,10 @@ int launch_in(const VerifyArgs& a, hipStream_t s) {
 bool mfma_verify_applies(const Dims& d);
 int launch_verify_mfma(const VerifyArgs& a, bool bf16, hipStream_t s);
 
+int launch_verify_fifo(const VerifyArgs& a, bool bf16, hipStream_t s);
+
 int launch_verify(const VerifyArgs& a, bool bf16, hipStream_t s) {
+  if (a.d.fifo) return launch_verify_fifo(a, bf16, s);
   if (mfma_verify_applies(a.d)) return launch_verify_mfma(a, bf16, s);
   return bf16 ? launch_in<bf16_t>(a, s) : launch_in<float>(a, s);
 }

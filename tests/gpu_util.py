@@ -38,13 +38,13 @@ def f32_bits_equal(a, b):
 class GpuCase:
     """One workload on the GPU: inputs uploaded once, verify / commit runs."""
 
-    def __init__(self, cfg, inp=None, device="cuda"):
+    def __init__(self, cfg, inp=None, device="cuda", fifo=False):
         import torch
         self.torch = torch
         self.cfg = cfg
         self.inp = inp if inp is not None else C.make_inputs(cfg)
         self.g = upload(self.inp, device)
-        self.dims = m.make_dims(cfg.L, cfg.Bsz, cfg.T, cfg.H, cfg.P, cfg.N, cfg.G, cfg.W, cfg.bf16, cfg.silu)
+        self.dims = m.make_dims(cfg.L, cfg.Bsz, cfg.T, cfg.H, cfg.P, cfg.N, cfg.G, cfg.W, cfg.bf16, cfg.silu, fifo)
         self.prm = m.make_params(self.g.A, self.g.D, self.g.dt_bias, self.g.conv_w, self.g.conv_b)
         self.device = device
 

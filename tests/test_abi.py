@@ -42,6 +42,8 @@ def test_header_constants_match_binding():
         assert consts["SSM_TREE_" + k] == v, k
     assert consts["SSM_TREE_PLAN_HEADER"] == m.PLAN_HEADER and consts["SSM_TREE_PLAN_STRIDE"] == m.PLAN_STRIDE
     assert consts["SSM_TREE_PLAN_UNUSED"] == m.PLAN_UNUSED
+    assert consts["SSM_TREE_CONV_SILU"] == m.SSM_TREE_CONV_SILU
+    assert consts["SSM_TREE_VERIFY_FIFO"] == m.SSM_TREE_VERIFY_FIFO
 
 
 def test_status_strings():
