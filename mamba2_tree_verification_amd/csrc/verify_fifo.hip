@@ -54,6 +54,35 @@ __device__ __forceinline__ void load_row(const TIn* p, float (&v)[NPL]) {
   for (int i = 0; i < NPL; ++i) v[i] = load_in(p, i);
 }
 
+// A lane's NPL consecutive inputs of one B or C row as raw words, loaded
+// with the widest aligned vector loads and widened when used.
+template <typename TIn, int NPL>
+struct Row {
+  static constexpr int NW = NPL * (int)sizeof(TIn) / 4;
+  uint32_t w[NW];
+  __device__ __forceinline__ void load(const TIn* p) {
+    if constexpr (NW % 4 == 0) {
+#pragma unroll
+      for (int i = 0; i < NW / 4; ++i) {
+        const uint4 q = reinterpret_cast<const uint4*>(p)[i];
+        w[4 * i] = q.x; w[4 * i + 1] = q.y; w[4 * i + 2] = q.z; w[4 * i + 3] = q.w;
+      }
+    } else if constexpr (NW % 2 == 0) {
+#pragma unroll
+      for (int i = 0; i < NW / 2; ++i) {
+        const uint2 q = reinterpret_cast<const uint2*>(p)[i];
+        w[2 * i] = q.x; w[2 * i + 1] = q.y;
+      }
+    } else {
+      w[0] = reinterpret_cast<const uint32_t*>(p)[0];
+    }
+  }
+  __device__ __forceinline__ float get(int i) const {
+    if constexpr (sizeof(TIn) == 2) return __uint_as_float((i & 1) ? (w[i >> 1] & 0xFFFF0000u) : (w[i >> 1] << 16));
+    return __uint_as_float(w[i]);
+  }
+};
+
 }  // namespace
 
 template <typename TIn, int NPL>
@@ -90,23 +119,32 @@ __global__ void __launch_bounds__(kWave) verify_fifo_kernel(VerifyArgs a) {
     return;
   }
 
-  // ---- plan: queue slots, peak occupancy, depth, conv rows (one lane) ----
-  if (lane == 0) {
-    int n_internal = 0, occ = 0, peak = 0, cur = -1;
-    for (int v = 0; v < T; ++v) {
-      const int p = s_parent[v];
-      if (p != cur) {  // the next queued parent comes off the front
-        if (p >= 0) --occ;
-        cur = p;
-      }
-      const bool internal = (v + 1 < T) && [&] {
-        for (int u = v + 1; u < T; ++u)
-          if (s_parent[u] == v) return true;
-        return false;
-      }();
-      s_slot[v] = internal ? (n_internal++) % kRing : kRing + 1;
-      if (internal) peak = max(peak, ++occ);
-      s_depth[v] = p >= 0 ? s_depth[p] + 1 : 1;
+  // ---- plan, one lane per node (T <= 64): queue slot, peak occupancy,
+  // depth, conv input rows ----
+  {
+    const int v = lane;
+    const int p = v < T ? s_parent[v] : -1;
+    const uint64_t upto = (v == 63) ? ~0ull : ((1ull << (v + 1)) - 1);  // nodes 0..v
+    // a parent leaves the queue at its first child (children are contiguous)
+    const bool first_child = v < T && p >= 0 && (v == 0 || s_parent[v - 1] != p);
+    const uint64_t pops = __ballot(first_child);
+    s_slot[v] = 0;
+    __syncthreads();
+    if (first_child) s_slot[p] = 1;  // p has children: it is queued when formed
+    __syncthreads();
+    const bool internal = v < T && s_slot[v] == 1;
+    __syncthreads();
+    const uint64_t queued = __ballot(internal);
+    const int rank = __popcll(queued & (upto >> 1));  // internal nodes before v
+    if (v < T) s_slot[v] = internal ? rank % kRing : kRing + 1;
+    // queue occupancy after node v: queued (internal, <= v) minus popped (parents whose first child is <= v)
+    int occ = v < T ? __popcll(queued & upto) - __popcll(pops & upto) : 0;
+    for (int off = 32; off > 0; off >>= 1) occ = max(occ, __shfl_xor(occ, off));
+    if (v == 0) s_peak = occ;
+    if (v < T) {
+      int dep = 0;
+      for (int u = v; u >= 0; u = s_parent[u]) ++dep;
+      s_depth[v] = dep;
       int packed = 0;
       for (int jj = 1; jj < W; ++jj) {
         const int code = conv_input_code(s_parent, v, jj, W);
@@ -114,7 +152,6 @@ __global__ void __launch_bounds__(kWave) verify_fifo_kernel(VerifyArgs a) {
       }
       s_cidx[v] = packed;
     }
-    s_peak = peak;
   }
   __syncthreads();
 
@@ -146,18 +183,16 @@ __global__ void __launch_bounds__(kWave) verify_fifo_kernel(VerifyArgs a) {
   const float Dh = a.prm.D[(int64_t)l * H + h];
   const TIn* Bg = reinterpret_cast<const TIn*>(a.B) + (unit * T * G + g) * (int64_t)N + s * NPL;
   const TIn* Cg = reinterpret_cast<const TIn*>(a.C) + (unit * T * G + g) * (int64_t)N + s * NPL;
-  float hv[NPL], bv[NPL], cv[NPL];
+  float hv[NPL], bv[NPL];
 
-  // child v of a parent state held in hv's place: update, output, queue
-  auto child = [&](int v, float (&hp)[NPL]) {
+  // child v of the parent state hp: update, output (B and C rows prefetched)
+  auto child = [&](int v, float (&hp)[NPL], const Row<TIn, NPL>& br, const Row<TIn, NPL>& cr) {
     const float dA = s_dA[v * kRows + r], dtx = s_dtx[v * kRows + r];
-    load_row<TIn, NPL>(Bg + (int64_t)v * G * N, bv);
-    load_row<TIn, NPL>(Cg + (int64_t)v * G * N, cv);
     float part = 0.0f;
 #pragma unroll
     for (int i = 0; i < NPL; ++i) {
-      hv[i] = fmaf(dA, hp[i], dtx * bv[i]);
-      part = fmaf(cv[i], hv[i], part);
+      hv[i] = fmaf(dA, hp[i], dtx * br.get(i));
+      part = fmaf(cr.get(i), hv[i], part);
     }
     part += __shfl_xor(part, 1);
     part += __shfl_xor(part, 2);
@@ -166,10 +201,17 @@ __global__ void __launch_bounds__(kWave) verify_fifo_kernel(VerifyArgs a) {
   };
 
   float hp[NPL];
+  // B and C rows two nodes ahead, in two register sets (even and odd nodes)
+  Row<TIn, NPL> b0, c0r, b1, c1r;
+  auto fetch = [&](int v, Row<TIn, NPL>& br, Row<TIn, NPL>& cr) {
+    v = v < T ? v : T - 1;  // past the end: the last row again (branch-free)
+    br.load(Bg + (int64_t)v * G * N);
+    cr.load(Cg + (int64_t)v * G * N);
+  };
   if (s_peak <= kRing) {
     // the page's walk: the parent's state comes off the queue (slot K: root)
     int cur = -2;
-    for (int v = 0; v < T; ++v) {
+    auto step = [&](int v, Row<TIn, NPL>& br, Row<TIn, NPL>& cr) {
       const int p = s_parent[v];
       if (p != cur) {
         const int slot = p < 0 ? kRing : s_slot[p];
@@ -177,10 +219,17 @@ __global__ void __launch_bounds__(kWave) verify_fifo_kernel(VerifyArgs a) {
         for (int i = 0; i < NPL; ++i) hp[i] = slot_at(slot, i);
         cur = p;
       }
-      child(v, hp);
+      child(v, hp, br, cr);
+      fetch(v + 2, br, cr);
       // queue the child's state (leaves go to the scratch slot)
 #pragma unroll
       for (int i = 0; i < NPL; ++i) slot_at(s_slot[v], i) = hv[i];
+    };
+    fetch(0, b0, c0r);
+    fetch(1, b1, c1r);
+    for (int v = 0; v < T; v += 2) {
+      step(v, b0, c0r);
+      if (v + 1 < T) step(v + 1, b1, c1r);
     }
   } else {
     // capacity exceeded: rebuild each parent state from the root along its path
@@ -202,7 +251,9 @@ __global__ void __launch_bounds__(kWave) verify_fifo_kernel(VerifyArgs a) {
         }
         cur = p;
       }
-      child(v, hp);
+      Row<TIn, NPL> br, cr;
+      fetch(v, br, cr);
+      child(v, hp, br, cr);
     }
   }
 }
