@@ -1,15 +1,20 @@
 #!/usr/bin/env python3
 """Throughput of the tree-verification hot path on one MI355X.
 
-One step = ssm_tree_verify over every (layer, sequence) of the workload,
-then ssm_tree_commit of each sequence's accepted path (in place), i.e. one
-pass of the whole hot path.  Inputs are generated on the host, copied to
-HBM before timing, and stay resident.
+One step = one round of speculative decoding over every (layer, sequence)
+of the workload: the previous tree's accepted path is committed into the
+root state and conv window (in place) and the next tree is verified from
+the committed state, by one ssm_tree_commit_verify call, i.e. one pass of
+the whole hot path.  Two trees of the workload's shape alternate as
+previous and next.  Inputs are generated on the host, copied to HBM before
+timing, and stay resident.
 
 The JSON line reports verified tree-node-layers/s (layers x sequences x
-nodes per step), the roofline of the dominant kernel (algorithmic bytes per
-launch over its HIP-event duration, against 8 TB/s), per-kernel figures,
-and the float64 oracle timed on a bounded sample on the host cores.
+nodes per step), the roofline of the step's kernel (algorithmic bytes per
+launch over its HIP-event duration, against 8 TB/s), the same figures for
+the separate ssm_tree_verify and ssm_tree_commit kernels and for the
+explicit FIFO walk (timed apart, outside the step), and the float64 oracle
+timed on a bounded sample on the host cores.
 """
 from __future__ import annotations
 
@@ -27,7 +32,8 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0
 METRIC = "verified tree-node-layers/sec (Mamba2-2.7B SSM, 16-node tree); % HBM peak"
 KERNEL_SOURCES = {"verify": "mamba2_tree_verification_amd/csrc/verify_mfma.hip",
-                  "commit": "mamba2_tree_verification_amd/csrc/commit.hip"}
+                  "commit": "mamba2_tree_verification_amd/csrc/commit.hip",
+                  "commit_verify": "mamba2_tree_verification_amd/csrc/commit_verify.hip"}
 
 
 def algorithmic_bytes(cfg, path_len):
@@ -36,7 +42,10 @@ def algorithmic_bytes(cfg, path_len):
     verify: root state + conv window per (layer, sequence); x, B, C, dt_raw
     and the fp32 y per node; parent[] once.  commit: root state read and
     written, window read and written, and x, B, dt_raw of each accepted
-    node; path and lengths once.  Parameters are excluded (reported apart).
+    node; path and lengths once.  commit_verify: the commit's bytes plus the
+    next tree's per-node inputs and y and its parent[] (the root state and
+    window are read once, by the commit).  Parameters are excluded (reported
+    apart).
     """
     e = cfg.e
     L, Bsz, T, H, P, N, G, W, d = cfg.L, cfg.Bsz, cfg.T, cfg.H, cfg.P, cfg.N, cfg.G, cfg.W, cfg.d_in
@@ -47,7 +56,8 @@ def algorithmic_bytes(cfg, path_len):
     acc = int(sum(int(n) for n in path_len))
     commit = L * (Bsz * (2 * state + 2 * window) + acc * (d * e + G * N * e + H * e)) + Bsz * (T + 1) * 4
     params = L * (3 * H * 4 + d * W * 4)
-    return verify, commit, params
+    fused = commit + L * Bsz * T * (node_in + d * 4) + Bsz * T * 4
+    return {"verify": verify, "commit": commit, "commit_verify": fused, "params": params}
 
 
 def source_sha(paths):
@@ -75,8 +85,8 @@ def load_traffic(kernel):
 
 
 PROBE_BYTES = 4 << 30  # the plain copy of hbm_probe: reads and writes this many bytes per dispatch
-KERNEL_MATCH = {"verify": ("verify_mfma_kernel", "verify_proj_kernel"), "commit": ("commit_kernel",),
-                "copy": ("copyBuffer",)}
+KERNEL_MATCH = {"verify": ("verify_mfma_kernel", "verify_proj_kernel"), "commit": ("::commit_kernel",),
+                "commit_verify": ("commit_verify_kernel",), "copy": ("copyBuffer",)}
 
 
 def _pmc_per_dispatch(run_dir, counter):
@@ -112,7 +122,7 @@ def record_traffic(prof_dir):
     sf, sw = PROBE_BYTES / (cf * 1024), PROBE_BYTES / (cw * 1024)
     out = {"scale": {"fetch": round(sf, 4), "write": round(sw, 4), "copy_bytes": PROBE_BYTES,
                      "copy_fetch_kib": cf, "copy_write_kib": cw}}
-    for k in ("verify", "commit"):
+    for k in KERNEL_SOURCES:
         out[k] = {"fetch_kib": fetch[k], "write_kib": write[k],
                   "bytes_per_launch": int(round(fetch[k] * 1024 * sf + write[k] * 1024 * sw)),
                   "source_sha": source_sha([KERNEL_SOURCES[k], "mamba2_tree_verification_amd/csrc/common.h"])}
@@ -230,6 +240,10 @@ def main(argv=None):
     t_gen = time.perf_counter()
     inp = C.make_inputs(cfg, nthreads=args.threads)
     g = upload(inp)
+    # a second tree per sequence (own nodes and accepted path, same layers)
+    inp2 = C.make_inputs(cfg.replace(cid=cfg.cid + 500), nthreads=args.threads,
+                         skip=("state", "window", "A", "D", "dt_bias", "conv_w", "conv_b"))
+    g2 = upload(inp2)
     t_gen = time.perf_counter() - t_gen
     dims = m.make_dims(cfg.L, cfg.Bsz, cfg.T, cfg.H, cfg.P, cfg.N, cfg.G, cfg.W, cfg.bf16, cfg.silu)
     prm = m.make_params(g.A, g.D, g.dt_bias, g.conv_w, g.conv_b)
@@ -238,55 +252,68 @@ def main(argv=None):
     st_c = torch.empty(cfg.Bsz, dtype=torch.int32, device="cuda")
     state = g.state  # committed in place, step after step
     window = g.window
+    trees = (g, g2)
 
-    def step(ev=None):
+    def step(k, ev=None):
+        prev, nxt = trees[k % 2], trees[(k + 1) % 2]
         if ev is not None:
             ev[0].record()
-        m.verify(dims, prm, g.parent, g.x, g.B, g.C, g.dt_raw, window, state, y, st_v)
+        m.commit_verify(dims, prm, prev.parent, prev.path, prev.path_len, prev.x, prev.B, prev.dt_raw, window, state,
+                        window, state, nxt.parent, nxt.x, nxt.B, nxt.C, nxt.dt_raw, y, st_c, st_v)
         if ev is not None:
             ev[1].record()
-        m.commit(dims, prm, g.parent, g.path, g.path_len, g.x, g.B, g.dt_raw, window, state, window, state, st_c)
-        if ev is not None:
-            ev[2].record()
 
-    for _ in range(args.warmup):
-        step()
+    for k in range(args.warmup):
+        step(k)
     torch.cuda.synchronize()
     if not (st_v.cpu() == 0).all() or not (st_c.cpu() == 0).all():
         print("bench: nonzero sequence status", file=sys.stderr)
         return 1
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
-        step(evs[k])
+        step(args.warmup + k, evs[k])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ver_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    com_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    cv_ms = [e[0].elapsed_time(e[1]) for e in evs]
     ms_per_step = wall * 1e3 / args.steps
     if torch.isnan(y).any():
         print("bench: NaN in y", file=sys.stderr)
         return 1
 
-    # the page's own form (explicit FIFO walk, every child state materialised),
-    # timed apart for comparison; not part of the step
-    dims_fifo = m.make_dims(cfg.L, cfg.Bsz, cfg.T, cfg.H, cfg.P, cfg.N, cfg.G, cfg.W, cfg.bf16, cfg.silu, fifo=True)
-    fifo_ms = []
-    for k in range(4):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        m.verify(dims_fifo, prm, g.parent, g.x, g.B, g.C, g.dt_raw, window, state, y, st_v)
-        e1.record()
-        torch.cuda.synchronize()
-        if k:
-            fifo_ms.append(e0.elapsed_time(e1))
+    # not part of the step, timed apart for comparison: the same round as two
+    # calls (verify from the state, then the in-place commit), and the page's
+    # own form of verification (explicit FIFO walk, every child state
+    # materialised)
+    def timed(fn, reps=5):
+        out = []
+        for k in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            if k:
+                out.append(e0.elapsed_time(e1))
+        return out
 
-    vb, cb, pb = algorithmic_bytes(cfg, inp.path_len)
-    v_avg = sum(ver_ms) / len(ver_ms)
-    c_avg = sum(com_ms) / len(com_ms)
+    ver_ms = timed(lambda: m.verify(dims, prm, g.parent, g.x, g.B, g.C, g.dt_raw, window, state, y, st_v))
+    com_ms = timed(lambda: m.commit(dims, prm, g.parent, g.path, g.path_len, g.x, g.B, g.dt_raw, window, state,
+                                    window, state, st_c))
+    dims_fifo = m.make_dims(cfg.L, cfg.Bsz, cfg.T, cfg.H, cfg.P, cfg.N, cfg.G, cfg.W, cfg.bf16, cfg.silu, fifo=True)
+    fifo_ms = timed(lambda: m.verify(dims_fifo, prm, g.parent, g.x, g.B, g.C, g.dt_raw, window, state, y, st_v),
+                    reps=3)
+
+    ab = algorithmic_bytes(cfg, inp.path_len)
+    ab2 = algorithmic_bytes(cfg, inp2.path_len)
+    # the step alternates which tree's path is committed: average the two
+    cvb = (ab["commit_verify"] + ab2["commit_verify"]) // 2
     node_layers = cfg.L * cfg.Bsz * cfg.T
+
+    def avg(v):
+        return sum(v) / len(v)
 
     def roof(kernel, nbytes, ms):
         ach = nbytes / (ms * 1e-3) / 1e9
@@ -294,14 +321,16 @@ def main(argv=None):
         return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": tr}
 
-    kern = {"verify": dict(ms=round(v_avg, 4), ms_min=round(min(ver_ms), 4), bytes=vb,
-                           node_layers_per_s=round(node_layers / (v_avg * 1e-3), 1),
-                           roofline=roof("verify", vb, v_avg)),
-            "commit": dict(ms=round(c_avg, 4), ms_min=round(min(com_ms), 4), bytes=cb,
-                           roofline=roof("commit", cb, c_avg)),
-            "verify_fifo_walk": dict(ms=round(sum(fifo_ms) / len(fifo_ms), 4), bytes=vb,
+    kern = {"commit_verify": dict(ms=round(avg(cv_ms), 4), ms_min=round(min(cv_ms), 4), bytes=cvb,
+                                  node_layers_per_s=round(node_layers / (avg(cv_ms) * 1e-3), 1),
+                                  roofline=roof("commit_verify", cvb, avg(cv_ms))),
+            "verify": dict(ms=round(avg(ver_ms), 4), ms_min=round(min(ver_ms), 4), bytes=ab["verify"],
+                           node_layers_per_s=round(node_layers / (avg(ver_ms) * 1e-3), 1),
+                           roofline=roof("verify", ab["verify"], avg(ver_ms)), note="not in the step"),
+            "commit": dict(ms=round(avg(com_ms), 4), ms_min=round(min(com_ms), 4), bytes=ab["commit"],
+                           roofline=roof("commit", ab["commit"], avg(com_ms)), note="not in the step"),
+            "verify_fifo_walk": dict(ms=round(avg(fifo_ms), 4), bytes=ab["verify"],
                                      note="SSM_TREE_VERIFY_FIFO, not in the step")}
-    dominant = "verify" if v_avg >= c_avg else "commit"
     rec = {
         "metric": METRIC,
         "value": round(node_layers / (ms_per_step * 1e-3), 1),
@@ -318,10 +347,12 @@ def main(argv=None):
         "config": {"workload": cfg.name, "layers": cfg.L, "batch": cfg.Bsz, "tree_nodes": cfg.T,
                    "nheads": cfg.H, "headdim": cfg.P, "d_state": cfg.N, "ngroups": cfg.G, "conv_width": cfg.W,
                    "inputs": "bf16" if cfg.bf16 else "f32", "state": "f32",
-                   "step": "ssm_tree_verify + in-place ssm_tree_commit", "parallelism": "single-gpu"},
-        "roofline": dict(kern[dominant]["roofline"], kernel=dominant),
+                   "step": "ssm_tree_commit_verify: in-place commit of the previous tree's accepted path, "
+                           "verify of the next tree", "parallelism": "single-gpu"},
+        "roofline": dict(kern["commit_verify"]["roofline"], kernel="commit_verify"),
         "kernels": kern,
-        "param_bytes_per_call": pb,
+        "two_call_step_ms": round(avg(ver_ms) + avg(com_ms), 4),
+        "param_bytes_per_call": ab["params"],
         "verify_hbm_frac": kern["verify"]["roofline"]["frac"],
     }
     if not args.no_cpu_baseline:

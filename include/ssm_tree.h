@@ -151,6 +151,39 @@ int ssm_tree_commit(const ssm_tree_dims* dims, const ssm_tree_params* params, co
                     int32_t* seq_status, void* hip_stream);
 
 /*
+ * ssm_tree_commit_verify: ssm_tree_commit of the previous tree's accepted
+ * path followed by ssm_tree_verify of the next tree from the committed state
+ * and window, in one pass over the root state (it is read and written once
+ * instead of being read by verify and read and written by commit).
+ *
+ * parent_prev, path, path_len, x_prev, B_prev, dt_raw_prev: the previous
+ *             tree and its accepted path, as for ssm_tree_commit
+ * conv_window_in, state_in -> conv_window_out, state_out: as for
+ *             ssm_tree_commit (exact in-place allowed)
+ * parent, x, B, C, dt_raw: the next tree, as for ssm_tree_verify (same
+ *             dims: T nodes)
+ * y           [L][Bsz][T][H*P] float32 out: the next tree's outputs
+ * commit_status [Bsz] or NULL: as ssm_tree_commit's seq_status.  A sequence
+ *             whose commit fails gets its state_in and conv_window_in copied
+ *             unchanged to state_out and conv_window_out, and its next tree
+ *             is verified from them.
+ * verify_status [Bsz] or NULL: as ssm_tree_verify's seq_status (next tree).
+ * Outputs equal ssm_tree_commit followed by ssm_tree_verify up to fp32
+ * rounding.  Trees of 1 to 16 nodes with a headdim that is a multiple of 16
+ * take the fused kernel; other shapes, and dims.flags with
+ * SSM_TREE_VERIFY_FIFO, copy state and window to the outputs (unless in
+ * place), run ssm_tree_commit in place on them and then ssm_tree_verify.
+ * Host-side errors as for the two calls; every output range is checked
+ * against every input range before anything is enqueued.
+ */
+int ssm_tree_commit_verify(const ssm_tree_dims* dims, const ssm_tree_params* params, const int32_t* parent_prev,
+                           const int32_t* path, const int32_t* path_len, const void* x_prev, const void* B_prev,
+                           const void* dt_raw_prev, const void* conv_window_in, const float* state_in,
+                           void* conv_window_out, float* state_out, const int32_t* parent, const void* x,
+                           const void* B, const void* C, const void* dt_raw, float* y, int32_t* commit_status,
+                           int32_t* verify_status, void* hip_stream);
+
+/*
  * ssm_tree_plan: the tree plan the kernels derive from parent[] (SpecMamba
  * page sec. 3.2: breadth-first flattening, FIFO of live states), exported
  * so that its integer bookkeeping can be compared exactly.

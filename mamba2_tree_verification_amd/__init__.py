@@ -1,9 +1,10 @@
 """Python binding of libssm_tree.so (argument marshalling only).
 
-The functions ``ssm_tree_verify``, ``ssm_tree_commit``, ``ssm_tree_plan``,
-``ssm_tree_status_string`` and ``ssm_tree_abi_version`` mirror the C ABI in
-``include/ssm_tree.h`` one to one and take raw device addresses.  The
-``verify`` / ``commit`` / ``plan`` helpers accept torch tensors on the GPU,
+The functions ``ssm_tree_verify``, ``ssm_tree_commit``,
+``ssm_tree_commit_verify``, ``ssm_tree_plan``, ``ssm_tree_status_string`` and
+``ssm_tree_abi_version`` mirror the C ABI in ``include/ssm_tree.h`` one to
+one and take raw device addresses.  The ``verify`` / ``commit`` /
+``commit_verify`` / ``plan`` helpers accept torch tensors on the GPU,
 check their dtypes and contiguity, pass ``data_ptr()`` and the current HIP
 stream, and raise ``SsmTreeError`` on a nonzero return.  Every step of the
 computation runs in the HIP kernels; there is no CPU fallback.
@@ -63,6 +64,8 @@ def load():
         L.ssm_tree_verify.restype = i
         L.ssm_tree_commit.argtypes = [p] * 14
         L.ssm_tree_commit.restype = i
+        L.ssm_tree_commit_verify.argtypes = [p] * 21
+        L.ssm_tree_commit_verify.restype = i
         L.ssm_tree_plan.argtypes = [p] * 4
         L.ssm_tree_plan.restype = i
         L.ssm_tree_status_string.argtypes = [i]
@@ -89,6 +92,15 @@ def ssm_tree_commit(dims: Dims, params: Params, parent, path, path_len, x, B, dt
                     conv_window_out, state_out, seq_status, hip_stream) -> int:
     return load().ssm_tree_commit(ctypes.byref(dims), ctypes.byref(params), parent, path, path_len, x, B, dt_raw,
                                   conv_window_in, state_in, conv_window_out, state_out, seq_status, hip_stream)
+
+
+def ssm_tree_commit_verify(dims: Dims, params: Params, parent_prev, path, path_len, x_prev, B_prev, dt_raw_prev,
+                           conv_window_in, state_in, conv_window_out, state_out, parent, x, B, C, dt_raw, y,
+                           commit_status, verify_status, hip_stream) -> int:
+    return load().ssm_tree_commit_verify(ctypes.byref(dims), ctypes.byref(params), parent_prev, path, path_len,
+                                         x_prev, B_prev, dt_raw_prev, conv_window_in, state_in, conv_window_out,
+                                         state_out, parent, x, B, C, dt_raw, y, commit_status, verify_status,
+                                         hip_stream)
 
 
 def ssm_tree_plan(dims: Dims, parent, plan_out, hip_stream) -> int:
@@ -166,6 +178,22 @@ def commit(dims: Dims, params: Params, parent, path, path_len, x, B, dt_raw, con
                          _ptr(seq_status), _stream(stream))
     if rc != OK:
         raise SsmTreeError(rc, "ssm_tree_commit")
+
+
+def commit_verify(dims: Dims, params: Params, parent_prev, path, path_len, x_prev, B_prev, dt_raw_prev,
+                  conv_window_in, state_in, conv_window_out, state_out, parent, x, B, C, dt_raw, y,
+                  commit_status=None, verify_status=None, stream=None):
+    for t, k in ((parent_prev, "int32"), (path, "int32"), (path_len, "int32"), (x_prev, "in"), (B_prev, "in"),
+                 (dt_raw_prev, "in"), (conv_window_in, "in"), (state_in, "float32"), (conv_window_out, "in"),
+                 (state_out, "float32"), (parent, "int32"), (x, "in"), (B, "in"), (C, "in"), (dt_raw, "in"),
+                 (y, "float32"), (commit_status, "int32"), (verify_status, "int32")):
+        _check(t, k)
+    rc = ssm_tree_commit_verify(dims, params, _ptr(parent_prev), _ptr(path), _ptr(path_len), _ptr(x_prev),
+                                _ptr(B_prev), _ptr(dt_raw_prev), _ptr(conv_window_in), _ptr(state_in),
+                                _ptr(conv_window_out), _ptr(state_out), _ptr(parent), _ptr(x), _ptr(B), _ptr(C),
+                                _ptr(dt_raw), _ptr(y), _ptr(commit_status), _ptr(verify_status), _stream(stream))
+    if rc != OK:
+        raise SsmTreeError(rc, "ssm_tree_commit_verify")
 
 
 def plan(dims: Dims, parent, plan_out, stream=None):

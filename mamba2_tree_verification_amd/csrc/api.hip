@@ -8,6 +8,8 @@
 namespace ssmt {
 int launch_verify(const VerifyArgs& a, bool bf16, hipStream_t s);  // status code
 hipError_t launch_commit(const CommitArgs& a, bool bf16, hipStream_t s);
+bool commit_verify_fused_applies(const Dims& d);
+int launch_commit_verify(const CommitVerifyArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_plan(const int32_t* parent, int Bsz, int T, int W, int32_t* out, hipStream_t s);
 hipError_t launch_status(int32_t* seq_status, int Bsz, int value, hipStream_t s);
 }  // namespace ssmt
@@ -185,6 +187,99 @@ int ssm_tree_commit(const ssm_tree_dims* dims, const ssm_tree_params* params, co
   a.state_out = state_out;
   a.seq_status = seq_status;
   return launch_commit(a, dims->in_dtype == SSM_TREE_BF16, s) == hipSuccess ? SSM_TREE_OK : SSM_TREE_E_HIP;
+}
+
+int ssm_tree_commit_verify(const ssm_tree_dims* dims, const ssm_tree_params* params, const int32_t* parent_prev,
+                           const int32_t* path, const int32_t* path_len, const void* x_prev, const void* B_prev,
+                           const void* dt_raw_prev, const void* conv_window_in, const float* state_in,
+                           void* conv_window_out, float* state_out, const int32_t* parent, const void* x,
+                           const void* B, const void* C, const void* dt_raw, float* y, int32_t* commit_status,
+                           int32_t* verify_status, void* hip_stream) {
+  Dims d;
+  int st = check_dims(dims, &d);
+  if (st) return st;
+  if (d.L == 0 || d.Bsz == 0) return SSM_TREE_OK;
+  if ((st = check_params(params))) return st;
+  if (!path_len || !state_in || !state_out) return SSM_TREE_E_NULL;
+  if (d.T > 0 && (!parent_prev || !path || !x_prev || !B_prev || !dt_raw_prev || !parent || !x || !B || !C ||
+                  !dt_raw || !y))
+    return SSM_TREE_E_NULL;
+  if (d.W > 1 && (!conv_window_in || !conv_window_out)) return SSM_TREE_E_NULL;
+  const void* ptrs[] = {parent_prev, path, path_len, x_prev, B_prev, dt_raw_prev, state_in, state_out, parent, x,
+                        B, C, dt_raw, y, commit_status, verify_status,
+                        d.W > 1 ? conv_window_in : nullptr, d.W > 1 ? conv_window_out : nullptr};
+  for (const void* p : ptrs)
+    if (p && misaligned(p)) return SSM_TREE_E_ALIGN;
+  const int64_t e = dims->in_dtype == SSM_TREE_BF16 ? 2 : 4;
+  const int64_t U = (int64_t)d.L * d.Bsz, T = d.T, DI = d.d_in;
+  const int64_t wbytes = d.W > 1 ? U * (d.W - 1) * DI * e : 0;
+  const Range rso = range_of(state_out, U * DI * d.N * 4), rsi = range_of(state_in, U * DI * d.N * 4);
+  const Range rwo = range_of(conv_window_out, wbytes), rwi = range_of(conv_window_in, wbytes);
+  const Range ry = range_of(y, U * T * DI * 4);
+  const Range rcs = range_of(commit_status, commit_status ? (int64_t)d.Bsz * 4 : 0);
+  const Range rvs = range_of(verify_status, verify_status ? (int64_t)d.Bsz * 4 : 0);
+  const Range ins[] = {range_of(parent_prev, (int64_t)d.Bsz * T * 4), range_of(path, (int64_t)d.Bsz * T * 4),
+                       range_of(path_len, (int64_t)d.Bsz * 4), range_of(x_prev, U * T * DI * e),
+                       range_of(B_prev, U * T * d.G * d.N * e), range_of(dt_raw_prev, U * T * d.H * e),
+                       range_of(parent, (int64_t)d.Bsz * T * 4), range_of(x, U * T * DI * e),
+                       range_of(B, U * T * d.G * d.N * e), range_of(C, U * T * d.G * d.N * e),
+                       range_of(dt_raw, U * T * d.H * e),
+                       range_of(params->A, d.L * (int64_t)d.H * 4), range_of(params->D, d.L * (int64_t)d.H * 4),
+                       range_of(params->dt_bias, d.L * (int64_t)d.H * 4),
+                       range_of(params->conv_w, d.L * DI * d.W * 4),
+                       range_of(params->conv_b, params->conv_b ? d.L * DI * 4 : 0)};
+  // outputs: state and window may equal their inputs exactly; nothing else may overlap
+  if (state_out != state_in && overlaps(rso, rsi)) return SSM_TREE_E_ALIAS;
+  if (d.W > 1 && conv_window_out != conv_window_in && overlaps(rwo, rwi)) return SSM_TREE_E_ALIAS;
+  const Range outs[] = {rso, rwo, ry, rcs, rvs};
+  for (int i = 0; i < 5; ++i) {
+    for (const Range& r : ins)
+      if (overlaps(outs[i], r)) return SSM_TREE_E_ALIAS;
+    for (int k = i + 1; k < 5; ++k)
+      if (overlaps(outs[i], outs[k])) return SSM_TREE_E_ALIAS;
+    if (i >= 1 && overlaps(outs[i], rsi)) return SSM_TREE_E_ALIAS;
+    if (i != 1 && overlaps(outs[i], rwi)) return SSM_TREE_E_ALIAS;
+  }
+  hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
+  if (d.fifo || !commit_verify_fused_applies(d)) {
+    // The two calls in turn, on the same stream.  The outputs first receive
+    // the inputs and the commit then runs in place on them, so that a
+    // sequence whose commit fails carries its old state and window into the
+    // verify, as the fused kernel does.
+    if (state_out != state_in &&
+        hipMemcpyAsync(state_out, state_in, rso.hi - rso.lo, hipMemcpyDeviceToDevice, s) != hipSuccess)
+      return SSM_TREE_E_HIP;
+    if (wbytes && conv_window_out != conv_window_in &&
+        hipMemcpyAsync(conv_window_out, conv_window_in, wbytes, hipMemcpyDeviceToDevice, s) != hipSuccess)
+      return SSM_TREE_E_HIP;
+    st = ssm_tree_commit(dims, params, parent_prev, path, path_len, x_prev, B_prev, dt_raw_prev, conv_window_out,
+                         state_out, conv_window_out, state_out, commit_status, hip_stream);
+    if (st) return st;
+    return ssm_tree_verify(dims, params, parent, x, B, C, dt_raw, conv_window_out, state_out, y, verify_status,
+                           hip_stream);
+  }
+  CommitVerifyArgs a;
+  a.d = d;
+  a.prm = Params{params->A, params->D, params->dt_bias, params->conv_w, params->conv_b};
+  a.parent_prev = parent_prev;
+  a.path = path;
+  a.path_len = path_len;
+  a.x_prev = x_prev;
+  a.B_prev = B_prev;
+  a.dt_prev = dt_raw_prev;
+  a.window_in = conv_window_in;
+  a.state_in = state_in;
+  a.window_out = conv_window_out;
+  a.state_out = state_out;
+  a.parent = parent;
+  a.x = x;
+  a.B = B;
+  a.C = C;
+  a.dt_raw = dt_raw;
+  a.y = y;
+  a.commit_status = commit_status;
+  a.verify_status = verify_status;
+  return launch_commit_verify(a, dims->in_dtype == SSM_TREE_BF16, s);
 }
 
 int ssm_tree_plan(const ssm_tree_dims* dims, const int32_t* parent, int32_t* plan_out, void* hip_stream) {

@@ -1,0 +1,530 @@
+// commit_verify.hip - ssm_tree_commit of the last step's accepted path fused
+// with ssm_tree_verify of the next tree, in one pass over the root state.
+//
+// Per (layer, sequence): the root state is read once, advanced along the
+// accepted path of the previous tree (SpecMamba page sec. 3.1: recompute
+// from the stored per-token dt, B and x), written once, and the next
+// tree's outputs are formed from the new state while it is still in
+// registers (the root projection of verify_mfma.hip:
+//   y_v = a_v (C_v . h) + sum_{u on path(v)} M[v][u] x~_u).
+// Results equal ssm_tree_commit followed by ssm_tree_verify on the
+// committed state and window, up to fp32 rounding.  A sequence whose commit
+// fails (invalid previous tree or path) passes its state and window through
+// unchanged to the outputs, and its next tree is verified from them.
+//
+// Mapping.  One workgroup of 4 waves per (layer, sequence, 64 channels);
+// wave w owns channels 16 w .. 16 w + 15.  Lane (j + 16 k) holds columns
+// 16 gg + 4 k .. + 3 of channel j for every column group gg, which is both
+// a coalesced 16-byte load and the B-operand layout of
+// v_mfma_f32_16x16x4_f32, so the committed state feeds C . h on the
+// matrix cores directly.
+//
+// Latency.  A workgroup's life is short (64 KiB of state in and out), so
+// the number of dependent trips to memory decides the throughput.  There
+// are two: every load that does not depend on the accepted path is issued
+// at entry (state, both trees' parent[], the next tree's x, B, C and dt
+// rows, the previous tree's dt rows, window, parameters); the path's x and
+// B rows are gathered right after, from the unvalidated path, while one
+// wave validates the trees and the path with ballots, one forms C_v . B_u
+// and one the next tree's ancestor sets and conv taps.  Everything after
+// that runs from LDS.  y is staged in LDS and leaves as whole 256-byte row
+// segments.  Trees of at most 16 nodes, heads a multiple of 16 channels
+// wide.
+#include "common.h"
+
+namespace ssmt {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kCvRows = 64;   // channels per workgroup
+constexpr int kCvWaves = 4;
+constexpr int kCvT = 16;      // node capacity
+constexpr int kRowPad = 16;   // bytes of padding per staged B / C row (LDS banks)
+
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+template <typename TIn>
+__device__ __forceinline__ f32x4 load4(const TIn* p);
+template <>
+__device__ __forceinline__ f32x4 load4<float>(const float* p) {
+  return *reinterpret_cast<const f32x4*>(p);
+}
+template <>
+__device__ __forceinline__ f32x4 load4<bf16_t>(const bf16_t* p) {
+  const uint2 w = *reinterpret_cast<const uint2*>(p);
+  f32x4 r;
+  r.x = __uint_as_float(w.x << 16);
+  r.y = __uint_as_float(w.x & 0xFFFF0000u);
+  r.z = __uint_as_float(w.y << 16);
+  r.w = __uint_as_float(w.y & 0xFFFF0000u);
+  return r;
+}
+
+// four consecutive input elements as raw bits
+template <int E>
+struct Raw4;
+template <>
+struct Raw4<2> {
+  typedef u32x2 T;
+};
+template <>
+struct Raw4<4> {
+  typedef u32x4 T;
+};
+
+__host__ __device__ constexpr int align16(int x) { return (x + 15) & ~15; }
+
+// LDS layout (byte offsets).  ys reuses the x staging of both trees, which
+// is dead once the conv outputs exist; dtx reuses the next tree's B rows,
+// dead once C . B is formed.
+struct CvLds {
+  int pparent, path, parent, misc, anc, cidx, dAp, dtp, dt, S, S2, D, cbt, cw, cb, win, xn, xp, ys, C, B, dtx, Bp,
+      xt, total, row;
+  __host__ __device__ CvLds(int N, int E) {
+    int o = 0;
+    row = N * E + kRowPad;                    // staged B / C row stride
+    pparent = o; o += 4 * kCvT;
+    path = o; o += 4 * kCvT;
+    parent = o; o += 4 * kCvT;
+    misc = o; o += 16;                        // [0] path length applied, [1] commit status, [2] next tree ok, [3] raw length
+    anc = o; o += 4 * kCvT;                   // next tree: root-path bitmask per node
+    cidx = o; o += 4 * kCvT;                  // next tree: conv inputs of taps 1..3 (node, or T + window row)
+    dAp = o; o += 4 * kCvT * 4;               // previous tree: dA per node and head
+    dtp = o; o += 4 * kCvT * 4;               // previous tree: dt per node and head
+    dt = o; o += 4 * 4 * kCvT;                // next tree: dt per head and node
+    S = o; o += 4 * 4 * kCvT;                 // next tree: dt * A per head and node
+    S2 = o; o += 4 * 4 * kCvT;                // next tree: cumulative S along the root path, times log2(e)
+    D = o; o += 16;
+    cbt = o; o += 4 * kCvT * kCvT;            // next tree: C_v . B_u
+    cw = o; o += 4 * 4 * kCvRows;             // conv weights per channel, tap order of the parameters
+    cb = o; o += 4 * kCvRows;                 // conv bias per channel
+    win = o; o += align16(3 * kCvRows * E);   // old window rows (raw)
+    xn = o; o += kCvT * kCvRows * E;          // next tree x (raw)
+    xp = o; o += kCvT * kCvRows * E;          // previous tree x of the path nodes (raw)
+    ys = xn;                                  // y staging [node][channel] fp32 (needs 4 KiB: 2 x 1024 E >= 4096)
+    C = o; o += kCvT * row;                   // next tree C rows (raw, padded)
+    B = o;                                    // next tree B rows (raw, padded) ...
+    dtx = o;                                  // ... then dt * x~ per path node and channel, fp32
+    o += kCvT * row > 4 * kCvT * kCvRows ? kCvT * row : 4 * kCvT * kCvRows;
+    Bp = o; o += kCvT * row;                  // previous tree B rows of the path nodes (raw, padded)
+    xt = o; o += 4 * kCvRows * kCvT;          // next tree conv outputs, MFMA B-operand layout
+    total = o;
+  }
+};
+
+}  // namespace
+
+template <typename TIn, int NG>
+__global__ void __launch_bounds__(kCvWaves * kWave) commit_verify_kernel(CommitVerifyArgs a) {
+  constexpr int N = 16 * NG;
+  constexpr int E = (int)sizeof(TIn);
+  typedef typename Raw4<E>::T RawQ;
+  constexpr int kChunks = N * E / 16;                           // 16-byte chunks per B / C row
+  constexpr int kCPT = (kCvT * kChunks + kCvWaves * kWave - 1) / (kCvWaves * kWave);  // chunks per thread
+  const Dims d = a.d;
+  const int T = d.T, P = d.P, H = d.H, W = d.W, DI = d.d_in, G = d.G;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int j = lane & 15, k = lane >> 4;
+  const int b = blockIdx.y, l = blockIdx.z;
+  const int64_t unit = (int64_t)l * d.Bsz + b;
+  const int c0 = blockIdx.x * kCvRows;
+  const int h_lo = c0 / P;
+  const int HW = (c0 + kCvRows - 1) / P - h_lo + 1;  // heads touched (<= 4: P is a multiple of 16)
+  const int g = c0 / (DI / G);
+
+  extern __shared__ __align__(16) unsigned char smem[];
+  const CvLds lo(N, E);
+  int32_t* s_pparent = reinterpret_cast<int32_t*>(smem + lo.pparent);
+  int32_t* s_path = reinterpret_cast<int32_t*>(smem + lo.path);
+  int32_t* s_parent = reinterpret_cast<int32_t*>(smem + lo.parent);
+  int32_t* s_misc = reinterpret_cast<int32_t*>(smem + lo.misc);
+  int32_t* s_anc = reinterpret_cast<int32_t*>(smem + lo.anc);
+  int32_t* s_cidx = reinterpret_cast<int32_t*>(smem + lo.cidx);
+  float* s_dAp = reinterpret_cast<float*>(smem + lo.dAp);
+  float* s_dtp = reinterpret_cast<float*>(smem + lo.dtp);
+  float* s_dt = reinterpret_cast<float*>(smem + lo.dt);
+  float* s_S = reinterpret_cast<float*>(smem + lo.S);
+  float* s_S2 = reinterpret_cast<float*>(smem + lo.S2);
+  float* s_D = reinterpret_cast<float*>(smem + lo.D);
+  float* s_cbt = reinterpret_cast<float*>(smem + lo.cbt);
+  float* s_cw = reinterpret_cast<float*>(smem + lo.cw);
+  float* s_cb = reinterpret_cast<float*>(smem + lo.cb);
+  TIn* s_win = reinterpret_cast<TIn*>(smem + lo.win);
+  TIn* s_xn = reinterpret_cast<TIn*>(smem + lo.xn);
+  TIn* s_xp = reinterpret_cast<TIn*>(smem + lo.xp);
+  float* s_ys = reinterpret_cast<float*>(smem + lo.ys);
+  unsigned char* s_C = smem + lo.C;
+  unsigned char* s_B = smem + lo.B;
+  float* s_dtx = reinterpret_cast<float*>(smem + lo.dtx);
+  unsigned char* s_Bp = smem + lo.Bp;
+  float* s_xt = reinterpret_cast<float*>(smem + lo.xt);
+  const int rs = lo.row;
+
+  // ======== trip 1: everything that does not depend on the path ========
+  const float* sin = a.state_in + (unit * DI + c0 + wave * 16 + j) * (int64_t)N + 4 * k;
+  f32x4 hq[NG];
+#pragma unroll
+  for (int gg = 0; gg < NG; ++gg) hq[gg] = *reinterpret_cast<const f32x4*>(sin + 16 * gg);
+
+  int r_pp = 0, r_path = 0, r_par = 0, r_len = 0;
+  if (tid < T) {
+    r_pp = a.parent_prev[(int64_t)b * T + tid];
+    r_path = a.path[(int64_t)b * T + tid];
+    r_par = a.parent[(int64_t)b * T + tid];
+  }
+  if (tid == kCvWaves * kWave - 1) r_len = a.path_len[b];
+
+  // x rows: thread (v, q) holds channels 4 q .. 4 q + 3 of node v
+  const int xv = tid >> 4, xq = (tid & 15) * 4;
+  RawQ rx{};
+  if (xv < T)
+    rx = *reinterpret_cast<const RawQ*>(reinterpret_cast<const TIn*>(a.x) + (unit * T + xv) * DI + c0 + xq);
+  // B and C rows of the next tree, 16-byte chunks
+  u32x4 rc[kCPT], rb[kCPT];
+  const unsigned char* Cg = reinterpret_cast<const unsigned char*>(a.C) + ((unit * T) * G + g) * (int64_t)N * E;
+  const unsigned char* Bg = reinterpret_cast<const unsigned char*>(a.B) + ((unit * T) * G + g) * (int64_t)N * E;
+#pragma unroll
+  for (int it = 0; it < kCPT; ++it) {
+    const int ci = tid + it * kCvWaves * kWave, v = ci / kChunks, q = ci % kChunks;
+    if (v < T) {
+      rc[it] = *reinterpret_cast<const u32x4*>(Cg + (int64_t)v * G * N * E + q * 16);
+      rb[it] = *reinterpret_cast<const u32x4*>(Bg + (int64_t)v * G * N * E + q * 16);
+    }
+  }
+  // per-head scalars: wave 0 the next tree's dt, wave 1 the previous tree's
+  const int sv = (lane >> 2), sh = lane & 3;
+  float r_dt = 0.0f, r_A = 0.0f, r_bias = 0.0f, r_D = 0.0f;
+  if (wave < 2 && sv < T && sh < HW) {
+    const TIn* src = reinterpret_cast<const TIn*>(wave == 0 ? a.dt_raw : a.dt_prev) + unit * T * H;
+    r_dt = load_in(src, (int64_t)sv * H + h_lo + sh);
+    r_A = a.prm.A[(int64_t)l * H + h_lo + sh];
+    r_bias = a.prm.dt_bias[(int64_t)l * H + h_lo + sh];
+  }
+  if (wave == 0 && lane < HW) r_D = a.prm.D[(int64_t)l * H + h_lo + lane];
+  // wave 2: old window rows; wave 3: conv weights and bias
+  TIn r_win[3];
+  float r_cw[4] = {0.0f, 0.0f, 0.0f, 0.0f}, r_cb = 0.0f;
+  if (wave == 2) {
+    const TIn* win_in = reinterpret_cast<const TIn*>(a.window_in) + unit * (W - 1) * (int64_t)DI + c0 + lane;
+#pragma unroll
+    for (int r = 0; r < 3; ++r)
+      if (r < W - 1) r_win[r] = win_in[(int64_t)r * DI];
+  } else if (wave == 3) {
+    const float* cw = a.prm.conv_w + ((int64_t)l * DI + c0 + lane) * W;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+      if (jj < W) r_cw[jj] = cw[jj];
+    if (a.prm.conv_b) r_cb = a.prm.conv_b[(int64_t)l * DI + c0 + lane];
+  }
+
+  // to LDS
+  if (tid < T) {
+    s_pparent[tid] = r_pp;
+    s_path[tid] = r_path;
+    s_parent[tid] = r_par;
+  }
+  if (tid == kCvWaves * kWave - 1) s_misc[3] = r_len;
+  if (xv < T) *reinterpret_cast<RawQ*>(s_xn + xv * kCvRows + xq) = rx;
+#pragma unroll
+  for (int it = 0; it < kCPT; ++it) {
+    const int ci = tid + it * kCvWaves * kWave, v = ci / kChunks, q = ci % kChunks;
+    if (v < T) {
+      *reinterpret_cast<u32x4*>(s_C + v * rs + q * 16) = rc[it];
+      *reinterpret_cast<u32x4*>(s_B + v * rs + q * 16) = rb[it];
+    }
+  }
+  if (wave < 2 && sv < T && sh < HW) {
+    const float dt = softplus_f32(r_dt + r_bias);
+    if (wave == 0) {
+      s_dt[sh * kCvT + sv] = dt;
+      s_S[sh * kCvT + sv] = dt * r_A;
+    } else {
+      s_dtp[sv * 4 + sh] = dt;
+      s_dAp[sv * 4 + sh] = expf(dt * r_A);
+    }
+  }
+  if (wave == 0 && lane < HW) s_D[lane] = r_D;
+  if (wave == 2) {
+#pragma unroll
+    for (int r = 0; r < 3; ++r)
+      if (r < W - 1) s_win[r * kCvRows + lane] = r_win[r];
+  } else if (wave == 3) {
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) s_cw[lane * 4 + jj] = r_cw[jj];
+    s_cb[lane] = r_cb;
+  }
+  __syncthreads();
+
+  // ======== trip 2: the path's x and B rows, gathered before validation ========
+  const int len_raw = s_misc[3];
+  const int lg = len_raw < 0 ? 0 : (len_raw > T ? T : len_raw);
+  RawQ rxp{};
+  if (xv < lg) {
+    const int v = s_path[xv];
+    const int vs = (v >= 0 && v < T) ? v : 0;  // an invalid path is discarded below
+    rxp = *reinterpret_cast<const RawQ*>(reinterpret_cast<const TIn*>(a.x_prev) + (unit * T + vs) * DI + c0 + xq);
+  }
+  u32x4 rbp[kCPT];
+  const unsigned char* Bpg = reinterpret_cast<const unsigned char*>(a.B_prev) + ((unit * T) * G + g) * (int64_t)N * E;
+#pragma unroll
+  for (int it = 0; it < kCPT; ++it) {
+    const int ci = tid + it * kCvWaves * kWave, q = ci / kChunks, ch = ci % kChunks;
+    if (q < lg) {
+      const int v = s_path[q];
+      const int vs = (v >= 0 && v < T) ? v : 0;
+      rbp[it] = *reinterpret_cast<const u32x4*>(Bpg + (int64_t)vs * G * N * E + ch * 16);
+    }
+  }
+
+  if (wave == 0) {
+    // both trees and the path, by ballot
+    bool bad_p = false, bad_n = false, bad_path = false;
+    if (lane < T) {
+      int p = s_pparent[lane];
+      bad_p = lane == 0 ? p != -1 : (p < -1 || p >= lane || p < s_pparent[lane - 1]);
+      p = s_parent[lane];
+      bad_n = lane == 0 ? p != -1 : (p < -1 || p >= lane || p < s_parent[lane - 1]);
+    }
+    if (lane < lg) {
+      const int v = s_path[lane];
+      bad_path = v < 0 || v >= T || s_pparent[v] != (lane == 0 ? -1 : s_path[lane - 1]);
+    }
+    const bool prev_ok = __ballot(bad_p) == 0, tree_ok = __ballot(bad_n) == 0;
+    const bool path_ok = len_raw >= 0 && len_raw <= T && __ballot(bad_path) == 0;
+    const int st = !prev_ok ? SSM_TREE_E_TREE : (!path_ok ? SSM_TREE_E_PATH : SSM_TREE_OK);
+    if (lane == 0) {
+      s_misc[0] = st == SSM_TREE_OK ? len_raw : 0;
+      s_misc[1] = st;
+      s_misc[2] = tree_ok ? 1 : 0;
+      if (blockIdx.x == 0 && l == 0) {
+        if (a.commit_status) a.commit_status[b] = st;
+        if (a.verify_status) a.verify_status[b] = tree_ok ? SSM_TREE_OK : SSM_TREE_E_TREE;
+      }
+    }
+  } else if (wave == 1) {
+    // C_v . B_u of the next tree: lane (u + 16 q) ends with CB[4 q + r][u]
+    f32x4 cbm = f32x4{0.f, 0.f, 0.f, 0.f};
+    const bool live = j < T;
+#pragma unroll
+    for (int gg = 0; gg < NG; ++gg) {
+      f32x4 cq = load4<TIn>(reinterpret_cast<const TIn*>(s_C + j * rs) + 16 * gg + 4 * k);
+      f32x4 bq = load4<TIn>(reinterpret_cast<const TIn*>(s_B + j * rs) + 16 * gg + 4 * k);
+      if (!live) cq = bq = f32x4{0.f, 0.f, 0.f, 0.f};
+      cbm = mfma4(cq.x, bq.x, cbm);
+      cbm = mfma4(cq.y, bq.y, cbm);
+      cbm = mfma4(cq.z, bq.z, cbm);
+      cbm = mfma4(cq.w, bq.w, cbm);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s_cbt[(4 * k + r) * kCvT + j] = cbm[r];
+  } else if (wave == 2 && lane < kCvT) {
+    // next tree: root-path set and conv inputs.  Every step requires
+    // -1 <= parent < node, so the walks end and stay in range even on an
+    // invalid tree (whose outputs are discarded).
+    int m = 0, packed = 0;
+    if (lane < T) {
+      int u = lane, a1 = -1, a2 = -1, a3 = -1;  // ancestors 1, 2, 3
+      int depth = 0;                            // nodes on the root path
+      for (int s = 0; s < kCvT && u >= 0; ++s) {
+        m |= 1 << u;
+        ++depth;
+        const int p = s_parent[u];
+        u = (p >= 0 && p < u) ? p : -1;
+        a1 = s == 0 ? u : a1;
+        a2 = s == 1 ? u : a2;
+        a3 = s == 2 ? u : a3;
+      }
+      // tap jj reads ancestor jj, or past the root window row W - 2 - (jj - depth)
+#pragma unroll
+      for (int jj = 1; jj < 4; ++jj) {
+        const int an = jj == 1 ? a1 : (jj == 2 ? a2 : a3);
+        const int code = an >= 0 ? an : T + (W - 2) - (jj - depth);
+        if (jj < W) packed |= code << (8 * (jj - 1));
+      }
+    }
+    s_anc[lane] = m;
+    s_cidx[lane] = packed;
+  }
+  if (xv < lg) *reinterpret_cast<RawQ*>(s_xp + xv * kCvRows + xq) = rxp;
+#pragma unroll
+  for (int it = 0; it < kCPT; ++it) {
+    const int ci = tid + it * kCvWaves * kWave, q = ci / kChunks, ch = ci % kChunks;
+    if (q < lg) *reinterpret_cast<u32x4*>(s_Bp + q * rs + ch * 16) = rbp[it];
+  }
+  __syncthreads();
+
+  // ======== from LDS: the path's conv and the new window; the next tree's
+  // S and conv outputs ========
+  const int len = s_misc[0];  // 0 when the commit fails: state and window pass through unchanged
+  if (wave == 0) {
+    const int c = c0 + lane, hh = c / P - h_lo;
+    float wj[4];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) wj[jj] = jj < W ? s_cw[lane * 4 + W - 1 - jj] : 0.0f;
+    const float cb = s_cb[lane];
+    float hist[3];  // raw inputs, newest first
+#pragma unroll
+    for (int r = 0; r < 3; ++r) hist[r] = r < W - 1 ? load_in(s_win, (W - 2 - r) * kCvRows + lane) : 0.0f;
+    for (int q = 0; q < len; ++q) {
+      const float xv = load_in(s_xp, q * kCvRows + lane);
+      float z = fmaf(wj[0], xv, cb);
+#pragma unroll
+      for (int jj = 1; jj < 4; ++jj)
+        if (jj < W) z = fmaf(wj[jj], hist[jj - 1], z);
+      const float xt = d.silu ? silu_f32(z) : z;
+      s_dtx[q * kCvRows + lane] = s_dtp[s_path[q] * 4 + hh] * xt;
+      hist[2] = hist[1];
+      hist[1] = hist[0];
+      hist[0] = xv;
+    }
+    // new window row r (oldest first) = element len + r of (old window, path x), bit for bit
+    if (W > 1) {
+      TIn* win_out = reinterpret_cast<TIn*>(a.window_out) + unit * (W - 1) * (int64_t)DI + c;
+#pragma unroll
+      for (int r = 0; r < 3; ++r) {
+        if (r < W - 1) {
+          const int e = len + r;
+          win_out[(int64_t)r * DI] = e < W - 1 ? s_win[e * kCvRows + lane] : s_xp[(e - (W - 1)) * kCvRows + lane];
+        }
+      }
+    }
+  } else if (wave == 1) {
+    const int hh = lane >> 4, v = lane & 15;
+    if (hh < HW) {
+      const int m = s_anc[v];
+      float acc = 0.0f;
+#pragma unroll
+      for (int u = 0; u < kCvT; ++u) acc += ((m >> u) & 1) ? s_S[hh * kCvT + u] : 0.0f;
+      s_S2[hh * kCvT + v] = acc * 1.4426950408889634f;
+    }
+  }
+  for (int i = tid; i < kCvT * kCvRows; i += kCvWaves * kWave) {
+    const int v = i / kCvRows, cl = i % kCvRows;
+    float xt = 0.0f;
+    if (v < T) {
+      float z = fmaf(s_cw[cl * 4 + W - 1], load_in(s_xn, v * kCvRows + cl), s_cb[cl]);
+      const int codes = s_cidx[v];
+      for (int jj = 1; jj < W; ++jj) {
+        const int code = (codes >> (8 * (jj - 1))) & 255;
+        float u;
+        if (code < T) {
+          u = load_in(s_xn, code * kCvRows + cl);
+        } else {  // committed window row code - T
+          const int e = len + code - T;
+          u = e < W - 1 ? load_in(s_win, e * kCvRows + cl) : load_in(s_xp, (e - (W - 1)) * kCvRows + cl);
+        }
+        z = fmaf(s_cw[cl * 4 + W - 1 - jj], u, z);
+      }
+      xt = d.silu ? silu_f32(z) : z;
+    }
+    // MFMA B-operand layout: channel row cl, quad v / 4 swizzled
+    s_xt[cl * kCvT + 4 * ((v >> 2) ^ ((cl >> 2) & 3)) + (v & 3)] = xt;
+  }
+  __syncthreads();
+
+  // ======== commit along the path, new state, next tree's y ========
+  {
+    const int row = wave * 16 + j;
+    const int hh = (c0 + wave * 16) / P - h_lo;  // the wave's head (P is a multiple of 16)
+    for (int q = 0; q < len; ++q) {
+      const float dA = s_dAp[s_path[q] * 4 + hh];
+      const float cx = s_dtx[q * kCvRows + row];
+      const TIn* bp = reinterpret_cast<const TIn*>(s_Bp + q * rs) + 4 * k;
+#pragma unroll
+      for (int gg = 0; gg < NG; ++gg) {
+        const f32x4 bq = load4<TIn>(bp + 16 * gg);
+        hq[gg].x = fmaf(dA, hq[gg].x, cx * bq.x);
+        hq[gg].y = fmaf(dA, hq[gg].y, cx * bq.y);
+        hq[gg].z = fmaf(dA, hq[gg].z, cx * bq.z);
+        hq[gg].w = fmaf(dA, hq[gg].w, cx * bq.w);
+      }
+    }
+    float* so = a.state_out + (unit * DI + c0 + row) * (int64_t)N + 4 * k;
+#pragma unroll
+    for (int gg = 0; gg < NG; ++gg) *reinterpret_cast<f32x4*>(so + 16 * gg) = hq[gg];
+
+    // C . h on the matrix cores: lane (c + 16 q) ends with (C_{4q+r} . h_c)
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    const bool live = j < T;
+    const TIn* cp = reinterpret_cast<const TIn*>(s_C + j * rs) + 4 * k;
+#pragma unroll
+    for (int gg = 0; gg < NG; ++gg) {
+      f32x4 cq = load4<TIn>(cp + 16 * gg);
+      if (!live) cq = f32x4{0.f, 0.f, 0.f, 0.f};
+      acc = mfma4(cq.x, hq[gg].x, acc);
+      acc = mfma4(cq.y, hq[gg].y, acc);
+      acc = mfma4(cq.z, hq[gg].z, acc);
+      acc = mfma4(cq.w, hq[gg].w, acc);
+    }
+    // then the path terms M[v][u] x~_u, with the diagonal D
+    const int i = j;
+    const float Sv = s_S2[hh * kCvT + i];
+    const f32x4 Sq = *reinterpret_cast<const f32x4*>(s_S2 + hh * kCvT + 4 * k);
+    const f32x4 dq = *reinterpret_cast<const f32x4*>(s_dt + hh * kCvT + 4 * k);
+    const f32x4 cbr = *reinterpret_cast<const f32x4*>(s_cbt + i * kCvT + 4 * k);
+    const int ancm = s_anc[i];
+    const float Dh = s_D[hh];
+    f32x4 mop, y;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const float mv = ((ancm >> (4 * k + t)) & 1) ? __builtin_amdgcn_exp2f(Sv - Sq[t]) * dq[t] * cbr[t] : 0.0f;
+      mop[t] = (4 * k + t == i) ? mv + Dh : mv;
+      y[t] = __builtin_amdgcn_exp2f(Sq[t]) * acc[t];
+    }
+    const f32x4 xq = *reinterpret_cast<const f32x4*>(s_xt + row * kCvT + 4 * (k ^ ((row >> 2) & 3)));
+    y = mfma4(mop.x, xq.x, y);
+    y = mfma4(mop.y, xq.y, y);
+    y = mfma4(mop.z, xq.z, y);
+    y = mfma4(mop.w, xq.w, y);
+    const bool tree_ok = s_misc[2] != 0;
+    // lane (c + 16 k) holds nodes 4 k + r of channel row
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s_ys[(4 * k + r) * kCvRows + row] = tree_ok ? y[r] : __builtin_nanf("");
+  }
+  __syncthreads();
+  {
+    const int v = tid / 16, q = tid % 16;  // node row, 16-byte chunk of the 256-byte row segment
+    if (v < T)
+      *reinterpret_cast<f32x4*>(a.y + (unit * T + v) * DI + c0 + 4 * q) =
+          *reinterpret_cast<const f32x4*>(s_ys + v * kCvRows + 4 * q);
+  }
+}
+
+namespace {
+
+template <typename TIn, int NG>
+int launch_cv_t(const CommitVerifyArgs& a, hipStream_t s) {
+  const size_t lds = (size_t)CvLds(16 * NG, (int)sizeof(TIn)).total;
+  if (allow_lds(commit_verify_kernel<TIn, NG>, lds) != hipSuccess) return SSM_TREE_E_HIP;
+  dim3 grid(a.d.d_in / kCvRows, a.d.Bsz, a.d.L);
+  hipLaunchKernelGGL((commit_verify_kernel<TIn, NG>), grid, dim3(kCvWaves * kWave), lds, s, a);
+  return hipGetLastError() == hipSuccess ? SSM_TREE_OK : SSM_TREE_E_HIP;
+}
+
+template <typename TIn>
+int launch_cv_in(const CommitVerifyArgs& a, hipStream_t s) {
+  switch (a.d.N) {
+    case 16: return launch_cv_t<TIn, 1>(a, s);
+    case 32: return launch_cv_t<TIn, 2>(a, s);
+    case 64: return launch_cv_t<TIn, 4>(a, s);
+    case 128: return launch_cv_t<TIn, 8>(a, s);
+    case 256: return launch_cv_t<TIn, 16>(a, s);
+    default: return SSM_TREE_E_DIMS;
+  }
+}
+
+}  // namespace
+
+bool commit_verify_fused_applies(const Dims& d) { return d.T >= 1 && d.T <= kCvT && d.P % 16 == 0; }
+
+int launch_commit_verify(const CommitVerifyArgs& a, bool bf16, hipStream_t s) {
+  return bf16 ? launch_cv_in<bf16_t>(a, s) : launch_cv_in<float>(a, s);
+}
+
+}  // namespace ssmt

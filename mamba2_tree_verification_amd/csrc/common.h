@@ -88,6 +88,30 @@ struct CommitArgs {
   int32_t* seq_status;
 };
 
+// commit of the previous tree's accepted path fused with verify of the next tree
+struct CommitVerifyArgs {
+  Dims d;
+  Params prm;
+  const int32_t* parent_prev;
+  const int32_t* path;
+  const int32_t* path_len;
+  const void* x_prev;
+  const void* B_prev;
+  const void* dt_prev;
+  const void* window_in;
+  const float* state_in;
+  void* window_out;
+  float* state_out;
+  const int32_t* parent;
+  const void* x;
+  const void* B;
+  const void* C;
+  const void* dt_raw;
+  float* y;
+  int32_t* commit_status;
+  int32_t* verify_status;
+};
+
 // Allow a kernel more than the default 64 KiB of dynamic LDS (gfx950 has
 // 160 KiB per CU).
 template <typename K>

@@ -21,8 +21,8 @@ def declared_functions():
 
 
 def test_header_declares_the_boundary():
-    assert declared_functions() == sorted(["ssm_tree_verify", "ssm_tree_commit", "ssm_tree_plan",
-                                           "ssm_tree_status_string", "ssm_tree_abi_version"])
+    assert declared_functions() == sorted(["ssm_tree_verify", "ssm_tree_commit", "ssm_tree_commit_verify",
+                                           "ssm_tree_plan", "ssm_tree_status_string", "ssm_tree_abi_version"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -140,6 +140,41 @@ def test_commit_host_checks():
     assert call_commit(d, p, win_out=fake(17, 4096)) == m.E_ALIAS           # window_out inside state_out
     assert call_commit(d, p, state_out=fake(17, 8)) == m.E_ALIGN
     assert call_commit(d, p, status=fake(17)) == m.E_ALIAS
+
+
+def call_commit_verify(dims, params, **kw):
+    a = dict(pparent=fake(1), path=fake(11), plen=fake(12), x_prev=fake(13), B_prev=fake(14), dt_prev=fake(15),
+             win_in=fake(6), state_in=fake(7), win_out=fake(16), state_out=fake(17), parent=fake(18), x=fake(2),
+             B=fake(3), C=fake(4), dt_raw=fake(5), y=fake(8), cst=fake(9), vst=fake(19))
+    a.update(kw)
+    return m.ssm_tree_commit_verify(dims, params, a["pparent"], a["path"], a["plen"], a["x_prev"], a["B_prev"],
+                                    a["dt_prev"], a["win_in"], a["state_in"], a["win_out"], a["state_out"],
+                                    a["parent"], a["x"], a["B"], a["C"], a["dt_raw"], a["y"], a["cst"], a["vst"],
+                                    None)
+
+
+@pytest.mark.parametrize("dkw", [dict(), dict(T=40), dict(H=8, P=40, N=16)])
+def test_commit_verify_host_checks(dkw):
+    # the same checks whichever way the call would run (fused kernel, or the two calls)
+    d, p = good_dims(**dkw), good_params()
+    for k in ("pparent", "path", "plen", "x_prev", "B_prev", "dt_prev", "state_in", "state_out", "parent", "x",
+              "B", "C", "dt_raw", "y", "win_in", "win_out"):
+        assert call_commit_verify(d, p, **{k: None}) == m.E_NULL, k
+    for k in ("pparent", "x_prev", "state_out", "C", "y", "cst", "vst", "win_out"):
+        assert call_commit_verify(d, p, **{k: fake(30, 8)}) == m.E_ALIGN, k
+    assert call_commit_verify(d, p, state_out=fake(7, 4096)) == m.E_ALIAS      # partial overlap with state_in
+    assert call_commit_verify(d, p, win_out=fake(6, 2048)) == m.E_ALIAS        # partial overlap with window_in
+    assert call_commit_verify(d, p, y=fake(7)) == m.E_ALIAS                    # y over state_in
+    assert call_commit_verify(d, p, y=fake(6)) == m.E_ALIAS                    # y over window_in
+    assert call_commit_verify(d, p, y=fake(17)) == m.E_ALIAS                   # y over state_out
+    assert call_commit_verify(d, p, state_out=fake(13)) == m.E_ALIAS           # over x_prev
+    assert call_commit_verify(d, p, win_out=fake(4)) == m.E_ALIAS              # over C
+    assert call_commit_verify(d, p, cst=fake(19)) == m.E_ALIAS                 # the two status arrays
+    assert call_commit_verify(d, p, vst=fake(1)) == m.E_ALIAS                  # status over parent_prev
+    assert call_commit_verify(d, good_params(A=None)) == m.E_NULL
+    bad = good_dims(**dkw)
+    bad.flags = 8
+    assert call_commit_verify(bad, p) == m.E_FLAGS
 
 
 def test_plan_host_checks():

@@ -1,0 +1,278 @@
+"""GPU parity of ssm_tree_commit_verify: the commit of one tree's accepted
+path followed by the verification of the next tree from the committed state
+and window (one decode step of the speculative loop, SpecMamba page
+sec. 3.1-3.2), against the float64 oracle's commit followed by its verify.
+
+Trees of 1..16 nodes with headdim % 16 == 0 take the fused kernel; other
+shapes and the FIFO flag take the two calls in turn.  Both are covered.
+Tolerance as elsewhere: |gpu - oracle| <= 1e-5 + 1e-4 |oracle| for y and
+the committed state; statuses and windows exactly.
+"""
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import mamba2_tree_verification_amd as m  # noqa: E402
+import oracle  # noqa: E402
+from testgen import as_f64  # noqa: E402
+from testgen import configs as C  # noqa: E402
+from testgen.device import tensor, upload  # noqa: E402
+from tests.gpu_util import assert_close, log, sample_units, window_f64  # noqa: E402
+from tests.test_gpu_parity import SMALL  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+NEXT_ONLY = ("state", "window", "A", "D", "dt_bias", "conv_w", "conv_b")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    m.load()
+
+
+def fused_applies(cfg):
+    return 1 <= cfg.T <= 16 and cfg.P % 16 == 0
+
+
+class Step:
+    """Previous tree (with its accepted path, root state, window and the
+    layer parameters) and the next tree (nodes only), on the GPU."""
+
+    def __init__(self, cfg, next_cid=None, prev=None, nxt=None, fifo=False):
+        self.cfg = cfg
+        self.prev = prev if prev is not None else C.make_inputs(cfg)
+        self.ncfg = cfg.replace(cid=cfg.cid + 500 if next_cid is None else next_cid)
+        self.nxt = nxt if nxt is not None else C.make_inputs(self.ncfg, skip=NEXT_ONLY)
+        self.gp = upload(self.prev)
+        self.gn = self._upload_next(self.nxt)
+        self.dims = m.make_dims(cfg.L, cfg.Bsz, cfg.T, cfg.H, cfg.P, cfg.N, cfg.G, cfg.W, cfg.bf16, cfg.silu, fifo)
+        g = self.gp
+        self.prm = m.make_params(g.A, g.D, g.dt_bias, g.conv_w, g.conv_b)
+
+    def _upload_next(self, nxt):
+        from types import SimpleNamespace
+        ns = SimpleNamespace()
+        ns.parent = torch.from_numpy(np.ascontiguousarray(nxt.parent, np.int32)).cuda()
+        for k in ("x", "B", "C", "dt_raw"):
+            setattr(ns, k, tensor(getattr(nxt, k), self.cfg.bf16))
+        return ns
+
+    def run(self, inplace=False, state=None, window=None, y=None):
+        cfg, gp, gn = self.cfg, self.gp, self.gn
+        s_in = gp.state if state is None else state
+        w_in = gp.window if window is None else window
+        if inplace:
+            s_out, w_out = s_in, w_in
+        else:
+            s_out = torch.full_like(s_in, -777.0)
+            w_out = None if w_in is None else torch.zeros_like(w_in)
+        if y is None:
+            y = torch.full((cfg.L, cfg.Bsz, cfg.T, cfg.d_in), float("nan"), dtype=torch.float32, device="cuda")
+        cst = torch.full((cfg.Bsz,), 12345, dtype=torch.int32, device="cuda")
+        vst = torch.full((cfg.Bsz,), 12345, dtype=torch.int32, device="cuda")
+        m.commit_verify(self.dims, self.prm, gp.parent, gp.path, gp.path_len, gp.x, gp.B, gp.dt_raw, w_in, s_in,
+                        w_out, s_out, gn.parent, gn.x, gn.B, gn.C, gn.dt_raw, y, cst, vst)
+        torch.cuda.synchronize()
+        return s_out, w_out, y, cst, vst
+
+    # -- oracle side --------------------------------------------------------
+    def next_unit(self, l, b, state, window, params):
+        shp = C.unit_shapes(self.cfg)
+        u = dict(params)
+        for k in ("x", "B", "C", "dt_raw"):
+            u[k] = as_f64(getattr(self.nxt, k)[l, b], self.cfg.bf16).reshape(shp[k])
+        u["state"] = state
+        u["window"] = window
+        return u
+
+    def oracle(self, units, threads=16):
+        """{(l, b): (state_out, window_out, commit status, y, verify status)}."""
+        cfg, prev, nxt = self.cfg, self.prev, self.nxt
+        o = oracle.get()
+        a = (cfg.H, cfg.P, cfg.N, cfg.G, cfg.W, cfg.silu)
+
+        def one(lb):
+            l, b = lb
+            u = C.unit_f64(cfg, l, b, prev)
+            n = int(prev.path_len[b])
+            so, wo, cst = o.commit(prev.parent[b], prev.path[b, :n], n, u, *a)
+            y, vst, _ = o.verify(nxt.parent[b], self.next_unit(l, b, so, wo, u), *a)
+            return lb, (so, wo, cst, y, vst)
+
+        with ThreadPoolExecutor(max_workers=threads) as ex:
+            return dict(ex.map(one, units))
+
+
+def check(step, out, units, state_in=None, window_in=None):
+    s_out, w_out, y, cst, vst = out
+    cfg = step.cfg
+    ref = step.oracle(units)
+    cs, vs = cst.cpu().numpy(), vst.cpu().numpy()
+    s_in = step.gp.state if state_in is None else state_in
+    w_in = step.gp.window if window_in is None else window_in
+    for (l, b), (so, wo, rc, yr, rv) in ref.items():
+        assert cs[b] == rc, ("commit status", b, cs[b], rc)
+        assert vs[b] == rv, ("verify status", b, vs[b], rv)
+        if rc == 0:
+            assert_close(s_out[l, b].double().cpu().numpy(), so, "%s state[l=%d,b=%d]" % (cfg.name, l, b))
+        else:  # passed through bit for bit
+            assert torch.equal(s_out[l, b].view(torch.int32), s_in[l, b].view(torch.int32)), (l, b)
+        if cfg.W > 1:
+            assert np.array_equal(window_f64(cfg, w_out, l, b), wo), "window l=%d b=%d" % (l, b)
+            if rc != 0:
+                assert torch.equal(w_out[l, b].view(torch.int16 if cfg.bf16 else torch.int32),
+                                   w_in[l, b].view(torch.int16 if cfg.bf16 else torch.int32))
+        yg = y[l, b].double().cpu().numpy()
+        if rv == 0:
+            assert_close(yg, yr, "%s y[l=%d,b=%d]" % (cfg.name, l, b))
+        else:
+            assert np.isnan(yg).all()
+
+
+# ----------------------------------------------------------------------------
+# the five workloads at full size (the 64-node stress trees take the two calls)
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("cid,k", [(0, 1), (1, 4), (2, 4), (3, 6), (4, 3)])
+def test_commit_verify_full_size(cid, k):
+    cfg = C.CONFIGS[cid]
+    log("commit_verify config %d %s (%s)" % (cid, cfg.name, "fused" if fused_applies(cfg) else "two calls"))
+    step = Step(cfg)
+    out = step.run()
+    assert not torch.isnan(out[2]).any(), "NaN in y"
+    rng = np.random.default_rng(300 + cid)
+    units = sample_units(cfg, k, rng, [(cfg.L - 1, cfg.Bsz - 1), (0, 0)])
+    log("commit_verify config %d: oracle on %d units" % (cid, len(units)))
+    check(step, out, units)
+
+
+@pytest.mark.parametrize("spec", SMALL, ids=lambda s: "L%dB%dT%dH%dP%dN%dG%dW%d%s%s%s" % (
+    s[0], s[1], s[2], s[3], s[4], s[5], s[6], s[7], "bf" if s[8] else "f32", "S" if s[9] else "",
+    "b" if s[10] else ""))
+def test_commit_verify_small_random(spec):
+    L, Bsz, T, H, P, N, G, W, bf16, silu, bias, tree = spec
+    cfg = C.Config(110 + SMALL.index(spec), "small", L, Bsz, T, H, P, N, G, W, bf16, 0.5, tree, silu, bias)
+    log("commit_verify small %s (%s)" % (spec, "fused" if fused_applies(cfg) else "two calls"))
+    step = Step(cfg)
+    check(step, step.run(), [(l, b) for l in range(L) for b in range(Bsz)])
+
+
+# ----------------------------------------------------------------------------
+# failures, in place, agreement with the separate calls, a multi-step loop
+# ----------------------------------------------------------------------------
+
+def _edge_cfg(**kw):
+    return C.Config(130, "edge", 2, 6, 12, 4, 64, 128, 1, 4, True, 0.5, "forest").replace(**kw)
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(T=24), dict(P=40, H=8)], ids=["fused", "T24", "P40"])
+@pytest.mark.parametrize("inplace", [False, True])
+def test_failed_commits_pass_state_through(kw, inplace):
+    cfg = _edge_cfg(**kw)
+    prev = C.make_inputs(cfg)
+    prev.parent[1, 3] = 5                      # previous tree invalid (forward reference)
+    prev.path_len[2] = cfg.T + 1               # path too long
+    v = int(np.nonzero(prev.parent[3] >= 0)[0][0])
+    prev.path[3, :2] = [v, 0]                  # first step not a root-level node
+    prev.path_len[3] = 2
+    step = Step(cfg, prev=prev)
+    step.nxt.parent[4, 2] = -2                 # next tree invalid
+    step.gn.parent.copy_(torch.from_numpy(step.nxt.parent))
+    s_in, w_in = step.gp.state.clone(), step.gp.window.clone()
+    out = step.run(inplace=inplace, state=s_in if inplace else None, window=w_in if inplace else None)
+    cs, vs = out[3].cpu().numpy(), out[4].cpu().numpy()
+    assert list(cs[1:4]) == [m.E_TREE, m.E_PATH, m.E_PATH], cs
+    assert vs[4] == m.E_TREE and (np.delete(vs, 4) == 0).all(), vs
+    check(step, out, [(l, b) for l in range(cfg.L) for b in range(cfg.Bsz)], state_in=step.gp.state,
+          window_in=step.gp.window)
+
+
+def test_inplace_equals_out_of_place():
+    cfg = _edge_cfg()
+    step = Step(cfg)
+    ref = step.run()
+    s_in, w_in = step.gp.state.clone(), step.gp.window.clone()
+    out = step.run(inplace=True, state=s_in, window=w_in)
+    assert out[0].data_ptr() == s_in.data_ptr()
+    for a, b in zip(ref, out):
+        assert torch.equal(a.view(torch.int32) if a.dtype == torch.float32 else a,
+                           b.view(torch.int32) if b.dtype == torch.float32 else b)
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(bf16=False, silu=True, conv_bias=True, N=64, W=3)])
+def test_fused_agrees_with_separate_calls(kw):
+    cfg = _edge_cfg(**kw)
+    step = Step(cfg)
+    s_f, w_f, y_f, cs_f, vs_f = step.run()
+    gp, gn = step.gp, step.gn
+    s_c = torch.empty_like(gp.state)
+    w_c = torch.empty_like(gp.window) if gp.window is not None else None
+    cs = torch.empty((cfg.Bsz,), dtype=torch.int32, device="cuda")
+    vs = torch.empty_like(cs)
+    y = torch.empty_like(y_f)
+    m.commit(step.dims, step.prm, gp.parent, gp.path, gp.path_len, gp.x, gp.B, gp.dt_raw, gp.window, gp.state,
+             w_c, s_c, cs)
+    m.verify(step.dims, step.prm, gn.parent, gn.x, gn.B, gn.C, gn.dt_raw, w_c, s_c, y, vs)
+    torch.cuda.synchronize()
+    assert torch.equal(cs, cs_f) and torch.equal(vs, vs_f)
+    if w_c is not None:
+        assert torch.equal(w_c, w_f)
+    assert_close(s_f.double().cpu().numpy(), s_c.double().cpu().numpy(), "state fused vs separate")
+    assert_close(y_f.double().cpu().numpy(), y.double().cpu().numpy(), "y fused vs separate")
+
+
+def test_fifo_flag_takes_the_two_calls():
+    cfg = _edge_cfg(Bsz=3)
+    a = Step(cfg).run()
+    b = Step(cfg, fifo=True).run()
+    assert torch.equal(a[1], b[1]) and torch.equal(a[3], b[3]) and torch.equal(a[4], b[4])
+    assert_close(b[0].double().cpu().numpy(), a[0].double().cpu().numpy(), "state fifo vs fused")
+    assert_close(b[2].double().cpu().numpy(), a[2].double().cpu().numpy(), "y fifo vs fused")
+
+
+@pytest.mark.parametrize("T", [16, 20])
+def test_three_tree_loop(T):
+    """Tree 1 -> (commit 1, verify 2) -> (commit 2, verify 3): the state
+    carried on the GPU in place through two fused steps equals the oracle's
+    commit / verify chain."""
+    cfg = _edge_cfg(Bsz=4, T=T)
+    s1 = Step(cfg, next_cid=901)
+    st, win = s1.gp.state.clone(), s1.gp.window.clone()
+    s1.run(inplace=True, state=st, window=win)
+    # step 2: tree 2 (with its own accepted path) is now the previous tree
+    t2 = C.make_inputs(s1.ncfg)
+    for k in NEXT_ONLY:  # the layer parameters stay those of step 1
+        setattr(t2, k, getattr(s1.prev, k))
+    s2 = Step(cfg, next_cid=902, prev=t2)
+    out = s2.run(inplace=True, state=st, window=win)
+    # oracle chain
+    o = oracle.get()
+    a = (cfg.H, cfg.P, cfg.N, cfg.G, cfg.W, cfg.silu)
+    for l in range(cfg.L):
+        for b in range(cfg.Bsz):
+            u1 = C.unit_f64(cfg, l, b, s1.prev)
+            n1 = int(s1.prev.path_len[b])
+            so1, wo1, c1 = o.commit(s1.prev.parent[b], s1.prev.path[b, :n1], n1, u1, *a)
+            u2 = s1.next_unit(l, b, so1, wo1, u1)
+            n2 = int(t2.path_len[b])
+            so2, wo2, c2 = o.commit(t2.parent[b], t2.path[b, :n2], n2, u2, *a)
+            y3, v3, _ = o.verify(s2.nxt.parent[b], s2.next_unit(l, b, so2, wo2, u1), *a)
+            assert c1 == 0 and c2 == 0 and v3 == 0
+            assert_close(out[0][l, b].double().cpu().numpy(), so2, "state after two steps l=%d b=%d" % (l, b))
+            assert np.array_equal(window_f64(cfg, out[1], l, b), wo2)
+            assert_close(out[2][l, b].double().cpu().numpy(), y3, "y of tree 3 l=%d b=%d" % (l, b))
+
+
+def test_zero_sizes():
+    for kw in (dict(L=0), dict(Bsz=0), dict(T=0)):
+        cfg = _edge_cfg(**kw)
+        step = Step(cfg)
+        s_out, w_out, y, cs, vs = step.run()
+        if cfg.L and cfg.Bsz:  # T = 0: nothing to commit, the state and window pass through
+            assert torch.equal(s_out, step.gp.state) and torch.equal(w_out, step.gp.window)
+            assert (cs.cpu().numpy() == 0).all() and (vs.cpu().numpy() == 0).all()
