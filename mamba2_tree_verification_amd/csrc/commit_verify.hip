@@ -22,8 +22,9 @@
 // Latency.  A workgroup's life is short (64 KiB of state in and out), so
 // the number of dependent trips to memory decides the throughput.  There
 // are two: every load that does not depend on the accepted path is issued
-// at entry (state, both trees' parent[], the next tree's x, B, C and dt
-// rows, the previous tree's dt rows, window, parameters); the path's x and
+// at entry (both trees' parent[], the next tree's x, B, C and dt rows, the
+// previous tree's dt rows, window, parameters, and the state last, so that
+// waiting for the small rows does not wait for it); the path's x and
 // B rows are gathered right after, from the unvalidated path, while one
 // wave validates the trees and the path with ballots, one forms C_v . B_u
 // and one the next tree's ancestor sets and conv taps.  Everything after
@@ -167,10 +168,6 @@ __global__ void __launch_bounds__(kCvWaves * kWave) commit_verify_kernel(CommitV
   const int rs = lo.row;
 
   // ======== trip 1: everything that does not depend on the path ========
-  const float* sin = a.state_in + (unit * DI + c0 + wave * 16 + j) * (int64_t)N + 4 * k;
-  f32x4 hq[NG];
-#pragma unroll
-  for (int gg = 0; gg < NG; ++gg) hq[gg] = *reinterpret_cast<const f32x4*>(sin + 16 * gg);
 
   int r_pp = 0, r_path = 0, r_par = 0, r_len = 0;
   if (tid < T) {
@@ -222,6 +219,13 @@ __global__ void __launch_bounds__(kCvWaves * kWave) commit_verify_kernel(CommitV
       if (jj < W) r_cw[jj] = cw[jj];
     if (a.prm.conv_b) r_cb = a.prm.conv_b[(int64_t)l * DI + c0 + lane];
   }
+
+  // the state last: the small rows above reach LDS while it is still in flight
+  // (loads complete in issue order)
+  const float* sin = a.state_in + (unit * DI + c0 + wave * 16 + j) * (int64_t)N + 4 * k;
+  f32x4 hq[NG];
+#pragma unroll
+  for (int gg = 0; gg < NG; ++gg) hq[gg] = *reinterpret_cast<const f32x4*>(sin + 16 * gg);
 
   // to LDS
   if (tid < T) {
