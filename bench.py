@@ -179,6 +179,52 @@ def cpu_baseline(cfg, inp, target_s=12.0, threads=16):
                                                               wall)}
 
 
+def per_layer_round(torch, m, cfg, g, g2, state, window, y, st_c, st_v, timed):
+    """The decode round as a model issues it: one ssm_tree_commit_verify call
+    per layer (L launches, each with L = 1), through the raw C entry point
+    with precomputed addresses, plain and replayed from a HIP graph captured
+    on a side stream.  Not part of the step; reported apart."""
+    dims1 = m.make_dims(1, cfg.Bsz, cfg.T, cfg.H, cfg.P, cfg.N, cfg.G, cfg.W, cfg.bf16, cfg.silu)
+    prms = [m.make_params(g.A[l], g.D[l], g.dt_bias[l], g.conv_w[l], None if g.conv_b is None else g.conv_b[l])
+            for l in range(cfg.L)]
+
+    def addr(t):
+        return None if t is None else t.data_ptr()
+
+    calls = [(prms[l], addr(g.parent), addr(g.path), addr(g.path_len), addr(g.x[l]), addr(g.B[l]),
+              addr(g.dt_raw[l]), addr(window[l]), addr(state[l]), addr(window[l]), addr(state[l]),
+              addr(g2.parent), addr(g2.x[l]), addr(g2.B[l]), addr(g2.C[l]), addr(g2.dt_raw[l]), addr(y[l]),
+              addr(st_c), addr(st_v)) for l in range(cfg.L)]
+
+    def round_():
+        hs = torch.cuda.current_stream().cuda_stream
+        for c in calls:
+            rc = m.ssm_tree_commit_verify(dims1, *c, hs)
+            if rc != m.OK:
+                raise m.SsmTreeError(rc, "ssm_tree_commit_verify")
+
+    plain = timed(round_)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        round_()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        round_()
+    torch.cuda.synchronize()
+    replay = timed(graph.replay)
+    node_layers = cfg.L * cfg.Bsz * cfg.T
+
+    def avg(v):
+        return sum(v) / len(v)
+
+    return {"launches": cfg.L, "plain_ms": round(avg(plain), 4), "graph_ms": round(avg(replay), 4),
+            "graph_node_layers_per_s": round(node_layers / (avg(replay) * 1e-3), 1),
+            "note": "one call per layer (L = 1 each); not in the step"}
+
+
 def hbm_probe(torch, nbytes=4 << 30, reps=10):
     """Plain device copy (torch copy_) and read (torch sum) bandwidth over
     buffers far larger than the 256 MB last-level cache."""
@@ -306,6 +352,8 @@ def main(argv=None):
     fifo_ms = timed(lambda: m.verify(dims_fifo, prm, g.parent, g.x, g.B, g.C, g.dt_raw, window, state, y, st_v),
                     reps=3)
 
+    per_layer = per_layer_round(torch, m, cfg, g, g2, state, window, y, st_c, st_v, timed)
+
     ab = algorithmic_bytes(cfg, inp.path_len)
     ab2 = algorithmic_bytes(cfg, inp2.path_len)
     # the step alternates which tree's path is committed: average the two
@@ -352,6 +400,7 @@ def main(argv=None):
         "roofline": dict(kern["commit_verify"]["roofline"], kernel="commit_verify"),
         "kernels": kern,
         "two_call_step_ms": round(avg(ver_ms) + avg(com_ms), 4),
+        "per_layer": per_layer,
         "param_bytes_per_call": ab["params"],
         "verify_hbm_frac": kern["verify"]["roofline"]["frac"],
     }

@@ -276,3 +276,43 @@ def test_zero_sizes():
         if cfg.L and cfg.Bsz:  # T = 0: nothing to commit, the state and window pass through
             assert torch.equal(s_out, step.gp.state) and torch.equal(w_out, step.gp.window)
             assert (cs.cpu().numpy() == 0).all() and (vs.cpu().numpy() == 0).all()
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(T=20)], ids=["fused", "two-calls"])
+def test_graph_replay_equals_eager(kw):
+    """One round captured in a HIP graph (in place on the state and window)
+    and replayed three times, with unrelated eager work and synchronisation
+    between replays, equals three eager rounds bit for bit after every
+    replay."""
+    cfg = _edge_cfg(Bsz=3, **kw)
+    step = Step(cfg)
+    s0, w0 = step.gp.state.clone(), step.gp.window.clone()
+    st, win = s0.clone(), w0.clone()
+    y = torch.empty((cfg.L, cfg.Bsz, cfg.T, cfg.d_in), dtype=torch.float32, device="cuda")
+    eager = []
+    for _ in range(3):
+        out = step.run(inplace=True, state=st, window=win, y=y)
+        eager.append([t.clone() for t in out])
+    st.copy_(s0)
+    win.copy_(w0)
+    y.fill_(0.0)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    gp, gn = step.gp, step.gn
+    cst = torch.empty((cfg.Bsz,), dtype=torch.int32, device="cuda")
+    vst = torch.empty_like(cst)
+    with torch.cuda.graph(graph, stream=side):
+        m.commit_verify(step.dims, step.prm, gp.parent, gp.path, gp.path_len, gp.x, gp.B, gp.dt_raw, win, st, win,
+                        st, gn.parent, gn.x, gn.B, gn.C, gn.dt_raw, y, cst, vst)
+    torch.cuda.synchronize()
+    assert torch.equal(st, s0), "capture must not execute the round"
+    for r in range(3):
+        graph.replay()
+        torch.cuda.synchronize()
+        for got, ref in zip((st, win, y, cst, vst), eager[r]):
+            assert torch.equal(got.view(torch.int32) if got.dtype == torch.float32 else got,
+                               ref.view(torch.int32) if ref.dtype == torch.float32 else ref), ("replay", r)
+        junk = torch.randn(1 << 20, device="cuda")  # unrelated eager work between replays
+        assert torch.isfinite(junk.sum())
+        torch.cuda.synchronize()
