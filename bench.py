@@ -225,6 +225,66 @@ def per_layer_round(torch, m, cfg, g, g2, state, window, y, st_c, st_v, timed):
             "note": "one call per layer (L = 1 each); not in the step"}
 
 
+def draft_decode(torch, m, C, upload, threads, timed, steps=15):
+    """The draft side (SpecMamba page sec. 3.1) on the Mamba2-370M draft
+    shape (48 layers, batch 1): tokens decoded one at a time, each a
+    one-node ssm_tree_commit_verify round that commits the previous token
+    into the working state (in place) and emits the new token's y.  A chain
+    of steps + 1 tokens is the per-token log.  Plain launches through the
+    raw entry point, and the whole chain replayed from a HIP graph."""
+    cfg = C.CONFIGS[1]
+    inp = C.make_inputs(cfg, nthreads=threads)
+    g = upload(inp)
+    dims1 = m.make_dims(cfg.L, cfg.Bsz, 1, cfg.H, cfg.P, cfg.N, cfg.G, cfg.W, cfg.bf16, cfg.silu)
+    prm = m.make_params(g.A, g.D, g.dt_bias, g.conv_w, g.conv_b)
+    one = torch.full((cfg.Bsz, 1), -1, dtype=torch.int32, device="cuda")
+    path0 = torch.zeros((cfg.Bsz, 1), dtype=torch.int32, device="cuda")
+    plen = torch.ones((cfg.Bsz,), dtype=torch.int32, device="cuda")
+    tok = {k: [t[:, :, i:i + 1].contiguous() for i in range(cfg.T)] for k, t in
+           (("x", g.x), ("B", g.B), ("C", g.C), ("dt", g.dt_raw))}
+    y = torch.empty((cfg.L, cfg.Bsz, 1, cfg.d_in), dtype=torch.float32, device="cuda")
+    cst = torch.empty((cfg.Bsz,), dtype=torch.int32, device="cuda")
+    vst = torch.empty_like(cst)
+    st, win = g.state, g.window
+    calls = [(prm, one.data_ptr(), path0.data_ptr(), plen.data_ptr(), tok["x"][k - 1].data_ptr(),
+              tok["B"][k - 1].data_ptr(), tok["dt"][k - 1].data_ptr(), win.data_ptr(), st.data_ptr(), win.data_ptr(),
+              st.data_ptr(), one.data_ptr(), tok["x"][k].data_ptr(), tok["B"][k].data_ptr(), tok["C"][k].data_ptr(),
+              tok["dt"][k].data_ptr(), y.data_ptr(), cst.data_ptr(), vst.data_ptr()) for k in range(1, steps + 1)]
+
+    def chain():
+        hs = torch.cuda.current_stream().cuda_stream
+        for c in calls:
+            rc = m.ssm_tree_commit_verify(dims1, *c, hs)
+            if rc != m.OK:
+                raise m.SsmTreeError(rc, "ssm_tree_commit_verify")
+
+    plain = timed(chain)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        chain()
+    torch.cuda.synchronize()
+    replay = timed(graph.replay)
+    torch.cuda.synchronize()
+    if not (cst.cpu() == 0).all() or not (vst.cpu() == 0).all() or torch.isnan(y).any():
+        raise SystemExit("bench: draft decode produced a bad status or NaN")
+    e = cfg.e
+    per_layer = (2 * cfg.H * cfg.P * cfg.N * 4 + 2 * (cfg.W - 1) * cfg.d_in * e +
+                 (cfg.d_in * e + cfg.G * cfg.N * e + cfg.H * e) +
+                 (cfg.d_in * e + 2 * cfg.G * cfg.N * e + cfg.H * e + cfg.d_in * 4))
+    token_bytes = cfg.L * cfg.Bsz * per_layer
+
+    def avg(v):
+        return sum(v) / len(v)
+
+    tp, tg = avg(plain) / steps, avg(replay) / steps
+    return {"workload": cfg.name, "layers": cfg.L, "batch": cfg.Bsz, "bytes_per_token": token_bytes,
+            "plain_us_per_token": round(tp * 1e3, 2), "graph_us_per_token": round(tg * 1e3, 2),
+            "graph_tokens_per_s": round(1e3 / tg, 1), "graph_GBps": round(token_bytes / (tg * 1e-3) / 1e9, 1),
+            "note": "one-node ssm_tree_commit_verify per draft token (all layers in one call); not in the step"}
+
+
 def hbm_probe(torch, nbytes=4 << 30, reps=10):
     """Plain device copy (torch copy_) and read (torch sum) bandwidth over
     buffers far larger than the 256 MB last-level cache."""
@@ -353,6 +413,7 @@ def main(argv=None):
                     reps=3)
 
     per_layer = per_layer_round(torch, m, cfg, g, g2, state, window, y, st_c, st_v, timed)
+    draft = draft_decode(torch, m, C, upload, args.threads, timed)
 
     ab = algorithmic_bytes(cfg, inp.path_len)
     ab2 = algorithmic_bytes(cfg, inp2.path_len)
@@ -401,6 +462,7 @@ def main(argv=None):
         "kernels": kern,
         "two_call_step_ms": round(avg(ver_ms) + avg(com_ms), 4),
         "per_layer": per_layer,
+        "draft_decode": draft,
         "param_bytes_per_call": ab["params"],
         "verify_hbm_frac": kern["verify"]["roofline"]["frac"],
     }

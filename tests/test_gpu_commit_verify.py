@@ -316,3 +316,61 @@ def test_graph_replay_equals_eager(kw):
         junk = torch.randn(1 << 20, device="cuda")  # unrelated eager work between replays
         assert torch.isfinite(junk.sum())
         torch.cuda.synchronize()
+
+
+def _token(t, k):
+    """Node k of a [L][Bsz][T][...] tensor as a one-node tree [L][Bsz][1][...]."""
+    return t[:, :, k:k + 1].contiguous()
+
+
+@pytest.mark.parametrize("bf16", [True, False])
+def test_draft_decode_then_rollback(bf16):
+    """The draft side of speculative decoding (SpecMamba page sec. 3.1): K
+    tokens decoded one at a time, each step a one-node round that commits
+    the previous token into a working state and emits the new token's y;
+    their x, B, dt_raw stay in a per-token log.  Rollback is a commit of
+    the accepted prefix of the chain from the root state.  Both against the
+    oracle's plain sequential scan."""
+    K = 7
+    cfg = C.Config(140, "draft", 3, 2, K, 8, 64, 128, 1, 4, bf16, 0.5, "chain")
+    log_inp = C.make_inputs(cfg)  # the log: a chain of K tokens per sequence
+    g = upload(log_inp)
+    dims1 = m.make_dims(cfg.L, cfg.Bsz, 1, cfg.H, cfg.P, cfg.N, cfg.G, cfg.W, cfg.bf16)
+    prm = m.make_params(g.A, g.D, g.dt_bias, g.conv_w, None)
+    one = torch.tensor([[-1]] * cfg.Bsz, dtype=torch.int32, device="cuda")
+    path0 = torch.zeros((cfg.Bsz, 1), dtype=torch.int32, device="cuda")
+    work_s, work_w = torch.empty_like(g.state), torch.empty_like(g.window)
+    cst = torch.empty((cfg.Bsz,), dtype=torch.int32, device="cuda")
+    vst = torch.empty_like(cst)
+    ys = []
+    for k in range(K):
+        plen = torch.full((cfg.Bsz,), 1 if k else 0, dtype=torch.int32, device="cuda")
+        kp = max(k - 1, 0)
+        y = torch.empty((cfg.L, cfg.Bsz, 1, cfg.d_in), dtype=torch.float32, device="cuda")
+        s_in, w_in = (g.state, g.window) if k == 0 else (work_s, work_w)
+        m.commit_verify(dims1, prm, one, path0, plen, _token(g.x, kp), _token(g.B, kp), _token(g.dt_raw, kp), w_in,
+                        s_in, work_w, work_s, one, _token(g.x, k), _token(g.B, k), _token(g.C, k),
+                        _token(g.dt_raw, k), y, cst, vst)
+        torch.cuda.synchronize()
+        assert (cst.cpu().numpy() == 0).all() and (vst.cpu().numpy() == 0).all()
+        ys.append(y[:, :, 0].double().cpu().numpy())
+    # rollback: commit the accepted prefix of the logged chain from the root state
+    acc = np.array([3, K][:cfg.Bsz], np.int32)
+    path = torch.from_numpy(np.tile(np.arange(K, dtype=np.int32), (cfg.Bsz, 1))).cuda()
+    plen = torch.from_numpy(acc).cuda()
+    dimsK = m.make_dims(cfg.L, cfg.Bsz, K, cfg.H, cfg.P, cfg.N, cfg.G, cfg.W, cfg.bf16)
+    s_out, w_out = torch.empty_like(g.state), torch.empty_like(g.window)
+    m.commit(dimsK, prm, g.parent, path, plen, g.x, g.B, g.dt_raw, g.window, g.state, w_out, s_out, cst)
+    torch.cuda.synchronize()
+    assert (cst.cpu().numpy() == 0).all()
+    o = oracle.get()
+    for l in range(cfg.L):
+        for b in range(cfg.Bsz):
+            u = C.unit_f64(cfg, l, b, log_inp)
+            y_scan, s_scan, w_scan = o.scan(u, K, cfg.H, cfg.P, cfg.N, cfg.G, cfg.W)
+            for k in range(K):
+                assert_close(ys[k][l, b], y_scan[k], "draft token %d l=%d b=%d" % (k, l, b))
+            n = int(acc[b])
+            _, s_pref, w_pref = o.scan(u, n, cfg.H, cfg.P, cfg.N, cfg.G, cfg.W)
+            assert_close(s_out[l, b].double().cpu().numpy(), s_pref, "rollback state l=%d b=%d" % (l, b))
+            assert np.array_equal(window_f64(cfg, w_out, l, b), w_pref), "rollback window l=%d b=%d" % (l, b)
