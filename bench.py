@@ -191,9 +191,9 @@ def per_layer_round(torch, m, cfg, g, g2, state, window, y, st_c, st_v, timed):
     def addr(t):
         return None if t is None else t.data_ptr()
 
-    calls = [(prms[l], addr(g.parent), addr(g.path), addr(g.path_len), addr(g.x[l]), addr(g.B[l]),
+    calls = [(prms[l], addr(g.parent), addr(g.path), addr(g.path_len), addr(g.x[l]), addr(g.B[l]), None,
               addr(g.dt_raw[l]), addr(window[l]), addr(state[l]), addr(window[l]), addr(state[l]),
-              addr(g2.parent), addr(g2.x[l]), addr(g2.B[l]), addr(g2.C[l]), addr(g2.dt_raw[l]), addr(y[l]),
+              addr(g2.parent), addr(g2.x[l]), addr(g2.B[l]), addr(g2.C[l]), addr(g2.dt_raw[l]), None, addr(y[l]),
               addr(st_c), addr(st_v)) for l in range(cfg.L)]
 
     def round_():
@@ -247,9 +247,10 @@ def draft_decode(torch, m, C, upload, threads, timed, steps=15):
     vst = torch.empty_like(cst)
     st, win = g.state, g.window
     calls = [(prm, one.data_ptr(), path0.data_ptr(), plen.data_ptr(), tok["x"][k - 1].data_ptr(),
-              tok["B"][k - 1].data_ptr(), tok["dt"][k - 1].data_ptr(), win.data_ptr(), st.data_ptr(), win.data_ptr(),
-              st.data_ptr(), one.data_ptr(), tok["x"][k].data_ptr(), tok["B"][k].data_ptr(), tok["C"][k].data_ptr(),
-              tok["dt"][k].data_ptr(), y.data_ptr(), cst.data_ptr(), vst.data_ptr()) for k in range(1, steps + 1)]
+              tok["B"][k - 1].data_ptr(), None, tok["dt"][k - 1].data_ptr(), win.data_ptr(), st.data_ptr(),
+              win.data_ptr(), st.data_ptr(), one.data_ptr(), tok["x"][k].data_ptr(), tok["B"][k].data_ptr(),
+              tok["C"][k].data_ptr(), tok["dt"][k].data_ptr(), None, y.data_ptr(), cst.data_ptr(),
+              vst.data_ptr()) for k in range(1, steps + 1)]
 
     def chain():
         hs = torch.cuda.current_stream().cuda_stream

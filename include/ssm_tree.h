@@ -21,7 +21,9 @@
  *   h_t = Abar (.) h_{t-1} + Bbar (.) X_t.
  *
  * Per (layer l, sequence b, node v, head h, headdim row p, state index n),
- * with g = h / (H / G) and c = h * P + p:
+ * with g = h / (H / G) and c = h * P + p (shown for the default conv over
+ * x; SSM_TREE_CONV_XBC convolves B and C the same way, and a gate input z
+ * multiplies y by silu(z)):
  *   dt_v[h]  = softplus(dt_raw_v[h] + dt_bias[h])   (softplus(z) = z, z > 20)
  *   dA_v[h]  = exp(dt_v[h] * A[h])
  *   x~_v[c]  = act(conv_b[c] + sum_{j<W} conv_w[c][W-1-j] * u_j[c])
@@ -54,7 +56,7 @@
 extern "C" {
 #endif
 
-#define SSM_TREE_ABI_VERSION 1
+#define SSM_TREE_ABI_VERSION 2
 
 /* input element types for x, B, C, dt_raw and the conv window */
 #define SSM_TREE_F32 0
@@ -62,6 +64,14 @@ extern "C" {
 
 /* dims.flags */
 #define SSM_TREE_CONV_SILU 1 /* SiLU after the conv (Mamba2 checkpoints use it; the pages name no activation) */
+/* The causal conv runs over x, B and C (the Mamba2 convention: in_proj's
+ * xBC passes conv1d as a whole) instead of over x only.  The conv window,
+ * conv_w and conv_b then span CH = H*P + 2*G*N channels in the order x,
+ * B [G][N], C [G][N]; the SSM uses the convolved B and C.  Supported by the
+ * trees of at most 16 nodes with a headdim that is a multiple of 16 in
+ * ssm_tree_verify and ssm_tree_commit_verify, and by ssm_tree_commit for
+ * every supported shape; other combinations return SSM_TREE_E_DIMS. */
+#define SSM_TREE_CONV_XBC 4
 /* ssm_tree_verify computes every child state explicitly, walking the tree
  * breadth-first with a FIFO of live states (SpecMamba page sec. 3.2), instead
  * of the default root projection.  Same outputs up to fp32 rounding; slower.
@@ -93,7 +103,7 @@ typedef struct ssm_tree_dims {
   int32_t ngroups;    /* G : B and C are shared by H/G consecutive heads */
   int32_t conv_width; /* W */
   int32_t in_dtype;   /* SSM_TREE_F32 or SSM_TREE_BF16 */
-  int32_t flags;      /* 0 or SSM_TREE_CONV_SILU | SSM_TREE_VERIFY_FIFO */
+  int32_t flags;      /* 0 or SSM_TREE_CONV_SILU | SSM_TREE_VERIFY_FIFO | SSM_TREE_CONV_XBC */
 } ssm_tree_dims;
 
 /* Per-layer parameters, float32 device pointers. */
@@ -101,8 +111,9 @@ typedef struct ssm_tree_params {
   const float* A;       /* [L][H]        decay rate per head (negative in Mamba2) */
   const float* D;       /* [L][H]        skip weight per head */
   const float* dt_bias; /* [L][H] */
-  const float* conv_w;  /* [L][H*P][W]   depthwise conv weights, tap W-1 = current token */
-  const float* conv_b;  /* [L][H*P]      or NULL for no conv bias */
+  const float* conv_w;  /* [L][CH][W]    depthwise conv weights, tap W-1 = current token;
+                           CH = H*P, or H*P + 2*G*N with SSM_TREE_CONV_XBC */
+  const float* conv_b;  /* [L][CH]       or NULL for no conv bias */
 } ssm_tree_params;
 
 /*
@@ -115,8 +126,13 @@ typedef struct ssm_tree_params {
  * x           [L][Bsz][T][H*P]   in_dtype   per-node conv input
  * B, C        [L][Bsz][T][G][N]  in_dtype
  * dt_raw      [L][Bsz][T][H]     in_dtype   step size before bias/softplus
- * conv_window [L][Bsz][W-1][H*P] in_dtype   raw x of the last W-1 committed
- *             tokens, oldest row first (may be NULL when W == 1)
+ * z           [L][Bsz][T][H*P]   in_dtype   gate input, or NULL for no gate:
+ *             y = (C . h + D x~) * silu(z) ([LM] "why Mamba is hard to
+ *             accelerate": Y is multiplied elementwise with Z).  Supported
+ *             with the same shapes as SSM_TREE_CONV_XBC.
+ * conv_window [L][Bsz][W-1][CH]  in_dtype   raw conv inputs (x, and B and C
+ *             with SSM_TREE_CONV_XBC) of the last W-1 committed tokens,
+ *             oldest row first (may be NULL when W == 1)
  * state       [L][Bsz][H][P][N]  float32    root SSM state (read only)
  * y           [L][Bsz][T][H][P]  float32    out; must not overlap any input
  * seq_status  [Bsz] int32 out, or NULL.  SSM_TREE_OK or SSM_TREE_E_TREE;
@@ -125,8 +141,8 @@ typedef struct ssm_tree_params {
  * Child states are never written to memory: the root state is read once.
  */
 int ssm_tree_verify(const ssm_tree_dims* dims, const ssm_tree_params* params, const int32_t* parent,
-                    const void* x, const void* B, const void* C, const void* dt_raw, const void* conv_window,
-                    const float* state, float* y, int32_t* seq_status, void* hip_stream);
+                    const void* x, const void* B, const void* C, const void* dt_raw, const void* z,
+                    const void* conv_window, const float* state, float* y, int32_t* seq_status, void* hip_stream);
 
 /*
  * ssm_tree_commit: advance the root state and conv window along the
@@ -137,8 +153,11 @@ int ssm_tree_verify(const ssm_tree_dims* dims, const ssm_tree_params* params, co
  *             ... (entries past len are ignored)
  * path_len    [Bsz] int32, 0 <= len <= T (0 = keep state and window)
  * x, B, dt_raw, conv_window_in, state_in: as for ssm_tree_verify
- * conv_window_out [L][Bsz][W-1][H*P] in_dtype: last W-1 rows of
- *             (old window, x of each path node), copied bit for bit
+ * C           as for ssm_tree_verify; read only with SSM_TREE_CONV_XBC (for
+ *             the window) and may be NULL otherwise
+ * conv_window_out [L][Bsz][W-1][CH] in_dtype: last W-1 rows of
+ *             (old window, raw conv inputs of each path node), copied bit
+ *             for bit
  * state_out   [L][Bsz][H][P][N] float32: state of the last path node
  * Outputs may equal the matching input exactly (in place); any other
  * overlap is SSM_TREE_E_ALIAS.
@@ -146,9 +165,9 @@ int ssm_tree_verify(const ssm_tree_dims* dims, const ssm_tree_params* params, co
  *             a failed sequence's outputs are left unwritten.
  */
 int ssm_tree_commit(const ssm_tree_dims* dims, const ssm_tree_params* params, const int32_t* parent,
-                    const int32_t* path, const int32_t* path_len, const void* x, const void* B, const void* dt_raw,
-                    const void* conv_window_in, const float* state_in, void* conv_window_out, float* state_out,
-                    int32_t* seq_status, void* hip_stream);
+                    const int32_t* path, const int32_t* path_len, const void* x, const void* B, const void* C,
+                    const void* dt_raw, const void* conv_window_in, const float* state_in, void* conv_window_out,
+                    float* state_out, int32_t* seq_status, void* hip_stream);
 
 /*
  * ssm_tree_commit_verify: ssm_tree_commit of the previous tree's accepted
@@ -156,12 +175,13 @@ int ssm_tree_commit(const ssm_tree_dims* dims, const ssm_tree_params* params, co
  * and window, in one pass over the root state (it is read and written once
  * instead of being read by verify and read and written by commit).
  *
- * parent_prev, path, path_len, x_prev, B_prev, dt_raw_prev: the previous
- *             tree and its accepted path, as for ssm_tree_commit
+ * parent_prev, path, path_len, x_prev, B_prev, C_prev, dt_raw_prev: the
+ *             previous tree and its accepted path, as for ssm_tree_commit
+ *             (C_prev read only with SSM_TREE_CONV_XBC, may be NULL otherwise)
  * conv_window_in, state_in -> conv_window_out, state_out: as for
  *             ssm_tree_commit (exact in-place allowed)
- * parent, x, B, C, dt_raw: the next tree, as for ssm_tree_verify (same
- *             dims: T nodes)
+ * parent, x, B, C, dt_raw, z: the next tree, as for ssm_tree_verify (same
+ *             dims: T nodes; z NULL for no gate)
  * y           [L][Bsz][T][H*P] float32 out: the next tree's outputs
  * commit_status [Bsz] or NULL: as ssm_tree_commit's seq_status.  A sequence
  *             whose commit fails gets its state_in and conv_window_in copied
@@ -178,10 +198,10 @@ int ssm_tree_commit(const ssm_tree_dims* dims, const ssm_tree_params* params, co
  */
 int ssm_tree_commit_verify(const ssm_tree_dims* dims, const ssm_tree_params* params, const int32_t* parent_prev,
                            const int32_t* path, const int32_t* path_len, const void* x_prev, const void* B_prev,
-                           const void* dt_raw_prev, const void* conv_window_in, const float* state_in,
-                           void* conv_window_out, float* state_out, const int32_t* parent, const void* x,
-                           const void* B, const void* C, const void* dt_raw, float* y, int32_t* commit_status,
-                           int32_t* verify_status, void* hip_stream);
+                           const void* C_prev, const void* dt_raw_prev, const void* conv_window_in,
+                           const float* state_in, void* conv_window_out, float* state_out, const int32_t* parent,
+                           const void* x, const void* B, const void* C, const void* dt_raw, const void* z,
+                           float* y, int32_t* commit_status, int32_t* verify_status, void* hip_stream);
 
 /*
  * ssm_tree_plan: the tree plan the kernels derive from parent[] (SpecMamba

@@ -18,10 +18,11 @@ import threading
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libssm_tree.so")
 
-SSM_TREE_ABI_VERSION = 1
+SSM_TREE_ABI_VERSION = 2
 SSM_TREE_F32, SSM_TREE_BF16 = 0, 1
 SSM_TREE_CONV_SILU = 1
 SSM_TREE_VERIFY_FIFO = 2
+SSM_TREE_CONV_XBC = 4
 OK, E_NULL, E_ALIGN, E_DIMS, E_DTYPE, E_ALIAS, E_HIP, E_FLAGS = 0, -1, -2, -3, -4, -5, -6, -7
 E_TREE, E_PATH = -10, -11
 PLAN_HEADER, PLAN_STRIDE, PLAN_UNUSED = 4, 8, -32768
@@ -60,11 +61,11 @@ def load():
             raise RuntimeError("libssm_tree.so is not built: run __graft_entry__.build() (hipcc, gfx950)")
         L = ctypes.CDLL(LIB_PATH)
         p, i = ctypes.c_void_p, ctypes.c_int
-        L.ssm_tree_verify.argtypes = [p] * 12
+        L.ssm_tree_verify.argtypes = [p] * 13
         L.ssm_tree_verify.restype = i
-        L.ssm_tree_commit.argtypes = [p] * 14
+        L.ssm_tree_commit.argtypes = [p] * 15
         L.ssm_tree_commit.restype = i
-        L.ssm_tree_commit_verify.argtypes = [p] * 21
+        L.ssm_tree_commit_verify.argtypes = [p] * 23
         L.ssm_tree_commit_verify.restype = i
         L.ssm_tree_plan.argtypes = [p] * 4
         L.ssm_tree_plan.restype = i
@@ -82,25 +83,25 @@ def load():
 # one-to-one wrappers of the C entry points (raw addresses, ints or None)
 # ---------------------------------------------------------------------------
 
-def ssm_tree_verify(dims: Dims, params: Params, parent, x, B, C, dt_raw, conv_window, state, y, seq_status,
+def ssm_tree_verify(dims: Dims, params: Params, parent, x, B, C, dt_raw, z, conv_window, state, y, seq_status,
                     hip_stream) -> int:
-    return load().ssm_tree_verify(ctypes.byref(dims), ctypes.byref(params), parent, x, B, C, dt_raw, conv_window,
+    return load().ssm_tree_verify(ctypes.byref(dims), ctypes.byref(params), parent, x, B, C, dt_raw, z, conv_window,
                                   state, y, seq_status, hip_stream)
 
 
-def ssm_tree_commit(dims: Dims, params: Params, parent, path, path_len, x, B, dt_raw, conv_window_in, state_in,
+def ssm_tree_commit(dims: Dims, params: Params, parent, path, path_len, x, B, C, dt_raw, conv_window_in, state_in,
                     conv_window_out, state_out, seq_status, hip_stream) -> int:
-    return load().ssm_tree_commit(ctypes.byref(dims), ctypes.byref(params), parent, path, path_len, x, B, dt_raw,
+    return load().ssm_tree_commit(ctypes.byref(dims), ctypes.byref(params), parent, path, path_len, x, B, C, dt_raw,
                                   conv_window_in, state_in, conv_window_out, state_out, seq_status, hip_stream)
 
 
-def ssm_tree_commit_verify(dims: Dims, params: Params, parent_prev, path, path_len, x_prev, B_prev, dt_raw_prev,
-                           conv_window_in, state_in, conv_window_out, state_out, parent, x, B, C, dt_raw, y,
-                           commit_status, verify_status, hip_stream) -> int:
+def ssm_tree_commit_verify(dims: Dims, params: Params, parent_prev, path, path_len, x_prev, B_prev, C_prev,
+                           dt_raw_prev, conv_window_in, state_in, conv_window_out, state_out, parent, x, B, C, dt_raw,
+                           z, y, commit_status, verify_status, hip_stream) -> int:
     return load().ssm_tree_commit_verify(ctypes.byref(dims), ctypes.byref(params), parent_prev, path, path_len,
-                                         x_prev, B_prev, dt_raw_prev, conv_window_in, state_in, conv_window_out,
-                                         state_out, parent, x, B, C, dt_raw, y, commit_status, verify_status,
-                                         hip_stream)
+                                         x_prev, B_prev, C_prev, dt_raw_prev, conv_window_in, state_in,
+                                         conv_window_out, state_out, parent, x, B, C, dt_raw, z, y, commit_status,
+                                         verify_status, hip_stream)
 
 
 def ssm_tree_plan(dims: Dims, parent, plan_out, hip_stream) -> int:
@@ -132,9 +133,11 @@ def _stream(stream):
     return s.cuda_stream
 
 
-def make_dims(L, Bsz, T, H, P, N, G, W, bf16: bool, silu: bool = False, fifo: bool = False) -> Dims:
+def make_dims(L, Bsz, T, H, P, N, G, W, bf16: bool, silu: bool = False, fifo: bool = False,
+              xbc: bool = False) -> Dims:
     return Dims(L, Bsz, T, H, P, N, G, W, SSM_TREE_BF16 if bf16 else SSM_TREE_F32,
-                (SSM_TREE_CONV_SILU if silu else 0) | (SSM_TREE_VERIFY_FIFO if fifo else 0))
+                (SSM_TREE_CONV_SILU if silu else 0) | (SSM_TREE_VERIFY_FIFO if fifo else 0) |
+                (SSM_TREE_CONV_XBC if xbc else 0))
 
 
 def make_params(A, D, dt_bias, conv_w, conv_b=None) -> Params:
@@ -157,41 +160,47 @@ def _check(t, kind):
 
 
 def verify(dims: Dims, params: Params, parent, x, B, C, dt_raw, conv_window, state, y, seq_status=None,
-           stream=None):
-    for t, k in ((parent, "int32"), (x, "in"), (B, "in"), (C, "in"), (dt_raw, "in"), (conv_window, "in"),
-                 (state, "float32"), (y, "float32"), (seq_status, "int32")):
+           stream=None, z=None):
+    """ssm_tree_verify; z (optional) gates y by silu(z)."""
+    for t, k in ((parent, "int32"), (x, "in"), (B, "in"), (C, "in"), (dt_raw, "in"), (z, "in"),
+                 (conv_window, "in"), (state, "float32"), (y, "float32"), (seq_status, "int32")):
         _check(t, k)
-    rc = ssm_tree_verify(dims, params, _ptr(parent), _ptr(x), _ptr(B), _ptr(C), _ptr(dt_raw), _ptr(conv_window),
-                         _ptr(state), _ptr(y), _ptr(seq_status), _stream(stream))
+    rc = ssm_tree_verify(dims, params, _ptr(parent), _ptr(x), _ptr(B), _ptr(C), _ptr(dt_raw), _ptr(z),
+                         _ptr(conv_window), _ptr(state), _ptr(y), _ptr(seq_status), _stream(stream))
     if rc != OK:
         raise SsmTreeError(rc, "ssm_tree_verify")
 
 
 def commit(dims: Dims, params: Params, parent, path, path_len, x, B, dt_raw, conv_window_in, state_in,
-           conv_window_out, state_out, seq_status=None, stream=None):
-    for t, k in ((parent, "int32"), (path, "int32"), (path_len, "int32"), (x, "in"), (B, "in"), (dt_raw, "in"),
-                 (conv_window_in, "in"), (state_in, "float32"), (conv_window_out, "in"), (state_out, "float32"),
-                 (seq_status, "int32")):
+           conv_window_out, state_out, seq_status=None, stream=None, C=None):
+    """ssm_tree_commit; C (the raw C rows) is needed only with the xBC conv."""
+    for t, k in ((parent, "int32"), (path, "int32"), (path_len, "int32"), (x, "in"), (B, "in"), (C, "in"),
+                 (dt_raw, "in"), (conv_window_in, "in"), (state_in, "float32"), (conv_window_out, "in"),
+                 (state_out, "float32"), (seq_status, "int32")):
         _check(t, k)
-    rc = ssm_tree_commit(dims, params, _ptr(parent), _ptr(path), _ptr(path_len), _ptr(x), _ptr(B), _ptr(dt_raw),
-                         _ptr(conv_window_in), _ptr(state_in), _ptr(conv_window_out), _ptr(state_out),
-                         _ptr(seq_status), _stream(stream))
+    rc = ssm_tree_commit(dims, params, _ptr(parent), _ptr(path), _ptr(path_len), _ptr(x), _ptr(B), _ptr(C),
+                         _ptr(dt_raw), _ptr(conv_window_in), _ptr(state_in), _ptr(conv_window_out),
+                         _ptr(state_out), _ptr(seq_status), _stream(stream))
     if rc != OK:
         raise SsmTreeError(rc, "ssm_tree_commit")
 
 
 def commit_verify(dims: Dims, params: Params, parent_prev, path, path_len, x_prev, B_prev, dt_raw_prev,
                   conv_window_in, state_in, conv_window_out, state_out, parent, x, B, C, dt_raw, y,
-                  commit_status=None, verify_status=None, stream=None):
+                  commit_status=None, verify_status=None, stream=None, C_prev=None, z=None):
+    """ssm_tree_commit_verify; C_prev is needed only with the xBC conv, z
+    (optional) gates the next tree's y by silu(z)."""
     for t, k in ((parent_prev, "int32"), (path, "int32"), (path_len, "int32"), (x_prev, "in"), (B_prev, "in"),
-                 (dt_raw_prev, "in"), (conv_window_in, "in"), (state_in, "float32"), (conv_window_out, "in"),
-                 (state_out, "float32"), (parent, "int32"), (x, "in"), (B, "in"), (C, "in"), (dt_raw, "in"),
-                 (y, "float32"), (commit_status, "int32"), (verify_status, "int32")):
+                 (C_prev, "in"), (dt_raw_prev, "in"), (conv_window_in, "in"), (state_in, "float32"),
+                 (conv_window_out, "in"), (state_out, "float32"), (parent, "int32"), (x, "in"), (B, "in"),
+                 (C, "in"), (dt_raw, "in"), (z, "in"), (y, "float32"), (commit_status, "int32"),
+                 (verify_status, "int32")):
         _check(t, k)
     rc = ssm_tree_commit_verify(dims, params, _ptr(parent_prev), _ptr(path), _ptr(path_len), _ptr(x_prev),
-                                _ptr(B_prev), _ptr(dt_raw_prev), _ptr(conv_window_in), _ptr(state_in),
-                                _ptr(conv_window_out), _ptr(state_out), _ptr(parent), _ptr(x), _ptr(B), _ptr(C),
-                                _ptr(dt_raw), _ptr(y), _ptr(commit_status), _ptr(verify_status), _stream(stream))
+                                _ptr(B_prev), _ptr(C_prev), _ptr(dt_raw_prev), _ptr(conv_window_in),
+                                _ptr(state_in), _ptr(conv_window_out), _ptr(state_out), _ptr(parent), _ptr(x),
+                                _ptr(B), _ptr(C), _ptr(dt_raw), _ptr(z), _ptr(y), _ptr(commit_status),
+                                _ptr(verify_status), _stream(stream))
     if rc != OK:
         raise SsmTreeError(rc, "ssm_tree_commit_verify")
 

@@ -9,6 +9,9 @@ namespace ssmt {
 int launch_verify(const VerifyArgs& a, bool bf16, hipStream_t s);  // status code
 hipError_t launch_commit(const CommitArgs& a, bool bf16, hipStream_t s);
 bool commit_verify_fused_applies(const Dims& d);
+bool verify_options_supported(const Dims& d, bool gate);  // SSM_TREE_CONV_XBC and the gate
+bool commit_options_supported(const Dims& d);
+bool commit_verify_options_supported(const Dims& d, bool gate);
 int launch_commit_verify(const CommitVerifyArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_plan(const int32_t* parent, int Bsz, int T, int W, int32_t* out, hipStream_t s);
 hipError_t launch_status(int32_t* seq_status, int Bsz, int value, hipStream_t s);
@@ -35,7 +38,7 @@ int check_dims(const ssm_tree_dims* dm, Dims* out) {
   if (!dm) return SSM_TREE_E_NULL;
   const ssm_tree_dims& d = *dm;
   if (d.in_dtype != SSM_TREE_F32 && d.in_dtype != SSM_TREE_BF16) return SSM_TREE_E_DTYPE;
-  if (d.flags & ~(SSM_TREE_CONV_SILU | SSM_TREE_VERIFY_FIFO)) return SSM_TREE_E_FLAGS;
+  if (d.flags & ~(SSM_TREE_CONV_SILU | SSM_TREE_VERIFY_FIFO | SSM_TREE_CONV_XBC)) return SSM_TREE_E_FLAGS;
   if (d.n_layers < 0 || d.batch < 0 || d.n_nodes < 0 || d.n_nodes > kMaxNodes) return SSM_TREE_E_DIMS;
   if (d.nheads < 1 || d.headdim < 1 || d.ngroups < 1 || d.nheads % d.ngroups) return SSM_TREE_E_DIMS;
   if (d.conv_width < 1 || d.conv_width > 4) return SSM_TREE_E_DIMS;
@@ -45,8 +48,10 @@ int check_dims(const ssm_tree_dims* dm, Dims* out) {
   if (di % kWave || di > (1 << 20) || (di / d.ngroups) % kWave) return SSM_TREE_E_DIMS;
   const int64_t units = (int64_t)d.n_layers * d.batch;
   if (d.batch > 65535 || d.n_layers > 65535 || units * di * d.d_state > ((int64_t)1 << 40)) return SSM_TREE_E_DIMS;
+  const int xbc = (d.flags & SSM_TREE_CONV_XBC) ? 1 : 0;
   *out = Dims{d.n_layers, d.batch, d.n_nodes, d.nheads, d.headdim, d.d_state, d.ngroups, d.conv_width,
-              (d.flags & SSM_TREE_CONV_SILU) ? 1 : 0, (int32_t)di, (d.flags & SSM_TREE_VERIFY_FIFO) ? 1 : 0};
+              (d.flags & SSM_TREE_CONV_SILU) ? 1 : 0, (int32_t)di, (d.flags & SSM_TREE_VERIFY_FIFO) ? 1 : 0, xbc,
+              (int32_t)(di + (xbc ? 2 * (int64_t)d.ngroups * d.d_state : 0))};
   return SSM_TREE_OK;
 }
 
@@ -81,8 +86,8 @@ const char* ssm_tree_status_string(int status) {
 }
 
 int ssm_tree_verify(const ssm_tree_dims* dims, const ssm_tree_params* params, const int32_t* parent,
-                    const void* x, const void* B, const void* C, const void* dt_raw, const void* conv_window,
-                    const float* state, float* y, int32_t* seq_status, void* hip_stream) {
+                    const void* x, const void* B, const void* C, const void* dt_raw, const void* z,
+                    const void* conv_window, const float* state, float* y, int32_t* seq_status, void* hip_stream) {
   Dims d;
   int st = check_dims(dims, &d);
   if (st) return st;
@@ -92,22 +97,24 @@ int ssm_tree_verify(const ssm_tree_dims* dims, const ssm_tree_params* params, co
     if (seq_status) return launch_status(seq_status, d.Bsz, SSM_TREE_OK, s) == hipSuccess ? SSM_TREE_OK : SSM_TREE_E_HIP;
     return SSM_TREE_OK;
   }
+  if (!verify_options_supported(d, z != nullptr)) return SSM_TREE_E_DIMS;
   if ((st = check_params(params))) return st;
   if (!parent || !x || !B || !C || !dt_raw || !state || !y || (d.W > 1 && !conv_window)) return SSM_TREE_E_NULL;
-  const void* ptrs[] = {parent, x, B, C, dt_raw, state, y, seq_status, d.W > 1 ? conv_window : nullptr};
+  const void* ptrs[] = {parent, x, B, C, dt_raw, z, state, y, seq_status, d.W > 1 ? conv_window : nullptr};
   for (const void* p : ptrs)
     if (p && misaligned(p)) return SSM_TREE_E_ALIGN;
   const int64_t e = dims->in_dtype == SSM_TREE_BF16 ? 2 : 4;
-  const int64_t U = (int64_t)d.L * d.Bsz, T = d.T, DI = d.d_in;
+  const int64_t U = (int64_t)d.L * d.Bsz, T = d.T, DI = d.d_in, CH = d.CH;
   const Range ry = range_of(y, U * T * DI * 4);
   const Range ins[] = {range_of(parent, (int64_t)d.Bsz * T * 4), range_of(x, U * T * DI * e),
                        range_of(B, U * T * d.G * d.N * e), range_of(C, U * T * d.G * d.N * e),
-                       range_of(dt_raw, U * T * d.H * e), range_of(state, U * DI * d.N * 4),
-                       range_of(conv_window, d.W > 1 ? U * (d.W - 1) * DI * e : 0),
+                       range_of(dt_raw, U * T * d.H * e), range_of(z, z ? U * T * DI * e : 0),
+                       range_of(state, U * DI * d.N * 4),
+                       range_of(conv_window, d.W > 1 ? U * (d.W - 1) * CH * e : 0),
                        range_of(params->A, d.L * (int64_t)d.H * 4), range_of(params->D, d.L * (int64_t)d.H * 4),
                        range_of(params->dt_bias, d.L * (int64_t)d.H * 4),
-                       range_of(params->conv_w, d.L * DI * d.W * 4),
-                       range_of(params->conv_b, params->conv_b ? d.L * DI * 4 : 0)};
+                       range_of(params->conv_w, d.L * CH * d.W * 4),
+                       range_of(params->conv_b, params->conv_b ? d.L * CH * 4 : 0)};
   for (const Range& r : ins)
     if (overlaps(ry, r)) return SSM_TREE_E_ALIAS;
   if (seq_status) {
@@ -124,6 +131,7 @@ int ssm_tree_verify(const ssm_tree_dims* dims, const ssm_tree_params* params, co
   a.B = B;
   a.C = C;
   a.dt_raw = dt_raw;
+  a.z = z;
   a.window = conv_window;
   a.state = state;
   a.y = y;
@@ -132,34 +140,37 @@ int ssm_tree_verify(const ssm_tree_dims* dims, const ssm_tree_params* params, co
 }
 
 int ssm_tree_commit(const ssm_tree_dims* dims, const ssm_tree_params* params, const int32_t* parent,
-                    const int32_t* path, const int32_t* path_len, const void* x, const void* B, const void* dt_raw,
-                    const void* conv_window_in, const float* state_in, void* conv_window_out, float* state_out,
-                    int32_t* seq_status, void* hip_stream) {
+                    const int32_t* path, const int32_t* path_len, const void* x, const void* B, const void* C,
+                    const void* dt_raw, const void* conv_window_in, const float* state_in, void* conv_window_out,
+                    float* state_out, int32_t* seq_status, void* hip_stream) {
   Dims d;
   int st = check_dims(dims, &d);
   if (st) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
   if (d.L == 0 || d.Bsz == 0) return SSM_TREE_OK;
+  if (!commit_options_supported(d)) return SSM_TREE_E_DIMS;
   if ((st = check_params(params))) return st;
   if (!path_len || !state_in || !state_out) return SSM_TREE_E_NULL;
-  if (d.T > 0 && (!parent || !path || !x || !B || !dt_raw)) return SSM_TREE_E_NULL;
+  if (d.T > 0 && (!parent || !path || !x || !B || !dt_raw || (d.xbc && !C))) return SSM_TREE_E_NULL;
   if (d.W > 1 && (!conv_window_in || !conv_window_out)) return SSM_TREE_E_NULL;
-  const void* ptrs[] = {parent, path, path_len, x, B, dt_raw, state_in, state_out, seq_status,
+  const void* Cx = d.xbc ? C : nullptr;  // C is read only with the xBC conv
+  const void* ptrs[] = {parent, path, path_len, x, B, Cx, dt_raw, state_in, state_out, seq_status,
                         d.W > 1 ? conv_window_in : nullptr, d.W > 1 ? conv_window_out : nullptr};
   for (const void* p : ptrs)
     if (p && misaligned(p)) return SSM_TREE_E_ALIGN;
   const int64_t e = dims->in_dtype == SSM_TREE_BF16 ? 2 : 4;
-  const int64_t U = (int64_t)d.L * d.Bsz, T = d.T, DI = d.d_in;
-  const int64_t wbytes = d.W > 1 ? U * (d.W - 1) * DI * e : 0;
+  const int64_t U = (int64_t)d.L * d.Bsz, T = d.T, DI = d.d_in, CH = d.CH;
+  const int64_t wbytes = d.W > 1 ? U * (d.W - 1) * CH * e : 0;
   const Range rso = range_of(state_out, U * DI * d.N * 4), rsi = range_of(state_in, U * DI * d.N * 4);
   const Range rwo = range_of(conv_window_out, wbytes), rwi = range_of(conv_window_in, wbytes);
   const Range others[] = {range_of(parent, (int64_t)d.Bsz * T * 4), range_of(path, (int64_t)d.Bsz * T * 4),
                           range_of(path_len, (int64_t)d.Bsz * 4), range_of(x, U * T * DI * e),
-                          range_of(B, U * T * d.G * d.N * e), range_of(dt_raw, U * T * d.H * e),
+                          range_of(B, U * T * d.G * d.N * e), range_of(Cx, Cx ? U * T * d.G * d.N * e : 0),
+                          range_of(dt_raw, U * T * d.H * e),
                           range_of(params->A, d.L * (int64_t)d.H * 4), range_of(params->D, d.L * (int64_t)d.H * 4),
                           range_of(params->dt_bias, d.L * (int64_t)d.H * 4),
-                          range_of(params->conv_w, d.L * DI * d.W * 4),
-                          range_of(params->conv_b, params->conv_b ? d.L * DI * 4 : 0)};
+                          range_of(params->conv_w, d.L * CH * d.W * 4),
+                          range_of(params->conv_b, params->conv_b ? d.L * CH * 4 : 0)};
   // outputs: exact in-place allowed, any other overlap rejected
   if (state_out != state_in && overlaps(rso, rsi)) return SSM_TREE_E_ALIAS;
   if (d.W > 1 && conv_window_out != conv_window_in && overlaps(rwo, rwi)) return SSM_TREE_E_ALIAS;
@@ -180,6 +191,7 @@ int ssm_tree_commit(const ssm_tree_dims* dims, const ssm_tree_params* params, co
   a.path_len = path_len;
   a.x = x;
   a.B = B;
+  a.C = Cx;
   a.dt_raw = dt_raw;
   a.window_in = conv_window_in;
   a.state_in = state_in;
@@ -191,28 +203,37 @@ int ssm_tree_commit(const ssm_tree_dims* dims, const ssm_tree_params* params, co
 
 int ssm_tree_commit_verify(const ssm_tree_dims* dims, const ssm_tree_params* params, const int32_t* parent_prev,
                            const int32_t* path, const int32_t* path_len, const void* x_prev, const void* B_prev,
-                           const void* dt_raw_prev, const void* conv_window_in, const float* state_in,
-                           void* conv_window_out, float* state_out, const int32_t* parent, const void* x,
-                           const void* B, const void* C, const void* dt_raw, float* y, int32_t* commit_status,
-                           int32_t* verify_status, void* hip_stream) {
+                           const void* C_prev, const void* dt_raw_prev, const void* conv_window_in,
+                           const float* state_in, void* conv_window_out, float* state_out, const int32_t* parent,
+                           const void* x, const void* B, const void* C, const void* dt_raw, const void* z,
+                           float* y, int32_t* commit_status, int32_t* verify_status, void* hip_stream) {
   Dims d;
   int st = check_dims(dims, &d);
   if (st) return st;
   if (d.L == 0 || d.Bsz == 0) return SSM_TREE_OK;
+  const bool fused = !d.fifo && commit_verify_fused_applies(d);
+  // the options (xBC conv, gate) must be supported by whichever kernels run,
+  // checked before anything is enqueued
+  if ((d.xbc || z) && d.T > 0 &&
+      !(fused ? commit_verify_options_supported(d, z != nullptr)
+              : commit_options_supported(d) && verify_options_supported(d, z != nullptr)))
+    return SSM_TREE_E_DIMS;
   if ((st = check_params(params))) return st;
   if (!path_len || !state_in || !state_out) return SSM_TREE_E_NULL;
   if (d.T > 0 && (!parent_prev || !path || !x_prev || !B_prev || !dt_raw_prev || !parent || !x || !B || !C ||
-                  !dt_raw || !y))
+                  !dt_raw || !y || (d.xbc && !C_prev)))
     return SSM_TREE_E_NULL;
   if (d.W > 1 && (!conv_window_in || !conv_window_out)) return SSM_TREE_E_NULL;
-  const void* ptrs[] = {parent_prev, path, path_len, x_prev, B_prev, dt_raw_prev, state_in, state_out, parent, x,
-                        B, C, dt_raw, y, commit_status, verify_status,
+  const void* Cp = d.xbc ? C_prev : nullptr;  // read only with the xBC conv
+  const void* ptrs[] = {parent_prev, path, path_len, x_prev, B_prev, Cp, dt_raw_prev, state_in, state_out, parent,
+                        x, B, C, dt_raw, z, y, commit_status, verify_status,
                         d.W > 1 ? conv_window_in : nullptr, d.W > 1 ? conv_window_out : nullptr};
   for (const void* p : ptrs)
     if (p && misaligned(p)) return SSM_TREE_E_ALIGN;
   const int64_t e = dims->in_dtype == SSM_TREE_BF16 ? 2 : 4;
-  const int64_t U = (int64_t)d.L * d.Bsz, T = d.T, DI = d.d_in;
-  const int64_t wbytes = d.W > 1 ? U * (d.W - 1) * DI * e : 0;
+  const int64_t U = (int64_t)d.L * d.Bsz, T = d.T, DI = d.d_in, CH = d.CH;
+  const int64_t wbytes = d.W > 1 ? U * (d.W - 1) * CH * e : 0;
+  const int64_t bcb = U * T * d.G * d.N * e;
   const Range rso = range_of(state_out, U * DI * d.N * 4), rsi = range_of(state_in, U * DI * d.N * 4);
   const Range rwo = range_of(conv_window_out, wbytes), rwi = range_of(conv_window_in, wbytes);
   const Range ry = range_of(y, U * T * DI * 4);
@@ -220,14 +241,13 @@ int ssm_tree_commit_verify(const ssm_tree_dims* dims, const ssm_tree_params* par
   const Range rvs = range_of(verify_status, verify_status ? (int64_t)d.Bsz * 4 : 0);
   const Range ins[] = {range_of(parent_prev, (int64_t)d.Bsz * T * 4), range_of(path, (int64_t)d.Bsz * T * 4),
                        range_of(path_len, (int64_t)d.Bsz * 4), range_of(x_prev, U * T * DI * e),
-                       range_of(B_prev, U * T * d.G * d.N * e), range_of(dt_raw_prev, U * T * d.H * e),
-                       range_of(parent, (int64_t)d.Bsz * T * 4), range_of(x, U * T * DI * e),
-                       range_of(B, U * T * d.G * d.N * e), range_of(C, U * T * d.G * d.N * e),
-                       range_of(dt_raw, U * T * d.H * e),
+                       range_of(B_prev, bcb), range_of(Cp, Cp ? bcb : 0), range_of(dt_raw_prev, U * T * d.H * e),
+                       range_of(parent, (int64_t)d.Bsz * T * 4), range_of(x, U * T * DI * e), range_of(B, bcb),
+                       range_of(C, bcb), range_of(dt_raw, U * T * d.H * e), range_of(z, z ? U * T * DI * e : 0),
                        range_of(params->A, d.L * (int64_t)d.H * 4), range_of(params->D, d.L * (int64_t)d.H * 4),
                        range_of(params->dt_bias, d.L * (int64_t)d.H * 4),
-                       range_of(params->conv_w, d.L * DI * d.W * 4),
-                       range_of(params->conv_b, params->conv_b ? d.L * DI * 4 : 0)};
+                       range_of(params->conv_w, d.L * CH * d.W * 4),
+                       range_of(params->conv_b, params->conv_b ? d.L * CH * 4 : 0)};
   // outputs: state and window may equal their inputs exactly; nothing else may overlap
   if (state_out != state_in && overlaps(rso, rsi)) return SSM_TREE_E_ALIAS;
   if (d.W > 1 && conv_window_out != conv_window_in && overlaps(rwo, rwi)) return SSM_TREE_E_ALIAS;
@@ -241,7 +261,7 @@ int ssm_tree_commit_verify(const ssm_tree_dims* dims, const ssm_tree_params* par
     if (i != 1 && overlaps(outs[i], rwi)) return SSM_TREE_E_ALIAS;
   }
   hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
-  if (d.fifo || !commit_verify_fused_applies(d)) {
+  if (!fused) {
     // The two calls in turn, on the same stream.  The outputs first receive
     // the inputs and the commit then runs in place on them, so that a
     // sequence whose commit fails carries its old state and window into the
@@ -252,10 +272,10 @@ int ssm_tree_commit_verify(const ssm_tree_dims* dims, const ssm_tree_params* par
     if (wbytes && conv_window_out != conv_window_in &&
         hipMemcpyAsync(conv_window_out, conv_window_in, wbytes, hipMemcpyDeviceToDevice, s) != hipSuccess)
       return SSM_TREE_E_HIP;
-    st = ssm_tree_commit(dims, params, parent_prev, path, path_len, x_prev, B_prev, dt_raw_prev, conv_window_out,
-                         state_out, conv_window_out, state_out, commit_status, hip_stream);
+    st = ssm_tree_commit(dims, params, parent_prev, path, path_len, x_prev, B_prev, Cp, dt_raw_prev,
+                         conv_window_out, state_out, conv_window_out, state_out, commit_status, hip_stream);
     if (st) return st;
-    return ssm_tree_verify(dims, params, parent, x, B, C, dt_raw, conv_window_out, state_out, y, verify_status,
+    return ssm_tree_verify(dims, params, parent, x, B, C, dt_raw, z, conv_window_out, state_out, y, verify_status,
                            hip_stream);
   }
   CommitVerifyArgs a;
@@ -266,6 +286,7 @@ int ssm_tree_commit_verify(const ssm_tree_dims* dims, const ssm_tree_params* par
   a.path_len = path_len;
   a.x_prev = x_prev;
   a.B_prev = B_prev;
+  a.C_prev = Cp;
   a.dt_prev = dt_raw_prev;
   a.window_in = conv_window_in;
   a.state_in = state_in;
@@ -276,6 +297,7 @@ int ssm_tree_commit_verify(const ssm_tree_dims* dims, const ssm_tree_params* par
   a.B = B;
   a.C = C;
   a.dt_raw = dt_raw;
+  a.z = z;
   a.y = y;
   a.commit_status = commit_status;
   a.verify_status = verify_status;

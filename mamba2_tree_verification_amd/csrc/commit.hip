@@ -17,6 +17,8 @@
 // (streamed past the caches): 1.08 -> 1.00 ms on the 2.7B batch-16
 // workload.  (The MFMA-layout kernels touch half a line per instruction;
 // there the non-temporal hint measured slower.)
+#include <type_traits>
+
 #include "common.h"
 
 namespace ssmt {
@@ -88,25 +90,41 @@ __global__ void __launch_bounds__(kCommitThreads) commit_kernel(CommitArgs a, in
     const float dt = softplus_f32(z);
     s_dA[k * HWMAX + hh] = expf(dt * a.prm.A[(int64_t)l * H + h]);
   }
+  const int CH = d.CH;  // conv channels = window row length
   const TIn* xin = reinterpret_cast<const TIn*>(a.x) + unit * T * DI;
   const TIn* Bg = reinterpret_cast<const TIn*>(a.B) + (unit * T * d.G + g) * (int64_t)N;
+  const TIn* win_in = reinterpret_cast<const TIn*>(a.window_in) + unit * (W - 1) * (int64_t)CH;
   for (int i = threadIdx.x; i < len * N; i += blockDim.x) {
     const int k = i / N, n = i % N;
-    s_B[k * N + n] = load_in(Bg + (int64_t)s_path[k] * d.G * N, n);
+    if (!d.xbc) {
+      s_B[k * N + n] = load_in(Bg + (int64_t)s_path[k] * d.G * N, n);
+    } else {
+      // the xBC conv of B channel (g, n) at path node k: its taps read the
+      // sequence (old window rows, then the path nodes) backwards from k
+      const int ch = DI + g * N + n;
+      const float* cw = a.prm.conv_w + ((int64_t)l * CH + ch) * W;
+      float acc = a.prm.conv_b ? a.prm.conv_b[(int64_t)l * CH + ch] : 0.0f;
+      for (int j = 0; j < W; ++j) {
+        const int e = k + W - 1 - j;
+        const float in = e < W - 1 ? load_in(win_in, (int64_t)e * CH + ch)
+                                   : load_in(Bg + (int64_t)s_path[e - (W - 1)] * d.G * N, n);
+        acc = fmaf(cw[W - 1 - j], in, acc);
+      }
+      s_B[k * N + n] = d.silu ? silu_f32(acc) : acc;
+    }
   }
   if (threadIdx.x < kCommitRows) {
     const int c = c0 + threadIdx.x, h = c / P;
-    const TIn* win_in = reinterpret_cast<const TIn*>(a.window_in) + unit * (W - 1) * (int64_t)DI;
     // wj[jj] weighs conv input jj (0 = the token itself, jj = the jj-th previous token)
     float wj[4];
-    const float* cw = a.prm.conv_w + ((int64_t)l * DI + c) * W;
+    const float* cw = a.prm.conv_w + ((int64_t)l * CH + c) * W;
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) wj[jj] = (jj < W) ? cw[W - 1 - jj] : 0.0f;
-    const float cb = a.prm.conv_b ? a.prm.conv_b[(int64_t)l * DI + c] : 0.0f;
+    const float cb = a.prm.conv_b ? a.prm.conv_b[(int64_t)l * CH + c] : 0.0f;
     // sliding window of raw inputs, hist[0] = newest
     float hist[3];
 #pragma unroll
-    for (int r = 0; r < 3; ++r) hist[r] = (r < W - 1) ? load_in(win_in, (int64_t)(W - 2 - r) * DI + c) : 0.0f;
+    for (int r = 0; r < 3; ++r) hist[r] = (r < W - 1) ? load_in(win_in, (int64_t)(W - 2 - r) * CH + c) : 0.0f;
     // new window row r (oldest first) is element len + r of the sequence
     // (old window rows, x of the path nodes); read every source before any
     // write so that an in-place window is safe
@@ -115,7 +133,7 @@ __global__ void __launch_bounds__(kCommitThreads) commit_kernel(CommitArgs a, in
     for (int r = 0; r < 3; ++r) {
       if (r < W - 1) {
         const int e = len + r;
-        nw[r] = (e < W - 1) ? win_in[(int64_t)e * DI + c] : xin[(int64_t)s_path[e - (W - 1)] * DI + c];
+        nw[r] = (e < W - 1) ? win_in[(int64_t)e * CH + c] : xin[(int64_t)s_path[e - (W - 1)] * DI + c];
       }
     }
     for (int k = 0; k < len; ++k) {
@@ -133,10 +151,10 @@ __global__ void __launch_bounds__(kCommitThreads) commit_kernel(CommitArgs a, in
       hist[0] = xv;
     }
     if (W > 1) {
-      TIn* win_out = reinterpret_cast<TIn*>(a.window_out) + unit * (W - 1) * (int64_t)DI;
+      TIn* win_out = reinterpret_cast<TIn*>(a.window_out) + unit * (W - 1) * (int64_t)CH;
 #pragma unroll
       for (int r = 0; r < 3; ++r)
-        if (r < W - 1) win_out[(int64_t)r * DI + c] = nw[r];
+        if (r < W - 1) win_out[(int64_t)r * CH + c] = nw[r];
     }
   }
   __syncthreads();
@@ -161,6 +179,79 @@ __global__ void __launch_bounds__(kCommitThreads) commit_kernel(CommitArgs a, in
     __builtin_nontemporal_store(h, reinterpret_cast<f32x4*>(sout) + qi);
   }
 }
+
+// The B and C rows of the conv window after a commit with the xBC conv:
+// row r = element len + r of (old window rows, raw B and C of each path
+// node), copied bit for bit.  Every workgroup of a (layer, sequence) reads
+// the old B and C rows, so they are rewritten only here, in a launch of
+// its own after those readers.  A thread owns one channel and reads all of
+// its old rows before writing any, so the update is safe in place.  A
+// sequence whose commit fails keeps its rows (pass_through: they are
+// copied to the output, as the fused round requires).
+template <typename TIn>
+__global__ void __launch_bounds__(kCommitThreads) commit_window_bc_kernel(WindowBcArgs a) {
+  const Dims d = a.d;
+  const int T = d.T, W = d.W, DI = d.d_in, CH = d.CH, GN = d.G * d.N;
+  const int b = blockIdx.y, l = blockIdx.z;
+  const int64_t unit = (int64_t)l * d.Bsz + b;
+  __shared__ int32_t s_parent[kMaxNodes], s_path[kMaxNodes], s_len;
+  for (int i = threadIdx.x; i < T; i += blockDim.x) {
+    s_parent[i] = a.parent[(int64_t)b * T + i];
+    s_path[i] = a.path[(int64_t)b * T + i];
+  }
+  __syncthreads();
+  const bool tree_ok = tree_is_valid(s_parent, T);
+  if (threadIdx.x == 0) {
+    int len = a.path_len[b];
+    bool ok = tree_ok && len >= 0 && len <= T;
+    for (int k = 0; ok && k < len; ++k) {
+      const int v = s_path[k];
+      ok = v >= 0 && v < T && s_parent[v] == (k == 0 ? -1 : s_path[k - 1]);
+    }
+    s_len = ok ? len : -1;
+  }
+  __syncthreads();
+  int len = s_len;
+  if (len < 0) {
+    if (!a.pass_through) return;
+    len = 0;
+  }
+  const int ch = blockIdx.x * blockDim.x + threadIdx.x;  // 0 .. 2 G N: B channels, then C channels
+  if (ch >= 2 * GN) return;
+  // raw bits of the input type: the rows are copied, never converted
+  typedef typename std::conditional<sizeof(TIn) == 2, uint16_t, uint32_t>::type R;
+  const R* win_in = reinterpret_cast<const R*>(a.window_in) + unit * (W - 1) * (int64_t)CH + DI + ch;
+  R* win_out = reinterpret_cast<R*>(a.window_out) + unit * (W - 1) * (int64_t)CH + DI + ch;
+  const R* src = reinterpret_cast<const R*>(ch < GN ? a.B : a.C) + unit * T * (int64_t)GN + (ch < GN ? ch : ch - GN);
+  R o0 = 0, o1 = 0, o2 = 0;  // old rows 0..W-2 (no dynamic indexing: that would go to scratch memory)
+  if (W > 1) o0 = win_in[0];
+  if (W > 2) o1 = win_in[(int64_t)CH];
+  if (W > 3) o2 = win_in[(int64_t)2 * CH];
+#pragma unroll
+  for (int r = 0; r < 3; ++r) {
+    if (r < W - 1) {
+      const int e = len + r;
+      win_out[(int64_t)r * CH] =
+          e < W - 1 ? (e == 0 ? o0 : (e == 1 ? o1 : o2)) : src[(int64_t)s_path[e - (W - 1)] * GN];
+    }
+  }
+}
+
+template <typename TIn>
+static hipError_t launch_wbc(const WindowBcArgs& a, hipStream_t s) {
+  dim3 grid((2 * a.d.G * a.d.N + kCommitThreads - 1) / kCommitThreads, a.d.Bsz, a.d.L);
+  hipLaunchKernelGGL((commit_window_bc_kernel<TIn>), grid, dim3(kCommitThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_window_bc(const WindowBcArgs& a, bool bf16, hipStream_t s) {
+  if (a.d.W < 2 || !a.d.xbc) return hipSuccess;
+  return bf16 ? launch_wbc<bf16_t>(a, s) : launch_wbc<float>(a, s);
+}
+
+// SSM_TREE_CONV_XBC: the commit kernel convolves the path's B rows; the
+// window's B and C rows follow in commit_window_bc_kernel.
+bool commit_options_supported(const Dims&) { return true; }
 
 template <typename TIn, int QPT>
 static hipError_t launch_c(const CommitArgs& a, hipStream_t s) {
@@ -188,7 +279,10 @@ static hipError_t launch_cin(const CommitArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_commit(const CommitArgs& a, bool bf16, hipStream_t s) {
-  return bf16 ? launch_cin<bf16_t>(a, s) : launch_cin<float>(a, s);
+  hipError_t e = bf16 ? launch_cin<bf16_t>(a, s) : launch_cin<float>(a, s);
+  if (e != hipSuccess || !a.d.xbc) return e;
+  WindowBcArgs w{a.d, a.parent, a.path, a.path_len, a.B, a.C, a.window_in, a.window_out, 0};
+  return launch_window_bc(w, bf16, s);
 }
 
 }  // namespace ssmt

@@ -34,6 +34,9 @@
 #include "common.h"
 
 namespace ssmt {
+
+hipError_t launch_window_bc(const WindowBcArgs& a, bool bf16, hipStream_t s);
+
 namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -86,7 +89,9 @@ __host__ __device__ constexpr int align16(int x) { return (x + 15) & ~15; }
 struct CvLds {
   int pparent, path, parent, misc, anc, cidx, dAp, dtp, dt, S, S2, D, cbt, cw, cb, win, xn, xp, ys, C, B, dtx, Bp,
       xt, total, row;
-  __host__ __device__ CvLds(int N, int E) {
+  // the options' own arrays (offset 0 when unused)
+  int z, cwbc, cbbc, winbc, Cp, Ct, Bt, Bpt;
+  __host__ __device__ CvLds(int N, int E, bool xbc = false, bool gate = false) {
     int o = 0;
     row = N * E + kRowPad;                    // staged B / C row stride
     pparent = o; o += 4 * kCvT;
@@ -114,13 +119,27 @@ struct CvLds {
     o += kCvT * row > 4 * kCvT * kCvRows ? kCvT * row : 4 * kCvT * kCvRows;
     Bp = o; o += kCvT * row;                  // previous tree B rows of the path nodes (raw, padded)
     xt = o; o += 4 * kCvRows * kCvT;          // next tree conv outputs, MFMA B-operand layout
+    z = cwbc = cbbc = winbc = Cp = Ct = Bt = Bpt = 0;
+    if (gate) { z = o; o += kCvT * kCvRows * E; }          // gate input rows (raw)
+    if (xbc) {
+      dtx = o; o += 4 * kCvT * kCvRows;       // the raw B rows stay live: dt * x~ gets its own space
+      cwbc = o; o += 4 * 4 * 2 * N;           // conv weights of the group's B then C channels, 4 taps
+      cbbc = o; o += 4 * 2 * N;               // their bias
+      winbc = o; o += align16(3 * 2 * N * E); // old window rows of those channels (raw)
+      Cp = o; o += kCvT * row;                // previous tree C rows of the path nodes (raw, padded)
+      Ct = o; o += 4 * kCvT * N;              // next tree convolved C rows, fp32
+      Bt = o; o += 4 * kCvT * N;              // next tree convolved B rows, fp32
+      Bpt = o; o += 4 * kCvT * N;             // convolved B rows of the path nodes, fp32
+    }
     total = o;
   }
 };
 
 }  // namespace
 
-template <typename TIn, int NG>
+// OPT: an instantiation of its own for the Mamba2-convention options (the
+// xBC conv, the gate), so that the plain path keeps its registers and LDS.
+template <typename TIn, int NG, bool OPT>
 __global__ void __launch_bounds__(kCvWaves * kWave) commit_verify_kernel(CommitVerifyArgs a) {
   constexpr int N = 16 * NG;
   constexpr int E = (int)sizeof(TIn);
@@ -138,9 +157,11 @@ __global__ void __launch_bounds__(kCvWaves * kWave) commit_verify_kernel(CommitV
   const int h_lo = c0 / P;
   const int HW = (c0 + kCvRows - 1) / P - h_lo + 1;  // heads touched (<= 4: P is a multiple of 16)
   const int g = c0 / (DI / G);
+  const int CH = d.CH;  // conv channels = window row length
+  const bool xbc = OPT && d.xbc, gate = OPT && a.z != nullptr;
 
   extern __shared__ __align__(16) unsigned char smem[];
-  const CvLds lo(N, E);
+  const CvLds lo(N, E, xbc, gate);
   int32_t* s_pparent = reinterpret_cast<int32_t*>(smem + lo.pparent);
   int32_t* s_path = reinterpret_cast<int32_t*>(smem + lo.path);
   int32_t* s_parent = reinterpret_cast<int32_t*>(smem + lo.parent);
@@ -166,6 +187,14 @@ __global__ void __launch_bounds__(kCvWaves * kWave) commit_verify_kernel(CommitV
   unsigned char* s_Bp = smem + lo.Bp;
   float* s_xt = reinterpret_cast<float*>(smem + lo.xt);
   const int rs = lo.row;
+  TIn* s_z = reinterpret_cast<TIn*>(smem + lo.z);
+  float* s_cwbc = reinterpret_cast<float*>(smem + lo.cwbc);
+  float* s_cbbc = reinterpret_cast<float*>(smem + lo.cbbc);
+  TIn* s_winbc = reinterpret_cast<TIn*>(smem + lo.winbc);
+  unsigned char* s_Cp = smem + lo.Cp;
+  float* s_Ct = reinterpret_cast<float*>(smem + lo.Ct);
+  float* s_Bt = reinterpret_cast<float*>(smem + lo.Bt);
+  float* s_Bpt = reinterpret_cast<float*>(smem + lo.Bpt);
 
   // ======== trip 1: everything that does not depend on the path ========
 
@@ -208,16 +237,43 @@ __global__ void __launch_bounds__(kCvWaves * kWave) commit_verify_kernel(CommitV
   TIn r_win[3];
   float r_cw[4] = {0.0f, 0.0f, 0.0f, 0.0f}, r_cb = 0.0f;
   if (wave == 2) {
-    const TIn* win_in = reinterpret_cast<const TIn*>(a.window_in) + unit * (W - 1) * (int64_t)DI + c0 + lane;
+    const TIn* win_in = reinterpret_cast<const TIn*>(a.window_in) + unit * (W - 1) * (int64_t)CH + c0 + lane;
 #pragma unroll
     for (int r = 0; r < 3; ++r)
-      if (r < W - 1) r_win[r] = win_in[(int64_t)r * DI];
+      if (r < W - 1) r_win[r] = win_in[(int64_t)r * CH];
   } else if (wave == 3) {
-    const float* cw = a.prm.conv_w + ((int64_t)l * DI + c0 + lane) * W;
+    const float* cw = a.prm.conv_w + ((int64_t)l * CH + c0 + lane) * W;
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj)
       if (jj < W) r_cw[jj] = cw[jj];
-    if (a.prm.conv_b) r_cb = a.prm.conv_b[(int64_t)l * DI + c0 + lane];
+    if (a.prm.conv_b) r_cb = a.prm.conv_b[(int64_t)l * CH + c0 + lane];
+  }
+  // the options: gate rows; the group's B and C conv weights, bias and old
+  // window rows (thread i < 2 N owns channel i: B channels, then C)
+  RawQ rz{};
+  constexpr int kBcPT = (2 * N + kCvWaves * kWave - 1) / (kCvWaves * kWave);
+  float o_cw[kBcPT][4], o_cb[kBcPT];
+  TIn o_win[kBcPT][3];
+  if constexpr (OPT) {
+    if (gate && xv < T)
+      rz = *reinterpret_cast<const RawQ*>(reinterpret_cast<const TIn*>(a.z) + (unit * T + xv) * DI + c0 + xq);
+    if (xbc) {
+#pragma unroll
+      for (int it = 0; it < kBcPT; ++it) {
+        const int i = tid + it * kCvWaves * kWave;
+        if (i < 2 * N) {
+          const int ch = DI + (i < N ? g * N + i : G * N + g * N + i - N);
+          const float* cw = a.prm.conv_w + ((int64_t)l * CH + ch) * W;
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) o_cw[it][jj] = jj < W ? cw[jj] : 0.0f;
+          o_cb[it] = a.prm.conv_b ? a.prm.conv_b[(int64_t)l * CH + ch] : 0.0f;
+          const TIn* wsrc = reinterpret_cast<const TIn*>(a.window_in) + unit * (W - 1) * (int64_t)CH + ch;
+#pragma unroll
+          for (int r = 0; r < 3; ++r)
+            if (r < W - 1) o_win[it][r] = wsrc[(int64_t)r * CH];
+        }
+      }
+    }
   }
 
   // the state last: the small rows above reach LDS while it is still in flight
@@ -263,6 +319,23 @@ __global__ void __launch_bounds__(kCvWaves * kWave) commit_verify_kernel(CommitV
     for (int jj = 0; jj < 4; ++jj) s_cw[lane * 4 + jj] = r_cw[jj];
     s_cb[lane] = r_cb;
   }
+  if constexpr (OPT) {
+    if (gate && xv < T) *reinterpret_cast<RawQ*>(s_z + xv * kCvRows + xq) = rz;
+    if (xbc) {
+#pragma unroll
+      for (int it = 0; it < kBcPT; ++it) {
+        const int i = tid + it * kCvWaves * kWave;
+        if (i < 2 * N) {
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) s_cwbc[i * 4 + jj] = o_cw[it][jj];
+          s_cbbc[i] = o_cb[it];
+#pragma unroll
+          for (int r = 0; r < 3; ++r)
+            if (r < W - 1) s_winbc[r * 2 * N + i] = o_win[it][r];
+        }
+      }
+    }
+  }
   __syncthreads();
 
   // ======== trip 2: the path's x and B rows, gathered before validation ========
@@ -274,8 +347,9 @@ __global__ void __launch_bounds__(kCvWaves * kWave) commit_verify_kernel(CommitV
     const int vs = (v >= 0 && v < T) ? v : 0;  // an invalid path is discarded below
     rxp = *reinterpret_cast<const RawQ*>(reinterpret_cast<const TIn*>(a.x_prev) + (unit * T + vs) * DI + c0 + xq);
   }
-  u32x4 rbp[kCPT];
+  u32x4 rbp[kCPT], rcp[kCPT];
   const unsigned char* Bpg = reinterpret_cast<const unsigned char*>(a.B_prev) + ((unit * T) * G + g) * (int64_t)N * E;
+  const unsigned char* Cpg = reinterpret_cast<const unsigned char*>(a.C_prev) + ((unit * T) * G + g) * (int64_t)N * E;
 #pragma unroll
   for (int it = 0; it < kCPT; ++it) {
     const int ci = tid + it * kCvWaves * kWave, q = ci / kChunks, ch = ci % kChunks;
@@ -283,6 +357,7 @@ __global__ void __launch_bounds__(kCvWaves * kWave) commit_verify_kernel(CommitV
       const int v = s_path[q];
       const int vs = (v >= 0 && v < T) ? v : 0;
       rbp[it] = *reinterpret_cast<const u32x4*>(Bpg + (int64_t)vs * G * N * E + ch * 16);
+      if (xbc) rcp[it] = *reinterpret_cast<const u32x4*>(Cpg + (int64_t)vs * G * N * E + ch * 16);
     }
   }
 
@@ -311,8 +386,9 @@ __global__ void __launch_bounds__(kCvWaves * kWave) commit_verify_kernel(CommitV
         if (a.verify_status) a.verify_status[b] = tree_ok ? SSM_TREE_OK : SSM_TREE_E_TREE;
       }
     }
-  } else if (wave == 1) {
+  } else if (wave == 1 && !xbc) {
     // C_v . B_u of the next tree: lane (u + 16 q) ends with CB[4 q + r][u]
+    // (with the xBC conv each wave forms it later from the convolved rows)
     f32x4 cbm = f32x4{0.f, 0.f, 0.f, 0.f};
     const bool live = j < T;
 #pragma unroll
@@ -359,7 +435,10 @@ __global__ void __launch_bounds__(kCvWaves * kWave) commit_verify_kernel(CommitV
 #pragma unroll
   for (int it = 0; it < kCPT; ++it) {
     const int ci = tid + it * kCvWaves * kWave, q = ci / kChunks, ch = ci % kChunks;
-    if (q < lg) *reinterpret_cast<u32x4*>(s_Bp + q * rs + ch * 16) = rbp[it];
+    if (q < lg) {
+      *reinterpret_cast<u32x4*>(s_Bp + q * rs + ch * 16) = rbp[it];
+      if (xbc) *reinterpret_cast<u32x4*>(s_Cp + q * rs + ch * 16) = rcp[it];
+    }
   }
   __syncthreads();
 
@@ -389,12 +468,12 @@ __global__ void __launch_bounds__(kCvWaves * kWave) commit_verify_kernel(CommitV
     }
     // new window row r (oldest first) = element len + r of (old window, path x), bit for bit
     if (W > 1) {
-      TIn* win_out = reinterpret_cast<TIn*>(a.window_out) + unit * (W - 1) * (int64_t)DI + c;
+      TIn* win_out = reinterpret_cast<TIn*>(a.window_out) + unit * (W - 1) * (int64_t)CH + c;
 #pragma unroll
       for (int r = 0; r < 3; ++r) {
         if (r < W - 1) {
           const int e = len + r;
-          win_out[(int64_t)r * DI] = e < W - 1 ? s_win[e * kCvRows + lane] : s_xp[(e - (W - 1)) * kCvRows + lane];
+          win_out[(int64_t)r * CH] = e < W - 1 ? s_win[e * kCvRows + lane] : s_xp[(e - (W - 1)) * kCvRows + lane];
         }
       }
     }
@@ -430,6 +509,49 @@ __global__ void __launch_bounds__(kCvWaves * kWave) commit_verify_kernel(CommitV
     // MFMA B-operand layout: channel row cl, quad v / 4 swizzled
     s_xt[cl * kCvT + 4 * ((v >> 2) ^ ((cl >> 2) & 3)) + (v & 3)] = xt;
   }
+  if constexpr (OPT) {
+    if (xbc) {
+      // the xBC conv of the group's B and C channels: the next tree's nodes
+      // over their ancestor paths (past the root: the committed window, i.e.
+      // element len + r of (old window rows, path rows)), and the path's
+      // nodes over (old window rows, path rows)
+      for (int i = tid; i < kCvT * 2 * N; i += kCvWaves * kWave) {
+        const int v = i / (2 * N), q = i % (2 * N), n = q < N ? q : q - N;
+        const unsigned char* rows = q < N ? s_B : s_C;      // next tree, raw
+        const unsigned char* prow = q < N ? s_Bp : s_Cp;    // path nodes, raw
+        float acc = 0.0f;
+        if (v < T) {
+          acc = fmaf(s_cwbc[q * 4 + W - 1], load_in(reinterpret_cast<const TIn*>(rows + v * rs), n), s_cbbc[q]);
+          const int codes = s_cidx[v];
+          for (int jj = 1; jj < W; ++jj) {
+            const int code = (codes >> (8 * (jj - 1))) & 255;
+            float u;
+            if (code < T) {
+              u = load_in(reinterpret_cast<const TIn*>(rows + code * rs), n);
+            } else {
+              const int e = len + code - T;
+              u = e < W - 1 ? load_in(s_winbc, e * 2 * N + q)
+                            : load_in(reinterpret_cast<const TIn*>(prow + (e - (W - 1)) * rs), n);
+            }
+            acc = fmaf(s_cwbc[q * 4 + W - 1 - jj], u, acc);
+          }
+          if (d.silu) acc = silu_f32(acc);
+        }
+        (q < N ? s_Bt : s_Ct)[v * N + n] = acc;  // zero rows past T
+      }
+      for (int i = tid; i < len * N; i += kCvWaves * kWave) {
+        const int k = i / N, n = i % N;
+        float acc = s_cbbc[n];
+        for (int j = 0; j < W; ++j) {
+          const int e = k + W - 1 - j;
+          const float u = e < W - 1 ? load_in(s_winbc, e * 2 * N + n)
+                                    : load_in(reinterpret_cast<const TIn*>(s_Bp + (e - (W - 1)) * rs), n);
+          acc = fmaf(s_cwbc[n * 4 + W - 1 - j], u, acc);
+        }
+        s_Bpt[k * N + n] = d.silu ? silu_f32(acc) : acc;
+      }
+    }
+  }
   __syncthreads();
 
   // ======== commit along the path, new state, next tree's y ========
@@ -440,9 +562,10 @@ __global__ void __launch_bounds__(kCvWaves * kWave) commit_verify_kernel(CommitV
       const float dA = s_dAp[s_path[q] * 4 + hh];
       const float cx = s_dtx[q * kCvRows + row];
       const TIn* bp = reinterpret_cast<const TIn*>(s_Bp + q * rs) + 4 * k;
+      const float* bpt = s_Bpt + q * N + 4 * k;
 #pragma unroll
       for (int gg = 0; gg < NG; ++gg) {
-        const f32x4 bq = load4<TIn>(bp + 16 * gg);
+        const f32x4 bq = xbc ? *reinterpret_cast<const f32x4*>(bpt + 16 * gg) : load4<TIn>(bp + 16 * gg);
         hq[gg].x = fmaf(dA, hq[gg].x, cx * bq.x);
         hq[gg].y = fmaf(dA, hq[gg].y, cx * bq.y);
         hq[gg].z = fmaf(dA, hq[gg].z, cx * bq.z);
@@ -457,21 +580,35 @@ __global__ void __launch_bounds__(kCvWaves * kWave) commit_verify_kernel(CommitV
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
     const bool live = j < T;
     const TIn* cp = reinterpret_cast<const TIn*>(s_C + j * rs) + 4 * k;
+    f32x4 cbx = f32x4{0.f, 0.f, 0.f, 0.f};  // with the xBC conv: C_v . B_u, formed below
 #pragma unroll
     for (int gg = 0; gg < NG; ++gg) {
-      f32x4 cq = load4<TIn>(cp + 16 * gg);
+      f32x4 cq = xbc ? *reinterpret_cast<const f32x4*>(s_Ct + j * N + 16 * gg + 4 * k) : load4<TIn>(cp + 16 * gg);
       if (!live) cq = f32x4{0.f, 0.f, 0.f, 0.f};
       acc = mfma4(cq.x, hq[gg].x, acc);
       acc = mfma4(cq.y, hq[gg].y, acc);
       acc = mfma4(cq.z, hq[gg].z, acc);
       acc = mfma4(cq.w, hq[gg].w, acc);
+      if constexpr (OPT) {
+        if (xbc) {
+          // B rows as the A operand and C rows as the B operand: lane
+          // (i + 16 k) ends with (B_{4k+t} . C_i) = CB[i][4 k + t], the
+          // layout the path terms read, with no transpose
+          f32x4 bq = *reinterpret_cast<const f32x4*>(s_Bt + j * N + 16 * gg + 4 * k);
+          if (!live) bq = f32x4{0.f, 0.f, 0.f, 0.f};
+          cbx = mfma4(bq.x, cq.x, cbx);
+          cbx = mfma4(bq.y, cq.y, cbx);
+          cbx = mfma4(bq.z, cq.z, cbx);
+          cbx = mfma4(bq.w, cq.w, cbx);
+        }
+      }
     }
     // then the path terms M[v][u] x~_u, with the diagonal D
     const int i = j;
     const float Sv = s_S2[hh * kCvT + i];
     const f32x4 Sq = *reinterpret_cast<const f32x4*>(s_S2 + hh * kCvT + 4 * k);
     const f32x4 dq = *reinterpret_cast<const f32x4*>(s_dt + hh * kCvT + 4 * k);
-    const f32x4 cbr = *reinterpret_cast<const f32x4*>(s_cbt + i * kCvT + 4 * k);
+    const f32x4 cbr = xbc ? cbx : *reinterpret_cast<const f32x4*>(s_cbt + i * kCvT + 4 * k);
     const int ancm = s_anc[i];
     const float Dh = s_D[hh];
     f32x4 mop, y;
@@ -489,7 +626,12 @@ __global__ void __launch_bounds__(kCvWaves * kWave) commit_verify_kernel(CommitV
     const bool tree_ok = s_misc[2] != 0;
     // lane (c + 16 k) holds nodes 4 k + r of channel row
 #pragma unroll
-    for (int r = 0; r < 4; ++r) s_ys[(4 * k + r) * kCvRows + row] = tree_ok ? y[r] : __builtin_nanf("");
+    for (int r = 0; r < 4; ++r) {
+      float yv = y[r];
+      if constexpr (OPT)
+        if (gate) yv *= silu_f32(load_in(s_z, (4 * k + r) * kCvRows + row));
+      s_ys[(4 * k + r) * kCvRows + row] = tree_ok ? yv : __builtin_nanf("");
+    }
   }
   __syncthreads();
   {
@@ -502,13 +644,23 @@ __global__ void __launch_bounds__(kCvWaves * kWave) commit_verify_kernel(CommitV
 
 namespace {
 
+template <typename TIn, int NG, bool OPT>
+int launch_cv_o(const CommitVerifyArgs& a, hipStream_t s) {
+  const size_t lds = (size_t)CvLds(16 * NG, (int)sizeof(TIn), OPT && a.d.xbc, OPT && a.z != nullptr).total;
+  if (allow_lds(commit_verify_kernel<TIn, NG, OPT>, lds) != hipSuccess) return SSM_TREE_E_HIP;
+  dim3 grid(a.d.d_in / kCvRows, a.d.Bsz, a.d.L);
+  hipLaunchKernelGGL((commit_verify_kernel<TIn, NG, OPT>), grid, dim3(kCvWaves * kWave), lds, s, a);
+  if (hipGetLastError() != hipSuccess) return SSM_TREE_E_HIP;
+  if (a.d.xbc) {  // the window's B and C rows, after every reader of the old ones
+    WindowBcArgs w{a.d, a.parent_prev, a.path, a.path_len, a.B_prev, a.C_prev, a.window_in, a.window_out, 1};
+    if (launch_window_bc(w, sizeof(TIn) == 2, s) != hipSuccess) return SSM_TREE_E_HIP;
+  }
+  return SSM_TREE_OK;
+}
+
 template <typename TIn, int NG>
 int launch_cv_t(const CommitVerifyArgs& a, hipStream_t s) {
-  const size_t lds = (size_t)CvLds(16 * NG, (int)sizeof(TIn)).total;
-  if (allow_lds(commit_verify_kernel<TIn, NG>, lds) != hipSuccess) return SSM_TREE_E_HIP;
-  dim3 grid(a.d.d_in / kCvRows, a.d.Bsz, a.d.L);
-  hipLaunchKernelGGL((commit_verify_kernel<TIn, NG>), grid, dim3(kCvWaves * kWave), lds, s, a);
-  return hipGetLastError() == hipSuccess ? SSM_TREE_OK : SSM_TREE_E_HIP;
+  return (a.d.xbc || a.z) ? launch_cv_o<TIn, NG, true>(a, s) : launch_cv_o<TIn, NG, false>(a, s);
 }
 
 template <typename TIn>
@@ -526,6 +678,9 @@ int launch_cv_in(const CommitVerifyArgs& a, hipStream_t s) {
 }  // namespace
 
 bool commit_verify_fused_applies(const Dims& d) { return d.T >= 1 && d.T <= kCvT && d.P % 16 == 0; }
+
+// SSM_TREE_CONV_XBC and the gate: taken by the kernel's OPT instantiation.
+bool commit_verify_options_supported(const Dims&, bool) { return true; }
 
 int launch_commit_verify(const CommitVerifyArgs& a, bool bf16, hipStream_t s) {
   return bf16 ? launch_cv_in<bf16_t>(a, s) : launch_cv_in<float>(a, s);

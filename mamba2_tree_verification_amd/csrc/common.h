@@ -48,6 +48,8 @@ struct Dims {
   int32_t L, Bsz, T, H, P, N, G, W, silu;
   int32_t d_in;  // H * P
   int32_t fifo;  // verify by the explicit FIFO walk
+  int32_t xbc;   // the conv runs over x, B and C
+  int32_t CH;    // conv channels (window row length): d_in, or d_in + 2 G N with xbc
 };
 
 struct Params {
@@ -66,6 +68,7 @@ struct VerifyArgs {
   const void* B;
   const void* C;
   const void* dt_raw;
+  const void* z;  // gate input, or null
   const void* window;
   const float* state;
   float* y;
@@ -80,12 +83,26 @@ struct CommitArgs {
   const int32_t* path_len;
   const void* x;
   const void* B;
+  const void* C;  // read only with xbc
   const void* dt_raw;
   const void* window_in;
   const float* state_in;
   void* window_out;
   float* state_out;
   int32_t* seq_status;
+};
+
+// the B and C rows of the conv window after a commit with the xBC conv
+struct WindowBcArgs {
+  Dims d;
+  const int32_t* parent;
+  const int32_t* path;
+  const int32_t* path_len;
+  const void* B;  // raw B and C of the committed tree's nodes
+  const void* C;
+  const void* window_in;
+  void* window_out;
+  int32_t pass_through;  // a failed commit copies its old rows (else leaves them unwritten)
 };
 
 // commit of the previous tree's accepted path fused with verify of the next tree
@@ -97,6 +114,7 @@ struct CommitVerifyArgs {
   const int32_t* path_len;
   const void* x_prev;
   const void* B_prev;
+  const void* C_prev;  // read only with xbc
   const void* dt_prev;
   const void* window_in;
   const float* state_in;
@@ -107,6 +125,7 @@ struct CommitVerifyArgs {
   const void* B;
   const void* C;
   const void* dt_raw;
+  const void* z;  // gate input, or null
   float* y;
   int32_t* commit_status;
   int32_t* verify_status;

@@ -659,6 +659,9 @@ int launch_verify_mfma(const VerifyArgs& a, bool bf16, hipStream_t s);
 
 int launch_verify_fifo(const VerifyArgs& a, bool bf16, hipStream_t s);
 
+// SSM_TREE_CONV_XBC and the gate: not yet taken by any verify kernel.
+bool verify_options_supported(const Dims& d, bool gate) { return !d.xbc && !gate; }
+
 int launch_verify(const VerifyArgs& a, bool bf16, hipStream_t s) {
   if (a.d.fifo) return launch_verify_fifo(a, bf16, s);
   if (mfma_verify_applies(a.d)) return launch_verify_mfma(a, bf16, s);

@@ -38,12 +38,12 @@ def build(force: bool = True, mutant: int = 0, out: str | None = None) -> str:
 
 
 class _Dims(ctypes.Structure):
-    _fields_ = [(k, ctypes.c_int32) for k in ("T", "H", "P", "N", "G", "W", "silu")]
+    _fields_ = [(k, ctypes.c_int32) for k in ("T", "H", "P", "N", "G", "W", "silu", "xbc")]
 
 
 class _Unit(ctypes.Structure):
     _fields_ = [(k, ctypes.c_void_p) for k in
-                ("x", "B", "C", "dt_raw", "window", "state", "A", "D", "dt_bias", "conv_w", "conv_b")]
+                ("x", "B", "C", "dt_raw", "window", "state", "A", "D", "dt_bias", "conv_w", "conv_b", "z")]
 
 
 class Oracle:
@@ -66,8 +66,13 @@ class Oracle:
 
     # -- helpers ------------------------------------------------------------
     @staticmethod
-    def _dims(T, H, P, N, G, W, silu):
-        return _Dims(T, H, P, N, G, W, int(bool(silu)))
+    def _dims(T, H, P, N, G, W, silu, xbc=False):
+        return _Dims(T, H, P, N, G, W, int(bool(silu)), int(bool(xbc)))
+
+    @staticmethod
+    def conv_channels(H, P, N, G, xbc=False):
+        """Channels of the causal conv: x, or x, B and C with xbc."""
+        return H * P + (2 * G * N if xbc else 0)
 
     @staticmethod
     def _unit(u: dict, keep: list):
@@ -79,7 +84,7 @@ class Oracle:
             keep.append(a)
             return a.ctypes.data
         return _Unit(*(ptr(k) for k in ("x", "B", "C", "dt_raw", "window", "state", "A", "D",
-                                          "dt_bias", "conv_w", "conv_b")))
+                                          "dt_bias", "conv_w", "conv_b", "z")))
 
     @staticmethod
     def _i32(a):
@@ -105,20 +110,21 @@ class Oracle:
                                   ctypes.byref(md), ctypes.byref(ni))
         return st, out[:T], dict(peak_fifo=pk.value, max_depth=md.value, n_internal=ni.value)
 
-    def verify(self, parent, u: dict, H, P, N, G, W, silu=False):
-        """y [T][H*P] float64, status, peak FIFO occupancy for one unit."""
+    def verify(self, parent, u: dict, H, P, N, G, W, silu=False, xbc=False):
+        """y [T][H*P] float64, status, peak FIFO occupancy for one unit.
+        u["z"] (optional) gates y by silu(z); xbc convolves B and C too."""
         p = self._i32(parent)
         T = len(p)
         keep: list = []
         y = np.zeros((T, H * P), np.float64)
         pk = ctypes.c_int32(0)
-        d = self._dims(T, H, P, N, G, W, silu)
+        d = self._dims(T, H, P, N, G, W, silu, xbc)
         st = self.lib.oracle_verify(ctypes.byref(d), p.ctypes.data if T else None,
                                     ctypes.byref(self._unit(u, keep)), y.ctypes.data, ctypes.byref(pk))
         return y, st, pk.value
 
-    def commit(self, parent, path, length, u: dict, H, P, N, G, W, silu=False):
-        """(state_out [H][P][N], window_out [W-1][H*P], status).  Outputs are
+    def commit(self, parent, path, length, u: dict, H, P, N, G, W, silu=False, xbc=False):
+        """(state_out [H][P][N], window_out [W-1][CH], status).  Outputs are
         copies of the inputs when the status is not OK (the oracle leaves its
         output buffers untouched, and they start as copies here)."""
         p = self._i32(parent)
@@ -127,21 +133,22 @@ class Oracle:
         if len(q) == 0:
             q = np.zeros(1, np.int32)
         keep: list = []
+        CH = self.conv_channels(H, P, N, G, xbc)
         so = np.array(u["state"], dtype=np.float64, copy=True)
-        wo = np.array(u["window"], dtype=np.float64, copy=True).reshape(max(W - 1, 0), H * P)
-        d = self._dims(T, H, P, N, G, W, silu)
+        wo = np.array(u["window"], dtype=np.float64, copy=True).reshape(max(W - 1, 0), CH)
+        d = self._dims(T, H, P, N, G, W, silu, xbc)
         st = self.lib.oracle_commit(ctypes.byref(d), p.ctypes.data if T else None, q.ctypes.data,
                                     int(length), ctypes.byref(self._unit(u, keep)), so.ctypes.data,
                                     wo.ctypes.data if W > 1 else None)
         return so, wo, st
 
-    def scan(self, u: dict, S, H, P, N, G, W, silu=False):
-        """Plain sequential scan of S tokens: (y [S][H*P], state_out, window_out)."""
+    def scan(self, u: dict, S, H, P, N, G, W, silu=False, xbc=False):
+        """Plain sequential scan of S tokens: (y [S][H*P], state_out, window_out [W-1][CH])."""
         keep: list = []
         y = np.zeros((S, H * P), np.float64)
         so = np.zeros((H, P, N), np.float64)
-        wo = np.zeros((max(W - 1, 0), H * P), np.float64)
-        d = self._dims(0, H, P, N, G, W, silu)
+        wo = np.zeros((max(W - 1, 0), self.conv_channels(H, P, N, G, xbc)), np.float64)
+        d = self._dims(0, H, P, N, G, W, silu, xbc)
         st = self.lib.oracle_scan(ctypes.byref(d), S, ctypes.byref(self._unit(u, keep)), y.ctypes.data,
                                   so.ctypes.data, wo.ctypes.data if W > 1 else None)
         assert st == OK, st
@@ -179,7 +186,7 @@ def verify_units(cfg, inputs, units, threads: int = 8, oracle: Oracle | None = N
         l, b = lb
         u = unit_f64(cfg, l, b, inputs)
         return lb, o.verify(inputs.parent[b] if inputs is not None else None, u, cfg.H, cfg.P, cfg.N,
-                            cfg.G, cfg.W, cfg.silu)
+                            cfg.G, cfg.W, cfg.silu, getattr(cfg, "xbc", False))
 
     with ThreadPoolExecutor(max_workers=max(1, threads)) as ex:
         return dict(ex.map(one, units))
@@ -194,7 +201,7 @@ def commit_units(cfg, inputs, units, threads: int = 8, oracle: Oracle | None = N
         u = unit_f64(cfg, l, b, inputs)
         n = int(inputs.path_len[b])
         return lb, o.commit(inputs.parent[b], inputs.path[b, :n], n, u, cfg.H, cfg.P, cfg.N, cfg.G,
-                            cfg.W, cfg.silu)
+                            cfg.W, cfg.silu, getattr(cfg, "xbc", False))
 
     with ThreadPoolExecutor(max_workers=max(1, threads)) as ex:
         return dict(ex.map(one, units))

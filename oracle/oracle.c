@@ -131,26 +131,48 @@ int oracle_plan(const int32_t* parent, int32_t T, int32_t W, int32_t* plan, int3
   return ORACLE_OK;
 }
 
-/* Causal depthwise conv1d of channel c at node v over its ancestor path
+/* Conv channels: x only, or x, B and C with the xbc option. */
+static int32_t conv_channels(const oracle_dims* d) { return d->H * d->P + (d->xbc ? 2 * d->G * d->N : 0); }
+
+/* Raw (pre-conv) input of conv channel ch at node or token v. */
+static double raw_in(const oracle_dims* d, const oracle_unit* u, int32_t v, int32_t ch) {
+  const int32_t DI = d->H * d->P, GN = d->G * d->N;
+  if (ch < DI) return u->x[(int64_t)v * DI + ch];
+  if (ch < DI + GN) return u->B[(int64_t)v * GN + (ch - DI)];
+  return u->C[(int64_t)v * GN + (ch - DI - GN)];
+}
+
+/* Row of conv weights used for channel ch. */
+static int32_t weight_row(const oracle_dims* d, int32_t ch) {
+  const int32_t DI = d->H * d->P, GN = d->G * d->N;
+  if (MUT(15) && ch >= DI && ch < DI + GN) return ch + GN; /* B convolved with C's weights */
+  return ch;
+}
+
+/* Causal depthwise conv1d of channel ch at node v over its ancestor path
  * ([LM]: X passes conv1d before the SSM).  Weight W-1 multiplies the node's
- * own x, weight W-1-j its j-th ancestor (or window row past the root). */
+ * own input, weight W-1-j its j-th ancestor's (or a window row past the
+ * root). */
 static double conv_at_node(const oracle_dims* d, const int32_t* parent, const oracle_unit* u, int32_t v,
-                           int32_t c) {
-  const int32_t W = d->W, DI = d->H * d->P;
-  double acc = u->conv_b ? u->conv_b[c] : 0.0;
+                           int32_t ch) {
+  const int32_t W = d->W, CH = conv_channels(d), wr = weight_row(d, ch);
+  double acc = u->conv_b ? u->conv_b[ch] : 0.0;
   for (int32_t j = 0; j < W; ++j) {
     double in;
     if (j == 0) {
-      in = u->x[(int64_t)v * DI + c];
+      in = raw_in(d, u, v, ch);
     } else {
       int32_t code = anc_code(parent, v, j, W);
-      in = code >= 0 ? u->x[(int64_t)code * DI + c] : u->window[(int64_t)(-1 - code) * DI + c];
+      in = code >= 0 ? raw_in(d, u, code, ch) : u->window[(int64_t)(-1 - code) * CH + ch];
     }
     int32_t tap = MUT(3) ? j : (W - 1 - j);
-    acc += u->conv_w[(int64_t)c * W + tap] * in;
+    acc += u->conv_w[(int64_t)wr * W + tap] * in;
   }
   return act(acc, d->silu);
 }
+
+/* Output gate: y * silu(z). */
+static double gate(double z) { return MUT(16) ? 1.0 / (1.0 + exp(-z)) : z / (1.0 + exp(-z)); }
 
 typedef struct {
   int32_t node;
@@ -178,16 +200,27 @@ int oracle_verify(const oracle_dims* d, const int32_t* parent, const oracle_unit
   const int64_t SZ = (int64_t)H * P * N;
   const int32_t hpg = H / G;
 
-  /* per-node step sizes and the conv output, recomputed from raw inputs */
+  /* per-node step sizes and the conv outputs, recomputed from raw inputs */
+  const int32_t GN = G * N;
   double* dt = (double*)malloc(sizeof(double) * (size_t)T * H);
   double* xt = (double*)malloc(sizeof(double) * (size_t)T * DI);
+  double* bt = d->xbc ? (double*)malloc(sizeof(double) * (size_t)T * GN) : NULL;
+  double* ct = d->xbc ? (double*)malloc(sizeof(double) * (size_t)T * GN) : NULL;
   for (int32_t v = 0; v < T; ++v) {
     for (int32_t h = 0; h < H; ++h) {
       double z = u->dt_raw[(int64_t)v * H + h] + (MUT(7) ? 0.0 : u->dt_bias[h]);
       dt[(int64_t)v * H + h] = softplus(z);
     }
     for (int32_t c = 0; c < DI; ++c) xt[(int64_t)v * DI + c] = conv_at_node(d, parent, u, v, c);
+    if (d->xbc) {
+      for (int32_t i = 0; i < GN; ++i) {
+        bt[(int64_t)v * GN + i] = conv_at_node(d, parent, u, v, DI + i);
+        ct[(int64_t)v * GN + i] = conv_at_node(d, parent, u, v, DI + GN + i);
+      }
+    }
   }
+  const double* Bsrc = d->xbc ? bt : u->B; /* the B and C the recurrence sees */
+  const double* Csrc = d->xbc ? ct : u->C;
 
   fifo_entry* q = (fifo_entry*)malloc(sizeof(fifo_entry) * (size_t)(T + 1));
   int32_t head = 0, tail = 0, peak = 0;
@@ -203,8 +236,8 @@ int oracle_verify(const oracle_dims* d, const int32_t* parent, const oracle_unit
         const int32_t g = MUT(14) ? (h % G) : (h / hpg);
         const double dtc = dt[(int64_t)c * H + h];
         const double dA = exp((MUT(2) ? -1.0 : 1.0) * dtc * u->A[h]);
-        const double* Bc = (MUT(6) ? u->C : u->B) + ((int64_t)c * G + g) * N;
-        const double* Cc = (MUT(6) ? u->B : u->C) + ((int64_t)c * G + g) * N;
+        const double* Bc = (MUT(6) ? Csrc : Bsrc) + ((int64_t)c * G + g) * N;
+        const double* Cc = (MUT(6) ? Bsrc : Csrc) + ((int64_t)c * G + g) * N;
         for (int32_t p = 0; p < P; ++p) {
           const int32_t ch = h * P + p;
           const double xin = xt[(int64_t)(MUT(4) ? par_x : c) * DI + ch];
@@ -217,6 +250,7 @@ int oracle_verify(const oracle_dims* d, const int32_t* parent, const oracle_unit
             acc += Cc[n] * (MUT(5) ? hp[n] : hn[n]);
           }
           y[(int64_t)c * DI + ch] = acc + (MUT(1) ? 0.0 : u->D[h] * xt[(int64_t)c * DI + ch]);
+          if (u->z) y[(int64_t)c * DI + ch] *= gate(u->z[(int64_t)c * DI + ch]);
         }
       }
       int has_children = 0;
@@ -236,6 +270,8 @@ int oracle_verify(const oracle_dims* d, const int32_t* parent, const oracle_unit
   }
   if (peak_fifo) *peak_fifo = peak;
   free(q);
+  free(ct);
+  free(bt);
   free(xt);
   free(dt);
   return ORACLE_OK;
@@ -243,36 +279,39 @@ int oracle_verify(const oracle_dims* d, const int32_t* parent, const oracle_unit
 
 /* [SM] sec. 3.1: the accepted path is committed by recomputing the root
  * state along it from the stored per-token dt_raw, B and x (no per-node
- * state is kept).  The window gains each path token's raw x, oldest row
- * dropped; it is a copy of input values. */
+ * state is kept).  The window gains each path token's raw conv inputs
+ * (x, and B and C with xbc), oldest row dropped; it is a copy of input
+ * values. */
 int oracle_commit(const oracle_dims* d, const int32_t* parent, const int32_t* path, int32_t len,
                   const oracle_unit* u, double* state_out, double* window_out) {
   const int32_t T = d->T, H = d->H, P = d->P, N = d->N, G = d->G, W = d->W, DI = H * P;
   if (T < 0 || H <= 0 || P <= 0 || N <= 0 || G <= 0 || H % G != 0 || W < 1 || W > 4) return ORACLE_E_ARG;
   int st = oracle_validate_path(parent, T, path, len);
   if (st != ORACLE_OK) return st;
+  const int32_t CH = conv_channels(d), GN = G * N;
   const int64_t SZ = (int64_t)H * P * N;
   const int32_t hpg = H / G;
   double* h = (double*)malloc(sizeof(double) * (size_t)SZ);
-  double* win = (double*)malloc(sizeof(double) * (size_t)(W > 1 ? W - 1 : 1) * DI);
-  double* xt = (double*)malloc(sizeof(double) * (size_t)DI);
+  double* win = (double*)malloc(sizeof(double) * (size_t)(W > 1 ? W - 1 : 1) * CH);
+  double* cv = (double*)malloc(sizeof(double) * (size_t)CH); /* conv outputs of every channel */
   memcpy(h, u->state, sizeof(double) * (size_t)SZ);
-  if (W > 1) memcpy(win, u->window, sizeof(double) * (size_t)(W - 1) * DI);
+  if (W > 1) memcpy(win, u->window, sizeof(double) * (size_t)(W - 1) * CH);
   for (int32_t k = 0; k < len; ++k) {
     const int32_t v = path[k];
-    for (int32_t c = 0; c < DI; ++c) {
-      double acc = u->conv_b ? u->conv_b[c] : 0.0;
-      acc += u->conv_w[(int64_t)c * W + (W - 1)] * u->x[(int64_t)v * DI + c];
-      for (int32_t j = 1; j < W; ++j) acc += u->conv_w[(int64_t)c * W + (W - 1 - j)] * win[(int64_t)(W - 1 - j) * DI + c];
-      xt[c] = act(acc, d->silu);
+    for (int32_t ch = 0; ch < CH; ++ch) {
+      const int32_t wr = weight_row(d, ch);
+      double acc = u->conv_b ? u->conv_b[ch] : 0.0;
+      acc += u->conv_w[(int64_t)wr * W + (W - 1)] * raw_in(d, u, v, ch);
+      for (int32_t j = 1; j < W; ++j) acc += u->conv_w[(int64_t)wr * W + (W - 1 - j)] * win[(int64_t)(W - 1 - j) * CH + ch];
+      cv[ch] = act(acc, d->silu);
     }
     for (int32_t hh = 0; hh < H; ++hh) {
       const int32_t g = hh / hpg;
       const double dtv = softplus(u->dt_raw[(int64_t)v * H + hh] + u->dt_bias[hh]);
       const double dA = exp(dtv * u->A[hh]);
-      const double* Bv = u->B + ((int64_t)v * G + g) * N;
+      const double* Bv = d->xbc ? cv + DI + (int64_t)g * N : u->B + ((int64_t)v * G + g) * N;
       for (int32_t p = 0; p < P; ++p) {
-        const double coef = dtv * xt[hh * P + p];
+        const double coef = dtv * cv[hh * P + p];
         double* hr = h + ((int64_t)hh * P + p) * N;
         for (int32_t n = 0; n < N; ++n) {
           hr[n] = dA * hr[n] + coef * Bv[n];
@@ -281,13 +320,15 @@ int oracle_commit(const oracle_dims* d, const int32_t* parent, const int32_t* pa
       }
     }
     if (W > 1) {
-      for (int32_t r = 0; r + 1 < W - 1; ++r) memcpy(win + (int64_t)r * DI, win + (int64_t)(r + 1) * DI, sizeof(double) * DI);
-      if (!MUT(10)) memcpy(win + (int64_t)(W - 2) * DI, u->x + (int64_t)v * DI, sizeof(double) * DI);
+      for (int32_t r = 0; r + 1 < W - 1; ++r) memcpy(win + (int64_t)r * CH, win + (int64_t)(r + 1) * CH, sizeof(double) * CH);
+      if (!MUT(10))
+        for (int32_t ch = 0; ch < (MUT(17) ? DI : CH); ++ch) win[(int64_t)(W - 2) * CH + ch] = raw_in(d, u, v, ch);
     }
   }
+  (void)GN;
   memcpy(state_out, h, sizeof(double) * (size_t)SZ);
-  if (W > 1) memcpy(window_out, win, sizeof(double) * (size_t)(W - 1) * DI);
-  free(xt);
+  if (W > 1) memcpy(window_out, win, sizeof(double) * (size_t)(W - 1) * CH);
+  free(cv);
   free(win);
   free(h);
   return ORACLE_OK;
@@ -295,22 +336,41 @@ int oracle_commit(const oracle_dims* d, const int32_t* parent, const int32_t* pa
 
 /* Textbook sequential Mamba2 SSM over a plain token sequence of length S
  * (no tree): the causal conv runs over the concatenation (window rows,
- * then x rows) by index, and the recurrence is applied token by token.
- * x, B, C, dt_raw are indexed by token.  Used as the independent special
- * case a chain tree must reduce to. */
+ * then the tokens' raw inputs) by index, and the recurrence is applied
+ * token by token.  x, B, C, dt_raw, z are indexed by token.  Used as the
+ * independent special case a chain tree must reduce to. */
 int oracle_scan(const oracle_dims* d, int32_t S, const oracle_unit* u, double* y, double* state_out,
                 double* window_out) {
   const int32_t H = d->H, P = d->P, N = d->N, G = d->G, W = d->W, DI = H * P;
   if (S < 0 || H <= 0 || P <= 0 || N <= 0 || G <= 0 || H % G != 0 || W < 1 || W > 4) return ORACLE_E_ARG;
+  const int32_t GN = G * N, CH = DI + (d->xbc ? 2 * GN : 0);
   const int64_t SZ = (int64_t)H * P * N;
   const int32_t hpg = H / G;
   const int32_t L = (W - 1) + S; /* concatenated sequence length */
-  double* seq = (double*)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1) * DI);
-  if (W > 1) memcpy(seq, u->window, sizeof(double) * (size_t)(W - 1) * DI);
-  if (S > 0) memcpy(seq + (int64_t)(W - 1) * DI, u->x, sizeof(double) * (size_t)S * DI);
+  double* seq = (double*)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1) * CH);
+  if (W > 1) memcpy(seq, u->window, sizeof(double) * (size_t)(W - 1) * CH);
+  for (int32_t t = 0; t < S; ++t) {
+    double* row = seq + (int64_t)(W - 1 + t) * CH;
+    memcpy(row, u->x + (int64_t)t * DI, sizeof(double) * DI);
+    if (d->xbc) {
+      memcpy(row + DI, u->B + (int64_t)t * GN, sizeof(double) * GN);
+      memcpy(row + DI + GN, u->C + (int64_t)t * GN, sizeof(double) * GN);
+    }
+  }
   double* h = (double*)malloc(sizeof(double) * (size_t)SZ);
+  double* bc = (double*)malloc(sizeof(double) * (size_t)(2 * GN)); /* this token's B and C as the SSM sees them */
   memcpy(h, u->state, sizeof(double) * (size_t)SZ);
   for (int32_t t = 0; t < S; ++t) {
+    for (int32_t i = 0; i < 2 * GN; ++i) {
+      if (!d->xbc) {
+        bc[i] = i < GN ? u->B[(int64_t)t * GN + i] : u->C[(int64_t)t * GN + i - GN];
+        continue;
+      }
+      const int32_t c = DI + i;
+      double cv = u->conv_b ? u->conv_b[c] : 0.0;
+      for (int32_t k = 0; k < W; ++k) cv += u->conv_w[(int64_t)c * W + k] * seq[(int64_t)(t + k) * CH + c];
+      bc[i] = d->silu ? cv / (1.0 + exp(-cv)) : cv;
+    }
     for (int32_t hh = 0; hh < H; ++hh) {
       const int32_t g = hh / hpg;
       const double z = u->dt_raw[(int64_t)t * H + hh] + u->dt_bias[hh];
@@ -319,20 +379,26 @@ int oracle_scan(const oracle_dims* d, int32_t S, const oracle_unit* u, double* y
       for (int32_t p = 0; p < P; ++p) {
         const int32_t c = hh * P + p;
         double cv = u->conv_b ? u->conv_b[c] : 0.0;
-        for (int32_t k = 0; k < W; ++k) cv += u->conv_w[(int64_t)c * W + k] * seq[(int64_t)(t + k) * DI + c];
+        for (int32_t k = 0; k < W; ++k) cv += u->conv_w[(int64_t)c * W + k] * seq[(int64_t)(t + k) * CH + c];
         if (d->silu) cv = cv / (1.0 + exp(-cv));
         double* hr = h + ((int64_t)hh * P + p) * N;
         double acc = 0.0;
         for (int32_t n = 0; n < N; ++n) {
-          hr[n] = dA * hr[n] + dtv * cv * u->B[((int64_t)t * G + g) * N + n];
-          acc += u->C[((int64_t)t * G + g) * N + n] * hr[n];
+          hr[n] = dA * hr[n] + dtv * cv * bc[g * N + n];
+          acc += bc[GN + g * N + n] * hr[n];
         }
-        y[(int64_t)t * DI + c] = acc + u->D[hh] * cv;
+        double out = acc + u->D[hh] * cv;
+        if (u->z) {
+          const double zz = u->z[(int64_t)t * DI + c];
+          out *= zz / (1.0 + exp(-zz));
+        }
+        y[(int64_t)t * DI + c] = out;
       }
     }
   }
   if (state_out) memcpy(state_out, h, sizeof(double) * (size_t)SZ);
-  if (window_out && W > 1) memcpy(window_out, seq + (int64_t)S * DI, sizeof(double) * (size_t)(W - 1) * DI);
+  if (window_out && W > 1) memcpy(window_out, seq + (int64_t)S * CH, sizeof(double) * (size_t)(W - 1) * CH);
+  free(bc);
   free(h);
   free(seq);
   return ORACLE_OK;

@@ -20,16 +20,22 @@
  *         the recurrence h_t = Abar (.) h_{t-1} + Bbar (.) X_t.
  *
  * Readings where the pages are silent (each listed in the design notes):
- * conv over x only, identity activation unless the SiLU flag is set, taps
+ * conv over x only (over x, B and C with the xbc option, the Mamba2
+ * convention), identity activation unless the SiLU flag is set, taps
  * in causal-conv1d order (weight W-1 multiplies the current token), the
  * SSM consumes the post-conv x, dt = softplus(dt_raw + dt_bias) with
  * softplus(z) = z for z > 20, dA = exp(dt * A), group of head h is
- * h / (H / G), parent -1 means "child of the root state".
+ * h / (H / G), parent -1 means "child of the root state".  The optional gate
+ * multiplies y by silu(z) ([LM] "why Mamba is hard to accelerate": Y is
+ * multiplied elementwise with Z).
  *
- * Layouts (row-major, one (layer, sequence) unit):
- *   x [T][H*P], B and C [T][G][N], dt_raw [T][H], window [W-1][H*P]
- *   (oldest row first), state [H][P][N], y [T][H][P];
- *   A, D, dt_bias [H]; conv_w [H*P][W]; conv_b [H*P] or NULL.
+ * Layouts (row-major, one (layer, sequence) unit), with CH = H*P conv
+ * channels, or H*P + 2*G*N with xbc (channel order: x, then B as [G][N],
+ * then C as [G][N]):
+ *   x [T][H*P], B and C [T][G][N], dt_raw [T][H], z [T][H*P] or NULL,
+ *   window [W-1][CH] (raw inputs of the last W-1 tokens, oldest row first),
+ *   state [H][P][N], y [T][H][P];
+ *   A, D, dt_bias [H]; conv_w [CH][W]; conv_b [CH] or NULL.
  */
 #ifndef SSM_ORACLE_H
 #define SSM_ORACLE_H
@@ -52,12 +58,13 @@ extern "C" {
 #define ORACLE_PLAN_UNUSED (-32768)
 
 typedef struct {
-  int32_t T, H, P, N, G, W, silu;
+  int32_t T, H, P, N, G, W, silu, xbc;
 } oracle_dims;
 
 typedef struct {
   const double *x, *B, *C, *dt_raw, *window, *state;
   const double *A, *D, *dt_bias, *conv_w, *conv_b;
+  const double* z; /* gate input [T][H*P], or NULL for no gate */
 } oracle_unit;
 
 int oracle_validate_tree(const int32_t* parent, int32_t T);

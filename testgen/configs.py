@@ -11,6 +11,10 @@ tokens; SpecMamba page, section 5.2).  Value distributions:
   D ~ N(0, 1) per (layer, head)
   root SSM state ~ N(0, 0.1), N(0, 1) for the stress workload
   conv weights ~ N(0, 0.5); no conv bias
+  gate input z ~ N(0, 1) (only with the gate option)
+
+With the xbc option (conv over x, B and C, the Mamba2 convention) the conv
+window, weights and bias span d_in + 2 G N channels: x, then B, then C.
 
 N(m, s) names the standard deviation s.  bf16 inputs are float32 draws
 rounded to nearest even.  Every tensor is a counter-based stream (seed,
@@ -29,7 +33,7 @@ from . import (DIST_NEG_EXP_UNIFORM, DIST_NORMAL, DIST_UNIFORM, as_f64, fill)
 SEED_BASE = 0x55D00000
 
 # stream ids, one per tensor
-S_X, S_B, S_C, S_DT, S_WIN, S_STATE, S_DTB, S_A, S_D, S_CONVW, S_CONVB = range(1, 12)
+S_X, S_B, S_C, S_DT, S_WIN, S_STATE, S_DTB, S_A, S_D, S_CONVW, S_CONVB, S_Z = range(1, 13)
 
 
 @dataclass(frozen=True)
@@ -49,10 +53,17 @@ class Config:
     tree: str
     silu: bool = False
     conv_bias: bool = False
+    xbc: bool = False
+    gate: bool = False
 
     @property
     def d_in(self) -> int:
         return self.H * self.P
+
+    @property
+    def conv_ch(self) -> int:
+        """Channels of the causal conv: x, or x, B and C with xbc."""
+        return self.H * self.P + (2 * self.G * self.N if self.xbc else 0)
 
     @property
     def seed(self) -> int:
@@ -272,14 +283,16 @@ class Inputs:
     dt_bias: np.ndarray
     conv_w: np.ndarray     # [L][d_in][W] float32
     conv_b: np.ndarray | None = None
+    z: np.ndarray | None = None   # [L][Bsz][T][d_in] gate input (gate option only)
     extra: dict = field(default_factory=dict)
 
 
 def tensor_shapes(cfg: Config) -> dict:
     L, Bsz, T, H, P, N, G, W, d = cfg.L, cfg.Bsz, cfg.T, cfg.H, cfg.P, cfg.N, cfg.G, cfg.W, cfg.d_in
+    ch = cfg.conv_ch
     return dict(x=(L, Bsz, T, d), B=(L, Bsz, T, G, N), C=(L, Bsz, T, G, N), dt_raw=(L, Bsz, T, H),
-                window=(L, Bsz, W - 1, d), state=(L, Bsz, H, P, N), A=(L, H), D=(L, H), dt_bias=(L, H),
-                conv_w=(L, d, W), conv_b=(L, d))
+                window=(L, Bsz, W - 1, ch), state=(L, Bsz, H, P, N), A=(L, H), D=(L, H), dt_bias=(L, H),
+                conv_w=(L, ch, W), conv_b=(L, ch), z=(L, Bsz, T, d))
 
 
 # (stream, dist, a, b, is_input_dtype)
@@ -296,6 +309,7 @@ def _specs(cfg: Config) -> dict:
         dt_bias=(S_DTB, DIST_UNIFORM, -4.0, -2.0, False),
         conv_w=(S_CONVW, DIST_NORMAL, 0.0, 0.5, False),
         conv_b=(S_CONVB, DIST_NORMAL, 0.0, 0.5, False),
+        z=(S_Z, DIST_NORMAL, 0.0, 1.0, True),
     )
 
 
@@ -308,7 +322,7 @@ def draw(cfg: Config, name: str, shape=None, offset: int = 0, nthreads=None) -> 
 def make_inputs(cfg: Config, nthreads=None, skip=()) -> Inputs:
     rng = np.random.Generator(np.random.PCG64(cfg.seed))
     parent, path, plen = make_trees(cfg, rng)
-    skip = set(skip) | (set() if cfg.conv_bias else {"conv_b"})
+    skip = set(skip) | (set() if cfg.conv_bias else {"conv_b"}) | (set() if cfg.gate else {"z"})
     t = {k: (None if k in skip else draw(cfg, k, nthreads=nthreads)) for k in tensor_shapes(cfg)}
     return Inputs(cfg=cfg, parent=parent, path=path, path_len=plen, **t)
 
@@ -317,14 +331,17 @@ def unit_offsets(cfg: Config, l: int, b: int) -> dict:
     """Flat element offset of the (layer l, sequence b) slice of each tensor."""
     L, Bsz, T, H, P, N, G, W, d = cfg.L, cfg.Bsz, cfg.T, cfg.H, cfg.P, cfg.N, cfg.G, cfg.W, cfg.d_in
     u = l * Bsz + b
-    return dict(x=u * T * d, B=u * T * G * N, C=u * T * G * N, dt_raw=u * T * H, window=u * (W - 1) * d,
-                state=u * H * P * N, A=l * H, D=l * H, dt_bias=l * H, conv_w=l * d * W, conv_b=l * d)
+    ch = cfg.conv_ch
+    return dict(x=u * T * d, B=u * T * G * N, C=u * T * G * N, dt_raw=u * T * H, window=u * (W - 1) * ch,
+                state=u * H * P * N, A=l * H, D=l * H, dt_bias=l * H, conv_w=l * ch * W, conv_b=l * ch,
+                z=u * T * d)
 
 
 def unit_shapes(cfg: Config) -> dict:
     T, H, P, N, G, W, d = cfg.T, cfg.H, cfg.P, cfg.N, cfg.G, cfg.W, cfg.d_in
-    return dict(x=(T, d), B=(T, G, N), C=(T, G, N), dt_raw=(T, H), window=(W - 1, d), state=(H, P, N),
-                A=(H,), D=(H,), dt_bias=(H,), conv_w=(d, W), conv_b=(d,))
+    ch = cfg.conv_ch
+    return dict(x=(T, d), B=(T, G, N), C=(T, G, N), dt_raw=(T, H), window=(W - 1, ch), state=(H, P, N),
+                A=(H,), D=(H,), dt_bias=(H,), conv_w=(ch, W), conv_b=(ch,), z=(T, d))
 
 
 def unit_f64(cfg: Config, l: int, b: int, inputs: Inputs | None = None) -> dict:
@@ -334,9 +351,9 @@ def unit_f64(cfg: Config, l: int, b: int, inputs: Inputs | None = None) -> dict:
     (bit-identical either way).
     """
     offs, shp = unit_offsets(cfg, l, b), unit_shapes(cfg)
-    out = {"conv_b": None}
+    out = {"conv_b": None, "z": None}
     for k in shp:
-        if k == "conv_b" and not cfg.conv_bias:
+        if (k == "conv_b" and not cfg.conv_bias) or (k == "z" and not cfg.gate):
             continue
         is_in = _specs(cfg)[k][4]
         if inputs is not None:

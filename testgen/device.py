@@ -27,7 +27,7 @@ def upload(inp, device="cuda") -> SimpleNamespace:
     ns.parent = torch.from_numpy(np.ascontiguousarray(inp.parent, np.int32)).to(device)
     ns.path = torch.from_numpy(np.ascontiguousarray(inp.path, np.int32)).to(device)
     ns.path_len = torch.from_numpy(np.ascontiguousarray(inp.path_len, np.int32)).to(device)
-    for k in ("x", "B", "C", "dt_raw", "window"):
+    for k in ("x", "B", "C", "dt_raw", "window", "z"):
         setattr(ns, k, tensor(getattr(inp, k), bf, device))
     for k in ("state", "A", "D", "dt_bias", "conv_w", "conv_b"):
         setattr(ns, k, tensor(getattr(inp, k), False, device))

@@ -44,7 +44,8 @@ class GpuCase:
         self.cfg = cfg
         self.inp = inp if inp is not None else C.make_inputs(cfg)
         self.g = upload(self.inp, device)
-        self.dims = m.make_dims(cfg.L, cfg.Bsz, cfg.T, cfg.H, cfg.P, cfg.N, cfg.G, cfg.W, cfg.bf16, cfg.silu, fifo)
+        self.dims = m.make_dims(cfg.L, cfg.Bsz, cfg.T, cfg.H, cfg.P, cfg.N, cfg.G, cfg.W, cfg.bf16, cfg.silu, fifo,
+                                cfg.xbc)
         self.prm = m.make_params(self.g.A, self.g.D, self.g.dt_bias, self.g.conv_w, self.g.conv_b)
         self.device = device
 
@@ -54,7 +55,7 @@ class GpuCase:
             y = t.full((cfg.L, cfg.Bsz, cfg.T, cfg.d_in), fill, dtype=t.float32, device=self.device)
         st = t.full((cfg.Bsz,), 12345, dtype=t.int32, device=self.device)
         g = self.g
-        m.verify(self.dims, self.prm, g.parent, g.x, g.B, g.C, g.dt_raw, g.window, g.state, y, st)
+        m.verify(self.dims, self.prm, g.parent, g.x, g.B, g.C, g.dt_raw, g.window, g.state, y, st, z=g.z)
         t.cuda.synchronize()
         return y, st
 
@@ -68,7 +69,8 @@ class GpuCase:
         else:
             s_out = t.full_like(s_in, -777.0)
             w_out = None if w_in is None else t.zeros_like(w_in)
-        m.commit(self.dims, self.prm, g.parent, g.path, g.path_len, g.x, g.B, g.dt_raw, w_in, s_in, w_out, s_out, st)
+        m.commit(self.dims, self.prm, g.parent, g.path, g.path_len, g.x, g.B, g.dt_raw, w_in, s_in, w_out, s_out, st,
+                 C=g.C if self.cfg.xbc else None)
         t.cuda.synchronize()
         return s_out, w_out, st
 

@@ -30,23 +30,29 @@ GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 # inputs
 # ----------------------------------------------------------------------------
 
-def rand_unit(rng, T, H, P, N, G, W, state_std=0.5, conv_b=False, S=None):
+def rand_unit(rng, T, H, P, N, G, W, state_std=0.5, conv_b=False, S=None, xbc=False, gate=False):
+    """Random unit; with xbc the conv (window, weights, bias) spans x, B and
+    C channels, with gate it carries z."""
     d = H * P
+    ch = d + (2 * G * N if xbc else 0)
     n = T if S is None else S
     u = dict(
         x=rng.normal(size=(n, d)), B=rng.normal(size=(n, G, N)), C=rng.normal(size=(n, G, N)),
-        dt_raw=rng.normal(size=(n, H)), window=rng.normal(size=(W - 1, d)),
+        dt_raw=rng.normal(size=(n, H)), window=rng.normal(size=(W - 1, ch)),
         state=rng.normal(scale=state_std, size=(H, P, N)), A=-np.exp(rng.uniform(0, np.log(16), size=H)),
-        D=rng.normal(size=H), dt_bias=rng.uniform(-4, -2, size=H), conv_w=rng.normal(scale=0.5, size=(d, W)),
+        D=rng.normal(size=H), dt_bias=rng.uniform(-4, -2, size=H), conv_w=rng.normal(scale=0.5, size=(ch, W)),
     )
-    u["conv_b"] = rng.normal(size=d) if conv_b else None
+    u["conv_b"] = rng.normal(size=ch) if conv_b else None
+    u["z"] = rng.normal(scale=2.0, size=(n, d)) if gate else None
     return u
 
 
 def take(u, idx):
     """Token-indexed unit made of the nodes idx (for scans along a path)."""
     v = dict(u)
-    for k in ("x", "B", "C", "dt_raw"):
+    for k in ("x", "B", "C", "dt_raw", "z"):
+        if u.get(k) is None:
+            continue
         v[k] = np.ascontiguousarray(u[k][list(idx)]) if len(idx) else u[k][:0].copy()
     return v
 
@@ -87,36 +93,46 @@ def close(a, b, tol=1e-10, what=""):
 # independent closed form
 # ----------------------------------------------------------------------------
 
-def closed_form_node(u, parent, v, H, P, N, G, W, silu=False):
+def closed_form_node(u, parent, v, H, P, N, G, W, silu=False, xbc=False):
     """y_v from cumulative log-decays along v's root path; no recurrence.
 
     With s_t = sum_{k<=t} dt_k A along the path (u_0 .. u_{m-1} = v):
       y_v = e^{s_{m-1}} C_v.h0 + sum_t e^{s_{m-1} - s_t} dt_t x~_t (C_v.B_t) + D x~_v
-    and x~ the causal conv (numpy.correlate) over (window rows, path x rows).
+    and x~ the causal conv (numpy.correlate) over (window rows, path x rows);
+    with xbc, B and C are the same conv of their own channels.  A gate input
+    z multiplies the result by z / (1 + e^-z).
     """
     path = root_path(parent, v)
     m = len(path)
-    d = H * P
-    seq = np.concatenate([u["window"].reshape(W - 1, d), u["x"][path]], axis=0)  # [(W-1)+m][d]
-    xt = np.empty((m, d))
-    for c in range(d):
+    d, gn = H * P, G * N
+    ch = d + (2 * gn if xbc else 0)
+    raw = np.concatenate([u["x"][path], u["B"][path].reshape(m, gn), u["C"][path].reshape(m, gn)], axis=1)[:, :ch]
+    seq = np.concatenate([u["window"].reshape(W - 1, ch), raw], axis=0)  # [(W-1)+m][ch]
+    conv = np.empty((m, ch))
+    for c in range(ch):
         col = np.correlate(seq[:, c], u["conv_w"][c], mode="valid")  # sum_k w[k] seq[t+k]
-        xt[:, c] = col + (u["conv_b"][c] if u.get("conv_b") is not None else 0.0)
+        conv[:, c] = col + (u["conv_b"][c] if u.get("conv_b") is not None else 0.0)
     if silu:
-        xt = xt / (1.0 + np.exp(-xt))
+        conv = conv / (1.0 + np.exp(-conv))
+    xt = conv[:, :d]
+    Bp = conv[:, d:d + gn].reshape(m, G, N) if xbc else u["B"][path]
+    Cp = conv[:, d + gn:].reshape(m, G, N) if xbc else u["C"][path]
     hpg = H // G
     y = np.empty(d)
     for h in range(H):
         g = h // hpg
         dt = np.logaddexp(0.0, u["dt_raw"][path, h] + u["dt_bias"][h])
         s = np.cumsum(dt * u["A"][h])
-        Cv = u["C"][v, g]
+        Cv = Cp[-1, g]
         for p in range(P):
             c = h * P + p
             tot = np.exp(s[-1]) * float(Cv @ u["state"][h, p])
-            for t, node in enumerate(path):
-                tot += np.exp(s[-1] - s[t]) * dt[t] * xt[t, c] * float(Cv @ u["B"][node, g])
+            for t in range(m):
+                tot += np.exp(s[-1] - s[t]) * dt[t] * xt[t, c] * float(Cv @ Bp[t, g])
             y[c] = tot + u["D"][h] * xt[-1, c]
+    if u.get("z") is not None:
+        z = u["z"][v]
+        y = y * z / (1.0 + np.exp(-z))
     return y
 
 
@@ -131,30 +147,44 @@ SHAPES = [  # (H, P, N, G, W, silu, conv_b)
     (2, 1, 2, 2, 1, False, False),
 ]
 
+# the Mamba2-convention options: (H, P, N, G, W, silu, conv_b, xbc, gate)
+SHAPES_X = [
+    (3, 2, 5, 1, 4, True, True, True, True),
+    (4, 3, 4, 2, 3, False, False, True, False),
+    (2, 2, 3, 1, 2, True, False, False, True),
+    (2, 1, 2, 2, 1, False, True, True, True),
+]
+
+
+def all_shapes():
+    """(H, P, N, G, W, silu, conv_b, xbc, gate) for the plain and the option shapes."""
+    return [s + (False, False) for s in SHAPES] + SHAPES_X
+
 
 def pin_chain_is_scan(o, seed=1):
     rng = np.random.default_rng(seed)
-    for (H, P, N, G, W, silu, cb) in SHAPES:
+    for (H, P, N, G, W, silu, cb, xbc, gate) in all_shapes():
         T = 7
-        u = rand_unit(rng, T, H, P, N, G, W, conv_b=cb)
+        u = rand_unit(rng, T, H, P, N, G, W, conv_b=cb, xbc=xbc, gate=gate)
         parent = np.arange(-1, T - 1, dtype=np.int32)
-        y, st, _ = o.verify(parent, u, H, P, N, G, W, silu)
+        y, st, _ = o.verify(parent, u, H, P, N, G, W, silu, xbc)
         assert st == 0
-        ys, _, _ = o.scan(u, T, H, P, N, G, W, silu)
-        close(y, ys, 1e-12, "chain vs scan %s" % ((H, P, N, G, W, silu, cb),))
+        ys, _, _ = o.scan(u, T, H, P, N, G, W, silu, xbc)
+        close(y, ys, 1e-12, "chain vs scan %s" % ((H, P, N, G, W, silu, cb, xbc, gate),))
 
 
 def pin_every_node_is_its_path_scan(o, seed=2, trees=6, T=10):
     rng = np.random.default_rng(seed)
-    for (H, P, N, G, W, silu, cb) in SHAPES[:2]:
+    shapes = all_shapes()
+    for (H, P, N, G, W, silu, cb, xbc, gate) in shapes[:2] + shapes[len(SHAPES):len(SHAPES) + 2]:
         for _ in range(trees):
             parent = _rand_parent(rng, T)
-            u = rand_unit(rng, T, H, P, N, G, W, conv_b=cb)
-            y, st, _ = o.verify(parent, u, H, P, N, G, W, silu)
+            u = rand_unit(rng, T, H, P, N, G, W, conv_b=cb, xbc=xbc, gate=gate)
+            y, st, _ = o.verify(parent, u, H, P, N, G, W, silu, xbc)
             assert st == 0
             for v in range(T):
                 pth = root_path(parent, v)
-                ys, _, _ = o.scan(take(u, pth), len(pth), H, P, N, G, W, silu)
+                ys, _, _ = o.scan(take(u, pth), len(pth), H, P, N, G, W, silu, xbc)
                 close(y[v], ys[-1], 1e-12, "node %d path scan" % v)
 
 
@@ -169,38 +199,42 @@ def _rand_parent(rng, T):
 CATALAN = [1, 1, 2, 5, 14, 42, 132, 429, 1430]
 
 
-def pin_bruteforce_forests(o, tmax=8, seed=3):
+def pin_bruteforce_forests(o, tmax=8, seed=3, tmax_options=6):
+    """Every BFS forest up to tmax nodes (up to tmax_options with the xbc
+    conv and the gate): every node's y equals the scan of its root path,
+    and committing that path equals the scan's state and window."""
     rng = np.random.default_rng(seed)
     H, P, N, G, W = 1, 2, 2, 1, 3
-    for T in range(0, tmax + 1):
-        forests = list(all_bfs_forests(T))
-        assert len(forests) == CATALAN[T], (T, len(forests))
-        u = rand_unit(rng, T, H, P, N, G, W)
-        # scans of every root path that occurs in any forest of this size
-        for parent in forests:
-            assert o.validate_tree(parent) == 0
-            y, st, _ = o.verify(parent, u, H, P, N, G, W)
-            assert st == 0
-            for v in range(T):
-                pth = root_path(parent, v)
-                ys, hs, ws = o.scan(take(u, pth), len(pth), H, P, N, G, W)
-                close(y[v], ys[-1], 1e-12, "forest %s node %d" % (parent.tolist(), v))
-                so, wo, cst = o.commit(parent, np.array(pth, np.int32), len(pth), u, H, P, N, G, W)
-                assert cst == 0
-                close(so, hs, 1e-12, "commit state")
-                assert np.array_equal(wo, ws), "commit window"
+    for opts in (False, True):
+        for T in range(0, (tmax_options if opts else tmax) + 1):
+            forests = list(all_bfs_forests(T))
+            assert len(forests) == CATALAN[T], (T, len(forests))
+            u = rand_unit(rng, T, H, P, N, G, W, xbc=opts, gate=opts)
+            # scans of every root path that occurs in any forest of this size
+            for parent in forests:
+                assert o.validate_tree(parent) == 0
+                y, st, _ = o.verify(parent, u, H, P, N, G, W, opts, opts)
+                assert st == 0
+                for v in range(T):
+                    pth = root_path(parent, v)
+                    ys, hs, ws = o.scan(take(u, pth), len(pth), H, P, N, G, W, opts, opts)
+                    close(y[v], ys[-1], 1e-12, "forest %s node %d" % (parent.tolist(), v))
+                    so, wo, cst = o.commit(parent, np.array(pth, np.int32), len(pth), u, H, P, N, G, W, opts, opts)
+                    assert cst == 0
+                    close(so, hs, 1e-12, "commit state")
+                    assert np.array_equal(wo, ws), "commit window"
 
 
 def pin_closed_form(o, seed=4):
     rng = np.random.default_rng(seed)
-    for (H, P, N, G, W, silu, cb) in SHAPES:
+    for (H, P, N, G, W, silu, cb, xbc, gate) in all_shapes():
         T = 9
         parent = _rand_parent(rng, T)
-        u = rand_unit(rng, T, H, P, N, G, W, conv_b=cb)
-        y, st, _ = o.verify(parent, u, H, P, N, G, W, silu)
+        u = rand_unit(rng, T, H, P, N, G, W, conv_b=cb, xbc=xbc, gate=gate)
+        y, st, _ = o.verify(parent, u, H, P, N, G, W, silu, xbc)
         assert st == 0
         for v in range(T):
-            close(y[v], closed_form_node(u, parent, v, H, P, N, G, W, silu), 1e-10, "closed form node %d" % v)
+            close(y[v], closed_form_node(u, parent, v, H, P, N, G, W, silu, xbc), 1e-10, "closed form node %d" % v)
 
 
 def pin_softplus_library(o):
@@ -290,42 +324,42 @@ def pin_special_cases(o, seed=6):
 
 def pin_commit(o, seed=7):
     rng = np.random.default_rng(seed)
-    for (H, P, N, G, W, silu, cb) in SHAPES:
+    for (H, P, N, G, W, silu, cb, xbc, gate) in all_shapes():
         T = 9
         parent = _rand_parent(rng, T)
-        u = rand_unit(rng, T + 1, H, P, N, G, W, conv_b=cb)
+        u = rand_unit(rng, T + 1, H, P, N, G, W, conv_b=cb, xbc=xbc, gate=gate)
         uT = take(u, range(T))
         # length 0 is the identity, bit for bit
-        so, wo, st = o.commit(parent, np.zeros(0, np.int32), 0, uT, H, P, N, G, W, silu)
+        so, wo, st = o.commit(parent, np.zeros(0, np.int32), 0, uT, H, P, N, G, W, silu, xbc)
         assert st == 0 and np.array_equal(so, uT["state"]) and np.array_equal(wo, uT["window"])
         # commit then a 1-node verify of the next token == scan over prefix + token
         leaf = int(rng.integers(T))
         pth = root_path(parent, leaf)
-        so, wo, st = o.commit(parent, np.array(pth, np.int32), len(pth), uT, H, P, N, G, W, silu)
+        so, wo, st = o.commit(parent, np.array(pth, np.int32), len(pth), uT, H, P, N, G, W, silu, xbc)
         assert st == 0
         nxt = dict(take(u, [T]), state=so, window=wo)
-        y1, st1, _ = o.verify(np.array([-1], np.int32), nxt, H, P, N, G, W, silu)
-        ys, hs, ws = o.scan(take(u, pth + [T]), len(pth) + 1, H, P, N, G, W, silu)
+        y1, st1, _ = o.verify(np.array([-1], np.int32), nxt, H, P, N, G, W, silu, xbc)
+        ys, hs, ws = o.scan(take(u, pth + [T]), len(pth) + 1, H, P, N, G, W, silu, xbc)
         close(y1[0], ys[-1], 1e-12, "commit then decode")
-        so2, wo2, _ = o.commit(np.array([-1], np.int32), np.array([0], np.int32), 1, nxt, H, P, N, G, W, silu)
+        so2, wo2, _ = o.commit(np.array([-1], np.int32), np.array([0], np.int32), 1, nxt, H, P, N, G, W, silu, xbc)
         close(so2, hs, 1e-12, "commit+commit state")
         assert np.array_equal(wo2, ws)
         # two commits along a split path == one commit of the whole path
         if len(pth) >= 2:
             k = len(pth) // 2
-            a, _, _ = o.commit(parent, np.array(pth[:k], np.int32), k, uT, H, P, N, G, W, silu)
+            a, _, _ = o.commit(parent, np.array(pth[:k], np.int32), k, uT, H, P, N, G, W, silu, xbc)
             sub = take(uT, pth[k:])
             sub_parent = np.arange(-1, len(pth) - k - 1, dtype=np.int32)
-            sa, wa, _ = o.commit(parent, np.array(pth[:k], np.int32), k, uT, H, P, N, G, W, silu)
+            sa, wa, _ = o.commit(parent, np.array(pth[:k], np.int32), k, uT, H, P, N, G, W, silu, xbc)
             sb, wb, _ = o.commit(sub_parent, np.arange(len(pth) - k, dtype=np.int32), len(pth) - k,
-                                 dict(sub, state=sa, window=wa), H, P, N, G, W, silu)
+                                 dict(sub, state=sa, window=wa), H, P, N, G, W, silu, xbc)
             close(sb, so, 1e-12, "two commits == one")
             assert np.array_equal(wb, wo)
             del a
         # an invalid path leaves outputs untouched and reports E_PATH
         if len(pth) >= 1:
             bad = np.array(pth[::-1], np.int32) if len(pth) > 1 else np.array([T], np.int32)
-            so3, wo3, st3 = o.commit(parent, bad, len(bad), uT, H, P, N, G, W, silu)
+            so3, wo3, st3 = o.commit(parent, bad, len(bad), uT, H, P, N, G, W, silu, xbc)
             assert st3 == -11 and np.array_equal(so3, uT["state"]) and np.array_equal(wo3, uT["window"])
 
 
@@ -457,6 +491,37 @@ def pin_golden(o):
             assert np.array_equal(wo.reshape(-1), np.array(cm["window"], np.float64).reshape(-1))
 
 
+
+
+def pin_option_special_cases(o, seed=8):
+    """The Mamba2-convention options against exact special cases:
+    (i) gate input z = 0 gives y = 0 exactly (silu(0) = 0);
+    (ii) with xbc, identity taps on the B and C channels (weight 1 on the
+    current token, no bias, no activation) give exactly the plain result,
+    since the convolved B and C then equal the raw ones;
+    (iii) a huge z makes the gate the identity times z up to e^-z terms."""
+    rng = np.random.default_rng(seed)
+    H, P, N, G, W = 2, 3, 4, 2, 4
+    T = 7
+    parent = np.array([-1, 0, 0, 1, 1, 2, 5], np.int32)
+    d, gn = H * P, G * N
+    u = rand_unit(rng, T, H, P, N, G, W, gate=True)
+    u["z"][:] = 0.0
+    y, st, _ = o.verify(parent, u, H, P, N, G, W)
+    assert st == 0 and np.all(y == 0.0), "gate with z = 0"
+    u = rand_unit(rng, T, H, P, N, G, W, xbc=True)
+    u["conv_w"][d:] = 0.0
+    u["conv_w"][d:, W - 1] = 1.0
+    y_x, st, _ = o.verify(parent, u, H, P, N, G, W, False, True)
+    plain = dict(u, window=np.ascontiguousarray(u["window"][:, :d]), conv_w=np.ascontiguousarray(u["conv_w"][:d]))
+    y_p, _, _ = o.verify(parent, plain, H, P, N, G, W)
+    assert st == 0 and np.array_equal(y_x, y_p), "xbc with identity B/C taps"
+    u = rand_unit(rng, T, H, P, N, G, W, gate=True)
+    y_g, _, _ = o.verify(parent, dict(u, z=np.full((T, d), 40.0)), H, P, N, G, W)
+    y_n, _, _ = o.verify(parent, dict(u, z=None), H, P, N, G, W)
+    close(y_g, 40.0 * y_n, 1e-15, "gate with z = 40")
+
+
 ALL_PINS = [pin_chain_is_scan, pin_every_node_is_its_path_scan, pin_bruteforce_forests, pin_closed_form,
             pin_softplus_library, pin_lfilter, pin_special_cases, pin_commit, pin_sibling_relabel,
-            pin_validator, pin_plan, pin_peak_from_verify, pin_golden]
+            pin_validator, pin_plan, pin_peak_from_verify, pin_golden, pin_option_special_cases]

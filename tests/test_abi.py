@@ -44,6 +44,7 @@ def test_header_constants_match_binding():
     assert consts["SSM_TREE_PLAN_UNUSED"] == m.PLAN_UNUSED
     assert consts["SSM_TREE_CONV_SILU"] == m.SSM_TREE_CONV_SILU
     assert consts["SSM_TREE_VERIFY_FIFO"] == m.SSM_TREE_VERIFY_FIFO
+    assert consts["SSM_TREE_CONV_XBC"] == m.SSM_TREE_CONV_XBC
 
 
 def test_status_strings():
@@ -77,7 +78,7 @@ def good_params(**kw):
 
 
 def verify_args(**kw):
-    a = dict(parent=fake(1), x=fake(2), B=fake(3), C=fake(4), dt_raw=fake(5), window=fake(6), state=fake(7),
+    a = dict(parent=fake(1), x=fake(2), B=fake(3), C=fake(4), dt_raw=fake(5), z=None, window=fake(6), state=fake(7),
              y=fake(8), status=fake(9))
     a.update(kw)
     return a
@@ -85,8 +86,8 @@ def verify_args(**kw):
 
 def call_verify(dims, params, **kw):
     a = verify_args(**kw)
-    return m.ssm_tree_verify(dims, params, a["parent"], a["x"], a["B"], a["C"], a["dt_raw"], a["window"], a["state"],
-                             a["y"], a["status"], None)
+    return m.ssm_tree_verify(dims, params, a["parent"], a["x"], a["B"], a["C"], a["dt_raw"], a["z"], a["window"],
+                             a["state"], a["y"], a["status"], None)
 
 
 @pytest.mark.parametrize("dkw,code", [
@@ -108,8 +109,8 @@ def test_dtype_flags_null_align_alias():
     d = good_dims()
     d.flags = 8
     assert call_verify(d, good_params()) == m.E_FLAGS
-    assert m.load().ssm_tree_verify(None, None, *([None] * 10)) == m.E_NULL
-    assert m.load().ssm_tree_verify(ctypes.byref(good_dims()), None, *([None] * 10)) == m.E_NULL
+    assert m.load().ssm_tree_verify(None, None, *([None] * 11)) == m.E_NULL
+    assert m.load().ssm_tree_verify(ctypes.byref(good_dims()), None, *([None] * 11)) == m.E_NULL
     assert call_verify(good_dims(), good_params(A=None)) == m.E_NULL
     for k in ("parent", "x", "B", "C", "dt_raw", "state", "y", "window"):
         assert call_verify(good_dims(), good_params(), **{k: None}) == m.E_NULL, k
@@ -123,10 +124,10 @@ def test_dtype_flags_null_align_alias():
 
 
 def call_commit(dims, params, **kw):
-    a = dict(parent=fake(1), path=fake(11), plen=fake(12), x=fake(2), B=fake(3), dt_raw=fake(5), win_in=fake(6),
-             state_in=fake(7), win_out=fake(16), state_out=fake(17), status=fake(9))
+    a = dict(parent=fake(1), path=fake(11), plen=fake(12), x=fake(2), B=fake(3), C=fake(4), dt_raw=fake(5),
+             win_in=fake(6), state_in=fake(7), win_out=fake(16), state_out=fake(17), status=fake(9))
     a.update(kw)
-    return m.ssm_tree_commit(dims, params, a["parent"], a["path"], a["plen"], a["x"], a["B"], a["dt_raw"],
+    return m.ssm_tree_commit(dims, params, a["parent"], a["path"], a["plen"], a["x"], a["B"], a["C"], a["dt_raw"],
                              a["win_in"], a["state_in"], a["win_out"], a["state_out"], a["status"], None)
 
 
@@ -143,14 +144,15 @@ def test_commit_host_checks():
 
 
 def call_commit_verify(dims, params, **kw):
-    a = dict(pparent=fake(1), path=fake(11), plen=fake(12), x_prev=fake(13), B_prev=fake(14), dt_prev=fake(15),
-             win_in=fake(6), state_in=fake(7), win_out=fake(16), state_out=fake(17), parent=fake(18), x=fake(2),
-             B=fake(3), C=fake(4), dt_raw=fake(5), y=fake(8), cst=fake(9), vst=fake(19))
+    a = dict(pparent=fake(1), path=fake(11), plen=fake(12), x_prev=fake(13), B_prev=fake(14), C_prev=fake(24),
+             dt_prev=fake(15), win_in=fake(6), state_in=fake(7), win_out=fake(16), state_out=fake(17),
+             parent=fake(18), x=fake(2), B=fake(3), C=fake(4), dt_raw=fake(5), z=None, y=fake(8), cst=fake(9),
+             vst=fake(19))
     a.update(kw)
     return m.ssm_tree_commit_verify(dims, params, a["pparent"], a["path"], a["plen"], a["x_prev"], a["B_prev"],
-                                    a["dt_prev"], a["win_in"], a["state_in"], a["win_out"], a["state_out"],
-                                    a["parent"], a["x"], a["B"], a["C"], a["dt_raw"], a["y"], a["cst"], a["vst"],
-                                    None)
+                                    a["C_prev"], a["dt_prev"], a["win_in"], a["state_in"], a["win_out"],
+                                    a["state_out"], a["parent"], a["x"], a["B"], a["C"], a["dt_raw"], a["z"],
+                                    a["y"], a["cst"], a["vst"], None)
 
 
 @pytest.mark.parametrize("dkw", [dict(), dict(T=40), dict(H=8, P=40, N=16)])

@@ -50,7 +50,8 @@ class Step:
         self.nxt = nxt if nxt is not None else C.make_inputs(self.ncfg, skip=NEXT_ONLY)
         self.gp = upload(self.prev)
         self.gn = self._upload_next(self.nxt)
-        self.dims = m.make_dims(cfg.L, cfg.Bsz, cfg.T, cfg.H, cfg.P, cfg.N, cfg.G, cfg.W, cfg.bf16, cfg.silu, fifo)
+        self.dims = m.make_dims(cfg.L, cfg.Bsz, cfg.T, cfg.H, cfg.P, cfg.N, cfg.G, cfg.W, cfg.bf16, cfg.silu, fifo,
+                                cfg.xbc)
         g = self.gp
         self.prm = m.make_params(g.A, g.D, g.dt_bias, g.conv_w, g.conv_b)
 
@@ -58,7 +59,7 @@ class Step:
         from types import SimpleNamespace
         ns = SimpleNamespace()
         ns.parent = torch.from_numpy(np.ascontiguousarray(nxt.parent, np.int32)).cuda()
-        for k in ("x", "B", "C", "dt_raw"):
+        for k in ("x", "B", "C", "dt_raw", "z"):
             setattr(ns, k, tensor(getattr(nxt, k), self.cfg.bf16))
         return ns
 
@@ -76,7 +77,8 @@ class Step:
         cst = torch.full((cfg.Bsz,), 12345, dtype=torch.int32, device="cuda")
         vst = torch.full((cfg.Bsz,), 12345, dtype=torch.int32, device="cuda")
         m.commit_verify(self.dims, self.prm, gp.parent, gp.path, gp.path_len, gp.x, gp.B, gp.dt_raw, w_in, s_in,
-                        w_out, s_out, gn.parent, gn.x, gn.B, gn.C, gn.dt_raw, y, cst, vst)
+                        w_out, s_out, gn.parent, gn.x, gn.B, gn.C, gn.dt_raw, y, cst, vst,
+                        C_prev=gp.C if cfg.xbc else None, z=gn.z)
         torch.cuda.synchronize()
         return s_out, w_out, y, cst, vst
 
@@ -84,7 +86,10 @@ class Step:
     def next_unit(self, l, b, state, window, params):
         shp = C.unit_shapes(self.cfg)
         u = dict(params)
-        for k in ("x", "B", "C", "dt_raw"):
+        for k in ("x", "B", "C", "dt_raw", "z"):
+            if getattr(self.nxt, k) is None:
+                u[k] = None
+                continue
             u[k] = as_f64(getattr(self.nxt, k)[l, b], self.cfg.bf16).reshape(shp[k])
         u["state"] = state
         u["window"] = window
@@ -94,7 +99,7 @@ class Step:
         """{(l, b): (state_out, window_out, commit status, y, verify status)}."""
         cfg, prev, nxt = self.cfg, self.prev, self.nxt
         o = oracle.get()
-        a = (cfg.H, cfg.P, cfg.N, cfg.G, cfg.W, cfg.silu)
+        a = (cfg.H, cfg.P, cfg.N, cfg.G, cfg.W, cfg.silu, cfg.xbc)
 
         def one(lb):
             l, b = lb

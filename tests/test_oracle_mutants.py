@@ -22,6 +22,9 @@ MUTANTS = {
     11: "validator accepts non-monotone parent[]",
     13: "commit applies the decay twice",
     14: "group of head h taken as h % G",
+    15: "xbc: B channels convolved with the C channels' weights",
+    16: "gate multiplies by sigmoid(z) instead of silu(z)",
+    17: "xbc: commit shifts only x, not B and C, into the window",
 }
 
 FAST_PINS = [pins.pin_chain_is_scan, pins.pin_closed_form, pins.pin_softplus_library, pins.pin_commit,
