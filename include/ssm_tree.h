@@ -67,10 +67,11 @@ extern "C" {
 /* The causal conv runs over x, B and C (the Mamba2 convention: in_proj's
  * xBC passes conv1d as a whole) instead of over x only.  The conv window,
  * conv_w and conv_b then span CH = H*P + 2*G*N channels in the order x,
- * B [G][N], C [G][N]; the SSM uses the convolved B and C.  Supported by the
- * trees of at most 16 nodes with a headdim that is a multiple of 16 in
- * ssm_tree_verify and ssm_tree_commit_verify, and by ssm_tree_commit for
- * every supported shape; other combinations return SSM_TREE_E_DIMS. */
+ * B [G][N], C [G][N]; the SSM uses the convolved B and C.  Supported by
+ * ssm_tree_verify and ssm_tree_commit_verify for trees of 1 to 16 nodes
+ * with a headdim that is a multiple of 16 (not with SSM_TREE_VERIFY_FIFO),
+ * and by ssm_tree_commit for every supported shape; other combinations
+ * return SSM_TREE_E_DIMS. */
 #define SSM_TREE_CONV_XBC 4
 /* ssm_tree_verify computes every child state explicitly, walking the tree
  * breadth-first with a FIFO of live states (SpecMamba page sec. 3.2), instead

@@ -123,6 +123,31 @@ int ssm_tree_verify(const ssm_tree_dims* dims, const ssm_tree_params* params, co
     for (const Range& r : ins)
       if (overlaps(rs, r)) return SSM_TREE_E_ALIAS;
   }
+  if (d.xbc || z) {
+    // the options run on the fused round's kernel with nothing to commit:
+    // no path length, no state or window output
+    CommitVerifyArgs a;
+    memset(&a, 0, sizeof(a));
+    a.d = d;
+    a.prm = Params{params->A, params->D, params->dt_bias, params->conv_w, params->conv_b};
+    a.parent_prev = parent;  // read but unused: the commit is empty
+    a.path = parent;
+    a.x_prev = x;
+    a.B_prev = B;
+    a.C_prev = C;
+    a.dt_prev = dt_raw;
+    a.window_in = conv_window;
+    a.state_in = state;
+    a.parent = parent;
+    a.x = x;
+    a.B = B;
+    a.C = C;
+    a.dt_raw = dt_raw;
+    a.z = z;
+    a.y = y;
+    a.verify_status = seq_status;
+    return launch_commit_verify(a, dims->in_dtype == SSM_TREE_BF16, s);
+  }
   VerifyArgs a;
   a.d = d;
   a.prm = Params{params->A, params->D, params->dt_bias, params->conv_w, params->conv_b};

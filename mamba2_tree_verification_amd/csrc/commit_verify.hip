@@ -204,7 +204,9 @@ __global__ void __launch_bounds__(kCvWaves * kWave) commit_verify_kernel(CommitV
     r_path = a.path[(int64_t)b * T + tid];
     r_par = a.parent[(int64_t)b * T + tid];
   }
-  if (tid == kCvWaves * kWave - 1) r_len = a.path_len[b];
+  // verify-only use (the options of ssm_tree_verify): no path length means
+  // nothing to commit, and no state or window output is written
+  if (tid == kCvWaves * kWave - 1) r_len = (!OPT || a.path_len) ? a.path_len[b] : 0;
 
   // x rows: thread (v, q) holds channels 4 q .. 4 q + 3 of node v
   const int xv = tid >> 4, xq = (tid & 15) * 4;
@@ -467,7 +469,7 @@ __global__ void __launch_bounds__(kCvWaves * kWave) commit_verify_kernel(CommitV
       hist[0] = xv;
     }
     // new window row r (oldest first) = element len + r of (old window, path x), bit for bit
-    if (W > 1) {
+    if (W > 1 && (!OPT || a.window_out)) {
       TIn* win_out = reinterpret_cast<TIn*>(a.window_out) + unit * (W - 1) * (int64_t)CH + c;
 #pragma unroll
       for (int r = 0; r < 3; ++r) {
@@ -572,9 +574,11 @@ __global__ void __launch_bounds__(kCvWaves * kWave) commit_verify_kernel(CommitV
         hq[gg].w = fmaf(dA, hq[gg].w, cx * bq.w);
       }
     }
-    float* so = a.state_out + (unit * DI + c0 + row) * (int64_t)N + 4 * k;
+    if (!OPT || a.state_out) {
+      float* so = a.state_out + (unit * DI + c0 + row) * (int64_t)N + 4 * k;
 #pragma unroll
-    for (int gg = 0; gg < NG; ++gg) *reinterpret_cast<f32x4*>(so + 16 * gg) = hq[gg];
+      for (int gg = 0; gg < NG; ++gg) *reinterpret_cast<f32x4*>(so + 16 * gg) = hq[gg];
+    }
 
     // C . h on the matrix cores: lane (c + 16 q) ends with (C_{4q+r} . h_c)
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -651,7 +655,7 @@ int launch_cv_o(const CommitVerifyArgs& a, hipStream_t s) {
   dim3 grid(a.d.d_in / kCvRows, a.d.Bsz, a.d.L);
   hipLaunchKernelGGL((commit_verify_kernel<TIn, NG, OPT>), grid, dim3(kCvWaves * kWave), lds, s, a);
   if (hipGetLastError() != hipSuccess) return SSM_TREE_E_HIP;
-  if (a.d.xbc) {  // the window's B and C rows, after every reader of the old ones
+  if (a.d.xbc && a.window_out) {  // the window's B and C rows, after every reader of the old ones
     WindowBcArgs w{a.d, a.parent_prev, a.path, a.path_len, a.B_prev, a.C_prev, a.window_in, a.window_out, 1};
     if (launch_window_bc(w, sizeof(TIn) == 2, s) != hipSuccess) return SSM_TREE_E_HIP;
   }

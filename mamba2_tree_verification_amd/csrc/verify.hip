@@ -659,8 +659,12 @@ int launch_verify_mfma(const VerifyArgs& a, bool bf16, hipStream_t s);
 
 int launch_verify_fifo(const VerifyArgs& a, bool bf16, hipStream_t s);
 
-// SSM_TREE_CONV_XBC and the gate: not yet taken by any verify kernel.
-bool verify_options_supported(const Dims& d, bool gate) { return !d.xbc && !gate; }
+// SSM_TREE_CONV_XBC and the gate: taken on the fused round's shapes, whose
+// kernel then runs with nothing to commit (see ssm_tree_verify).
+bool commit_verify_fused_applies(const Dims& d);
+bool verify_options_supported(const Dims& d, bool gate) {
+  return (!d.xbc && !gate) || (!d.fifo && commit_verify_fused_applies(d));
+}
 
 int launch_verify(const VerifyArgs& a, bool bf16, hipStream_t s) {
   if (a.d.fifo) return launch_verify_fifo(a, bf16, s);

@@ -5,9 +5,10 @@ in_proj's xBC passes conv1d as a whole) and the output gate y * silu(z)
 elementwise with Z).
 
 ssm_tree_commit takes the xBC conv for every shape; ssm_tree_commit_verify
-takes both options on its fused shapes (trees of at most 16 nodes, headdim
-a multiple of 16); every other combination must be refused on the host
-with SSM_TREE_E_DIMS before anything is enqueued.  Tolerance as elsewhere:
+and ssm_tree_verify take both options on the fused round's shapes (trees
+of at most 16 nodes, headdim a multiple of 16); every other combination
+must be refused on the host with SSM_TREE_E_DIMS before anything is
+enqueued.  Tolerance as elsewhere:
 |gpu - oracle| <= 1e-5 + 1e-4 |oracle|; windows and statuses exactly.
 """
 import numpy as np
@@ -19,7 +20,8 @@ import mamba2_tree_verification_amd as m  # noqa: E402
 import oracle  # noqa: E402
 from testgen import configs as C  # noqa: E402
 from testgen.device import upload  # noqa: E402
-from tests.gpu_util import GpuCase, assert_close, check_commit, log, sample_units, window_f64  # noqa: E402
+from tests.gpu_util import (GpuCase, assert_close, check_commit, check_verify, log, sample_units,  # noqa: E402
+                            window_f64)
 from tests.test_gpu_commit_verify import Step, check  # noqa: E402
 
 pytestmark = pytest.mark.gpu
@@ -108,6 +110,34 @@ def test_round_options(spec, inplace):
     check(step, out, [(l, b) for l in range(cfg.L) for b in range(cfg.Bsz)])
 
 
+@pytest.mark.parametrize("spec", ROUND_SPECS, ids=lambda s: "T%dH%dP%dN%dG%dW%d%s%s%s" % (
+    s[:6] + ("bf" if s[6] else "f32", "X" if s[9] else "", "Z" if s[10] else "")))
+def test_verify_options(spec):
+    """ssm_tree_verify alone with the options (the fused kernel with nothing
+    to commit): y against the oracle's verify, state and window untouched."""
+    T, H, P, N, G, W, bf16, silu, cb, xbc, gate = spec
+    cfg = C.Config(200 + ROUND_SPECS.index(spec), "opt-verify", 2, 4, T, H, P, N, G, W, bf16, 0.5, "forest", silu,
+                   cb, xbc, gate)
+    log("verify options %s" % (spec,))
+    inp = C.make_inputs(cfg)
+    inp.parent[3, min(2, T - 1)] = 5 if T > 2 else -2  # one invalid tree
+    case = GpuCase(cfg, inp)
+    s0, w0 = case.g.state.clone(), case.g.window.clone()
+    y, st = case.verify()
+    assert torch.equal(case.g.state, s0) and torch.equal(case.g.window, w0)
+    assert st.cpu().numpy()[3] == m.E_TREE
+    check_verify(case, y, st, [(l, b) for l in range(cfg.L) for b in range(cfg.Bsz)])
+
+
+def test_verify_options_full_size():
+    cfg = C.CONFIGS[3].replace(cid=210, silu=True, xbc=True, gate=True)
+    case = GpuCase(cfg)
+    y, st = case.verify()
+    assert not torch.isnan(y).any()
+    units = sample_units(cfg, 6, np.random.default_rng(210), [(0, 0), (cfg.L - 1, cfg.Bsz - 1)])
+    check_verify(case, y, st, units)
+
+
 def test_round_options_full_size():
     """The 2.7B batch-16 tree-16 workload with both options (Mamba2
     convention: SiLU over the xBC conv, gate), sampled units."""
@@ -188,13 +218,20 @@ def test_draft_decode_with_options():
 # ----------------------------------------------------------------------------
 
 def test_unsupported_option_combinations_refused():
-    # verify alone: no verify kernel takes the options yet
-    cfg = _cfg(190)
-    case = GpuCase(cfg)
-    y = torch.full((cfg.L, cfg.Bsz, cfg.T, cfg.d_in), 5.0, device="cuda")
+    # verify alone on a shape the fused kernel does not take (T > 16), and
+    # with the FIFO walk: refused, y untouched
+    for kw in (dict(T=20), dict(P=40, H=8)):
+        cfg = _cfg(190, **kw)
+        case = GpuCase(cfg)
+        y = torch.full((cfg.L, cfg.Bsz, cfg.T, cfg.d_in), 5.0, device="cuda")
+        with pytest.raises(m.SsmTreeError) as e:
+            case.verify(y=y)
+        assert e.value.code == m.E_DIMS and (y == 5.0).all()
+    cfg = _cfg(192)
+    case = GpuCase(cfg, fifo=True)
     with pytest.raises(m.SsmTreeError) as e:
-        case.verify(y=y)
-    assert e.value.code == m.E_DIMS and (y == 5.0).all()
+        case.verify()
+    assert e.value.code == m.E_DIMS
     # the fused round on a shape it does not fuse (T > 16): the two calls would
     # need verify to take the options; nothing may run, the state stays
     cfg = _cfg(191, T=20)
