@@ -286,6 +286,52 @@ def draft_decode(torch, m, C, upload, threads, timed, steps=15):
             "note": "one-node ssm_tree_commit_verify per draft token (all layers in one call); not in the step"}
 
 
+def options_round(torch, m, C, cfg, g, g2, state, timed, threads, path_lens):
+    """The same decode round with the Mamba2-convention options: SiLU over
+    the conv of x, B and C (SSM_TREE_CONV_XBC) and the output gate
+    y * silu(z).  The window, conv weights and gate inputs of the option
+    shapes are drawn for the workload; trees, state and the other inputs are
+    the bench's own.  Not part of the step; reported apart."""
+    from testgen.device import tensor
+    co = cfg.replace(cid=cfg.cid + 600, silu=True, xbc=True, gate=True)
+    win = tensor(C.draw(co, "window", nthreads=threads), cfg.bf16)
+    cw = tensor(C.draw(co, "conv_w", nthreads=threads), False)
+    zs = [tensor(C.draw(co.replace(cid=co.cid + i), "z", nthreads=threads), cfg.bf16) for i in range(2)]
+    dims = m.make_dims(cfg.L, cfg.Bsz, cfg.T, cfg.H, cfg.P, cfg.N, cfg.G, cfg.W, cfg.bf16, True, xbc=True)
+    prm = m.make_params(g.A, g.D, g.dt_bias, cw, None)
+    y = torch.empty((cfg.L, cfg.Bsz, cfg.T, cfg.d_in), dtype=torch.float32, device="cuda")
+    cst = torch.empty((cfg.Bsz,), dtype=torch.int32, device="cuda")
+    vst = torch.empty_like(cst)
+    trees = (g, g2)
+    k = [0]
+
+    def step():
+        prev, nxt = trees[k[0] % 2], trees[(k[0] + 1) % 2]
+        m.commit_verify(dims, prm, prev.parent, prev.path, prev.path_len, prev.x, prev.B, prev.dt_raw, win, state,
+                        win, state, nxt.parent, nxt.x, nxt.B, nxt.C, nxt.dt_raw, y, cst, vst, C_prev=prev.C,
+                        z=zs[(k[0] + 1) % 2])
+        k[0] += 1
+
+    ms = timed(step, reps=9)
+    torch.cuda.synchronize()
+    if not (cst.cpu() == 0).all() or not (vst.cpu() == 0).all() or torch.isnan(y).any():
+        raise SystemExit("bench: the option round produced a bad status or NaN")
+    e = cfg.e
+    gn = cfg.G * cfg.N
+    plain = [algorithmic_bytes(cfg, pl)["commit_verify"] for pl in path_lens]
+    acc = [int(sum(int(n) for n in pl)) for pl in path_lens]
+    # extra: the window's B and C rows read and written, the gate input, and
+    # the C row of every accepted node
+    extra = [cfg.L * (cfg.Bsz * (2 * (cfg.W - 1) * 2 * gn * e + cfg.T * cfg.d_in * e) + a * gn * e) for a in acc]
+    nbytes = (sum(plain) + sum(extra)) // 2
+    avg = sum(ms) / len(ms)
+    ach = nbytes / (avg * 1e-3) / 1e9
+    return {"options": "SiLU over the conv of x, B and C; y * silu(z)", "ms": round(avg, 4),
+            "ms_min": round(min(ms), 4), "bytes": nbytes, "GBps": round(ach, 1),
+            "frac": round(ach / HBM_PEAK_GBS, 4),
+            "node_layers_per_s": round(cfg.L * cfg.Bsz * cfg.T / (avg * 1e-3), 1), "note": "not in the step"}
+
+
 def hbm_probe(torch, nbytes=4 << 30, reps=10):
     """Plain device copy (torch copy_) and read (torch sum) bandwidth over
     buffers far larger than the 256 MB last-level cache."""
@@ -415,6 +461,7 @@ def main(argv=None):
 
     per_layer = per_layer_round(torch, m, cfg, g, g2, state, window, y, st_c, st_v, timed)
     draft = draft_decode(torch, m, C, upload, args.threads, timed)
+    opts = options_round(torch, m, C, cfg, g, g2, state, timed, args.threads, (inp.path_len, inp2.path_len))
 
     ab = algorithmic_bytes(cfg, inp.path_len)
     ab2 = algorithmic_bytes(cfg, inp2.path_len)
@@ -464,6 +511,7 @@ def main(argv=None):
         "two_call_step_ms": round(avg(ver_ms) + avg(com_ms), 4),
         "per_layer": per_layer,
         "draft_decode": draft,
+        "options_round": opts,
         "param_bytes_per_call": ab["params"],
         "verify_hbm_frac": kern["verify"]["roofline"]["frac"],
     }
