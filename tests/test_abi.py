@@ -192,3 +192,41 @@ def test_binding_refuses_cpu_tensors():
     t = torch.zeros(4)
     with pytest.raises(ValueError):
         m.make_params(t, t, t, t)
+
+
+def test_option_host_checks():
+    """The xBC conv and the gate: null, alignment and alias checks on their
+    arguments, and refusal of shapes no kernel takes (nothing launches)."""
+    p = good_params()
+    dx = good_dims()
+    dx.flags = m.SSM_TREE_CONV_XBC
+    # verify: the gate input is checked like any input
+    assert call_verify(good_dims(), p, z=fake(30, 8)) == m.E_ALIGN
+    assert call_verify(good_dims(), p, z=fake(8)) == m.E_ALIAS           # z over y
+    assert call_verify(good_dims(), p, z=fake(30), status=fake(30, 64)) == m.E_ALIAS
+    # shapes no kernel takes with an option: T > 16, headdim not a multiple of 16, the FIFO walk
+    assert call_verify(good_dims(T=20), p, z=fake(30)) == m.E_DIMS
+    assert call_verify(good_dims(H=8, P=40), p, z=fake(30)) == m.E_DIMS
+    d = good_dims(T=20)
+    d.flags = m.SSM_TREE_CONV_XBC
+    assert call_verify(d, p) == m.E_DIMS
+    d = good_dims()
+    d.flags = m.SSM_TREE_VERIFY_FIFO
+    assert call_verify(d, p, z=fake(30)) == m.E_DIMS
+    # commit with xBC: C is required and checked; the window spans d_in + 2GN channels
+    assert call_commit(dx, p, C=None) == m.E_NULL
+    assert call_commit(dx, p, C=fake(4, 8)) == m.E_ALIGN
+    assert call_commit(dx, p, C=fake(17)) == m.E_ALIAS                    # C under state_out
+    # without xBC, C is ignored (may be NULL or anything)
+    assert call_commit(good_dims(), p, C=None, plen=None) == m.E_NULL     # fails on path_len, not C
+    # 2 layers x 3 sequences x 3 rows x (256 + 256) channels x 2 bytes = 18432 bytes: a window_out starting
+    # 10000 bytes into window_in (past the 9216 bytes of x-only rows) overlaps it with rows d_in + 2GN wide
+    assert call_commit(dx, p, win_out=fake(6, 10000)) == m.E_ALIAS
+    # the fused round
+    assert call_commit_verify(dx, p, C_prev=None) == m.E_NULL
+    assert call_commit_verify(good_dims(), p, z=fake(8)) == m.E_ALIAS    # z over y
+    assert call_commit_verify(good_dims(), p, z=fake(30, 8)) == m.E_ALIGN
+    assert call_commit_verify(good_dims(T=20), p, z=fake(30)) == m.E_DIMS
+    d = good_dims(T=20)
+    d.flags = m.SSM_TREE_CONV_XBC
+    assert call_commit_verify(d, p) == m.E_DIMS
