@@ -466,7 +466,8 @@ def main(argv=None):
     if not args.no_extras:
         per_layer = per_layer_round(torch, m, cfg, g, g2, state, window, y, st_c, st_v, timed)
         draft = draft_decode(torch, m, C, upload, args.threads, timed)
-        opts = options_round(torch, m, C, cfg, g, g2, state, timed, args.threads, (inp.path_len, inp2.path_len))
+        if 1 <= cfg.T <= 16 and cfg.P % 16 == 0:  # the shapes the options run on
+            opts = options_round(torch, m, C, cfg, g, g2, state, timed, args.threads, (inp.path_len, inp2.path_len))
 
     ab = algorithmic_bytes(cfg, inp.path_len)
     ab2 = algorithmic_bytes(cfg, inp2.path_len)
@@ -483,12 +484,25 @@ def main(argv=None):
         return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": tr}
 
+    # verify's arithmetic: C . h0 is 2 T flops per root-state element (the
+    # path terms are O(T^2) per channel and left out); on the matrix cores for
+    # trees of at most 64 nodes with headdim % 16 == 0 (and 64-channel blocks
+    # per B/C group), else on the vector ALU without packed fp32
+    # (78.6 TFLOP/s = 256 CUs x 64 FMA lanes x 2 x 2.4 GHz)
+    on_mfma = 1 <= cfg.T <= 64 and cfg.P % 16 == 0 and (cfg.d_in // cfg.G) % 64 == 0
+    vflops = 2 * cfg.L * cfg.Bsz * cfg.T * cfg.H * cfg.P * cfg.N
+    vpeak = 157.3 if on_mfma else 78.6
+    vach = vflops / (avg(ver_ms) * 1e-3) / 1e12
+    vcompute = {"engine": "mfma fp32" if on_mfma else "valu fp32", "flops": vflops, "achieved": round(vach, 2),
+                "peak": vpeak, "unit": "TFLOP/s", "frac": round(vach / vpeak, 4)}
+
     kern = {"commit_verify": dict(ms=round(avg(cv_ms), 4), ms_min=round(min(cv_ms), 4), bytes=cvb,
                                   node_layers_per_s=round(node_layers / (avg(cv_ms) * 1e-3), 1),
                                   roofline=roof("commit_verify", cvb, avg(cv_ms))),
             "verify": dict(ms=round(avg(ver_ms), 4), ms_min=round(min(ver_ms), 4), bytes=ab["verify"],
                            node_layers_per_s=round(node_layers / (avg(ver_ms) * 1e-3), 1),
-                           roofline=roof("verify", ab["verify"], avg(ver_ms)), note="not in the step"),
+                           roofline=roof("verify", ab["verify"], avg(ver_ms)), compute=vcompute,
+                           note="not in the step"),
             "commit": dict(ms=round(avg(com_ms), 4), ms_min=round(min(com_ms), 4), bytes=ab["commit"],
                            roofline=roof("commit", ab["commit"], avg(com_ms)), note="not in the step"),
             "verify_fifo_walk": dict(ms=round(avg(fifo_ms), 4), bytes=ab["verify"],

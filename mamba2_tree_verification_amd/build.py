@@ -15,7 +15,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libssm_tree.so")
-SOURCES = ["api.hip", "verify.hip", "verify_mfma.hip", "verify_fifo.hip", "commit.hip", "commit_verify.hip", "plan.hip"]
+SOURCES = ["api.hip", "verify.hip", "verify_mfma.hip", "verify_tt.hip", "verify_fifo.hip", "commit.hip", "commit_verify.hip",
+           "plan.hip"]
 ARCH = "gfx950"
 
 

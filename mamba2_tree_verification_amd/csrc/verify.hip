@@ -666,9 +666,16 @@ bool verify_options_supported(const Dims& d, bool gate) {
   return (!d.xbc && !gate) || (!d.fifo && commit_verify_fused_applies(d));
 }
 
+bool tt_verify_applies(const Dims& d);
+int launch_verify_tt(const VerifyArgs& a, bool bf16, hipStream_t s);
+
 int launch_verify(const VerifyArgs& a, bool bf16, hipStream_t s) {
   if (a.d.fifo) return launch_verify_fifo(a, bf16, s);
   if (mfma_verify_applies(a.d)) return launch_verify_mfma(a, bf16, s);
+  if (tt_verify_applies(a.d)) {
+    const int st = launch_verify_tt(a, bf16, s);
+    if (st != SSM_TREE_E_DIMS) return st;  // E_DIMS: its LDS does not fit this shape, nothing launched
+  }
   return bf16 ? launch_in<bf16_t>(a, s) : launch_in<float>(a, s);
 }
 

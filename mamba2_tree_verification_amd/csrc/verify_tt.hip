@@ -1,0 +1,405 @@
+// verify_tt.hip - ssm_tree_verify for trees of 17 to 64 nodes, on the gfx950
+// matrix cores.
+//
+// The root projection of verify_mfma.hip (SpecMamba page sec. 3.2
+// recurrence, unrolled along each root path):
+//   y_v[c] = a_v (C_v . h0[c]) + sum_{u on path(v)} M_h[v][u] x~_u[c],
+//   M_h[v][u] = exp(S_v - S_u) dt_u (C_v . B_u), plus D_h when u = v,
+//   a_v = exp(S_v), S_v = sum of dt * A over v's root path,
+// with the tree padded to TT tiles of 16 nodes.  At 64 nodes C . h0 is 32
+// flop per state byte, above the fp32 matrix-core ridge (19.7 flop/B) and
+// far above the vector ALU's (9.8 without packed fp32): the product runs on
+// v_mfma_f32_16x16x4_f32 in TT row tiles, and M_h . X~ over the
+// lower-triangular tile pairs (an ancestor's index is below its
+// descendant's).
+//
+// Mapping.  A workgroup of 4 waves owns one (layer, sequence) and NBLK
+// consecutive blocks of 64 channels inside one B/C group; wave w owns
+// channels 16 w .. 16 w + 15 of a block, in the MFMA B-operand layout
+// (lane j + 16 k holds columns 16 gg + 4 k .. + 3 of channel j).  The tree
+// bookkeeping, the C rows and the C_v . B_u dots (formed once for the NBLK
+// blocks, with B rows as the A operand so that the result lands in the
+// layout the path terms read) stay in LDS.  Per block: conv outputs and the
+// heads' S and dt, then C . h0 (the next block's state is loaded as soon as
+// each column group has been consumed), the path terms, and y staged in LDS
+// and stored as whole 256-byte row segments.
+#include "common.h"
+
+namespace ssmt {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kTtRows = 64;   // channels per block
+constexpr int kTtWaves = 4;
+constexpr int kTtThreads = kTtWaves * kWave;
+constexpr int kTtMaxT = 64;
+
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+template <typename TIn>
+__device__ __forceinline__ f32x4 load4(const TIn* p);
+template <>
+__device__ __forceinline__ f32x4 load4<float>(const float* p) {
+  return *reinterpret_cast<const f32x4*>(p);
+}
+template <>
+__device__ __forceinline__ f32x4 load4<bf16_t>(const bf16_t* p) {
+  const u32x2 w = *reinterpret_cast<const u32x2*>(p);
+  f32x4 r;
+  r.x = __uint_as_float(w.x << 16);
+  r.y = __uint_as_float(w.x & 0xFFFF0000u);
+  r.z = __uint_as_float(w.y << 16);
+  r.w = __uint_as_float(w.y & 0xFFFF0000u);
+  return r;
+}
+
+template <int E>
+struct Raw4;
+template <>
+struct Raw4<2> {
+  typedef u32x2 T;
+};
+template <>
+struct Raw4<4> {
+  typedef u32x4 T;
+};
+
+// conv outputs [channel][node] in the MFMA B-operand layout: quad q (nodes
+// 4 q .. 4 q + 3) of channel row c sits at quad q ^ (c & 15), so that the 16
+// channels a wave reads at once fall on different banks
+__device__ __forceinline__ int xt_at(int c, int v) { return c * kTtMaxT + 4 * ((v >> 2) ^ (c & 15)) + (v & 3); }
+
+// LDS layout (byte offsets)
+struct TtLds {
+  int parent, anc, cidx, misc, C, cbt, X, Y, win, So, S2, dt, D, cw, cb, total, row;
+  __host__ __device__ TtLds(int N, int E) {
+    int o = 0;
+    row = N * E + 16;                          // staged B / C row stride (padded)
+    parent = o; o += 4 * kTtMaxT;
+    anc = o; o += 8 * kTtMaxT;                 // root-path bitmask per node (64 bits)
+    cidx = o; o += 4 * kTtMaxT;                // conv inputs of taps 1..3: node, or T + window row
+    misc = o; o += 16;                         // [0] tree ok
+    C = o; o += kTtMaxT * row;                 // C rows (raw)
+    cbt = o; o += 4 * kTtMaxT * kTtMaxT;       // C_v . B_u, [v][u]
+    X = o;                                     // B rows (raw) until the dots exist, then conv outputs
+    o += kTtMaxT * row > 4 * kTtRows * kTtMaxT ? kTtMaxT * row : 4 * kTtRows * kTtMaxT;
+    Y = o; o += 4 * kTtMaxT * kTtRows;         // y staging [node][channel]; raw x rows of a block first
+    win = o; o += 16 * ((3 * kTtRows * E + 15) / 16);  // the block's old window rows (raw)
+    So = o; o += 4 * 4 * kTtMaxT;              // [head][node] dt * A
+    S2 = o; o += 8 * 4 * kTtMaxT;              // [head][node] cumulative over the root path, times log2(e), fp64
+    dt = o; o += 4 * 4 * kTtMaxT;              // [head][node]
+    D = o; o += 16;
+    cw = o; o += 4 * 4 * kTtRows;              // [channel][tap]
+    cb = o; o += 4 * kTtRows;
+    total = o;
+  }
+};
+
+}  // namespace
+
+template <typename TIn, int NG, int TT>
+__global__ void __launch_bounds__(kTtThreads) verify_tt_kernel(VerifyArgs a, int NBLK) {
+  constexpr int N = 16 * NG;
+  constexpr int E = (int)sizeof(TIn);
+  constexpr int KT = 16 * TT;                      // node capacity
+  typedef typename Raw4<E>::T RawQ;
+  constexpr int kChunks = N * E / 16;              // 16-byte chunks per B / C row
+  const Dims d = a.d;
+  const int T = d.T, P = d.P, H = d.H, W = d.W, DI = d.d_in, G = d.G, CH = d.CH;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int j = lane & 15, k = lane >> 4;
+  const int b = blockIdx.y, l = blockIdx.z;
+  const int64_t unit = (int64_t)l * d.Bsz + b;
+  const int cw0 = blockIdx.x * NBLK * kTtRows;
+  const int g = cw0 / (DI / G);
+
+  extern __shared__ __align__(16) unsigned char smem[];
+  const TtLds lo(N, E);
+  int32_t* s_parent = reinterpret_cast<int32_t*>(smem + lo.parent);
+  uint64_t* s_anc = reinterpret_cast<uint64_t*>(smem + lo.anc);
+  int32_t* s_cidx = reinterpret_cast<int32_t*>(smem + lo.cidx);
+  int32_t* s_misc = reinterpret_cast<int32_t*>(smem + lo.misc);
+  unsigned char* s_C = smem + lo.C;
+  float* s_cbt = reinterpret_cast<float*>(smem + lo.cbt);
+  unsigned char* s_B = smem + lo.X;
+  float* s_xt = reinterpret_cast<float*>(smem + lo.X);
+  float* s_ys = reinterpret_cast<float*>(smem + lo.Y);
+  TIn* s_xr = reinterpret_cast<TIn*>(smem + lo.Y);
+  TIn* s_win = reinterpret_cast<TIn*>(smem + lo.win);
+  float* s_So = reinterpret_cast<float*>(smem + lo.So);
+  double* s_S2 = reinterpret_cast<double*>(smem + lo.S2);
+  float* s_dt = reinterpret_cast<float*>(smem + lo.dt);
+  float* s_D = reinterpret_cast<float*>(smem + lo.D);
+  float* s_cw = reinterpret_cast<float*>(smem + lo.cw);
+  float* s_cb = reinterpret_cast<float*>(smem + lo.cb);
+  const int rs = lo.row;
+
+  // ---- the first block's state, in flight during the tree prologue ----
+  f32x4 hq[NG];
+  {
+    const float* sin = a.state + (unit * DI + cw0 + wave * 16 + j) * (int64_t)N + 4 * k;
+#pragma unroll
+    for (int gg = 0; gg < NG; ++gg) hq[gg] = *reinterpret_cast<const f32x4*>(sin + 16 * gg);
+  }
+
+  // ---- tree prologue: parent[], C and B rows ----
+  if (tid < kTtMaxT) s_parent[tid] = tid < T ? a.parent[(int64_t)b * T + tid] : 0;
+  const unsigned char* Cg = reinterpret_cast<const unsigned char*>(a.C) + ((unit * T) * G + g) * (int64_t)N * E;
+  const unsigned char* Bg = reinterpret_cast<const unsigned char*>(a.B) + ((unit * T) * G + g) * (int64_t)N * E;
+  for (int ci = tid; ci < KT * kChunks; ci += kTtThreads) {
+    const int v = ci / kChunks, q = ci % kChunks;
+    u32x4 c4 = u32x4{0u, 0u, 0u, 0u}, b4 = c4;  // zero rows past T
+    if (v < T) {
+      c4 = *reinterpret_cast<const u32x4*>(Cg + (int64_t)v * G * N * E + q * 16);
+      b4 = *reinterpret_cast<const u32x4*>(Bg + (int64_t)v * G * N * E + q * 16);
+    }
+    *reinterpret_cast<u32x4*>(s_C + v * rs + q * 16) = c4;
+    *reinterpret_cast<u32x4*>(s_B + v * rs + q * 16) = b4;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    // validation by ballot (lane = node), then per node the root-path set and
+    // the conv taps; the walks require -1 <= parent < node at every step, so
+    // they end and stay in range even on an invalid tree
+    bool bad = false;
+    if (lane < T) {
+      const int p = s_parent[lane];
+      bad = lane == 0 ? p != -1 : (p < -1 || p >= lane || p < s_parent[lane - 1]);
+    }
+    const bool ok = __ballot(bad) == 0;
+    uint64_t m = 0;
+    int packed = 0;
+    if (lane < T) {
+      int u = lane, a1 = -1, a2 = -1, a3 = -1, depth = 0;
+      for (int s = 0; s < kTtMaxT && u >= 0; ++s) {
+        m |= 1ull << u;
+        ++depth;
+        const int p = s_parent[u];
+        u = (p >= 0 && p < u) ? p : -1;
+        a1 = s == 0 ? u : a1;
+        a2 = s == 1 ? u : a2;
+        a3 = s == 2 ? u : a3;
+      }
+#pragma unroll
+      for (int jj = 1; jj < 4; ++jj) {
+        const int an = jj == 1 ? a1 : (jj == 2 ? a2 : a3);
+        const int code = an >= 0 ? an : T + (W - 2) - (jj - depth);
+        if (jj < W) packed |= code << (8 * (jj - 1));
+      }
+    }
+    s_anc[lane] = m;  // zero past T
+    s_cidx[lane] = packed;
+    if (lane == 0) {
+      s_misc[0] = ok ? 1 : 0;
+      if (blockIdx.x == 0 && l == 0 && a.seq_status) a.seq_status[b] = ok ? SSM_TREE_OK : SSM_TREE_E_TREE;
+    }
+  }
+  // C_v . B_u over the lower-triangular tile pairs, B rows as the A operand
+  // and C rows as the B operand: lane (i + 16 k) ends with
+  // (B_{16 tj + 4k + t} . C_{16 ti + i}) = CB[16 ti + i][16 tj + 4 k + t]
+  for (int pi = wave; pi < TT * (TT + 1) / 2; pi += kTtWaves) {
+    int ti = 0;
+    while ((ti + 1) * (ti + 2) / 2 <= pi) ++ti;
+    const int tj = pi - ti * (ti + 1) / 2;
+    f32x4 cb = f32x4{0.f, 0.f, 0.f, 0.f};
+    const TIn* brow = reinterpret_cast<const TIn*>(s_B + (16 * tj + j) * rs) + 4 * k;
+    const TIn* crow = reinterpret_cast<const TIn*>(s_C + (16 * ti + j) * rs) + 4 * k;
+#pragma unroll
+    for (int gg = 0; gg < NG; ++gg) {
+      const f32x4 bq = load4<TIn>(brow + 16 * gg);
+      const f32x4 cq = load4<TIn>(crow + 16 * gg);
+      cb = mfma4(bq.x, cq.x, cb);
+      cb = mfma4(bq.y, cq.y, cb);
+      cb = mfma4(bq.z, cq.z, cb);
+      cb = mfma4(bq.w, cq.w, cb);
+    }
+    *reinterpret_cast<f32x4*>(s_cbt + (16 * ti + j) * kTtMaxT + 16 * tj + 4 * k) = cb;
+  }
+  __syncthreads();  // the B rows are dead from here: their space holds the conv outputs
+  const bool tree_ok = s_misc[0] != 0;
+
+  const TIn* xg = reinterpret_cast<const TIn*>(a.x) + unit * T * (int64_t)DI;
+  const TIn* wg = reinterpret_cast<const TIn*>(a.window) + unit * (W - 1) * (int64_t)CH;
+  const TIn* dtg = reinterpret_cast<const TIn*>(a.dt_raw) + unit * T * (int64_t)H;
+  for (int blk = 0; blk < NBLK; ++blk) {
+    const int c0 = cw0 + blk * kTtRows;
+    const int h_lo = c0 / P;
+    const int HW = (c0 + kTtRows - 1) / P - h_lo + 1;  // heads touched (<= 4: P is a multiple of 16)
+
+    // ---- the block's raw x rows, window rows, conv parameters and head scalars ----
+    for (int qi = tid; qi < KT * (kTtRows / 4); qi += kTtThreads) {
+      const int v = qi / (kTtRows / 4), c4 = (qi % (kTtRows / 4)) * 4;
+      RawQ r{};
+      if (v < T) r = *reinterpret_cast<const RawQ*>(xg + (int64_t)v * DI + c0 + c4);
+      *reinterpret_cast<RawQ*>(s_xr + v * kTtRows + c4) = r;
+    }
+    if (tid < kTtRows) {
+      const int c = c0 + tid;
+#pragma unroll
+      for (int r = 0; r < 3; ++r)
+        if (r < W - 1) s_win[r * kTtRows + tid] = wg[(int64_t)r * CH + c];
+      const float* cw = a.prm.conv_w + ((int64_t)l * CH + c) * W;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) s_cw[tid * 4 + jj] = jj < W ? cw[jj] : 0.0f;
+      s_cb[tid] = a.prm.conv_b ? a.prm.conv_b[(int64_t)l * CH + c] : 0.0f;
+    }
+    {
+      const int hh = tid / kTtMaxT, v = tid % kTtMaxT;  // 4 heads x 64 nodes
+      float dtv = 0.0f, so = 0.0f;
+      if (hh < HW && v < T) {
+        const int h = h_lo + hh;
+        dtv = softplus_f32(load_in(dtg, (int64_t)v * H + h) + a.prm.dt_bias[(int64_t)l * H + h]);
+        so = dtv * a.prm.A[(int64_t)l * H + h];
+      }
+      s_dt[hh * kTtMaxT + v] = dtv;
+      s_So[hh * kTtMaxT + v] = so;
+      if (tid < HW) s_D[tid] = a.prm.D[(int64_t)l * H + h_lo + tid];
+    }
+    __syncthreads();
+    {
+      // S along each root path (base-2 units), accumulated in fp64: down a
+      // 64-node chain it reaches ~-70, and the decay between two nodes is
+      // the difference of two such sums, which fp32 would leave with ~1e-5
+      // of cancellation error; fp64 keeps the difference exact to the fp32
+      // rounding of its own terms
+      const int hh = tid / kTtMaxT, v = tid % kTtMaxT;
+      const uint64_t m = s_anc[v];
+      double acc = 0.0;
+      for (int u = 0; u < KT; ++u) acc += ((m >> u) & 1) ? (double)s_So[hh * kTtMaxT + u] : 0.0;
+      s_S2[hh * kTtMaxT + v] = acc * 1.4426950408889634;
+    }
+    for (int i = tid; i < KT * kTtRows; i += kTtThreads) {
+      const int v = i / kTtRows, cl = i % kTtRows;
+      float xt = 0.0f;
+      if (v < T) {
+        float z = fmaf(s_cw[cl * 4 + W - 1], load_in(s_xr, v * kTtRows + cl), s_cb[cl]);
+        const int codes = s_cidx[v];
+        for (int jj = 1; jj < W; ++jj) {
+          const int code = (codes >> (8 * (jj - 1))) & 255;
+          const float u = code < T ? load_in(s_xr, code * kTtRows + cl) : load_in(s_win, (code - T) * kTtRows + cl);
+          z = fmaf(s_cw[cl * 4 + W - 1 - jj], u, z);
+        }
+        xt = d.silu ? silu_f32(z) : z;
+      }
+      s_xt[xt_at(cl, v)] = xt;
+    }
+    __syncthreads();
+
+    // ---- C . h0 on the matrix cores: lane (c + 16 q) ends with (C_{16 ti + 4q + r} . h_c) ----
+    f32x4 acc[TT];
+#pragma unroll
+    for (int ti = 0; ti < TT; ++ti) acc[ti] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const bool more = blk + 1 < NBLK;
+    const float* nsin = a.state + (unit * DI + c0 + kTtRows + wave * 16 + j) * (int64_t)N + 4 * k;
+#pragma unroll
+    for (int gg = 0; gg < NG; ++gg) {
+#pragma unroll
+      for (int ti = 0; ti < TT; ++ti) {
+        const f32x4 cq = load4<TIn>(reinterpret_cast<const TIn*>(s_C + (16 * ti + j) * rs) + 16 * gg + 4 * k);
+        acc[ti] = mfma4(cq.x, hq[gg].x, acc[ti]);
+        acc[ti] = mfma4(cq.y, hq[gg].y, acc[ti]);
+        acc[ti] = mfma4(cq.z, hq[gg].z, acc[ti]);
+        acc[ti] = mfma4(cq.w, hq[gg].w, acc[ti]);
+      }
+      // this column group is consumed: the next block's takes its registers
+      if (more) hq[gg] = *reinterpret_cast<const f32x4*>(nsin + 16 * gg);
+    }
+
+    // ---- the path terms M[v][u] x~_u (u in tiles tj <= ti), with the diagonal D ----
+    const int row = wave * 16 + j;                   // this lane's channel in the block
+    const int hl = (c0 + wave * 16) / P - h_lo;      // the wave's head
+    const float Dh = s_D[hl];
+    const double* S2h = s_S2 + hl * kTtMaxT;
+    const float* dth = s_dt + hl * kTtMaxT;
+#pragma unroll
+    for (int ti = 0; ti < TT; ++ti) {
+      const int vi = 16 * ti + j;                    // the M row (node) this lane supplies
+      const double Sv = S2h[vi];
+      const uint64_t ancm = s_anc[vi];
+      f32x4 y;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) y[t] = __builtin_amdgcn_exp2f((float)S2h[16 * ti + 4 * k + t]) * acc[ti][t];
+#pragma unroll
+      for (int tj = 0; tj <= ti; ++tj) {
+        const int u0 = 16 * tj + 4 * k;
+        const f32x4 du = *reinterpret_cast<const f32x4*>(dth + u0);
+        const f32x4 cbr = *reinterpret_cast<const f32x4*>(s_cbt + vi * kTtMaxT + u0);
+        f32x4 mop;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const float mv =
+              ((ancm >> (u0 + t)) & 1) ? __builtin_amdgcn_exp2f((float)(Sv - S2h[u0 + t])) * du[t] * cbr[t] : 0.0f;
+          mop[t] = (u0 + t == vi) ? mv + Dh : mv;
+        }
+        const f32x4 xq = *reinterpret_cast<const f32x4*>(s_xt + row * kTtMaxT + 4 * ((4 * tj + k) ^ (row & 15)));
+        y = mfma4(mop.x, xq.x, y);
+        y = mfma4(mop.y, xq.y, y);
+        y = mfma4(mop.z, xq.z, y);
+        y = mfma4(mop.w, xq.w, y);
+      }
+      // lane (c + 16 k) holds nodes 16 ti + 4 k + r of channel row
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s_ys[(16 * ti + 4 * k + r) * kTtRows + row] = tree_ok ? y[r] : __builtin_nanf("");
+    }
+    __syncthreads();
+    for (int i = tid; i < T * (kTtRows / 4); i += kTtThreads) {
+      const int v = i / (kTtRows / 4), q = i % (kTtRows / 4);
+      *reinterpret_cast<f32x4*>(a.y + (unit * T + v) * DI + c0 + 4 * q) =
+          *reinterpret_cast<const f32x4*>(s_ys + v * kTtRows + 4 * q);
+    }
+    __syncthreads();  // the staging space takes the next block's x rows
+  }
+}
+
+namespace {
+
+template <typename TIn, int NG, int TT>
+int launch_tt_t(const VerifyArgs& a, hipStream_t s) {
+  const size_t lds = (size_t)TtLds(16 * NG, (int)sizeof(TIn)).total;
+  if (lds > 160 * 1024) return SSM_TREE_E_DIMS;  // (fp32 inputs with d_state 256) the caller falls back
+  if (allow_lds(verify_tt_kernel<TIn, NG, TT>, lds) != hipSuccess) return SSM_TREE_E_HIP;
+  const int blocks = a.d.d_in / a.d.G / kTtRows;  // 64-channel blocks per B/C group
+  const int nblk = blocks % 4 == 0 ? 4 : (blocks % 2 == 0 ? 2 : 1);
+  dim3 grid(a.d.d_in / (nblk * kTtRows), a.d.Bsz, a.d.L);
+  hipLaunchKernelGGL((verify_tt_kernel<TIn, NG, TT>), grid, dim3(kTtThreads), lds, s, a, nblk);
+  return hipGetLastError() == hipSuccess ? SSM_TREE_OK : SSM_TREE_E_HIP;
+}
+
+template <typename TIn, int NG>
+int launch_tt_g(const VerifyArgs& a, hipStream_t s) {
+  const int T = a.d.T;
+  if (T <= 32) return launch_tt_t<TIn, NG, 2>(a, s);
+  if (T <= 48) return launch_tt_t<TIn, NG, 3>(a, s);
+  return launch_tt_t<TIn, NG, 4>(a, s);
+}
+
+template <typename TIn>
+int launch_tt_in(const VerifyArgs& a, hipStream_t s) {
+  switch (a.d.N) {
+    case 16: return launch_tt_g<TIn, 1>(a, s);
+    case 32: return launch_tt_g<TIn, 2>(a, s);
+    case 64: return launch_tt_g<TIn, 4>(a, s);
+    case 128: return launch_tt_g<TIn, 8>(a, s);
+    case 256: return launch_tt_g<TIn, 16>(a, s);
+    default: return SSM_TREE_E_DIMS;
+  }
+}
+
+}  // namespace
+
+// trees of 17..64 nodes, heads a multiple of 16 channels, 64-channel blocks
+bool tt_verify_applies(const Dims& d) {
+  return d.T > 16 && d.T <= kTtMaxT && d.P % 16 == 0 && (d.d_in / d.G) % kTtRows == 0;
+}
+
+int launch_verify_tt(const VerifyArgs& a, bool bf16, hipStream_t s) {
+  return bf16 ? launch_tt_in<bf16_t>(a, s) : launch_tt_in<float>(a, s);
+}
+
+}  // namespace ssmt
