@@ -36,6 +36,7 @@ constexpr int kTtRows = 64;   // channels per block
 constexpr int kTtWaves = 4;
 constexpr int kTtThreads = kTtWaves * kWave;
 constexpr int kTtMaxT = 64;
+constexpr int kCbStride = kTtMaxT + 4;  // C.B row stride: rows of a node tile on different LDS banks
 
 __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -69,6 +70,36 @@ struct Raw4<4> {
   typedef u32x4 T;
 };
 
+// an input element's raw bits in a 32-bit register, and back
+template <typename TIn>
+__device__ __forceinline__ uint32_t raw_bits(const TIn* p);
+template <>
+__device__ __forceinline__ uint32_t raw_bits<float>(const float* p) {
+  return __float_as_uint(*p);
+}
+template <>
+__device__ __forceinline__ uint32_t raw_bits<bf16_t>(const bf16_t* p) {
+  return p->bits;
+}
+template <typename TIn>
+__device__ __forceinline__ TIn from_bits(uint32_t r);
+template <>
+__device__ __forceinline__ float from_bits<float>(uint32_t r) {
+  return __uint_as_float(r);
+}
+template <>
+__device__ __forceinline__ bf16_t from_bits<bf16_t>(uint32_t r) {
+  return bf16_t{(uint16_t)r};
+}
+// threadIdx.x through an empty asm: values derived from it inside a phase
+// are recomputed there instead of being hoisted out of the block loop and
+// kept live across it (which ran the kernel out of registers)
+__device__ __forceinline__ int opaque_tid() {
+  int v = threadIdx.x;
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
 // conv outputs [channel][node] in the MFMA B-operand layout: quad q (nodes
 // 4 q .. 4 q + 3) of channel row c sits at quad q ^ (c & 15), so that the 16
 // channels a wave reads at once fall on different banks
@@ -85,7 +116,7 @@ struct TtLds {
     cidx = o; o += 4 * kTtMaxT;                // conv inputs of taps 1..3: node, or T + window row
     misc = o; o += 16;                         // [0] tree ok
     C = o; o += kTtMaxT * row;                 // C rows (raw)
-    cbt = o; o += 4 * kTtMaxT * kTtMaxT;       // C_v . B_u, [v][u]
+    cbt = o; o += 4 * kTtMaxT * kCbStride;     // C_v . B_u, [v][u] (padded rows)
     X = o;                                     // B rows (raw) until the dots exist, then conv outputs
     o += kTtMaxT * row > 4 * kTtRows * kTtMaxT ? kTtMaxT * row : 4 * kTtRows * kTtMaxT;
     Y = o; o += 4 * kTtMaxT * kTtRows;         // y staging [node][channel]; raw x rows of a block first
@@ -94,7 +125,7 @@ struct TtLds {
     S2 = o; o += 8 * 4 * kTtMaxT;              // [head][node] cumulative over the root path, times log2(e), fp64
     dt = o; o += 4 * 4 * kTtMaxT;              // [head][node]
     D = o; o += 16;
-    cw = o; o += 4 * 4 * kTtRows;              // [channel][tap]
+    cw = o; o += 4 * 4 * kTtRows;              // [tap][channel]
     cb = o; o += 4 * kTtRows;
     total = o;
   }
@@ -219,7 +250,7 @@ __global__ void __launch_bounds__(kTtThreads) verify_tt_kernel(VerifyArgs a, int
       cb = mfma4(bq.z, cq.z, cb);
       cb = mfma4(bq.w, cq.w, cb);
     }
-    *reinterpret_cast<f32x4*>(s_cbt + (16 * ti + j) * kTtMaxT + 16 * tj + 4 * k) = cb;
+    *reinterpret_cast<f32x4*>(s_cbt + (16 * ti + j) * kCbStride + 16 * tj + 4 * k) = cb;
   }
   __syncthreads();  // the B rows are dead from here: their space holds the conv outputs
   const bool tree_ok = s_misc[0] != 0;
@@ -227,63 +258,118 @@ __global__ void __launch_bounds__(kTtThreads) verify_tt_kernel(VerifyArgs a, int
   const TIn* xg = reinterpret_cast<const TIn*>(a.x) + unit * T * (int64_t)DI;
   const TIn* wg = reinterpret_cast<const TIn*>(a.window) + unit * (W - 1) * (int64_t)CH;
   const TIn* dtg = reinterpret_cast<const TIn*>(a.dt_raw) + unit * T * (int64_t)H;
-  for (int blk = 0; blk < NBLK; ++blk) {
+  // per-block inputs, loaded a block ahead into registers: raw x quads,
+  // and by role the window rows and conv parameters (threads < 64) and the
+  // head scalars (thread = head x node)
+  constexpr int kXQ = (KT * (kTtRows / 4) + kTtThreads - 1) / kTtThreads;
+  RawQ pxr[kXQ];
+  // (raw values only: arithmetic on a loaded value would wait for the load at once)
+  uint32_t pwin[3] = {0u, 0u, 0u}, pdt = 0u;
+  float pcw[4] = {0.f, 0.f, 0.f, 0.f}, pcb = 0.f, pbias = 0.f, pA = 0.f, pD = 0.f;
+  auto prefetch = [&](int blk) {
+    const int tid = opaque_tid();
     const int c0 = cw0 + blk * kTtRows;
     const int h_lo = c0 / P;
-    const int HW = (c0 + kTtRows - 1) / P - h_lo + 1;  // heads touched (<= 4: P is a multiple of 16)
-
-    // ---- the block's raw x rows, window rows, conv parameters and head scalars ----
-    for (int qi = tid; qi < KT * (kTtRows / 4); qi += kTtThreads) {
+    const int HW = (c0 + kTtRows - 1) / P - h_lo + 1;
+#pragma unroll
+    for (int it = 0; it < kXQ; ++it) {
+      const int qi = tid + it * kTtThreads;
       const int v = qi / (kTtRows / 4), c4 = (qi % (kTtRows / 4)) * 4;
-      RawQ r{};
-      if (v < T) r = *reinterpret_cast<const RawQ*>(xg + (int64_t)v * DI + c0 + c4);
-      *reinterpret_cast<RawQ*>(s_xr + v * kTtRows + c4) = r;
+      pxr[it] = RawQ{};
+      if (v < T) pxr[it] = *reinterpret_cast<const RawQ*>(xg + (int64_t)v * DI + c0 + c4);
     }
     if (tid < kTtRows) {
       const int c = c0 + tid;
 #pragma unroll
       for (int r = 0; r < 3; ++r)
-        if (r < W - 1) s_win[r * kTtRows + tid] = wg[(int64_t)r * CH + c];
+        if (r < W - 1) pwin[r] = raw_bits<TIn>(wg + (int64_t)r * CH + c);
       const float* cw = a.prm.conv_w + ((int64_t)l * CH + c) * W;
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) s_cw[tid * 4 + jj] = jj < W ? cw[jj] : 0.0f;
-      s_cb[tid] = a.prm.conv_b ? a.prm.conv_b[(int64_t)l * CH + c] : 0.0f;
+      for (int jj = 0; jj < 4; ++jj)
+        if (jj < W) pcw[jj] = cw[jj];
+      if (a.prm.conv_b) pcb = a.prm.conv_b[(int64_t)l * CH + c];
+    }
+    const int hh = tid / kTtMaxT, v = tid % kTtMaxT;  // 4 heads x 64 nodes
+    if (hh < HW && v < T) {
+      const int h = h_lo + hh;
+      pdt = raw_bits<TIn>(dtg + (int64_t)v * H + h);
+      pbias = a.prm.dt_bias[(int64_t)l * H + h];
+      pA = a.prm.A[(int64_t)l * H + h];
+    }
+    if (tid < HW) pD = a.prm.D[(int64_t)l * H + h_lo + tid];
+  };
+  prefetch(0);
+  for (int blk = 0; blk < NBLK; ++blk) {
+    const int c0 = cw0 + blk * kTtRows;
+    const int h_lo = c0 / P;
+    const int HW = (c0 + kTtRows - 1) / P - h_lo + 1;  // heads touched (<= 4: P is a multiple of 16)
+
+    // ---- deliver the block's inputs to LDS, then start the next block's ----
+    {
+    const int tid = opaque_tid();
+#pragma unroll
+    for (int it = 0; it < kXQ; ++it) {
+      const int qi = tid + it * kTtThreads;
+      const int v = qi / (kTtRows / 4), c4 = (qi % (kTtRows / 4)) * 4;
+      if (qi < KT * (kTtRows / 4)) *reinterpret_cast<RawQ*>(s_xr + v * kTtRows + c4) = pxr[it];
+    }
+    if (tid < kTtRows) {
+#pragma unroll
+      for (int r = 0; r < 3; ++r)
+        if (r < W - 1) s_win[r * kTtRows + tid] = from_bits<TIn>(pwin[r]);
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) s_cw[jj * kTtRows + tid] = pcw[jj];  // [tap][channel]
+      s_cb[tid] = pcb;
     }
     {
-      const int hh = tid / kTtMaxT, v = tid % kTtMaxT;  // 4 heads x 64 nodes
+      const int hh = tid / kTtMaxT, v = tid % kTtMaxT;
       float dtv = 0.0f, so = 0.0f;
       if (hh < HW && v < T) {
-        const int h = h_lo + hh;
-        dtv = softplus_f32(load_in(dtg, (int64_t)v * H + h) + a.prm.dt_bias[(int64_t)l * H + h]);
-        so = dtv * a.prm.A[(int64_t)l * H + h];
+        dtv = softplus_f32((sizeof(TIn) == 2 ? __uint_as_float(pdt << 16) : __uint_as_float(pdt)) + pbias);
+        so = dtv * pA;
       }
       s_dt[hh * kTtMaxT + v] = dtv;
       s_So[hh * kTtMaxT + v] = so;
-      if (tid < HW) s_D[tid] = a.prm.D[(int64_t)l * H + h_lo + tid];
+      if (tid < HW) s_D[tid] = pD;
     }
+    }
+    if (blk + 1 < NBLK) prefetch(blk + 1);
     __syncthreads();
     {
       // S along each root path (base-2 units), accumulated in fp64: down a
       // 64-node chain it reaches ~-70, and the decay between two nodes is
       // the difference of two such sums, which fp32 would leave with ~1e-5
       // of cancellation error; fp64 keeps the difference exact to the fp32
-      // rounding of its own terms
+      // rounding of its own terms.  Wave = head, lane = node: pointer
+      // jumping over the parent links, 6 rounds for paths of up to 64 nodes
+      // (each round adds the partial sum of the node 2^r steps up).
+      const int tid = opaque_tid();
       const int hh = tid / kTtMaxT, v = tid % kTtMaxT;
-      const uint64_t m = s_anc[v];
-      double acc = 0.0;
-      for (int u = 0; u < KT; ++u) acc += ((m >> u) & 1) ? (double)s_So[hh * kTtMaxT + u] : 0.0;
+      double acc = (double)s_So[hh * kTtMaxT + v];  // zero past T
+      int up = v < T ? s_parent[v] : -1;
+      up = (up >= 0 && up < v) ? up : -1;  // (an invalid tree's output is discarded; keep indices in range)
+#pragma unroll
+      for (int r = 0; r < 6; ++r) {
+        const int src = up >= 0 ? up : v;
+        const double acc_up = __shfl(acc, src);
+        const int up_up = __shfl(up, src);
+        if (up >= 0) {
+          acc += acc_up;
+          up = up_up;
+        }
+      }
       s_S2[hh * kTtMaxT + v] = acc * 1.4426950408889634;
     }
-    for (int i = tid; i < KT * kTtRows; i += kTtThreads) {
+    for (int i = opaque_tid(); i < KT * kTtRows; i += kTtThreads) {
       const int v = i / kTtRows, cl = i % kTtRows;
       float xt = 0.0f;
       if (v < T) {
-        float z = fmaf(s_cw[cl * 4 + W - 1], load_in(s_xr, v * kTtRows + cl), s_cb[cl]);
+        float z = fmaf(s_cw[(W - 1) * kTtRows + cl], load_in(s_xr, v * kTtRows + cl), s_cb[cl]);
         const int codes = s_cidx[v];
         for (int jj = 1; jj < W; ++jj) {
           const int code = (codes >> (8 * (jj - 1))) & 255;
           const float u = code < T ? load_in(s_xr, code * kTtRows + cl) : load_in(s_win, (code - T) * kTtRows + cl);
-          z = fmaf(s_cw[cl * 4 + W - 1 - jj], u, z);
+          z = fmaf(s_cw[(W - 1 - jj) * kTtRows + cl], u, z);
         }
         xt = d.silu ? silu_f32(z) : z;
       }
@@ -292,6 +378,7 @@ __global__ void __launch_bounds__(kTtThreads) verify_tt_kernel(VerifyArgs a, int
     __syncthreads();
 
     // ---- C . h0 on the matrix cores: lane (c + 16 q) ends with (C_{16 ti + 4q + r} . h_c) ----
+    const int ln = opaque_tid() & (kWave - 1), j = ln & 15, k = ln >> 4;
     f32x4 acc[TT];
 #pragma unroll
     for (int ti = 0; ti < TT; ++ti) acc[ti] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -309,6 +396,9 @@ __global__ void __launch_bounds__(kTtThreads) verify_tt_kernel(VerifyArgs a, int
       }
       // this column group is consumed: the next block's takes its registers
       if (more) hq[gg] = *reinterpret_cast<const f32x4*>(nsin + 16 * gg);
+      // one column group's C operands at a time (hoisting all of them would
+      // take 4 NG x 4 registers)
+      asm volatile("" ::: "memory");
     }
 
     // ---- the path terms M[v][u] x~_u (u in tiles tj <= ti), with the diagonal D ----
@@ -329,12 +419,13 @@ __global__ void __launch_bounds__(kTtThreads) verify_tt_kernel(VerifyArgs a, int
       for (int tj = 0; tj <= ti; ++tj) {
         const int u0 = 16 * tj + 4 * k;
         const f32x4 du = *reinterpret_cast<const f32x4*>(dth + u0);
-        const f32x4 cbr = *reinterpret_cast<const f32x4*>(s_cbt + vi * kTtMaxT + u0);
+        const f32x4 cbr = *reinterpret_cast<const f32x4*>(s_cbt + vi * kCbStride + u0);
+        const uint32_t nib = (uint32_t)(ancm >> u0) & 15u;  // which of u0 .. u0 + 3 are on vi's root path
         f32x4 mop;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           const float mv =
-              ((ancm >> (u0 + t)) & 1) ? __builtin_amdgcn_exp2f((float)(Sv - S2h[u0 + t])) * du[t] * cbr[t] : 0.0f;
+              ((nib >> t) & 1) ? __builtin_amdgcn_exp2f((float)(Sv - S2h[u0 + t])) * du[t] * cbr[t] : 0.0f;
           mop[t] = (u0 + t == vi) ? mv + Dh : mv;
         }
         const f32x4 xq = *reinterpret_cast<const f32x4*>(s_xt + row * kTtMaxT + 4 * ((4 * tj + k) ^ (row & 15)));
@@ -346,9 +437,12 @@ __global__ void __launch_bounds__(kTtThreads) verify_tt_kernel(VerifyArgs a, int
       // lane (c + 16 k) holds nodes 16 ti + 4 k + r of channel row
 #pragma unroll
       for (int r = 0; r < 4; ++r) s_ys[(16 * ti + 4 * k + r) * kTtRows + row] = tree_ok ? y[r] : __builtin_nanf("");
+      // one node tile's operands at a time: hoisting the LDS reads of all
+      // tiles above the loop would take most of the register file
+      asm volatile("" ::: "memory");
     }
     __syncthreads();
-    for (int i = tid; i < T * (kTtRows / 4); i += kTtThreads) {
+    for (int i = opaque_tid(); i < T * (kTtRows / 4); i += kTtThreads) {
       const int v = i / (kTtRows / 4), q = i % (kTtRows / 4);
       *reinterpret_cast<f32x4*>(a.y + (unit * T + v) * DI + c0 + 4 * q) =
           *reinterpret_cast<const f32x4*>(s_ys + v * kTtRows + 4 * q);
