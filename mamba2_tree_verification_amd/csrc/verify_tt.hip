@@ -31,15 +31,48 @@ namespace {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kTtRows = 64;   // channels per block
 constexpr int kTtWaves = 4;
 constexpr int kTtThreads = kTtWaves * kWave;
 constexpr int kTtMaxT = 64;
-constexpr int kCbStride = kTtMaxT + 4;  // C.B row stride: rows of a node tile on different LDS banks
+constexpr int kCbStride = kTtMaxT + 4;  // C.B and M row stride: rows of a node tile on different LDS banks
+constexpr int kYsStride = kTtRows + 4;  // y staging row stride
 
 __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+// 16 x 16 x 32 bf16 product: each lane brings 8 values of its A row and of
+// its B column; only the pairing of A's and B's k slots matters for the sum,
+// and both operands here fill their slots from the same state indices
+__device__ __forceinline__ f32x4 mfma32(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                  0, 0);
+}
+// two bf16 (raw bits, in the high halves of lo and hi) packed into a dword
+__device__ __forceinline__ uint32_t pack_hi(uint32_t lo, uint32_t hi) { return (lo >> 16) | (hi & 0xFFFF0000u); }
+// eight fp32 values as the sum of three bf16 terms, by truncation: each
+// remainder is exact in fp32, and the third term leaves less than 2^-21 of
+// the value
+__device__ __forceinline__ void split3(f32x4 p, f32x4 q, u32x4& t0, u32x4& t1, u32x4& t2) {
+  uint32_t b0[8], b1[8], b2[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float v = e < 4 ? p[e] : q[e - 4];
+    const uint32_t h = __float_as_uint(v) & 0xFFFF0000u;
+    const float r = v - __uint_as_float(h);
+    const uint32_t m = __float_as_uint(r) & 0xFFFF0000u;
+    b0[e] = h;
+    b1[e] = m;
+    b2[e] = __float_as_uint(r - __uint_as_float(m));
+  }
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    t0[w] = pack_hi(b0[2 * w], b0[2 * w + 1]);
+    t1[w] = pack_hi(b1[2 * w], b1[2 * w + 1]);
+    t2[w] = pack_hi(b2[2 * w], b2[2 * w + 1]);
+  }
 }
 
 template <typename TIn>
@@ -100,14 +133,42 @@ __device__ __forceinline__ int opaque_tid() {
   return v;
 }
 
+// silu with the hardware exp2 and reciprocal (about 1 ulp each)
+__device__ __forceinline__ float silu_hw(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * z));
+}
+
 // conv outputs [channel][node] in the MFMA B-operand layout: quad q (nodes
 // 4 q .. 4 q + 3) of channel row c sits at quad q ^ (c & 15), so that the 16
 // channels a wave reads at once fall on different banks
 __device__ __forceinline__ int xt_at(int c, int v) { return c * kTtMaxT + 4 * ((v >> 2) ^ (c & 15)) + (v & 3); }
 
+// M[v][u0 .. u0 + 3] of one head: exp(S_v - S_u) dt_u (C_v . B_u) where u is
+// on v's root path (ancestor bits ancv), zero elsewhere, plus D on the
+// diagonal; S in base-2 units, fp64 (the difference is taken before rounding)
+__device__ __forceinline__ f32x4 m_quad(int v, int u0, const double* S2h, const float* dth, uint64_t ancv,
+                                        const float* cbr, float Dh) {
+  typedef double f64x2 __attribute__((ext_vector_type(2)));
+  const double Sv = S2h[v];
+  const f32x4 du = *reinterpret_cast<const f32x4*>(dth + u0);
+  const f32x4 cb = *reinterpret_cast<const f32x4*>(cbr);
+  const f64x2 sa = *reinterpret_cast<const f64x2*>(S2h + u0);
+  const f64x2 sb = *reinterpret_cast<const f64x2*>(S2h + u0 + 2);
+  const uint32_t nib = (uint32_t)(ancv >> u0) & 15u;
+  f32x4 m;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const double su = t == 0 ? sa.x : (t == 1 ? sa.y : (t == 2 ? sb.x : sb.y));
+    const float e = __builtin_amdgcn_exp2f((float)(Sv - su)) * du[t] * cb[t];
+    const float mv = ((nib >> t) & 1) ? e : 0.0f;
+    m[t] = u0 + t == v ? mv + Dh : mv;
+  }
+  return m;
+}
+
 // LDS layout (byte offsets)
 struct TtLds {
-  int parent, anc, cidx, misc, C, cbt, X, Y, win, So, S2, dt, D, cw, cb, total, row;
+  int parent, anc, cidx, misc, C, cbt, X, Y, win, So, S2, Ah, dt, D, cw, cb, total, row;
   __host__ __device__ TtLds(int N, int E) {
     int o = 0;
     row = N * E + 16;                          // staged B / C row stride (padded)
@@ -119,13 +180,14 @@ struct TtLds {
     cbt = o; o += 4 * kTtMaxT * kCbStride;     // C_v . B_u, [v][u] (padded rows)
     X = o;                                     // B rows (raw) until the dots exist, then conv outputs
     o += kTtMaxT * row > 4 * kTtRows * kTtMaxT ? kTtMaxT * row : 4 * kTtRows * kTtMaxT;
-    Y = o; o += 4 * kTtMaxT * kTtRows;         // y staging [node][channel]; raw x rows of a block first
+    Y = o; o += 4 * kTtMaxT * kYsStride;       // raw x rows of a block, then M [v][u], then y staging [node][channel]
     win = o; o += 16 * ((3 * kTtRows * E + 15) / 16);  // the block's old window rows (raw)
     So = o; o += 4 * 4 * kTtMaxT;              // [head][node] dt * A
     S2 = o; o += 8 * 4 * kTtMaxT;              // [head][node] cumulative over the root path, times log2(e), fp64
+    Ah = o; o += 4 * 4 * kTtMaxT;              // [head][node] exp(S)
     dt = o; o += 4 * 4 * kTtMaxT;              // [head][node]
     D = o; o += 16;
-    cw = o; o += 4 * 4 * kTtRows;              // [tap][channel]
+    cw = o; o += 4 * 4 * kTtRows;              // [tap][channel], tap t = the node t steps up the path
     cb = o; o += 4 * kTtRows;
     total = o;
   }
@@ -161,10 +223,12 @@ __global__ void __launch_bounds__(kTtThreads) verify_tt_kernel(VerifyArgs a, int
   unsigned char* s_B = smem + lo.X;
   float* s_xt = reinterpret_cast<float*>(smem + lo.X);
   float* s_ys = reinterpret_cast<float*>(smem + lo.Y);
+  float* s_m = reinterpret_cast<float*>(smem + lo.Y);
   TIn* s_xr = reinterpret_cast<TIn*>(smem + lo.Y);
   TIn* s_win = reinterpret_cast<TIn*>(smem + lo.win);
   float* s_So = reinterpret_cast<float*>(smem + lo.So);
   double* s_S2 = reinterpret_cast<double*>(smem + lo.S2);
+  float* s_Ah = reinterpret_cast<float*>(smem + lo.Ah);
   float* s_dt = reinterpret_cast<float*>(smem + lo.dt);
   float* s_D = reinterpret_cast<float*>(smem + lo.D);
   float* s_cw = reinterpret_cast<float*>(smem + lo.cw);
@@ -241,14 +305,30 @@ __global__ void __launch_bounds__(kTtThreads) verify_tt_kernel(VerifyArgs a, int
     f32x4 cb = f32x4{0.f, 0.f, 0.f, 0.f};
     const TIn* brow = reinterpret_cast<const TIn*>(s_B + (16 * tj + j) * rs) + 4 * k;
     const TIn* crow = reinterpret_cast<const TIn*>(s_C + (16 * ti + j) * rs) + 4 * k;
+    if constexpr (E == 2) {
+      // bf16 rows are exact bf16 operands: k slots = state indices
+      // 16 g + 4 k .. + 3 of column groups g = 2 m, 2 m + 1
 #pragma unroll
-    for (int gg = 0; gg < NG; ++gg) {
-      const f32x4 bq = load4<TIn>(brow + 16 * gg);
-      const f32x4 cq = load4<TIn>(crow + 16 * gg);
-      cb = mfma4(bq.x, cq.x, cb);
-      cb = mfma4(bq.y, cq.y, cb);
-      cb = mfma4(bq.z, cq.z, cb);
-      cb = mfma4(bq.w, cq.w, cb);
+      for (int m = 0; m < (NG + 1) / 2; ++m) {
+        const u32x2 b0 = *reinterpret_cast<const u32x2*>(brow + 32 * m);
+        const u32x2 c0 = *reinterpret_cast<const u32x2*>(crow + 32 * m);
+        u32x2 b1 = u32x2{0u, 0u}, c1 = b1;
+        if (2 * m + 1 < NG) {
+          b1 = *reinterpret_cast<const u32x2*>(brow + 32 * m + 16);
+          c1 = *reinterpret_cast<const u32x2*>(crow + 32 * m + 16);
+        }
+        cb = mfma32(u32x4{b0.x, b0.y, b1.x, b1.y}, u32x4{c0.x, c0.y, c1.x, c1.y}, cb);
+      }
+    } else {
+#pragma unroll
+      for (int gg = 0; gg < NG; ++gg) {
+        const f32x4 bq = load4<TIn>(brow + 16 * gg);
+        const f32x4 cq = load4<TIn>(crow + 16 * gg);
+        cb = mfma4(bq.x, cq.x, cb);
+        cb = mfma4(bq.y, cq.y, cb);
+        cb = mfma4(bq.z, cq.z, cb);
+        cb = mfma4(bq.w, cq.w, cb);
+      }
     }
     *reinterpret_cast<f32x4*>(s_cbt + (16 * ti + j) * kCbStride + 16 * tj + 4 * k) = cb;
   }
@@ -285,8 +365,8 @@ __global__ void __launch_bounds__(kTtThreads) verify_tt_kernel(VerifyArgs a, int
         if (r < W - 1) pwin[r] = raw_bits<TIn>(wg + (int64_t)r * CH + c);
       const float* cw = a.prm.conv_w + ((int64_t)l * CH + c) * W;
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
-        if (jj < W) pcw[jj] = cw[jj];
+      for (int t = 0; t < 4; ++t)
+        if (t < W) pcw[t] = cw[W - 1 - t];  // tap t weighs the node t steps up the path
       if (a.prm.conv_b) pcb = a.prm.conv_b[(int64_t)l * CH + c];
     }
     const int hh = tid / kTtMaxT, v = tid % kTtMaxT;  // 4 heads x 64 nodes
@@ -318,7 +398,7 @@ __global__ void __launch_bounds__(kTtThreads) verify_tt_kernel(VerifyArgs a, int
       for (int r = 0; r < 3; ++r)
         if (r < W - 1) s_win[r * kTtRows + tid] = from_bits<TIn>(pwin[r]);
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) s_cw[jj * kTtRows + tid] = pcw[jj];  // [tap][channel]
+      for (int t = 0; t < 4; ++t) s_cw[t * kTtRows + tid] = pcw[t];  // zero past W
       s_cb[tid] = pcb;
     }
     {
@@ -358,24 +438,70 @@ __global__ void __launch_bounds__(kTtThreads) verify_tt_kernel(VerifyArgs a, int
           up = up_up;
         }
       }
-      s_S2[hh * kTtMaxT + v] = acc * 1.4426950408889634;
+      const double s2 = acc * 1.4426950408889634;
+      s_S2[hh * kTtMaxT + v] = s2;
+      s_Ah[hh * kTtMaxT + v] = __builtin_amdgcn_exp2f((float)s2);
     }
-    for (int i = opaque_tid(); i < KT * kTtRows; i += kTtThreads) {
-      const int v = i / kTtRows, cl = i % kTtRows;
-      float xt = 0.0f;
-      if (v < T) {
-        float z = fmaf(s_cw[(W - 1) * kTtRows + cl], load_in(s_xr, v * kTtRows + cl), s_cb[cl]);
-        const int codes = s_cidx[v];
-        for (int jj = 1; jj < W; ++jj) {
-          const int code = (codes >> (8 * (jj - 1))) & 255;
-          const float u = code < T ? load_in(s_xr, code * kTtRows + cl) : load_in(s_win, (code - T) * kTtRows + cl);
-          z = fmaf(s_cw[(W - 1 - jj) * kTtRows + cl], u, z);
+    {
+      // causal conv over each node's root path, lane = channel, wave = node
+      // quads wave, wave + 4, ...: a node's tap sources are the same for the
+      // whole wave, and a quad leaves as one 16-byte store
+      const int tid = opaque_tid();
+      const int cl = tid & (kWave - 1);
+      const int wq = __builtin_amdgcn_readfirstlane(tid / kWave);
+      float wt[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) wt[t] = s_cw[t * kTtRows + cl];
+      const float cbv = s_cb[cl];
+#pragma unroll
+      for (int it = 0; it < TT; ++it) {
+        const int q = wq + kTtWaves * it;
+        f32x4 xq;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int v = 4 * q + r;
+          float xt = 0.0f;
+          if (v < T) {
+            const int codes = __builtin_amdgcn_readfirstlane(s_cidx[v]);
+            float z = fmaf(wt[0], load_in(s_xr, v * kTtRows + cl), cbv);
+#pragma unroll
+            for (int t = 1; t < 4; ++t) {
+              if (t < W) {
+                const int code = (codes >> (8 * (t - 1))) & 255;
+                const TIn* src = code < T ? s_xr + code * kTtRows : s_win + (code - T) * kTtRows;
+                z = fmaf(wt[t], load_in(src, cl), z);
+              }
+            }
+            xt = d.silu ? silu_hw(z) : z;
+          }
+          xq[r] = xt;
         }
-        xt = d.silu ? silu_f32(z) : z;
+        *reinterpret_cast<f32x4*>(s_xt + cl * kTtMaxT + 4 * (q ^ (cl & 15))) = xq;
       }
-      s_xt[xt_at(cl, v)] = xt;
     }
-    __syncthreads();
+    __syncthreads();  // the raw x rows are dead from here: their space holds M
+
+    // ---- M[v][u] for the block's head, once for all four waves, when the
+    // block lies inside one head (P a multiple of 64): thread = (tile pair
+    // slot, row, column quad) ----
+    const bool shared_m = P % kTtRows == 0;
+    if (shared_m) {
+      const int tid = opaque_tid();
+      const int slot = __builtin_amdgcn_readfirstlane(tid / kWave), r = (tid >> 2) & 15, cq = tid & 3;
+      const float Dh0 = s_D[0];
+#pragma unroll
+      for (int pp = 0; pp < (TT * (TT + 1) / 2 + kTtWaves - 1) / kTtWaves; ++pp) {
+        const int pi = kTtWaves * pp + slot;
+        if (pi < TT * (TT + 1) / 2) {
+          int ti = 0;
+          while ((ti + 1) * (ti + 2) / 2 <= pi) ++ti;
+          const int tj = pi - ti * (ti + 1) / 2;
+          const int v = 16 * ti + r, u0 = 16 * tj + 4 * cq;
+          *reinterpret_cast<f32x4*>(s_m + v * kCbStride + u0) =
+              m_quad(v, u0, s_S2, s_dt, s_anc[v], s_cbt + v * kCbStride + u0, Dh0);
+        }
+      }
+    }
 
     // ---- C . h0 on the matrix cores: lane (c + 16 q) ends with (C_{16 ti + 4q + r} . h_c) ----
     const int ln = opaque_tid() & (kWave - 1), j = ln & 15, k = ln >> 4;
@@ -384,68 +510,92 @@ __global__ void __launch_bounds__(kTtThreads) verify_tt_kernel(VerifyArgs a, int
     for (int ti = 0; ti < TT; ++ti) acc[ti] = f32x4{0.f, 0.f, 0.f, 0.f};
     const bool more = blk + 1 < NBLK;
     const float* nsin = a.state + (unit * DI + c0 + kTtRows + wave * 16 + j) * (int64_t)N + 4 * k;
+    if constexpr (E == 2) {
+      // bf16 C rows against the state split into three bf16 terms, two
+      // column groups per product
 #pragma unroll
-    for (int gg = 0; gg < NG; ++gg) {
+      for (int m = 0; m < (NG + 1) / 2; ++m) {
+        const bool two = 2 * m + 1 < NG;
+        u32x4 h0, h1, h2;
+        split3(hq[2 * m], two ? hq[2 * m + 1] : f32x4{0.f, 0.f, 0.f, 0.f}, h0, h1, h2);
 #pragma unroll
-      for (int ti = 0; ti < TT; ++ti) {
-        const f32x4 cq = load4<TIn>(reinterpret_cast<const TIn*>(s_C + (16 * ti + j) * rs) + 16 * gg + 4 * k);
-        acc[ti] = mfma4(cq.x, hq[gg].x, acc[ti]);
-        acc[ti] = mfma4(cq.y, hq[gg].y, acc[ti]);
-        acc[ti] = mfma4(cq.z, hq[gg].z, acc[ti]);
-        acc[ti] = mfma4(cq.w, hq[gg].w, acc[ti]);
+        for (int ti = 0; ti < TT; ++ti) {
+          const TIn* crow = reinterpret_cast<const TIn*>(s_C + (16 * ti + j) * rs) + 32 * m + 4 * k;
+          const u32x2 c0 = *reinterpret_cast<const u32x2*>(crow);
+          const u32x2 c1 = two ? *reinterpret_cast<const u32x2*>(crow + 16) : u32x2{0u, 0u};
+          const u32x4 ca = u32x4{c0.x, c0.y, c1.x, c1.y};
+          acc[ti] = mfma32(ca, h2, acc[ti]);
+          acc[ti] = mfma32(ca, h1, acc[ti]);
+          acc[ti] = mfma32(ca, h0, acc[ti]);
+        }
+        // these column groups are consumed: the next block's take their registers
+        if (more) {
+          hq[2 * m] = *reinterpret_cast<const f32x4*>(nsin + 32 * m);
+          if (two) hq[2 * m + 1] = *reinterpret_cast<const f32x4*>(nsin + 32 * m + 16);
+        }
+        asm volatile("" ::: "memory");
       }
-      // this column group is consumed: the next block's takes its registers
-      if (more) hq[gg] = *reinterpret_cast<const f32x4*>(nsin + 16 * gg);
-      // one column group's C operands at a time (hoisting all of them would
-      // take 4 NG x 4 registers)
-      asm volatile("" ::: "memory");
+    } else {
+#pragma unroll
+      for (int gg = 0; gg < NG; ++gg) {
+#pragma unroll
+        for (int ti = 0; ti < TT; ++ti) {
+          const f32x4 cq = load4<TIn>(reinterpret_cast<const TIn*>(s_C + (16 * ti + j) * rs) + 16 * gg + 4 * k);
+          acc[ti] = mfma4(cq.x, hq[gg].x, acc[ti]);
+          acc[ti] = mfma4(cq.y, hq[gg].y, acc[ti]);
+          acc[ti] = mfma4(cq.z, hq[gg].z, acc[ti]);
+          acc[ti] = mfma4(cq.w, hq[gg].w, acc[ti]);
+        }
+        // this column group is consumed: the next block's takes its registers
+        if (more) hq[gg] = *reinterpret_cast<const f32x4*>(nsin + 16 * gg);
+        // one column group's C operands at a time (hoisting all of them would
+        // take 4 NG x 4 registers)
+        asm volatile("" ::: "memory");
+      }
     }
 
     // ---- the path terms M[v][u] x~_u (u in tiles tj <= ti), with the diagonal D ----
+    __syncthreads();  // M is complete
     const int row = wave * 16 + j;                   // this lane's channel in the block
     const int hl = (c0 + wave * 16) / P - h_lo;      // the wave's head
     const float Dh = s_D[hl];
     const double* S2h = s_S2 + hl * kTtMaxT;
     const float* dth = s_dt + hl * kTtMaxT;
+    const float* Ahh = s_Ah + hl * kTtMaxT;
+    f32x4 yt[TT];
 #pragma unroll
     for (int ti = 0; ti < TT; ++ti) {
       const int vi = 16 * ti + j;                    // the M row (node) this lane supplies
-      const double Sv = S2h[vi];
-      const uint64_t ancm = s_anc[vi];
-      f32x4 y;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) y[t] = __builtin_amdgcn_exp2f((float)S2h[16 * ti + 4 * k + t]) * acc[ti][t];
+      const uint64_t ancm = shared_m ? 0 : s_anc[vi];
+      f32x4 y = *reinterpret_cast<const f32x4*>(Ahh + 16 * ti + 4 * k) * acc[ti];
 #pragma unroll
       for (int tj = 0; tj <= ti; ++tj) {
         const int u0 = 16 * tj + 4 * k;
-        const f32x4 du = *reinterpret_cast<const f32x4*>(dth + u0);
-        const f32x4 cbr = *reinterpret_cast<const f32x4*>(s_cbt + vi * kCbStride + u0);
-        const uint32_t nib = (uint32_t)(ancm >> u0) & 15u;  // which of u0 .. u0 + 3 are on vi's root path
-        f32x4 mop;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const float mv =
-              ((nib >> t) & 1) ? __builtin_amdgcn_exp2f((float)(Sv - S2h[u0 + t])) * du[t] * cbr[t] : 0.0f;
-          mop[t] = (u0 + t == vi) ? mv + Dh : mv;
-        }
+        const f32x4 mop = shared_m ? *reinterpret_cast<const f32x4*>(s_m + vi * kCbStride + u0)
+                                   : m_quad(vi, u0, S2h, dth, ancm, s_cbt + vi * kCbStride + u0, Dh);
         const f32x4 xq = *reinterpret_cast<const f32x4*>(s_xt + row * kTtMaxT + 4 * ((4 * tj + k) ^ (row & 15)));
         y = mfma4(mop.x, xq.x, y);
         y = mfma4(mop.y, xq.y, y);
         y = mfma4(mop.z, xq.z, y);
         y = mfma4(mop.w, xq.w, y);
       }
-      // lane (c + 16 k) holds nodes 16 ti + 4 k + r of channel row
-#pragma unroll
-      for (int r = 0; r < 4; ++r) s_ys[(16 * ti + 4 * k + r) * kTtRows + row] = tree_ok ? y[r] : __builtin_nanf("");
+      yt[ti] = y;
       // one node tile's operands at a time: hoisting the LDS reads of all
       // tiles above the loop would take most of the register file
       asm volatile("" ::: "memory");
     }
+    __syncthreads();  // M is consumed: its space takes the y staging
+    // lane (c + 16 k) holds nodes 16 ti + 4 k + r of channel row
+#pragma unroll
+    for (int ti = 0; ti < TT; ++ti)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        s_ys[(16 * ti + 4 * k + r) * kYsStride + row] = tree_ok ? yt[ti][r] : __builtin_nanf("");
     __syncthreads();
     for (int i = opaque_tid(); i < T * (kTtRows / 4); i += kTtThreads) {
       const int v = i / (kTtRows / 4), q = i % (kTtRows / 4);
       *reinterpret_cast<f32x4*>(a.y + (unit * T + v) * DI + c0 + 4 * q) =
-          *reinterpret_cast<const f32x4*>(s_ys + v * kTtRows + 4 * q);
+          *reinterpret_cast<const f32x4*>(s_ys + v * kYsStride + 4 * q);
     }
     __syncthreads();  // the staging space takes the next block's x rows
   }

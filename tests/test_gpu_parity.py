@@ -64,6 +64,13 @@ SMALL = [
     (1, 2, 1, 8, 16, 16, 1, 4, False, True, True, "forest"),
     (2, 5, 9, 12, 16, 64, 1, 4, True, False, False, "forest"),
     (1, 2, 24, 5, 64, 128, 5, 4, True, False, False, "forest"),
+    # 17..64-node trees on the matrix cores: one column group (d_state 16)
+    # and heads of 16 channels (four heads per 64-channel block), silu
+    (1, 3, 20, 8, 16, 16, 1, 4, True, True, False, "forest"),
+    # heads of 32 channels (two heads per block), width 3, bias
+    (2, 2, 50, 8, 32, 32, 2, 3, True, True, True, "forest"),
+    # fp32 inputs, chain and star trees of 33 nodes, silu
+    (1, 2, 33, 4, 64, 128, 1, 4, False, True, False, "chain_or_star"),
 ]
 
 
