@@ -133,6 +133,18 @@ __device__ __forceinline__ int opaque_tid() {
   return v;
 }
 
+// softplus(z) = max(z, 0) + log1p(exp(-|z|)) with the hardware exp2 and
+// log2; log1p(t) as log(u) t / (u - 1), u = 1 + t, which cancels the
+// rounding of u (Goldberg's form), so small t keeps its relative accuracy;
+// above 20 the result is z, as in the plain definition's usual cut-over
+__device__ __forceinline__ float softplus_hw(float z) {
+  const float t = __builtin_amdgcn_exp2f(-1.4426950408889634f * fabsf(z));
+  const float u = 1.0f + t;
+  const float lp =
+      u == 1.0f ? t : __builtin_amdgcn_logf(u) * 0.6931471805599453f * t * __builtin_amdgcn_rcpf(u - 1.0f);
+  return z > 20.0f ? z : fmaxf(z, 0.0f) + lp;
+}
+
 // silu with the hardware exp2 and reciprocal (about 1 ulp each)
 __device__ __forceinline__ float silu_hw(float z) {
   return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * z));
@@ -146,6 +158,7 @@ __device__ __forceinline__ int xt_at(int c, int v) { return c * kTtMaxT + 4 * ((
 // M[v][u0 .. u0 + 3] of one head: exp(S_v - S_u) dt_u (C_v . B_u) where u is
 // on v's root path (ancestor bits ancv), zero elsewhere, plus D on the
 // diagonal; S in base-2 units, fp64 (the difference is taken before rounding)
+template <bool kDiag>
 __device__ __forceinline__ f32x4 m_quad(int v, int u0, const double* S2h, const float* dth, uint64_t ancv,
                                         const float* cbr, float Dh) {
   typedef double f64x2 __attribute__((ext_vector_type(2)));
@@ -161,27 +174,28 @@ __device__ __forceinline__ f32x4 m_quad(int v, int u0, const double* S2h, const 
     const double su = t == 0 ? sa.x : (t == 1 ? sa.y : (t == 2 ? sb.x : sb.y));
     const float e = __builtin_amdgcn_exp2f((float)(Sv - su)) * du[t] * cb[t];
     const float mv = ((nib >> t) & 1) ? e : 0.0f;
-    m[t] = u0 + t == v ? mv + Dh : mv;
+    m[t] = kDiag && u0 + t == v ? mv + Dh : mv;
   }
   return m;
 }
 
 // LDS layout (byte offsets)
 struct TtLds {
-  int parent, anc, cidx, misc, C, cbt, X, Y, win, So, S2, Ah, dt, D, cw, cb, total, row;
+  int parent, anc, cidx, misc, C, cbt, X, Y, So, S2, Ah, dt, D, cw, cb, total, row;
   __host__ __device__ TtLds(int N, int E) {
     int o = 0;
     row = N * E + 16;                          // staged B / C row stride (padded)
     parent = o; o += 4 * kTtMaxT;
     anc = o; o += 8 * kTtMaxT;                 // root-path bitmask per node (64 bits)
-    cidx = o; o += 4 * kTtMaxT;                // conv inputs of taps 1..3: node, or T + window row
+    cidx = o; o += 4 * kTtMaxT;                // conv inputs of taps 1..3: row of the window-and-x rows
     misc = o; o += 16;                         // [0] tree ok
     C = o; o += kTtMaxT * row;                 // C rows (raw)
     cbt = o; o += 4 * kTtMaxT * kCbStride;     // C_v . B_u, [v][u] (padded rows)
     X = o;                                     // B rows (raw) until the dots exist, then conv outputs
     o += kTtMaxT * row > 4 * kTtRows * kTtMaxT ? kTtMaxT * row : 4 * kTtRows * kTtMaxT;
-    Y = o; o += 4 * kTtMaxT * kYsStride;       // raw x rows of a block, then M [v][u], then y staging [node][channel]
-    win = o; o += 16 * ((3 * kTtRows * E + 15) / 16);  // the block's old window rows (raw)
+    // a block's 3 window rows (the last one at row 2) and x rows (node v at
+    // row 3 + v), raw; then M [v][u]; then y staging [node][channel]
+    Y = o; o += 4 * kTtMaxT * kYsStride;
     So = o; o += 4 * 4 * kTtMaxT;              // [head][node] dt * A
     S2 = o; o += 8 * 4 * kTtMaxT;              // [head][node] cumulative over the root path, times log2(e), fp64
     Ah = o; o += 4 * 4 * kTtMaxT;              // [head][node] exp(S)
@@ -224,8 +238,8 @@ __global__ void __launch_bounds__(kTtThreads) verify_tt_kernel(VerifyArgs a, int
   float* s_xt = reinterpret_cast<float*>(smem + lo.X);
   float* s_ys = reinterpret_cast<float*>(smem + lo.Y);
   float* s_m = reinterpret_cast<float*>(smem + lo.Y);
-  TIn* s_xr = reinterpret_cast<TIn*>(smem + lo.Y);
-  TIn* s_win = reinterpret_cast<TIn*>(smem + lo.win);
+  TIn* s_xw = reinterpret_cast<TIn*>(smem + lo.Y);
+  TIn* s_xr = s_xw + 3 * kTtRows;
   float* s_So = reinterpret_cast<float*>(smem + lo.So);
   double* s_S2 = reinterpret_cast<double*>(smem + lo.S2);
   float* s_Ah = reinterpret_cast<float*>(smem + lo.Ah);
@@ -284,7 +298,9 @@ __global__ void __launch_bounds__(kTtThreads) verify_tt_kernel(VerifyArgs a, int
 #pragma unroll
       for (int jj = 1; jj < 4; ++jj) {
         const int an = jj == 1 ? a1 : (jj == 2 ? a2 : a3);
-        const int code = an >= 0 ? an : T + (W - 2) - (jj - depth);
+        // past the root: window row (W - 2) - (jj - depth), stored at row
+        // 2 - (jj - depth) of the window-and-x rows
+        const int code = an >= 0 ? an + 3 : 2 - (jj - depth);
         if (jj < W) packed |= code << (8 * (jj - 1));
       }
     }
@@ -396,7 +412,7 @@ __global__ void __launch_bounds__(kTtThreads) verify_tt_kernel(VerifyArgs a, int
     if (tid < kTtRows) {
 #pragma unroll
       for (int r = 0; r < 3; ++r)
-        if (r < W - 1) s_win[r * kTtRows + tid] = from_bits<TIn>(pwin[r]);
+        if (r < W - 1) s_xw[(4 - W + r) * kTtRows + tid] = from_bits<TIn>(pwin[r]);
 #pragma unroll
       for (int t = 0; t < 4; ++t) s_cw[t * kTtRows + tid] = pcw[t];  // zero past W
       s_cb[tid] = pcb;
@@ -405,7 +421,7 @@ __global__ void __launch_bounds__(kTtThreads) verify_tt_kernel(VerifyArgs a, int
       const int hh = tid / kTtMaxT, v = tid % kTtMaxT;
       float dtv = 0.0f, so = 0.0f;
       if (hh < HW && v < T) {
-        dtv = softplus_f32((sizeof(TIn) == 2 ? __uint_as_float(pdt << 16) : __uint_as_float(pdt)) + pbias);
+        dtv = softplus_hw((sizeof(TIn) == 2 ? __uint_as_float(pdt << 16) : __uint_as_float(pdt)) + pbias);
         so = dtv * pA;
       }
       s_dt[hh * kTtMaxT + v] = dtv;
@@ -467,9 +483,8 @@ __global__ void __launch_bounds__(kTtThreads) verify_tt_kernel(VerifyArgs a, int
 #pragma unroll
             for (int t = 1; t < 4; ++t) {
               if (t < W) {
-                const int code = (codes >> (8 * (t - 1))) & 255;
-                const TIn* src = code < T ? s_xr + code * kTtRows : s_win + (code - T) * kTtRows;
-                z = fmaf(wt[t], load_in(src, cl), z);
+                const int row = (codes >> (8 * (t - 1))) & 255;
+                z = fmaf(wt[t], load_in(s_xw, row * kTtRows + cl), z);
               }
             }
             xt = d.silu ? silu_hw(z) : z;
@@ -490,15 +505,16 @@ __global__ void __launch_bounds__(kTtThreads) verify_tt_kernel(VerifyArgs a, int
       const int slot = __builtin_amdgcn_readfirstlane(tid / kWave), r = (tid >> 2) & 15, cq = tid & 3;
       const float Dh0 = s_D[0];
 #pragma unroll
-      for (int pp = 0; pp < (TT * (TT + 1) / 2 + kTtWaves - 1) / kTtWaves; ++pp) {
-        const int pi = kTtWaves * pp + slot;
-        if (pi < TT * (TT + 1) / 2) {
-          int ti = 0;
-          while ((ti + 1) * (ti + 2) / 2 <= pi) ++ti;
-          const int tj = pi - ti * (ti + 1) / 2;
-          const int v = 16 * ti + r, u0 = 16 * tj + 4 * cq;
-          *reinterpret_cast<f32x4*>(s_m + v * kCbStride + u0) =
-              m_quad(v, u0, s_S2, s_dt, s_anc[v], s_cbt + v * kCbStride + u0, Dh0);
+      for (int ti = 0; ti < TT; ++ti) {
+#pragma unroll
+        for (int tj = 0; tj <= ti; ++tj) {
+          if ((ti * (ti + 1) / 2 + tj) % kTtWaves == slot) {  // tile pairs dealt round the waves
+            const int v = 16 * ti + r, u0 = 16 * tj + 4 * cq;
+            const float* cbr = s_cbt + v * kCbStride + u0;
+            *reinterpret_cast<f32x4*>(s_m + v * kCbStride + u0) =
+                ti == tj ? m_quad<true>(v, u0, s_S2, s_dt, s_anc[v], cbr, Dh0)
+                         : m_quad<false>(v, u0, s_S2, s_dt, s_anc[v], cbr, Dh0);
+          }
         }
       }
     }
@@ -571,8 +587,10 @@ __global__ void __launch_bounds__(kTtThreads) verify_tt_kernel(VerifyArgs a, int
 #pragma unroll
       for (int tj = 0; tj <= ti; ++tj) {
         const int u0 = 16 * tj + 4 * k;
-        const f32x4 mop = shared_m ? *reinterpret_cast<const f32x4*>(s_m + vi * kCbStride + u0)
-                                   : m_quad(vi, u0, S2h, dth, ancm, s_cbt + vi * kCbStride + u0, Dh);
+        const float* cbr = s_cbt + vi * kCbStride + u0;
+        const f32x4 mop = shared_m    ? *reinterpret_cast<const f32x4*>(s_m + vi * kCbStride + u0)
+                          : tj == ti ? m_quad<true>(vi, u0, S2h, dth, ancm, cbr, Dh)
+                                     : m_quad<false>(vi, u0, S2h, dth, ancm, cbr, Dh);
         const f32x4 xq = *reinterpret_cast<const f32x4*>(s_xt + row * kTtMaxT + 4 * ((4 * tj + k) ^ (row & 15)));
         y = mfma4(mop.x, xq.x, y);
         y = mfma4(mop.y, xq.y, y);
