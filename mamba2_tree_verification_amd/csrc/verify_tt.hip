@@ -414,6 +414,9 @@ __global__ void __launch_bounds__(kTtThreads) verify_tt_kernel(VerifyArgs a, int
       for (int r = 0; r < 3; ++r)
         if (r < W - 1) s_xw[(4 - W + r) * kTtRows + tid] = from_bits<TIn>(pwin[r]);
 #pragma unroll
+      for (int r = 0; r < 3; ++r)  // rows above the window: read by unused taps (weight zero), so zero
+        if (r < 4 - W) s_xw[r * kTtRows + tid] = from_bits<TIn>(0u);
+#pragma unroll
       for (int t = 0; t < 4; ++t) s_cw[t * kTtRows + tid] = pcw[t];  // zero past W
       s_cb[tid] = pcb;
     }
@@ -472,24 +475,24 @@ __global__ void __launch_bounds__(kTtThreads) verify_tt_kernel(VerifyArgs a, int
 #pragma unroll
       for (int it = 0; it < TT; ++it) {
         const int q = wq + kTtWaves * it;
+        // all sixteen tap reads of the quad first, then the arithmetic:
+        // unused taps (weight zero) and nodes past T read zeroed rows
+        const u32x4 codes4 = *reinterpret_cast<const u32x4*>(s_cidx + 4 * q);
+        float xs[4][4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const uint32_t codes = __builtin_amdgcn_readfirstlane(codes4[r]);
+          xs[r][0] = load_in(s_xr, (4 * q + r) * kTtRows + cl);
+#pragma unroll
+          for (int t = 1; t < 4; ++t) xs[r][t] = load_in(s_xw, ((codes >> (8 * (t - 1))) & 255) * kTtRows + cl);
+        }
         f32x4 xq;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int v = 4 * q + r;
-          float xt = 0.0f;
-          if (v < T) {
-            const int codes = __builtin_amdgcn_readfirstlane(s_cidx[v]);
-            float z = fmaf(wt[0], load_in(s_xr, v * kTtRows + cl), cbv);
+          float z = fmaf(wt[0], xs[r][0], cbv);
 #pragma unroll
-            for (int t = 1; t < 4; ++t) {
-              if (t < W) {
-                const int row = (codes >> (8 * (t - 1))) & 255;
-                z = fmaf(wt[t], load_in(s_xw, row * kTtRows + cl), z);
-              }
-            }
-            xt = d.silu ? silu_hw(z) : z;
-          }
-          xq[r] = xt;
+          for (int t = 1; t < 4; ++t) z = fmaf(wt[t], xs[r][t], z);
+          xq[r] = 4 * q + r < T ? (d.silu ? silu_hw(z) : z) : 0.0f;
         }
         *reinterpret_cast<f32x4*>(s_xt + cl * kTtMaxT + 4 * (q ^ (cl & 15))) = xq;
       }
