@@ -37,8 +37,11 @@ constexpr int kTtRows = 64;   // channels per block
 constexpr int kTtWaves = 4;
 constexpr int kTtThreads = kTtWaves * kWave;
 constexpr int kTtMaxT = 64;
-constexpr int kCbStride = kTtMaxT + 4;  // C.B and M row stride: rows of a node tile on different LDS banks
-constexpr int kYsStride = kTtRows + 4;  // y staging row stride
+// C.B and M are kept by lower-triangular tile pair (ti, tj), pair index
+// ti (ti + 1) / 2 + tj, as 16 rows of 16 values; rows are 20 floats apart so
+// that the 16 rows a wave reads at once fall on different LDS banks
+constexpr int kPairStride = 20;
+__host__ __device__ constexpr int pair_of(int ti, int tj) { return ti * (ti + 1) / 2 + tj; }
 
 __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -150,6 +153,24 @@ __device__ __forceinline__ float silu_hw(float z) {
   return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * z));
 }
 
+// the sum of acc over the root path of node (lane) v, given each node's
+// parent up (-1 at a root) within one wave: pointer jumping, six rounds for
+// paths of up to 64 nodes (round r adds the partial sum of the node 2^r
+// steps up)
+__device__ __forceinline__ double root_path_sum(double acc, int up, int v) {
+#pragma unroll
+  for (int r = 0; r < 6; ++r) {
+    const int src = up >= 0 ? up : v;
+    const double acc_up = __shfl(acc, src);
+    const int up_up = __shfl(up, src);
+    if (up >= 0) {
+      acc += acc_up;
+      up = up_up;
+    }
+  }
+  return acc;
+}
+
 // conv outputs [channel][node] in the MFMA B-operand layout: quad q (nodes
 // 4 q .. 4 q + 3) of channel row c sits at quad q ^ (c & 15), so that the 16
 // channels a wave reads at once fall on different banks
@@ -181,26 +202,30 @@ __device__ __forceinline__ f32x4 m_quad(int v, int u0, const double* S2h, const 
 
 // LDS layout (byte offsets)
 struct TtLds {
-  int parent, anc, cidx, misc, C, cbt, X, Y, So, S2, Ah, dt, D, cw, cb, total, row;
-  __host__ __device__ TtLds(int N, int E) {
+  int parent, anc, cidx, misc, C, cbt, X, Y, Mo, So, S2, Ah, dt, D, cw, cb, total, row;
+  __host__ __device__ TtLds(int N, int E, int TT) {
+    const int KT = 16 * TT, pair_bytes = 4 * 16 * kPairStride * pair_of(TT, 0);
     int o = 0;
     row = N * E + 16;                          // staged B / C row stride (padded)
     parent = o; o += 4 * kTtMaxT;
     anc = o; o += 8 * kTtMaxT;                 // root-path bitmask per node (64 bits)
     cidx = o; o += 4 * kTtMaxT;                // conv inputs of taps 1..3: row of the window-and-x rows
     misc = o; o += 16;                         // [0] tree ok
-    C = o; o += kTtMaxT * row;                 // C rows (raw)
-    cbt = o; o += 4 * kTtMaxT * kCbStride;     // C_v . B_u, [v][u] (padded rows)
+    C = o; o += KT * row;                      // C rows (raw)
+    cbt = o; o += pair_bytes;                  // C_v . B_u by tile pair
     X = o;                                     // B rows (raw) until the dots exist, then conv outputs
-    o += kTtMaxT * row > 4 * kTtRows * kTtMaxT ? kTtMaxT * row : 4 * kTtRows * kTtMaxT;
+    o += KT * row > 4 * kTtRows * kTtMaxT ? KT * row : 4 * kTtRows * kTtMaxT;
     // a block's 3 window rows (the last one at row 2) and x rows (node v at
-    // row 3 + v), raw; then M [v][u]; then y staging [node][channel]
-    Y = o; o += 4 * kTtMaxT * kYsStride;
+    // row 3 + v), raw
+    Y = o; o += ((3 + KT) * kTtRows * E + 15) / 16 * 16;
+    Mo = o; o += pair_bytes;                   // M of the block's head by tile pair (one head per block)
     So = o; o += 4 * 4 * kTtMaxT;              // [head][node] dt * A
-    S2 = o; o += 8 * 4 * kTtMaxT;              // [head][node] cumulative over the root path, times log2(e), fp64
+    // [head][node] S over the root path times log2(e), fp64; with one head
+    // per block, [wave][node]: each wave's own copy of the head's
+    S2 = o; o += 8 * 4 * kTtMaxT;
     Ah = o; o += 4 * 4 * kTtMaxT;              // [head][node] exp(S)
-    dt = o; o += 4 * 4 * kTtMaxT;              // [head][node]
-    D = o; o += 16;
+    dt = o; o += 4 * 8 * kTtMaxT;              // [block][node]; several heads per block: [parity][head][node]
+    D = o; o += 32;                            // [block]; several heads per block: [parity][head]
     cw = o; o += 4 * 4 * kTtRows;              // [tap][channel], tap t = the node t steps up the path
     cb = o; o += 4 * kTtRows;
     total = o;
@@ -227,7 +252,7 @@ __global__ void __launch_bounds__(kTtThreads) verify_tt_kernel(VerifyArgs a, int
   const int g = cw0 / (DI / G);
 
   extern __shared__ __align__(16) unsigned char smem[];
-  const TtLds lo(N, E);
+  const TtLds lo(N, E, TT);
   int32_t* s_parent = reinterpret_cast<int32_t*>(smem + lo.parent);
   uint64_t* s_anc = reinterpret_cast<uint64_t*>(smem + lo.anc);
   int32_t* s_cidx = reinterpret_cast<int32_t*>(smem + lo.cidx);
@@ -236,8 +261,7 @@ __global__ void __launch_bounds__(kTtThreads) verify_tt_kernel(VerifyArgs a, int
   float* s_cbt = reinterpret_cast<float*>(smem + lo.cbt);
   unsigned char* s_B = smem + lo.X;
   float* s_xt = reinterpret_cast<float*>(smem + lo.X);
-  float* s_ys = reinterpret_cast<float*>(smem + lo.Y);
-  float* s_m = reinterpret_cast<float*>(smem + lo.Y);
+  float* s_m = reinterpret_cast<float*>(smem + lo.Mo);
   TIn* s_xw = reinterpret_cast<TIn*>(smem + lo.Y);
   TIn* s_xr = s_xw + 3 * kTtRows;
   float* s_So = reinterpret_cast<float*>(smem + lo.So);
@@ -346,7 +370,7 @@ __global__ void __launch_bounds__(kTtThreads) verify_tt_kernel(VerifyArgs a, int
         cb = mfma4(bq.w, cq.w, cb);
       }
     }
-    *reinterpret_cast<f32x4*>(s_cbt + (16 * ti + j) * kCbStride + 16 * tj + 4 * k) = cb;
+    *reinterpret_cast<f32x4*>(s_cbt + (16 * pi + j) * kPairStride + 4 * k) = cb;
   }
   __syncthreads();  // the B rows are dead from here: their space holds the conv outputs
   const bool tree_ok = s_misc[0] != 0;
@@ -354,6 +378,28 @@ __global__ void __launch_bounds__(kTtThreads) verify_tt_kernel(VerifyArgs a, int
   const TIn* xg = reinterpret_cast<const TIn*>(a.x) + unit * T * (int64_t)DI;
   const TIn* wg = reinterpret_cast<const TIn*>(a.window) + unit * (W - 1) * (int64_t)CH;
   const TIn* dtg = reinterpret_cast<const TIn*>(a.dt_raw) + unit * T * (int64_t)H;
+  // a 64-channel block inside one head (P a multiple of 64): the head's dt,
+  // S and exp(S) are formed here for all the workgroup's blocks (wave =
+  // block, lane = node), and M once per block for all four waves
+  const bool shared_m = P % kTtRows == 0;
+  if (shared_m) {
+    const int tid = opaque_tid();
+    const int bw = __builtin_amdgcn_readfirstlane(tid / kWave), v = tid % kWave;
+    if (bw < NBLK) {
+      const int h = (cw0 + bw * kTtRows) / P;
+      float dtv = 0.0f;  // zero past T
+      if (v < T) dtv = softplus_hw(load_in(dtg, (int64_t)v * H + h) + a.prm.dt_bias[(int64_t)l * H + h]);
+      int up = v < T ? s_parent[v] : -1;
+      up = (up >= 0 && up < v) ? up : -1;  // (an invalid tree's output is discarded; keep indices in range)
+      // S in fp64: down a 64-node chain it reaches ~-70, and M takes
+      // differences of two such sums
+      const double s2 = root_path_sum((double)(dtv * a.prm.A[(int64_t)l * H + h]), up, v) * 1.4426950408889634;
+      s_dt[bw * kTtMaxT + v] = dtv;
+      s_S2[bw * kTtMaxT + v] = s2;
+      s_Ah[bw * kTtMaxT + v] = __builtin_amdgcn_exp2f((float)s2);
+      if (v == 0) s_D[bw] = a.prm.D[(int64_t)l * H + h];
+    }
+  }
   // per-block inputs, loaded a block ahead into registers: raw x quads,
   // and by role the window rows and conv parameters (threads < 64) and the
   // head scalars (thread = head x node)
@@ -371,8 +417,11 @@ __global__ void __launch_bounds__(kTtThreads) verify_tt_kernel(VerifyArgs a, int
     for (int it = 0; it < kXQ; ++it) {
       const int qi = tid + it * kTtThreads;
       const int v = qi / (kTtRows / 4), c4 = (qi % (kTtRows / 4)) * 4;
-      pxr[it] = RawQ{};
-      if (v < T) pxr[it] = *reinterpret_cast<const RawQ*>(xg + (int64_t)v * DI + c0 + c4);
+      // rows past T repeat row T - 1: no tap reads them, and their own conv
+      // output is discarded (an unconditional load keeps the register free
+      // of a reset that would wait on every load in flight)
+      const int vr = v < T ? v : T - 1;
+      pxr[it] = *reinterpret_cast<const RawQ*>(xg + (int64_t)vr * DI + c0 + c4);
     }
     if (tid < kTtRows) {
       const int c = c0 + tid;
@@ -386,23 +435,22 @@ __global__ void __launch_bounds__(kTtThreads) verify_tt_kernel(VerifyArgs a, int
       if (a.prm.conv_b) pcb = a.prm.conv_b[(int64_t)l * CH + c];
     }
     const int hh = tid / kTtMaxT, v = tid % kTtMaxT;  // 4 heads x 64 nodes
-    if (hh < HW && v < T) {
+    if (!shared_m && hh < HW && v < T) {
       const int h = h_lo + hh;
       pdt = raw_bits<TIn>(dtg + (int64_t)v * H + h);
       pbias = a.prm.dt_bias[(int64_t)l * H + h];
       pA = a.prm.A[(int64_t)l * H + h];
     }
-    if (tid < HW) pD = a.prm.D[(int64_t)l * H + h_lo + tid];
+    if (!shared_m && tid < HW) pD = a.prm.D[(int64_t)l * H + h_lo + tid];
   };
-  prefetch(0);
-  for (int blk = 0; blk < NBLK; ++blk) {
+  // a block's inputs from the prefetch registers into LDS: x and window
+  // rows, conv parameters, and (blocks of several heads) the heads' dt, dt A
+  // and D, dt and D double-buffered by block parity
+  auto deliver = [&](int blk) {
+    const int tid = opaque_tid();
     const int c0 = cw0 + blk * kTtRows;
     const int h_lo = c0 / P;
-    const int HW = (c0 + kTtRows - 1) / P - h_lo + 1;  // heads touched (<= 4: P is a multiple of 16)
-
-    // ---- deliver the block's inputs to LDS, then start the next block's ----
-    {
-    const int tid = opaque_tid();
+    const int HW = (c0 + kTtRows - 1) / P - h_lo + 1;
 #pragma unroll
     for (int it = 0; it < kXQ; ++it) {
       const int qi = tid + it * kTtThreads;
@@ -420,44 +468,41 @@ __global__ void __launch_bounds__(kTtThreads) verify_tt_kernel(VerifyArgs a, int
       for (int t = 0; t < 4; ++t) s_cw[t * kTtRows + tid] = pcw[t];  // zero past W
       s_cb[tid] = pcb;
     }
-    {
+    if (!shared_m) {
       const int hh = tid / kTtMaxT, v = tid % kTtMaxT;
       float dtv = 0.0f, so = 0.0f;
       if (hh < HW && v < T) {
         dtv = softplus_hw((sizeof(TIn) == 2 ? __uint_as_float(pdt << 16) : __uint_as_float(pdt)) + pbias);
         so = dtv * pA;
       }
-      s_dt[hh * kTtMaxT + v] = dtv;
+      s_dt[((blk & 1) * 4 + hh) * kTtMaxT + v] = dtv;
       s_So[hh * kTtMaxT + v] = so;
-      if (tid < HW) s_D[tid] = pD;
+      if (tid < HW) s_D[(blk & 1) * 4 + tid] = pD;
     }
-    }
-    if (blk + 1 < NBLK) prefetch(blk + 1);
-    __syncthreads();
-    {
+  };
+  // Order within a block: [S, conv, M] barrier [next block's delivery, C . h
+  // (loading the next block's state), prefetch of the block after, path
+  // terms and y] barrier.  Every wait on a prefetch register then covers
+  // only loads issued at least a phase earlier (the wait counter also
+  // counts the y stores).
+  prefetch(0);
+  deliver(0);
+  if (NBLK > 1) prefetch(1);
+  for (int blk = 0; blk < NBLK; ++blk) {
+    const int c0 = cw0 + blk * kTtRows;
+    const int h_lo = c0 / P;
+    __syncthreads();  // the block's inputs are in LDS; the previous block's path terms are done
+    if (!shared_m) {
       // S along each root path (base-2 units), accumulated in fp64: down a
       // 64-node chain it reaches ~-70, and the decay between two nodes is
       // the difference of two such sums, which fp32 would leave with ~1e-5
       // of cancellation error; fp64 keeps the difference exact to the fp32
-      // rounding of its own terms.  Wave = head, lane = node: pointer
-      // jumping over the parent links, 6 rounds for paths of up to 64 nodes
-      // (each round adds the partial sum of the node 2^r steps up).
+      // rounding of its own terms.  Wave = head, lane = node.
       const int tid = opaque_tid();
       const int hh = tid / kTtMaxT, v = tid % kTtMaxT;
-      double acc = (double)s_So[hh * kTtMaxT + v];  // zero past T
       int up = v < T ? s_parent[v] : -1;
       up = (up >= 0 && up < v) ? up : -1;  // (an invalid tree's output is discarded; keep indices in range)
-#pragma unroll
-      for (int r = 0; r < 6; ++r) {
-        const int src = up >= 0 ? up : v;
-        const double acc_up = __shfl(acc, src);
-        const int up_up = __shfl(up, src);
-        if (up >= 0) {
-          acc += acc_up;
-          up = up_up;
-        }
-      }
-      const double s2 = acc * 1.4426950408889634;
+      const double s2 = root_path_sum((double)s_So[hh * kTtMaxT + v], up, v) * 1.4426950408889634;  // zero past T
       s_S2[hh * kTtMaxT + v] = s2;
       s_Ah[hh * kTtMaxT + v] = __builtin_amdgcn_exp2f((float)s2);
     }
@@ -497,30 +542,32 @@ __global__ void __launch_bounds__(kTtThreads) verify_tt_kernel(VerifyArgs a, int
         *reinterpret_cast<f32x4*>(s_xt + cl * kTtMaxT + 4 * (q ^ (cl & 15))) = xq;
       }
     }
-    __syncthreads();  // the raw x rows are dead from here: their space holds M
 
-    // ---- M[v][u] for the block's head, once for all four waves, when the
-    // block lies inside one head (P a multiple of 64): thread = (tile pair
+    // ---- M[v][u] of the block's head when shared: thread = (tile pair
     // slot, row, column quad) ----
-    const bool shared_m = P % kTtRows == 0;
     if (shared_m) {
       const int tid = opaque_tid();
       const int slot = __builtin_amdgcn_readfirstlane(tid / kWave), r = (tid >> 2) & 15, cq = tid & 3;
-      const float Dh0 = s_D[0];
+      const double* S2w = s_S2 + blk * kTtMaxT;
+      const float* dtw = s_dt + blk * kTtMaxT;
+      const float Dh0 = s_D[blk];
 #pragma unroll
       for (int ti = 0; ti < TT; ++ti) {
 #pragma unroll
         for (int tj = 0; tj <= ti; ++tj) {
-          if ((ti * (ti + 1) / 2 + tj) % kTtWaves == slot) {  // tile pairs dealt round the waves
+          const int pi = pair_of(ti, tj);
+          if (pi % kTtWaves == slot) {  // tile pairs dealt round the waves
             const int v = 16 * ti + r, u0 = 16 * tj + 4 * cq;
-            const float* cbr = s_cbt + v * kCbStride + u0;
-            *reinterpret_cast<f32x4*>(s_m + v * kCbStride + u0) =
-                ti == tj ? m_quad<true>(v, u0, s_S2, s_dt, s_anc[v], cbr, Dh0)
-                         : m_quad<false>(v, u0, s_S2, s_dt, s_anc[v], cbr, Dh0);
+            const float* cbr = s_cbt + (16 * pi + r) * kPairStride + 4 * cq;
+            *reinterpret_cast<f32x4*>(s_m + (16 * pi + r) * kPairStride + 4 * cq) =
+                ti == tj ? m_quad<true>(v, u0, S2w, dtw, s_anc[v], cbr, Dh0)
+                         : m_quad<false>(v, u0, S2w, dtw, s_anc[v], cbr, Dh0);
           }
         }
       }
     }
+    __syncthreads();  // conv outputs and M are complete; x rows, conv parameters and dt A are free
+    if (blk + 1 < NBLK) deliver(blk + 1);
 
     // ---- C . h0 on the matrix cores: lane (c + 16 q) ends with (C_{16 ti + 4q + r} . h_c) ----
     const int ln = opaque_tid() & (kWave - 1), j = ln & 15, k = ln >> 4;
@@ -573,15 +620,16 @@ __global__ void __launch_bounds__(kTtThreads) verify_tt_kernel(VerifyArgs a, int
       }
     }
 
+    if (blk + 2 < NBLK) prefetch(blk + 2);
+
     // ---- the path terms M[v][u] x~_u (u in tiles tj <= ti), with the diagonal D ----
-    __syncthreads();  // M is complete
     const int row = wave * 16 + j;                   // this lane's channel in the block
     const int hl = (c0 + wave * 16) / P - h_lo;      // the wave's head
-    const float Dh = s_D[hl];
+    const float Dh = s_D[(blk & 1) * 4 + hl];
     const double* S2h = s_S2 + hl * kTtMaxT;
-    const float* dth = s_dt + hl * kTtMaxT;
-    const float* Ahh = s_Ah + hl * kTtMaxT;
-    f32x4 yt[TT];
+    const float* dth = s_dt + ((blk & 1) * 4 + hl) * kTtMaxT;
+    const float* Ahh = s_Ah + (shared_m ? blk : hl) * kTtMaxT;
+    float* yrow = a.y + unit * T * (int64_t)DI + c0 + row;
 #pragma unroll
     for (int ti = 0; ti < TT; ++ti) {
       const int vi = 16 * ti + j;                    // the M row (node) this lane supplies
@@ -590,8 +638,9 @@ __global__ void __launch_bounds__(kTtThreads) verify_tt_kernel(VerifyArgs a, int
 #pragma unroll
       for (int tj = 0; tj <= ti; ++tj) {
         const int u0 = 16 * tj + 4 * k;
-        const float* cbr = s_cbt + vi * kCbStride + u0;
-        const f32x4 mop = shared_m    ? *reinterpret_cast<const f32x4*>(s_m + vi * kCbStride + u0)
+        const int pq = (16 * pair_of(ti, tj) + j) * kPairStride + 4 * k;  // this lane's quad of the pair
+        const float* cbr = s_cbt + pq;
+        const f32x4 mop = shared_m    ? *reinterpret_cast<const f32x4*>(s_m + pq)
                           : tj == ti ? m_quad<true>(vi, u0, S2h, dth, ancm, cbr, Dh)
                                      : m_quad<false>(vi, u0, S2h, dth, ancm, cbr, Dh);
         const f32x4 xq = *reinterpret_cast<const f32x4*>(s_xt + row * kTtMaxT + 4 * ((4 * tj + k) ^ (row & 15)));
@@ -600,25 +649,18 @@ __global__ void __launch_bounds__(kTtThreads) verify_tt_kernel(VerifyArgs a, int
         y = mfma4(mop.z, xq.z, y);
         y = mfma4(mop.w, xq.w, y);
       }
-      yt[ti] = y;
+      // lane (c + 16 k) holds nodes 16 ti + 4 k + r of channel row: each
+      // store covers 16 channels (64 bytes) of four nodes; the four waves
+      // fill each node's 256-byte row segment
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int v = 16 * ti + 4 * k + r;
+        if (v < T) yrow[(int64_t)v * DI] = tree_ok ? y[r] : __builtin_nanf("");
+      }
       // one node tile's operands at a time: hoisting the LDS reads of all
       // tiles above the loop would take most of the register file
       asm volatile("" ::: "memory");
     }
-    __syncthreads();  // M is consumed: its space takes the y staging
-    // lane (c + 16 k) holds nodes 16 ti + 4 k + r of channel row
-#pragma unroll
-    for (int ti = 0; ti < TT; ++ti)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        s_ys[(16 * ti + 4 * k + r) * kYsStride + row] = tree_ok ? yt[ti][r] : __builtin_nanf("");
-    __syncthreads();
-    for (int i = opaque_tid(); i < T * (kTtRows / 4); i += kTtThreads) {
-      const int v = i / (kTtRows / 4), q = i % (kTtRows / 4);
-      *reinterpret_cast<f32x4*>(a.y + (unit * T + v) * DI + c0 + 4 * q) =
-          *reinterpret_cast<const f32x4*>(s_ys + v * kYsStride + 4 * q);
-    }
-    __syncthreads();  // the staging space takes the next block's x rows
   }
 }
 
@@ -626,7 +668,7 @@ namespace {
 
 template <typename TIn, int NG, int TT>
 int launch_tt_t(const VerifyArgs& a, hipStream_t s) {
-  const size_t lds = (size_t)TtLds(16 * NG, (int)sizeof(TIn)).total;
+  const size_t lds = (size_t)TtLds(16 * NG, (int)sizeof(TIn), TT).total;
   if (lds > 160 * 1024) return SSM_TREE_E_DIMS;  // (fp32 inputs with d_state 256) the caller falls back
   if (allow_lds(verify_tt_kernel<TIn, NG, TT>, lds) != hipSuccess) return SSM_TREE_E_HIP;
   const int blocks = a.d.d_in / a.d.G / kTtRows;  // 64-channel blocks per B/C group
