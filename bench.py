@@ -31,9 +31,30 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "verified tree-node-layers/sec (Mamba2-2.7B SSM, 16-node tree); % HBM peak"
-KERNEL_SOURCES = {"verify": "mamba2_tree_verification_amd/csrc/verify_mfma.hip",
-                  "commit": "mamba2_tree_verification_amd/csrc/commit.hip",
-                  "commit_verify": "mamba2_tree_verification_amd/csrc/commit_verify.hip"}
+CSRC = "mamba2_tree_verification_amd/csrc/"
+KERNELS = ("verify", "commit", "commit_verify")
+
+
+def verify_source(cfg):
+    """The verify kernel a workload's shape dispatches to (plain flags)."""
+    if cfg.T <= 16 and cfg.P % 16 == 0:
+        return CSRC + "verify_mfma.hip"
+    if cfg.T <= 64 and cfg.P % 16 == 0 and (cfg.d_in // cfg.G) % 64 == 0:
+        return CSRC + "verify_tt.hip"
+    return CSRC + "verify.hip"
+
+
+def kernel_sources(kernel, cfg):
+    """Source files whose change invalidates a recorded traffic figure."""
+    if kernel == "verify":
+        files = [verify_source(cfg)]
+    elif kernel == "commit":
+        files = [CSRC + "commit.hip"]
+    elif cfg.T <= 16 and cfg.P % 16 == 0:
+        files = [CSRC + "commit_verify.hip"]
+    else:  # the round runs as a commit followed by a verify
+        files = [CSRC + "commit.hip", verify_source(cfg)]
+    return files + [CSRC + "common.h"]
 
 
 def algorithmic_bytes(cfg, path_len):
@@ -68,24 +89,24 @@ def source_sha(paths):
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel):
-    """HBM bytes per launch measured with rocprofv3 counters, if recorded for
-    the current kernel source (see profiles/)."""
+def load_traffic(kernel, cfg):
+    """HBM bytes per launch measured with rocprofv3 counters on this
+    workload, if recorded for the current kernel source (see profiles/)."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     try:
         with open(path) as f:
-            rec = json.load(f).get(kernel)
+            rec = json.load(f).get("workloads", {}).get(cfg.name, {}).get(kernel)
     except (OSError, ValueError):
         return None
-    if not rec or rec.get("source_sha") != source_sha([KERNEL_SOURCES[kernel], "mamba2_tree_verification_amd/csrc/common.h"]):
+    if not rec or rec.get("source_sha") != source_sha(kernel_sources(kernel, cfg)):
         return None
     return rec.get("bytes_per_launch")
 
 
 PROBE_BYTES = 4 << 30  # the plain copy of hbm_probe: reads and writes this many bytes per dispatch
-KERNEL_MATCH = {"verify": ("verify_mfma_kernel", "verify_proj_kernel"), "commit": ("::commit_kernel",),
+KERNEL_MATCH = {"verify": ("verify_mfma_kernel", "verify_tt_kernel", "verify_proj_kernel"), "commit": ("::commit_kernel",),
                 "commit_verify": ("commit_verify_kernel",), "copy": ("copyBuffer",)}
 
 
@@ -109,24 +130,36 @@ def _pmc_per_dispatch(run_dir, counter):
     return {fam: sum(v) / len(v) for fam, v in acc.items()}
 
 
-def record_traffic(prof_dir):
-    """Write profiles/traffic.json from four rocprofv3 --pmc runs under
-    prof_dir: fetch/ and write/ (FETCH_SIZE, WRITE_SIZE of this bench),
-    copy_fetch/ and copy_write/ (the same counters over `bench.py --probe`).
-    Each counter is scaled by bytes-moved / counter-reading of the plain
-    4 GiB device copy, so traffic is in bytes per launch."""
+def record_traffic(prof_dir, cfg):
+    """Add this workload's entry to profiles/traffic.json from four
+    rocprofv3 --pmc runs under prof_dir: fetch/ and write/ (FETCH_SIZE,
+    WRITE_SIZE of this bench on the workload), copy_fetch/ and copy_write/
+    (the same counters over `bench.py --probe`).  Each counter is scaled by
+    bytes-moved / counter-reading of the plain 4 GiB device copy, so traffic
+    is in bytes per launch.  A kernel the workload runs as several launches
+    (the round of a tree too deep for the fused kernel) is not recorded."""
     fetch = _pmc_per_dispatch(os.path.join(prof_dir, "fetch"), "FETCH_SIZE")
     write = _pmc_per_dispatch(os.path.join(prof_dir, "write"), "WRITE_SIZE")
     cf = _pmc_per_dispatch(os.path.join(prof_dir, "copy_fetch"), "FETCH_SIZE")["copy"]
     cw = _pmc_per_dispatch(os.path.join(prof_dir, "copy_write"), "WRITE_SIZE")["copy"]
     sf, sw = PROBE_BYTES / (cf * 1024), PROBE_BYTES / (cw * 1024)
-    out = {"scale": {"fetch": round(sf, 4), "write": round(sw, 4), "copy_bytes": PROBE_BYTES,
-                     "copy_fetch_kib": cf, "copy_write_kib": cw}}
-    for k in KERNEL_SOURCES:
-        out[k] = {"fetch_kib": fetch[k], "write_kib": write[k],
-                  "bytes_per_launch": int(round(fetch[k] * 1024 * sf + write[k] * 1024 * sw)),
-                  "source_sha": source_sha([KERNEL_SOURCES[k], "mamba2_tree_verification_amd/csrc/common.h"])}
     path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            out = json.load(f)
+    except (OSError, ValueError):
+        out = {}
+    out.setdefault("workloads", {})
+    out = {"scale": {"fetch": round(sf, 4), "write": round(sw, 4), "copy_bytes": PROBE_BYTES,
+                     "copy_fetch_kib": cf, "copy_write_kib": cw}, "workloads": out["workloads"]}
+    ent = {}
+    for k in KERNELS:
+        if k not in fetch or k not in write:
+            continue
+        ent[k] = {"fetch_kib": fetch[k], "write_kib": write[k],
+                  "bytes_per_launch": int(round(fetch[k] * 1024 * sf + write[k] * 1024 * sw)),
+                  "source_sha": source_sha(kernel_sources(k, cfg))}
+    out["workloads"][cfg.name] = ent
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
         f.write("\n")
@@ -372,7 +405,8 @@ def main(argv=None):
     args = ap.parse_args(argv)
 
     if args.record_traffic:
-        return record_traffic(args.record_traffic)
+        from testgen import configs as C
+        return record_traffic(args.record_traffic, C.CONFIGS[args.config])
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (the verify and commit "
               "kernels shard by sequence or head with no exchange; see the design notes). Run with --gpus 1.",
@@ -480,20 +514,28 @@ def main(argv=None):
 
     def roof(kernel, nbytes, ms):
         ach = nbytes / (ms * 1e-3) / 1e9
-        tr = load_traffic(kernel)
+        tr = load_traffic(kernel, cfg)
         return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": tr}
 
     # verify's arithmetic: C . h0 is 2 T flops per root-state element (the
-    # path terms are O(T^2) per channel and left out); on the matrix cores for
-    # trees of at most 64 nodes with headdim % 16 == 0 (and 64-channel blocks
-    # per B/C group), else on the vector ALU without packed fp32
+    # path terms are O(T^2) per channel and left out).  Trees of at most 16
+    # nodes: fp32 matrix-core products (157.3 TFLOP/s); 17-64 nodes with bf16
+    # inputs: bf16 products against the state split into three bf16 terms,
+    # counted as executed (3 x, nodes padded to 16-node tiles) against the
+    # bf16 peak (2500 TFLOP/s); other shapes: vector ALU without packed fp32
     # (78.6 TFLOP/s = 256 CUs x 64 FMA lanes x 2 x 2.4 GHz)
-    on_mfma = 1 <= cfg.T <= 64 and cfg.P % 16 == 0 and (cfg.d_in // cfg.G) % 64 == 0
+    vsrc = os.path.basename(verify_source(cfg))
     vflops = 2 * cfg.L * cfg.Bsz * cfg.T * cfg.H * cfg.P * cfg.N
-    vpeak = 157.3 if on_mfma else 78.6
-    vach = vflops / (avg(ver_ms) * 1e-3) / 1e12
-    vcompute = {"engine": "mfma fp32" if on_mfma else "valu fp32", "flops": vflops, "achieved": round(vach, 2),
+    if vsrc == "verify_tt.hip" and cfg.bf16:
+        engine, vpeak = "mfma bf16 (state split in 3 bf16 terms)", 2500.0
+        xflops = 3 * 2 * cfg.L * cfg.Bsz * (16 * ((cfg.T + 15) // 16)) * cfg.H * cfg.P * cfg.N
+    elif vsrc in ("verify_tt.hip", "verify_mfma.hip"):
+        engine, vpeak, xflops = "mfma fp32", 157.3, vflops
+    else:
+        engine, vpeak, xflops = "valu fp32", 78.6, vflops
+    vach = xflops / (avg(ver_ms) * 1e-3) / 1e12
+    vcompute = {"engine": engine, "flops": xflops, "achieved": round(vach, 2),
                 "peak": vpeak, "unit": "TFLOP/s", "frac": round(vach / vpeak, 4)}
 
     kern = {"commit_verify": dict(ms=round(avg(cv_ms), 4), ms_min=round(min(cv_ms), 4), bytes=cvb,
