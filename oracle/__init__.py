@@ -58,6 +58,8 @@ class Oracle:
         L.oracle_verify.argtypes = [p, p, p, p, p]
         L.oracle_commit.argtypes = [p, p, p, i32, p, p, p]
         L.oracle_scan.argtypes = [p, i32, p, p, p, p]
+        L.oracle_round_bf16.argtypes = [p, p, p, ctypes.c_int64]
+        L.oracle_round_bf16.restype = None
         for f in ("oracle_validate_tree", "oracle_validate_path", "oracle_plan", "oracle_verify",
                   "oracle_commit", "oracle_scan"):
             getattr(L, f).restype = ctypes.c_int
@@ -141,6 +143,16 @@ class Oracle:
                                     int(length), ctypes.byref(self._unit(u, keep)), so.ctypes.data,
                                     wo.ctypes.data if W > 1 else None)
         return so, wo, st
+
+    def round_bf16(self, x):
+        """Storage rounding of a committed state to bfloat16 (oracle.h):
+        (rounded values as float64, distance to the nearest rounding
+        boundary relative to |x|), both shaped like x."""
+        a = np.ascontiguousarray(x, dtype=np.float64)
+        out = np.empty_like(a)
+        gap = np.empty_like(a)
+        self.lib.oracle_round_bf16(a.ctypes.data, out.ctypes.data, gap.ctypes.data, a.size)
+        return out, gap
 
     def scan(self, u: dict, S, H, P, N, G, W, silu=False, xbc=False):
         """Plain sequential scan of S tokens: (y [S][H*P], state_out, window_out [W-1][CH])."""

@@ -403,3 +403,42 @@ int oracle_scan(const oracle_dims* d, int32_t S, const oracle_unit* u, double* y
   free(seq);
   return ORACLE_OK;
 }
+
+/* One value to the bfloat16 grid (see oracle.h).  The grid spacing of x's
+ * binade is q = 2^(e - 8) for |x| in [2^(e-1), 2^e) with e - 1 >= -126, and
+ * 2^-133 below; x / q is exact in float64, and its integer part k and
+ * fraction decide the rounding. */
+static double round_bf16_one(double x, double* gap) {
+  if (x == 0.0 || isnan(x) || isinf(x)) {
+    if (gap) *gap = INFINITY;
+    return x;
+  }
+  const double a = fabs(x);
+  int e;
+  frexp(a, &e); /* a = m 2^e, m in [0.5, 1) */
+  const int qe = (e - 1 >= -126) ? e - 8 : -133;
+  const double q = ldexp(1.0, qe);
+  const double r = a / q;
+  const double k = floor(r), f = r - k;
+  double kr;
+  if (f > 0.5)
+    kr = k + 1.0;
+  else if (f < 0.5)
+    kr = k;
+  else /* a tie: the even significand (k even) */
+    kr = (MUT(18) ? 1.0 : (fmod(k, 2.0) == 0.0 ? 0.0 : 1.0)) + k;
+  double v = kr * q;
+  if (v > 255.0 * ldexp(1.0, 120)) v = INFINITY;
+  if (gap) {
+    /* the nearest boundary is k + 1/2, or, at the bottom of a binade whose
+     * lower neighbour is twice as fine, the midpoint k - 1/4 below it */
+    double g = fabs(f - 0.5);
+    if (k == 128.0 && e - 1 > -126 && f + 0.25 < g) g = f + 0.25;
+    *gap = g * q / a;
+  }
+  return x < 0 ? -v : v;
+}
+
+void oracle_round_bf16(const double* x, double* out, double* gap, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = round_bf16_one(x[i], gap ? gap + i : NULL);
+}

@@ -78,6 +78,17 @@ int oracle_commit(const oracle_dims* d, const int32_t* parent, const int32_t* pa
 int oracle_scan(const oracle_dims* d, int32_t S, const oracle_unit* u, double* y, double* state_out,
                 double* window_out);
 
+/* Storage of a committed root state in bfloat16 ([SM] names mixed precision
+ * among its memory optimisations; the format is a reading).  Each value is
+ * rounded to the bfloat16 grid: 8 significant bits, float32's exponent
+ * range with its subnormals (spacing 2^-133 below 2^-126), nearest value,
+ * ties to the even significand, infinite beyond the largest finite value
+ * (255 * 2^120); zeros, infinities and NaNs pass through.  gap (may be
+ * NULL) receives, per value, the distance from x to the nearest rounding
+ * boundary (a midpoint between grid values) divided by |x|, or +inf where
+ * there is none (zero, inf, NaN). */
+void oracle_round_bf16(const double* x, double* out, double* gap, int64_t n);
+
 #ifdef __cplusplus
 }
 #endif

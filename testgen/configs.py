@@ -55,6 +55,7 @@ class Config:
     conv_bias: bool = False
     xbc: bool = False
     gate: bool = False
+    state_bf16: bool = False  # root state stored as bfloat16 (drawn, then rounded like the inputs)
 
     @property
     def d_in(self) -> int:
@@ -277,7 +278,7 @@ class Inputs:
     C: np.ndarray          # [L][Bsz][T][G][N]
     dt_raw: np.ndarray     # [L][Bsz][T][H]
     window: np.ndarray     # [L][Bsz][W-1][d_in]
-    state: np.ndarray      # [L][Bsz][H][P][N] float32
+    state: np.ndarray      # [L][Bsz][H][P][N] float32 (uint16 bf16 bits with state_bf16)
     A: np.ndarray          # [L][H] float32
     D: np.ndarray
     dt_bias: np.ndarray
@@ -313,10 +314,15 @@ def _specs(cfg: Config) -> dict:
     )
 
 
+def stored_bf16(cfg: Config, name: str) -> bool:
+    """Whether tensor `name` is stored as bfloat16 bits."""
+    return (_specs(cfg)[name][4] and cfg.bf16) or (name == "state" and cfg.state_bf16)
+
+
 def draw(cfg: Config, name: str, shape=None, offset: int = 0, nthreads=None) -> np.ndarray:
     stream, dist, a, b, is_in = _specs(cfg)[name]
     shp = tensor_shapes(cfg)[name] if shape is None else shape
-    return fill(shp, cfg.seed, stream, dist, a, b, bf16=(is_in and cfg.bf16), offset=offset, nthreads=nthreads)
+    return fill(shp, cfg.seed, stream, dist, a, b, bf16=stored_bf16(cfg, name), offset=offset, nthreads=nthreads)
 
 
 def make_inputs(cfg: Config, nthreads=None, skip=()) -> Inputs:
@@ -355,7 +361,6 @@ def unit_f64(cfg: Config, l: int, b: int, inputs: Inputs | None = None) -> dict:
     for k in shp:
         if (k == "conv_b" and not cfg.conv_bias) or (k == "z" and not cfg.gate):
             continue
-        is_in = _specs(cfg)[k][4]
         if inputs is not None:
             full = getattr(inputs, k)
             if k in ("A", "D", "dt_bias", "conv_w", "conv_b"):
@@ -364,5 +369,5 @@ def unit_f64(cfg: Config, l: int, b: int, inputs: Inputs | None = None) -> dict:
                 arr = full[l, b]
         else:
             arr = draw(cfg, k, shape=shp[k], offset=offs[k], nthreads=1)
-        out[k] = as_f64(arr, is_in and cfg.bf16).reshape(shp[k])
+        out[k] = as_f64(arr, stored_bf16(cfg, k)).reshape(shp[k])
     return out

@@ -29,6 +29,7 @@ def upload(inp, device="cuda") -> SimpleNamespace:
     ns.path_len = torch.from_numpy(np.ascontiguousarray(inp.path_len, np.int32)).to(device)
     for k in ("x", "B", "C", "dt_raw", "window", "z"):
         setattr(ns, k, tensor(getattr(inp, k), bf, device))
-    for k in ("state", "A", "D", "dt_bias", "conv_w", "conv_b"):
+    ns.state = tensor(inp.state, bool(getattr(cfg, "state_bf16", False)), device)
+    for k in ("A", "D", "dt_bias", "conv_w", "conv_b"):
         setattr(ns, k, tensor(getattr(inp, k), False, device))
     return ns

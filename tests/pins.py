@@ -522,6 +522,53 @@ def pin_option_special_cases(o, seed=8):
     close(y_g, 40.0 * y_n, 1e-15, "gate with z = 40")
 
 
+def pin_round_bf16(o, seed=10):
+    """bf16 storage rounding of a committed state against its definition:
+    bf16 values stay put; exact ties go to the even significand (worked
+    values in a normal binade, in the subnormal range and at the overflow
+    edge); any other value goes to the nearer of its bf16 neighbours,
+    enumerated from float32 bit patterns; the reported gap is the distance
+    to the nearest midpoint between neighbours."""
+    rng = np.random.default_rng(seed)
+    bits = rng.integers(0, 1 << 16, 4000).astype(np.uint32)
+    vals = (bits << 16).view(np.float32).astype(np.float64)
+    vals = vals[np.isfinite(vals)]
+    r, _ = o.round_bf16(vals)
+    assert np.array_equal(r, vals), "a bf16 value moved"
+    sub, top = 2.0 ** -133, 255.0 * 2.0 ** 120
+    worked = [(1 + 2 ** -8, 1.0), (1 + 3 * 2 ** -8, 1 + 2 ** -6), (-(1 + 2 ** -8), -1.0),
+              (1 + 2 ** -8 + 2 ** -30, 1 + 2 ** -7), (1 + 2 ** -8 - 2 ** -30, 1.0),
+              (0.75 + 2 ** -10, 0.75), (0.75 + 3 * 2 ** -10, 0.75 + 2 ** -8),
+              (0.5 * sub, 0.0), (1.5 * sub, 2 * sub), (2.5 * sub, 2 * sub), (-3.5 * sub, -4 * sub),
+              (2.0 ** 127 * (1 + 2 ** -8), 2.0 ** 127), (top + 2.0 ** 119, np.inf),
+              (top + 2.0 ** 119 - 2.0 ** 100, top), (-(top + 2.0 ** 119), -np.inf), (1e39, np.inf)]
+    xs = np.array([w[0] for w in worked])
+    r, _ = o.round_bf16(xs)
+    for (x, want), got in zip(worked, r):
+        assert got == want, "round_bf16(%r) = %r, want %r" % (x, got, want)
+    # random magnitudes across the float32 range, both signs
+    n = 20000
+    x = np.ldexp(1.0 + rng.random(n), rng.integers(-140, 127, n)) * rng.choice([-1.0, 1.0], n)
+    r, gap = o.round_bf16(x)
+    f32 = x.astype(np.float32)
+    hi16 = (f32.view(np.uint32) >> 16).astype(np.int64)
+    cand = np.stack([hi16 + k for k in (-1, 0, 1, 2)], axis=1)
+    cval = ((cand.astype(np.uint32) & 0xFFFF) << 16).view(np.float32).astype(np.float64)
+    dist = np.abs(cval - x[:, None])
+    dist[~np.isfinite(cval)] = np.inf  # patterns next to zero or infinity that are not values
+    best = dist.min(axis=1)
+    on_tie = (dist == best[:, None]).sum(axis=1) > 1
+    pick = cval[np.arange(n), dist.argmin(axis=1)]
+    even = cval[np.arange(n), np.argmax((dist == best[:, None]) & (cand % 2 == 0), axis=1)]
+    want = np.where(on_tie, even, pick)
+    assert np.array_equal(r, want), "not the nearest bf16 value"
+    srt = np.sort(np.where(np.isfinite(cval), cval, np.nan), axis=1)
+    mids = 0.5 * (srt[:, 1:] + srt[:, :-1])
+    gap_want = np.nanmin(np.abs(mids - x[:, None]), axis=1) / np.abs(x)
+    close(gap, gap_want, 1e-12, "distance to the nearest rounding boundary")
+
+
 ALL_PINS = [pin_chain_is_scan, pin_every_node_is_its_path_scan, pin_bruteforce_forests, pin_closed_form,
             pin_softplus_library, pin_lfilter, pin_special_cases, pin_commit, pin_sibling_relabel,
-            pin_validator, pin_plan, pin_peak_from_verify, pin_golden, pin_option_special_cases]
+            pin_validator, pin_plan, pin_peak_from_verify, pin_golden, pin_option_special_cases,
+            pin_round_bf16]

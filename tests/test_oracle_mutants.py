@@ -25,10 +25,11 @@ MUTANTS = {
     15: "xbc: B channels convolved with the C channels' weights",
     16: "gate multiplies by sigmoid(z) instead of silu(z)",
     17: "xbc: commit shifts only x, not B and C, into the window",
+    18: "bf16 state storage rounds ties up instead of to even",
 }
 
 FAST_PINS = [pins.pin_chain_is_scan, pins.pin_closed_form, pins.pin_softplus_library, pins.pin_commit,
-             pins.pin_validator, functools.partial(pins.pin_bruteforce_forests, tmax=5)]
+             pins.pin_validator, functools.partial(pins.pin_bruteforce_forests, tmax=5), pins.pin_round_bf16]
 
 
 @pytest.mark.parametrize("k", sorted(MUTANTS), ids=lambda k: "m%d" % k)

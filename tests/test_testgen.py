@@ -97,3 +97,17 @@ def test_stress_trees():
         assert _is_bfs_labelling(p)
         assert C.depths(p).max() <= 8
         assert np.bincount(p[p >= 0]).max() <= 4
+
+
+def test_state_bf16_is_stored_as_bf16_bits():
+    """With state_bf16 the root state is drawn like the fp32 state and kept
+    as bfloat16 bits; the oracle's float64 view of it is exact."""
+    cfg = C.Config(95, "tiny", 1, 2, 3, 2, 16, 16, 1, 4, True, 0.5, "forest", state_bf16=True)
+    inp = C.make_inputs(cfg)
+    assert inp.state.dtype == np.uint16 and inp.state.shape == (1, 2, 2, 16, 16)
+    u = C.unit_f64(cfg, 0, 1, inp)
+    as32 = u["state"].astype(np.float32)
+    assert np.array_equal(as32.astype(np.float64), u["state"])
+    assert not (as32.view(np.uint32) & 0xFFFF).any(), "not on the bf16 grid"
+    f32 = C.make_inputs(cfg.replace(state_bf16=False)).state
+    assert np.abs(u["state"] - f32[0, 1]).max() <= 2.0 ** -8 * np.abs(f32[0, 1]).max()
