@@ -365,6 +365,44 @@ def options_round(torch, m, C, cfg, g, g2, state, timed, threads, path_lens):
             "node_layers_per_s": round(cfg.L * cfg.Bsz * cfg.T / (avg * 1e-3), 1), "note": "not in the step"}
 
 
+def state_bf16_round(torch, m, cfg, g, g2, state, window, timed, path_lens):
+    """The same decode round with the root state stored as bfloat16
+    (SSM_TREE_STATE_BF16): the bench's state rounded to bf16, committed and
+    verified in place.  Not part of the step; reported apart."""
+    sb = state.to(torch.bfloat16)
+    win = None if window is None else window.clone()
+    dims = m.make_dims(cfg.L, cfg.Bsz, cfg.T, cfg.H, cfg.P, cfg.N, cfg.G, cfg.W, cfg.bf16, cfg.silu,
+                       state_bf16=True)
+    prm = m.make_params(g.A, g.D, g.dt_bias, g.conv_w, g.conv_b)
+    y = torch.empty((cfg.L, cfg.Bsz, cfg.T, cfg.d_in), dtype=torch.float32, device="cuda")
+    cst = torch.empty((cfg.Bsz,), dtype=torch.int32, device="cuda")
+    vst = torch.empty_like(cst)
+    trees = (g, g2)
+    k = [0]
+
+    def step():
+        prev, nxt = trees[k[0] % 2], trees[(k[0] + 1) % 2]
+        m.commit_verify(dims, prm, prev.parent, prev.path, prev.path_len, prev.x, prev.B, prev.dt_raw, win, sb,
+                        win, sb, nxt.parent, nxt.x, nxt.B, nxt.C, nxt.dt_raw, y, cst, vst)
+        k[0] += 1
+
+    try:
+        ms = timed(step, reps=9)
+    except m.SsmTreeError as e:  # shapes no kernel takes with a bf16 state
+        return {"skipped": str(e)}
+    torch.cuda.synchronize()
+    if not (cst.cpu() == 0).all() or not (vst.cpu() == 0).all() or torch.isnan(y).any():
+        raise SystemExit("bench: the bf16-state round produced a bad status or NaN")
+    # the root state is read and written once per round, 2 bytes per element instead of 4
+    saved = cfg.L * cfg.Bsz * 2 * (cfg.H * cfg.P * cfg.N * 2)
+    nbytes = sum(algorithmic_bytes(cfg, pl)["commit_verify"] for pl in path_lens) // len(path_lens) - saved
+    avg = sum(ms) / len(ms)
+    ach = nbytes / (avg * 1e-3) / 1e9
+    return {"state": "bf16 (rounded to nearest even on store)", "ms": round(avg, 4), "ms_min": round(min(ms), 4),
+            "bytes": nbytes, "GBps": round(ach, 1), "frac": round(ach / HBM_PEAK_GBS, 4),
+            "node_layers_per_s": round(cfg.L * cfg.Bsz * cfg.T / (avg * 1e-3), 1), "note": "not in the step"}
+
+
 def hbm_probe(torch, nbytes=4 << 30, reps=10):
     """Plain device copy (torch copy_) and read (torch sum) bandwidth over
     buffers far larger than the 256 MB last-level cache."""
@@ -496,8 +534,9 @@ def main(argv=None):
     fifo_ms = timed(lambda: m.verify(dims_fifo, prm, g.parent, g.x, g.B, g.C, g.dt_raw, window, state, y, st_v),
                     reps=3)
 
-    per_layer = draft = opts = None
+    per_layer = draft = opts = sbf = None
     if not args.no_extras:
+        sbf = state_bf16_round(torch, m, cfg, g, g2, state, window, timed, (inp.path_len, inp2.path_len))
         per_layer = per_layer_round(torch, m, cfg, g, g2, state, window, y, st_c, st_v, timed)
         draft = draft_decode(torch, m, C, upload, args.threads, timed)
         if 1 <= cfg.T <= 16 and cfg.P % 16 == 0:  # the shapes the options run on
@@ -573,6 +612,7 @@ def main(argv=None):
         "per_layer": per_layer,
         "draft_decode": draft,
         "options_round": opts,
+        "state_bf16_round": sbf,
         "param_bytes_per_call": ab["params"],
         "verify_hbm_frac": kern["verify"]["roofline"]["frac"],
     }

@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define SSM_TREE_ABI_VERSION 2
+#define SSM_TREE_ABI_VERSION 3
 
 /* input element types for x, B, C, dt_raw and the conv window */
 #define SSM_TREE_F32 0
@@ -78,6 +78,19 @@ extern "C" {
  * of the default root projection.  Same outputs up to fp32 rounding; slower.
  * Ignored by ssm_tree_commit. */
 #define SSM_TREE_VERIFY_FIFO 2
+/* The root state (state, state_in, state_out) is stored as bfloat16 instead
+ * of float32, halving its bytes, which dominate the traffic (SpecMamba page
+ * sec. 3.1 lists mixed precision among its memory optimisations; the
+ * format is a reading).  Arithmetic stays float32; a committed state is
+ * rounded to the nearest bfloat16, ties to even, when stored, and the
+ * fused round verifies the next tree from that stored value.  Supported by
+ * ssm_tree_commit for every shape; by ssm_tree_verify for trees of 1 to 64
+ * nodes with a headdim that is a multiple of 16 (and, past 16 nodes,
+ * (H*P/G) a multiple of 64; not fp32 inputs with d_state 256 past 16
+ * nodes); by ssm_tree_commit_verify where both its calls are; never with
+ * SSM_TREE_VERIFY_FIFO, SSM_TREE_CONV_XBC or the gate.  Other combinations
+ * return SSM_TREE_E_DIMS before anything is enqueued. */
+#define SSM_TREE_STATE_BF16 8
 
 /* return / status codes */
 #define SSM_TREE_OK 0
@@ -104,7 +117,7 @@ typedef struct ssm_tree_dims {
   int32_t ngroups;    /* G : B and C are shared by H/G consecutive heads */
   int32_t conv_width; /* W */
   int32_t in_dtype;   /* SSM_TREE_F32 or SSM_TREE_BF16 */
-  int32_t flags;      /* 0 or SSM_TREE_CONV_SILU | SSM_TREE_VERIFY_FIFO | SSM_TREE_CONV_XBC */
+  int32_t flags;      /* 0 or SSM_TREE_CONV_SILU | SSM_TREE_VERIFY_FIFO | SSM_TREE_CONV_XBC | SSM_TREE_STATE_BF16 */
 } ssm_tree_dims;
 
 /* Per-layer parameters, float32 device pointers. */
@@ -134,7 +147,8 @@ typedef struct ssm_tree_params {
  * conv_window [L][Bsz][W-1][CH]  in_dtype   raw conv inputs (x, and B and C
  *             with SSM_TREE_CONV_XBC) of the last W-1 committed tokens,
  *             oldest row first (may be NULL when W == 1)
- * state       [L][Bsz][H][P][N]  float32    root SSM state (read only)
+ * state       [L][Bsz][H][P][N]  float32, or bfloat16 with SSM_TREE_STATE_BF16:
+ *             root SSM state (read only)
  * y           [L][Bsz][T][H][P]  float32    out; must not overlap any input
  * seq_status  [Bsz] int32 out, or NULL.  SSM_TREE_OK or SSM_TREE_E_TREE;
  *             a sequence with an invalid tree gets NaN in all its y.
@@ -143,7 +157,7 @@ typedef struct ssm_tree_params {
  */
 int ssm_tree_verify(const ssm_tree_dims* dims, const ssm_tree_params* params, const int32_t* parent,
                     const void* x, const void* B, const void* C, const void* dt_raw, const void* z,
-                    const void* conv_window, const float* state, float* y, int32_t* seq_status, void* hip_stream);
+                    const void* conv_window, const void* state, float* y, int32_t* seq_status, void* hip_stream);
 
 /*
  * ssm_tree_commit: advance the root state and conv window along the
@@ -159,7 +173,8 @@ int ssm_tree_verify(const ssm_tree_dims* dims, const ssm_tree_params* params, co
  * conv_window_out [L][Bsz][W-1][CH] in_dtype: last W-1 rows of
  *             (old window, raw conv inputs of each path node), copied bit
  *             for bit
- * state_out   [L][Bsz][H][P][N] float32: state of the last path node
+ * state_out   [L][Bsz][H][P][N] float32 (bfloat16 with SSM_TREE_STATE_BF16,
+ *             rounded to nearest even): state of the last path node
  * Outputs may equal the matching input exactly (in place); any other
  * overlap is SSM_TREE_E_ALIAS.
  * seq_status  [Bsz] or NULL: SSM_TREE_OK, SSM_TREE_E_TREE or SSM_TREE_E_PATH;
@@ -167,8 +182,8 @@ int ssm_tree_verify(const ssm_tree_dims* dims, const ssm_tree_params* params, co
  */
 int ssm_tree_commit(const ssm_tree_dims* dims, const ssm_tree_params* params, const int32_t* parent,
                     const int32_t* path, const int32_t* path_len, const void* x, const void* B, const void* C,
-                    const void* dt_raw, const void* conv_window_in, const float* state_in, void* conv_window_out,
-                    float* state_out, int32_t* seq_status, void* hip_stream);
+                    const void* dt_raw, const void* conv_window_in, const void* state_in, void* conv_window_out,
+                    void* state_out, int32_t* seq_status, void* hip_stream);
 
 /*
  * ssm_tree_commit_verify: ssm_tree_commit of the previous tree's accepted
@@ -200,7 +215,7 @@ int ssm_tree_commit(const ssm_tree_dims* dims, const ssm_tree_params* params, co
 int ssm_tree_commit_verify(const ssm_tree_dims* dims, const ssm_tree_params* params, const int32_t* parent_prev,
                            const int32_t* path, const int32_t* path_len, const void* x_prev, const void* B_prev,
                            const void* C_prev, const void* dt_raw_prev, const void* conv_window_in,
-                           const float* state_in, void* conv_window_out, float* state_out, const int32_t* parent,
+                           const void* state_in, void* conv_window_out, void* state_out, const int32_t* parent,
                            const void* x, const void* B, const void* C, const void* dt_raw, const void* z,
                            float* y, int32_t* commit_status, int32_t* verify_status, void* hip_stream);
 

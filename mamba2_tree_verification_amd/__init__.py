@@ -18,11 +18,12 @@ import threading
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libssm_tree.so")
 
-SSM_TREE_ABI_VERSION = 2
+SSM_TREE_ABI_VERSION = 3
 SSM_TREE_F32, SSM_TREE_BF16 = 0, 1
 SSM_TREE_CONV_SILU = 1
 SSM_TREE_VERIFY_FIFO = 2
 SSM_TREE_CONV_XBC = 4
+SSM_TREE_STATE_BF16 = 8
 OK, E_NULL, E_ALIGN, E_DIMS, E_DTYPE, E_ALIAS, E_HIP, E_FLAGS = 0, -1, -2, -3, -4, -5, -6, -7
 E_TREE, E_PATH = -10, -11
 PLAN_HEADER, PLAN_STRIDE, PLAN_UNUSED = 4, 8, -32768
@@ -134,10 +135,10 @@ def _stream(stream):
 
 
 def make_dims(L, Bsz, T, H, P, N, G, W, bf16: bool, silu: bool = False, fifo: bool = False,
-              xbc: bool = False) -> Dims:
+              xbc: bool = False, state_bf16: bool = False) -> Dims:
     return Dims(L, Bsz, T, H, P, N, G, W, SSM_TREE_BF16 if bf16 else SSM_TREE_F32,
                 (SSM_TREE_CONV_SILU if silu else 0) | (SSM_TREE_VERIFY_FIFO if fifo else 0) |
-                (SSM_TREE_CONV_XBC if xbc else 0))
+                (SSM_TREE_CONV_XBC if xbc else 0) | (SSM_TREE_STATE_BF16 if state_bf16 else 0))
 
 
 def make_params(A, D, dt_bias, conv_w, conv_b=None) -> Params:
@@ -154,16 +155,21 @@ def _check(t, kind):
         raise ValueError("tensor must be on the GPU")
     if not t.is_contiguous():
         raise ValueError("tensor must be contiguous")
-    want = {"float32": (torch.float32,), "int32": (torch.int32,), "in": (torch.float32, torch.bfloat16)}[kind]
+    want = {"float32": (torch.float32,), "int32": (torch.int32,), "in": (torch.float32, torch.bfloat16),
+            "state": (torch.float32,), "state_bf16": (torch.bfloat16,)}[kind]
     if t.dtype not in want:
         raise ValueError("unexpected dtype %s" % t.dtype)
+
+
+def _state_kind(dims: Dims) -> str:
+    return "state_bf16" if dims.flags & SSM_TREE_STATE_BF16 else "state"
 
 
 def verify(dims: Dims, params: Params, parent, x, B, C, dt_raw, conv_window, state, y, seq_status=None,
            stream=None, z=None):
     """ssm_tree_verify; z (optional) gates y by silu(z)."""
     for t, k in ((parent, "int32"), (x, "in"), (B, "in"), (C, "in"), (dt_raw, "in"), (z, "in"),
-                 (conv_window, "in"), (state, "float32"), (y, "float32"), (seq_status, "int32")):
+                 (conv_window, "in"), (state, _state_kind(dims)), (y, "float32"), (seq_status, "int32")):
         _check(t, k)
     rc = ssm_tree_verify(dims, params, _ptr(parent), _ptr(x), _ptr(B), _ptr(C), _ptr(dt_raw), _ptr(z),
                          _ptr(conv_window), _ptr(state), _ptr(y), _ptr(seq_status), _stream(stream))
@@ -175,8 +181,8 @@ def commit(dims: Dims, params: Params, parent, path, path_len, x, B, dt_raw, con
            conv_window_out, state_out, seq_status=None, stream=None, C=None):
     """ssm_tree_commit; C (the raw C rows) is needed only with the xBC conv."""
     for t, k in ((parent, "int32"), (path, "int32"), (path_len, "int32"), (x, "in"), (B, "in"), (C, "in"),
-                 (dt_raw, "in"), (conv_window_in, "in"), (state_in, "float32"), (conv_window_out, "in"),
-                 (state_out, "float32"), (seq_status, "int32")):
+                 (dt_raw, "in"), (conv_window_in, "in"), (state_in, _state_kind(dims)), (conv_window_out, "in"),
+                 (state_out, _state_kind(dims)), (seq_status, "int32")):
         _check(t, k)
     rc = ssm_tree_commit(dims, params, _ptr(parent), _ptr(path), _ptr(path_len), _ptr(x), _ptr(B), _ptr(C),
                          _ptr(dt_raw), _ptr(conv_window_in), _ptr(state_in), _ptr(conv_window_out),
@@ -191,8 +197,8 @@ def commit_verify(dims: Dims, params: Params, parent_prev, path, path_len, x_pre
     """ssm_tree_commit_verify; C_prev is needed only with the xBC conv, z
     (optional) gates the next tree's y by silu(z)."""
     for t, k in ((parent_prev, "int32"), (path, "int32"), (path_len, "int32"), (x_prev, "in"), (B_prev, "in"),
-                 (C_prev, "in"), (dt_raw_prev, "in"), (conv_window_in, "in"), (state_in, "float32"),
-                 (conv_window_out, "in"), (state_out, "float32"), (parent, "int32"), (x, "in"), (B, "in"),
+                 (C_prev, "in"), (dt_raw_prev, "in"), (conv_window_in, "in"), (state_in, _state_kind(dims)),
+                 (conv_window_out, "in"), (state_out, _state_kind(dims)), (parent, "int32"), (x, "in"), (B, "in"),
                  (C, "in"), (dt_raw, "in"), (z, "in"), (y, "float32"), (commit_status, "int32"),
                  (verify_status, "int32")):
         _check(t, k)

@@ -9,7 +9,8 @@ namespace ssmt {
 int launch_verify(const VerifyArgs& a, bool bf16, hipStream_t s);  // status code
 hipError_t launch_commit(const CommitArgs& a, bool bf16, hipStream_t s);
 bool commit_verify_fused_applies(const Dims& d);
-bool verify_options_supported(const Dims& d, bool gate);  // SSM_TREE_CONV_XBC and the gate
+// SSM_TREE_CONV_XBC, the gate and SSM_TREE_STATE_BF16
+bool verify_options_supported(const Dims& d, bool gate, bool bf16);
 bool commit_options_supported(const Dims& d);
 bool commit_verify_options_supported(const Dims& d, bool gate);
 int launch_commit_verify(const CommitVerifyArgs& a, bool bf16, hipStream_t s);
@@ -38,7 +39,8 @@ int check_dims(const ssm_tree_dims* dm, Dims* out) {
   if (!dm) return SSM_TREE_E_NULL;
   const ssm_tree_dims& d = *dm;
   if (d.in_dtype != SSM_TREE_F32 && d.in_dtype != SSM_TREE_BF16) return SSM_TREE_E_DTYPE;
-  if (d.flags & ~(SSM_TREE_CONV_SILU | SSM_TREE_VERIFY_FIFO | SSM_TREE_CONV_XBC)) return SSM_TREE_E_FLAGS;
+  if (d.flags & ~(SSM_TREE_CONV_SILU | SSM_TREE_VERIFY_FIFO | SSM_TREE_CONV_XBC | SSM_TREE_STATE_BF16))
+    return SSM_TREE_E_FLAGS;
   if (d.n_layers < 0 || d.batch < 0 || d.n_nodes < 0 || d.n_nodes > kMaxNodes) return SSM_TREE_E_DIMS;
   if (d.nheads < 1 || d.headdim < 1 || d.ngroups < 1 || d.nheads % d.ngroups) return SSM_TREE_E_DIMS;
   if (d.conv_width < 1 || d.conv_width > 4) return SSM_TREE_E_DIMS;
@@ -51,7 +53,8 @@ int check_dims(const ssm_tree_dims* dm, Dims* out) {
   const int xbc = (d.flags & SSM_TREE_CONV_XBC) ? 1 : 0;
   *out = Dims{d.n_layers, d.batch, d.n_nodes, d.nheads, d.headdim, d.d_state, d.ngroups, d.conv_width,
               (d.flags & SSM_TREE_CONV_SILU) ? 1 : 0, (int32_t)di, (d.flags & SSM_TREE_VERIFY_FIFO) ? 1 : 0, xbc,
-              (int32_t)(di + (xbc ? 2 * (int64_t)d.ngroups * d.d_state : 0))};
+              (int32_t)(di + (xbc ? 2 * (int64_t)d.ngroups * d.d_state : 0)),
+              (d.flags & SSM_TREE_STATE_BF16) ? 1 : 0};
   return SSM_TREE_OK;
 }
 
@@ -87,7 +90,7 @@ const char* ssm_tree_status_string(int status) {
 
 int ssm_tree_verify(const ssm_tree_dims* dims, const ssm_tree_params* params, const int32_t* parent,
                     const void* x, const void* B, const void* C, const void* dt_raw, const void* z,
-                    const void* conv_window, const float* state, float* y, int32_t* seq_status, void* hip_stream) {
+                    const void* conv_window, const void* state, float* y, int32_t* seq_status, void* hip_stream) {
   Dims d;
   int st = check_dims(dims, &d);
   if (st) return st;
@@ -97,19 +100,19 @@ int ssm_tree_verify(const ssm_tree_dims* dims, const ssm_tree_params* params, co
     if (seq_status) return launch_status(seq_status, d.Bsz, SSM_TREE_OK, s) == hipSuccess ? SSM_TREE_OK : SSM_TREE_E_HIP;
     return SSM_TREE_OK;
   }
-  if (!verify_options_supported(d, z != nullptr)) return SSM_TREE_E_DIMS;
+  if (!verify_options_supported(d, z != nullptr, dims->in_dtype == SSM_TREE_BF16)) return SSM_TREE_E_DIMS;
   if ((st = check_params(params))) return st;
   if (!parent || !x || !B || !C || !dt_raw || !state || !y || (d.W > 1 && !conv_window)) return SSM_TREE_E_NULL;
   const void* ptrs[] = {parent, x, B, C, dt_raw, z, state, y, seq_status, d.W > 1 ? conv_window : nullptr};
   for (const void* p : ptrs)
     if (p && misaligned(p)) return SSM_TREE_E_ALIGN;
-  const int64_t e = dims->in_dtype == SSM_TREE_BF16 ? 2 : 4;
+  const int64_t e = dims->in_dtype == SSM_TREE_BF16 ? 2 : 4, es = d.sbf16 ? 2 : 4;
   const int64_t U = (int64_t)d.L * d.Bsz, T = d.T, DI = d.d_in, CH = d.CH;
   const Range ry = range_of(y, U * T * DI * 4);
   const Range ins[] = {range_of(parent, (int64_t)d.Bsz * T * 4), range_of(x, U * T * DI * e),
                        range_of(B, U * T * d.G * d.N * e), range_of(C, U * T * d.G * d.N * e),
                        range_of(dt_raw, U * T * d.H * e), range_of(z, z ? U * T * DI * e : 0),
-                       range_of(state, U * DI * d.N * 4),
+                       range_of(state, U * DI * d.N * es),
                        range_of(conv_window, d.W > 1 ? U * (d.W - 1) * CH * e : 0),
                        range_of(params->A, d.L * (int64_t)d.H * 4), range_of(params->D, d.L * (int64_t)d.H * 4),
                        range_of(params->dt_bias, d.L * (int64_t)d.H * 4),
@@ -166,8 +169,8 @@ int ssm_tree_verify(const ssm_tree_dims* dims, const ssm_tree_params* params, co
 
 int ssm_tree_commit(const ssm_tree_dims* dims, const ssm_tree_params* params, const int32_t* parent,
                     const int32_t* path, const int32_t* path_len, const void* x, const void* B, const void* C,
-                    const void* dt_raw, const void* conv_window_in, const float* state_in, void* conv_window_out,
-                    float* state_out, int32_t* seq_status, void* hip_stream) {
+                    const void* dt_raw, const void* conv_window_in, const void* state_in, void* conv_window_out,
+                    void* state_out, int32_t* seq_status, void* hip_stream) {
   Dims d;
   int st = check_dims(dims, &d);
   if (st) return st;
@@ -183,10 +186,10 @@ int ssm_tree_commit(const ssm_tree_dims* dims, const ssm_tree_params* params, co
                         d.W > 1 ? conv_window_in : nullptr, d.W > 1 ? conv_window_out : nullptr};
   for (const void* p : ptrs)
     if (p && misaligned(p)) return SSM_TREE_E_ALIGN;
-  const int64_t e = dims->in_dtype == SSM_TREE_BF16 ? 2 : 4;
+  const int64_t e = dims->in_dtype == SSM_TREE_BF16 ? 2 : 4, es = d.sbf16 ? 2 : 4;
   const int64_t U = (int64_t)d.L * d.Bsz, T = d.T, DI = d.d_in, CH = d.CH;
   const int64_t wbytes = d.W > 1 ? U * (d.W - 1) * CH * e : 0;
-  const Range rso = range_of(state_out, U * DI * d.N * 4), rsi = range_of(state_in, U * DI * d.N * 4);
+  const Range rso = range_of(state_out, U * DI * d.N * es), rsi = range_of(state_in, U * DI * d.N * es);
   const Range rwo = range_of(conv_window_out, wbytes), rwi = range_of(conv_window_in, wbytes);
   const Range others[] = {range_of(parent, (int64_t)d.Bsz * T * 4), range_of(path, (int64_t)d.Bsz * T * 4),
                           range_of(path_len, (int64_t)d.Bsz * 4), range_of(x, U * T * DI * e),
@@ -229,7 +232,7 @@ int ssm_tree_commit(const ssm_tree_dims* dims, const ssm_tree_params* params, co
 int ssm_tree_commit_verify(const ssm_tree_dims* dims, const ssm_tree_params* params, const int32_t* parent_prev,
                            const int32_t* path, const int32_t* path_len, const void* x_prev, const void* B_prev,
                            const void* C_prev, const void* dt_raw_prev, const void* conv_window_in,
-                           const float* state_in, void* conv_window_out, float* state_out, const int32_t* parent,
+                           const void* state_in, void* conv_window_out, void* state_out, const int32_t* parent,
                            const void* x, const void* B, const void* C, const void* dt_raw, const void* z,
                            float* y, int32_t* commit_status, int32_t* verify_status, void* hip_stream) {
   Dims d;
@@ -237,11 +240,12 @@ int ssm_tree_commit_verify(const ssm_tree_dims* dims, const ssm_tree_params* par
   if (st) return st;
   if (d.L == 0 || d.Bsz == 0) return SSM_TREE_OK;
   const bool fused = !d.fifo && commit_verify_fused_applies(d);
-  // the options (xBC conv, gate) must be supported by whichever kernels run,
-  // checked before anything is enqueued
-  if ((d.xbc || z) && d.T > 0 &&
+  // the options (xBC conv, gate, bfloat16 state) must be supported by
+  // whichever kernels run, checked before anything is enqueued
+  if ((d.xbc || z || d.sbf16) && d.T > 0 &&
       !(fused ? commit_verify_options_supported(d, z != nullptr)
-              : commit_options_supported(d) && verify_options_supported(d, z != nullptr)))
+              : commit_options_supported(d) &&
+                    verify_options_supported(d, z != nullptr, dims->in_dtype == SSM_TREE_BF16)))
     return SSM_TREE_E_DIMS;
   if ((st = check_params(params))) return st;
   if (!path_len || !state_in || !state_out) return SSM_TREE_E_NULL;
@@ -255,11 +259,11 @@ int ssm_tree_commit_verify(const ssm_tree_dims* dims, const ssm_tree_params* par
                         d.W > 1 ? conv_window_in : nullptr, d.W > 1 ? conv_window_out : nullptr};
   for (const void* p : ptrs)
     if (p && misaligned(p)) return SSM_TREE_E_ALIGN;
-  const int64_t e = dims->in_dtype == SSM_TREE_BF16 ? 2 : 4;
+  const int64_t e = dims->in_dtype == SSM_TREE_BF16 ? 2 : 4, es = d.sbf16 ? 2 : 4;
   const int64_t U = (int64_t)d.L * d.Bsz, T = d.T, DI = d.d_in, CH = d.CH;
   const int64_t wbytes = d.W > 1 ? U * (d.W - 1) * CH * e : 0;
   const int64_t bcb = U * T * d.G * d.N * e;
-  const Range rso = range_of(state_out, U * DI * d.N * 4), rsi = range_of(state_in, U * DI * d.N * 4);
+  const Range rso = range_of(state_out, U * DI * d.N * es), rsi = range_of(state_in, U * DI * d.N * es);
   const Range rwo = range_of(conv_window_out, wbytes), rwi = range_of(conv_window_in, wbytes);
   const Range ry = range_of(y, U * T * DI * 4);
   const Range rcs = range_of(commit_status, commit_status ? (int64_t)d.Bsz * 4 : 0);

@@ -28,8 +28,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kCommitRows = 64;
 constexpr int kCommitThreads = 256;
 
-template <typename TIn, int QPT>
+template <typename TIn, typename TS, int QPT>
 __global__ void __launch_bounds__(kCommitThreads) commit_kernel(CommitArgs a, int HWMAX) {
+  typedef StateQuad<TS> SQ;
   const Dims d = a.d;
   const int T = d.T, N = d.N, P = d.P, H = d.H, W = d.W, DI = d.d_in;
   const int b = blockIdx.y, l = blockIdx.z;
@@ -48,12 +49,12 @@ __global__ void __launch_bounds__(kCommitThreads) commit_kernel(CommitArgs a, in
   float* s_B = s_dtx + kMaxNodes * kCommitRows;            // [T][N]
 
   // ---- issue the state loads first (QPT quads per thread) ----
-  const float* sin = a.state_in + (unit * DI + c0) * (int64_t)N;
-  f32x4 hq[QPT];
+  const TS* sin = reinterpret_cast<const TS*>(a.state_in) + (unit * DI + c0) * (int64_t)N;
+  typename SQ::Raw hq[QPT];
 #pragma unroll
   for (int it = 0; it < QPT; ++it) {
     const int qi = threadIdx.x + it * kCommitThreads;
-    hq[it] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(sin) + qi);
+    hq[it] = SQ::load_nt(sin + 4 * qi);
   }
 
   // ---- validate tree and path ----
@@ -160,13 +161,13 @@ __global__ void __launch_bounds__(kCommitThreads) commit_kernel(CommitArgs a, in
   __syncthreads();
 
   // ---- state update along the path ----
-  float* sout = a.state_out + (unit * DI + c0) * (int64_t)N;
+  TS* sout = reinterpret_cast<TS*>(a.state_out) + (unit * DI + c0) * (int64_t)N;
 #pragma unroll
   for (int it = 0; it < QPT; ++it) {
     const int qi = threadIdx.x + it * kCommitThreads;
     const int row = qi / qpr, n = (qi % qpr) * 4;
     const int hh = (c0 + row) / P - h_lo;
-    f32x4 h = hq[it];
+    f32x4 h = SQ::to_f32(hq[it]);
     for (int k = 0; k < len; ++k) {
       const float dA = s_dA[k * HWMAX + hh];
       const float cx = s_dtx[k * kCommitRows + row];
@@ -176,7 +177,7 @@ __global__ void __launch_bounds__(kCommitThreads) commit_kernel(CommitArgs a, in
       h.z = fmaf(dA, h.z, cx * bq.z);
       h.w = fmaf(dA, h.w, cx * bq.w);
     }
-    __builtin_nontemporal_store(h, reinterpret_cast<f32x4*>(sout) + qi);
+    SQ::store_nt(sout + 4 * qi, SQ::from_f32(h));
   }
 }
 
@@ -253,33 +254,34 @@ hipError_t launch_window_bc(const WindowBcArgs& a, bool bf16, hipStream_t s) {
 // window's B and C rows follow in commit_window_bc_kernel.
 bool commit_options_supported(const Dims&) { return true; }
 
-template <typename TIn, int QPT>
+template <typename TIn, typename TS, int QPT>
 static hipError_t launch_c(const CommitArgs& a, hipStream_t s) {
   const int HWMAX = ((kCommitRows + a.d.P - 1) / a.d.P + 1 + 3) & ~3;
   const size_t lds = sizeof(int32_t) * (2 * kMaxNodes + 4) +
                      sizeof(float) * ((size_t)kMaxNodes * HWMAX + kMaxNodes * kCommitRows + (size_t)a.d.T * a.d.N);
   dim3 grid(a.d.d_in / kCommitRows, a.d.Bsz, a.d.L);
-  hipError_t e = allow_lds(commit_kernel<TIn, QPT>, lds);
+  hipError_t e = allow_lds(commit_kernel<TIn, TS, QPT>, lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((commit_kernel<TIn, QPT>), grid, dim3(kCommitThreads), lds, s, a, HWMAX);
+  hipLaunchKernelGGL((commit_kernel<TIn, TS, QPT>), grid, dim3(kCommitThreads), lds, s, a, HWMAX);
   return hipGetLastError();
 }
 
-template <typename TIn>
+template <typename TIn, typename TS>
 static hipError_t launch_cin(const CommitArgs& a, hipStream_t s) {
   // quads per thread = 64 rows * N / 4 / 256 threads = N / 16
   switch (a.d.N) {
-    case 16: return launch_c<TIn, 1>(a, s);
-    case 32: return launch_c<TIn, 2>(a, s);
-    case 64: return launch_c<TIn, 4>(a, s);
-    case 128: return launch_c<TIn, 8>(a, s);
-    case 256: return launch_c<TIn, 16>(a, s);
+    case 16: return launch_c<TIn, TS, 1>(a, s);
+    case 32: return launch_c<TIn, TS, 2>(a, s);
+    case 64: return launch_c<TIn, TS, 4>(a, s);
+    case 128: return launch_c<TIn, TS, 8>(a, s);
+    case 256: return launch_c<TIn, TS, 16>(a, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_commit(const CommitArgs& a, bool bf16, hipStream_t s) {
-  hipError_t e = bf16 ? launch_cin<bf16_t>(a, s) : launch_cin<float>(a, s);
+  hipError_t e = bf16 ? (a.d.sbf16 ? launch_cin<bf16_t, bf16_t>(a, s) : launch_cin<bf16_t, float>(a, s))
+                      : (a.d.sbf16 ? launch_cin<float, bf16_t>(a, s) : launch_cin<float, float>(a, s));
   if (e != hipSuccess || !a.d.xbc) return e;
   WindowBcArgs w{a.d, a.parent, a.path, a.path_len, a.B, a.C, a.window_in, a.window_out, 0};
   return launch_window_bc(w, bf16, s);

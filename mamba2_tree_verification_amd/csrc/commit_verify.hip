@@ -139,8 +139,9 @@ struct CvLds {
 
 // OPT: an instantiation of its own for the Mamba2-convention options (the
 // xBC conv, the gate), so that the plain path keeps its registers and LDS.
-template <typename TIn, int NG, bool OPT>
+template <typename TIn, typename TS, int NG, bool OPT>
 __global__ void __launch_bounds__(kCvWaves * kWave) commit_verify_kernel(CommitVerifyArgs a) {
+  typedef StateQuad<TS> SQ;
   constexpr int N = 16 * NG;
   constexpr int E = (int)sizeof(TIn);
   typedef typename Raw4<E>::T RawQ;
@@ -280,10 +281,10 @@ __global__ void __launch_bounds__(kCvWaves * kWave) commit_verify_kernel(CommitV
 
   // the state last: the small rows above reach LDS while it is still in flight
   // (loads complete in issue order)
-  const float* sin = a.state_in + (unit * DI + c0 + wave * 16 + j) * (int64_t)N + 4 * k;
-  f32x4 hq[NG];
+  const TS* sin = reinterpret_cast<const TS*>(a.state_in) + (unit * DI + c0 + wave * 16 + j) * (int64_t)N + 4 * k;
+  typename SQ::Raw hraw[NG];
 #pragma unroll
-  for (int gg = 0; gg < NG; ++gg) hq[gg] = *reinterpret_cast<const f32x4*>(sin + 16 * gg);
+  for (int gg = 0; gg < NG; ++gg) hraw[gg] = SQ::load(sin + 16 * gg);
 
   // to LDS
   if (tid < T) {
@@ -560,6 +561,9 @@ __global__ void __launch_bounds__(kCvWaves * kWave) commit_verify_kernel(CommitV
   {
     const int row = wave * 16 + j;
     const int hh = (c0 + wave * 16) / P - h_lo;  // the wave's head (P is a multiple of 16)
+    f32x4 hq[NG];
+#pragma unroll
+    for (int gg = 0; gg < NG; ++gg) hq[gg] = SQ::to_f32(hraw[gg]);
     for (int q = 0; q < len; ++q) {
       const float dA = s_dAp[s_path[q] * 4 + hh];
       const float cx = s_dtx[q * kCvRows + row];
@@ -574,10 +578,17 @@ __global__ void __launch_bounds__(kCvWaves * kWave) commit_verify_kernel(CommitV
         hq[gg].w = fmaf(dA, hq[gg].w, cx * bq.w);
       }
     }
-    if (!OPT || a.state_out) {
-      float* so = a.state_out + (unit * DI + c0 + row) * (int64_t)N + 4 * k;
+    // the committed state as stored (a bfloat16 state is rounded): the
+    // next tree is verified from exactly what the two-call round would read
 #pragma unroll
-      for (int gg = 0; gg < NG; ++gg) *reinterpret_cast<f32x4*>(so + 16 * gg) = hq[gg];
+    for (int gg = 0; gg < NG; ++gg) {
+      hraw[gg] = SQ::from_f32(hq[gg]);
+      hq[gg] = SQ::to_f32(hraw[gg]);
+    }
+    if (!OPT || a.state_out) {
+      TS* so = reinterpret_cast<TS*>(a.state_out) + (unit * DI + c0 + row) * (int64_t)N + 4 * k;
+#pragma unroll
+      for (int gg = 0; gg < NG; ++gg) SQ::store(so + 16 * gg, hraw[gg]);
     }
 
     // C . h on the matrix cores: lane (c + 16 q) ends with (C_{4q+r} . h_c)
@@ -648,12 +659,12 @@ __global__ void __launch_bounds__(kCvWaves * kWave) commit_verify_kernel(CommitV
 
 namespace {
 
-template <typename TIn, int NG, bool OPT>
+template <typename TIn, typename TS, int NG, bool OPT>
 int launch_cv_o(const CommitVerifyArgs& a, hipStream_t s) {
   const size_t lds = (size_t)CvLds(16 * NG, (int)sizeof(TIn), OPT && a.d.xbc, OPT && a.z != nullptr).total;
-  if (allow_lds(commit_verify_kernel<TIn, NG, OPT>, lds) != hipSuccess) return SSM_TREE_E_HIP;
+  if (allow_lds(commit_verify_kernel<TIn, TS, NG, OPT>, lds) != hipSuccess) return SSM_TREE_E_HIP;
   dim3 grid(a.d.d_in / kCvRows, a.d.Bsz, a.d.L);
-  hipLaunchKernelGGL((commit_verify_kernel<TIn, NG, OPT>), grid, dim3(kCvWaves * kWave), lds, s, a);
+  hipLaunchKernelGGL((commit_verify_kernel<TIn, TS, NG, OPT>), grid, dim3(kCvWaves * kWave), lds, s, a);
   if (hipGetLastError() != hipSuccess) return SSM_TREE_E_HIP;
   if (a.d.xbc && a.window_out) {  // the window's B and C rows, after every reader of the old ones
     WindowBcArgs w{a.d, a.parent_prev, a.path, a.path_len, a.B_prev, a.C_prev, a.window_in, a.window_out, 1};
@@ -664,7 +675,9 @@ int launch_cv_o(const CommitVerifyArgs& a, hipStream_t s) {
 
 template <typename TIn, int NG>
 int launch_cv_t(const CommitVerifyArgs& a, hipStream_t s) {
-  return (a.d.xbc || a.z) ? launch_cv_o<TIn, NG, true>(a, s) : launch_cv_o<TIn, NG, false>(a, s);
+  if (a.d.sbf16)  // (no options with a bfloat16 state)
+    return (a.d.xbc || a.z) ? SSM_TREE_E_DIMS : launch_cv_o<TIn, bf16_t, NG, false>(a, s);
+  return (a.d.xbc || a.z) ? launch_cv_o<TIn, float, NG, true>(a, s) : launch_cv_o<TIn, float, NG, false>(a, s);
 }
 
 template <typename TIn>
@@ -683,8 +696,9 @@ int launch_cv_in(const CommitVerifyArgs& a, hipStream_t s) {
 
 bool commit_verify_fused_applies(const Dims& d) { return d.T >= 1 && d.T <= kCvT && d.P % 16 == 0; }
 
-// SSM_TREE_CONV_XBC and the gate: taken by the kernel's OPT instantiation.
-bool commit_verify_options_supported(const Dims&, bool) { return true; }
+// SSM_TREE_CONV_XBC and the gate: taken by the kernel's OPT instantiation,
+// with a float32 state.
+bool commit_verify_options_supported(const Dims& d, bool gate) { return !d.sbf16 || (!d.xbc && !gate); }
 
 int launch_commit_verify(const CommitVerifyArgs& a, bool bf16, hipStream_t s) {
   return bf16 ? launch_cv_in<bf16_t>(a, s) : launch_cv_in<float>(a, s);

@@ -35,6 +35,61 @@ __device__ __forceinline__ float load_in<bf16_t>(const bf16_t* p, int64_t i) {
   return bf16_bits_to_float(p[i].bits);
 }
 
+// ---------------------------------------------------------------------------
+// root-state elements: float32, or bfloat16 with SSM_TREE_STATE_BF16
+// (arithmetic is float32 either way; a bfloat16 state is rounded on store)
+// ---------------------------------------------------------------------------
+
+typedef float sf32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int su32x2 __attribute__((ext_vector_type(2)));
+
+// float32 to bfloat16 bits: nearest, ties to the even significand (adding
+// 0x7fff plus the kept LSB carries exactly past the halfway point); values
+// past the largest finite bf16 become infinite, NaN stays a quiet NaN
+__device__ __forceinline__ uint32_t bf16_round_bits(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// four consecutive state elements: Raw is what memory holds
+template <typename TS>
+struct StateQuad;
+template <>
+struct StateQuad<float> {
+  typedef sf32x4 Raw;
+  static __device__ __forceinline__ Raw load(const float* p) { return *reinterpret_cast<const sf32x4*>(p); }
+  static __device__ __forceinline__ Raw load_nt(const float* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const sf32x4*>(p));
+  }
+  static __device__ __forceinline__ sf32x4 to_f32(Raw r) { return r; }
+  static __device__ __forceinline__ Raw from_f32(sf32x4 v) { return v; }
+  static __device__ __forceinline__ void store(float* p, Raw r) { *reinterpret_cast<sf32x4*>(p) = r; }
+  static __device__ __forceinline__ void store_nt(float* p, Raw r) {
+    __builtin_nontemporal_store(r, reinterpret_cast<sf32x4*>(p));
+  }
+};
+template <>
+struct StateQuad<bf16_t> {
+  typedef su32x2 Raw;
+  static __device__ __forceinline__ Raw load(const bf16_t* p) { return *reinterpret_cast<const su32x2*>(p); }
+  static __device__ __forceinline__ Raw load_nt(const bf16_t* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const su32x2*>(p));
+  }
+  static __device__ __forceinline__ sf32x4 to_f32(Raw r) {
+    return sf32x4{__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xFFFF0000u), __uint_as_float(r.y << 16),
+                  __uint_as_float(r.y & 0xFFFF0000u)};
+  }
+  static __device__ __forceinline__ Raw from_f32(sf32x4 v) {
+    return su32x2{bf16_round_bits(v.x) | (bf16_round_bits(v.y) << 16),
+                  bf16_round_bits(v.z) | (bf16_round_bits(v.w) << 16)};
+  }
+  static __device__ __forceinline__ void store(bf16_t* p, Raw r) { *reinterpret_cast<su32x2*>(p) = r; }
+  static __device__ __forceinline__ void store_nt(bf16_t* p, Raw r) {
+    __builtin_nontemporal_store(r, reinterpret_cast<su32x2*>(p));
+  }
+};
+
 // softplus with the large-argument cut-over used by Mamba2 (z for z > 20)
 __device__ __forceinline__ float softplus_f32(float z) { return z > 20.0f ? z : log1pf(expf(z)); }
 
@@ -50,6 +105,7 @@ struct Dims {
   int32_t fifo;  // verify by the explicit FIFO walk
   int32_t xbc;   // the conv runs over x, B and C
   int32_t CH;    // conv channels (window row length): d_in, or d_in + 2 G N with xbc
+  int32_t sbf16; // the root state is stored as bfloat16
 };
 
 struct Params {
@@ -70,7 +126,7 @@ struct VerifyArgs {
   const void* dt_raw;
   const void* z;  // gate input, or null
   const void* window;
-  const float* state;
+  const void* state;  // float32, or bfloat16 with sbf16
   float* y;
   int32_t* seq_status;
 };
@@ -86,9 +142,9 @@ struct CommitArgs {
   const void* C;  // read only with xbc
   const void* dt_raw;
   const void* window_in;
-  const float* state_in;
+  const void* state_in;  // float32, or bfloat16 with sbf16
   void* window_out;
-  float* state_out;
+  void* state_out;
   int32_t* seq_status;
 };
 
@@ -117,9 +173,9 @@ struct CommitVerifyArgs {
   const void* C_prev;  // read only with xbc
   const void* dt_prev;
   const void* window_in;
-  const float* state_in;
+  const void* state_in;  // float32, or bfloat16 with sbf16
   void* window_out;
-  float* state_out;
+  void* state_out;
   const int32_t* parent;
   const void* x;
   const void* B;

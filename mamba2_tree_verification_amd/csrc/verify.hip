@@ -269,7 +269,7 @@ __global__ void __launch_bounds__(kThreads) verify_proj_kernel(VerifyArgs a, Ver
   const int NCH = N / kChunk;
   const int total = NBLK * NCH;
   // lane -> (row lane/4 + 16 i, quad lane%4) of instruction i of a chunk
-  const float* st_wave = a.state + (unit * DI + c_wg + wave * R * kWave + (lane >> 2)) * (int64_t)N + (lane & 3) * 4;
+  const float* st_wave = reinterpret_cast<const float*>(a.state) + (unit * DI + c_wg + wave * R * kWave + (lane >> 2)) * (int64_t)N + (lane & 3) * 4;
   const int64_t row_step = (int64_t)16 * N;
   auto chunk_src = [&](int s) {
     const int blk = s / NCH, ch = s % NCH;
@@ -662,20 +662,28 @@ int launch_verify_fifo(const VerifyArgs& a, bool bf16, hipStream_t s);
 // SSM_TREE_CONV_XBC and the gate: taken on the fused round's shapes, whose
 // kernel then runs with nothing to commit (see ssm_tree_verify).
 bool commit_verify_fused_applies(const Dims& d);
-bool verify_options_supported(const Dims& d, bool gate) {
+bool tt_verify_applies(const Dims& d);
+bool tt_verify_fits(const Dims& d, bool bf16);
+int launch_verify_tt(const VerifyArgs& a, bool bf16, hipStream_t s);
+
+// A bfloat16 root state (SSM_TREE_STATE_BF16) is read by the matrix-core
+// kernels only: no FIFO walk, no options.
+bool verify_options_supported(const Dims& d, bool gate, bool bf16) {
+  if (d.sbf16)
+    return d.T == 0 || (!d.fifo && !d.xbc && !gate &&
+                        (mfma_verify_applies(d) || (tt_verify_applies(d) && tt_verify_fits(d, bf16))));
   return (!d.xbc && !gate) || (!d.fifo && commit_verify_fused_applies(d));
 }
-
-bool tt_verify_applies(const Dims& d);
-int launch_verify_tt(const VerifyArgs& a, bool bf16, hipStream_t s);
 
 int launch_verify(const VerifyArgs& a, bool bf16, hipStream_t s) {
   if (a.d.fifo) return launch_verify_fifo(a, bf16, s);
   if (mfma_verify_applies(a.d)) return launch_verify_mfma(a, bf16, s);
   if (tt_verify_applies(a.d)) {
     const int st = launch_verify_tt(a, bf16, s);
-    if (st != SSM_TREE_E_DIMS) return st;  // E_DIMS: its LDS does not fit this shape, nothing launched
+    // E_DIMS: its LDS does not fit this shape, nothing launched
+    if (st != SSM_TREE_E_DIMS || a.d.sbf16) return st;
   }
+  if (a.d.sbf16) return SSM_TREE_E_DIMS;
   return bf16 ? launch_in<bf16_t>(a, s) : launch_in<float>(a, s);
 }
 

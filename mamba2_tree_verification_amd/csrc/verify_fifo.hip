@@ -175,7 +175,7 @@ __global__ void __launch_bounds__(kWave) verify_fifo_kernel(VerifyArgs a) {
     s_dA[v * kRows + rr] = expf(dt * a.prm.A[(int64_t)l * H + hh]);
   }
   // root state into slot K
-  const float* h0p = a.state + (unit * DI + c) * (int64_t)N + s * NPL;
+  const float* h0p = reinterpret_cast<const float*>(a.state) + (unit * DI + c) * (int64_t)N + s * NPL;
 #pragma unroll
   for (int i = 0; i < NPL; ++i) slot_at(kRing, i) = h0p[i];
   __syncthreads();

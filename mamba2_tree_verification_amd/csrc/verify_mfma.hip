@@ -128,7 +128,7 @@ __device__ __forceinline__ int opaque_lane() {
 // its four tiles a lane owns four adjacent channels and y leaves in 16-byte
 // stores of whole 256-byte row segments; otherwise tile tl holds channels
 // 16 tl + j (one head per tile) and y leaves per tile.
-template <typename TIn, int NG, int RD, int WPG, bool ILV>
+template <typename TIn, typename TS, int NG, int RD, int WPG, bool ILV>
 __global__ void __launch_bounds__(WPG * 64) verify_mfma_kernel(VerifyArgs a, int items_per_wg) {
   constexpr int N = 16 * NG;
   typedef WaveLds<sizeof(TIn)> Lw;
@@ -170,12 +170,12 @@ __global__ void __launch_bounds__(WPG * 64) verify_mfma_kernel(VerifyArgs a, int
   int nxt = grab();
 
   // ---- the state stream: piece i of an item = (tile i / NG, columns 16 (i % NG) ..) ----
-  const float* sbase = a.state + (int64_t)(ILV ? 4 * j : j) * N + 4 * k;
+  typedef StateQuad<TS> SQ;
+  const TS* sbase = reinterpret_cast<const TS*>(a.state) + (int64_t)(ILV ? 4 * j : j) * N + 4 * k;
   auto piece = [&](int item, int i) {
-    return *reinterpret_cast<const f32x4*>(sbase + ((int64_t)item * kSlab + (i / NG) * (ILV ? 1 : 16)) * N +
-                                           (i % NG) * 16);
+    return SQ::load(sbase + ((int64_t)item * kSlab + (i / NG) * (ILV ? 1 : 16)) * N + (i % NG) * 16);
   };
-  f32x4 ring[RD];
+  typename SQ::Raw ring[RD];  // raw: converted where the products take it
 #pragma unroll
   for (int i = 0; i < RD; ++i) ring[i] = piece(cur, i);
 
@@ -442,7 +442,7 @@ __global__ void __launch_bounds__(WPG * 64) verify_mfma_kernel(VerifyArgs a, int
 #pragma unroll
       for (int gg = 0; gg < NG; ++gg) {
         const int i = tl * NG + gg;  // static
-        const f32x4 h = ring[i % RD];
+        const f32x4 h = SQ::to_f32(ring[i % RD]);
         acc = mfma4(cop[gg].x, h.x, acc);
         acc = mfma4(cop[gg].y, h.y, acc);
         acc = mfma4(cop[gg].z, h.z, acc);
@@ -462,11 +462,11 @@ __global__ void __launch_bounds__(WPG * 64) verify_mfma_kernel(VerifyArgs a, int
 
 namespace {
 
-template <typename TIn, int NG, int RD, bool ILV>
+template <typename TIn, typename TS, int NG, int RD, bool ILV>
 int launch_mfma_t(const VerifyArgs& a, hipStream_t s) {
   // sixteen waves per CU where registers and LDS allow, else twelve
   constexpr int kWpg = (sizeof(TIn) == 2 && NG <= 8) ? 16 : 12;
-  auto kern = verify_mfma_kernel<TIn, NG, RD, kWpg, ILV>;
+  auto kern = verify_mfma_kernel<TIn, TS, NG, RD, kWpg, ILV>;
   const size_t lds = (size_t)kWpg * WaveLds<sizeof(TIn)>::bytes + 16;
   if (allow_lds(kern, lds) != hipSuccess) return SSM_TREE_E_HIP;
   int dev = 0, n_cu = 0, resident = 0;
@@ -485,21 +485,21 @@ int launch_mfma_t(const VerifyArgs& a, hipStream_t s) {
   return hipGetLastError() == hipSuccess ? SSM_TREE_OK : SSM_TREE_E_HIP;
 }
 
-template <typename TIn, bool ILV>
+template <typename TIn, typename TS, bool ILV>
 int launch_mfma_n(const VerifyArgs& a, hipStream_t s) {
   switch (a.d.N) {
-    case 16: return launch_mfma_t<TIn, 1, 4, ILV>(a, s);
-    case 32: return launch_mfma_t<TIn, 2, 8, ILV>(a, s);
-    case 64: return launch_mfma_t<TIn, 4, 8, ILV>(a, s);
-    case 128: return launch_mfma_t<TIn, 8, 8, ILV>(a, s);
-    case 256: return launch_mfma_t<TIn, 16, 4, ILV>(a, s);
+    case 16: return launch_mfma_t<TIn, TS, 1, 4, ILV>(a, s);
+    case 32: return launch_mfma_t<TIn, TS, 2, 8, ILV>(a, s);
+    case 64: return launch_mfma_t<TIn, TS, 4, 8, ILV>(a, s);
+    case 128: return launch_mfma_t<TIn, TS, 8, 8, ILV>(a, s);
+    case 256: return launch_mfma_t<TIn, TS, 16, 4, ILV>(a, s);
     default: return SSM_TREE_E_DIMS;
   }
 }
 
-template <typename TIn>
+template <typename TIn, typename TS>
 int launch_mfma_in(const VerifyArgs& a, hipStream_t s) {
-  return a.d.P % kSlab == 0 ? launch_mfma_n<TIn, true>(a, s) : launch_mfma_n<TIn, false>(a, s);
+  return a.d.P % kSlab == 0 ? launch_mfma_n<TIn, TS, true>(a, s) : launch_mfma_n<TIn, TS, false>(a, s);
 }
 
 }  // namespace
@@ -508,7 +508,8 @@ int launch_mfma_in(const VerifyArgs& a, hipStream_t s) {
 bool mfma_verify_applies(const Dims& d) { return d.T >= 1 && d.T <= kTile && d.P % 16 == 0 && d.d_in % kSlab == 0; }
 
 int launch_verify_mfma(const VerifyArgs& a, bool bf16, hipStream_t s) {
-  return bf16 ? launch_mfma_in<bf16_t>(a, s) : launch_mfma_in<float>(a, s);
+  if (a.d.sbf16) return bf16 ? launch_mfma_in<bf16_t, bf16_t>(a, s) : launch_mfma_in<float, bf16_t>(a, s);
+  return bf16 ? launch_mfma_in<bf16_t, float>(a, s) : launch_mfma_in<float, float>(a, s);
 }
 
 }  // namespace ssmt

@@ -234,8 +234,9 @@ struct TtLds {
 
 }  // namespace
 
-template <typename TIn, int NG, int TT>
+template <typename TIn, typename TS, int NG, int TT>
 __global__ void __launch_bounds__(kTtThreads) verify_tt_kernel(VerifyArgs a, int NBLK) {
+  typedef StateQuad<TS> SQ;
   constexpr int N = 16 * NG;
   constexpr int E = (int)sizeof(TIn);
   constexpr int KT = 16 * TT;                      // node capacity
@@ -274,11 +275,11 @@ __global__ void __launch_bounds__(kTtThreads) verify_tt_kernel(VerifyArgs a, int
   const int rs = lo.row;
 
   // ---- the first block's state, in flight during the tree prologue ----
-  f32x4 hq[NG];
+  typename SQ::Raw hq[NG];  // raw until the products take it
   {
-    const float* sin = a.state + (unit * DI + cw0 + wave * 16 + j) * (int64_t)N + 4 * k;
+    const TS* sin = reinterpret_cast<const TS*>(a.state) + (unit * DI + cw0 + wave * 16 + j) * (int64_t)N + 4 * k;
 #pragma unroll
-    for (int gg = 0; gg < NG; ++gg) hq[gg] = *reinterpret_cast<const f32x4*>(sin + 16 * gg);
+    for (int gg = 0; gg < NG; ++gg) hq[gg] = SQ::load(sin + 16 * gg);
   }
 
   // ---- tree prologue: parent[], C and B rows ----
@@ -575,45 +576,54 @@ __global__ void __launch_bounds__(kTtThreads) verify_tt_kernel(VerifyArgs a, int
 #pragma unroll
     for (int ti = 0; ti < TT; ++ti) acc[ti] = f32x4{0.f, 0.f, 0.f, 0.f};
     const bool more = blk + 1 < NBLK;
-    const float* nsin = a.state + (unit * DI + c0 + kTtRows + wave * 16 + j) * (int64_t)N + 4 * k;
+    const TS* nsin = reinterpret_cast<const TS*>(a.state) + (unit * DI + c0 + kTtRows + wave * 16 + j) * (int64_t)N + 4 * k;
     if constexpr (E == 2) {
-      // bf16 C rows against the state split into three bf16 terms, two
-      // column groups per product
+      // bf16 C rows against the state, two column groups per product: a
+      // bf16 state is an exact operand as it stands; an fp32 state is split
+      // into three bf16 terms
 #pragma unroll
       for (int m = 0; m < (NG + 1) / 2; ++m) {
         const bool two = 2 * m + 1 < NG;
         u32x4 h0, h1, h2;
-        split3(hq[2 * m], two ? hq[2 * m + 1] : f32x4{0.f, 0.f, 0.f, 0.f}, h0, h1, h2);
+        if constexpr (sizeof(TS) == 2) {
+          const u32x2 lo = hq[2 * m], hi = two ? hq[2 * m + 1] : u32x2{0u, 0u};
+          h0 = u32x4{lo.x, lo.y, hi.x, hi.y};
+        } else {
+          split3(hq[2 * m], two ? hq[2 * m + 1] : f32x4{0.f, 0.f, 0.f, 0.f}, h0, h1, h2);
+        }
 #pragma unroll
         for (int ti = 0; ti < TT; ++ti) {
           const TIn* crow = reinterpret_cast<const TIn*>(s_C + (16 * ti + j) * rs) + 32 * m + 4 * k;
           const u32x2 c0 = *reinterpret_cast<const u32x2*>(crow);
           const u32x2 c1 = two ? *reinterpret_cast<const u32x2*>(crow + 16) : u32x2{0u, 0u};
           const u32x4 ca = u32x4{c0.x, c0.y, c1.x, c1.y};
-          acc[ti] = mfma32(ca, h2, acc[ti]);
-          acc[ti] = mfma32(ca, h1, acc[ti]);
+          if constexpr (sizeof(TS) != 2) {
+            acc[ti] = mfma32(ca, h2, acc[ti]);
+            acc[ti] = mfma32(ca, h1, acc[ti]);
+          }
           acc[ti] = mfma32(ca, h0, acc[ti]);
         }
         // these column groups are consumed: the next block's take their registers
         if (more) {
-          hq[2 * m] = *reinterpret_cast<const f32x4*>(nsin + 32 * m);
-          if (two) hq[2 * m + 1] = *reinterpret_cast<const f32x4*>(nsin + 32 * m + 16);
+          hq[2 * m] = SQ::load(nsin + 32 * m);
+          if (two) hq[2 * m + 1] = SQ::load(nsin + 32 * m + 16);
         }
         asm volatile("" ::: "memory");
       }
     } else {
 #pragma unroll
       for (int gg = 0; gg < NG; ++gg) {
+        const f32x4 h = SQ::to_f32(hq[gg]);
 #pragma unroll
         for (int ti = 0; ti < TT; ++ti) {
           const f32x4 cq = load4<TIn>(reinterpret_cast<const TIn*>(s_C + (16 * ti + j) * rs) + 16 * gg + 4 * k);
-          acc[ti] = mfma4(cq.x, hq[gg].x, acc[ti]);
-          acc[ti] = mfma4(cq.y, hq[gg].y, acc[ti]);
-          acc[ti] = mfma4(cq.z, hq[gg].z, acc[ti]);
-          acc[ti] = mfma4(cq.w, hq[gg].w, acc[ti]);
+          acc[ti] = mfma4(cq.x, h.x, acc[ti]);
+          acc[ti] = mfma4(cq.y, h.y, acc[ti]);
+          acc[ti] = mfma4(cq.z, h.z, acc[ti]);
+          acc[ti] = mfma4(cq.w, h.w, acc[ti]);
         }
         // this column group is consumed: the next block's takes its registers
-        if (more) hq[gg] = *reinterpret_cast<const f32x4*>(nsin + 16 * gg);
+        if (more) hq[gg] = SQ::load(nsin + 16 * gg);
         // one column group's C operands at a time (hoisting all of them would
         // take 4 NG x 4 registers)
         asm volatile("" ::: "memory");
@@ -666,34 +676,34 @@ __global__ void __launch_bounds__(kTtThreads) verify_tt_kernel(VerifyArgs a, int
 
 namespace {
 
-template <typename TIn, int NG, int TT>
+template <typename TIn, typename TS, int NG, int TT>
 int launch_tt_t(const VerifyArgs& a, hipStream_t s) {
   const size_t lds = (size_t)TtLds(16 * NG, (int)sizeof(TIn), TT).total;
   if (lds > 160 * 1024) return SSM_TREE_E_DIMS;  // (fp32 inputs with d_state 256) the caller falls back
-  if (allow_lds(verify_tt_kernel<TIn, NG, TT>, lds) != hipSuccess) return SSM_TREE_E_HIP;
+  if (allow_lds(verify_tt_kernel<TIn, TS, NG, TT>, lds) != hipSuccess) return SSM_TREE_E_HIP;
   const int blocks = a.d.d_in / a.d.G / kTtRows;  // 64-channel blocks per B/C group
   const int nblk = blocks % 4 == 0 ? 4 : (blocks % 2 == 0 ? 2 : 1);
   dim3 grid(a.d.d_in / (nblk * kTtRows), a.d.Bsz, a.d.L);
-  hipLaunchKernelGGL((verify_tt_kernel<TIn, NG, TT>), grid, dim3(kTtThreads), lds, s, a, nblk);
+  hipLaunchKernelGGL((verify_tt_kernel<TIn, TS, NG, TT>), grid, dim3(kTtThreads), lds, s, a, nblk);
   return hipGetLastError() == hipSuccess ? SSM_TREE_OK : SSM_TREE_E_HIP;
 }
 
-template <typename TIn, int NG>
+template <typename TIn, typename TS, int NG>
 int launch_tt_g(const VerifyArgs& a, hipStream_t s) {
   const int T = a.d.T;
-  if (T <= 32) return launch_tt_t<TIn, NG, 2>(a, s);
-  if (T <= 48) return launch_tt_t<TIn, NG, 3>(a, s);
-  return launch_tt_t<TIn, NG, 4>(a, s);
+  if (T <= 32) return launch_tt_t<TIn, TS, NG, 2>(a, s);
+  if (T <= 48) return launch_tt_t<TIn, TS, NG, 3>(a, s);
+  return launch_tt_t<TIn, TS, NG, 4>(a, s);
 }
 
-template <typename TIn>
+template <typename TIn, typename TS>
 int launch_tt_in(const VerifyArgs& a, hipStream_t s) {
   switch (a.d.N) {
-    case 16: return launch_tt_g<TIn, 1>(a, s);
-    case 32: return launch_tt_g<TIn, 2>(a, s);
-    case 64: return launch_tt_g<TIn, 4>(a, s);
-    case 128: return launch_tt_g<TIn, 8>(a, s);
-    case 256: return launch_tt_g<TIn, 16>(a, s);
+    case 16: return launch_tt_g<TIn, TS, 1>(a, s);
+    case 32: return launch_tt_g<TIn, TS, 2>(a, s);
+    case 64: return launch_tt_g<TIn, TS, 4>(a, s);
+    case 128: return launch_tt_g<TIn, TS, 8>(a, s);
+    case 256: return launch_tt_g<TIn, TS, 16>(a, s);
     default: return SSM_TREE_E_DIMS;
   }
 }
@@ -705,8 +715,16 @@ bool tt_verify_applies(const Dims& d) {
   return d.T > 16 && d.T <= kTtMaxT && d.P % 16 == 0 && (d.d_in / d.G) % kTtRows == 0;
 }
 
+// whether the kernel's LDS fits the shape (it does except for fp32 inputs
+// with d_state 256)
+bool tt_verify_fits(const Dims& d, bool bf16) {
+  const int TT = (d.T + 15) / 16;
+  return TtLds(d.N, bf16 ? 2 : 4, TT < 2 ? 2 : TT).total <= 160 * 1024;
+}
+
 int launch_verify_tt(const VerifyArgs& a, bool bf16, hipStream_t s) {
-  return bf16 ? launch_tt_in<bf16_t>(a, s) : launch_tt_in<float>(a, s);
+  if (a.d.sbf16) return bf16 ? launch_tt_in<bf16_t, bf16_t>(a, s) : launch_tt_in<float, bf16_t>(a, s);
+  return bf16 ? launch_tt_in<bf16_t, float>(a, s) : launch_tt_in<float, float>(a, s);
 }
 
 }  // namespace ssmt

@@ -45,7 +45,7 @@ class GpuCase:
         self.inp = inp if inp is not None else C.make_inputs(cfg)
         self.g = upload(self.inp, device)
         self.dims = m.make_dims(cfg.L, cfg.Bsz, cfg.T, cfg.H, cfg.P, cfg.N, cfg.G, cfg.W, cfg.bf16, cfg.silu, fifo,
-                                cfg.xbc)
+                                cfg.xbc, getattr(cfg, "state_bf16", False))
         self.prm = m.make_params(self.g.A, self.g.D, self.g.dt_bias, self.g.conv_w, self.g.conv_b)
         self.device = device
 

@@ -45,6 +45,7 @@ def test_header_constants_match_binding():
     assert consts["SSM_TREE_CONV_SILU"] == m.SSM_TREE_CONV_SILU
     assert consts["SSM_TREE_VERIFY_FIFO"] == m.SSM_TREE_VERIFY_FIFO
     assert consts["SSM_TREE_CONV_XBC"] == m.SSM_TREE_CONV_XBC
+    assert consts["SSM_TREE_STATE_BF16"] == m.SSM_TREE_STATE_BF16
 
 
 def test_status_strings():
@@ -107,7 +108,7 @@ def test_dtype_flags_null_align_alias():
     d.in_dtype = 7
     assert call_verify(d, good_params()) == m.E_DTYPE
     d = good_dims()
-    d.flags = 8
+    d.flags = 16  # the first unassigned bit
     assert call_verify(d, good_params()) == m.E_FLAGS
     assert m.load().ssm_tree_verify(None, None, *([None] * 11)) == m.E_NULL
     assert m.load().ssm_tree_verify(ctypes.byref(good_dims()), None, *([None] * 11)) == m.E_NULL
@@ -175,7 +176,7 @@ def test_commit_verify_host_checks(dkw):
     assert call_commit_verify(d, p, vst=fake(1)) == m.E_ALIAS                  # status over parent_prev
     assert call_commit_verify(d, good_params(A=None)) == m.E_NULL
     bad = good_dims(**dkw)
-    bad.flags = 8
+    bad.flags = 16  # the first unassigned bit
     assert call_commit_verify(bad, p) == m.E_FLAGS
 
 
@@ -230,3 +231,33 @@ def test_option_host_checks():
     d = good_dims(T=20)
     d.flags = m.SSM_TREE_CONV_XBC
     assert call_commit_verify(d, p) == m.E_DIMS
+
+
+def test_state_bf16_host_checks():
+    """A bfloat16 root state: refused, before anything is enqueued, where no
+    kernel takes it (the FIFO walk, the options, the vector-ALU shapes, fp32
+    inputs with d_state 256 past 16 nodes), and its byte size is what the
+    range checks use.  Every call here fails on a host check."""
+    p = good_params()
+
+    def sb(flags=0, **kw):
+        d = good_dims(**kw)
+        d.flags = m.SSM_TREE_STATE_BF16 | flags
+        return d
+
+    assert call_verify(sb(m.SSM_TREE_VERIFY_FIFO), p) == m.E_DIMS
+    assert call_verify(sb(m.SSM_TREE_CONV_XBC), p) == m.E_DIMS
+    assert call_verify(sb(), p, z=fake(30)) == m.E_DIMS                        # the gate
+    assert call_verify(sb(H=8, P=40), p) == m.E_DIMS                          # headdim not a multiple of 16
+    assert call_verify(sb(T=40, H=6, P=32, G=2), p) == m.E_DIMS               # 96-channel B/C groups, T > 16
+    assert call_verify(sb(T=64, N=256, bf16=False), p) == m.E_DIMS            # fp32 in, N 256: 184 KiB of LDS
+    assert call_commit_verify(sb(m.SSM_TREE_VERIFY_FIFO), p) == m.E_DIMS
+    assert call_commit_verify(sb(T=20, H=8, P=40), p) == m.E_DIMS
+    assert call_commit_verify(sb(), p, z=fake(30)) == m.E_DIMS
+    # the state is 2 bytes per element with the flag: 2 x 3 x 256 x 128 x 2 = 393216 bytes, so
+    # state_out 393200 bytes into state_in overlaps it; without the flag (4 bytes per element)
+    # so does one 600000 bytes in (alias checks are the last before a launch, so only overlaps
+    # are asserted here)
+    assert call_commit(sb(), p, state_out=fake(7, 393200)) == m.E_ALIAS
+    assert call_commit_verify(sb(), p, state_out=fake(7, 393200)) == m.E_ALIAS
+    assert call_commit(good_dims(), p, state_out=fake(7, 600000)) == m.E_ALIAS
