@@ -394,13 +394,22 @@ def state_bf16_round(torch, m, cfg, g, g2, state, window, timed, path_lens):
     if not (cst.cpu() == 0).all() or not (vst.cpu() == 0).all() or torch.isnan(y).any():
         raise SystemExit("bench: the bf16-state round produced a bad status or NaN")
     # the root state is read and written once per round, 2 bytes per element instead of 4
-    saved = cfg.L * cfg.Bsz * 2 * (cfg.H * cfg.P * cfg.N * 2)
-    nbytes = sum(algorithmic_bytes(cfg, pl)["commit_verify"] for pl in path_lens) // len(path_lens) - saved
+    half = cfg.L * cfg.Bsz * cfg.H * cfg.P * cfg.N * 2
+    nbytes = sum(algorithmic_bytes(cfg, pl)["commit_verify"] for pl in path_lens) // len(path_lens) - 2 * half
     avg = sum(ms) / len(ms)
     ach = nbytes / (avg * 1e-3) / 1e9
-    return {"state": "bf16 (rounded to nearest even on store)", "ms": round(avg, 4), "ms_min": round(min(ms), 4),
-            "bytes": nbytes, "GBps": round(ach, 1), "frac": round(ach / HBM_PEAK_GBS, 4),
-            "node_layers_per_s": round(cfg.L * cfg.Bsz * cfg.T / (avg * 1e-3), 1), "note": "not in the step"}
+    out = {"state": "bf16 (rounded to nearest even on store)", "ms": round(avg, 4), "ms_min": round(min(ms), 4),
+           "bytes": nbytes, "GBps": round(ach, 1), "frac": round(ach / HBM_PEAK_GBS, 4),
+           "node_layers_per_s": round(cfg.L * cfg.Bsz * cfg.T / (avg * 1e-3), 1), "note": "not in the step"}
+    # the two calls apart (verify reads the state once, commit reads and writes it)
+    ab = algorithmic_bytes(cfg, path_lens[0])
+    vms = timed(lambda: m.verify(dims, prm, g.parent, g.x, g.B, g.C, g.dt_raw, win, sb, y, vst))
+    cms = timed(lambda: m.commit(dims, prm, g.parent, g.path, g.path_len, g.x, g.B, g.dt_raw, win, sb, win, sb, cst))
+    for name, v, nb in (("verify", vms, ab["verify"] - half), ("commit", cms, ab["commit"] - 2 * half)):
+        a = sum(v) / len(v)
+        out[name] = {"ms": round(a, 4), "bytes": nb, "GBps": round(nb / (a * 1e-3) / 1e9, 1),
+                     "frac": round(nb / (a * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    return out
 
 
 def hbm_probe(torch, nbytes=4 << 30, reps=10):
