@@ -43,9 +43,10 @@ __global__ void __launch_bounds__(kCommitThreads) commit_kernel(CommitArgs a, in
   extern __shared__ __align__(16) unsigned char smem[];
   int32_t* s_parent = reinterpret_cast<int32_t*>(smem);
   int32_t* s_path = s_parent + kMaxNodes;
-  int32_t* s_misc = s_path + kMaxNodes;  // [0] = len, [1] = valid status
+  int32_t* s_misc = s_path + kMaxNodes;
   float* s_dA = reinterpret_cast<float*>(s_misc + 4);      // [T][HWMAX]
-  float* s_dtx = s_dA + kMaxNodes * HWMAX;                 // [T][64]
+  float* s_dtv = s_dA + kMaxNodes * HWMAX;                 // [T][HWMAX] dt
+  float* s_dtx = s_dtv + kMaxNodes * HWMAX;                // [T][64] raw x of the path nodes, then dt x~
   float* s_B = s_dtx + kMaxNodes * kCommitRows;            // [T][N]
 
   // ---- issue the state loads first (QPT quads per thread) ----
@@ -64,23 +65,21 @@ __global__ void __launch_bounds__(kCommitThreads) commit_kernel(CommitArgs a, in
   }
   __syncthreads();
   const bool tree_ok = tree_is_valid(s_parent, T);
-  if (threadIdx.x == 0) {
-    int st = tree_ok ? SSM_TREE_OK : SSM_TREE_E_TREE;
-    const int len = a.path_len[b];
-    if (st == SSM_TREE_OK) {
-      if (len < 0 || len > T) st = SSM_TREE_E_PATH;
-      for (int k = 0; st == SSM_TREE_OK && k < len; ++k) {
-        const int v = s_path[k];
-        if (v < 0 || v >= T || s_parent[v] != (k == 0 ? -1 : s_path[k - 1])) st = SSM_TREE_E_PATH;
-      }
+  // the path, one link per thread: path[0] is a root-level node and each
+  // later entry a child of the one before
+  const int plen = a.path_len[b];
+  int bad = 0;
+  if (tree_ok && plen >= 0 && plen <= T) {
+    for (int k = threadIdx.x; k < plen; k += blockDim.x) {
+      const int v = s_path[k];
+      bad |= (v < 0 || v >= T || s_parent[v] != (k == 0 ? -1 : s_path[k - 1]));
     }
-    s_misc[0] = st == SSM_TREE_OK ? len : 0;
-    s_misc[1] = st;
-    if (blockIdx.x == 0 && l == 0 && a.seq_status) a.seq_status[b] = st;
   }
-  __syncthreads();
-  if (s_misc[1] != SSM_TREE_OK) return;  // outputs of a failed sequence stay unwritten
-  const int len = s_misc[0];
+  const bool path_bad = __syncthreads_or(bad) != 0 || plen < 0 || plen > T;
+  const int st = !tree_ok ? SSM_TREE_E_TREE : (path_bad ? SSM_TREE_E_PATH : SSM_TREE_OK);
+  if (threadIdx.x == 0 && blockIdx.x == 0 && l == 0 && a.seq_status) a.seq_status[b] = st;
+  if (st != SSM_TREE_OK) return;  // outputs of a failed sequence stay unwritten
+  const int len = plen;
 
   // ---- per-path scalars, conv outputs, B rows ----
   const int HW = (c0 + kCommitRows - 1) / P - h_lo + 1;
@@ -90,9 +89,13 @@ __global__ void __launch_bounds__(kCommitThreads) commit_kernel(CommitArgs a, in
     const float z = load_in(dtr, (int64_t)s_path[k] * H + h) + a.prm.dt_bias[(int64_t)l * H + h];
     const float dt = softplus_f32(z);
     s_dA[k * HWMAX + hh] = expf(dt * a.prm.A[(int64_t)l * H + h]);
+    s_dtv[k * HWMAX + hh] = dt;
   }
   const int CH = d.CH;  // conv channels = window row length
   const TIn* xin = reinterpret_cast<const TIn*>(a.x) + unit * T * DI;
+  // the path nodes' raw x of the workgroup's channels, all loads in flight at once
+  for (int i = threadIdx.x; i < len * kCommitRows; i += blockDim.x)
+    s_dtx[i] = load_in(xin, (int64_t)s_path[i / kCommitRows] * DI + c0 + i % kCommitRows);
   const TIn* Bg = reinterpret_cast<const TIn*>(a.B) + (unit * T * d.G + g) * (int64_t)N;
   const TIn* win_in = reinterpret_cast<const TIn*>(a.window_in) + unit * (W - 1) * (int64_t)CH;
   for (int i = threadIdx.x; i < len * N; i += blockDim.x) {
@@ -114,8 +117,9 @@ __global__ void __launch_bounds__(kCommitThreads) commit_kernel(CommitArgs a, in
       s_B[k * N + n] = d.silu ? silu_f32(acc) : acc;
     }
   }
+  __syncthreads();  // the path's x rows and dt are in LDS
   if (threadIdx.x < kCommitRows) {
-    const int c = c0 + threadIdx.x, h = c / P;
+    const int c = c0 + threadIdx.x, hh = c / P - h_lo;
     // wj[jj] weighs conv input jj (0 = the token itself, jj = the jj-th previous token)
     float wj[4];
     const float* cw = a.prm.conv_w + ((int64_t)l * CH + c) * W;
@@ -138,15 +142,13 @@ __global__ void __launch_bounds__(kCommitThreads) commit_kernel(CommitArgs a, in
       }
     }
     for (int k = 0; k < len; ++k) {
-      const int v = s_path[k];
-      const float xv = load_in(xin, (int64_t)v * DI + c);
+      const float xv = s_dtx[k * kCommitRows + threadIdx.x];  // (this thread's own entry, rewritten below)
       float z = fmaf(wj[0], xv, cb);
 #pragma unroll
       for (int jj = 1; jj < 4; ++jj)
         if (jj < W) z = fmaf(wj[jj], hist[jj - 1], z);
       const float xt = d.silu ? silu_f32(z) : z;
-      const float zdt = load_in(dtr, (int64_t)v * H + h) + a.prm.dt_bias[(int64_t)l * H + h];
-      s_dtx[k * kCommitRows + threadIdx.x] = softplus_f32(zdt) * xt;
+      s_dtx[k * kCommitRows + threadIdx.x] = s_dtv[k * HWMAX + hh] * xt;
       hist[2] = hist[1];
       hist[1] = hist[0];
       hist[0] = xv;
@@ -258,7 +260,7 @@ template <typename TIn, typename TS, int QPT>
 static hipError_t launch_c(const CommitArgs& a, hipStream_t s) {
   const int HWMAX = ((kCommitRows + a.d.P - 1) / a.d.P + 1 + 3) & ~3;
   const size_t lds = sizeof(int32_t) * (2 * kMaxNodes + 4) +
-                     sizeof(float) * ((size_t)kMaxNodes * HWMAX + kMaxNodes * kCommitRows + (size_t)a.d.T * a.d.N);
+                     sizeof(float) * ((size_t)2 * kMaxNodes * HWMAX + kMaxNodes * kCommitRows + (size_t)a.d.T * a.d.N);
   dim3 grid(a.d.d_in / kCommitRows, a.d.Bsz, a.d.L);
   hipError_t e = allow_lds(commit_kernel<TIn, TS, QPT>, lds);
   if (e != hipSuccess) return e;
