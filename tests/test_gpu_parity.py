@@ -119,8 +119,11 @@ def test_plan_matches_oracle_exactly():
             assert np.array_equal(g[4:].reshape(T, 8), plan), (par.tolist(), W)
 
 
-def test_invalid_trees_flagged_and_isolated():
-    cfg = _small_cfg()
+@pytest.mark.parametrize("T,P", [(12, 64), (40, 64), (40, 32)], ids=["T12", "T40", "T40P32"])
+def test_invalid_trees_flagged_and_isolated(T, P):
+    """Up to 16 nodes and past 16 (the 17-64-node kernel, with M shared by
+    the workgroup's waves or formed per wave)."""
+    cfg = _small_cfg(T=T, P=P, H=4 if P == 64 else 8, cid=80 + T + P)
     inp = C.make_inputs(cfg)
     inp.parent[1, 3] = 5          # forward reference
     inp.parent[2, 0] = 0          # first node not attached to the root state
@@ -138,10 +141,11 @@ def test_invalid_trees_flagged_and_isolated():
     assert (s_out[:, 1:4] == -777.0).all(), "failed sequences must stay unwritten"
 
 
-def test_invalid_paths_flagged_and_untouched():
-    cfg = _small_cfg(tree="chain_or_star", Bsz=4)
+@pytest.mark.parametrize("T", [12, 40])
+def test_invalid_paths_flagged_and_untouched(T):
+    cfg = _small_cfg(tree="chain_or_star", Bsz=4, T=T, cid=80 + T)
     inp = C.make_inputs(cfg)
-    inp.path_len[:] = [3, 2, 3, 13]
+    inp.path_len[:] = [3, 2, 3, T + 1]
     inp.path[0, :3] = [0, 1, 2]            # valid chain prefix
     inp.path[1, :2] = [1, 2]               # star: starts below the root
     inp.path[2, :3] = [0, 2, 1]            # chain: broken link
