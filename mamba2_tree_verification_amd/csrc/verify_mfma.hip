@@ -323,20 +323,29 @@ __global__ void __launch_bounds__(WPG * 64) verify_mfma_kernel(VerifyArgs a, int
     int4 cq[4];  // every node's conv input rows, read at once
 #pragma unroll
     for (int q = 0; q < 4; ++q) cq[q] = *reinterpret_cast<const int4*>(s_cidx + 4 * q);
+    // tap reads without branches (every row holds an input or a clamped copy
+    // of one; unused taps and nodes past T are dropped by selects, never
+    // scaled by a zero weight), so that the reads need not wait one by one
     float xt[kTile];
+    const float bias = a.prm.conv_b ? wt[4] : 0.0f;
 #pragma unroll
     for (int v = 0; v < kTile; ++v) {
-      xt[v] = 0.0f;
-      if (v < T) {
-        const int ci = __builtin_amdgcn_readfirstlane(v % 4 == 0 ? cq[v / 4].x : v % 4 == 1 ? cq[v / 4].y
-                                                                  : v % 4 == 2 ? cq[v / 4].z : cq[v / 4].w);
-        float z = fmaf(wt[0], Pair<TIn>::get(s_xr, v * kSlab + lane), a.prm.conv_b ? wt[4] : 0.0f);
+      const int ci = __builtin_amdgcn_readfirstlane(v % 4 == 0 ? cq[v / 4].x : v % 4 == 1 ? cq[v / 4].y
+                                                                : v % 4 == 2 ? cq[v / 4].z : cq[v / 4].w);
+      float z = fmaf(wt[0], Pair<TIn>::get(s_xr, v * kSlab + lane), bias);
 #pragma unroll
-        for (int jj = 1; jj < 4; ++jj)
-          if (jj < W) z = fmaf(wt[jj], Pair<TIn>::get(s_xr, ((ci >> (8 * (jj - 1))) & 255) * kSlab + lane), z);
-        xt[v] = d.silu ? z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)) : z;
+      for (int jj = 1; jj < 4; ++jj) {
+        const float u = Pair<TIn>::get(s_xr, ((ci >> (8 * (jj - 1))) & 255) * kSlab + lane);
+        z = jj < W ? fmaf(wt[jj], u, z) : z;
       }
+      xt[v] = z;
     }
+    if (d.silu) {  // (a uniform branch: a select would run the transcendentals either way)
+#pragma unroll
+      for (int v = 0; v < kTile; ++v) xt[v] = xt[v] * __builtin_amdgcn_rcpf(1.0f + __expf(-xt[v]));
+    }
+#pragma unroll
+    for (int v = 0; v < kTile; ++v) xt[v] = v < T ? xt[v] : 0.0f;
     // S and dt of the slab's heads: lane (hl, v)
     {
       const int hl = lane >> 4, v = lane & 15;

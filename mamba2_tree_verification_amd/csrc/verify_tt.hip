@@ -42,6 +42,12 @@ constexpr int kTtMaxT = 64;
 // that the 16 rows a wave reads at once fall on different LDS banks
 constexpr int kPairStride = 20;
 __host__ __device__ constexpr int pair_of(int ti, int tj) { return ti * (ti + 1) / 2 + tj; }
+__host__ __device__ constexpr int pair_ti(int pi) {
+  int ti = 0;
+  while ((ti + 1) * (ti + 2) / 2 <= pi) ++ti;
+  return ti;
+}
+__host__ __device__ constexpr int pair_tj(int pi) { return pi - pair_of(pair_ti(pi), 0); }
 
 __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -179,25 +185,65 @@ __device__ __forceinline__ int xt_at(int c, int v) { return c * kTtMaxT + 4 * ((
 // M[v][u0 .. u0 + 3] of one head: exp(S_v - S_u) dt_u (C_v . B_u) where u is
 // on v's root path (ancestor bits ancv), zero elsewhere, plus D on the
 // diagonal; S in base-2 units, fp64 (the difference is taken before rounding)
+typedef double f64x2 __attribute__((ext_vector_type(2)));
+// the LDS inputs of one M quad, loaded apart from the arithmetic so that a
+// wave can have several quads' loads in flight
+struct MQuadIn {
+  double Sv;
+  f64x2 sa, sb;
+  f32x4 du, cb;
+  uint32_t nib;
+};
+__device__ __forceinline__ MQuadIn m_load(int v, int u0, const double* S2h, const float* dth, uint64_t ancv,
+                                          const float* cbr) {
+  MQuadIn q;
+  q.Sv = S2h[v];
+  q.du = *reinterpret_cast<const f32x4*>(dth + u0);
+  q.cb = *reinterpret_cast<const f32x4*>(cbr);
+  q.sa = *reinterpret_cast<const f64x2*>(S2h + u0);
+  q.sb = *reinterpret_cast<const f64x2*>(S2h + u0 + 2);
+  q.nib = (uint32_t)(ancv >> u0) & 15u;
+  return q;
+}
 template <bool kDiag>
-__device__ __forceinline__ f32x4 m_quad(int v, int u0, const double* S2h, const float* dth, uint64_t ancv,
-                                        const float* cbr, float Dh) {
-  typedef double f64x2 __attribute__((ext_vector_type(2)));
-  const double Sv = S2h[v];
-  const f32x4 du = *reinterpret_cast<const f32x4*>(dth + u0);
-  const f32x4 cb = *reinterpret_cast<const f32x4*>(cbr);
-  const f64x2 sa = *reinterpret_cast<const f64x2*>(S2h + u0);
-  const f64x2 sb = *reinterpret_cast<const f64x2*>(S2h + u0 + 2);
-  const uint32_t nib = (uint32_t)(ancv >> u0) & 15u;
+__device__ __forceinline__ f32x4 m_compute(const MQuadIn& q, int v, int u0, float Dh) {
   f32x4 m;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    const double su = t == 0 ? sa.x : (t == 1 ? sa.y : (t == 2 ? sb.x : sb.y));
-    const float e = __builtin_amdgcn_exp2f((float)(Sv - su)) * du[t] * cb[t];
-    const float mv = ((nib >> t) & 1) ? e : 0.0f;
+    const double su = t == 0 ? q.sa.x : (t == 1 ? q.sa.y : (t == 2 ? q.sb.x : q.sb.y));
+    const float e = __builtin_amdgcn_exp2f((float)(q.Sv - su)) * q.du[t] * q.cb[t];
+    const float mv = ((q.nib >> t) & 1) ? e : 0.0f;
     m[t] = kDiag && u0 + t == v ? mv + Dh : mv;
   }
   return m;
+}
+template <bool kDiag>
+__device__ __forceinline__ f32x4 m_quad(int v, int u0, const double* S2h, const float* dth, uint64_t ancv,
+                                        const float* cbr, float Dh) {
+  return m_compute<kDiag>(m_load(v, u0, S2h, dth, ancv, cbr), v, u0, Dh);
+}
+
+// M of the block's head for the tile pairs slot, slot + 4, ... (at most 3 for
+// 64 nodes): all loads first, then the arithmetic and the stores
+template <int TT, int kSlot>
+__device__ __forceinline__ void m_form_slot(float* s_m, const float* s_cbt, const uint64_t* s_anc,
+                                            const double* S2w, const float* dtw, float Dh0, int r, int cq) {
+  constexpr int kPairs = TT * (TT + 1) / 2;
+  constexpr int kMine = (kPairs - kSlot + 3) / 4;
+  MQuadIn in[kMine > 0 ? kMine : 1];
+#pragma unroll
+  for (int k = 0; k < kMine; ++k) {
+    const int pi = kSlot + 4 * k;
+    const int v = 16 * pair_ti(pi) + r, u0 = 16 * pair_tj(pi) + 4 * cq;
+    in[k] = m_load(v, u0, S2w, dtw, s_anc[v], s_cbt + (16 * pi + r) * kPairStride + 4 * cq);
+  }
+#pragma unroll
+  for (int k = 0; k < kMine; ++k) {
+    const int pi = kSlot + 4 * k;
+    const int v = 16 * pair_ti(pi) + r, u0 = 16 * pair_tj(pi) + 4 * cq;
+    *reinterpret_cast<f32x4*>(s_m + (16 * pi + r) * kPairStride + 4 * cq) =
+        pair_ti(pi) == pair_tj(pi) ? m_compute<true>(in[k], v, u0, Dh0) : m_compute<false>(in[k], v, u0, Dh0);
+  }
 }
 
 // LDS layout (byte offsets)
@@ -518,28 +564,43 @@ __global__ void __launch_bounds__(kTtThreads) verify_tt_kernel(VerifyArgs a, int
 #pragma unroll
       for (int t = 0; t < 4; ++t) wt[t] = s_cw[t * kTtRows + cl];
       const float cbv = s_cb[cl];
+      // every tap read of the wave's TT node quads is issued before any
+      // arithmetic or store (the stores could alias the reads as far as the
+      // compiler can tell, which would serialise quad after quad); unused
+      // taps (weight zero) and nodes past T read zeroed rows
+      u32x4 codes4[TT];
+#pragma unroll
+      for (int it = 0; it < TT; ++it) codes4[it] = *reinterpret_cast<const u32x4*>(s_cidx + 4 * (wq + kTtWaves * it));
+      float xs[TT][4][4];
 #pragma unroll
       for (int it = 0; it < TT; ++it) {
         const int q = wq + kTtWaves * it;
-        // all sixteen tap reads of the quad first, then the arithmetic:
-        // unused taps (weight zero) and nodes past T read zeroed rows
-        const u32x4 codes4 = *reinterpret_cast<const u32x4*>(s_cidx + 4 * q);
-        float xs[4][4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const uint32_t codes = __builtin_amdgcn_readfirstlane(codes4[r]);
-          xs[r][0] = load_in(s_xr, (4 * q + r) * kTtRows + cl);
+          const uint32_t codes = __builtin_amdgcn_readfirstlane(codes4[it][r]);
+          xs[it][r][0] = load_in(s_xr, (4 * q + r) * kTtRows + cl);
 #pragma unroll
-          for (int t = 1; t < 4; ++t) xs[r][t] = load_in(s_xw, ((codes >> (8 * (t - 1))) & 255) * kTtRows + cl);
+          for (int t = 1; t < 4; ++t)
+            xs[it][r][t] = load_in(s_xw, ((codes >> (8 * (t - 1))) & 255) * kTtRows + cl);
         }
+      }
+#pragma unroll
+      for (int it = 0; it < TT; ++it) {
+        const int q = wq + kTtWaves * it;
         f32x4 xq;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          float z = fmaf(wt[0], xs[r][0], cbv);
+          float z = fmaf(wt[0], xs[it][r][0], cbv);
 #pragma unroll
-          for (int t = 1; t < 4; ++t) z = fmaf(wt[t], xs[r][t], z);
-          xq[r] = 4 * q + r < T ? (d.silu ? silu_hw(z) : z) : 0.0f;
+          for (int t = 1; t < 4; ++t) z = fmaf(wt[t], xs[it][r][t], z);
+          xq[r] = z;
         }
+        if (d.silu) {  // (a uniform branch: a select would run the transcendentals either way)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) xq[r] = silu_hw(xq[r]);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) xq[r] = 4 * q + r < T ? xq[r] : 0.0f;
         *reinterpret_cast<f32x4*>(s_xt + cl * kTtMaxT + 4 * (q ^ (cl & 15))) = xq;
       }
     }
@@ -552,19 +613,12 @@ __global__ void __launch_bounds__(kTtThreads) verify_tt_kernel(VerifyArgs a, int
       const double* S2w = s_S2 + blk * kTtMaxT;
       const float* dtw = s_dt + blk * kTtMaxT;
       const float Dh0 = s_D[blk];
-#pragma unroll
-      for (int ti = 0; ti < TT; ++ti) {
-#pragma unroll
-        for (int tj = 0; tj <= ti; ++tj) {
-          const int pi = pair_of(ti, tj);
-          if (pi % kTtWaves == slot) {  // tile pairs dealt round the waves
-            const int v = 16 * ti + r, u0 = 16 * tj + 4 * cq;
-            const float* cbr = s_cbt + (16 * pi + r) * kPairStride + 4 * cq;
-            *reinterpret_cast<f32x4*>(s_m + (16 * pi + r) * kPairStride + 4 * cq) =
-                ti == tj ? m_quad<true>(v, u0, S2w, dtw, s_anc[v], cbr, Dh0)
-                         : m_quad<false>(v, u0, S2w, dtw, s_anc[v], cbr, Dh0);
-          }
-        }
+      // tile pairs dealt round the waves, each wave's list fixed at compile time
+      switch (slot) {
+        case 0: m_form_slot<TT, 0>(s_m, s_cbt, s_anc, S2w, dtw, Dh0, r, cq); break;
+        case 1: m_form_slot<TT, 1>(s_m, s_cbt, s_anc, S2w, dtw, Dh0, r, cq); break;
+        case 2: m_form_slot<TT, 2>(s_m, s_cbt, s_anc, S2w, dtw, Dh0, r, cq); break;
+        default: m_form_slot<TT, 3>(s_m, s_cbt, s_anc, S2w, dtw, Dh0, r, cq); break;
       }
     }
     __syncthreads();  // conv outputs and M are complete; x rows, conv parameters and dt A are free
