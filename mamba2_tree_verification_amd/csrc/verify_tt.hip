@@ -728,7 +728,451 @@ __global__ void __launch_bounds__(kTtThreads) verify_tt_kernel(VerifyArgs a, int
   }
 }
 
+// ---------------------------------------------------------------------------
+// The same verify with the waves split by role, for blocks that lie in one
+// head (P a multiple of 64) and at least 8 blocks per workgroup.  Waves 0-3
+// (producers) run the vector work of block ph: the conv and M, then deliver
+// block ph + 1's inputs and prefetch block ph + 2's.  Waves 4-7 (consumers)
+// run the matrix work: C . h0 of block ph, then the path terms and y of
+// block ph - 1.  Conv outputs, M, the x rows and the conv parameters are
+// double-buffered by block parity, so one barrier per phase separates
+// writers from readers, and each SIMD holds one wave of each role whose
+// vector and matrix instructions overlap.
+// ---------------------------------------------------------------------------
+
 namespace {
+
+constexpr int kWsWaves = 8;
+constexpr int kWsThreads = kWsWaves * kWave;
+constexpr int kWsMaxBlk = 16;
+
+struct TtWsLds {
+  int parent, anc, cidx, misc, C, cbt, X, Y, Mo, S2, Ah, dt, D, cw, cb, total, row, xbuf, ybuf, mbuf, cwbuf;
+  __host__ __device__ TtWsLds(int N, int E, int TT) {
+    const int KT = 16 * TT, pair_bytes = 4 * 16 * kPairStride * pair_of(TT, 0);
+    int o = 0;
+    row = N * E + 16;
+    parent = o; o += 4 * kTtMaxT;
+    anc = o; o += 8 * kTtMaxT;
+    cidx = o; o += 4 * kTtMaxT;
+    misc = o; o += 16;
+    C = o; o += KT * row;
+    cbt = o; o += pair_bytes;
+    // two conv-output buffers [channel][node]; the B rows (KT rows) sit here
+    // until the C . B dots exist
+    xbuf = 4 * kTtRows * kTtMaxT;
+    X = o; o += 2 * xbuf > KT * row ? 2 * xbuf : KT * row;
+    ybuf = ((3 + KT) * kTtRows * E + 15) / 16 * 16;  // window and x rows, raw
+    Y = o; o += 2 * ybuf;
+    mbuf = pair_bytes;
+    Mo = o; o += 2 * mbuf;
+    S2 = o; o += 8 * kWsMaxBlk * kTtMaxT;   // [block][node] fp64
+    Ah = o; o += 4 * kWsMaxBlk * kTtMaxT;   // [block][node]
+    dt = o; o += 4 * kWsMaxBlk * kTtMaxT;   // [block][node]
+    D = o; o += 4 * kWsMaxBlk;
+    cwbuf = 4 * 4 * kTtRows;
+    cw = o; o += 2 * cwbuf;                  // [parity][tap][channel]
+    cb = o; o += 2 * 4 * kTtRows;            // [parity][channel]
+    total = o;
+  }
+};
+
+}  // namespace
+
+template <typename TIn, typename TS, int NG, int TT>
+__global__ void __launch_bounds__(kWsThreads) verify_tt_ws_kernel(VerifyArgs a, int NBLK) {
+  typedef StateQuad<TS> SQ;
+  constexpr int N = 16 * NG;
+  constexpr int E = (int)sizeof(TIn);
+  constexpr int KT = 16 * TT;
+  typedef typename Raw4<E>::T RawQ;
+  constexpr int kChunks = N * E / 16;
+  const Dims d = a.d;
+  const int T = d.T, P = d.P, H = d.H, W = d.W, DI = d.d_in, G = d.G, CH = d.CH;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const bool producer = wave < 4;
+  const int rw = wave & 3;  // the wave's index within its role
+  const int j = lane & 15, k = lane >> 4;
+  const int b = blockIdx.y, l = blockIdx.z;
+  const int64_t unit = (int64_t)l * d.Bsz + b;
+  const int cw0 = blockIdx.x * NBLK * kTtRows;
+  const int g = cw0 / (DI / G);
+
+  extern __shared__ __align__(16) unsigned char smem[];
+  const TtWsLds lo(N, E, TT);
+  int32_t* s_parent = reinterpret_cast<int32_t*>(smem + lo.parent);
+  uint64_t* s_anc = reinterpret_cast<uint64_t*>(smem + lo.anc);
+  int32_t* s_cidx = reinterpret_cast<int32_t*>(smem + lo.cidx);
+  int32_t* s_misc = reinterpret_cast<int32_t*>(smem + lo.misc);
+  unsigned char* s_C = smem + lo.C;
+  float* s_cbt = reinterpret_cast<float*>(smem + lo.cbt);
+  unsigned char* s_B = smem + lo.X;
+  double* s_S2 = reinterpret_cast<double*>(smem + lo.S2);
+  float* s_Ah = reinterpret_cast<float*>(smem + lo.Ah);
+  float* s_dt = reinterpret_cast<float*>(smem + lo.dt);
+  float* s_D = reinterpret_cast<float*>(smem + lo.D);
+  const int rs = lo.row;
+  auto s_xt = [&](int par) { return reinterpret_cast<float*>(smem + lo.X + par * lo.xbuf); };
+  auto s_xw = [&](int par) { return reinterpret_cast<TIn*>(smem + lo.Y + par * lo.ybuf); };
+  auto s_m = [&](int par) { return reinterpret_cast<float*>(smem + lo.Mo + par * lo.mbuf); };
+  auto s_cw = [&](int par) { return reinterpret_cast<float*>(smem + lo.cw + par * lo.cwbuf); };
+  auto s_cb = [&](int par) { return reinterpret_cast<float*>(smem + lo.cb + par * 4 * kTtRows); };
+
+  // ---- consumers: the first block's state, in flight during the prologue ----
+  typename SQ::Raw hq[NG];
+  if (!producer) {
+    const TS* sin = reinterpret_cast<const TS*>(a.state) + (unit * DI + cw0 + rw * 16 + j) * (int64_t)N + 4 * k;
+#pragma unroll
+    for (int gg = 0; gg < NG; ++gg) hq[gg] = SQ::load(sin + 16 * gg);
+  }
+
+  // ---- tree prologue (all waves): parent[], C and B rows ----
+  if (tid < kTtMaxT) s_parent[tid] = tid < T ? a.parent[(int64_t)b * T + tid] : 0;
+  const unsigned char* Cg = reinterpret_cast<const unsigned char*>(a.C) + ((unit * T) * G + g) * (int64_t)N * E;
+  const unsigned char* Bg = reinterpret_cast<const unsigned char*>(a.B) + ((unit * T) * G + g) * (int64_t)N * E;
+  for (int ci = tid; ci < KT * kChunks; ci += kWsThreads) {
+    const int v = ci / kChunks, q = ci % kChunks;
+    u32x4 c4 = u32x4{0u, 0u, 0u, 0u}, b4 = c4;
+    if (v < T) {
+      c4 = *reinterpret_cast<const u32x4*>(Cg + (int64_t)v * G * N * E + q * 16);
+      b4 = *reinterpret_cast<const u32x4*>(Bg + (int64_t)v * G * N * E + q * 16);
+    }
+    *reinterpret_cast<u32x4*>(s_C + v * rs + q * 16) = c4;
+    *reinterpret_cast<u32x4*>(s_B + v * rs + q * 16) = b4;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    // validation by ballot, root-path sets and conv tap rows, as in
+    // verify_tt_kernel
+    bool bad = false;
+    if (lane < T) {
+      const int p = s_parent[lane];
+      bad = lane == 0 ? p != -1 : (p < -1 || p >= lane || p < s_parent[lane - 1]);
+    }
+    const bool ok = __ballot(bad) == 0;
+    uint64_t m = 0;
+    int packed = 0;
+    if (lane < T) {
+      int u = lane, a1 = -1, a2 = -1, a3 = -1, depth = 0;
+      for (int s = 0; s < kTtMaxT && u >= 0; ++s) {
+        m |= 1ull << u;
+        ++depth;
+        const int p = s_parent[u];
+        u = (p >= 0 && p < u) ? p : -1;
+        a1 = s == 0 ? u : a1;
+        a2 = s == 1 ? u : a2;
+        a3 = s == 2 ? u : a3;
+      }
+#pragma unroll
+      for (int jj = 1; jj < 4; ++jj) {
+        const int an = jj == 1 ? a1 : (jj == 2 ? a2 : a3);
+        const int code = an >= 0 ? an + 3 : 2 - (jj - depth);
+        if (jj < W) packed |= code << (8 * (jj - 1));
+      }
+    }
+    s_anc[lane] = m;
+    s_cidx[lane] = packed;
+    if (lane == 0) {
+      s_misc[0] = ok ? 1 : 0;
+      if (blockIdx.x == 0 && l == 0 && a.seq_status) a.seq_status[b] = ok ? SSM_TREE_OK : SSM_TREE_E_TREE;
+    }
+  }
+  // C_v . B_u over the lower-triangular tile pairs (eight waves)
+  for (int pi = wave; pi < TT * (TT + 1) / 2; pi += kWsWaves) {
+    const int ti = pair_ti(pi), tj = pair_tj(pi);
+    f32x4 cb = f32x4{0.f, 0.f, 0.f, 0.f};
+    const TIn* brow = reinterpret_cast<const TIn*>(s_B + (16 * tj + j) * rs) + 4 * k;
+    const TIn* crow = reinterpret_cast<const TIn*>(s_C + (16 * ti + j) * rs) + 4 * k;
+    if constexpr (E == 2) {
+#pragma unroll
+      for (int m = 0; m < (NG + 1) / 2; ++m) {
+        const u32x2 b0 = *reinterpret_cast<const u32x2*>(brow + 32 * m);
+        const u32x2 c0 = *reinterpret_cast<const u32x2*>(crow + 32 * m);
+        u32x2 b1 = u32x2{0u, 0u}, c1 = b1;
+        if (2 * m + 1 < NG) {
+          b1 = *reinterpret_cast<const u32x2*>(brow + 32 * m + 16);
+          c1 = *reinterpret_cast<const u32x2*>(crow + 32 * m + 16);
+        }
+        cb = mfma32(u32x4{b0.x, b0.y, b1.x, b1.y}, u32x4{c0.x, c0.y, c1.x, c1.y}, cb);
+      }
+    } else {
+#pragma unroll
+      for (int gg = 0; gg < NG; ++gg) {
+        const f32x4 bq = load4<TIn>(brow + 16 * gg);
+        const f32x4 cq = load4<TIn>(crow + 16 * gg);
+        cb = mfma4(bq.x, cq.x, cb);
+        cb = mfma4(bq.y, cq.y, cb);
+        cb = mfma4(bq.z, cq.z, cb);
+        cb = mfma4(bq.w, cq.w, cb);
+      }
+    }
+    *reinterpret_cast<f32x4*>(s_cbt + (16 * pi + j) * kPairStride + 4 * k) = cb;
+  }
+  __syncthreads();  // the B rows are dead: their space holds the conv outputs
+  const bool tree_ok = s_misc[0] != 0;
+
+  const TIn* xg = reinterpret_cast<const TIn*>(a.x) + unit * T * (int64_t)DI;
+  const TIn* wg = reinterpret_cast<const TIn*>(a.window) + unit * (W - 1) * (int64_t)CH;
+  const TIn* dtg = reinterpret_cast<const TIn*>(a.dt_raw) + unit * T * (int64_t)H;
+  // each block's head: dt, S (fp64) and exp(S), wave = block, lane = node
+  for (int bw = wave; bw < NBLK; bw += kWsWaves) {
+    const int v = lane;
+    const int h = (cw0 + bw * kTtRows) / P;
+    float dtv = 0.0f;
+    if (v < T) dtv = softplus_hw(load_in(dtg, (int64_t)v * H + h) + a.prm.dt_bias[(int64_t)l * H + h]);
+    int up = v < T ? s_parent[v] : -1;
+    up = (up >= 0 && up < v) ? up : -1;
+    const double s2 = root_path_sum((double)(dtv * a.prm.A[(int64_t)l * H + h]), up, v) * 1.4426950408889634;
+    s_dt[bw * kTtMaxT + v] = dtv;
+    s_S2[bw * kTtMaxT + v] = s2;
+    s_Ah[bw * kTtMaxT + v] = __builtin_amdgcn_exp2f((float)s2);
+    if (v == 0) s_D[bw] = a.prm.D[(int64_t)l * H + h];
+  }
+
+  // ---- producers' per-block inputs, a block ahead in registers ----
+  constexpr int kXQ = (KT * (kTtRows / 4) + kTtThreads - 1) / kTtThreads;  // (256 producer threads)
+  RawQ pxr[kXQ];
+  uint32_t pwin[3] = {0u, 0u, 0u};
+  float pcw[4] = {0.f, 0.f, 0.f, 0.f}, pcb = 0.f;
+  auto prefetch = [&](int blk) {
+    const int ptid = opaque_tid();  // < 256
+    const int c0 = cw0 + blk * kTtRows;
+#pragma unroll
+    for (int it = 0; it < kXQ; ++it) {
+      const int qi = ptid + it * kTtThreads;
+      const int v = qi / (kTtRows / 4), c4 = (qi % (kTtRows / 4)) * 4;
+      const int vr = v < T ? v : T - 1;  // rows past T repeat row T - 1 (never a tap source)
+      pxr[it] = *reinterpret_cast<const RawQ*>(xg + (int64_t)vr * DI + c0 + c4);
+    }
+    if (ptid < kTtRows) {
+      const int c = c0 + ptid;
+#pragma unroll
+      for (int r = 0; r < 3; ++r)
+        if (r < W - 1) pwin[r] = raw_bits<TIn>(wg + (int64_t)r * CH + c);
+      const float* cwp = a.prm.conv_w + ((int64_t)l * CH + c) * W;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        if (t < W) pcw[t] = cwp[W - 1 - t];
+      if (a.prm.conv_b) pcb = a.prm.conv_b[(int64_t)l * CH + c];
+    }
+  };
+  auto deliver = [&](int blk) {
+    const int ptid = opaque_tid();
+    const int par = blk & 1;
+    TIn* xw = s_xw(par);
+    TIn* xr = xw + 3 * kTtRows;
+#pragma unroll
+    for (int it = 0; it < kXQ; ++it) {
+      const int qi = ptid + it * kTtThreads;
+      const int v = qi / (kTtRows / 4), c4 = (qi % (kTtRows / 4)) * 4;
+      if (qi < KT * (kTtRows / 4)) *reinterpret_cast<RawQ*>(xr + v * kTtRows + c4) = pxr[it];
+    }
+    if (ptid < kTtRows) {
+#pragma unroll
+      for (int r = 0; r < 3; ++r)
+        if (r < W - 1) xw[(4 - W + r) * kTtRows + ptid] = from_bits<TIn>(pwin[r]);
+#pragma unroll
+      for (int r = 0; r < 3; ++r)
+        if (r < 4 - W) xw[r * kTtRows + ptid] = from_bits<TIn>(0u);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) s_cw(par)[t * kTtRows + ptid] = pcw[t];
+      s_cb(par)[ptid] = pcb;
+    }
+  };
+  if (producer) {
+    prefetch(0);
+    deliver(0);
+    if (NBLK > 1) prefetch(1);
+  }
+  f32x4 accp[TT];  // consumers: the previous block's C . h0
+#pragma unroll
+  for (int ti = 0; ti < TT; ++ti) accp[ti] = f32x4{0.f, 0.f, 0.f, 0.f};
+  __syncthreads();
+
+  for (int ph = 0; ph <= NBLK; ++ph) {
+    if (producer) {
+      if (ph < NBLK) {
+        const int par = ph & 1;
+        // ---- conv of block ph (lane = channel, wave = node quads) ----
+        {
+          const int ptid = opaque_tid();
+          const int cl = ptid & (kWave - 1);
+          const TIn* xw = s_xw(par);
+          const TIn* xr = xw + 3 * kTtRows;
+          float wt[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) wt[t] = s_cw(par)[t * kTtRows + cl];
+          const float cbv = s_cb(par)[cl];
+          u32x4 codes4[TT];
+#pragma unroll
+          for (int it = 0; it < TT; ++it)
+            codes4[it] = *reinterpret_cast<const u32x4*>(s_cidx + 4 * (rw + kTtWaves * it));
+          float xs[TT][4][4];
+#pragma unroll
+          for (int it = 0; it < TT; ++it) {
+            const int q = rw + kTtWaves * it;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const uint32_t codes = __builtin_amdgcn_readfirstlane(codes4[it][r]);
+              xs[it][r][0] = load_in(xr, (4 * q + r) * kTtRows + cl);
+#pragma unroll
+              for (int t = 1; t < 4; ++t)
+                xs[it][r][t] = load_in(xw, ((codes >> (8 * (t - 1))) & 255) * kTtRows + cl);
+            }
+          }
+          float* xt = s_xt(par);
+#pragma unroll
+          for (int it = 0; it < TT; ++it) {
+            const int q = rw + kTtWaves * it;
+            f32x4 xq;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              float z = fmaf(wt[0], xs[it][r][0], cbv);
+#pragma unroll
+              for (int t = 1; t < 4; ++t) z = fmaf(wt[t], xs[it][r][t], z);
+              xq[r] = z;
+            }
+            if (d.silu) {
+#pragma unroll
+              for (int r = 0; r < 4; ++r) xq[r] = silu_hw(xq[r]);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) xq[r] = 4 * q + r < T ? xq[r] : 0.0f;
+            *reinterpret_cast<f32x4*>(xt + cl * kTtMaxT + 4 * (q ^ (cl & 15))) = xq;
+          }
+        }
+        // ---- M of block ph ----
+        {
+          const int ptid = opaque_tid();
+          const int r = (ptid >> 2) & 15, cq = ptid & 3;
+          const double* S2w = s_S2 + ph * kTtMaxT;
+          const float* dtw = s_dt + ph * kTtMaxT;
+          const float Dh0 = s_D[ph];
+          float* mm = s_m(par);
+          switch (rw) {
+            case 0: m_form_slot<TT, 0>(mm, s_cbt, s_anc, S2w, dtw, Dh0, r, cq); break;
+            case 1: m_form_slot<TT, 1>(mm, s_cbt, s_anc, S2w, dtw, Dh0, r, cq); break;
+            case 2: m_form_slot<TT, 2>(mm, s_cbt, s_anc, S2w, dtw, Dh0, r, cq); break;
+            default: m_form_slot<TT, 3>(mm, s_cbt, s_anc, S2w, dtw, Dh0, r, cq); break;
+          }
+        }
+      }
+      if (ph + 1 < NBLK) deliver(ph + 1);
+      if (ph + 2 < NBLK) prefetch(ph + 2);
+    } else {
+      // ---- C . h0 of block ph first (its state arrived a phase ago) ----
+      f32x4 acc[TT];
+#pragma unroll
+      for (int ti = 0; ti < TT; ++ti) acc[ti] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (ph < NBLK) {
+        const int ln = opaque_tid() & (kWave - 1), jj = ln & 15, kk = ln >> 4;
+        const int c0 = cw0 + ph * kTtRows;
+        const bool more = ph + 1 < NBLK;
+        const TS* nsin =
+            reinterpret_cast<const TS*>(a.state) + (unit * DI + c0 + kTtRows + rw * 16 + jj) * (int64_t)N + 4 * kk;
+        if constexpr (E == 2) {
+#pragma unroll
+          for (int m = 0; m < (NG + 1) / 2; ++m) {
+            const bool two = 2 * m + 1 < NG;
+            u32x4 h0, h1, h2;
+            if constexpr (sizeof(TS) == 2) {
+              const u32x2 lo2 = hq[2 * m], hi2 = two ? hq[2 * m + 1] : u32x2{0u, 0u};
+              h0 = u32x4{lo2.x, lo2.y, hi2.x, hi2.y};
+            } else {
+              split3(hq[2 * m], two ? hq[2 * m + 1] : f32x4{0.f, 0.f, 0.f, 0.f}, h0, h1, h2);
+            }
+#pragma unroll
+            for (int ti = 0; ti < TT; ++ti) {
+              const TIn* crow = reinterpret_cast<const TIn*>(s_C + (16 * ti + jj) * rs) + 32 * m + 4 * kk;
+              const u32x2 c0q = *reinterpret_cast<const u32x2*>(crow);
+              const u32x2 c1q = two ? *reinterpret_cast<const u32x2*>(crow + 16) : u32x2{0u, 0u};
+              const u32x4 ca = u32x4{c0q.x, c0q.y, c1q.x, c1q.y};
+              if constexpr (sizeof(TS) != 2) {
+                acc[ti] = mfma32(ca, h2, acc[ti]);
+                acc[ti] = mfma32(ca, h1, acc[ti]);
+              }
+              acc[ti] = mfma32(ca, h0, acc[ti]);
+            }
+            if (more) {
+              hq[2 * m] = SQ::load(nsin + 32 * m);
+              if (two) hq[2 * m + 1] = SQ::load(nsin + 32 * m + 16);
+            }
+            asm volatile("" ::: "memory");
+          }
+        } else {
+#pragma unroll
+          for (int gg = 0; gg < NG; ++gg) {
+            const f32x4 h = SQ::to_f32(hq[gg]);
+#pragma unroll
+            for (int ti = 0; ti < TT; ++ti) {
+              const f32x4 cq =
+                  load4<TIn>(reinterpret_cast<const TIn*>(s_C + (16 * ti + jj) * rs) + 16 * gg + 4 * kk);
+              acc[ti] = mfma4(cq.x, h.x, acc[ti]);
+              acc[ti] = mfma4(cq.y, h.y, acc[ti]);
+              acc[ti] = mfma4(cq.z, h.z, acc[ti]);
+              acc[ti] = mfma4(cq.w, h.w, acc[ti]);
+            }
+            if (more) hq[gg] = SQ::load(nsin + 16 * gg);
+            asm volatile("" ::: "memory");
+          }
+        }
+      }
+      // ---- path terms and y of block ph - 1 ----
+      if (ph >= 1) {
+        const int pb = ph - 1, par = pb & 1;
+        const int ln = opaque_tid() & (kWave - 1), jj = ln & 15, kk = ln >> 4;
+        const int c0 = cw0 + pb * kTtRows;
+        const int row = rw * 16 + jj;
+        const float* Ahh = s_Ah + pb * kTtMaxT;
+        const float* xt = s_xt(par);
+        const float* mm = s_m(par);
+        float* yrow = a.y + unit * T * (int64_t)DI + c0 + row;
+        // column tile outermost: one x~ quad per tj serves every node tile
+        // ti >= tj, and the TT accumulators are independent product chains
+        f32x4 y[TT];
+#pragma unroll
+        for (int ti = 0; ti < TT; ++ti) y[ti] = *reinterpret_cast<const f32x4*>(Ahh + 16 * ti + 4 * kk) * accp[ti];
+#pragma unroll
+        for (int tj = 0; tj < TT; ++tj) {
+          const f32x4 xq = *reinterpret_cast<const f32x4*>(xt + row * kTtMaxT + 4 * ((4 * tj + kk) ^ (row & 15)));
+#pragma unroll
+          for (int ti = tj; ti < TT; ++ti) {
+            const f32x4 mop = *reinterpret_cast<const f32x4*>(mm + (16 * pair_of(ti, tj) + jj) * kPairStride + 4 * kk);
+            y[ti] = mfma4(mop.x, xq.x, y[ti]);
+            y[ti] = mfma4(mop.y, xq.y, y[ti]);
+            y[ti] = mfma4(mop.z, xq.z, y[ti]);
+            y[ti] = mfma4(mop.w, xq.w, y[ti]);
+          }
+          asm volatile("" ::: "memory");  // one column tile's operands at a time
+        }
+        // lane (c + 16 k) holds nodes 16 ti + 4 k + r of channel row
+#pragma unroll
+        for (int ti = 0; ti < TT; ++ti)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int v = 16 * ti + 4 * kk + r;
+            if (v < T) yrow[(int64_t)v * DI] = tree_ok ? y[ti][r] : __builtin_nanf("");
+          }
+      }
+#pragma unroll
+      for (int ti = 0; ti < TT; ++ti) accp[ti] = acc[ti];
+    }
+    __syncthreads();
+  }
+}
+
+namespace {
+
+template <typename TIn, typename TS, int NG, int TT>
+int launch_ws_t(const VerifyArgs& a, int nblk, hipStream_t s) {
+  const size_t lds = (size_t)TtWsLds(16 * NG, (int)sizeof(TIn), TT).total;
+  if (lds > 160 * 1024) return SSM_TREE_E_DIMS;
+  if (allow_lds(verify_tt_ws_kernel<TIn, TS, NG, TT>, lds) != hipSuccess) return SSM_TREE_E_HIP;
+  dim3 grid(a.d.d_in / (nblk * kTtRows), a.d.Bsz, a.d.L);
+  hipLaunchKernelGGL((verify_tt_ws_kernel<TIn, TS, NG, TT>), grid, dim3(kWsThreads), lds, s, a, nblk);
+  return hipGetLastError() == hipSuccess ? SSM_TREE_OK : SSM_TREE_E_HIP;
+}
 
 template <typename TIn, typename TS, int NG, int TT>
 int launch_tt_t(const VerifyArgs& a, hipStream_t s) {
@@ -742,12 +1186,24 @@ int launch_tt_t(const VerifyArgs& a, hipStream_t s) {
   return hipGetLastError() == hipSuccess ? SSM_TREE_OK : SSM_TREE_E_HIP;
 }
 
+// the role-split kernel where each block lies in one head and a workgroup
+// can take 8 or 16 blocks (else the per-block kernel)
+template <typename TIn, typename TS, int NG, int TT>
+int launch_tt_pick(const VerifyArgs& a, hipStream_t s) {
+  const int blocks = a.d.d_in / a.d.G / kTtRows;
+  if (a.d.P % kTtRows == 0 && blocks % 8 == 0) {
+    const int st = launch_ws_t<TIn, TS, NG, TT>(a, blocks % kWsMaxBlk == 0 ? kWsMaxBlk : 8, s);
+    if (st != SSM_TREE_E_DIMS) return st;  // E_DIMS: its LDS does not fit, nothing launched
+  }
+  return launch_tt_t<TIn, TS, NG, TT>(a, s);
+}
+
 template <typename TIn, typename TS, int NG>
 int launch_tt_g(const VerifyArgs& a, hipStream_t s) {
   const int T = a.d.T;
-  if (T <= 32) return launch_tt_t<TIn, TS, NG, 2>(a, s);
-  if (T <= 48) return launch_tt_t<TIn, TS, NG, 3>(a, s);
-  return launch_tt_t<TIn, TS, NG, 4>(a, s);
+  if (T <= 32) return launch_tt_pick<TIn, TS, NG, 2>(a, s);
+  if (T <= 48) return launch_tt_pick<TIn, TS, NG, 3>(a, s);
+  return launch_tt_pick<TIn, TS, NG, 4>(a, s);
 }
 
 template <typename TIn, typename TS>

@@ -71,6 +71,13 @@ SMALL = [
     (2, 2, 50, 8, 32, 32, 2, 3, True, True, True, "forest"),
     # fp32 inputs, chain and star trees of 33 nodes, silu
     (1, 2, 33, 4, 64, 128, 1, 4, False, True, False, "chain_or_star"),
+    # 17-64 nodes with 8 or 16 one-head blocks per B/C group (the role-split
+    # kernel): 8 blocks; 16 blocks with chains and stars and silu; fp32
+    # inputs with bias; two groups of 8 blocks
+    (1, 2, 40, 8, 64, 128, 1, 4, True, False, False, "forest"),
+    (1, 2, 64, 16, 64, 64, 1, 4, True, True, False, "chain_or_star"),
+    (1, 2, 33, 8, 64, 64, 1, 3, False, False, True, "forest"),
+    (1, 2, 24, 16, 64, 32, 2, 4, True, False, False, "forest"),
 ]
 
 

@@ -45,6 +45,7 @@ VERIFY_SPECS = [
     (2, 2, 64, 2, 64, 128, 1, 4, True, True, "chain_or_star"),
     (1, 2, 33, 4, 64, 128, 1, 4, False, False, "forest"),      # 17-64 nodes, fp32 inputs
     (1, 3, 20, 8, 16, 16, 1, 4, True, True, "forest"),         # heads of 16 channels
+    (1, 2, 48, 8, 64, 128, 1, 4, True, False, "forest"),       # 8 one-head blocks: the role-split kernel
 ]
 COMMIT_SPECS = VERIFY_SPECS + [
     (1, 3, 12, 8, 40, 32, 1, 4, True, False, "forest"),        # headdim 40: commit takes every shape
