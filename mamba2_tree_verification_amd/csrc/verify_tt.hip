@@ -985,6 +985,26 @@ __global__ void __launch_bounds__(kWsThreads) verify_tt_ws_kernel(VerifyArgs a, 
     deliver(0);
     if (NBLK > 1) prefetch(1);
   }
+  // consumers with bf16 inputs and d_state <= 128: the C operands of every
+  // node tile and column group pair stay in registers for all the
+  // workgroup's blocks (wider states read them from LDS per block)
+  constexpr bool kCReg = E == 2 && NG <= 8;
+  constexpr int kCM = kCReg ? (NG + 1) / 2 : 1;
+  u32x4 creg[kCReg ? TT : 1][kCM];
+  if constexpr (kCReg) {
+    if (!producer) {
+      const int ln = opaque_tid() & (kWave - 1), jj = ln & 15, kk = ln >> 4;
+#pragma unroll
+      for (int ti = 0; ti < TT; ++ti)
+#pragma unroll
+        for (int m = 0; m < kCM; ++m) {
+          const TIn* crow = reinterpret_cast<const TIn*>(s_C + (16 * ti + jj) * rs) + 32 * m + 4 * kk;
+          const u32x2 c0q = *reinterpret_cast<const u32x2*>(crow);
+          const u32x2 c1q = 2 * m + 1 < NG ? *reinterpret_cast<const u32x2*>(crow + 16) : u32x2{0u, 0u};
+          creg[ti][m] = u32x4{c0q.x, c0q.y, c1q.x, c1q.y};
+        }
+    }
+  }
   f32x4 accp[TT];  // consumers: the previous block's C . h0
 #pragma unroll
   for (int ti = 0; ti < TT; ++ti) accp[ti] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1084,10 +1104,15 @@ __global__ void __launch_bounds__(kWsThreads) verify_tt_ws_kernel(VerifyArgs a, 
             }
 #pragma unroll
             for (int ti = 0; ti < TT; ++ti) {
-              const TIn* crow = reinterpret_cast<const TIn*>(s_C + (16 * ti + jj) * rs) + 32 * m + 4 * kk;
-              const u32x2 c0q = *reinterpret_cast<const u32x2*>(crow);
-              const u32x2 c1q = two ? *reinterpret_cast<const u32x2*>(crow + 16) : u32x2{0u, 0u};
-              const u32x4 ca = u32x4{c0q.x, c0q.y, c1q.x, c1q.y};
+              u32x4 ca;
+              if constexpr (kCReg) {
+                ca = creg[ti][m];
+              } else {
+                const TIn* crow = reinterpret_cast<const TIn*>(s_C + (16 * ti + jj) * rs) + 32 * m + 4 * kk;
+                const u32x2 c0q = *reinterpret_cast<const u32x2*>(crow);
+                const u32x2 c1q = two ? *reinterpret_cast<const u32x2*>(crow + 16) : u32x2{0u, 0u};
+                ca = u32x4{c0q.x, c0q.y, c1q.x, c1q.y};
+              }
               if constexpr (sizeof(TS) != 2) {
                 acc[ti] = mfma32(ca, h2, acc[ti]);
                 acc[ti] = mfma32(ca, h1, acc[ti]);
