@@ -114,7 +114,7 @@ __global__ void __launch_bounds__(kCommitThreads) commit_kernel(CommitArgs a, in
                                    : load_in(Bg + (int64_t)s_path[e - (W - 1)] * d.G * N, n);
         acc = fmaf(cw[W - 1 - j], in, acc);
       }
-      s_B[k * N + n] = d.silu ? silu_f32(acc) : acc;
+      s_B[k * N + n] = d.silu ? silu_fast(acc) : acc;
     }
   }
   __syncthreads();  // the path's x rows and dt are in LDS
@@ -147,7 +147,7 @@ __global__ void __launch_bounds__(kCommitThreads) commit_kernel(CommitArgs a, in
 #pragma unroll
       for (int jj = 1; jj < 4; ++jj)
         if (jj < W) z = fmaf(wj[jj], hist[jj - 1], z);
-      const float xt = d.silu ? silu_f32(z) : z;
+      const float xt = d.silu ? silu_fast(z) : z;
       s_dtx[k * kCommitRows + threadIdx.x] = s_dtv[k * HWMAX + hh] * xt;
       hist[2] = hist[1];
       hist[1] = hist[0];

@@ -463,7 +463,7 @@ __global__ void __launch_bounds__(kCvWaves * kWave) commit_verify_kernel(CommitV
 #pragma unroll
       for (int jj = 1; jj < 4; ++jj)
         if (jj < W) z = fmaf(wj[jj], hist[jj - 1], z);
-      const float xt = d.silu ? silu_f32(z) : z;
+      const float xt = d.silu ? silu_fast(z) : z;
       s_dtx[q * kCvRows + lane] = s_dtp[s_path[q] * 4 + hh] * xt;
       hist[2] = hist[1];
       hist[1] = hist[0];
@@ -507,7 +507,7 @@ __global__ void __launch_bounds__(kCvWaves * kWave) commit_verify_kernel(CommitV
         }
         z = fmaf(s_cw[cl * 4 + W - 1 - jj], u, z);
       }
-      xt = d.silu ? silu_f32(z) : z;
+      xt = d.silu ? silu_fast(z) : z;
     }
     // MFMA B-operand layout: channel row cl, quad v / 4 swizzled
     s_xt[cl * kCvT + 4 * ((v >> 2) ^ ((cl >> 2) & 3)) + (v & 3)] = xt;
@@ -538,7 +538,7 @@ __global__ void __launch_bounds__(kCvWaves * kWave) commit_verify_kernel(CommitV
             }
             acc = fmaf(s_cwbc[q * 4 + W - 1 - jj], u, acc);
           }
-          if (d.silu) acc = silu_f32(acc);
+          if (d.silu) acc = silu_fast(acc);
         }
         (q < N ? s_Bt : s_Ct)[v * N + n] = acc;  // zero rows past T
       }
@@ -551,7 +551,7 @@ __global__ void __launch_bounds__(kCvWaves * kWave) commit_verify_kernel(CommitV
                                     : load_in(reinterpret_cast<const TIn*>(s_Bp + (e - (W - 1)) * rs), n);
           acc = fmaf(s_cwbc[n * 4 + W - 1 - j], u, acc);
         }
-        s_Bpt[k * N + n] = d.silu ? silu_f32(acc) : acc;
+        s_Bpt[k * N + n] = d.silu ? silu_fast(acc) : acc;
       }
     }
   }
@@ -644,7 +644,7 @@ __global__ void __launch_bounds__(kCvWaves * kWave) commit_verify_kernel(CommitV
     for (int r = 0; r < 4; ++r) {
       float yv = y[r];
       if constexpr (OPT)
-        if (gate) yv *= silu_f32(load_in(s_z, (4 * k + r) * kCvRows + row));
+        if (gate) yv *= silu_fast(load_in(s_z, (4 * k + r) * kCvRows + row));
       s_ys[(4 * k + r) * kCvRows + row] = tree_ok ? yv : __builtin_nanf("");
     }
   }

@@ -95,6 +95,12 @@ __device__ __forceinline__ float softplus_f32(float z) { return z > 20.0f ? z : 
 
 __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + expf(-z)); }
 
+// silu with the hardware exp2 and reciprocal (about 1 ulp each): z large and
+// negative gives exp2 = inf and a zero reciprocal, so the result is -0
+__device__ __forceinline__ float silu_fast(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * z));
+}
+
 // ---------------------------------------------------------------------------
 // launch argument blocks (passed by value)
 // ---------------------------------------------------------------------------

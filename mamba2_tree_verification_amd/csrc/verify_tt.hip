@@ -154,10 +154,6 @@ __device__ __forceinline__ float softplus_hw(float z) {
   return z > 20.0f ? z : fmaxf(z, 0.0f) + lp;
 }
 
-// silu with the hardware exp2 and reciprocal (about 1 ulp each)
-__device__ __forceinline__ float silu_hw(float z) {
-  return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * z));
-}
 
 // the sum of acc over the root path of node (lane) v, given each node's
 // parent up (-1 at a root) within one wave: pointer jumping, six rounds for
@@ -597,7 +593,7 @@ __global__ void __launch_bounds__(kTtThreads) verify_tt_kernel(VerifyArgs a, int
         }
         if (d.silu) {  // (a uniform branch: a select would run the transcendentals either way)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) xq[r] = silu_hw(xq[r]);
+          for (int r = 0; r < 4; ++r) xq[r] = silu_fast(xq[r]);
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) xq[r] = 4 * q + r < T ? xq[r] : 0.0f;
@@ -1055,7 +1051,7 @@ __global__ void __launch_bounds__(kWsThreads) verify_tt_ws_kernel(VerifyArgs a, 
             }
             if (d.silu) {
 #pragma unroll
-              for (int r = 0; r < 4; ++r) xq[r] = silu_hw(xq[r]);
+              for (int r = 0; r < 4; ++r) xq[r] = silu_fast(xq[r]);
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) xq[r] = 4 * q + r < T ? xq[r] : 0.0f;
