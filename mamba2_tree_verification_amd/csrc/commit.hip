@@ -27,18 +27,24 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kCommitRows = 64;
 constexpr int kCommitThreads = 256;
+constexpr int kCommitChunk = 16;  // path nodes staged in LDS at a time
+static_assert(kCommitChunk * kCommitRows % kCommitThreads == 0, "x staging trip count");
 
+// d_state up to 128 fits 5 waves per SIMD (<= 96 VGPRs) without spills;
+// the 256 form holds twice the state and keeps the compiler's choice
 template <typename TIn, typename TS, int QPT>
-__global__ void __launch_bounds__(kCommitThreads) commit_kernel(CommitArgs a, int HWMAX) {
+__global__ void __launch_bounds__(kCommitThreads) __attribute__((amdgpu_waves_per_eu(QPT <= 8 ? 5 : 1)))
+commit_kernel(CommitArgs a, int HWMAX) {
   typedef StateQuad<TS> SQ;
   const Dims d = a.d;
-  const int T = d.T, N = d.N, P = d.P, H = d.H, W = d.W, DI = d.d_in;
+  // d_state is N = 16 QPT (64 rows of N, 4 per quad, over 256 threads)
+  constexpr int N = 16 * QPT, qpr = N / 4;  // qpr: float4 quads per row
+  const int T = d.T, P = d.P, H = d.H, W = d.W, DI = d.d_in;
   const int b = blockIdx.y, l = blockIdx.z;
   const int64_t unit = (int64_t)l * d.Bsz + b;
   const int c0 = blockIdx.x * kCommitRows;
   const int g = c0 / (DI / d.G);
   const int h_lo = c0 / P;
-  const int qpr = N / 4;  // float4 quads per row
 
   extern __shared__ __align__(16) unsigned char smem[];
   int32_t* s_parent = reinterpret_cast<int32_t*>(smem);
@@ -46,8 +52,9 @@ __global__ void __launch_bounds__(kCommitThreads) commit_kernel(CommitArgs a, in
   int32_t* s_misc = s_path + kMaxNodes;
   float* s_dA = reinterpret_cast<float*>(s_misc + 4);      // [T][HWMAX]
   float* s_dtv = s_dA + kMaxNodes * HWMAX;                 // [T][HWMAX] dt
-  float* s_dtx = s_dtv + kMaxNodes * HWMAX;                // [T][64] raw x of the path nodes, then dt x~
-  float* s_B = s_dtx + kMaxNodes * kCommitRows;            // [T][N]
+  float* s_dtx = s_dtv + kMaxNodes * HWMAX;                // [chunk][64] raw x of the path nodes
+  float2* s_ax = reinterpret_cast<float2*>(s_dtx + kCommitChunk * kCommitRows);  // [chunk][64] (dA, dt x~) per row
+  float* s_B = reinterpret_cast<float*>(s_ax + kCommitChunk * kCommitRows);     // [chunk][N]
 
   // ---- issue the state loads first (QPT quads per thread) ----
   const TS* sin = reinterpret_cast<const TS*>(a.state_in) + (unit * DI + c0) * (int64_t)N;
@@ -93,93 +100,141 @@ __global__ void __launch_bounds__(kCommitThreads) commit_kernel(CommitArgs a, in
   }
   const int CH = d.CH;  // conv channels = window row length
   const TIn* xin = reinterpret_cast<const TIn*>(a.x) + unit * T * DI;
-  // the path nodes' raw x of the workgroup's channels, all loads in flight at once
-  for (int i = threadIdx.x; i < len * kCommitRows; i += blockDim.x)
-    s_dtx[i] = load_in(xin, (int64_t)s_path[i / kCommitRows] * DI + c0 + i % kCommitRows);
   const TIn* Bg = reinterpret_cast<const TIn*>(a.B) + (unit * T * d.G + g) * (int64_t)N;
   const TIn* win_in = reinterpret_cast<const TIn*>(a.window_in) + unit * (W - 1) * (int64_t)CH;
-  for (int i = threadIdx.x; i < len * N; i += blockDim.x) {
-    const int k = i / N, n = i % N;
-    if (!d.xbc) {
-      s_B[k * N + n] = load_in(Bg + (int64_t)s_path[k] * d.G * N, n);
-    } else {
-      // the xBC conv of B channel (g, n) at path node k: its taps read the
-      // sequence (old window rows, then the path nodes) backwards from k
-      const int ch = DI + g * N + n;
-      const float* cw = a.prm.conv_w + ((int64_t)l * CH + ch) * W;
-      float acc = a.prm.conv_b ? a.prm.conv_b[(int64_t)l * CH + ch] : 0.0f;
-      for (int j = 0; j < W; ++j) {
-        const int e = k + W - 1 - j;
-        const float in = e < W - 1 ? load_in(win_in, (int64_t)e * CH + ch)
-                                   : load_in(Bg + (int64_t)s_path[e - (W - 1)] * d.G * N, n);
-        acc = fmaf(cw[W - 1 - j], in, acc);
-      }
-      s_B[k * N + n] = d.silu ? silu_fast(acc) : acc;
-    }
-  }
-  __syncthreads();  // the path's x rows and dt are in LDS
-  if (threadIdx.x < kCommitRows) {
-    const int c = c0 + threadIdx.x, hh = c / P - h_lo;
-    // wj[jj] weighs conv input jj (0 = the token itself, jj = the jj-th previous token)
-    float wj[4];
-    const float* cw = a.prm.conv_w + ((int64_t)l * CH + c) * W;
+
+  // the conv threads (one per channel) carry their weights, the sliding
+  // window of raw inputs and the new window rows across the path's chunks
+  const bool conv_thr = threadIdx.x < kCommitRows;
+  const int cc = c0 + (conv_thr ? threadIdx.x : 0), hhc = cc / P - h_lo;
+  // wj[jj] weighs conv input jj (0 = the token itself, jj = the jj-th previous token)
+  float wj[4] = {0.f, 0.f, 0.f, 0.f}, cbc = 0.f, hist[3] = {0.f, 0.f, 0.f};  // hist[0] = newest
+  TIn nw[3];
+  if (conv_thr) {
+    const float* cw = a.prm.conv_w + ((int64_t)l * CH + cc) * W;
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) wj[jj] = (jj < W) ? cw[W - 1 - jj] : 0.0f;
-    const float cb = a.prm.conv_b ? a.prm.conv_b[(int64_t)l * CH + c] : 0.0f;
-    // sliding window of raw inputs, hist[0] = newest
-    float hist[3];
+    cbc = a.prm.conv_b ? a.prm.conv_b[(int64_t)l * CH + cc] : 0.0f;
 #pragma unroll
-    for (int r = 0; r < 3; ++r) hist[r] = (r < W - 1) ? load_in(win_in, (int64_t)(W - 2 - r) * CH + c) : 0.0f;
+    for (int r = 0; r < 3; ++r) hist[r] = (r < W - 1) ? load_in(win_in, (int64_t)(W - 2 - r) * CH + cc) : 0.0f;
     // new window row r (oldest first) is element len + r of the sequence
-    // (old window rows, x of the path nodes); read every source before any
-    // write so that an in-place window is safe
-    TIn nw[3];
+    // (old window rows, x of the path nodes); every source is read before
+    // any write, so that an in-place window is safe
 #pragma unroll
     for (int r = 0; r < 3; ++r) {
       if (r < W - 1) {
         const int e = len + r;
-        nw[r] = (e < W - 1) ? win_in[(int64_t)e * CH + c] : xin[(int64_t)s_path[e - (W - 1)] * DI + c];
+        nw[r] = (e < W - 1) ? win_in[(int64_t)e * CH + cc] : xin[(int64_t)s_path[e - (W - 1)] * DI + cc];
       }
     }
-    for (int k = 0; k < len; ++k) {
-      const float xv = s_dtx[k * kCommitRows + threadIdx.x];  // (this thread's own entry, rewritten below)
-      float z = fmaf(wj[0], xv, cb);
+  }
+
+  // the state in fp32 registers for the whole path
+  f32x4 h[QPT];
 #pragma unroll
-      for (int jj = 1; jj < 4; ++jj)
-        if (jj < W) z = fmaf(wj[jj], hist[jj - 1], z);
-      const float xt = d.silu ? silu_fast(z) : z;
-      s_dtx[k * kCommitRows + threadIdx.x] = s_dtv[k * HWMAX + hh] * xt;
-      hist[2] = hist[1];
-      hist[1] = hist[0];
-      hist[0] = xv;
+  for (int it = 0; it < QPT; ++it) h[it] = SQ::to_f32(hq[it]);
+
+  // ---- the path in chunks of kCommitChunk nodes (LDS holds one chunk) ----
+  for (int k0 = 0; k0 < len; k0 += kCommitChunk) {
+    const int kn = len - k0 < kCommitChunk ? len - k0 : kCommitChunk;
+    if (k0 > 0) __syncthreads();  // the previous chunk's rows are consumed
+    // the chunk's raw x of the workgroup's channels and (no xBC conv) its
+    // B rows, in quads of 4 inputs: fixed trip counts and clamped
+    // addresses, so that every load of a thread is in flight before the
+    // first LDS write.  x: 16 nodes x 16 quads = one quad per thread.
+    {
+      typedef StateQuad<TIn> IQ;
+      constexpr int kQx = kCommitRows / 4, kQb = N / 4;  // quads per x row, per B row
+      constexpr int kBr = (kCommitChunk * kQb + kCommitThreads - 1) / kCommitThreads;
+      static_assert(kCommitChunk * kQx == kCommitThreads, "one x quad per thread");
+      const int kx = min((int)threadIdx.x / kQx, kn - 1);
+      const typename IQ::Raw xr = IQ::load(xin + (int64_t)s_path[k0 + kx] * DI + c0 + (threadIdx.x % kQx) * 4);
+      typename IQ::Raw br[kBr];
+      if (!d.xbc) {
+#pragma unroll
+        for (int r = 0; r < kBr; ++r) {
+          const int q = min((int)threadIdx.x + r * kCommitThreads, kCommitChunk * kQb - 1);
+          const int kk = min(q / kQb, kn - 1);
+          br[r] = IQ::load(Bg + (int64_t)s_path[k0 + kk] * d.G * N + (q % kQb) * 4);
+        }
+      }
+      if ((int)threadIdx.x < kn * kQx)
+        *reinterpret_cast<f32x4*>(s_dtx + threadIdx.x * 4) = IQ::to_f32(xr);
+      if (!d.xbc) {
+#pragma unroll
+        for (int r = 0; r < kBr; ++r) {
+          const int q = threadIdx.x + r * kCommitThreads;
+          if (q < kn * kQb) *reinterpret_cast<f32x4*>(s_B + q * 4) = IQ::to_f32(br[r]);
+        }
+      }
     }
-    if (W > 1) {
-      TIn* win_out = reinterpret_cast<TIn*>(a.window_out) + unit * (W - 1) * (int64_t)CH;
+    if (d.xbc) {
+      for (int i = threadIdx.x; i < kn * N; i += blockDim.x) {
+        // the xBC conv of B channel (g, n) at path node k: its taps read the
+        // sequence (old window rows, then the path nodes) backwards from k
+        const int kk = i / N, k = k0 + kk, n = i % N;
+        const int ch = DI + g * N + n;
+        const float* cw = a.prm.conv_w + ((int64_t)l * CH + ch) * W;
+        float acc = a.prm.conv_b ? a.prm.conv_b[(int64_t)l * CH + ch] : 0.0f;
+        for (int j = 0; j < W; ++j) {
+          const int e = k + W - 1 - j;
+          const float in = e < W - 1 ? load_in(win_in, (int64_t)e * CH + ch)
+                                     : load_in(Bg + (int64_t)s_path[e - (W - 1)] * d.G * N, n);
+          acc = fmaf(cw[W - 1 - j], in, acc);
+        }
+        s_B[kk * N + n] = d.silu ? silu_fast(acc) : acc;
+      }
+    }
+    __syncthreads();  // the chunk's x rows and B rows are in LDS
+    if (conv_thr) {
+#pragma unroll 1
+      for (int kk = 0; kk < kn; ++kk) {
+        const float xv = s_dtx[kk * kCommitRows + threadIdx.x];
+        float z = fmaf(wj[0], xv, cbc);
 #pragma unroll
-      for (int r = 0; r < 3; ++r)
-        if (r < W - 1) win_out[(int64_t)r * CH + c] = nw[r];
+        for (int jj = 1; jj < 4; ++jj)
+          if (jj < W) z = fmaf(wj[jj], hist[jj - 1], z);
+        const float xt = d.silu ? silu_fast(z) : z;
+        s_ax[kk * kCommitRows + threadIdx.x] =
+            make_float2(s_dA[(k0 + kk) * HWMAX + hhc], s_dtv[(k0 + kk) * HWMAX + hhc] * xt);
+        hist[2] = hist[1];
+        hist[1] = hist[0];
+        hist[0] = xv;
+      }
+    }
+    __syncthreads();  // (dA, dt x~) of the chunk
+    // ---- state update along the chunk ----
+    // quad it of a thread is row tid / qpr + it * (256 / qpr), columns
+    // 4 (tid % qpr) .. +3: qpr = N / 4 divides 256, so every quad of a
+    // thread shares its B columns and one B read per node serves them all
+#pragma unroll 1
+    for (int kk = 0; kk < kn; ++kk) {
+      const f32x4 bq = *reinterpret_cast<const f32x4*>(s_B + kk * N + (threadIdx.x % qpr) * 4);
+#pragma unroll
+      for (int it = 0; it < QPT; ++it) {
+        const int row = (threadIdx.x + it * kCommitThreads) / qpr;
+        const float2 ax = s_ax[kk * kCommitRows + row];
+        // scale in place, then one fused multiply-add: both steps write
+        // the state's own registers (no copy of the state per node)
+        h[it] *= ax.x;
+        h[it].x = fmaf(ax.y, bq.x, h[it].x);
+        h[it].y = fmaf(ax.y, bq.y, h[it].y);
+        h[it].z = fmaf(ax.y, bq.z, h[it].z);
+        h[it].w = fmaf(ax.y, bq.w, h[it].w);
+      }
     }
   }
-  __syncthreads();
-
-  // ---- state update along the path ----
+  if (conv_thr && W > 1) {
+    TIn* win_out = reinterpret_cast<TIn*>(a.window_out) + unit * (W - 1) * (int64_t)CH;
+#pragma unroll
+    for (int r = 0; r < 3; ++r)
+      if (r < W - 1) win_out[(int64_t)r * CH + cc] = nw[r];
+  }
   TS* sout = reinterpret_cast<TS*>(a.state_out) + (unit * DI + c0) * (int64_t)N;
 #pragma unroll
   for (int it = 0; it < QPT; ++it) {
     const int qi = threadIdx.x + it * kCommitThreads;
-    const int row = qi / qpr, n = (qi % qpr) * 4;
-    const int hh = (c0 + row) / P - h_lo;
-    f32x4 h = SQ::to_f32(hq[it]);
-    for (int k = 0; k < len; ++k) {
-      const float dA = s_dA[k * HWMAX + hh];
-      const float cx = s_dtx[k * kCommitRows + row];
-      const f32x4 bq = *reinterpret_cast<const f32x4*>(s_B + k * N + n);
-      h.x = fmaf(dA, h.x, cx * bq.x);
-      h.y = fmaf(dA, h.y, cx * bq.y);
-      h.z = fmaf(dA, h.z, cx * bq.z);
-      h.w = fmaf(dA, h.w, cx * bq.w);
-    }
-    SQ::store_nt(sout + 4 * qi, SQ::from_f32(h));
+    SQ::store_nt(sout + 4 * qi, SQ::from_f32(h[it]));
   }
 }
 
@@ -260,7 +315,8 @@ template <typename TIn, typename TS, int QPT>
 static hipError_t launch_c(const CommitArgs& a, hipStream_t s) {
   const int HWMAX = ((kCommitRows + a.d.P - 1) / a.d.P + 1 + 3) & ~3;
   const size_t lds = sizeof(int32_t) * (2 * kMaxNodes + 4) +
-                     sizeof(float) * ((size_t)2 * kMaxNodes * HWMAX + kMaxNodes * kCommitRows + (size_t)a.d.T * a.d.N);
+                     sizeof(float) * ((size_t)2 * kMaxNodes * HWMAX + 3 * kCommitChunk * kCommitRows +
+                                      (size_t)(a.d.T < kCommitChunk ? a.d.T : kCommitChunk) * a.d.N);
   dim3 grid(a.d.d_in / kCommitRows, a.d.Bsz, a.d.L);
   hipError_t e = allow_lds(commit_kernel<TIn, TS, QPT>, lds);
   if (e != hipSuccess) return e;
