@@ -572,10 +572,13 @@ __global__ void __launch_bounds__(kCvWaves * kWave) commit_verify_kernel(CommitV
 #pragma unroll
       for (int gg = 0; gg < NG; ++gg) {
         const f32x4 bq = xbc ? *reinterpret_cast<const f32x4*>(bpt + 16 * gg) : load4<TIn>(bp + 16 * gg);
-        hq[gg].x = fmaf(dA, hq[gg].x, cx * bq.x);
-        hq[gg].y = fmaf(dA, hq[gg].y, cx * bq.y);
-        hq[gg].z = fmaf(dA, hq[gg].z, cx * bq.z);
-        hq[gg].w = fmaf(dA, hq[gg].w, cx * bq.w);
+        // scale in place, then one fused multiply-add: both steps write
+        // the state's own registers (no copy of the state per node)
+        hq[gg] *= dA;
+        hq[gg].x = fmaf(cx, bq.x, hq[gg].x);
+        hq[gg].y = fmaf(cx, bq.y, hq[gg].y);
+        hq[gg].z = fmaf(cx, bq.z, hq[gg].z);
+        hq[gg].w = fmaf(cx, bq.w, hq[gg].w);
       }
     }
     // the committed state as stored (a bfloat16 state is rounded): the
