@@ -106,7 +106,8 @@ def load_traffic(kernel, cfg):
 
 
 PROBE_BYTES = 4 << 30  # the plain copy of hbm_probe: reads and writes this many bytes per dispatch
-KERNEL_MATCH = {"verify": ("verify_mfma_kernel", "verify_tt_kernel", "verify_proj_kernel"), "commit": ("::commit_kernel",),
+KERNEL_MATCH = {"verify": ("verify_mfma_kernel", "verify_tt_kernel", "verify_tt_ws_kernel", "verify_proj_kernel"),
+                "commit": ("::commit_kernel",),
                 "commit_verify": ("commit_verify_kernel",), "copy": ("copyBuffer",)}
 
 
