@@ -90,7 +90,7 @@ struct CvLds {
   int pparent, path, parent, misc, anc, cidx, dAp, dtp, dt, S, S2, D, cbt, cw, cb, win, xn, xp, ys, C, B, dtx, Bp,
       xt, total, row;
   // the options' own arrays (offset 0 when unused)
-  int z, cwbc, cbbc, winbc, Cp, Ct, Bt, Bpt;
+  int z, cwbc, cbbc, winbc, Cp, Bpt;
   __host__ __device__ CvLds(int N, int E, bool xbc = false, bool gate = false) {
     int o = 0;
     row = N * E + kRowPad;                    // staged B / C row stride
@@ -106,7 +106,7 @@ struct CvLds {
     S = o; o += 4 * 4 * kCvT;                 // next tree: dt * A per head and node
     S2 = o; o += 4 * 4 * kCvT;                // next tree: cumulative S along the root path, times log2(e)
     D = o; o += 16;
-    cbt = o; o += 4 * kCvT * kCvT;            // next tree: C_v . B_u
+    cbt = o; o += xbc ? 0 : 4 * kCvT * kCvT;  // next tree: C_v . B_u (with the xBC conv each wave forms it itself)
     cw = o; o += 4 * 4 * kCvRows;             // conv weights per channel, tap order of the parameters
     cb = o; o += 4 * kCvRows;                 // conv bias per channel
     win = o; o += align16(3 * kCvRows * E);   // old window rows (raw)
@@ -119,17 +119,17 @@ struct CvLds {
     o += kCvT * row > 4 * kCvT * kCvRows ? kCvT * row : 4 * kCvT * kCvRows;
     Bp = o; o += kCvT * row;                  // previous tree B rows of the path nodes (raw, padded)
     xt = o; o += 4 * kCvRows * kCvT;          // next tree conv outputs, MFMA B-operand layout
-    z = cwbc = cbbc = winbc = Cp = Ct = Bt = Bpt = 0;
+    z = cwbc = cbbc = winbc = Cp = Bpt = 0;
     if (gate) { z = o; o += kCvT * kCvRows * E; }          // gate input rows (raw)
     if (xbc) {
       dtx = o; o += 4 * kCvT * kCvRows;       // the raw B rows stay live: dt * x~ gets its own space
-      cwbc = o; o += 4 * 4 * 2 * N;           // conv weights of the group's B then C channels, 4 taps
+      cwbc = o; o += 4 * 4 * 2 * N;           // conv weights of the group's B then C channels, by taps back
       cbbc = o; o += 4 * 2 * N;               // their bias
       winbc = o; o += align16(3 * 2 * N * E); // old window rows of those channels (raw)
       Cp = o; o += kCvT * row;                // previous tree C rows of the path nodes (raw, padded)
-      Ct = o; o += 4 * kCvT * N;              // next tree convolved C rows, fp32
-      Bt = o; o += 4 * kCvT * N;              // next tree convolved B rows, fp32
       Bpt = o; o += 4 * kCvT * N;             // convolved B rows of the path nodes, fp32
+      // (the next tree's convolved B and C rows are formed in registers by
+      // the lanes that take them, from the raw rows, which stay live)
     }
     total = o;
   }
@@ -193,8 +193,6 @@ __global__ void __launch_bounds__(kCvWaves * kWave) commit_verify_kernel(CommitV
   float* s_cbbc = reinterpret_cast<float*>(smem + lo.cbbc);
   TIn* s_winbc = reinterpret_cast<TIn*>(smem + lo.winbc);
   unsigned char* s_Cp = smem + lo.Cp;
-  float* s_Ct = reinterpret_cast<float*>(smem + lo.Ct);
-  float* s_Bt = reinterpret_cast<float*>(smem + lo.Bt);
   float* s_Bpt = reinterpret_cast<float*>(smem + lo.Bpt);
 
   // ======== trip 1: everything that does not depend on the path ========
@@ -267,8 +265,9 @@ __global__ void __launch_bounds__(kCvWaves * kWave) commit_verify_kernel(CommitV
         if (i < 2 * N) {
           const int ch = DI + (i < N ? g * N + i : G * N + g * N + i - N);
           const float* cw = a.prm.conv_w + ((int64_t)l * CH + ch) * W;
+          // by taps back: o_cw[jj] weighs the input jj steps before the token
 #pragma unroll
-          for (int jj = 0; jj < 4; ++jj) o_cw[it][jj] = jj < W ? cw[jj] : 0.0f;
+          for (int jj = 0; jj < 4; ++jj) o_cw[it][jj] = jj < W ? cw[W - 1 - jj] : 0.0f;
           o_cb[it] = a.prm.conv_b ? a.prm.conv_b[(int64_t)l * CH + ch] : 0.0f;
           const TIn* wsrc = reinterpret_cast<const TIn*>(a.window_in) + unit * (W - 1) * (int64_t)CH + ch;
 #pragma unroll
@@ -514,42 +513,17 @@ __global__ void __launch_bounds__(kCvWaves * kWave) commit_verify_kernel(CommitV
   }
   if constexpr (OPT) {
     if (xbc) {
-      // the xBC conv of the group's B and C channels: the next tree's nodes
-      // over their ancestor paths (past the root: the committed window, i.e.
-      // element len + r of (old window rows, path rows)), and the path's
-      // nodes over (old window rows, path rows)
-      for (int i = tid; i < kCvT * 2 * N; i += kCvWaves * kWave) {
-        const int v = i / (2 * N), q = i % (2 * N), n = q < N ? q : q - N;
-        const unsigned char* rows = q < N ? s_B : s_C;      // next tree, raw
-        const unsigned char* prow = q < N ? s_Bp : s_Cp;    // path nodes, raw
-        float acc = 0.0f;
-        if (v < T) {
-          acc = fmaf(s_cwbc[q * 4 + W - 1], load_in(reinterpret_cast<const TIn*>(rows + v * rs), n), s_cbbc[q]);
-          const int codes = s_cidx[v];
-          for (int jj = 1; jj < W; ++jj) {
-            const int code = (codes >> (8 * (jj - 1))) & 255;
-            float u;
-            if (code < T) {
-              u = load_in(reinterpret_cast<const TIn*>(rows + code * rs), n);
-            } else {
-              const int e = len + code - T;
-              u = e < W - 1 ? load_in(s_winbc, e * 2 * N + q)
-                            : load_in(reinterpret_cast<const TIn*>(prow + (e - (W - 1)) * rs), n);
-            }
-            acc = fmaf(s_cwbc[q * 4 + W - 1 - jj], u, acc);
-          }
-          if (d.silu) acc = silu_fast(acc);
-        }
-        (q < N ? s_Bt : s_Ct)[v * N + n] = acc;  // zero rows past T
-      }
+      // the xBC conv of the group's B channels over the path's nodes, along
+      // (old window rows, path rows); the next tree's B and C rows are
+      // convolved where the products take them
       for (int i = tid; i < len * N; i += kCvWaves * kWave) {
         const int k = i / N, n = i % N;
         float acc = s_cbbc[n];
-        for (int j = 0; j < W; ++j) {
+        for (int j = 0; j < W; ++j) {  // the input j steps back
           const int e = k + W - 1 - j;
           const float u = e < W - 1 ? load_in(s_winbc, e * 2 * N + n)
                                     : load_in(reinterpret_cast<const TIn*>(s_Bp + (e - (W - 1)) * rs), n);
-          acc = fmaf(s_cwbc[n * 4 + W - 1 - j], u, acc);
+          acc = fmaf(s_cwbc[n * 4 + j], u, acc);
         }
         s_Bpt[k * N + n] = d.silu ? silu_fast(acc) : acc;
       }
@@ -599,9 +573,77 @@ __global__ void __launch_bounds__(kCvWaves * kWave) commit_verify_kernel(CommitV
     const bool live = j < T;
     const TIn* cp = reinterpret_cast<const TIn*>(s_C + j * rs) + 4 * k;
     f32x4 cbx = f32x4{0.f, 0.f, 0.f, 0.f};  // with the xBC conv: C_v . B_u, formed below
+    // with the xBC conv, the raw rows that tap jj (steps back) of node j
+    // reads: the node itself, an ancestor, or past the root a row of the
+    // committed window (old window rows, then the path's rows)
+    const unsigned char* tb[4] = {s_B + j * rs, s_B, s_B, s_B};
+    const unsigned char* tc[4] = {s_C + j * rs, s_C, s_C, s_C};
+    if constexpr (OPT) {
+      if (xbc) {
+        const int codes = s_cidx[j];
+#pragma unroll
+        for (int jj = 1; jj < 4; ++jj) {
+          if (jj < W) {
+            const int code = (codes >> (8 * (jj - 1))) & 255;
+            if (code < T) {
+              tb[jj] = s_B + code * rs;
+              tc[jj] = s_C + code * rs;
+            } else {
+              const int e = len + code - T;
+              if (e < W - 1) {
+                tb[jj] = reinterpret_cast<const unsigned char*>(s_winbc) + e * 2 * N * E;
+                tc[jj] = tb[jj] + N * E;
+              } else {
+                tb[jj] = s_Bp + (e - (W - 1)) * rs;
+                tc[jj] = s_Cp + (e - (W - 1)) * rs;
+              }
+            }
+          }
+        }
+      }
+    }
 #pragma unroll
     for (int gg = 0; gg < NG; ++gg) {
-      f32x4 cq = xbc ? *reinterpret_cast<const f32x4*>(s_Ct + j * N + 16 * gg + 4 * k) : load4<TIn>(cp + 16 * gg);
+      f32x4 cq, bxq = f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (OPT) {
+        if (xbc) {
+          // the convolved B and C values of node j, columns n0 .. n0 + 3
+          const int n0 = 16 * gg + 4 * k;
+          f32x4 ab = *reinterpret_cast<const f32x4*>(s_cbbc + n0);
+          f32x4 ac = *reinterpret_cast<const f32x4*>(s_cbbc + N + n0);
+          f32x4 wb[4], wc[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            wb[t] = *reinterpret_cast<const f32x4*>(s_cwbc + (n0 + t) * 4);
+            wc[t] = *reinterpret_cast<const f32x4*>(s_cwbc + (N + n0 + t) * 4);
+          }
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            if (jj < W) {
+              const f32x4 ub = load4<TIn>(reinterpret_cast<const TIn*>(tb[jj]) + n0);
+              const f32x4 uc = load4<TIn>(reinterpret_cast<const TIn*>(tc[jj]) + n0);
+#pragma unroll
+              for (int t = 0; t < 4; ++t) {
+                ab[t] = fmaf(wb[t][jj], ub[t], ab[t]);
+                ac[t] = fmaf(wc[t][jj], uc[t], ac[t]);
+              }
+            }
+          }
+          if (d.silu) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              ab[t] = silu_fast(ab[t]);
+              ac[t] = silu_fast(ac[t]);
+            }
+          }
+          cq = ac;
+          bxq = ab;
+        } else {
+          cq = load4<TIn>(cp + 16 * gg);
+        }
+      } else {
+        cq = load4<TIn>(cp + 16 * gg);
+      }
       if (!live) cq = f32x4{0.f, 0.f, 0.f, 0.f};
       acc = mfma4(cq.x, hq[gg].x, acc);
       acc = mfma4(cq.y, hq[gg].y, acc);
@@ -612,7 +654,7 @@ __global__ void __launch_bounds__(kCvWaves * kWave) commit_verify_kernel(CommitV
           // B rows as the A operand and C rows as the B operand: lane
           // (i + 16 k) ends with (B_{4k+t} . C_i) = CB[i][4 k + t], the
           // layout the path terms read, with no transpose
-          f32x4 bq = *reinterpret_cast<const f32x4*>(s_Bt + j * N + 16 * gg + 4 * k);
+          f32x4 bq = bxq;
           if (!live) bq = f32x4{0.f, 0.f, 0.f, 0.f};
           cbx = mfma4(bq.x, cq.x, cbx);
           cbx = mfma4(bq.y, cq.y, cbx);
