@@ -48,6 +48,12 @@ constexpr int kCvWaves = 4;
 constexpr int kCvT = 16;      // node capacity
 constexpr int kRowPad = 16;   // bytes of padding per staged B / C row (LDS banks)
 
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+// 16x16x32 bf16 products, fp32 accumulate; the operands as raw bits
+__device__ __forceinline__ f32x4 mfma32(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                  0, 0);
+}
 __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
@@ -602,64 +608,81 @@ __global__ void __launch_bounds__(kCvWaves * kWave) commit_verify_kernel(CommitV
         }
       }
     }
+    // bf16 C rows and a bf16 state are exact bf16 operands: one 16x16x32
+    // product per pair of column groups (lane j + 16 k feeds columns
+    // 16 gg + 4 k .. + 3 of both groups, the same slots in C and in h)
+    constexpr bool kBf16Ch = E == 2 && sizeof(TS) == 2 && !OPT;
+    if constexpr (kBf16Ch) {
 #pragma unroll
-    for (int gg = 0; gg < NG; ++gg) {
-      f32x4 cq, bxq = f32x4{0.f, 0.f, 0.f, 0.f};
-      if constexpr (OPT) {
-        if (xbc) {
-          // the convolved B and C values of node j, columns n0 .. n0 + 3
-          const int n0 = 16 * gg + 4 * k;
-          f32x4 ab = *reinterpret_cast<const f32x4*>(s_cbbc + n0);
-          f32x4 ac = *reinterpret_cast<const f32x4*>(s_cbbc + N + n0);
-          f32x4 wb[4], wc[4];
+      for (int gp = 0; gp < (NG + 1) / 2; ++gp) {
+        const u32x2 c0 = *reinterpret_cast<const u32x2*>(cp + 32 * gp);
+        const u32x2 c1 = 2 * gp + 1 < NG ? *reinterpret_cast<const u32x2*>(cp + 32 * gp + 16) : u32x2{0u, 0u};
+        const u32x2 h0 = hraw[2 * gp];
+        const u32x2 h1 = 2 * gp + 1 < NG ? hraw[(2 * gp + 1) % NG] : u32x2{0u, 0u};
+        u32x4 ca = u32x4{c0.x, c0.y, c1.x, c1.y};
+        if (!live) ca = u32x4{0u, 0u, 0u, 0u};
+        acc = mfma32(ca, u32x4{h0.x, h0.y, h1.x, h1.y}, acc);
+      }
+    } else {
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            wb[t] = *reinterpret_cast<const f32x4*>(s_cwbc + (n0 + t) * 4);
-            wc[t] = *reinterpret_cast<const f32x4*>(s_cwbc + (N + n0 + t) * 4);
-          }
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            if (jj < W) {
-              const f32x4 ub = load4<TIn>(reinterpret_cast<const TIn*>(tb[jj]) + n0);
-              const f32x4 uc = load4<TIn>(reinterpret_cast<const TIn*>(tc[jj]) + n0);
-#pragma unroll
-              for (int t = 0; t < 4; ++t) {
-                ab[t] = fmaf(wb[t][jj], ub[t], ab[t]);
-                ac[t] = fmaf(wc[t][jj], uc[t], ac[t]);
-              }
-            }
-          }
-          if (d.silu) {
+      for (int gg = 0; gg < NG; ++gg) {
+        f32x4 cq, bxq = f32x4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (OPT) {
+          if (xbc) {
+            // the convolved B and C values of node j, columns n0 .. n0 + 3
+            const int n0 = 16 * gg + 4 * k;
+            f32x4 ab = *reinterpret_cast<const f32x4*>(s_cbbc + n0);
+            f32x4 ac = *reinterpret_cast<const f32x4*>(s_cbbc + N + n0);
+            f32x4 wb[4], wc[4];
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-              ab[t] = silu_fast(ab[t]);
-              ac[t] = silu_fast(ac[t]);
+              wb[t] = *reinterpret_cast<const f32x4*>(s_cwbc + (n0 + t) * 4);
+              wc[t] = *reinterpret_cast<const f32x4*>(s_cwbc + (N + n0 + t) * 4);
             }
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+              if (jj < W) {
+                const f32x4 ub = load4<TIn>(reinterpret_cast<const TIn*>(tb[jj]) + n0);
+                const f32x4 uc = load4<TIn>(reinterpret_cast<const TIn*>(tc[jj]) + n0);
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                  ab[t] = fmaf(wb[t][jj], ub[t], ab[t]);
+                  ac[t] = fmaf(wc[t][jj], uc[t], ac[t]);
+                }
+              }
+            }
+            if (d.silu) {
+#pragma unroll
+              for (int t = 0; t < 4; ++t) {
+                ab[t] = silu_fast(ab[t]);
+                ac[t] = silu_fast(ac[t]);
+              }
+            }
+            cq = ac;
+            bxq = ab;
+          } else {
+            cq = load4<TIn>(cp + 16 * gg);
           }
-          cq = ac;
-          bxq = ab;
         } else {
           cq = load4<TIn>(cp + 16 * gg);
         }
-      } else {
-        cq = load4<TIn>(cp + 16 * gg);
-      }
-      if (!live) cq = f32x4{0.f, 0.f, 0.f, 0.f};
-      acc = mfma4(cq.x, hq[gg].x, acc);
-      acc = mfma4(cq.y, hq[gg].y, acc);
-      acc = mfma4(cq.z, hq[gg].z, acc);
-      acc = mfma4(cq.w, hq[gg].w, acc);
-      if constexpr (OPT) {
-        if (xbc) {
-          // B rows as the A operand and C rows as the B operand: lane
-          // (i + 16 k) ends with (B_{4k+t} . C_i) = CB[i][4 k + t], the
-          // layout the path terms read, with no transpose
-          f32x4 bq = bxq;
-          if (!live) bq = f32x4{0.f, 0.f, 0.f, 0.f};
-          cbx = mfma4(bq.x, cq.x, cbx);
-          cbx = mfma4(bq.y, cq.y, cbx);
-          cbx = mfma4(bq.z, cq.z, cbx);
-          cbx = mfma4(bq.w, cq.w, cbx);
+        if (!live) cq = f32x4{0.f, 0.f, 0.f, 0.f};
+        acc = mfma4(cq.x, hq[gg].x, acc);
+        acc = mfma4(cq.y, hq[gg].y, acc);
+        acc = mfma4(cq.z, hq[gg].z, acc);
+        acc = mfma4(cq.w, hq[gg].w, acc);
+        if constexpr (OPT) {
+          if (xbc) {
+            // B rows as the A operand and C rows as the B operand: lane
+            // (i + 16 k) ends with (B_{4k+t} . C_i) = CB[i][4 k + t], the
+            // layout the path terms read, with no transpose
+            f32x4 bq = bxq;
+            if (!live) bq = f32x4{0.f, 0.f, 0.f, 0.f};
+            cbx = mfma4(bq.x, cq.x, cbx);
+            cbx = mfma4(bq.y, cq.y, cbx);
+            cbx = mfma4(bq.z, cq.z, cbx);
+            cbx = mfma4(bq.w, cq.w, cbx);
+          }
         }
       }
     }
