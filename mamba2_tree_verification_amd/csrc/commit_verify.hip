@@ -399,15 +399,32 @@ __global__ void __launch_bounds__(kCvWaves * kWave) commit_verify_kernel(CommitV
     // (with the xBC conv each wave forms it later from the convolved rows)
     f32x4 cbm = f32x4{0.f, 0.f, 0.f, 0.f};
     const bool live = j < T;
+    if constexpr (E == 2) {
+      // bf16 rows are exact bf16 operands: one 16x16x32 product per pair
+      // of column groups
+      const TIn* cr = reinterpret_cast<const TIn*>(s_C + j * rs) + 4 * k;
+      const TIn* br = reinterpret_cast<const TIn*>(s_B + j * rs) + 4 * k;
 #pragma unroll
-    for (int gg = 0; gg < NG; ++gg) {
-      f32x4 cq = load4<TIn>(reinterpret_cast<const TIn*>(s_C + j * rs) + 16 * gg + 4 * k);
-      f32x4 bq = load4<TIn>(reinterpret_cast<const TIn*>(s_B + j * rs) + 16 * gg + 4 * k);
-      if (!live) cq = bq = f32x4{0.f, 0.f, 0.f, 0.f};
-      cbm = mfma4(cq.x, bq.x, cbm);
-      cbm = mfma4(cq.y, bq.y, cbm);
-      cbm = mfma4(cq.z, bq.z, cbm);
-      cbm = mfma4(cq.w, bq.w, cbm);
+      for (int gp = 0; gp < (NG + 1) / 2; ++gp) {
+        const u32x2 c0 = *reinterpret_cast<const u32x2*>(cr + 32 * gp);
+        const u32x2 b0 = *reinterpret_cast<const u32x2*>(br + 32 * gp);
+        const u32x2 c1 = 2 * gp + 1 < NG ? *reinterpret_cast<const u32x2*>(cr + 32 * gp + 16) : u32x2{0u, 0u};
+        const u32x2 b1 = 2 * gp + 1 < NG ? *reinterpret_cast<const u32x2*>(br + 32 * gp + 16) : u32x2{0u, 0u};
+        u32x4 ca = u32x4{c0.x, c0.y, c1.x, c1.y};
+        if (!live) ca = u32x4{0u, 0u, 0u, 0u};
+        cbm = mfma32(ca, u32x4{b0.x, b0.y, b1.x, b1.y}, cbm);
+      }
+    } else {
+#pragma unroll
+      for (int gg = 0; gg < NG; ++gg) {
+        f32x4 cq = load4<TIn>(reinterpret_cast<const TIn*>(s_C + j * rs) + 16 * gg + 4 * k);
+        f32x4 bq = load4<TIn>(reinterpret_cast<const TIn*>(s_B + j * rs) + 16 * gg + 4 * k);
+        if (!live) cq = bq = f32x4{0.f, 0.f, 0.f, 0.f};
+        cbm = mfma4(cq.x, bq.x, cbm);
+        cbm = mfma4(cq.y, bq.y, cbm);
+        cbm = mfma4(cq.z, bq.z, cbm);
+        cbm = mfma4(cq.w, bq.w, cbm);
+      }
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) s_cbt[(4 * k + r) * kCvT + j] = cbm[r];
