@@ -63,6 +63,13 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+// 16x16x32 bf16 products, fp32 accumulate; the operands as raw bits
+__device__ __forceinline__ f32x4 mfma32(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                  0, 0);
+}
 __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
@@ -241,11 +248,20 @@ __global__ void __launch_bounds__(WPG * 64) verify_mfma_kernel(VerifyArgs a, int
   int cur_unit = -1;
   int cur_group = -1;
   bool ok = false;
+  // bf16 inputs with a bf16 state: C and the state are exact bf16 operands,
+  // and C . h0 takes one 16x16x32 product per pair of column groups (lane
+  // i + 16 k feeds columns 16 gg + 4 k .. + 3 of both, the same slots in C
+  // and in the state); C stays as raw bits
+  constexpr bool kRawC = sizeof(TIn) == 2 && sizeof(TS) == 2;
   f32x4 cop[NG];  // lane (i + 16 k): C_i[16 gg + 4 k .. + 3], zero for i >= T
+  su32x2 craw[NG];  // the same as raw bits (kRawC)
   f32x4 cbop;     // lane (i + 16 k): C_i . B_(4 k + t), zero off i's root path
   int ancm = 0;   // anc[i]
 #pragma unroll
-  for (int gg = 0; gg < NG; ++gg) cop[gg] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int gg = 0; gg < NG; ++gg) {
+    cop[gg] = f32x4{0.f, 0.f, 0.f, 0.f};
+    craw[gg] = su32x2{0u, 0u};
+  }
   cbop = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // start of item it: tree bookkeeping on a new (layer, sequence), C operands
@@ -293,20 +309,37 @@ __global__ void __launch_bounds__(WPG * 64) verify_mfma_kernel(VerifyArgs a, int
       const float keep = i < T ? 1.0f : 0.0f;
       const TIn* cg = reinterpret_cast<const TIn*>(a.C) + (((int64_t)unit * T + ic) * G + g) * N + 4 * k;
       const TIn* bg = reinterpret_cast<const TIn*>(a.B) + (((int64_t)unit * T + ic) * G + g) * N + 4 * k;
-      f32x4 bop[NG];
-#pragma unroll
-      for (int gg = 0; gg < NG; ++gg) {
-        cop[gg] = load4<TIn>(cg + 16 * gg) * keep;
-        bop[gg] = load4<TIn>(bg + 16 * gg) * keep;
-      }
       // CB[v][u] = C_v . B_u: A = C rows, B = B rows (lane j + 16 k holds B_j)
       f32x4 cb = f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (kRawC) {
+        su32x2 braw[NG];
 #pragma unroll
-      for (int gg = 0; gg < NG; ++gg) {
-        cb = mfma4(cop[gg].x, bop[gg].x, cb);
-        cb = mfma4(cop[gg].y, bop[gg].y, cb);
-        cb = mfma4(cop[gg].z, bop[gg].z, cb);
-        cb = mfma4(cop[gg].w, bop[gg].w, cb);
+        for (int gg = 0; gg < NG; ++gg) {
+          craw[gg] = *reinterpret_cast<const su32x2*>(cg + 16 * gg);
+          braw[gg] = *reinterpret_cast<const su32x2*>(bg + 16 * gg);
+          if (i >= T) craw[gg] = braw[gg] = su32x2{0u, 0u};
+        }
+#pragma unroll
+        for (int gp = 0; gp < (NG + 1) / 2; ++gp) {
+          const su32x2 c1 = 2 * gp + 1 < NG ? craw[(2 * gp + 1) % NG] : su32x2{0u, 0u};
+          const su32x2 b1 = 2 * gp + 1 < NG ? braw[(2 * gp + 1) % NG] : su32x2{0u, 0u};
+          cb = mfma32(u32x4{craw[2 * gp].x, craw[2 * gp].y, c1.x, c1.y},
+                      u32x4{braw[2 * gp].x, braw[2 * gp].y, b1.x, b1.y}, cb);
+        }
+      } else {
+        f32x4 bop[NG];
+#pragma unroll
+        for (int gg = 0; gg < NG; ++gg) {
+          cop[gg] = load4<TIn>(cg + 16 * gg) * keep;
+          bop[gg] = load4<TIn>(bg + 16 * gg) * keep;
+        }
+#pragma unroll
+        for (int gg = 0; gg < NG; ++gg) {
+          cb = mfma4(cop[gg].x, bop[gg].x, cb);
+          cb = mfma4(cop[gg].y, bop[gg].y, cb);
+          cb = mfma4(cop[gg].z, bop[gg].z, cb);
+          cb = mfma4(cop[gg].w, bop[gg].w, cb);
+        }
       }
       // result layout: lane (u + 16 q) holds CB[4 q + r][u]; transpose through LDS
 #pragma unroll
@@ -448,15 +481,30 @@ __global__ void __launch_bounds__(WPG * 64) verify_mfma_kernel(VerifyArgs a, int
 #pragma unroll
     for (int tl = 0; tl < 4; ++tl) {
       f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (kRawC) {
 #pragma unroll
-      for (int gg = 0; gg < NG; ++gg) {
-        const int i = tl * NG + gg;  // static
-        const f32x4 h = SQ::to_f32(ring[i % RD]);
-        acc = mfma4(cop[gg].x, h.x, acc);
-        acc = mfma4(cop[gg].y, h.y, acc);
-        acc = mfma4(cop[gg].z, h.z, acc);
-        acc = mfma4(cop[gg].w, h.w, acc);
-        ring[i % RD] = i + RD < 4 * NG ? piece(cur, i + RD) : piece(nx, i + RD - 4 * NG);
+        for (int gp = 0; gp < (NG + 1) / 2; ++gp) {
+          const int i = tl * NG + 2 * gp;  // static
+          const bool two = 2 * gp + 1 < NG;
+          const su32x2 c1 = two ? craw[(2 * gp + 1) % NG] : su32x2{0u, 0u};
+          const su32x2 h0 = ring[i % RD];
+          const su32x2 h1 = two ? ring[(i + 1) % RD] : su32x2{0u, 0u};
+          acc = mfma32(u32x4{craw[2 * gp].x, craw[2 * gp].y, c1.x, c1.y}, u32x4{h0.x, h0.y, h1.x, h1.y}, acc);
+          ring[i % RD] = i + RD < 4 * NG ? piece(cur, i + RD) : piece(nx, i + RD - 4 * NG);
+          if (two)
+            ring[(i + 1) % RD] = i + 1 + RD < 4 * NG ? piece(cur, i + 1 + RD) : piece(nx, i + 1 + RD - 4 * NG);
+        }
+      } else {
+#pragma unroll
+        for (int gg = 0; gg < NG; ++gg) {
+          const int i = tl * NG + gg;  // static
+          const f32x4 h = SQ::to_f32(ring[i % RD]);
+          acc = mfma4(cop[gg].x, h.x, acc);
+          acc = mfma4(cop[gg].y, h.y, acc);
+          acc = mfma4(cop[gg].z, h.z, acc);
+          acc = mfma4(cop[gg].w, h.w, acc);
+          ring[i % RD] = i + RD < 4 * NG ? piece(cur, i + RD) : piece(nx, i + RD - 4 * NG);
+        }
       }
       ys[tl] = tile_end(cur, par, tl, acc);
       if (!ILV) store_tile(cur, tl, ys[tl]);
