@@ -46,6 +46,11 @@ VERIFY_SPECS = [
     (1, 2, 33, 4, 64, 128, 1, 4, False, False, "forest"),      # 17-64 nodes, fp32 inputs
     (1, 3, 20, 8, 16, 16, 1, 4, True, True, "forest"),         # heads of 16 channels
     (1, 2, 48, 8, 64, 128, 1, 4, True, False, "forest"),       # 8 one-head blocks: the role-split kernel
+    # bf16 products over pairs of column groups (up to 16 nodes): d_state
+    # 32, 64 (heads of 32 channels) and 256 (a ring of four pieces)
+    (1, 3, 12, 4, 64, 32, 1, 4, True, False, "forest"),
+    (2, 2, 9, 4, 32, 64, 2, 3, True, True, "forest"),
+    (1, 2, 16, 2, 64, 256, 1, 4, True, True, "forest"),
 ]
 COMMIT_SPECS = VERIFY_SPECS + [
     (1, 3, 12, 8, 40, 32, 1, 4, True, False, "forest"),        # headdim 40: commit takes every shape
