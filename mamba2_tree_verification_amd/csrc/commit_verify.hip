@@ -470,27 +470,37 @@ __global__ void __launch_bounds__(kCvWaves * kWave) commit_verify_kernel(CommitV
   // ======== from LDS: the path's conv and the new window; the next tree's
   // S and conv outputs ========
   const int len = s_misc[0];  // 0 when the commit fails: state and window pass through unchanged
-  if (wave == 0) {
-    const int c = c0 + lane, hh = c / P - h_lo;
-    float wj[4];
+  // conv weights of channel `lane` by taps back (0 = the token itself)
+  float wx[4];
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) wj[jj] = jj < W ? s_cw[lane * 4 + W - 1 - jj] : 0.0f;
-    const float cb = s_cb[lane];
-    float hist[3];  // raw inputs, newest first
-#pragma unroll
-    for (int r = 0; r < 3; ++r) hist[r] = r < W - 1 ? load_in(s_win, (W - 2 - r) * kCvRows + lane) : 0.0f;
-    for (int q = 0; q < len; ++q) {
+  for (int jj = 0; jj < 4; ++jj) wx[jj] = jj < W ? s_cw[lane * 4 + W - 1 - jj] : 0.0f;
+  const float cbias = s_cb[lane];
+  // the path's conv: its inputs are raw rows only, so its positions are
+  // independent; wave w takes positions q = w, w + 4, ... (lane = channel).
+  // Tap jj of position q reads element q + W - 1 - jj of (old window rows,
+  // path x rows).
+  {
+    const int hh = (c0 + lane) / P - h_lo;
+    for (int q = wave; q < len; q += kCvWaves) {
       const float xv = load_in(s_xp, q * kCvRows + lane);
-      float z = fmaf(wj[0], xv, cb);
+      float u[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int jj = 1; jj < 4; ++jj) {
+        if (jj < W) {
+          const int e = q + W - 1 - jj;
+          u[jj] = e < W - 1 ? load_in(s_win, e * kCvRows + lane) : load_in(s_xp, (e - (W - 1)) * kCvRows + lane);
+        }
+      }
+      float z = fmaf(wx[0], xv, cbias);
 #pragma unroll
       for (int jj = 1; jj < 4; ++jj)
-        if (jj < W) z = fmaf(wj[jj], hist[jj - 1], z);
+        if (jj < W) z = fmaf(wx[jj], u[jj], z);
       const float xt = d.silu ? silu_fast(z) : z;
       s_dtx[q * kCvRows + lane] = s_dtp[s_path[q] * 4 + hh] * xt;
-      hist[2] = hist[1];
-      hist[1] = hist[0];
-      hist[0] = xv;
     }
+  }
+  if (wave == 0) {
+    const int c = c0 + lane;
     // new window row r (oldest first) = element len + r of (old window, path x), bit for bit
     if (W > 1 && (!OPT || a.window_out)) {
       TIn* win_out = reinterpret_cast<TIn*>(a.window_out) + unit * (W - 1) * (int64_t)CH + c;
@@ -512,27 +522,41 @@ __global__ void __launch_bounds__(kCvWaves * kWave) commit_verify_kernel(CommitV
       s_S2[hh * kCvT + v] = acc * 1.4426950408889634f;
     }
   }
-  for (int i = tid; i < kCvT * kCvRows; i += kCvWaves * kWave) {
-    const int v = i / kCvRows, cl = i % kCvRows;
+  // the next tree's conv outputs: thread (wave, lane) takes channel lane of
+  // nodes wave, wave + 4, wave + 8, wave + 12 (each node uniform in its
+  // wave, so its tap sources are resolved once)
+  static_assert(kCvT == 4 * kCvWaves && kCvRows == kWave, "x~ mapping");
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int v = wave + kCvWaves * it;
     float xt = 0.0f;
     if (v < T) {
-      float z = fmaf(s_cw[cl * 4 + W - 1], load_in(s_xn, v * kCvRows + cl), s_cb[cl]);
       const int codes = s_cidx[v];
-      for (int jj = 1; jj < W; ++jj) {
-        const int code = (codes >> (8 * (jj - 1))) & 255;
-        float u;
-        if (code < T) {
-          u = load_in(s_xn, code * kCvRows + cl);
-        } else {  // committed window row code - T
-          const int e = len + code - T;
-          u = e < W - 1 ? load_in(s_win, e * kCvRows + cl) : load_in(s_xp, (e - (W - 1)) * kCvRows + cl);
+      float u[4];
+      u[0] = load_in(s_xn, v * kCvRows + lane);
+#pragma unroll
+      for (int jj = 1; jj < 4; ++jj) {
+        u[jj] = 0.0f;
+        if (jj < W) {
+          const int code = (codes >> (8 * (jj - 1))) & 255;
+          const TIn* src;
+          if (code < T) {
+            src = s_xn + code * kCvRows;
+          } else {  // committed window row code - T
+            const int e = len + code - T;
+            src = e < W - 1 ? s_win + e * kCvRows : s_xp + (e - (W - 1)) * kCvRows;
+          }
+          u[jj] = load_in(src, lane);
         }
-        z = fmaf(s_cw[cl * 4 + W - 1 - jj], u, z);
       }
+      float z = fmaf(wx[0], u[0], cbias);
+#pragma unroll
+      for (int jj = 1; jj < 4; ++jj)
+        if (jj < W) z = fmaf(wx[jj], u[jj], z);
       xt = d.silu ? silu_fast(z) : z;
     }
-    // MFMA B-operand layout: channel row cl, quad v / 4 swizzled
-    s_xt[cl * kCvT + 4 * ((v >> 2) ^ ((cl >> 2) & 3)) + (v & 3)] = xt;
+    // MFMA B-operand layout: channel row lane, quad v / 4 swizzled
+    s_xt[lane * kCvT + 4 * ((v >> 2) ^ ((lane >> 2) & 3)) + (v & 3)] = xt;
   }
   if constexpr (OPT) {
     if (xbc) {
