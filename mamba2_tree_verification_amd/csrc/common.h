@@ -43,13 +43,14 @@ __device__ __forceinline__ float load_in<bf16_t>(const bf16_t* p, int64_t i) {
 typedef float sf32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int su32x2 __attribute__((ext_vector_type(2)));
 
-// float32 to bfloat16 bits: nearest, ties to the even significand (adding
-// 0x7fff plus the kept LSB carries exactly past the halfway point); values
-// past the largest finite bf16 become infinite, NaN stays a quiet NaN
-__device__ __forceinline__ uint32_t bf16_round_bits(float f) {
-  const uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+// two fp32 values rounded to bf16 (first in the low half): the hardware
+// conversion v_cvt_pk_bf16_f32, round to nearest even, with subnormals kept
+// (the kernels run with fp32 denormals preserved); values past the largest
+// finite bf16 become infinite and NaN stays a quiet NaN
+__device__ __forceinline__ uint32_t bf16_round_pair(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
 // four consecutive state elements: Raw is what memory holds
@@ -81,8 +82,7 @@ struct StateQuad<bf16_t> {
                   __uint_as_float(r.y & 0xFFFF0000u)};
   }
   static __device__ __forceinline__ Raw from_f32(sf32x4 v) {
-    return su32x2{bf16_round_bits(v.x) | (bf16_round_bits(v.y) << 16),
-                  bf16_round_bits(v.z) | (bf16_round_bits(v.w) << 16)};
+    return su32x2{bf16_round_pair(v.x, v.y), bf16_round_pair(v.z, v.w)};
   }
   static __device__ __forceinline__ void store(bf16_t* p, Raw r) { *reinterpret_cast<su32x2*>(p) = r; }
   static __device__ __forceinline__ void store_nt(bf16_t* p, Raw r) {
