@@ -221,3 +221,33 @@ def test_round_state_bf16_failures():
     cstn = cst.cpu().numpy()
     assert cstn[1] == m.E_PATH and (cstn[[0, 2, 3]] == m.OK).all()
     check_round(case, s_out, w_out, y, cst, vst, [(0, b) for b in range(cfg.Bsz)])
+
+
+@pytest.mark.parametrize("spec", [(2, 3, 16, 8, 64, 128, 1, 4, True, True, "forest"),
+                                  (1, 4, 40, 4, 32, 64, 2, 3, False, False, "chain_or_star")],
+                         ids=["T16bf", "T40f32"])
+def test_commit_bf16_store_rounds_the_fp32_commit(spec):
+    """The commit's arithmetic is float32 whatever the stored state type, so
+    a bf16-state commit must store exactly the round-to-nearest-even of what
+    the float32-state commit computes from the same (widened) state: the
+    device rounding checked bit for bit against the oracle's rounding."""
+    cfg = cfg_of(spec, 112 + (spec[2] == 40))
+    log("bf16 store vs rounded fp32 commit %s" % (spec,))
+    case = GpuCase(cfg)
+    g = case.g
+    s_bf = torch.empty_like(g.state)
+    w_bf = torch.empty_like(g.window)
+    st_bf = torch.empty((cfg.Bsz,), dtype=torch.int32, device="cuda")
+    m.commit(case.dims, case.prm, g.parent, g.path, g.path_len, g.x, g.B, g.dt_raw, g.window, g.state, w_bf, s_bf,
+             st_bf)
+    dims32 = m.make_dims(cfg.L, cfg.Bsz, cfg.T, cfg.H, cfg.P, cfg.N, cfg.G, cfg.W, cfg.bf16, cfg.silu)
+    s32_in = g.state.float()
+    s32 = torch.empty_like(s32_in)
+    w32 = torch.empty_like(g.window)
+    st32 = torch.empty_like(st_bf)
+    m.commit(dims32, case.prm, g.parent, g.path, g.path_len, g.x, g.B, g.dt_raw, g.window, s32_in, w32, s32, st32)
+    torch.cuda.synchronize()
+    assert torch.equal(st_bf, st32) and (st32.cpu().numpy() == 0).all()
+    assert torch.equal(w_bf, w32)
+    r, _ = oracle.get().round_bf16(s32.double().cpu().numpy())
+    assert np.array_equal(s_bf.double().cpu().numpy(), r)
