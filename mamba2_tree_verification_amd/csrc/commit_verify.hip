@@ -232,10 +232,14 @@ __global__ void __launch_bounds__(kCvWaves * kWave) commit_verify_kernel(CommitV
   }
   // per-head scalars: wave 0 the next tree's dt, wave 1 the previous tree's
   const int sv = (lane >> 2), sh = lane & 3;
-  float r_dt = 0.0f, r_A = 0.0f, r_bias = 0.0f, r_D = 0.0f;
+  // dt_raw as raw bits, widened only after the state loads are out (a
+  // conversion here would make waves 0 and 1 wait for it first)
+  uint32_t r_dt = 0;
+  float r_A = 0.0f, r_bias = 0.0f, r_D = 0.0f;
   if (wave < 2 && sv < T && sh < HW) {
-    const TIn* src = reinterpret_cast<const TIn*>(wave == 0 ? a.dt_raw : a.dt_prev) + unit * T * H;
-    r_dt = load_in(src, (int64_t)sv * H + h_lo + sh);
+    const int64_t di = unit * T * H + (int64_t)sv * H + h_lo + sh;
+    const void* src = wave == 0 ? a.dt_raw : a.dt_prev;
+    r_dt = E == 2 ? (uint32_t)reinterpret_cast<const uint16_t*>(src)[di] : reinterpret_cast<const uint32_t*>(src)[di];
     r_A = a.prm.A[(int64_t)l * H + h_lo + sh];
     r_bias = a.prm.dt_bias[(int64_t)l * H + h_lo + sh];
   }
@@ -290,6 +294,7 @@ __global__ void __launch_bounds__(kCvWaves * kWave) commit_verify_kernel(CommitV
   typename SQ::Raw hraw[NG];
 #pragma unroll
   for (int gg = 0; gg < NG; ++gg) hraw[gg] = SQ::load(sin + 16 * gg);
+  asm volatile("" : "+v"(r_dt));  // (keeps dt_raw's widening below the state loads)
 
   // to LDS
   if (tid < T) {
@@ -308,7 +313,7 @@ __global__ void __launch_bounds__(kCvWaves * kWave) commit_verify_kernel(CommitV
     }
   }
   if (wave < 2 && sv < T && sh < HW) {
-    const float dt = softplus_f32(r_dt + r_bias);
+    const float dt = softplus_f32(__uint_as_float(E == 2 ? r_dt << 16 : r_dt) + r_bias);
     if (wave == 0) {
       s_dt[sh * kCvT + sv] = dt;
       s_S[sh * kCvT + sv] = dt * r_A;
