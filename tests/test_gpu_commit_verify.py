@@ -379,3 +379,28 @@ def test_draft_decode_then_rollback(bf16):
             _, s_pref, w_pref = o.scan(u, n, cfg.H, cfg.P, cfg.N, cfg.G, cfg.W)
             assert_close(s_out[l, b].double().cpu().numpy(), s_pref, "rollback state l=%d b=%d" % (l, b))
             assert np.array_equal(window_f64(cfg, w_out, l, b), w_pref), "rollback window l=%d b=%d" % (l, b)
+
+
+# ----------------------------------------------------------------------------
+# the fused round along long accepted paths, every conv width
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("W", [1, 2, 3, 4])
+def test_fused_round_long_paths_every_width(W):
+    """The previous tree is a 16-chain whose accepted paths run 0, 1, 3, 4,
+    5, 8, 15 and 16 nodes (the fused kernel spreads the path's conv over its
+    four waves), the next tree a random forest; conv widths 1-4, SiLU and a
+    bias on the even widths, bf16 and fp32 inputs alternating."""
+    cfg = C.Config(260 + W, "long-paths", 2, 8, 16, 4, 64, 64, 1, W, W % 2 == 1, 0.5, "chain", W % 2 == 0,
+                   W % 2 == 0)
+    prev = C.make_inputs(cfg)
+    for b, n in enumerate([0, 1, 3, 4, 5, 8, 15, 16]):
+        prev.path[b, :] = -1
+        prev.path[b, :n] = np.arange(n, dtype=np.int32)
+        prev.path_len[b] = n
+    nxt = C.make_inputs(cfg.replace(cid=cfg.cid + 500, tree="forest"), skip=NEXT_ONLY)
+    log("fused round, 16-chain paths, W=%d" % W)
+    step = Step(cfg, prev=prev, nxt=nxt)
+    assert fused_applies(cfg)
+    out = step.run()
+    check(step, out, [(l, b) for l in range(cfg.L) for b in range(cfg.Bsz)])
