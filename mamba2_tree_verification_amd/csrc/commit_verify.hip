@@ -290,10 +290,26 @@ __global__ void __launch_bounds__(kCvWaves * kWave) commit_verify_kernel(CommitV
 
   // the state last: the small rows above reach LDS while it is still in flight
   // (loads complete in issue order)
-  const TS* sin = reinterpret_cast<const TS*>(a.state_in) + (unit * DI + c0 + wave * 16 + j) * (int64_t)N + 4 * k;
+  // Columns of quad gg in lane j + 16 k: 16 gg + 4 k .. + 3, or with a bf16
+  // state (and an even number of column groups) 32 (gg / 2) + 8 k + 4 (gg % 2)
+  // .. + 3, so that a pair of quads is 8 consecutive columns and the state
+  // moves in 16-byte accesses.  C, B and the state take the same columns of
+  // a lane (the contractions only need them to agree).
+  constexpr bool kWide = sizeof(TS) == 2 && NG % 2 == 0 && !OPT;
+  auto colq = [&](int gg) { return kWide ? 32 * (gg >> 1) + 8 * k + 4 * (gg & 1) : 16 * gg + 4 * k; };
+  const TS* sin = reinterpret_cast<const TS*>(a.state_in) + (unit * DI + c0 + wave * 16 + j) * (int64_t)N;
   typename SQ::Raw hraw[NG];
+  if constexpr (kWide) {
 #pragma unroll
-  for (int gg = 0; gg < NG; ++gg) hraw[gg] = SQ::load(sin + 16 * gg);
+    for (int gp = 0; gp < NG / 2; ++gp) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(sin + colq(2 * gp));
+      hraw[2 * gp] = u32x2{w.x, w.y};
+      hraw[2 * gp + 1] = u32x2{w.z, w.w};
+    }
+  } else {
+#pragma unroll
+    for (int gg = 0; gg < NG; ++gg) hraw[gg] = SQ::load(sin + colq(gg));
+  }
   asm volatile("" : "+v"(r_dt));  // (keeps dt_raw's widening below the state loads)
 
   // to LDS
@@ -593,11 +609,11 @@ __global__ void __launch_bounds__(kCvWaves * kWave) commit_verify_kernel(CommitV
     for (int q = 0; q < len; ++q) {
       const float dA = s_dAp[s_path[q] * 4 + hh];
       const float cx = s_dtx[q * kCvRows + row];
-      const TIn* bp = reinterpret_cast<const TIn*>(s_Bp + q * rs) + 4 * k;
+      const TIn* bp = reinterpret_cast<const TIn*>(s_Bp + q * rs);
       const float* bpt = s_Bpt + q * N + 4 * k;
 #pragma unroll
       for (int gg = 0; gg < NG; ++gg) {
-        const f32x4 bq = xbc ? *reinterpret_cast<const f32x4*>(bpt + 16 * gg) : load4<TIn>(bp + 16 * gg);
+        const f32x4 bq = xbc ? *reinterpret_cast<const f32x4*>(bpt + 16 * gg) : load4<TIn>(bp + colq(gg));
         // scale in place, then one fused multiply-add: both steps write
         // the state's own registers (no copy of the state per node)
         hq[gg] *= dA;
@@ -615,15 +631,21 @@ __global__ void __launch_bounds__(kCvWaves * kWave) commit_verify_kernel(CommitV
       hq[gg] = SQ::to_f32(hraw[gg]);
     }
     if (!OPT || a.state_out) {
-      TS* so = reinterpret_cast<TS*>(a.state_out) + (unit * DI + c0 + row) * (int64_t)N + 4 * k;
+      TS* so = reinterpret_cast<TS*>(a.state_out) + (unit * DI + c0 + row) * (int64_t)N;
+      if constexpr (kWide) {
 #pragma unroll
-      for (int gg = 0; gg < NG; ++gg) SQ::store(so + 16 * gg, hraw[gg]);
+        for (int gp = 0; gp < NG / 2; ++gp)
+          *reinterpret_cast<u32x4*>(so + colq(2 * gp)) =
+              u32x4{hraw[2 * gp].x, hraw[2 * gp].y, hraw[2 * gp + 1].x, hraw[2 * gp + 1].y};
+      } else {
+#pragma unroll
+        for (int gg = 0; gg < NG; ++gg) SQ::store(so + colq(gg), hraw[gg]);
+      }
     }
 
     // C . h on the matrix cores: lane (c + 16 q) ends with (C_{4q+r} . h_c)
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
     const bool live = j < T;
-    const TIn* cp = reinterpret_cast<const TIn*>(s_C + j * rs) + 4 * k;
     f32x4 cbx = f32x4{0.f, 0.f, 0.f, 0.f};  // with the xBC conv: C_v . B_u, formed below
     // with the xBC conv, the raw rows that tap jj (steps back) of node j
     // reads: the node itself, an ancestor, or past the root a row of the
@@ -661,8 +683,9 @@ __global__ void __launch_bounds__(kCvWaves * kWave) commit_verify_kernel(CommitV
     if constexpr (kBf16Ch) {
 #pragma unroll
       for (int gp = 0; gp < (NG + 1) / 2; ++gp) {
-        const u32x2 c0 = *reinterpret_cast<const u32x2*>(cp + 32 * gp);
-        const u32x2 c1 = 2 * gp + 1 < NG ? *reinterpret_cast<const u32x2*>(cp + 32 * gp + 16) : u32x2{0u, 0u};
+        const TIn* cq0 = reinterpret_cast<const TIn*>(s_C + j * rs);
+        const u32x2 c0 = *reinterpret_cast<const u32x2*>(cq0 + colq(2 * gp));
+        const u32x2 c1 = 2 * gp + 1 < NG ? *reinterpret_cast<const u32x2*>(cq0 + colq((2 * gp + 1) % NG)) : u32x2{0u, 0u};
         const u32x2 h0 = hraw[2 * gp];
         const u32x2 h1 = 2 * gp + 1 < NG ? hraw[(2 * gp + 1) % NG] : u32x2{0u, 0u};
         u32x4 ca = u32x4{c0.x, c0.y, c1.x, c1.y};
@@ -707,10 +730,10 @@ __global__ void __launch_bounds__(kCvWaves * kWave) commit_verify_kernel(CommitV
             cq = ac;
             bxq = ab;
           } else {
-            cq = load4<TIn>(cp + 16 * gg);
+            cq = load4<TIn>(reinterpret_cast<const TIn*>(s_C + j * rs) + colq(gg));
           }
         } else {
-          cq = load4<TIn>(cp + 16 * gg);
+          cq = load4<TIn>(reinterpret_cast<const TIn*>(s_C + j * rs) + colq(gg));
         }
         if (!live) cq = f32x4{0.f, 0.f, 0.f, 0.f};
         acc = mfma4(cq.x, hq[gg].x, acc);
