@@ -183,8 +183,26 @@ __global__ void __launch_bounds__(WPG * 64) verify_mfma_kernel(VerifyArgs a, int
     return SQ::load(sbase + ((int64_t)item * kSlab + (i / NG) * (ILV ? 1 : 16)) * N + (i % NG) * 16);
   };
   typename SQ::Raw ring[RD];  // raw: converted where the products take it
+  // With bf16 inputs and a bf16 state (kRawC below) and an even number of
+  // column groups, pieces go in pairs: lane j + 16 k loads the 8 consecutive
+  // columns 32 p + 8 k .. + 7 of column-group pair p with one 16-byte load,
+  // and C and B take the same columns (colq).  ring2 holds RD / 2 pairs.
+  constexpr bool kWide = sizeof(TIn) == 2 && sizeof(TS) == 2 && NG % 2 == 0;
+  auto colq = [&](int gg) { return kWide ? 32 * (gg >> 1) + 8 * k + 4 * (gg & 1) : 16 * gg + 4 * k; };
+  const TS* sbase2 = reinterpret_cast<const TS*>(a.state) + (int64_t)(ILV ? 4 * j : j) * N + 8 * k;
+  auto pair = [&](int item, int p) {  // pieces 2 p and 2 p + 1
+    const int i = 2 * p;
+    return *reinterpret_cast<const u32x4*>(sbase2 + ((int64_t)item * kSlab + (i / NG) * (ILV ? 1 : 16)) * N +
+                                           32 * ((i % NG) >> 1));
+  };
+  u32x4 ring2[kWide ? RD / 2 : 1];
+  if constexpr (kWide) {
 #pragma unroll
-  for (int i = 0; i < RD; ++i) ring[i] = piece(cur, i);
+    for (int p = 0; p < RD / 2; ++p) ring2[p] = pair(cur, p);
+  } else {
+#pragma unroll
+    for (int i = 0; i < RD; ++i) ring[i] = piece(cur, i);
+  }
 
   // ---- per-item inputs, loaded one item ahead ----
   const TIn* xg = reinterpret_cast<const TIn*>(a.x);
@@ -309,14 +327,15 @@ __global__ void __launch_bounds__(WPG * 64) verify_mfma_kernel(VerifyArgs a, int
       const float keep = i < T ? 1.0f : 0.0f;
       const TIn* cg = reinterpret_cast<const TIn*>(a.C) + (((int64_t)unit * T + ic) * G + g) * N + 4 * k;
       const TIn* bg = reinterpret_cast<const TIn*>(a.B) + (((int64_t)unit * T + ic) * G + g) * N + 4 * k;
+      const TIn* cg0 = cg - 4 * k, *bg0 = bg - 4 * k;  // row starts (for colq)
       // CB[v][u] = C_v . B_u: A = C rows, B = B rows (lane j + 16 k holds B_j)
       f32x4 cb = f32x4{0.f, 0.f, 0.f, 0.f};
       if constexpr (kRawC) {
         su32x2 braw[NG];
 #pragma unroll
         for (int gg = 0; gg < NG; ++gg) {
-          craw[gg] = *reinterpret_cast<const su32x2*>(cg + 16 * gg);
-          braw[gg] = *reinterpret_cast<const su32x2*>(bg + 16 * gg);
+          craw[gg] = *reinterpret_cast<const su32x2*>(cg0 + colq(gg));
+          braw[gg] = *reinterpret_cast<const su32x2*>(bg0 + colq(gg));
           if (i >= T) craw[gg] = braw[gg] = su32x2{0u, 0u};
         }
 #pragma unroll
@@ -481,7 +500,15 @@ __global__ void __launch_bounds__(WPG * 64) verify_mfma_kernel(VerifyArgs a, int
 #pragma unroll
     for (int tl = 0; tl < 4; ++tl) {
       f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-      if constexpr (kRawC) {
+      if constexpr (kWide) {
+#pragma unroll
+        for (int gp = 0; gp < NG / 2; ++gp) {
+          const int pp = tl * (NG / 2) + gp;  // pair index within the item, static
+          acc = mfma32(u32x4{craw[2 * gp].x, craw[2 * gp].y, craw[2 * gp + 1].x, craw[2 * gp + 1].y},
+                       ring2[pp % (RD / 2)], acc);
+          ring2[pp % (RD / 2)] = pp + RD / 2 < 2 * NG ? pair(cur, pp + RD / 2) : pair(nx, pp + RD / 2 - 2 * NG);
+        }
+      } else if constexpr (kRawC) {
 #pragma unroll
         for (int gp = 0; gp < (NG + 1) / 2; ++gp) {
           const int i = tl * NG + 2 * gp;  // static
