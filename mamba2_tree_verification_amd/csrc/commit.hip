@@ -57,12 +57,27 @@ commit_kernel(CommitArgs a, int HWMAX) {
   float* s_B = reinterpret_cast<float*>(s_ax + kCommitChunk * kCommitRows);     // [chunk][N]
 
   // ---- issue the state loads first (QPT quads per thread) ----
+  // A bf16 state moves in 16-byte accesses: access it2 of a thread is the 8
+  // consecutive elements 8 (tid + 256 it2) .., i.e. quads 2 it2 and 2 it2 + 1;
+  // otherwise quad it is the 4 elements 4 (tid + 256 it) ..
+  constexpr bool kWide = sizeof(TS) == 2 && QPT % 2 == 0;
+  typedef unsigned int u32x4c __attribute__((ext_vector_type(4)));
   const TS* sin = reinterpret_cast<const TS*>(a.state_in) + (unit * DI + c0) * (int64_t)N;
   typename SQ::Raw hq[QPT];
+  if constexpr (kWide) {
 #pragma unroll
-  for (int it = 0; it < QPT; ++it) {
-    const int qi = threadIdx.x + it * kCommitThreads;
-    hq[it] = SQ::load_nt(sin + 4 * qi);
+    for (int it2 = 0; it2 < QPT / 2; ++it2) {
+      const int qo = threadIdx.x + it2 * kCommitThreads;
+      const u32x4c w = __builtin_nontemporal_load(reinterpret_cast<const u32x4c*>(sin + 8 * qo));
+      hq[2 * it2] = typename SQ::Raw{w.x, w.y};
+      hq[2 * it2 + 1] = typename SQ::Raw{w.z, w.w};
+    }
+  } else {
+#pragma unroll
+    for (int it = 0; it < QPT; ++it) {
+      const int qi = threadIdx.x + it * kCommitThreads;
+      hq[it] = SQ::load_nt(sin + 4 * qi);
+    }
   }
 
   // ---- validate tree and path ----
@@ -204,23 +219,51 @@ commit_kernel(CommitArgs a, int HWMAX) {
     }
     __syncthreads();  // (dA, dt x~) of the chunk
     // ---- state update along the chunk ----
-    // quad it of a thread is row tid / qpr + it * (256 / qpr), columns
-    // 4 (tid % qpr) .. +3: qpr = N / 4 divides 256, so every quad of a
-    // thread shares its B columns and one B read per node serves them all
+    // every access of a thread shares its B columns (N / 4 and N / 8 divide
+    // 256), so one B read per node serves all of them
+    if constexpr (kWide) {
+      constexpr int opr = N / 8;  // 8-element accesses per row
 #pragma unroll 1
-    for (int kk = 0; kk < kn; ++kk) {
-      const f32x4 bq = *reinterpret_cast<const f32x4*>(s_B + kk * N + (threadIdx.x % qpr) * 4);
+      for (int kk = 0; kk < kn; ++kk) {
+        const f32x4 bq0 = *reinterpret_cast<const f32x4*>(s_B + kk * N + (threadIdx.x % opr) * 8);
+        const f32x4 bq1 = *reinterpret_cast<const f32x4*>(s_B + kk * N + (threadIdx.x % opr) * 8 + 4);
 #pragma unroll
-      for (int it = 0; it < QPT; ++it) {
-        const int row = (threadIdx.x + it * kCommitThreads) / qpr;
-        const float2 ax = s_ax[kk * kCommitRows + row];
-        // scale in place, then one fused multiply-add: both steps write
-        // the state's own registers (no copy of the state per node)
-        h[it] *= ax.x;
-        h[it].x = fmaf(ax.y, bq.x, h[it].x);
-        h[it].y = fmaf(ax.y, bq.y, h[it].y);
-        h[it].z = fmaf(ax.y, bq.z, h[it].z);
-        h[it].w = fmaf(ax.y, bq.w, h[it].w);
+        for (int it2 = 0; it2 < QPT / 2; ++it2) {
+          const int row = (threadIdx.x + it2 * kCommitThreads) / opr;
+          const float2 ax = s_ax[kk * kCommitRows + row];
+          f32x4& h0 = h[2 * it2];
+          f32x4& h1 = h[2 * it2 + 1];
+          h0 *= ax.x;
+          h1 *= ax.x;
+          h0.x = fmaf(ax.y, bq0.x, h0.x);
+          h0.y = fmaf(ax.y, bq0.y, h0.y);
+          h0.z = fmaf(ax.y, bq0.z, h0.z);
+          h0.w = fmaf(ax.y, bq0.w, h0.w);
+          h1.x = fmaf(ax.y, bq1.x, h1.x);
+          h1.y = fmaf(ax.y, bq1.y, h1.y);
+          h1.z = fmaf(ax.y, bq1.z, h1.z);
+          h1.w = fmaf(ax.y, bq1.w, h1.w);
+        }
+      }
+    } else {
+      // quad it of a thread is row tid / qpr + it * (256 / qpr), columns
+      // 4 (tid % qpr) .. +3: qpr = N / 4 divides 256, so every quad of a
+      // thread shares its B columns and one B read per node serves them all
+#pragma unroll 1
+      for (int kk = 0; kk < kn; ++kk) {
+        const f32x4 bq = *reinterpret_cast<const f32x4*>(s_B + kk * N + (threadIdx.x % qpr) * 4);
+#pragma unroll
+        for (int it = 0; it < QPT; ++it) {
+          const int row = (threadIdx.x + it * kCommitThreads) / qpr;
+          const float2 ax = s_ax[kk * kCommitRows + row];
+          // scale in place, then one fused multiply-add: both steps write
+          // the state's own registers (no copy of the state per node)
+          h[it] *= ax.x;
+          h[it].x = fmaf(ax.y, bq.x, h[it].x);
+          h[it].y = fmaf(ax.y, bq.y, h[it].y);
+          h[it].z = fmaf(ax.y, bq.z, h[it].z);
+          h[it].w = fmaf(ax.y, bq.w, h[it].w);
+        }
       }
     }
   }
@@ -231,10 +274,19 @@ commit_kernel(CommitArgs a, int HWMAX) {
       if (r < W - 1) win_out[(int64_t)r * CH + cc] = nw[r];
   }
   TS* sout = reinterpret_cast<TS*>(a.state_out) + (unit * DI + c0) * (int64_t)N;
+  if constexpr (kWide) {
 #pragma unroll
-  for (int it = 0; it < QPT; ++it) {
-    const int qi = threadIdx.x + it * kCommitThreads;
-    SQ::store_nt(sout + 4 * qi, SQ::from_f32(h[it]));
+    for (int it2 = 0; it2 < QPT / 2; ++it2) {
+      const int qo = threadIdx.x + it2 * kCommitThreads;
+      const typename SQ::Raw r0 = SQ::from_f32(h[2 * it2]), r1 = SQ::from_f32(h[2 * it2 + 1]);
+      __builtin_nontemporal_store(u32x4c{r0.x, r0.y, r1.x, r1.y}, reinterpret_cast<u32x4c*>(sout + 8 * qo));
+    }
+  } else {
+#pragma unroll
+    for (int it = 0; it < QPT; ++it) {
+      const int qi = threadIdx.x + it * kCommitThreads;
+      SQ::store_nt(sout + 4 * qi, SQ::from_f32(h[it]));
+    }
   }
 }
 
