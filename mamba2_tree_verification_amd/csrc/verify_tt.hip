@@ -173,11 +173,6 @@ __device__ __forceinline__ double root_path_sum(double acc, int up, int v) {
   return acc;
 }
 
-// conv outputs [channel][node] in the MFMA B-operand layout: quad q (nodes
-// 4 q .. 4 q + 3) of channel row c sits at quad q ^ (c & 15), so that the 16
-// channels a wave reads at once fall on different banks
-__device__ __forceinline__ int xt_at(int c, int v) { return c * kTtMaxT + 4 * ((v >> 2) ^ (c & 15)) + (v & 3); }
-
 // M[v][u0 .. u0 + 3] of one head: exp(S_v - S_u) dt_u (C_v . B_u) where u is
 // on v's root path (ancestor bits ancv), zero elsewhere, plus D on the
 // diagonal; S in base-2 units, fp64 (the difference is taken before rounding)
@@ -597,6 +592,9 @@ __global__ void __launch_bounds__(kTtThreads) verify_tt_kernel(VerifyArgs a, int
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) xq[r] = 4 * q + r < T ? xq[r] : 0.0f;
+        // conv outputs [channel][node] in the MFMA B-operand layout: quad q
+        // (nodes 4 q .. 4 q + 3) of channel row cl sits at quad q ^ (cl & 15),
+        // so that the 16 channels a wave reads at once fall on different banks
         *reinterpret_cast<f32x4*>(s_xt + cl * kTtMaxT + 4 * (q ^ (cl & 15))) = xq;
       }
     }
@@ -1055,6 +1053,7 @@ __global__ void __launch_bounds__(kWsThreads) verify_tt_ws_kernel(VerifyArgs a, 
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) xq[r] = 4 * q + r < T ? xq[r] : 0.0f;
+            // (the swizzled [channel][node] layout of verify_tt_kernel's conv outputs)
             *reinterpret_cast<f32x4*>(xt + cl * kTtMaxT + 4 * (q ^ (cl & 15))) = xq;
           }
         }
