@@ -5,8 +5,10 @@ The functions ``ssm_tree_verify``, ``ssm_tree_commit``,
 ``ssm_tree_abi_version`` mirror the C ABI in ``include/ssm_tree.h`` one to
 one and take raw device addresses.  The ``verify`` / ``commit`` /
 ``commit_verify`` / ``plan`` helpers accept torch tensors on the GPU,
-check their dtypes and contiguity, pass ``data_ptr()`` and the current HIP
-stream, and raise ``SsmTreeError`` on a nonzero return.  Every step of the
+check their dtypes (inputs in ``dims.in_dtype``, the state in the dtype its
+flag names), contiguity and element counts against the dims, raising
+``ValueError`` before the library is called, pass ``data_ptr()`` and the
+current HIP stream, and raise ``SsmTreeError`` on a nonzero return.  Every step of the
 computation runs in the HIP kernels; there is no CPU fallback.
 """
 from __future__ import annotations
@@ -144,14 +146,21 @@ def make_dims(L, Bsz, T, H, P, N, G, W, bf16: bool, silu: bool = False, fifo: bo
 def make_params(A, D, dt_bias, conv_w, conv_b=None) -> Params:
     for t in (A, D, dt_bias, conv_w, conv_b):
         _check(t, "float32")
-    return Params(_ptr(A), _ptr(D), _ptr(dt_bias), _ptr(conv_w), _ptr(conv_b))
+    p = Params(_ptr(A), _ptr(D), _ptr(dt_bias), _ptr(conv_w), _ptr(conv_b))
+    # element counts, checked against the dims of each call
+    p.numels = tuple(None if t is None else t.numel() for t in (A, D, dt_bias, conv_w, conv_b))
+    return p
+
+
+def _on_device(t) -> bool:
+    return t.is_cuda
 
 
 def _check(t, kind):
     if t is None:
         return
     import torch
-    if not t.is_cuda:
+    if not _on_device(t):
         raise ValueError("tensor must be on the GPU")
     if not t.is_contiguous():
         raise ValueError("tensor must be contiguous")
@@ -165,12 +174,52 @@ def _state_kind(dims: Dims) -> str:
     return "state_bf16" if dims.flags & SSM_TREE_STATE_BF16 else "state"
 
 
+def _sizes(dims: Dims) -> dict:
+    """Element count of every tensor argument, from the layouts in
+    include/ssm_tree.h."""
+    L, Bsz, T, H, P, N, G, W = (dims.n_layers, dims.batch, dims.n_nodes, dims.nheads, dims.headdim, dims.d_state,
+                                dims.ngroups, dims.conv_width)
+    di = H * P
+    ch = di + (2 * G * N if dims.flags & SSM_TREE_CONV_XBC else 0)
+    U = L * Bsz
+    return dict(tok=U * T * di, bc=U * T * G * N, dt=U * T * H, window=U * (W - 1) * ch, state=U * di * N,
+                tree=Bsz * T, seq=Bsz, head=L * H, conv_w=L * ch * W, conv_b=L * ch)
+
+
+def _check_call(dims: Dims, params: Params, items) -> None:
+    """Dtype and size of every tensor of a call, before anything reaches
+    the library: inputs in the dims' input dtype, the state in the dtype
+    its flag names, and each element count exactly what the dims imply
+    (a short tensor would otherwise be read or written past its end)."""
+    import torch
+    ind = torch.bfloat16 if dims.in_dtype == SSM_TREE_BF16 else torch.float32
+    want = _sizes(dims)
+    for name, t, kind, size in items:
+        if t is None:
+            continue
+        _check(t, kind)
+        if kind == "in" and t.dtype != ind:
+            raise ValueError("%s: dtype %s, but dims.in_dtype asks for %s" % (name, t.dtype, ind))
+        if size == "window" and dims.conv_width == 1:
+            continue  # no window rows: never read
+        if t.numel() != want[size]:
+            raise ValueError("%s: %d elements, the dims imply %d" % (name, t.numel(), want[size]))
+    numels = getattr(params, "numels", None)
+    if numels is not None:
+        for name, n, size in zip(("A", "D", "dt_bias", "conv_w", "conv_b"), numels,
+                                 ("head", "head", "head", "conv_w", "conv_b")):
+            if n is not None and n != want[size]:
+                raise ValueError("params.%s: %d elements, the dims imply %d" % (name, n, want[size]))
+
+
 def verify(dims: Dims, params: Params, parent, x, B, C, dt_raw, conv_window, state, y, seq_status=None,
            stream=None, z=None):
     """ssm_tree_verify; z (optional) gates y by silu(z)."""
-    for t, k in ((parent, "int32"), (x, "in"), (B, "in"), (C, "in"), (dt_raw, "in"), (z, "in"),
-                 (conv_window, "in"), (state, _state_kind(dims)), (y, "float32"), (seq_status, "int32")):
-        _check(t, k)
+    sk = _state_kind(dims)
+    _check_call(dims, params, (("parent", parent, "int32", "tree"), ("x", x, "in", "tok"), ("B", B, "in", "bc"),
+                               ("C", C, "in", "bc"), ("dt_raw", dt_raw, "in", "dt"), ("z", z, "in", "tok"),
+                               ("conv_window", conv_window, "in", "window"), ("state", state, sk, "state"),
+                               ("y", y, "float32", "tok"), ("seq_status", seq_status, "int32", "seq")))
     rc = ssm_tree_verify(dims, params, _ptr(parent), _ptr(x), _ptr(B), _ptr(C), _ptr(dt_raw), _ptr(z),
                          _ptr(conv_window), _ptr(state), _ptr(y), _ptr(seq_status), _stream(stream))
     if rc != OK:
@@ -180,10 +229,13 @@ def verify(dims: Dims, params: Params, parent, x, B, C, dt_raw, conv_window, sta
 def commit(dims: Dims, params: Params, parent, path, path_len, x, B, dt_raw, conv_window_in, state_in,
            conv_window_out, state_out, seq_status=None, stream=None, C=None):
     """ssm_tree_commit; C (the raw C rows) is needed only with the xBC conv."""
-    for t, k in ((parent, "int32"), (path, "int32"), (path_len, "int32"), (x, "in"), (B, "in"), (C, "in"),
-                 (dt_raw, "in"), (conv_window_in, "in"), (state_in, _state_kind(dims)), (conv_window_out, "in"),
-                 (state_out, _state_kind(dims)), (seq_status, "int32")):
-        _check(t, k)
+    sk = _state_kind(dims)
+    _check_call(dims, params, (("parent", parent, "int32", "tree"), ("path", path, "int32", "tree"),
+                               ("path_len", path_len, "int32", "seq"), ("x", x, "in", "tok"), ("B", B, "in", "bc"),
+                               ("C", C, "in", "bc"), ("dt_raw", dt_raw, "in", "dt"),
+                               ("conv_window_in", conv_window_in, "in", "window"), ("state_in", state_in, sk, "state"),
+                               ("conv_window_out", conv_window_out, "in", "window"),
+                               ("state_out", state_out, sk, "state"), ("seq_status", seq_status, "int32", "seq")))
     rc = ssm_tree_commit(dims, params, _ptr(parent), _ptr(path), _ptr(path_len), _ptr(x), _ptr(B), _ptr(C),
                          _ptr(dt_raw), _ptr(conv_window_in), _ptr(state_in), _ptr(conv_window_out),
                          _ptr(state_out), _ptr(seq_status), _stream(stream))
@@ -196,12 +248,18 @@ def commit_verify(dims: Dims, params: Params, parent_prev, path, path_len, x_pre
                   commit_status=None, verify_status=None, stream=None, C_prev=None, z=None):
     """ssm_tree_commit_verify; C_prev is needed only with the xBC conv, z
     (optional) gates the next tree's y by silu(z)."""
-    for t, k in ((parent_prev, "int32"), (path, "int32"), (path_len, "int32"), (x_prev, "in"), (B_prev, "in"),
-                 (C_prev, "in"), (dt_raw_prev, "in"), (conv_window_in, "in"), (state_in, _state_kind(dims)),
-                 (conv_window_out, "in"), (state_out, _state_kind(dims)), (parent, "int32"), (x, "in"), (B, "in"),
-                 (C, "in"), (dt_raw, "in"), (z, "in"), (y, "float32"), (commit_status, "int32"),
-                 (verify_status, "int32")):
-        _check(t, k)
+    sk = _state_kind(dims)
+    _check_call(dims, params, (("parent_prev", parent_prev, "int32", "tree"), ("path", path, "int32", "tree"),
+                               ("path_len", path_len, "int32", "seq"), ("x_prev", x_prev, "in", "tok"),
+                               ("B_prev", B_prev, "in", "bc"), ("C_prev", C_prev, "in", "bc"),
+                               ("dt_raw_prev", dt_raw_prev, "in", "dt"),
+                               ("conv_window_in", conv_window_in, "in", "window"), ("state_in", state_in, sk, "state"),
+                               ("conv_window_out", conv_window_out, "in", "window"),
+                               ("state_out", state_out, sk, "state"), ("parent", parent, "int32", "tree"),
+                               ("x", x, "in", "tok"), ("B", B, "in", "bc"), ("C", C, "in", "bc"),
+                               ("dt_raw", dt_raw, "in", "dt"), ("z", z, "in", "tok"), ("y", y, "float32", "tok"),
+                               ("commit_status", commit_status, "int32", "seq"),
+                               ("verify_status", verify_status, "int32", "seq")))
     rc = ssm_tree_commit_verify(dims, params, _ptr(parent_prev), _ptr(path), _ptr(path_len), _ptr(x_prev),
                                 _ptr(B_prev), _ptr(C_prev), _ptr(dt_raw_prev), _ptr(conv_window_in),
                                 _ptr(state_in), _ptr(conv_window_out), _ptr(state_out), _ptr(parent), _ptr(x),
@@ -214,6 +272,11 @@ def commit_verify(dims: Dims, params: Params, parent_prev, path, path_len, x_pre
 def plan(dims: Dims, parent, plan_out, stream=None):
     _check(parent, "int32")
     _check(plan_out, "int32")
+    if parent is not None and parent.numel() != dims.batch * dims.n_nodes:
+        raise ValueError("parent: %d elements, the dims imply %d" % (parent.numel(), dims.batch * dims.n_nodes))
+    want = dims.batch * (PLAN_HEADER + dims.n_nodes * PLAN_STRIDE)
+    if plan_out is not None and plan_out.numel() != want:
+        raise ValueError("plan_out: %d elements, the dims imply %d" % (plan_out.numel(), want))
     rc = ssm_tree_plan(dims, _ptr(parent), _ptr(plan_out), _stream(stream))
     if rc != OK:
         raise SsmTreeError(rc, "ssm_tree_plan")

@@ -51,10 +51,11 @@ int oracle_validate_tree(const int32_t* parent, int32_t T) {
 int oracle_validate_path(const int32_t* parent, int32_t T, const int32_t* path, int32_t len) {
   int st = oracle_validate_tree(parent, T);
   if (st != ORACLE_OK) return st;
-  if (len < 0 || len > T) return ORACLE_E_PATH;
+  if (len < 0 || (MUT(20) ? len >= T : len > T)) return ORACLE_E_PATH;
   for (int32_t k = 0; k < len; ++k) {
     int32_t v = path[k];
     if (v < 0 || v >= T) return ORACLE_E_PATH;
+    if (MUT(19) && k == 0) continue;
     int32_t want = (k == 0) ? -1 : path[k - 1];
     if (parent[v] != want) return ORACLE_E_PATH;
   }

@@ -418,6 +418,51 @@ def pin_validator(o, tmax=5):
             assert got == want, (parent, got, want)
 
 
+def _is_root_path(parent, path):
+    """Independent definition of an accepted path: its length is between 0
+    and the node count, every entry names a node, and the entries are
+    exactly the root path of the last entry, root-level node first."""
+    T, n = len(parent), len(path)
+    if n == 0:
+        return True
+    if n > T or any(not (0 <= int(v) < T) for v in path):
+        return False
+    return [int(v) for v in path] == root_path(parent, int(path[-1]))
+
+
+def pin_path_validator(o, tmax=4, sample_t5=4000, seed=11):
+    """Every path of length 0..T+1 over the alphabet -1..T, for every BFS
+    forest of up to `tmax` nodes, classified like the independent
+    definition; for 5-node forests every valid path plus a random sample of
+    invalid ones (starts below the root, broken links, ids out of range,
+    one entry too many)."""
+    for T in range(0, tmax + 1):
+        for parent in all_bfs_forests(T):
+            for n in range(0, T + 2):
+                for path in itertools.product(range(-1, T + 1), repeat=n):
+                    q = np.array(path, np.int32)
+                    want = 0 if _is_root_path(parent, q) else -11
+                    got = o.validate_path(parent, q, n)
+                    assert got == want, (parent.tolist(), path, got, want)
+    rng = np.random.default_rng(seed)
+    forests = list(all_bfs_forests(5))
+    for parent in forests:
+        for v in range(5):
+            q = np.array(root_path(parent, v), np.int32)
+            assert o.validate_path(parent, q, len(q)) == 0, (parent.tolist(), q.tolist())
+            if len(q) >= 2:
+                # the same path with its root-level node cut off starts below the root
+                assert o.validate_path(parent, q[1:], len(q) - 1) == -11, (parent.tolist(), q[1:].tolist())
+    for _ in range(sample_t5):
+        parent = forests[int(rng.integers(len(forests)))]
+        n = int(rng.integers(0, 7))
+        q = rng.integers(-1, 6, size=n).astype(np.int32)
+        want = 0 if _is_root_path(parent, q) else -11
+        assert o.validate_path(parent, q, n) == want, (parent.tolist(), q.tolist())
+    # an invalid tree is reported as such, whatever the path
+    assert o.validate_path(np.array([0, 0], np.int32), np.zeros(0, np.int32), 0) == -10
+
+
 def pin_plan(o, seed=9):
     rng = np.random.default_rng(seed)
     cases = [np.arange(-1, 12, dtype=np.int32), np.array([-1] + [0] * 11, np.int32),
@@ -570,5 +615,5 @@ def pin_round_bf16(o, seed=10):
 
 ALL_PINS = [pin_chain_is_scan, pin_every_node_is_its_path_scan, pin_bruteforce_forests, pin_closed_form,
             pin_softplus_library, pin_lfilter, pin_special_cases, pin_commit, pin_sibling_relabel,
-            pin_validator, pin_plan, pin_peak_from_verify, pin_golden, pin_option_special_cases,
+            pin_validator, pin_path_validator, pin_plan, pin_peak_from_verify, pin_golden, pin_option_special_cases,
             pin_round_bf16]

@@ -26,10 +26,12 @@ MUTANTS = {
     16: "gate multiplies by sigmoid(z) instead of silu(z)",
     17: "xbc: commit shifts only x, not B and C, into the window",
     18: "bf16 state storage rounds ties up instead of to even",
+    19: "path validator skips the root-level check of the first path node",
+    20: "path validator's length bound off by one (rejects a full-length path)",
 }
 
 FAST_PINS = [pins.pin_chain_is_scan, pins.pin_closed_form, pins.pin_softplus_library, pins.pin_commit,
-             pins.pin_validator, functools.partial(pins.pin_bruteforce_forests, tmax=5), pins.pin_round_bf16]
+             pins.pin_validator, pins.pin_path_validator, functools.partial(pins.pin_bruteforce_forests, tmax=5), pins.pin_round_bf16]
 
 
 @pytest.mark.parametrize("k", sorted(MUTANTS), ids=lambda k: "m%d" % k)
