@@ -105,10 +105,12 @@ def load_traffic(kernel, cfg):
     return rec.get("bytes_per_launch")
 
 
-PROBE_BYTES = 4 << 30  # the plain copy of hbm_probe: reads and writes this many bytes per dispatch
+PROBE_BYTES = 4 << 30  # hbm_probe's buffer: the copy probe reads and writes this many bytes per dispatch
 KERNEL_MATCH = {"verify": ("verify_mfma_kernel", "verify_tt_kernel", "verify_tt_ws_kernel", "verify_proj_kernel"),
                 "commit": ("::commit_kernel",),
-                "commit_verify": ("commit_verify_kernel",), "copy": ("copyBuffer",)}
+                "commit_verify": ("commit_verify_kernel",),
+                # the coalesced plain copy probe (kind 1, layout 0, plain loads and stores, one tile per workgroup)
+                "copy": ("probe_kernel<1, 0, false>",)}
 
 
 def _pmc_per_dispatch(run_dir, counter):
@@ -135,9 +137,9 @@ def record_traffic(prof_dir, cfg):
     """Add this workload's entry to profiles/traffic.json from four
     rocprofv3 --pmc runs under prof_dir: fetch/ and write/ (FETCH_SIZE,
     WRITE_SIZE of this bench on the workload), copy_fetch/ and copy_write/
-    (the same counters over `bench.py --probe`).  Each counter is scaled by
-    bytes-moved / counter-reading of the plain 4 GiB device copy, so traffic
-    is in bytes per launch.  A kernel the workload runs as several launches
+    (the same counters over `bench.py --probe --copy-only`).  Each counter is
+    scaled by bytes-moved / counter-reading of the plain 4 GiB copy probe,
+    so traffic is in bytes per launch.  A kernel the workload runs as several launches
     (the round of a tree too deep for the fused kernel) is not recorded."""
     fetch = _pmc_per_dispatch(os.path.join(prof_dir, "fetch"), "FETCH_SIZE")
     write = _pmc_per_dispatch(os.path.join(prof_dir, "write"), "WRITE_SIZE")
@@ -168,9 +170,29 @@ def record_traffic(prof_dir, cfg):
     return 0
 
 
-def cpu_baseline(cfg, inp, target_s=12.0, threads=16):
+def host_cpu():
+    """CPU model and counts of the host this runs on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count() or 1
+    return {"cpu_model": model, "host_logical_cpus": os.cpu_count(), "usable_cpus": usable}
+
+
+def cpu_baseline(cfg, inp, target_s=12.0, threads=16, per_core_cfg=None):
     """Time the float64 oracle (verify + commit) on whole layers of the
-    workload until about target_s of wall time is covered."""
+    workload until about target_s of CPU time is covered, on `threads`
+    worker threads (at most the CPUs this process may use); then one thread
+    on the per-core workload for a per-core rate."""
     import numpy as np  # noqa: F401
     from concurrent.futures import ThreadPoolExecutor
 
@@ -178,6 +200,8 @@ def cpu_baseline(cfg, inp, target_s=12.0, threads=16):
     from testgen.configs import unit_f64
 
     o = oracle.get()
+    host = host_cpu()
+    threads = max(1, min(threads, host["usable_cpus"]))
     # calibrate on one unit, single thread
     u0 = unit_f64(cfg, 0, 0, inp)
     t0 = time.perf_counter()
@@ -189,28 +213,125 @@ def cpu_baseline(cfg, inp, target_s=12.0, threads=16):
     units = [(l, b) for l in range(layers) for b in range(cfg.Bsz)]
     prepared = {lb: unit_f64(cfg, lb[0], lb[1], inp) for lb in units}
 
-    def one(lb):
+    def one(ci, pin, lb, u):
         l, b = lb
-        u = prepared[lb]
-        n = int(inp.path_len[b])
-        o.verify(inp.parent[b], u, cfg.H, cfg.P, cfg.N, cfg.G, cfg.W, cfg.silu)
-        o.commit(inp.parent[b], inp.path[b, :n], n, u, cfg.H, cfg.P, cfg.N, cfg.G, cfg.W, cfg.silu)
+        n = int(pin.path_len[b])
+        o.verify(pin.parent[b], u, ci.H, ci.P, ci.N, ci.G, ci.W, ci.silu)
+        o.commit(pin.parent[b], pin.path[b, :n], n, u, ci.H, ci.P, ci.N, ci.G, ci.W, ci.silu)
 
     # whole passes over the sample until about target_s / threads of wall time
     passes = 0
     t0 = time.perf_counter()
     with ThreadPoolExecutor(max_workers=threads) as ex:
         while True:
-            list(ex.map(one, units))
+            list(ex.map(lambda lb: one(cfg, inp, lb, prepared[lb]), units))
             passes += 1
             if time.perf_counter() - t0 >= target_s / threads * 4 or passes >= 100:
                 break
     wall = time.perf_counter() - t0
     node_layers = passes * len(units) * cfg.T
-    return {"value": node_layers / wall, "unit": "tree-node-layers/s", "cores": threads, "kind": "oracle",
-            "sample": "verify+commit of layers 0..%d x %d sequences (%d of %d (layer, sequence) units), "
-                      "%d pass(es), float64, %.1f s wall" % (layers - 1, cfg.Bsz, len(units), cfg.L * cfg.Bsz, passes,
-                                                              wall)}
+    out = {"value": node_layers / wall, "unit": "tree-node-layers/s", "cores": threads, "kind": "oracle",
+           "sample": "verify+commit of layers 0..%d x %d sequences (%d of %d (layer, sequence) units), "
+                     "%d pass(es), float64, %.1f s wall on %d threads" % (
+                         layers - 1, cfg.Bsz, len(units), cfg.L * cfg.Bsz, passes, wall, threads), **host}
+    if per_core_cfg is not None:
+        from testgen import configs as C
+        pc = per_core_cfg
+        pin = C.make_inputs(pc, nthreads=threads)
+        punits = [(l, b) for l in range(pc.L) for b in range(pc.Bsz)]
+        pprep = {lb: unit_f64(pc, lb[0], lb[1], pin) for lb in punits}
+        done = 0
+        t0 = time.perf_counter()
+        while True:
+            for lb in punits:
+                one(pc, pin, lb, pprep[lb])
+            done += 1
+            if time.perf_counter() - t0 >= 2.0:
+                break
+        w1 = time.perf_counter() - t0
+        out["per_core"] = {"workload": pc.name, "threads": 1,
+                           "value": round(done * len(punits) * pc.T / w1, 1), "unit": "tree-node-layers/s",
+                           "sample": "verify+commit of all %d units, %d pass(es), %.1f s" % (len(punits), done, w1)}
+    return out
+
+
+def rotated_rates(torch, m, C, cid, threads, min_bytes=1 << 30, reps=3):
+    """Verify alone and the fused round on a workload small enough to sit in
+    the 256 MB last-level cache, with enough independent input sets (each
+    with its own trees, inputs, root state and window) that consecutive
+    calls never find their bytes in that cache: the sets are cycled in
+    turn, every call timed with HIP events on the launch stream."""
+    from testgen.device import upload
+    cfg = C.CONFIGS[cid]
+    ab = algorithmic_bytes(cfg, np_zeros(cfg.Bsz))
+    per_set = ab["verify"] + ab["commit_verify"]
+    K = max(3, -(-min_bytes // per_set))
+    sets = []
+    for k in range(K):
+        ck = cfg.replace(cid=cfg.cid + 1000 + k)
+        inp = C.make_inputs(ck, nthreads=threads)
+        nx = C.make_inputs(ck.replace(cid=ck.cid + 500), nthreads=threads,
+                           skip=("state", "window", "A", "D", "dt_bias", "conv_w", "conv_b"))
+        g, g2 = upload(inp), upload(nx)
+        sets.append((g, g2, inp.path_len, nx.path_len))
+    dims = m.make_dims(cfg.L, cfg.Bsz, cfg.T, cfg.H, cfg.P, cfg.N, cfg.G, cfg.W, cfg.bf16, cfg.silu)
+    prms = [m.make_params(g.A, g.D, g.dt_bias, g.conv_w, g.conv_b) for g, _, _, _ in sets]
+    y = torch.empty((cfg.L, cfg.Bsz, cfg.T, cfg.d_in), dtype=torch.float32, device="cuda")
+    st_c = torch.empty(cfg.Bsz, dtype=torch.int32, device="cuda")
+    st_v = torch.empty_like(st_c)
+    flips = [0] * K
+
+    def verify(i):
+        g = sets[i][0]
+        m.verify(dims, prms[i], g.parent, g.x, g.B, g.C, g.dt_raw, g.window, g.state, y, st_v)
+
+    def round_(i):
+        g, g2 = sets[i][0], sets[i][1]
+        prev, nxt = (g, g2) if flips[i] % 2 == 0 else (g2, g)
+        flips[i] += 1
+        m.commit_verify(dims, prms[i], prev.parent, prev.path, prev.path_len, prev.x, prev.B, prev.dt_raw, g.window,
+                        g.state, g.window, g.state, nxt.parent, nxt.x, nxt.B, nxt.C, nxt.dt_raw, y, st_c, st_v)
+
+    def timed_cycle(fn):
+        for i in range(K):  # one untimed pass
+            fn(i)
+        torch.cuda.synchronize()
+        evs = []
+        for r in range(reps):
+            for i in range(K):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                fn(i)
+                e1.record()
+                evs.append((e0, e1))
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) for a, b in evs]
+
+    vms, rms = timed_cycle(verify), timed_cycle(round_)
+    if not (st_v.cpu() == 0).all() or not (st_c.cpu() == 0).all() or torch.isnan(y).any():
+        raise SystemExit("bench: bad status or NaN on workload %d" % cid)
+    nl = cfg.L * cfg.Bsz * cfg.T
+    rb = sum((algorithmic_bytes(cfg, a)["commit_verify"] + algorithmic_bytes(cfg, b)["commit_verify"]) // 2
+             for _, _, a, b in sets) // K
+
+    def rate(ms, nbytes):
+        a = sum(ms) / len(ms)
+        gbs = nbytes / (a * 1e-3) / 1e9
+        return {"ms": round(a, 4), "ms_min": round(min(ms), 4), "bytes": nbytes,
+                "node_layers_per_s": round(nl / (a * 1e-3), 1), "GBps": round(gbs, 1),
+                "frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+    out = {"workload": cfg.name, "input_sets": K, "bytes_per_set": per_set,
+           "verify": rate(vms, ab["verify"]), "round": rate(rms, rb),
+           "note": "sets cycled so that no call finds its inputs in the last-level cache; not in the step"}
+    del sets, prms
+    torch.cuda.empty_cache()
+    return out
+
+
+def np_zeros(n):
+    import numpy as np
+    return np.zeros(n, np.int32)
 
 
 def per_layer_round(torch, m, cfg, g, g2, state, window, y, st_c, st_v, timed):
@@ -413,25 +534,75 @@ def state_bf16_round(torch, m, cfg, g, g2, state, window, timed, path_lens):
     return out
 
 
-def hbm_probe(torch, nbytes=4 << 30, reps=10):
-    """Plain device copy (torch copy_) and read (torch sum) bandwidth over
-    buffers far larger than the 256 MB last-level cache."""
-    n = nbytes // 4
-    a = torch.empty(n, dtype=torch.float32, device="cuda").uniform_()
-    b = torch.empty_like(a)
-    out = {}
-    for name, fn, moved in (("copy", lambda: b.copy_(a), 2 * nbytes), ("read", lambda: a.sum(), nbytes)):
-        fn()
+PROBE_KINDS = {0: "read", 1: "copy", 2: "read+1/8 write"}
+PROBE_LAYOUTS = {0: "coalesced", 1: "mfma"}
+
+
+def load_probe():
+    """libssm_tree_probe.so: hand-written streaming kernels in the root
+    state's tiles and access patterns (csrc/probe.hip)."""
+    import ctypes
+    from mamba2_tree_verification_amd import build as hb
+    if not os.path.exists(hb.PROBE_LIB):
+        raise SystemExit("libssm_tree_probe.so is not built: run __graft_entry__.build()")
+    L = ctypes.CDLL(hb.PROBE_LIB)
+    p, i = ctypes.c_void_p, ctypes.c_int
+    L.ssm_probe_stream.argtypes = [i, i, i, i, p, p, ctypes.c_int64, p, p]
+    L.ssm_probe_stream.restype = i
+    L.ssm_probe_dst_bytes.argtypes = [i, ctypes.c_int64]
+    L.ssm_probe_dst_bytes.restype = ctypes.c_int64
+    return L
+
+
+def hbm_probe(torch, nbytes=PROBE_BYTES, reps=8, variants=None):
+    """Bandwidth of the hand-written probe kernels over a buffer far larger
+    than the 256 MB last-level cache: read only, copy, and read with one
+    row written per eight read, in the coalesced and the matrix-core
+    operand layouts, plain and non-temporal, one workgroup per 32 KiB tile
+    or a persistent grid of 4 workgroups per CU.  Bytes moved per launch
+    over the HIP-event time of the launch."""
+    L = load_probe()
+    tiles = nbytes // (64 * 512)
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").uniform_()
+    dst = torch.empty(L.ssm_probe_dst_bytes(1, tiles) // 4, dtype=torch.float32, device="cuda")
+    sink = torch.zeros(256, dtype=torch.int32, device="cuda")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    if variants is None:  # nt: bit 0 non-temporal loads, bit 1 non-temporal stores
+        variants = [(k, lay, nt, grid) for k in (0, 1, 2) for lay in (0, 1) for nt in ((0, 1) if k == 0 else (0, 1, 2, 3))
+                    for grid in (0, 4 * cus)]
+    hs = torch.cuda.current_stream().cuda_stream
+    out = []
+    for kind, lay, nt, grid in variants:
+        def run():
+            rc = L.ssm_probe_stream(kind, lay, nt, grid, src.data_ptr(), dst.data_ptr(), tiles, sink.data_ptr(), hs)
+            if rc:
+                raise SystemExit("probe launch failed: %d" % rc)
+        run()
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
+        ms = []
         for _ in range(reps):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / reps
-        out[name] = {"GB/s": round(moved / (ms * 1e-3) / 1e9, 1), "ms": round(ms, 4), "bytes": moved}
-    return {"probe": "hbm", "buffer_bytes": nbytes, **out}
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            run()
+            e1.record()
+            torch.cuda.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        moved = nbytes + L.ssm_probe_dst_bytes(kind, tiles)
+        a = sum(ms) / len(ms)
+        out.append({"kind": PROBE_KINDS[kind], "layout": PROBE_LAYOUTS[lay],
+                    "nt": ("loads " if nt & 1 else "") + ("stores" if nt & 2 else "") or "none",
+                    "grid": "per tile" if grid == 0 else "persistent %d" % grid, "bytes": moved,
+                    "ms": round(a, 4), "GBps": round(moved / (a * 1e-3) / 1e9, 1)})
+    del src, dst
+    torch.cuda.empty_cache()
+    best = {}
+    for r in out:
+        if r["GBps"] > best.get(r["kind"], {}).get("GBps", 0):
+            best[r["kind"]] = r
+    return {"probe": "hbm", "buffer_bytes": nbytes, "variants": out,
+            "best": {k: {"GBps": v["GBps"], "frac": round(v["GBps"] / HBM_PEAK_GBS, 4),
+                         "variant": "%s %s, non-temporal %s, %s" % (v["layout"], k, v["nt"], v["grid"])}
+                     for k, v in best.items()}}
 
 
 def main(argv=None):
@@ -449,7 +620,9 @@ def main(argv=None):
     ap.add_argument("--record-traffic", metavar="DIR",
                     help="write profiles/traffic.json from rocprofv3 FETCH_SIZE/WRITE_SIZE runs under DIR and exit")
     ap.add_argument("--probe", action="store_true",
-                    help="only measure plain HBM copy and read bandwidth (practical ceilings) and exit")
+                    help="only run the hand-written HBM probe kernels (practical ceilings) and exit")
+    ap.add_argument("--copy-only", action="store_true",
+                    help="with --probe: only the coalesced plain copy probe (the counter scale of --record-traffic)")
     args = ap.parse_args(argv)
 
     if args.record_traffic:
@@ -471,7 +644,7 @@ def main(argv=None):
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
     if args.probe:
-        print(json.dumps(hbm_probe(torch)), flush=True)
+        print(json.dumps(hbm_probe(torch, variants=[(1, 0, 0, 0)] if args.copy_only else None)), flush=True)
         return 0
     m.load()
     cfg = C.CONFIGS[args.config]
@@ -544,8 +717,15 @@ def main(argv=None):
     fifo_ms = timed(lambda: m.verify(dims_fifo, prm, g.parent, g.x, g.B, g.C, g.dt_raw, window, state, y, st_v),
                     reps=3)
 
-    per_layer = draft = opts = sbf = None
+    per_layer = draft = opts = sbf = ceiling = None
+    small = {}
     if not args.no_extras:
+        # practical ceilings of the same GPU, by the hand-written probes
+        ceiling = hbm_probe(torch, nbytes=2 << 30, reps=4,
+                            variants=[(0, 0, 1, 0), (0, 1, 0, 0), (1, 0, 0, 0), (1, 0, 1, 0), (1, 1, 0, 0),
+                                      (2, 0, 1, 0), (2, 1, 0, 0)])
+        for cid in (1, 2):
+            small[C.CONFIGS[cid].name] = rotated_rates(torch, m, C, cid, args.threads)
         sbf = state_bf16_round(torch, m, cfg, g, g2, state, window, timed, (inp.path_len, inp2.path_len))
         per_layer = per_layer_round(torch, m, cfg, g, g2, state, window, y, st_c, st_v, timed)
         draft = draft_decode(torch, m, C, upload, args.threads, timed)
@@ -623,11 +803,14 @@ def main(argv=None):
         "draft_decode": draft,
         "options_round": opts,
         "state_bf16_round": sbf,
+        "small_workloads": small or None,
+        "ceiling": ceiling,
         "param_bytes_per_call": ab["params"],
         "verify_hbm_frac": kern["verify"]["roofline"]["frac"],
     }
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds, args.threads)
+        rec["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds, args.threads,
+                                           per_core_cfg=C.CONFIGS[2])
     rec["setup_s"] = round(t_gen, 1)
     print(json.dumps(rec), flush=True)
     return 0

@@ -31,6 +31,8 @@
 // that runs from LDS.  y is staged in LDS and leaves as whole 256-byte row
 // segments.  Trees of at most 16 nodes, heads a multiple of 16 channels
 // wide.
+#include <string.h>
+
 #include "common.h"
 
 namespace ssmt {
@@ -92,12 +94,17 @@ __host__ __device__ constexpr int align16(int x) { return (x + 15) & ~15; }
 // LDS layout (byte offsets).  ys reuses the x staging of both trees, which
 // is dead once the conv outputs exist; dtx reuses the next tree's B rows,
 // dead once C . B is formed.
+// Heads a 64-channel slab touches (P a multiple of 16): one when P is a
+// multiple of 64, four at P = 16, otherwise at most two.
+__host__ __device__ constexpr int slab_heads(int P) { return P % 64 == 0 ? 1 : (P == 16 ? 4 : 2); }
+
 struct CvLds {
-  int pparent, path, parent, misc, anc, cidx, dAp, dtp, dt, S, S2, D, cbt, cw, cb, win, xn, xp, ys, C, B, dtx, Bp,
-      xt, total, row;
+  int pparent, path, parent, misc, anc, cidx, dAp, dtp, dt, S, Sd, av, Mt, D, cbt, cw, cb, win, xn, xp, ys, C, B, dtx,
+      Bp, xt, total, row;
   // the options' own arrays (offset 0 when unused)
   int z, cwbc, cbbc, winbc, Cp, Bpt;
-  __host__ __device__ CvLds(int N, int E, bool xbc = false, bool gate = false) {
+  // vo: verify only (nothing committed: no previous tree's rows)
+  __host__ __device__ CvLds(int N, int E, int P, bool xbc = false, bool gate = false, bool vo = false) {
     int o = 0;
     row = N * E + kRowPad;                    // staged B / C row stride
     pparent = o; o += 4 * kCvT;
@@ -110,20 +117,24 @@ struct CvLds {
     dtp = o; o += 4 * kCvT * 4;               // previous tree: dt per node and head
     dt = o; o += 4 * 4 * kCvT;                // next tree: dt per head and node
     S = o; o += 4 * 4 * kCvT;                 // next tree: dt * A per head and node
-    S2 = o; o += 4 * 4 * kCvT;                // next tree: cumulative S along the root path, times log2(e)
+    Sd = o; o += 8 * 4 * kCvT;                // next tree: S_v = sum of dt * A over the root path, float64
+    av = o; o += 4 * 4 * kCvT;                // next tree: a_v = exp(S_v) per head and node
+    Mt = o; o += 4 * slab_heads(P) * kCvT * kCvT;  // next tree: exp(S_v - S_u) dt_u, u on v's root path, else 0
     D = o; o += 16;
     cbt = o; o += xbc ? 0 : 4 * kCvT * kCvT;  // next tree: C_v . B_u (with the xBC conv each wave forms it itself)
     cw = o; o += 4 * 4 * kCvRows;             // conv weights per channel, tap order of the parameters
     cb = o; o += 4 * kCvRows;                 // conv bias per channel
     win = o; o += align16(3 * kCvRows * E);   // old window rows (raw)
     xn = o; o += kCvT * kCvRows * E;          // next tree x (raw)
-    xp = o; o += kCvT * kCvRows * E;          // previous tree x of the path nodes (raw)
-    ys = xn;                                  // y staging [node][channel] fp32 (needs 4 KiB: 2 x 1024 E >= 4096)
+    // previous tree x of the path nodes (raw); with bf16 inputs it also backs
+    // the second half of the y staging, so verify-only keeps it then
+    xp = o; o += (vo && E == 4) ? 0 : kCvT * kCvRows * E;
+    ys = xn;                                  // y staging [node][channel] fp32 (4 KiB: xn, then xp or C)
     C = o; o += kCvT * row;                   // next tree C rows (raw, padded)
     B = o;                                    // next tree B rows (raw, padded) ...
     dtx = o;                                  // ... then dt * x~ per path node and channel, fp32
     o += kCvT * row > 4 * kCvT * kCvRows ? kCvT * row : 4 * kCvT * kCvRows;
-    Bp = o; o += kCvT * row;                  // previous tree B rows of the path nodes (raw, padded)
+    Bp = o; o += vo ? 0 : kCvT * row;         // previous tree B rows of the path nodes (raw, padded)
     xt = o; o += 4 * kCvRows * kCvT;          // next tree conv outputs, MFMA B-operand layout
     z = cwbc = cbbc = winbc = Cp = Bpt = 0;
     if (gate) { z = o; o += kCvT * kCvRows * E; }          // gate input rows (raw)
@@ -143,9 +154,21 @@ struct CvLds {
 
 }  // namespace
 
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ bool finite4(f32x4 v) {
+  return __builtin_isfinite(v.x) && __builtin_isfinite(v.y) && __builtin_isfinite(v.z) && __builtin_isfinite(v.w);
+}
+
 // OPT: an instantiation of its own for the Mamba2-convention options (the
 // xBC conv, the gate), so that the plain path keeps its registers and LDS.
-template <typename TIn, typename TS, int NG, bool OPT>
+// VO: verify only (ssm_tree_verify): no previous tree, nothing committed,
+// no state or window written.
+template <typename TIn, typename TS, int NG, bool OPT, bool VO>
 __global__ void __launch_bounds__(kCvWaves * kWave) commit_verify_kernel(CommitVerifyArgs a) {
   typedef StateQuad<TS> SQ;
   constexpr int N = 16 * NG;
@@ -168,7 +191,7 @@ __global__ void __launch_bounds__(kCvWaves * kWave) commit_verify_kernel(CommitV
   const bool xbc = OPT && d.xbc, gate = OPT && a.z != nullptr;
 
   extern __shared__ __align__(16) unsigned char smem[];
-  const CvLds lo(N, E, xbc, gate);
+  const CvLds lo(N, E, P, xbc, gate, VO);
   int32_t* s_pparent = reinterpret_cast<int32_t*>(smem + lo.pparent);
   int32_t* s_path = reinterpret_cast<int32_t*>(smem + lo.path);
   int32_t* s_parent = reinterpret_cast<int32_t*>(smem + lo.parent);
@@ -179,7 +202,9 @@ __global__ void __launch_bounds__(kCvWaves * kWave) commit_verify_kernel(CommitV
   float* s_dtp = reinterpret_cast<float*>(smem + lo.dtp);
   float* s_dt = reinterpret_cast<float*>(smem + lo.dt);
   float* s_S = reinterpret_cast<float*>(smem + lo.S);
-  float* s_S2 = reinterpret_cast<float*>(smem + lo.S2);
+  double* s_Sd = reinterpret_cast<double*>(smem + lo.Sd);
+  float* s_a = reinterpret_cast<float*>(smem + lo.av);
+  float* s_Mt = reinterpret_cast<float*>(smem + lo.Mt);
   float* s_D = reinterpret_cast<float*>(smem + lo.D);
   float* s_cbt = reinterpret_cast<float*>(smem + lo.cbt);
   float* s_cw = reinterpret_cast<float*>(smem + lo.cw);
@@ -205,13 +230,15 @@ __global__ void __launch_bounds__(kCvWaves * kWave) commit_verify_kernel(CommitV
 
   int r_pp = 0, r_path = 0, r_par = 0, r_len = 0;
   if (tid < T) {
-    r_pp = a.parent_prev[(int64_t)b * T + tid];
-    r_path = a.path[(int64_t)b * T + tid];
+    if constexpr (!VO) {
+      r_pp = a.parent_prev[(int64_t)b * T + tid];
+      r_path = a.path[(int64_t)b * T + tid];
+    }
     r_par = a.parent[(int64_t)b * T + tid];
   }
   // verify-only use (the options of ssm_tree_verify): no path length means
   // nothing to commit, and no state or window output is written
-  if (tid == kCvWaves * kWave - 1) r_len = (!OPT || a.path_len) ? a.path_len[b] : 0;
+  if (tid == kCvWaves * kWave - 1) r_len = (!VO && (!OPT || a.path_len)) ? a.path_len[b] : 0;
 
   // x rows: thread (v, q) holds channels 4 q .. 4 q + 3 of node v
   const int xv = tid >> 4, xq = (tid & 15) * 4;
@@ -236,7 +263,7 @@ __global__ void __launch_bounds__(kCvWaves * kWave) commit_verify_kernel(CommitV
   // conversion here would make waves 0 and 1 wait for it first)
   uint32_t r_dt = 0;
   float r_A = 0.0f, r_bias = 0.0f, r_D = 0.0f;
-  if (wave < 2 && sv < T && sh < HW) {
+  if ((wave == 0 || (!VO && wave == 1)) && sv < T && sh < HW) {
     const int64_t di = unit * T * H + (int64_t)sv * H + h_lo + sh;
     const void* src = wave == 0 ? a.dt_raw : a.dt_prev;
     r_dt = E == 2 ? (uint32_t)reinterpret_cast<const uint16_t*>(src)[di] : reinterpret_cast<const uint32_t*>(src)[di];
@@ -314,8 +341,10 @@ __global__ void __launch_bounds__(kCvWaves * kWave) commit_verify_kernel(CommitV
 
   // to LDS
   if (tid < T) {
-    s_pparent[tid] = r_pp;
-    s_path[tid] = r_path;
+    if constexpr (!VO) {
+      s_pparent[tid] = r_pp;
+      s_path[tid] = r_path;
+    }
     s_parent[tid] = r_par;
   }
   if (tid == kCvWaves * kWave - 1) s_misc[3] = r_len;
@@ -328,7 +357,7 @@ __global__ void __launch_bounds__(kCvWaves * kWave) commit_verify_kernel(CommitV
       *reinterpret_cast<u32x4*>(s_B + v * rs + q * 16) = rb[it];
     }
   }
-  if (wave < 2 && sv < T && sh < HW) {
+  if ((wave == 0 || (!VO && wave == 1)) && sv < T && sh < HW) {
     const float dt = softplus_f32(__uint_as_float(E == 2 ? r_dt << 16 : r_dt) + r_bias);
     if (wave == 0) {
       s_dt[sh * kCvT + sv] = dt;
@@ -394,8 +423,11 @@ __global__ void __launch_bounds__(kCvWaves * kWave) commit_verify_kernel(CommitV
     // both trees and the path, by ballot
     bool bad_p = false, bad_n = false, bad_path = false;
     if (lane < T) {
-      int p = s_pparent[lane];
-      bad_p = lane == 0 ? p != -1 : (p < -1 || p >= lane || p < s_pparent[lane - 1]);
+      int p;
+      if constexpr (!VO) {
+        p = s_pparent[lane];
+        bad_p = lane == 0 ? p != -1 : (p < -1 || p >= lane || p < s_pparent[lane - 1]);
+      }
       p = s_parent[lane];
       bad_n = lane == 0 ? p != -1 : (p < -1 || p >= lane || p < s_parent[lane - 1]);
     }
@@ -411,7 +443,7 @@ __global__ void __launch_bounds__(kCvWaves * kWave) commit_verify_kernel(CommitV
       s_misc[1] = st;
       s_misc[2] = tree_ok ? 1 : 0;
       if (blockIdx.x == 0 && l == 0) {
-        if (a.commit_status) a.commit_status[b] = st;
+        if (!VO && a.commit_status) a.commit_status[b] = st;
         if (a.verify_status) a.verify_status[b] = tree_ok ? SSM_TREE_OK : SSM_TREE_E_TREE;
       }
     }
@@ -523,7 +555,7 @@ __global__ void __launch_bounds__(kCvWaves * kWave) commit_verify_kernel(CommitV
   if (wave == 0) {
     const int c = c0 + lane;
     // new window row r (oldest first) = element len + r of (old window, path x), bit for bit
-    if (W > 1 && (!OPT || a.window_out)) {
+    if (!VO && W > 1 && (!OPT || a.window_out)) {
       TIn* win_out = reinterpret_cast<TIn*>(a.window_out) + unit * (W - 1) * (int64_t)CH + c;
 #pragma unroll
       for (int r = 0; r < 3; ++r) {
@@ -534,13 +566,40 @@ __global__ void __launch_bounds__(kCvWaves * kWave) commit_verify_kernel(CommitV
       }
     }
   } else if (wave == 1) {
+    // lane (head hh, node v): S_v = sum of dt * A over v's root path, in
+    // float64, then a_v = exp(S_v) and row v of the decay table,
+    // exp(S_v - S_u) dt_u for u on v's root path and 0 elsewhere.  The
+    // differences are taken in float64: on a deep path with large steps
+    // S_v and S_u are large and close, and a float32 difference would lose
+    // the digits that matter (the float64 sums of the same float32 terms
+    // cancel exactly, leaving the terms between u and v).
     const int hh = lane >> 4, v = lane & 15;
+    const int m = s_anc[v];
+    double S = 0.0;
     if (hh < HW) {
-      const int m = s_anc[v];
-      float acc = 0.0f;
+#pragma unroll 4
+      for (int u = 0; u < kCvT; ++u) S += ((m >> u) & 1) ? (double)s_S[hh * kCvT + u] : 0.0;
+      s_Sd[hh * kCvT + v] = S;
+    }
+    wave_sync();
+    if (hh < HW) {
+      constexpr double kLog2e = 1.4426950408889634;
+      s_a[hh * kCvT + v] = __builtin_amdgcn_exp2f((float)(S * kLog2e));
+      float* mt = s_Mt + (hh * kCvT + v) * kCvT;
+      // (one quad at a time: the state of the whole workgroup is in flight in
+      // registers meanwhile)
+#pragma unroll 1
+      for (int u4 = 0; u4 < kCvT / 4; ++u4) {
+        f32x4 q;
 #pragma unroll
-      for (int u = 0; u < kCvT; ++u) acc += ((m >> u) & 1) ? s_S[hh * kCvT + u] : 0.0f;
-      s_S2[hh * kCvT + v] = acc * 1.4426950408889634f;
+        for (int t = 0; t < 4; ++t) {
+          const int u = 4 * u4 + t;
+          q[t] = ((m >> u) & 1)
+                     ? __builtin_amdgcn_exp2f((float)((S - s_Sd[hh * kCvT + u]) * kLog2e)) * s_dt[hh * kCvT + u]
+                     : 0.0f;
+        }
+        *reinterpret_cast<f32x4*>(mt + 4 * u4) = q;
+      }
     }
   }
   // the next tree's conv outputs: thread (wave, lane) takes channel lane of
@@ -606,7 +665,7 @@ __global__ void __launch_bounds__(kCvWaves * kWave) commit_verify_kernel(CommitV
     f32x4 hq[NG];
 #pragma unroll
     for (int gg = 0; gg < NG; ++gg) hq[gg] = SQ::to_f32(hraw[gg]);
-    for (int q = 0; q < len; ++q) {
+    for (int q = 0; q < (VO ? 0 : len); ++q) {
       const float dA = s_dAp[s_path[q] * 4 + hh];
       const float cx = s_dtx[q * kCvRows + row];
       const TIn* bp = reinterpret_cast<const TIn*>(s_Bp + q * rs);
@@ -630,7 +689,7 @@ __global__ void __launch_bounds__(kCvWaves * kWave) commit_verify_kernel(CommitV
       hraw[gg] = SQ::from_f32(hq[gg]);
       hq[gg] = SQ::to_f32(hraw[gg]);
     }
-    if (!OPT || a.state_out) {
+    if (!VO && (!OPT || a.state_out)) {
       TS* so = reinterpret_cast<TS*>(a.state_out) + (unit * DI + c0 + row) * (int64_t)N;
       if constexpr (kWide) {
 #pragma unroll
@@ -757,24 +816,54 @@ __global__ void __launch_bounds__(kCvWaves * kWave) commit_verify_kernel(CommitV
     }
     // then the path terms M[v][u] x~_u, with the diagonal D
     const int i = j;
-    const float Sv = s_S2[hh * kCvT + i];
-    const f32x4 Sq = *reinterpret_cast<const f32x4*>(s_S2 + hh * kCvT + 4 * k);
-    const f32x4 dq = *reinterpret_cast<const f32x4*>(s_dt + hh * kCvT + 4 * k);
+    const f32x4 mq = *reinterpret_cast<const f32x4*>(s_Mt + (hh * kCvT + i) * kCvT + 4 * k);
+    const f32x4 aq = *reinterpret_cast<const f32x4*>(s_a + hh * kCvT + 4 * k);
     const f32x4 cbr = xbc ? cbx : *reinterpret_cast<const f32x4*>(s_cbt + i * kCvT + 4 * k);
     const int ancm = s_anc[i];
     const float Dh = s_D[hh];
     f32x4 mop, y;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const float mv = ((ancm >> (4 * k + t)) & 1) ? __builtin_amdgcn_exp2f(Sv - Sq[t]) * dq[t] * cbr[t] : 0.0f;
+      const float mv = ((ancm >> (4 * k + t)) & 1) ? mq[t] * cbr[t] : 0.0f;
       mop[t] = (4 * k + t == i) ? mv + Dh : mv;
-      y[t] = __builtin_amdgcn_exp2f(Sq[t]) * acc[t];
+      y[t] = aq[t] * acc[t];
     }
     const f32x4 xq = *reinterpret_cast<const f32x4*>(s_xt + row * kCvT + 4 * (k ^ ((row >> 2) & 3)));
-    y = mfma4(mop.x, xq.x, y);
-    y = mfma4(mop.y, xq.y, y);
-    y = mfma4(mop.z, xq.z, y);
-    y = mfma4(mop.w, xq.w, y);
+    if (__ballot(!finite4(xq)) == 0) {
+      y = mfma4(mop.x, xq.x, y);
+      y = mfma4(mop.y, xq.y, y);
+      y = mfma4(mop.z, xq.z, y);
+      y = mfma4(mop.w, xq.w, y);
+    } else {
+      // A non-finite conv output in the wave's tile: in the product, the
+      // zero weight of a node off v's root path would still turn it into
+      // NaN in y_v.  Each node's sum runs over its own root path alone
+      // instead, as the definition has it.
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int v = 4 * k + t;
+        const int av = s_anc[v];
+        const float* mrow = s_Mt + (hh * kCvT + v) * kCvT;
+        float yy = y[t];
+        for (int u = 0; u < kCvT; ++u) {
+          // C_v . B_u: lane v + 16 (u / 4), element u % 4 of cbx, or the table
+          float cb = 0.0f;
+          if (xbc) {
+            const f32x4 cq4 = cbx;
+            const float e = (u & 3) == 0 ? cq4.x : (u & 3) == 1 ? cq4.y : (u & 3) == 2 ? cq4.z : cq4.w;
+            cb = __shfl(e, v + 16 * (u >> 2));
+          } else {
+            cb = s_cbt[v * kCvT + u];
+          }
+          if ((av >> u) & 1) {
+            const float mv = mrow[u] * cb;
+            const float xu = s_xt[row * kCvT + 4 * ((u >> 2) ^ ((row >> 2) & 3)) + (u & 3)];
+            yy = fmaf(u == v ? mv + Dh : mv, xu, yy);
+          }
+        }
+        y[t] = yy;
+      }
+    }
     const bool tree_ok = s_misc[2] != 0;
     // lane (c + 16 k) holds nodes 4 k + r of channel row
 #pragma unroll
@@ -796,14 +885,15 @@ __global__ void __launch_bounds__(kCvWaves * kWave) commit_verify_kernel(CommitV
 
 namespace {
 
-template <typename TIn, typename TS, int NG, bool OPT>
+template <typename TIn, typename TS, int NG, bool OPT, bool VO = false>
 int launch_cv_o(const CommitVerifyArgs& a, hipStream_t s) {
-  const size_t lds = (size_t)CvLds(16 * NG, (int)sizeof(TIn), OPT && a.d.xbc, OPT && a.z != nullptr).total;
-  if (allow_lds(commit_verify_kernel<TIn, TS, NG, OPT>, lds) != hipSuccess) return SSM_TREE_E_HIP;
+  const size_t lds =
+      (size_t)CvLds(16 * NG, (int)sizeof(TIn), a.d.P, OPT && a.d.xbc, OPT && a.z != nullptr, VO).total;
+  if (allow_lds(commit_verify_kernel<TIn, TS, NG, OPT, VO>, lds) != hipSuccess) return SSM_TREE_E_HIP;
   dim3 grid(a.d.d_in / kCvRows, a.d.Bsz, a.d.L);
-  hipLaunchKernelGGL((commit_verify_kernel<TIn, TS, NG, OPT>), grid, dim3(kCvWaves * kWave), lds, s, a);
+  hipLaunchKernelGGL((commit_verify_kernel<TIn, TS, NG, OPT, VO>), grid, dim3(kCvWaves * kWave), lds, s, a);
   if (hipGetLastError() != hipSuccess) return SSM_TREE_E_HIP;
-  if (a.d.xbc && a.window_out) {  // the window's B and C rows, after every reader of the old ones
+  if (!VO && a.d.xbc && a.window_out) {  // the window's B and C rows, after every reader of the old ones
     WindowBcArgs w{a.d, a.parent_prev, a.path, a.path_len, a.B_prev, a.C_prev, a.window_in, a.window_out, 1};
     if (launch_window_bc(w, sizeof(TIn) == 2, s) != hipSuccess) return SSM_TREE_E_HIP;
   }
@@ -829,7 +919,45 @@ int launch_cv_in(const CommitVerifyArgs& a, hipStream_t s) {
   }
 }
 
+// verify only: the plain instantiation with nothing to commit
+template <typename TIn, int NG>
+int launch_vo_t(const CommitVerifyArgs& a, hipStream_t s) {
+  return a.d.sbf16 ? launch_cv_o<TIn, bf16_t, NG, false, true>(a, s) : launch_cv_o<TIn, float, NG, false, true>(a, s);
+}
+
+template <typename TIn>
+int launch_vo_in(const CommitVerifyArgs& a, hipStream_t s) {
+  switch (a.d.N) {
+    case 16: return launch_vo_t<TIn, 1>(a, s);
+    case 32: return launch_vo_t<TIn, 2>(a, s);
+    case 64: return launch_vo_t<TIn, 4>(a, s);
+    case 128: return launch_vo_t<TIn, 8>(a, s);
+    case 256: return launch_vo_t<TIn, 16>(a, s);
+    default: return SSM_TREE_E_DIMS;
+  }
+}
+
 }  // namespace
+
+// ssm_tree_verify on the fused round's shapes without the options: the
+// round's kernel with nothing to commit (one workgroup per 64 channels of a
+// (layer, sequence), the root state read once and never written).
+int launch_verify_oneshot(const VerifyArgs& v, bool bf16, hipStream_t s) {
+  CommitVerifyArgs a;
+  memset(&a, 0, sizeof(a));
+  a.d = v.d;
+  a.prm = v.prm;
+  a.window_in = v.window;
+  a.state_in = v.state;
+  a.parent = v.parent;
+  a.x = v.x;
+  a.B = v.B;
+  a.C = v.C;
+  a.dt_raw = v.dt_raw;
+  a.y = v.y;
+  a.verify_status = v.seq_status;
+  return bf16 ? launch_vo_in<bf16_t>(a, s) : launch_vo_in<float>(a, s);
+}
 
 bool commit_verify_fused_applies(const Dims& d) { return d.T >= 1 && d.T <= kCvT && d.P % 16 == 0; }
 

@@ -214,7 +214,7 @@ struct VerifyLds {
     path = o; o += (TMAX * TMAX + 15) & ~15;
     onk = o; o += (TMAX * TMAX + 15) & ~15;
     dt = o; o += 4 * TMAX * g.HWG;
-    S = o; o += 4 * TMAX * g.HWG;
+    S = o; o += 8 * TMAX * g.HWG;                              // float64
     Dh = o; o += 4 * ((g.HWG + 3) & ~3);
     cb = o; o += 4 * TMAX * TMAX;
     pair = o; o += (2 * kPairs + 15) & ~15;
@@ -253,7 +253,10 @@ __global__ void __launch_bounds__(kThreads) verify_proj_kernel(VerifyArgs a, Ver
   uint8_t* s_path = smem + lo.path;                                // [TMAX][TMAX] root path, top first
   uint8_t* s_onk = smem + lo.onk;                                  // [TMAX][TMAX] k + 1 if u = path(v)[k], else 0
   float* s_dt = reinterpret_cast<float*>(smem + lo.dt);            // [TMAX][HWG] dt
-  float* s_S = reinterpret_cast<float*>(smem + lo.S);              // [TMAX][HWG] sum of dt * A over the root path
+  // [TMAX][HWG] sum of dt * A over the root path, float64: on a deep path
+  // with large steps S_v and S_u are large and close, and their difference
+  // (the decay between u and v) must not lose its digits to rounding
+  double* s_S = reinterpret_cast<double*>(smem + lo.S);
   float* s_D = reinterpret_cast<float*>(smem + lo.Dh);             // [HWG]
   float* s_cb = reinterpret_cast<float*>(smem + lo.cb);            // [TMAX][TMAX] C_v . B_(k-th path node)
   uint16_t* s_pair = reinterpret_cast<uint16_t*>(smem + lo.pair);  // (v << 8 | k)
@@ -358,7 +361,7 @@ __global__ void __launch_bounds__(kThreads) verify_proj_kernel(VerifyArgs a, Ver
     const int v = i / HWG, hh = i % HWG, h = h_wg + hh;
     const float dt = softplus_f32(load_in(dtr, (int64_t)v * H + h) + a.prm.dt_bias[(int64_t)l * H + h]);
     s_dt[v * HWG + hh] = dt;
-    s_S[v * HWG + hh] = dt * a.prm.A[(int64_t)l * H + h];  // this node's own term for now
+    s_S[v * HWG + hh] = (double)(dt * a.prm.A[(int64_t)l * H + h]);  // this node's own term for now
   }
   for (int i = tid; i < TMAX * TMAX; i += nthr) s_onk[i] = 0;
   for (int i = tid; i < HWG; i += nthr) s_D[i] = a.prm.D[(int64_t)l * H + h_wg + i];
@@ -424,22 +427,24 @@ __global__ void __launch_bounds__(kThreads) verify_proj_kernel(VerifyArgs a, Ver
     float* sa = s_a + buf * TMAX * geo.HB;
     for (int i = tid + part * nthr; i < T * HBk; i += nparts * nthr) {
       const int v = i / HBk, hb = i % HBk;
-      const float Sv = s_S[v * HWG + hb0 + hb];
-      sa[v * geo.HB + hb] = expf(Sv);
+      const double Sv = s_S[v * HWG + hb0 + hb];
+      sa[v * geo.HB + hb] = expf((float)Sv);
       if constexpr (!DENSE) {
         const int p = s_parent[v];
-        s_dA[buf * TMAX * geo.HB + v * geo.HB + hb] = expf(p >= 0 ? Sv - s_S[p * HWG + hb0 + hb] : Sv);
+        s_dA[buf * TMAX * geo.HB + v * geo.HB + hb] = expf((float)(p >= 0 ? Sv - s_S[p * HWG + hb0 + hb] : Sv));
       }
     }
     if constexpr (DENSE) {
       float* sm = s_M + buf * geo.HB * TMAX * TMAX;
-      for (int i = tid + part * nthr; i < HBk * T * T; i += nparts * nthr) {
-        const int hb = i / (T * T), v = (i / T) % T, u = i % T;
-        const int k1 = s_onk[v * TMAX + u];
+      // every column of the rows read, zero past T as well as off the path:
+      // the product below runs over all TMAX columns
+      for (int i = tid + part * nthr; i < HBk * T * TMAX; i += nparts * nthr) {
+        const int hb = i / (T * TMAX), v = (i / TMAX) % T, u = i % TMAX;
+        const int k1 = u < T ? s_onk[v * TMAX + u] : 0;
         float val = 0.0f;
         if (k1) {
           const int hw = hb0 + hb;
-          val = expf(s_S[v * HWG + hw] - s_S[u * HWG + hw]) * s_dt[u * HWG + hw] * s_cb[v * TMAX + k1 - 1];
+          val = expf((float)(s_S[v * HWG + hw] - s_S[u * HWG + hw])) * s_dt[u * HWG + hw] * s_cb[v * TMAX + k1 - 1];
           if (u == v) val += s_D[hw];
         }
         sm[(hb * TMAX + v) * TMAX + u] = val;
@@ -487,19 +492,37 @@ __global__ void __launch_bounds__(kThreads) verify_proj_kernel(VerifyArgs a, Ver
 #pragma unroll
         for (int v = 0; v < TMAX; ++v) accs[v * kWave + lane] = acc[j][v];
         const float* Mh = s_M + ((blk % 3) * geo.HB + hb) * TMAX * TMAX;
-#pragma unroll 4
-        for (int v = 0; v < T; ++v) {
-          const f32x4* Mrow = reinterpret_cast<const f32x4*>(Mh + v * TMAX);
-          float yv = sa[v * geo.HB + hb] * accs[v * kWave + lane];
+        bool fin = true;
 #pragma unroll
-          for (int u4 = 0; u4 < TMAX / 4; ++u4) {
-            const f32x4 m = Mrow[u4];
-            yv = fmaf(m.x, xt[4 * u4 + 0], yv);
-            yv = fmaf(m.y, xt[4 * u4 + 1], yv);
-            yv = fmaf(m.z, xt[4 * u4 + 2], yv);
-            yv = fmaf(m.w, xt[4 * u4 + 3], yv);
+        for (int v = 0; v < TMAX; ++v) fin = fin && __builtin_isfinite(xt[v]);
+        if (__ballot(!fin) == 0) {
+#pragma unroll 4
+          for (int v = 0; v < T; ++v) {
+            const f32x4* Mrow = reinterpret_cast<const f32x4*>(Mh + v * TMAX);
+            float yv = sa[v * geo.HB + hb] * accs[v * kWave + lane];
+#pragma unroll
+            for (int u4 = 0; u4 < TMAX / 4; ++u4) {
+              const f32x4 m = Mrow[u4];
+              yv = fmaf(m.x, xt[4 * u4 + 0], yv);
+              yv = fmaf(m.y, xt[4 * u4 + 1], yv);
+              yv = fmaf(m.z, xt[4 * u4 + 2], yv);
+              yv = fmaf(m.w, xt[4 * u4 + 3], yv);
+            }
+            yo[(int64_t)v * DI] = yv;
           }
-          yo[(int64_t)v * DI] = yv;
+        } else {
+          // a non-finite conv output among the wave's channels: the zero
+          // weight of a node off v's root path would still make y_v NaN, so
+          // each node sums over its own root path alone, as the definition
+          // has it
+          for (int v = 0; v < T; ++v) {
+            const float* Mrow = Mh + v * TMAX;
+            float yv = sa[v * geo.HB + hb] * accs[v * kWave + lane];
+#pragma unroll
+            for (int u = 0; u < TMAX; ++u)
+              if (u < T && s_onk[v * TMAX + u]) yv = fmaf(Mrow[u], xt[u], yv);
+            yo[(int64_t)v * DI] = yv;
+          }
         }
       } else {
         // deep trees: conv in place over LDS (descending, so every input is
@@ -656,6 +679,10 @@ int launch_in(const VerifyArgs& a, hipStream_t s) {
 
 bool mfma_verify_applies(const Dims& d);
 int launch_verify_mfma(const VerifyArgs& a, bool bf16, hipStream_t s);
+#ifndef SSMT_VERIFY_ONESHOT
+#define SSMT_VERIFY_ONESHOT 1
+#endif
+constexpr bool kVerifyOneshot = SSMT_VERIFY_ONESHOT != 0;
 
 int launch_verify_fifo(const VerifyArgs& a, bool bf16, hipStream_t s);
 
@@ -675,9 +702,11 @@ bool verify_options_supported(const Dims& d, bool gate, bool bf16) {
   return (!d.xbc && !gate) || (!d.fifo && commit_verify_fused_applies(d));
 }
 
+int launch_verify_oneshot(const VerifyArgs& a, bool bf16, hipStream_t s);
+
 int launch_verify(const VerifyArgs& a, bool bf16, hipStream_t s) {
   if (a.d.fifo) return launch_verify_fifo(a, bf16, s);
-  if (mfma_verify_applies(a.d)) return launch_verify_mfma(a, bf16, s);
+  if (mfma_verify_applies(a.d)) return kVerifyOneshot ? launch_verify_oneshot(a, bf16, s) : launch_verify_mfma(a, bf16, s);
   if (tt_verify_applies(a.d)) {
     const int st = launch_verify_tt(a, bf16, s);
     // E_DIMS: its LDS does not fit this shape, nothing launched

@@ -239,7 +239,7 @@ __device__ __forceinline__ void m_form_slot(float* s_m, const float* s_cbt, cons
 
 // LDS layout (byte offsets)
 struct TtLds {
-  int parent, anc, cidx, misc, C, cbt, X, Y, Mo, So, S2, Ah, dt, D, cw, cb, total, row;
+  int parent, anc, cidx, misc, C, cbt, X, Y, Mo, So, S2, Ah, dt, D, cw, cb, nf, total, row;
   __host__ __device__ TtLds(int N, int E, int TT) {
     const int KT = 16 * TT, pair_bytes = 4 * 16 * kPairStride * pair_of(TT, 0);
     int o = 0;
@@ -265,11 +265,39 @@ struct TtLds {
     D = o; o += 32;                            // [block]; several heads per block: [parity][head]
     cw = o; o += 4 * 4 * kTtRows;              // [tap][channel], tap t = the node t steps up the path
     cb = o; o += 4 * kTtRows;
+    nf = o; o += kTtRows * kTtMaxT / 4;        // [channel][node quad] codes of non-finite conv outputs
     total = o;
   }
 };
 
 }  // namespace
+
+// Non-finite conv outputs.  In the product M . X~ the zero weight of a node u
+// off v's root path would still turn a non-finite x~_u into NaN in y_v.  So
+// the conv stores such an entry as zero, with a bit beside it (nibble q of
+// channel c: nodes 4 q .. 4 q + 3), and a block that has one (rare) then
+// overwrites, after the product, every y_v whose root path holds a
+// non-finite x~_u with NaN: by the definition's sum y_v is not finite there
+// (NaN, or an infinity that NaN stands for).
+__device__ __forceinline__ uint32_t nonfinite_quad(f32x4& q) {
+  uint32_t bits = 0;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const bool nf = !__builtin_isfinite(q[t]);
+    bits |= (nf ? 1u : 0u) << t;
+    q[t] = nf ? 0.0f : q[t];
+  }
+  return bits;
+}
+
+// The nodes whose conv output in channel `row` is not finite, as a bit mask.
+__device__ __forceinline__ uint64_t nonfinite_nodes(const uint8_t* nf, int row) {
+  const u32x4 w = *reinterpret_cast<const u32x4*>(nf + row * (kTtMaxT / 4));
+  uint64_t m = 0;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) m |= (uint64_t)((w[q >> 2] >> (8 * (q & 3))) & 15u) << (4 * q);
+  return m;
+}
 
 template <typename TIn, typename TS, int NG, int TT>
 __global__ void __launch_bounds__(kTtThreads) verify_tt_kernel(VerifyArgs a, int NBLK) {
@@ -299,6 +327,7 @@ __global__ void __launch_bounds__(kTtThreads) verify_tt_kernel(VerifyArgs a, int
   float* s_cbt = reinterpret_cast<float*>(smem + lo.cbt);
   unsigned char* s_B = smem + lo.X;
   float* s_xt = reinterpret_cast<float*>(smem + lo.X);
+  uint8_t* s_nf = smem + lo.nf;
   float* s_m = reinterpret_cast<float*>(smem + lo.Mo);
   TIn* s_xw = reinterpret_cast<TIn*>(smem + lo.Y);
   TIn* s_xr = s_xw + 3 * kTtRows;
@@ -544,6 +573,7 @@ __global__ void __launch_bounds__(kTtThreads) verify_tt_kernel(VerifyArgs a, int
       s_S2[hh * kTtMaxT + v] = s2;
       s_Ah[hh * kTtMaxT + v] = __builtin_amdgcn_exp2f((float)s2);
     }
+    uint32_t nf_any = 0;  // non-finite bits of this thread's conv outputs, or-ed
     {
       // causal conv over each node's root path, lane = channel, wave = node
       // quads wave, wave + 4, ...: a node's tap sources are the same for the
@@ -592,6 +622,9 @@ __global__ void __launch_bounds__(kTtThreads) verify_tt_kernel(VerifyArgs a, int
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) xq[r] = 4 * q + r < T ? xq[r] : 0.0f;
+        const uint32_t nfb = nonfinite_quad(xq);
+        s_nf[cl * (kTtMaxT / 4) + q] = (uint8_t)nfb;
+        nf_any |= nfb;
         // conv outputs [channel][node] in the MFMA B-operand layout: quad q
         // (nodes 4 q .. 4 q + 3) of channel row cl sits at quad q ^ (cl & 15),
         // so that the 16 channels a wave reads at once fall on different banks
@@ -615,7 +648,8 @@ __global__ void __launch_bounds__(kTtThreads) verify_tt_kernel(VerifyArgs a, int
         default: m_form_slot<TT, 3>(s_m, s_cbt, s_anc, S2w, dtw, Dh0, r, cq); break;
       }
     }
-    __syncthreads();  // conv outputs and M are complete; x rows, conv parameters and dt A are free
+    // conv outputs and M are complete; x rows, conv parameters and dt A are free
+    const bool xt_nonfinite = __syncthreads_or(nf_any != 0) != 0;
     if (blk + 1 < NBLK) deliver(blk + 1);
 
     // ---- C . h0 on the matrix cores: lane (c + 16 q) ends with (C_{16 ti + 4q + r} . h_c) ----
@@ -719,6 +753,11 @@ __global__ void __launch_bounds__(kTtThreads) verify_tt_kernel(VerifyArgs a, int
       // tiles above the loop would take most of the register file
       asm volatile("" ::: "memory");
     }
+    if (xt_nonfinite) {  // (rare) y_v not finite where v's root path holds a non-finite x~_u
+      const uint64_t nfm = nonfinite_nodes(s_nf, row);
+      for (int v = 4 * k; v < T; v = (v & 3) == 3 ? v + 13 : v + 1)  // this lane's nodes 16 ti + 4 k + r
+        if (s_anc[v] & nfm) yrow[(int64_t)v * DI] = __builtin_nanf("");
+    }
   }
 }
 
@@ -741,7 +780,7 @@ constexpr int kWsThreads = kWsWaves * kWave;
 constexpr int kWsMaxBlk = 16;
 
 struct TtWsLds {
-  int parent, anc, cidx, misc, C, cbt, X, Y, Mo, S2, Ah, dt, D, cw, cb, total, row, xbuf, ybuf, mbuf, cwbuf;
+  int parent, anc, cidx, misc, C, cbt, X, Y, Mo, S2, Ah, dt, D, cw, cb, nf, total, row, xbuf, ybuf, mbuf, cwbuf;
   __host__ __device__ TtWsLds(int N, int E, int TT) {
     const int KT = 16 * TT, pair_bytes = 4 * 16 * kPairStride * pair_of(TT, 0);
     int o = 0;
@@ -767,6 +806,7 @@ struct TtWsLds {
     cwbuf = 4 * 4 * kTtRows;
     cw = o; o += 2 * cwbuf;                  // [parity][tap][channel]
     cb = o; o += 2 * 4 * kTtRows;            // [parity][channel]
+    nf = o; o += 2 * kTtRows * kTtMaxT / 4;  // [parity][channel][node quad] codes of non-finite conv outputs
     total = o;
   }
 };
@@ -808,6 +848,7 @@ __global__ void __launch_bounds__(kWsThreads) verify_tt_ws_kernel(VerifyArgs a, 
   float* s_D = reinterpret_cast<float*>(smem + lo.D);
   const int rs = lo.row;
   auto s_xt = [&](int par) { return reinterpret_cast<float*>(smem + lo.X + par * lo.xbuf); };
+  auto s_nf = [&](int par) { return smem + lo.nf + par * (kTtRows * kTtMaxT / 4); };
   auto s_xw = [&](int par) { return reinterpret_cast<TIn*>(smem + lo.Y + par * lo.ybuf); };
   auto s_m = [&](int par) { return reinterpret_cast<float*>(smem + lo.Mo + par * lo.mbuf); };
   auto s_cw = [&](int par) { return reinterpret_cast<float*>(smem + lo.cw + par * lo.cwbuf); };
@@ -1004,7 +1045,11 @@ __global__ void __launch_bounds__(kWsThreads) verify_tt_ws_kernel(VerifyArgs a, 
   for (int ti = 0; ti < TT; ++ti) accp[ti] = f32x4{0.f, 0.f, 0.f, 0.f};
   __syncthreads();
 
+  // whether block ph - 1's conv outputs (set by the producers in phase ph - 1,
+  // read by the consumers in phase ph) hold a non-finite value
+  bool xt_nonfinite = false;
   for (int ph = 0; ph <= NBLK; ++ph) {
+    uint32_t nf_any = 0;  // (as in verify_tt_kernel)
     if (producer) {
       if (ph < NBLK) {
         const int par = ph & 1;
@@ -1053,6 +1098,9 @@ __global__ void __launch_bounds__(kWsThreads) verify_tt_ws_kernel(VerifyArgs a, 
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) xq[r] = 4 * q + r < T ? xq[r] : 0.0f;
+            const uint32_t nfb = nonfinite_quad(xq);
+            s_nf(par)[cl * (kTtMaxT / 4) + q] = (uint8_t)nfb;
+            nf_any |= nfb;
             // (the swizzled [channel][node] layout of verify_tt_kernel's conv outputs)
             *reinterpret_cast<f32x4*>(xt + cl * kTtMaxT + 4 * (q ^ (cl & 15))) = xq;
           }
@@ -1174,11 +1222,16 @@ __global__ void __launch_bounds__(kWsThreads) verify_tt_ws_kernel(VerifyArgs a, 
             const int v = 16 * ti + 4 * kk + r;
             if (v < T) yrow[(int64_t)v * DI] = tree_ok ? y[ti][r] : __builtin_nanf("");
           }
+        if (xt_nonfinite) {  // (rare) y_v not finite where v's root path holds a non-finite x~_u
+          const uint64_t nfm = nonfinite_nodes(s_nf(par), row);
+          for (int v = 4 * kk; v < T; v = (v & 3) == 3 ? v + 13 : v + 1)  // this lane's nodes 16 ti + 4 k + r
+            if (s_anc[v] & nfm) yrow[(int64_t)v * DI] = __builtin_nanf("");
+        }
       }
 #pragma unroll
       for (int ti = 0; ti < TT; ++ti) accp[ti] = acc[ti];
     }
-    __syncthreads();
+    xt_nonfinite = __syncthreads_or(nf_any != 0) != 0;
   }
 }
 
