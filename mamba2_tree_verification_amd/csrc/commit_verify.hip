@@ -168,8 +168,11 @@ __device__ __forceinline__ bool finite4(f32x4 v) {
 // xBC conv, the gate), so that the plain path keeps its registers and LDS.
 // VO: verify only (ssm_tree_verify): no previous tree, nothing committed,
 // no state or window written.
+// (verify only with bf16 inputs holds 7 waves per SIMD: its LDS leaves room
+// for 7 workgroups per CU)
 template <typename TIn, typename TS, int NG, bool OPT, bool VO>
-__global__ void __launch_bounds__(kCvWaves * kWave) commit_verify_kernel(CommitVerifyArgs a) {
+__global__ void __launch_bounds__(kCvWaves * kWave)
+    __attribute__((amdgpu_waves_per_eu(VO && sizeof(TIn) == 2 && NG <= 8 ? 7 : 1))) commit_verify_kernel(CommitVerifyArgs a) {
   typedef StateQuad<TS> SQ;
   constexpr int N = 16 * NG;
   constexpr int E = (int)sizeof(TIn);
@@ -329,13 +332,14 @@ __global__ void __launch_bounds__(kCvWaves * kWave) commit_verify_kernel(CommitV
   if constexpr (kWide) {
 #pragma unroll
     for (int gp = 0; gp < NG / 2; ++gp) {
-      const u32x4 w = *reinterpret_cast<const u32x4*>(sin + colq(2 * gp));
+      const u32x4* src = reinterpret_cast<const u32x4*>(sin + colq(2 * gp));
+      const u32x4 w = VO ? __builtin_nontemporal_load(src) : *src;
       hraw[2 * gp] = u32x2{w.x, w.y};
       hraw[2 * gp + 1] = u32x2{w.z, w.w};
     }
   } else {
 #pragma unroll
-    for (int gg = 0; gg < NG; ++gg) hraw[gg] = SQ::load(sin + colq(gg));
+    for (int gg = 0; gg < NG; ++gg) hraw[gg] = VO ? SQ::load_nt(sin + colq(gg)) : SQ::load(sin + colq(gg));
   }
   asm volatile("" : "+v"(r_dt));  // (keeps dt_raw's widening below the state loads)
 
@@ -481,33 +485,72 @@ __global__ void __launch_bounds__(kCvWaves * kWave) commit_verify_kernel(CommitV
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) s_cbt[(4 * k + r) * kCvT + j] = cbm[r];
-  } else if (wave == 2 && lane < kCvT) {
+  } else if (wave == 2) {
     // next tree: root-path set and conv inputs.  Every step requires
     // -1 <= parent < node, so the walks end and stay in range even on an
     // invalid tree (whose outputs are discarded).
-    int m = 0, packed = 0;
-    if (lane < T) {
-      int u = lane, a1 = -1, a2 = -1, a3 = -1;  // ancestors 1, 2, 3
-      int depth = 0;                            // nodes on the root path
-      for (int s = 0; s < kCvT && u >= 0; ++s) {
-        m |= 1 << u;
-        ++depth;
-        const int p = s_parent[u];
-        u = (p >= 0 && p < u) ? p : -1;
-        a1 = s == 0 ? u : a1;
-        a2 = s == 1 ? u : a2;
-        a3 = s == 2 ? u : a3;
-      }
-      // tap jj reads ancestor jj, or past the root window row W - 2 - (jj - depth)
+    if (lane < kCvT) {
+      int m = 0, packed = 0;
+      if (lane < T) {
+        int u = lane, a1 = -1, a2 = -1, a3 = -1;  // ancestors 1, 2, 3
+        int depth = 0;                            // nodes on the root path
+        for (int s = 0; s < kCvT && u >= 0; ++s) {
+          m |= 1 << u;
+          ++depth;
+          const int p = s_parent[u];
+          u = (p >= 0 && p < u) ? p : -1;
+          a1 = s == 0 ? u : a1;
+          a2 = s == 1 ? u : a2;
+          a3 = s == 2 ? u : a3;
+        }
+        // tap jj reads ancestor jj, or past the root window row W - 2 - (jj - depth)
 #pragma unroll
-      for (int jj = 1; jj < 4; ++jj) {
-        const int an = jj == 1 ? a1 : (jj == 2 ? a2 : a3);
-        const int code = an >= 0 ? an : T + (W - 2) - (jj - depth);
-        if (jj < W) packed |= code << (8 * (jj - 1));
+        for (int jj = 1; jj < 4; ++jj) {
+          const int an = jj == 1 ? a1 : (jj == 2 ? a2 : a3);
+          const int code = an >= 0 ? an : T + (W - 2) - (jj - depth);
+          if (jj < W) packed |= code << (8 * (jj - 1));
+        }
+      }
+      s_anc[lane] = m;
+      s_cidx[lane] = packed;
+    }
+    wave_sync();
+    // then the decay table, while the state is still in flight
+    // lane (head hh, node v): S_v = sum of dt * A over v's root path, in
+    // float64, then a_v = exp(S_v) and row v of the decay table,
+    // exp(S_v - S_u) dt_u for u on v's root path and 0 elsewhere.  The
+    // differences are taken in float64: on a deep path with large steps
+    // S_v and S_u are large and close, and a float32 difference would lose
+    // the digits that matter (the float64 sums of the same float32 terms
+    // cancel exactly, leaving the terms between u and v).
+    const int hh = lane >> 4, v = lane & 15;
+    const int m = s_anc[v];
+    double S = 0.0;
+    if (hh < HW) {
+#pragma unroll 4
+      for (int u = 0; u < kCvT; ++u) S += ((m >> u) & 1) ? (double)s_S[hh * kCvT + u] : 0.0;
+      s_Sd[hh * kCvT + v] = S;
+    }
+    wave_sync();
+    if (hh < HW) {
+      constexpr double kLog2e = 1.4426950408889634;
+      s_a[hh * kCvT + v] = __builtin_amdgcn_exp2f((float)(S * kLog2e));
+      float* mt = s_Mt + (hh * kCvT + v) * kCvT;
+      // (one quad at a time: the state of the whole workgroup is in flight in
+      // registers meanwhile)
+#pragma unroll 1
+      for (int u4 = 0; u4 < kCvT / 4; ++u4) {
+        f32x4 q;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int u = 4 * u4 + t;
+          q[t] = ((m >> u) & 1)
+                     ? __builtin_amdgcn_exp2f((float)((S - s_Sd[hh * kCvT + u]) * kLog2e)) * s_dt[hh * kCvT + u]
+                     : 0.0f;
+        }
+        *reinterpret_cast<f32x4*>(mt + 4 * u4) = q;
       }
     }
-    s_anc[lane] = m;
-    s_cidx[lane] = packed;
   }
   if (xv < lg) *reinterpret_cast<RawQ*>(s_xp + xv * kCvRows + xq) = rxp;
 #pragma unroll
@@ -563,42 +606,6 @@ __global__ void __launch_bounds__(kCvWaves * kWave) commit_verify_kernel(CommitV
           const int e = len + r;
           win_out[(int64_t)r * CH] = e < W - 1 ? s_win[e * kCvRows + lane] : s_xp[(e - (W - 1)) * kCvRows + lane];
         }
-      }
-    }
-  } else if (wave == 1) {
-    // lane (head hh, node v): S_v = sum of dt * A over v's root path, in
-    // float64, then a_v = exp(S_v) and row v of the decay table,
-    // exp(S_v - S_u) dt_u for u on v's root path and 0 elsewhere.  The
-    // differences are taken in float64: on a deep path with large steps
-    // S_v and S_u are large and close, and a float32 difference would lose
-    // the digits that matter (the float64 sums of the same float32 terms
-    // cancel exactly, leaving the terms between u and v).
-    const int hh = lane >> 4, v = lane & 15;
-    const int m = s_anc[v];
-    double S = 0.0;
-    if (hh < HW) {
-#pragma unroll 4
-      for (int u = 0; u < kCvT; ++u) S += ((m >> u) & 1) ? (double)s_S[hh * kCvT + u] : 0.0;
-      s_Sd[hh * kCvT + v] = S;
-    }
-    wave_sync();
-    if (hh < HW) {
-      constexpr double kLog2e = 1.4426950408889634;
-      s_a[hh * kCvT + v] = __builtin_amdgcn_exp2f((float)(S * kLog2e));
-      float* mt = s_Mt + (hh * kCvT + v) * kCvT;
-      // (one quad at a time: the state of the whole workgroup is in flight in
-      // registers meanwhile)
-#pragma unroll 1
-      for (int u4 = 0; u4 < kCvT / 4; ++u4) {
-        f32x4 q;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int u = 4 * u4 + t;
-          q[t] = ((m >> u) & 1)
-                     ? __builtin_amdgcn_exp2f((float)((S - s_Sd[hh * kCvT + u]) * kLog2e)) * s_dt[hh * kCvT + u]
-                     : 0.0f;
-        }
-        *reinterpret_cast<f32x4*>(mt + 4 * u4) = q;
       }
     }
   }
@@ -878,8 +885,8 @@ __global__ void __launch_bounds__(kCvWaves * kWave) commit_verify_kernel(CommitV
   {
     const int v = tid / 16, q = tid % 16;  // node row, 16-byte chunk of the 256-byte row segment
     if (v < T)
-      *reinterpret_cast<f32x4*>(a.y + (unit * T + v) * DI + c0 + 4 * q) =
-          *reinterpret_cast<const f32x4*>(s_ys + v * kCvRows + 4 * q);
+      __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(s_ys + v * kCvRows + 4 * q),
+                                  reinterpret_cast<f32x4*>(a.y + (unit * T + v) * DI + c0 + 4 * q));
   }
 }
 
