@@ -68,10 +68,14 @@ extern "C" {
  * xBC passes conv1d as a whole) instead of over x only.  The conv window,
  * conv_w and conv_b then span CH = H*P + 2*G*N channels in the order x,
  * B [G][N], C [G][N]; the SSM uses the convolved B and C.  Supported by
- * ssm_tree_verify and ssm_tree_commit_verify for trees of 1 to 16 nodes
- * with a headdim that is a multiple of 16 (not with SSM_TREE_VERIFY_FIFO),
- * and by ssm_tree_commit for every supported shape; other combinations
- * return SSM_TREE_E_DIMS. */
+ * ssm_tree_verify and ssm_tree_commit_verify for trees of 1 to 64 nodes
+ * with a headdim that is a multiple of 16 and, past 16 nodes, (H*P/G) a
+ * multiple of 64 and the float32-staged B and C rows within the LDS (bf16
+ * inputs: d_state up to 128 at 64 nodes, 256 up to 32 nodes; fp32 inputs:
+ * up to 64 at 64 nodes, 128 up to 48 nodes, 256 up to 32 nodes); not with
+ * SSM_TREE_VERIFY_FIFO; and by
+ * ssm_tree_commit for every supported shape.  Other combinations return
+ * SSM_TREE_E_DIMS before anything is enqueued. */
 #define SSM_TREE_CONV_XBC 4
 /* ssm_tree_verify computes every child state explicitly, walking the tree
  * breadth-first with a FIFO of live states (SpecMamba page sec. 3.2), instead

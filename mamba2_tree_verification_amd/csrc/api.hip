@@ -126,9 +126,9 @@ int ssm_tree_verify(const ssm_tree_dims* dims, const ssm_tree_params* params, co
     for (const Range& r : ins)
       if (overlaps(rs, r)) return SSM_TREE_E_ALIAS;
   }
-  if (d.xbc || z) {
-    // the options run on the fused round's kernel with nothing to commit:
-    // no path length, no state or window output
+  if ((d.xbc || z) && commit_verify_fused_applies(d)) {
+    // the options on trees of 1-16 nodes run on the fused round's kernel
+    // with nothing to commit: no path length, no state or window output
     CommitVerifyArgs a;
     memset(&a, 0, sizeof(a));
     a.d = d;

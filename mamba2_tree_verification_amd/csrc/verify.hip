@@ -690,7 +690,7 @@ int launch_verify_fifo(const VerifyArgs& a, bool bf16, hipStream_t s);
 // kernel then runs with nothing to commit (see ssm_tree_verify).
 bool commit_verify_fused_applies(const Dims& d);
 bool tt_verify_applies(const Dims& d);
-bool tt_verify_fits(const Dims& d, bool bf16);
+bool tt_verify_fits(const Dims& d, bool bf16, bool opt);
 int launch_verify_tt(const VerifyArgs& a, bool bf16, hipStream_t s);
 
 // A bfloat16 root state (SSM_TREE_STATE_BF16) is read by the matrix-core
@@ -698,8 +698,11 @@ int launch_verify_tt(const VerifyArgs& a, bool bf16, hipStream_t s);
 bool verify_options_supported(const Dims& d, bool gate, bool bf16) {
   if (d.sbf16)
     return d.T == 0 || (!d.fifo && !d.xbc && !gate &&
-                        (mfma_verify_applies(d) || (tt_verify_applies(d) && tt_verify_fits(d, bf16))));
-  return (!d.xbc && !gate) || (!d.fifo && commit_verify_fused_applies(d));
+                        (mfma_verify_applies(d) || (tt_verify_applies(d) && tt_verify_fits(d, bf16, false))));
+  // the options: trees of 1-16 nodes on the fused round's kernel, 17-64 on
+  // the options' instantiation of verify_tt_kernel
+  return (!d.xbc && !gate) ||
+         (!d.fifo && (commit_verify_fused_applies(d) || (tt_verify_applies(d) && tt_verify_fits(d, bf16, true))));
 }
 
 int launch_verify_oneshot(const VerifyArgs& a, bool bf16, hipStream_t s);
@@ -709,8 +712,9 @@ int launch_verify(const VerifyArgs& a, bool bf16, hipStream_t s) {
   if (mfma_verify_applies(a.d)) return kVerifyOneshot ? launch_verify_oneshot(a, bf16, s) : launch_verify_mfma(a, bf16, s);
   if (tt_verify_applies(a.d)) {
     const int st = launch_verify_tt(a, bf16, s);
-    // E_DIMS: its LDS does not fit this shape, nothing launched
-    if (st != SSM_TREE_E_DIMS || a.d.sbf16) return st;
+    // E_DIMS: its LDS does not fit this shape, nothing launched (the vector
+    // ALU kernel below takes neither the options nor a bf16 state)
+    if (st != SSM_TREE_E_DIMS || a.d.sbf16 || a.d.xbc || a.z) return st;
   }
   if (a.d.sbf16) return SSM_TREE_E_DIMS;
   return bf16 ? launch_in<bf16_t>(a, s) : launch_in<float>(a, s);

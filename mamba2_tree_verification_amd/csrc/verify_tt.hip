@@ -23,6 +23,8 @@
 // heads' S and dt, then C . h0 (the next block's state is loaded as soon as
 // each column group has been consumed), the path terms, and y staged in LDS
 // and stored as whole 256-byte row segments.
+#include <type_traits>
+
 #include "common.h"
 
 namespace ssmt {
@@ -239,11 +241,14 @@ __device__ __forceinline__ void m_form_slot(float* s_m, const float* s_cbt, cons
 
 // LDS layout (byte offsets)
 struct TtLds {
-  int parent, anc, cidx, misc, C, cbt, X, Y, Mo, So, S2, Ah, dt, D, cw, cb, nf, total, row;
-  __host__ __device__ TtLds(int N, int E, int TT) {
+  int parent, anc, cidx, misc, C, cbt, X, Y, Mo, So, S2, Ah, dt, D, cw, cb, nf, R, total, row, rawrow;
+  // opt: the Mamba2-convention options' instantiation, whose B and C rows are
+  // staged as float32 (convolved with the xBC conv), the raw rows apart
+  __host__ __device__ TtLds(int N, int E, int TT, bool opt = false) {
     const int KT = 16 * TT, pair_bytes = 4 * 16 * kPairStride * pair_of(TT, 0);
     int o = 0;
-    row = N * E + 16;                          // staged B / C row stride (padded)
+    rawrow = N * E + 16;                       // raw B / C row stride (padded)
+    row = opt ? N * 4 + 16 : rawrow;           // staged B / C row stride (padded)
     parent = o; o += 4 * kTtMaxT;
     anc = o; o += 8 * kTtMaxT;                 // root-path bitmask per node (64 bits)
     cidx = o; o += 4 * kTtMaxT;                // conv inputs of taps 1..3: row of the window-and-x rows
@@ -266,6 +271,7 @@ struct TtLds {
     cw = o; o += 4 * 4 * kTtRows;              // [tap][channel], tap t = the node t steps up the path
     cb = o; o += 4 * kTtRows;
     nf = o; o += kTtRows * kTtMaxT / 4;        // [channel][node quad] codes of non-finite conv outputs
+    R = o; o += opt ? 2 * KT * rawrow : 0;     // (opt) raw B rows, then raw C rows
     total = o;
   }
 };
@@ -299,9 +305,14 @@ __device__ __forceinline__ uint64_t nonfinite_nodes(const uint8_t* nf, int row) 
   return m;
 }
 
-template <typename TIn, typename TS, int NG, int TT>
+// OPT: the Mamba2-convention options (the xBC conv, the gate) in an
+// instantiation of their own: B and C rows staged as float32 (convolved over
+// each node's path with the xBC conv), products on the float32 matrix
+// cores, y gated by silu(z).
+template <typename TIn, typename TS, int NG, int TT, bool OPT>
 __global__ void __launch_bounds__(kTtThreads) verify_tt_kernel(VerifyArgs a, int NBLK) {
   typedef StateQuad<TS> SQ;
+  typedef typename std::conditional<OPT, float, TIn>::type TR;  // element type of the staged B and C rows
   constexpr int N = 16 * NG;
   constexpr int E = (int)sizeof(TIn);
   constexpr int KT = 16 * TT;                      // node capacity
@@ -318,7 +329,7 @@ __global__ void __launch_bounds__(kTtThreads) verify_tt_kernel(VerifyArgs a, int
   const int g = cw0 / (DI / G);
 
   extern __shared__ __align__(16) unsigned char smem[];
-  const TtLds lo(N, E, TT);
+  const TtLds lo(N, E, TT, OPT);
   int32_t* s_parent = reinterpret_cast<int32_t*>(smem + lo.parent);
   uint64_t* s_anc = reinterpret_cast<uint64_t*>(smem + lo.anc);
   int32_t* s_cidx = reinterpret_cast<int32_t*>(smem + lo.cidx);
@@ -352,6 +363,9 @@ __global__ void __launch_bounds__(kTtThreads) verify_tt_kernel(VerifyArgs a, int
   if (tid < kTtMaxT) s_parent[tid] = tid < T ? a.parent[(int64_t)b * T + tid] : 0;
   const unsigned char* Cg = reinterpret_cast<const unsigned char*>(a.C) + ((unit * T) * G + g) * (int64_t)N * E;
   const unsigned char* Bg = reinterpret_cast<const unsigned char*>(a.B) + ((unit * T) * G + g) * (int64_t)N * E;
+  // (with the options the raw rows go to a staging area of their own)
+  unsigned char* rawB = OPT ? smem + lo.R : s_B;
+  unsigned char* rawC = OPT ? smem + lo.R + KT * lo.rawrow : s_C;
   for (int ci = tid; ci < KT * kChunks; ci += kTtThreads) {
     const int v = ci / kChunks, q = ci % kChunks;
     u32x4 c4 = u32x4{0u, 0u, 0u, 0u}, b4 = c4;  // zero rows past T
@@ -359,8 +373,8 @@ __global__ void __launch_bounds__(kTtThreads) verify_tt_kernel(VerifyArgs a, int
       c4 = *reinterpret_cast<const u32x4*>(Cg + (int64_t)v * G * N * E + q * 16);
       b4 = *reinterpret_cast<const u32x4*>(Bg + (int64_t)v * G * N * E + q * 16);
     }
-    *reinterpret_cast<u32x4*>(s_C + v * rs + q * 16) = c4;
-    *reinterpret_cast<u32x4*>(s_B + v * rs + q * 16) = b4;
+    *reinterpret_cast<u32x4*>(rawC + v * lo.rawrow + q * 16) = c4;
+    *reinterpret_cast<u32x4*>(rawB + v * lo.rawrow + q * 16) = b4;
   }
   __syncthreads();
   if (wave == 0) {
@@ -402,6 +416,56 @@ __global__ void __launch_bounds__(kTtThreads) verify_tt_kernel(VerifyArgs a, int
       if (blockIdx.x == 0 && l == 0 && a.seq_status) a.seq_status[b] = ok ? SSM_TREE_OK : SSM_TREE_E_TREE;
     }
   }
+  if constexpr (OPT) {
+    // the B and C rows as float32: with the xBC conv, each node's row
+    // convolved over its root path (taps past the root read the committed
+    // window's B and C channels), with SiLU when set; thread = state column
+    // n of B (i < N) or of C
+    __syncthreads();  // the tap codes
+    const TIn* wing = reinterpret_cast<const TIn*>(a.window) + unit * (W - 1) * (int64_t)CH;
+    for (int i = tid; i < 2 * N; i += kTtThreads) {
+      const bool isC = i >= N;
+      const int n = isC ? i - N : i;
+      const unsigned char* raw = isC ? rawC : rawB;
+      unsigned char* dst = isC ? s_C : s_B;
+      float w[4] = {0.f, 0.f, 0.f, 0.f}, bias = 0.f, win[3] = {0.f, 0.f, 0.f};
+      if (d.xbc) {
+        const int ch = DI + (isC ? G * N : 0) + g * N + n;
+        const float* cw = a.prm.conv_w + ((int64_t)l * CH + ch) * W;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) w[jj] = jj < W ? cw[W - 1 - jj] : 0.0f;  // by taps back
+        if (a.prm.conv_b) bias = a.prm.conv_b[(int64_t)l * CH + ch];
+#pragma unroll
+        for (int r = 0; r < 3; ++r)
+          if (r < W - 1) win[r] = load_in(wing, (int64_t)r * CH + ch);
+      }
+      for (int v = 0; v < KT; ++v) {
+        float z = 0.0f;
+        if (v < T) {
+          const float u0 = load_in(reinterpret_cast<const TIn*>(raw + v * lo.rawrow), n);
+          if (d.xbc) {
+            const int codes = s_cidx[v];
+            z = fmaf(w[0], u0, bias);
+#pragma unroll
+            for (int jj = 1; jj < 4; ++jj) {
+              if (jj < W) {
+                // code >= 3: node code - 3; else window row code + W - 4
+                const int code = (codes >> (8 * (jj - 1))) & 255;
+                const float u = code >= 3 ? load_in(reinterpret_cast<const TIn*>(raw + (code - 3) * lo.rawrow), n)
+                                          : (code + W - 4 == 0 ? win[0] : (code + W - 4 == 1 ? win[1] : win[2]));
+                z = fmaf(w[jj], u, z);
+              }
+            }
+            if (d.silu) z = silu_fast(z);
+          } else {
+            z = u0;
+          }
+        }
+        reinterpret_cast<float*>(dst + v * rs)[n] = z;
+      }
+    }
+    __syncthreads();
+  }
   // C_v . B_u over the lower-triangular tile pairs, B rows as the A operand
   // and C rows as the B operand: lane (i + 16 k) ends with
   // (B_{16 tj + 4k + t} . C_{16 ti + i}) = CB[16 ti + i][16 tj + 4 k + t]
@@ -410,9 +474,9 @@ __global__ void __launch_bounds__(kTtThreads) verify_tt_kernel(VerifyArgs a, int
     while ((ti + 1) * (ti + 2) / 2 <= pi) ++ti;
     const int tj = pi - ti * (ti + 1) / 2;
     f32x4 cb = f32x4{0.f, 0.f, 0.f, 0.f};
-    const TIn* brow = reinterpret_cast<const TIn*>(s_B + (16 * tj + j) * rs) + 4 * k;
-    const TIn* crow = reinterpret_cast<const TIn*>(s_C + (16 * ti + j) * rs) + 4 * k;
-    if constexpr (E == 2) {
+    const TR* brow = reinterpret_cast<const TR*>(s_B + (16 * tj + j) * rs) + 4 * k;
+    const TR* crow = reinterpret_cast<const TR*>(s_C + (16 * ti + j) * rs) + 4 * k;
+    if constexpr (sizeof(TR) == 2) {
       // bf16 rows are exact bf16 operands: k slots = state indices
       // 16 g + 4 k .. + 3 of column groups g = 2 m, 2 m + 1
 #pragma unroll
@@ -429,8 +493,8 @@ __global__ void __launch_bounds__(kTtThreads) verify_tt_kernel(VerifyArgs a, int
     } else {
 #pragma unroll
       for (int gg = 0; gg < NG; ++gg) {
-        const f32x4 bq = load4<TIn>(brow + 16 * gg);
-        const f32x4 cq = load4<TIn>(crow + 16 * gg);
+        const f32x4 bq = load4<TR>(brow + 16 * gg);
+        const f32x4 cq = load4<TR>(crow + 16 * gg);
         cb = mfma4(bq.x, cq.x, cb);
         cb = mfma4(bq.y, cq.y, cb);
         cb = mfma4(bq.z, cq.z, cb);
@@ -659,7 +723,7 @@ __global__ void __launch_bounds__(kTtThreads) verify_tt_kernel(VerifyArgs a, int
     for (int ti = 0; ti < TT; ++ti) acc[ti] = f32x4{0.f, 0.f, 0.f, 0.f};
     const bool more = blk + 1 < NBLK;
     const TS* nsin = reinterpret_cast<const TS*>(a.state) + (unit * DI + c0 + kTtRows + wave * 16 + j) * (int64_t)N + 4 * k;
-    if constexpr (E == 2) {
+    if constexpr (sizeof(TR) == 2) {
       // bf16 C rows against the state, two column groups per product: a
       // bf16 state is an exact operand as it stands; an fp32 state is split
       // into three bf16 terms
@@ -675,7 +739,7 @@ __global__ void __launch_bounds__(kTtThreads) verify_tt_kernel(VerifyArgs a, int
         }
 #pragma unroll
         for (int ti = 0; ti < TT; ++ti) {
-          const TIn* crow = reinterpret_cast<const TIn*>(s_C + (16 * ti + j) * rs) + 32 * m + 4 * k;
+          const TR* crow = reinterpret_cast<const TR*>(s_C + (16 * ti + j) * rs) + 32 * m + 4 * k;
           const u32x2 c0 = *reinterpret_cast<const u32x2*>(crow);
           const u32x2 c1 = two ? *reinterpret_cast<const u32x2*>(crow + 16) : u32x2{0u, 0u};
           const u32x4 ca = u32x4{c0.x, c0.y, c1.x, c1.y};
@@ -698,7 +762,7 @@ __global__ void __launch_bounds__(kTtThreads) verify_tt_kernel(VerifyArgs a, int
         const f32x4 h = SQ::to_f32(hq[gg]);
 #pragma unroll
         for (int ti = 0; ti < TT; ++ti) {
-          const f32x4 cq = load4<TIn>(reinterpret_cast<const TIn*>(s_C + (16 * ti + j) * rs) + 16 * gg + 4 * k);
+          const f32x4 cq = load4<TR>(reinterpret_cast<const TR*>(s_C + (16 * ti + j) * rs) + 16 * gg + 4 * k);
           acc[ti] = mfma4(cq.x, h.x, acc[ti]);
           acc[ti] = mfma4(cq.y, h.y, acc[ti]);
           acc[ti] = mfma4(cq.z, h.z, acc[ti]);
@@ -747,7 +811,10 @@ __global__ void __launch_bounds__(kTtThreads) verify_tt_kernel(VerifyArgs a, int
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int v = 16 * ti + 4 * k + r;
-        if (v < T) yrow[(int64_t)v * DI] = tree_ok ? y[r] : __builtin_nanf("");
+        float yv = y[r];
+        if constexpr (OPT)  // the gate: y silu(z)
+          if (a.z) yv *= silu_fast(load_in(reinterpret_cast<const TIn*>(a.z) + (unit * T + v) * (int64_t)DI + c0 + row, 0));
+        if (v < T) yrow[(int64_t)v * DI] = tree_ok ? yv : __builtin_nanf("");
       }
       // one node tile's operands at a time: hoisting the LDS reads of all
       // tiles above the loop would take most of the register file
@@ -1247,15 +1314,15 @@ int launch_ws_t(const VerifyArgs& a, int nblk, hipStream_t s) {
   return hipGetLastError() == hipSuccess ? SSM_TREE_OK : SSM_TREE_E_HIP;
 }
 
-template <typename TIn, typename TS, int NG, int TT>
+template <typename TIn, typename TS, int NG, int TT, bool OPT = false>
 int launch_tt_t(const VerifyArgs& a, hipStream_t s) {
-  const size_t lds = (size_t)TtLds(16 * NG, (int)sizeof(TIn), TT).total;
+  const size_t lds = (size_t)TtLds(16 * NG, (int)sizeof(TIn), TT, OPT).total;
   if (lds > 160 * 1024) return SSM_TREE_E_DIMS;  // (fp32 inputs with d_state 256) the caller falls back
-  if (allow_lds(verify_tt_kernel<TIn, TS, NG, TT>, lds) != hipSuccess) return SSM_TREE_E_HIP;
+  if (allow_lds(verify_tt_kernel<TIn, TS, NG, TT, OPT>, lds) != hipSuccess) return SSM_TREE_E_HIP;
   const int blocks = a.d.d_in / a.d.G / kTtRows;  // 64-channel blocks per B/C group
   const int nblk = blocks % 4 == 0 ? 4 : (blocks % 2 == 0 ? 2 : 1);
   dim3 grid(a.d.d_in / (nblk * kTtRows), a.d.Bsz, a.d.L);
-  hipLaunchKernelGGL((verify_tt_kernel<TIn, TS, NG, TT>), grid, dim3(kTtThreads), lds, s, a, nblk);
+  hipLaunchKernelGGL((verify_tt_kernel<TIn, TS, NG, TT, OPT>), grid, dim3(kTtThreads), lds, s, a, nblk);
   return hipGetLastError() == hipSuccess ? SSM_TREE_OK : SSM_TREE_E_HIP;
 }
 
@@ -1263,6 +1330,8 @@ int launch_tt_t(const VerifyArgs& a, hipStream_t s) {
 // can take 8 or 16 blocks (else the per-block kernel)
 template <typename TIn, typename TS, int NG, int TT>
 int launch_tt_pick(const VerifyArgs& a, hipStream_t s) {
+  if constexpr (sizeof(TS) == 4)  // the options: the per-block kernel's instantiation of their own
+    if (a.d.xbc || a.z) return launch_tt_t<TIn, TS, NG, TT, true>(a, s);
   const int blocks = a.d.d_in / a.d.G / kTtRows;
   if (a.d.P % kTtRows == 0 && blocks % 8 == 0) {
     const int st = launch_ws_t<TIn, TS, NG, TT>(a, blocks % kWsMaxBlk == 0 ? kWsMaxBlk : 8, s);
@@ -1299,10 +1368,10 @@ bool tt_verify_applies(const Dims& d) {
 }
 
 // whether the kernel's LDS fits the shape (it does except for fp32 inputs
-// with d_state 256)
-bool tt_verify_fits(const Dims& d, bool bf16) {
+// with d_state 256); opt: the options' instantiation
+bool tt_verify_fits(const Dims& d, bool bf16, bool opt) {
   const int TT = (d.T + 15) / 16;
-  return TtLds(d.N, bf16 ? 2 : 4, TT < 2 ? 2 : TT).total <= 160 * 1024;
+  return TtLds(d.N, bf16 ? 2 : 4, TT < 2 ? 2 : TT, opt).total <= 160 * 1024;
 }
 
 int launch_verify_tt(const VerifyArgs& a, bool bf16, hipStream_t s) {

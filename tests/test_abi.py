@@ -205,10 +205,11 @@ def test_option_host_checks():
     assert call_verify(good_dims(), p, z=fake(30, 8)) == m.E_ALIGN
     assert call_verify(good_dims(), p, z=fake(8)) == m.E_ALIAS           # z over y
     assert call_verify(good_dims(), p, z=fake(30), status=fake(30, 64)) == m.E_ALIAS
-    # shapes no kernel takes with an option: T > 16, headdim not a multiple of 16, the FIFO walk
-    assert call_verify(good_dims(T=20), p, z=fake(30)) == m.E_DIMS
+    # shapes no kernel takes with an option: headdim not a multiple of 16,
+    # fp32 inputs with 64 nodes and d_state 128 (LDS), the FIFO walk
+    assert call_verify(good_dims(T=64, bf16=False), p, z=fake(30)) == m.E_DIMS
     assert call_verify(good_dims(H=8, P=40), p, z=fake(30)) == m.E_DIMS
-    d = good_dims(T=20)
+    d = good_dims(T=64, bf16=False)
     d.flags = m.SSM_TREE_CONV_XBC
     assert call_verify(d, p) == m.E_DIMS
     d = good_dims()
@@ -227,8 +228,8 @@ def test_option_host_checks():
     assert call_commit_verify(dx, p, C_prev=None) == m.E_NULL
     assert call_commit_verify(good_dims(), p, z=fake(8)) == m.E_ALIAS    # z over y
     assert call_commit_verify(good_dims(), p, z=fake(30, 8)) == m.E_ALIGN
-    assert call_commit_verify(good_dims(T=20), p, z=fake(30)) == m.E_DIMS
-    d = good_dims(T=20)
+    assert call_commit_verify(good_dims(T=64, bf16=False), p, z=fake(30)) == m.E_DIMS
+    d = good_dims(T=64, bf16=False)
     d.flags = m.SSM_TREE_CONV_XBC
     assert call_commit_verify(d, p) == m.E_DIMS
 

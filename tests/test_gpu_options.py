@@ -4,11 +4,13 @@ in_proj's xBC passes conv1d as a whole) and the output gate y * silu(z)
 (LightMamba part, "why Mamba is hard to accelerate": Y is multiplied
 elementwise with Z).
 
-ssm_tree_commit takes the xBC conv for every shape; ssm_tree_commit_verify
-and ssm_tree_verify take both options on the fused round's shapes (trees
-of at most 16 nodes, headdim a multiple of 16); every other combination
-must be refused on the host with SSM_TREE_E_DIMS before anything is
-enqueued.  Tolerance as elsewhere:
+ssm_tree_commit takes the xBC conv for every shape; ssm_tree_verify takes
+both options on trees of 1-16 nodes (the fused round's kernel with nothing
+to commit) and of 17-64 nodes (the options' instantiation of the 17-64-node
+matrix-core kernel), with a headdim that is a multiple of 16;
+ssm_tree_commit_verify fuses them up to 16 nodes and runs the two calls
+past that.  Every other combination must be refused on the host with
+SSM_TREE_E_DIMS before anything is enqueued.  Tolerance as elsewhere:
 |gpu - oracle| <= 1e-5 + 1e-4 |oracle|; windows and statuses exactly.
 """
 import numpy as np
@@ -90,6 +92,14 @@ ROUND_SPECS = [  # T, H, P, N, G, W, bf16, silu, conv_b, xbc, gate
     (1, 8, 16, 16, 1, 2, True, False, False, True, True),
     (13, 2, 128, 256, 1, 4, True, True, False, True, True),
     (10, 6, 32, 32, 3, 1, False, False, True, True, True),
+    # 17-64 nodes: verify on the options' instantiation of the 17-64-node
+    # kernel (the round as commit + verify)
+    (40, 4, 64, 128, 1, 4, True, True, False, True, True),
+    (64, 2, 64, 128, 1, 4, True, True, True, True, False),
+    (24, 8, 32, 64, 2, 3, False, True, True, True, True),
+    (33, 4, 16, 32, 1, 4, True, False, False, False, True),
+    (20, 2, 128, 256, 1, 2, True, True, False, True, True),
+    (50, 6, 32, 16, 3, 1, True, False, True, True, True),
 ]
 
 
@@ -146,6 +156,23 @@ def test_round_options_full_size():
     out = step.run(inplace=True, state=step.gp.state.clone(), window=step.gp.window.clone())
     assert not torch.isnan(out[2]).any()
     units = sample_units(cfg, 6, np.random.default_rng(180), [(0, 0), (cfg.L - 1, cfg.Bsz - 1)])
+    check(step, out, units)
+
+
+def test_options_stress_full_size():
+    """The stress workload (64 layers, batch 64, trees of 64 nodes: chains,
+    stars, random depth <= 8) with SiLU over the xBC conv and the gate:
+    verify alone, then the round (commit + verify), on sampled units
+    including the 64-chain and the 64-star."""
+    cfg = C.CONFIGS[4].replace(cid=220, silu=True, xbc=True, gate=True)
+    log("options stress: generating")
+    step = Step(cfg)
+    must = [(0, 0), (cfg.L - 1, cfg.Bsz - 1), (cfg.L // 2, 0), (cfg.L // 3, 1)]
+    units = sample_units(cfg, 4, np.random.default_rng(220), must)
+    log("options stress: round on GPU")
+    out = step.run(inplace=True, state=step.gp.state.clone(), window=step.gp.window.clone())
+    assert not torch.isnan(out[2]).any()
+    log("options stress: oracle on %d units" % len(units))
     check(step, out, units)
 
 
@@ -218,9 +245,11 @@ def test_draft_decode_with_options():
 # ----------------------------------------------------------------------------
 
 def test_unsupported_option_combinations_refused():
-    # verify alone on a shape the fused kernel does not take (T > 16), and
-    # with the FIFO walk: refused, y untouched
-    for kw in (dict(T=20), dict(P=40, H=8)):
+    # verify alone on shapes no kernel takes with the options (headdim not a
+    # multiple of 16; fp32 inputs with 64 nodes and d_state 128, whose
+    # float32 B, C and raw rows exceed the LDS), and with the FIFO walk:
+    # refused, y untouched
+    for kw in (dict(P=40, H=8), dict(T=64, bf16=False)):
         cfg = _cfg(190, **kw)
         case = GpuCase(cfg)
         y = torch.full((cfg.L, cfg.Bsz, cfg.T, cfg.d_in), 5.0, device="cuda")
@@ -232,9 +261,10 @@ def test_unsupported_option_combinations_refused():
     with pytest.raises(m.SsmTreeError) as e:
         case.verify()
     assert e.value.code == m.E_DIMS
-    # the fused round on a shape it does not fuse (T > 16): the two calls would
-    # need verify to take the options; nothing may run, the state stays
-    cfg = _cfg(191, T=20)
+    # the round on a shape it does not fuse (T > 16): the two calls would need
+    # verify to take the options, which it does not here; nothing may run,
+    # the state stays
+    cfg = _cfg(191, T=64, bf16=False)
     step = Step(cfg)
     s_in = step.gp.state.clone()
     with pytest.raises(m.SsmTreeError) as e:
