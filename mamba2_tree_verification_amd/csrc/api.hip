@@ -14,6 +14,8 @@ bool verify_options_supported(const Dims& d, bool gate, bool bf16);
 bool commit_options_supported(const Dims& d);
 bool commit_verify_options_supported(const Dims& d, bool gate);
 int launch_commit_verify(const CommitVerifyArgs& a, bool bf16, hipStream_t s);
+bool tt_round_applies(const Dims& d, bool bf16, bool gate);
+int launch_tt_round(const CommitVerifyArgs& a, hipStream_t s);
 hipError_t launch_plan(const int32_t* parent, int Bsz, int T, int W, int32_t* out, hipStream_t s);
 hipError_t launch_status(int32_t* seq_status, int Bsz, int value, hipStream_t s);
 }  // namespace ssmt
@@ -21,6 +23,13 @@ hipError_t launch_status(int32_t* seq_status, int Bsz, int value, hipStream_t s)
 using namespace ssmt;
 
 namespace {
+
+// the one-launch round for trees of 17-64 nodes (0 in a build that times
+// the two-call form against it)
+#ifndef SSMT_TT_ROUND
+#define SSMT_TT_ROUND 1
+#endif
+constexpr bool kTtRound = SSMT_TT_ROUND != 0;
 
 struct Range {
   uintptr_t lo, hi;  // [lo, hi)
@@ -290,23 +299,7 @@ int ssm_tree_commit_verify(const ssm_tree_dims* dims, const ssm_tree_params* par
     if (i != 1 && overlaps(outs[i], rwi)) return SSM_TREE_E_ALIAS;
   }
   hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
-  if (!fused) {
-    // The two calls in turn, on the same stream.  The outputs first receive
-    // the inputs and the commit then runs in place on them, so that a
-    // sequence whose commit fails carries its old state and window into the
-    // verify, as the fused kernel does.
-    if (state_out != state_in &&
-        hipMemcpyAsync(state_out, state_in, rso.hi - rso.lo, hipMemcpyDeviceToDevice, s) != hipSuccess)
-      return SSM_TREE_E_HIP;
-    if (wbytes && conv_window_out != conv_window_in &&
-        hipMemcpyAsync(conv_window_out, conv_window_in, wbytes, hipMemcpyDeviceToDevice, s) != hipSuccess)
-      return SSM_TREE_E_HIP;
-    st = ssm_tree_commit(dims, params, parent_prev, path, path_len, x_prev, B_prev, Cp, dt_raw_prev,
-                         conv_window_out, state_out, conv_window_out, state_out, commit_status, hip_stream);
-    if (st) return st;
-    return ssm_tree_verify(dims, params, parent, x, B, C, dt_raw, z, conv_window_out, state_out, y, verify_status,
-                           hip_stream);
-  }
+  const bool bf16 = dims->in_dtype == SSM_TREE_BF16;
   CommitVerifyArgs a;
   a.d = d;
   a.prm = Params{params->A, params->D, params->dt_bias, params->conv_w, params->conv_b};
@@ -330,7 +323,28 @@ int ssm_tree_commit_verify(const ssm_tree_dims* dims, const ssm_tree_params* par
   a.y = y;
   a.commit_status = commit_status;
   a.verify_status = verify_status;
-  return launch_commit_verify(a, dims->in_dtype == SSM_TREE_BF16, s);
+  if (fused) return launch_commit_verify(a, bf16, s);
+  // trees of 17-64 nodes: one launch where the role-split verify applies
+  // (E_DIMS from it: nothing was launched)
+  if (kTtRound && tt_round_applies(d, bf16, z != nullptr)) {
+    st = launch_tt_round(a, s);
+    if (st != SSM_TREE_E_DIMS) return st;
+  }
+  // The two calls in turn, on the same stream.  The outputs first receive
+  // the inputs and the commit then runs in place on them, so that a
+  // sequence whose commit fails carries its old state and window into the
+  // verify, as the fused kernels do.
+  if (state_out != state_in &&
+      hipMemcpyAsync(state_out, state_in, rso.hi - rso.lo, hipMemcpyDeviceToDevice, s) != hipSuccess)
+    return SSM_TREE_E_HIP;
+  if (wbytes && conv_window_out != conv_window_in &&
+      hipMemcpyAsync(conv_window_out, conv_window_in, wbytes, hipMemcpyDeviceToDevice, s) != hipSuccess)
+    return SSM_TREE_E_HIP;
+  st = ssm_tree_commit(dims, params, parent_prev, path, path_len, x_prev, B_prev, Cp, dt_raw_prev, conv_window_out,
+                       state_out, conv_window_out, state_out, commit_status, hip_stream);
+  if (st) return st;
+  return ssm_tree_verify(dims, params, parent, x, B, C, dt_raw, z, conv_window_out, state_out, y, verify_status,
+                         hip_stream);
 }
 
 int ssm_tree_plan(const ssm_tree_dims* dims, const int32_t* parent, int32_t* plan_out, void* hip_stream) {

@@ -847,8 +847,10 @@ constexpr int kWsThreads = kWsWaves * kWave;
 constexpr int kWsMaxBlk = 16;
 
 struct TtWsLds {
-  int parent, anc, cidx, misc, C, cbt, X, Y, Mo, S2, Ah, dt, D, cw, cb, nf, total, row, xbuf, ybuf, mbuf, cwbuf;
-  __host__ __device__ TtWsLds(int N, int E, int TT) {
+  int parent, anc, cidx, misc, C, cbt, X, Y, Mo, S2, Ah, dt, D, cw, cb, nf, nff, total, row, xbuf, ybuf, mbuf, cwbuf;
+  // cm: the commit's own arrays (offset 0 when unused)
+  int pparent, path, Pr, wt, at;
+  __host__ __device__ TtWsLds(int N, int E, int TT, bool cm = false) {
     const int KT = 16 * TT, pair_bytes = 4 * 16 * kPairStride * pair_of(TT, 0);
     int o = 0;
     row = N * E + 16;
@@ -874,14 +876,25 @@ struct TtWsLds {
     cw = o; o += 2 * cwbuf;                  // [parity][tap][channel]
     cb = o; o += 2 * 4 * kTtRows;            // [parity][channel]
     nf = o; o += 2 * kTtRows * kTtMaxT / 4;  // [parity][channel][node quad] codes of non-finite conv outputs
+    nff = o; o += 4 * (kWsMaxBlk + 1);       // [phase] whether the block's conv outputs hold a non-finite value
+    pparent = path = Pr = wt = at = 0;
+    if (cm) {
+      pparent = o; o += 4 * kTtMaxT;         // the committed tree's parent[]
+      path = o; o += 4 * kTtMaxT;            // the accepted path
+      Pr = o; o += 2 * ybuf;                 // [parity] old window rows and the path's x rows, raw
+      wt = o; o += 4 * kWsMaxBlk * kTtMaxT;  // [block][path position] exp(P_last - P_q) dt_q
+      at = o; o += 4 * kWsMaxBlk;            // [block] exp(P_last)
+      // the path's B rows (raw, zero past its length) take the C rows' place
+      // once the matrix-core operands hold those
+    }
     total = o;
   }
 };
 
 }  // namespace
 
-template <typename TIn, typename TS, int NG, int TT>
-__global__ void __launch_bounds__(kWsThreads) verify_tt_ws_kernel(VerifyArgs a, int NBLK) {
+template <typename TIn, typename TS, int NG, int TT, bool CM>
+__global__ void __launch_bounds__(kWsThreads) verify_tt_ws_kernel(CommitVerifyArgs a, int NBLK) {
   typedef StateQuad<TS> SQ;
   constexpr int N = 16 * NG;
   constexpr int E = (int)sizeof(TIn);
@@ -900,9 +913,19 @@ __global__ void __launch_bounds__(kWsThreads) verify_tt_ws_kernel(VerifyArgs a, 
   const int cw0 = blockIdx.x * NBLK * kTtRows;
   const int g = cw0 / (DI / G);
 
+  // the commit's path B rows replace the C rows, which the consumers then
+  // hold in registers
+  static_assert(!CM || (E == 2 && NG <= 8), "commit: bf16 inputs, d_state <= 128");
+
   extern __shared__ __align__(16) unsigned char smem[];
-  const TtWsLds lo(N, E, TT);
+  const TtWsLds lo(N, E, TT, CM);
   int32_t* s_parent = reinterpret_cast<int32_t*>(smem + lo.parent);
+  int32_t* s_pparent = reinterpret_cast<int32_t*>(smem + lo.pparent);
+  int32_t* s_path = reinterpret_cast<int32_t*>(smem + lo.path);
+  float* s_wt = reinterpret_cast<float*>(smem + lo.wt);
+  float* s_at = reinterpret_cast<float*>(smem + lo.at);
+  auto s_pr = [&](int par) { return reinterpret_cast<TIn*>(smem + lo.Pr + par * lo.ybuf); };
+  int32_t* s_nff = reinterpret_cast<int32_t*>(smem + lo.nff);
   uint64_t* s_anc = reinterpret_cast<uint64_t*>(smem + lo.anc);
   int32_t* s_cidx = reinterpret_cast<int32_t*>(smem + lo.cidx);
   int32_t* s_misc = reinterpret_cast<int32_t*>(smem + lo.misc);
@@ -924,13 +947,21 @@ __global__ void __launch_bounds__(kWsThreads) verify_tt_ws_kernel(VerifyArgs a, 
   // ---- consumers: the first block's state, in flight during the prologue ----
   typename SQ::Raw hq[NG];
   if (!producer) {
-    const TS* sin = reinterpret_cast<const TS*>(a.state) + (unit * DI + cw0 + rw * 16 + j) * (int64_t)N + 4 * k;
+    const TS* sin = reinterpret_cast<const TS*>(a.state_in) + (unit * DI + cw0 + rw * 16 + j) * (int64_t)N + 4 * k;
 #pragma unroll
     for (int gg = 0; gg < NG; ++gg) hq[gg] = SQ::load(sin + 16 * gg);
   }
 
   // ---- tree prologue (all waves): parent[], C and B rows ----
   if (tid < kTtMaxT) s_parent[tid] = tid < T ? a.parent[(int64_t)b * T + tid] : 0;
+  if (tid <= kWsMaxBlk) s_nff[tid] = 0;
+  if constexpr (CM) {
+    if (tid < kTtMaxT) {
+      s_pparent[tid] = tid < T ? a.parent_prev[(int64_t)b * T + tid] : 0;
+      s_path[tid] = tid < T ? a.path[(int64_t)b * T + tid] : 0;
+    }
+    if (tid == kWsThreads - 1) s_misc[3] = a.path_len[b];
+  }
   const unsigned char* Cg = reinterpret_cast<const unsigned char*>(a.C) + ((unit * T) * G + g) * (int64_t)N * E;
   const unsigned char* Bg = reinterpret_cast<const unsigned char*>(a.B) + ((unit * T) * G + g) * (int64_t)N * E;
   for (int ci = tid; ci < KT * kChunks; ci += kWsThreads) {
@@ -944,6 +975,45 @@ __global__ void __launch_bounds__(kWsThreads) verify_tt_ws_kernel(VerifyArgs a, 
     *reinterpret_cast<u32x4*>(s_B + v * rs + q * 16) = b4;
   }
   __syncthreads();
+  // the commit: the path's B rows, gathered before the path is validated
+  // (a failed commit applies none of them), held until the C rows are dead
+  constexpr int kBPT = CM ? (KT * kChunks + kWsThreads - 1) / kWsThreads : 1;
+  u32x4 rbp[kBPT];
+  if constexpr (CM) {
+    const int len_raw = s_misc[3];
+    const int lg = len_raw < 0 ? 0 : (len_raw > T ? T : len_raw);
+    const unsigned char* Bpg =
+        reinterpret_cast<const unsigned char*>(a.B_prev) + ((unit * T) * G + g) * (int64_t)N * E;
+#pragma unroll
+    for (int it = 0; it < kBPT; ++it) {
+      const int ci = tid + it * kWsThreads, q = ci / kChunks, ch = ci % kChunks;
+      rbp[it] = u32x4{0u, 0u, 0u, 0u};
+      if (q < lg) {
+        const int v = s_path[q];
+        const int vs = (v >= 0 && v < T) ? v : 0;
+        rbp[it] = *reinterpret_cast<const u32x4*>(Bpg + (int64_t)vs * G * N * E + ch * 16);
+      }
+    }
+    if (wave == 1) {
+      // the committed tree and the path, by ballot
+      bool bad_p = false, bad_path = false;
+      if (lane < T) {
+        const int p = s_pparent[lane];
+        bad_p = lane == 0 ? p != -1 : (p < -1 || p >= lane || p < s_pparent[lane - 1]);
+      }
+      if (lane < lg) {
+        const int v = s_path[lane];
+        bad_path = v < 0 || v >= T || s_pparent[v] != (lane == 0 ? -1 : s_path[lane - 1]);
+      }
+      const bool prev_ok = __ballot(bad_p) == 0;
+      const bool path_ok = len_raw >= 0 && len_raw <= T && __ballot(bad_path) == 0;
+      const int st = !prev_ok ? SSM_TREE_E_TREE : (!path_ok ? SSM_TREE_E_PATH : SSM_TREE_OK);
+      if (lane == 0) {
+        s_misc[1] = st == SSM_TREE_OK ? len_raw : 0;  // 0: state and window pass through unchanged
+        if (blockIdx.x == 0 && l == 0 && a.commit_status) a.commit_status[b] = st;
+      }
+    }
+  }
   if (wave == 0) {
     // validation by ballot, root-path sets and conv tap rows, as in
     // verify_tt_kernel
@@ -977,7 +1047,7 @@ __global__ void __launch_bounds__(kWsThreads) verify_tt_ws_kernel(VerifyArgs a, 
     s_cidx[lane] = packed;
     if (lane == 0) {
       s_misc[0] = ok ? 1 : 0;
-      if (blockIdx.x == 0 && l == 0 && a.seq_status) a.seq_status[b] = ok ? SSM_TREE_OK : SSM_TREE_E_TREE;
+      if (blockIdx.x == 0 && l == 0 && a.verify_status) a.verify_status[b] = ok ? SSM_TREE_OK : SSM_TREE_E_TREE;
     }
   }
   // C_v . B_u over the lower-triangular tile pairs (eight waves)
@@ -1015,7 +1085,7 @@ __global__ void __launch_bounds__(kWsThreads) verify_tt_ws_kernel(VerifyArgs a, 
   const bool tree_ok = s_misc[0] != 0;
 
   const TIn* xg = reinterpret_cast<const TIn*>(a.x) + unit * T * (int64_t)DI;
-  const TIn* wg = reinterpret_cast<const TIn*>(a.window) + unit * (W - 1) * (int64_t)CH;
+  const TIn* wg = reinterpret_cast<const TIn*>(a.window_in) + unit * (W - 1) * (int64_t)CH;
   const TIn* dtg = reinterpret_cast<const TIn*>(a.dt_raw) + unit * T * (int64_t)H;
   // each block's head: dt, S (fp64) and exp(S), wave = block, lane = node
   for (int bw = wave; bw < NBLK; bw += kWsWaves) {
@@ -1030,16 +1100,85 @@ __global__ void __launch_bounds__(kWsThreads) verify_tt_ws_kernel(VerifyArgs a, 
     s_S2[bw * kTtMaxT + v] = s2;
     s_Ah[bw * kTtMaxT + v] = __builtin_amdgcn_exp2f((float)s2);
     if (v == 0) s_D[bw] = a.prm.D[(int64_t)l * H + h];
+    if constexpr (CM) {
+      // the accepted path in closed form (lane = path position q):
+      //   h_new = exp(P_last) h + sum_q exp(P_last - P_q) dt_q x~_q B_q,
+      // P_q = sum of dt * A over positions 0..q, in fp64 (zero steps past
+      // the path's length leave P_last in lane 63)
+      const int len = s_misc[1];
+      float dtq = 0.0f;
+      if (v < len)
+        dtq = softplus_hw(load_in(reinterpret_cast<const TIn*>(a.dt_prev) + unit * T * (int64_t)H,
+                                  (int64_t)s_path[v] * H + h) +
+                          a.prm.dt_bias[(int64_t)l * H + h]);
+      double pq = (double)(dtq * a.prm.A[(int64_t)l * H + h]);
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) {
+        const double o = __shfl_up(pq, off);
+        if (v >= off) pq += o;
+      }
+      const double plast = __shfl(pq, kWave - 1);
+      s_wt[bw * kTtMaxT + v] =
+          v < len ? __builtin_amdgcn_exp2f((float)((plast - pq) * 1.4426950408889634)) * dtq : 0.0f;
+      if (v == 0) s_at[bw] = __builtin_amdgcn_exp2f((float)(plast * 1.4426950408889634));
+    }
   }
 
   // ---- producers' per-block inputs, a block ahead in registers ----
   constexpr int kXQ = (KT * (kTtRows / 4) + kTtThreads - 1) / kTtThreads;  // (256 producer threads)
+  // the commit: the old window rows and the path's x rows, rows 0..2 and
+  // 3.. of the block's path buffer (the window right-aligned: element e of
+  // (old window, path rows) sits at row 4 - W + e)
+  constexpr int kPQ = CM ? ((3 + KT) * (kTtRows / 4) + kTtThreads - 1) / kTtThreads : 1;
   RawQ pxr[kXQ];
+  RawQ ppr[kPQ];
   uint32_t pwin[3] = {0u, 0u, 0u};
   float pcw[4] = {0.f, 0.f, 0.f, 0.f}, pcb = 0.f;
+  const int clen = CM ? s_misc[1] : 0;  // path length applied (0 when nothing is committed)
+  const TIn* xpg = CM ? reinterpret_cast<const TIn*>(a.x_prev) + unit * T * (int64_t)DI : nullptr;
+  // Every prefetch load is unconditional, from a clamped address where its
+  // value is not needed (selected away at delivery): a load under a branch
+  // makes the compiler wait for it where the branches join, which turned
+  // the one-phase lead into a wait inside the same phase.  Unused lanes of
+  // a load all read one address.
+  const int pch = opaque_tid() & (kTtRows - 1);  // the channel of the per-channel rows (all four waves)
+  // The sources of a thread's path and window rows are the same for every
+  // block but for the block's channel offset: resolved once here (through
+  // the path in LDS), so that a prefetch issues its loads without waiting on
+  // LDS reads.  Each points at the row's element for channel offset 0 of
+  // block 0 (plus the thread's channel within the block).
+  const TIn* psrc[kPQ];
+  const TIn* wsrc[3];
+  {
+    const int ptid = opaque_tid();
+#pragma unroll
+    for (int it = 0; it < kPQ; ++it) {
+      psrc[it] = xg + cw0;  // (unused rows)
+      if constexpr (CM) {
+        const int qi = ptid + it * kTtThreads;
+        const int rr = qi / (kTtRows / 4), c4 = (qi % (kTtRows / 4)) * 4;
+        if (rr >= 3 && rr < 3 + clen) psrc[it] = xpg + (int64_t)s_path[rr - 3] * DI + cw0 + c4;
+        if (rr < 3 && rr >= 4 - W) psrc[it] = wg + (int64_t)(rr - (4 - W)) * CH + cw0 + c4;
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 3; ++r) {
+      const int c = cw0 + pch;
+      wsrc[r] = xg + c;  // (unused taps)
+      if (r < W - 1) {
+        wsrc[r] = wg + (int64_t)r * CH + c;
+        if constexpr (CM) {  // the committed window: element clen + r of (old window, path rows)
+          const int e = clen + r;
+          wsrc[r] = e < W - 1 ? wg + (int64_t)e * CH + c : xpg + (int64_t)s_path[e - (W - 1)] * DI + c;
+        }
+      }
+    }
+  }
+  const float* cwb = a.prm.conv_w + ((int64_t)l * CH + cw0 + pch) * W;
+  const float* cbb = a.prm.conv_b ? a.prm.conv_b + (int64_t)l * CH + cw0 + pch : cwb;
   auto prefetch = [&](int blk) {
     const int ptid = opaque_tid();  // < 256
-    const int c0 = cw0 + blk * kTtRows;
+    const int c0 = cw0 + blk * kTtRows, boff = blk * kTtRows;
 #pragma unroll
     for (int it = 0; it < kXQ; ++it) {
       const int qi = ptid + it * kTtThreads;
@@ -1047,17 +1186,21 @@ __global__ void __launch_bounds__(kWsThreads) verify_tt_ws_kernel(VerifyArgs a, 
       const int vr = v < T ? v : T - 1;  // rows past T repeat row T - 1 (never a tap source)
       pxr[it] = *reinterpret_cast<const RawQ*>(xg + (int64_t)vr * DI + c0 + c4);
     }
-    if (ptid < kTtRows) {
-      const int c = c0 + ptid;
+    if constexpr (CM) {
 #pragma unroll
-      for (int r = 0; r < 3; ++r)
-        if (r < W - 1) pwin[r] = raw_bits<TIn>(wg + (int64_t)r * CH + c);
-      const float* cwp = a.prm.conv_w + ((int64_t)l * CH + c) * W;
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-        if (t < W) pcw[t] = cwp[W - 1 - t];
-      if (a.prm.conv_b) pcb = a.prm.conv_b[(int64_t)l * CH + c];
+      for (int it = 0; it < kPQ; ++it) ppr[it] = *reinterpret_cast<const RawQ*>(psrc[it] + boff);
     }
+#pragma unroll
+    for (int r = 0; r < 3; ++r) {
+      // bf16: the aligned dword holding the element (the rows start at even
+      // elements), its half picked at delivery
+      const TIn* src = wsrc[r] + boff;
+      pwin[r] = E == 2 ? *reinterpret_cast<const uint32_t*>(src - (pch & 1)) : raw_bits<TIn>(src);
+    }
+    const float* cwp = cwb + (int64_t)boff * W;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) pcw[t] = cwp[t < W ? W - 1 - t : 0];
+    pcb = (a.prm.conv_b ? cbb + boff : cwp)[0];
   };
   auto deliver = [&](int blk) {
     const int ptid = opaque_tid();
@@ -1070,7 +1213,20 @@ __global__ void __launch_bounds__(kWsThreads) verify_tt_ws_kernel(VerifyArgs a, 
       const int v = qi / (kTtRows / 4), c4 = (qi % (kTtRows / 4)) * 4;
       if (qi < KT * (kTtRows / 4)) *reinterpret_cast<RawQ*>(xr + v * kTtRows + c4) = pxr[it];
     }
+    if constexpr (CM) {
+      TIn* pr = s_pr(par);
+#pragma unroll
+      for (int it = 0; it < kPQ; ++it) {
+        const int qi = ptid + it * kTtThreads;
+        const int rr = qi / (kTtRows / 4), c4 = (qi % (kTtRows / 4)) * 4;
+        if ((rr >= 3 && rr < 3 + clen) || (rr < 3 && rr >= 4 - W))
+          *reinterpret_cast<RawQ*>(pr + rr * kTtRows + c4) = ppr[it];
+      }
+    }
     if (ptid < kTtRows) {
+#pragma unroll
+      for (int r = 0; r < 3; ++r)
+        if (E == 2) pwin[r] = (pwin[r] >> (16 * (ptid & 1))) & 0xFFFFu;
 #pragma unroll
       for (int r = 0; r < 3; ++r)
         if (r < W - 1) xw[(4 - W + r) * kTtRows + ptid] = from_bits<TIn>(pwin[r]);
@@ -1078,8 +1234,14 @@ __global__ void __launch_bounds__(kWsThreads) verify_tt_ws_kernel(VerifyArgs a, 
       for (int r = 0; r < 3; ++r)
         if (r < 4 - W) xw[r * kTtRows + ptid] = from_bits<TIn>(0u);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) s_cw(par)[t * kTtRows + ptid] = pcw[t];
-      s_cb(par)[ptid] = pcb;
+      for (int t = 0; t < 4; ++t) s_cw(par)[t * kTtRows + ptid] = t < W ? pcw[t] : 0.0f;
+      s_cb(par)[ptid] = a.prm.conv_b ? pcb : 0.0f;
+      if constexpr (CM) {  // the committed window leaves with its block
+        TIn* wo = reinterpret_cast<TIn*>(a.window_out) + unit * (W - 1) * (int64_t)CH + cw0 + blk * kTtRows + ptid;
+#pragma unroll
+        for (int r = 0; r < 3; ++r)
+          if (r < W - 1) wo[(int64_t)r * CH] = from_bits<TIn>(pwin[r]);
+      }
     }
   };
   if (producer) {
@@ -1111,13 +1273,37 @@ __global__ void __launch_bounds__(kWsThreads) verify_tt_ws_kernel(VerifyArgs a, 
 #pragma unroll
   for (int ti = 0; ti < TT; ++ti) accp[ti] = f32x4{0.f, 0.f, 0.f, 0.f};
   __syncthreads();
+  if constexpr (CM) {
+    // the C rows are dead: the path's B rows take their place, as
+    // [position q][column j][group gg] (NG bf16 per (q, j)), so that the
+    // lane that brings B_q[16 gg + j] for every gg reads them at once
+    uint16_t* s_bt = reinterpret_cast<uint16_t*>(s_C);
+#pragma unroll
+    for (int it = 0; it < kBPT; ++it) {
+      const int ci = tid + it * kWsThreads, q = ci / kChunks, ch = ci % kChunks;
+      if (q < KT) {  // chunk ch holds columns 8 ch .. 8 ch + 7
+        const u32x4 w = rbp[it];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t word = e < 2 ? w.x : (e < 4 ? w.y : (e < 6 ? w.z : w.w));
+          s_bt[(q * 16 + (ch & 1) * 8 + e) * NG + (ch >> 1)] = (uint16_t)(word >> (16 * (e & 1)));
+        }
+      }
+    }
+    __syncthreads();
+  }
 
   // whether block ph - 1's conv outputs (set by the producers in phase ph - 1,
   // read by the consumers in phase ph) hold a non-finite value
   bool xt_nonfinite = false;
-  for (int ph = 0; ph <= NBLK; ++ph) {
-    uint32_t nf_any = 0;  // (as in verify_tt_kernel)
-    if (producer) {
+  // Each role runs its own loop of NBLK + 1 phases, one barrier each (the
+  // role is uniform per wave): in one shared loop the registers the
+  // consumers load for the next block had to survive the producers' branch
+  // as well, the allocator gave the loads other registers, and the copy at
+  // the end of every phase waited for them.
+  if (producer) {
+    for (int ph = 0; ph <= NBLK; ++ph) {
+      uint32_t nf_any = 0;  // (as in verify_tt_kernel)
       if (ph < NBLK) {
         const int par = ph & 1;
         // ---- conv of block ph (lane = channel, wave = node quads) ----
@@ -1190,7 +1376,11 @@ __global__ void __launch_bounds__(kWsThreads) verify_tt_ws_kernel(VerifyArgs a, 
       }
       if (ph + 1 < NBLK) deliver(ph + 1);
       if (ph + 2 < NBLK) prefetch(ph + 2);
-    } else {
+      if (nf_any) s_nff[ph] = 1;  // (a plain flag: the reduction of __syncthreads_or
+      __syncthreads();             // put its temporaries on registers with loads in flight)
+    }
+  } else {
+    for (int ph = 0; ph <= NBLK; ++ph) {
       // ---- C . h0 of block ph first (its state arrived a phase ago) ----
       f32x4 acc[TT];
 #pragma unroll
@@ -1198,9 +1388,69 @@ __global__ void __launch_bounds__(kWsThreads) verify_tt_ws_kernel(VerifyArgs a, 
       if (ph < NBLK) {
         const int ln = opaque_tid() & (kWave - 1), jj = ln & 15, kk = ln >> 4;
         const int c0 = cw0 + ph * kTtRows;
-        const bool more = ph + 1 < NBLK;
+        // the next block's state, loaded unconditionally (the last block
+        // reloads its own: a conditional load would leave the old value
+        // live beside the new one and cost a copy that waits for the load)
+        const int nb = ph + 1 < NBLK ? kTtRows : 0;
         const TS* nsin =
-            reinterpret_cast<const TS*>(a.state) + (unit * DI + c0 + kTtRows + rw * 16 + jj) * (int64_t)N + 4 * kk;
+            reinterpret_cast<const TS*>(a.state_in) + (unit * DI + c0 + nb + rw * 16 + jj) * (int64_t)N + 4 * kk;
+        if constexpr (CM) {
+          // ---- the commit of block ph's channels, then the state leaves ----
+          // h_new^T = exp(P_last) h^T + Bp^T W on the matrix cores, four path
+          // positions per product: lane j + 16 k brings B_q[16 gg + j] and
+          // W[q][channel j] for q = s4 + k, and its state quads are the
+          // accumulator rows (columns 16 gg + 4 k .. + 3 of channel j)
+          const int ch = rw * 16 + jj;
+          if (clen > 0) {
+            const int par = ph & 1;
+            const TIn* pr = s_pr(par);
+            const float at = s_at[ph];
+            float cwv[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) cwv[t] = s_cw(par)[t * kTtRows + ch];
+            const float cbv = s_cb(par)[ch];
+            f32x4 hc[NG];
+#pragma unroll
+            for (int gg = 0; gg < NG; ++gg) hc[gg] = SQ::to_f32(hq[gg]) * at;
+            const unsigned char* bt = s_C + jj * 2 * NG;  // this lane's column of the path's B rows
+#pragma unroll 2
+            for (int s4 = 0; s4 < clen; s4 += 4) {
+              const int q = s4 + kk;  // positions past the path read stale rows, selected away
+              uint32_t bw[(NG + 1) / 2];  // B_q[16 gg + j] for every gg (zero past the path)
+              const unsigned char* bq = bt + q * 32 * NG;
+              if constexpr (NG == 8) {
+                const u32x4 v = *reinterpret_cast<const u32x4*>(bq);
+                bw[0] = v.x; bw[1] = v.y; bw[2] = v.z; bw[3] = v.w;
+              } else if constexpr (NG == 4) {
+                const u32x2 v = *reinterpret_cast<const u32x2*>(bq);
+                bw[0] = v.x; bw[1] = v.y;
+              } else if constexpr (NG == 2) {
+                bw[0] = *reinterpret_cast<const uint32_t*>(bq);
+              } else {
+                bw[0] = *reinterpret_cast<const uint16_t*>(bq);
+              }
+              float z = fmaf(cwv[0], load_in(pr, (3 + q) * kTtRows + ch), cbv);
+#pragma unroll
+              for (int t = 1; t < 4; ++t)
+                if (t < W) z = fmaf(cwv[t], load_in(pr, (3 + q - t) * kTtRows + ch), z);
+              const float xt = d.silu ? silu_fast(z) : z;
+              const float wv = q < clen ? s_wt[ph * kTtMaxT + q] * xt : 0.0f;
+#pragma unroll
+              for (int gg = 0; gg < NG; ++gg) {
+                const uint32_t w2 = bw[gg >> 1];
+                const float bv = __uint_as_float((gg & 1) ? (w2 & 0xFFFF0000u) : (w2 << 16));
+                hc[gg] = mfma4(bv, wv, hc[gg]);
+              }
+            }
+            // the committed state as stored (a bfloat16 state is rounded):
+            // the next tree is verified from exactly what was written
+#pragma unroll
+            for (int gg = 0; gg < NG; ++gg) hq[gg] = SQ::from_f32(hc[gg]);
+          }
+          TS* so = reinterpret_cast<TS*>(a.state_out) + (unit * DI + c0 + ch) * (int64_t)N + 4 * kk;
+#pragma unroll
+          for (int gg = 0; gg < NG; ++gg) SQ::store(so + 16 * gg, hq[gg]);
+        }
         if constexpr (E == 2) {
 #pragma unroll
           for (int m = 0; m < (NG + 1) / 2; ++m) {
@@ -1229,10 +1479,8 @@ __global__ void __launch_bounds__(kWsThreads) verify_tt_ws_kernel(VerifyArgs a, 
               }
               acc[ti] = mfma32(ca, h0, acc[ti]);
             }
-            if (more) {
-              hq[2 * m] = SQ::load(nsin + 32 * m);
-              if (two) hq[2 * m + 1] = SQ::load(nsin + 32 * m + 16);
-            }
+            hq[2 * m] = SQ::load(nsin + 32 * m);
+            if (two) hq[2 * m + 1] = SQ::load(nsin + 32 * m + 16);
             asm volatile("" ::: "memory");
           }
         } else {
@@ -1248,7 +1496,7 @@ __global__ void __launch_bounds__(kWsThreads) verify_tt_ws_kernel(VerifyArgs a, 
               acc[ti] = mfma4(cq.z, h.z, acc[ti]);
               acc[ti] = mfma4(cq.w, h.w, acc[ti]);
             }
-            if (more) hq[gg] = SQ::load(nsin + 16 * gg);
+            hq[gg] = SQ::load(nsin + 16 * gg);
             asm volatile("" ::: "memory");
           }
         }
@@ -1297,21 +1545,40 @@ __global__ void __launch_bounds__(kWsThreads) verify_tt_ws_kernel(VerifyArgs a, 
       }
 #pragma unroll
       for (int ti = 0; ti < TT; ++ti) accp[ti] = acc[ti];
+      __syncthreads();
+      xt_nonfinite = s_nff[ph] != 0;  // block ph's conv outputs, whose path terms come next
     }
-    xt_nonfinite = __syncthreads_or(nf_any != 0) != 0;
   }
 }
 
 namespace {
 
-template <typename TIn, typename TS, int NG, int TT>
-int launch_ws_t(const VerifyArgs& a, int nblk, hipStream_t s) {
-  const size_t lds = (size_t)TtWsLds(16 * NG, (int)sizeof(TIn), TT).total;
+template <typename TIn, typename TS, int NG, int TT, bool CM = false>
+int launch_ws_t(const CommitVerifyArgs& a, int nblk, hipStream_t s) {
+  const size_t lds = (size_t)TtWsLds(16 * NG, (int)sizeof(TIn), TT, CM).total;
   if (lds > 160 * 1024) return SSM_TREE_E_DIMS;
-  if (allow_lds(verify_tt_ws_kernel<TIn, TS, NG, TT>, lds) != hipSuccess) return SSM_TREE_E_HIP;
+  if (allow_lds(verify_tt_ws_kernel<TIn, TS, NG, TT, CM>, lds) != hipSuccess) return SSM_TREE_E_HIP;
   dim3 grid(a.d.d_in / (nblk * kTtRows), a.d.Bsz, a.d.L);
-  hipLaunchKernelGGL((verify_tt_ws_kernel<TIn, TS, NG, TT>), grid, dim3(kWsThreads), lds, s, a, nblk);
+  hipLaunchKernelGGL((verify_tt_ws_kernel<TIn, TS, NG, TT, CM>), grid, dim3(kWsThreads), lds, s, a, nblk);
   return hipGetLastError() == hipSuccess ? SSM_TREE_OK : SSM_TREE_E_HIP;
+}
+
+// a verify's arguments in the round's argument block (nothing committed)
+CommitVerifyArgs ws_args(const VerifyArgs& v) {
+  CommitVerifyArgs a{};
+  a.d = v.d;
+  a.prm = v.prm;
+  a.parent = v.parent;
+  a.x = v.x;
+  a.B = v.B;
+  a.C = v.C;
+  a.dt_raw = v.dt_raw;
+  a.z = v.z;
+  a.window_in = v.window;
+  a.state_in = v.state;
+  a.y = v.y;
+  a.verify_status = v.seq_status;
+  return a;
 }
 
 template <typename TIn, typename TS, int NG, int TT, bool OPT = false>
@@ -1334,7 +1601,7 @@ int launch_tt_pick(const VerifyArgs& a, hipStream_t s) {
     if (a.d.xbc || a.z) return launch_tt_t<TIn, TS, NG, TT, true>(a, s);
   const int blocks = a.d.d_in / a.d.G / kTtRows;
   if (a.d.P % kTtRows == 0 && blocks % 8 == 0) {
-    const int st = launch_ws_t<TIn, TS, NG, TT>(a, blocks % kWsMaxBlk == 0 ? kWsMaxBlk : 8, s);
+    const int st = launch_ws_t<TIn, TS, NG, TT>(ws_args(a), blocks % kWsMaxBlk == 0 ? kWsMaxBlk : 8, s);
     if (st != SSM_TREE_E_DIMS) return st;  // E_DIMS: its LDS does not fit, nothing launched
   }
   return launch_tt_t<TIn, TS, NG, TT>(a, s);
@@ -1360,7 +1627,43 @@ int launch_tt_in(const VerifyArgs& a, hipStream_t s) {
   }
 }
 
+// the round (commit of the accepted path, then verify of the next tree) in
+// the role-split kernel
+template <typename TS, int NG>
+int launch_tt_round_g(const CommitVerifyArgs& a, hipStream_t s) {
+  const int blocks = a.d.d_in / a.d.G / kTtRows;
+  const int nblk = blocks % kWsMaxBlk == 0 ? kWsMaxBlk : 8;
+  const int T = a.d.T;
+  if (T <= 32) return launch_ws_t<bf16_t, TS, NG, 2, true>(a, nblk, s);
+  if (T <= 48) return launch_ws_t<bf16_t, TS, NG, 3, true>(a, nblk, s);
+  return launch_ws_t<bf16_t, TS, NG, 4, true>(a, nblk, s);
+}
+
+template <typename TS>
+int launch_tt_round_in(const CommitVerifyArgs& a, hipStream_t s) {
+  switch (a.d.N) {
+    case 16: return launch_tt_round_g<TS, 1>(a, s);
+    case 32: return launch_tt_round_g<TS, 2>(a, s);
+    case 64: return launch_tt_round_g<TS, 4>(a, s);
+    case 128: return launch_tt_round_g<TS, 8>(a, s);
+    default: return SSM_TREE_E_DIMS;
+  }
+}
+
 }  // namespace
+
+// whether the round of trees of 17..64 nodes runs as one launch: bf16
+// inputs, d_state <= 128, every 64-channel block inside one head, B/C
+// groups of a multiple of 8 blocks, none of the options (their rounds run
+// as commit then verify)
+bool tt_round_applies(const Dims& d, bool bf16, bool gate) {
+  return bf16 && d.T > 16 && d.T <= kTtMaxT && !d.fifo && !d.xbc && !gate && d.N <= 128 && d.P % kTtRows == 0 &&
+         (d.d_in / d.G) % (8 * kTtRows) == 0;
+}
+
+int launch_tt_round(const CommitVerifyArgs& a, hipStream_t s) {
+  return a.d.sbf16 ? launch_tt_round_in<bf16_t>(a, s) : launch_tt_round_in<float>(a, s);
+}
 
 // trees of 17..64 nodes, heads a multiple of 16 channels, 64-channel blocks
 bool tt_verify_applies(const Dims& d) {

@@ -3,8 +3,11 @@ path followed by the verification of the next tree from the committed state
 and window (one decode step of the speculative loop, SpecMamba page
 sec. 3.1-3.2), against the float64 oracle's commit followed by its verify.
 
-Trees of 1..16 nodes with headdim % 16 == 0 take the fused kernel; other
-shapes and the FIFO flag take the two calls in turn.  Both are covered.
+Trees of 1..16 nodes with headdim % 16 == 0 take the fused kernel; trees
+of 17..64 nodes with bf16 inputs, d_state <= 128, heads a multiple of 64
+channels and B/C groups of a multiple of 512 channels take the one-launch
+round of the 17-64-node verify; other shapes, the options on 17-64 nodes
+and the FIFO flag take the two calls in turn.  All are covered.
 Tolerance as elsewhere: |gpu - oracle| <= 1e-5 + 1e-4 |oracle| for y and
 the committed state; statuses and windows exactly.
 """
@@ -37,6 +40,16 @@ def _gpu():
 
 def fused_applies(cfg):
     return 1 <= cfg.T <= 16 and cfg.P % 16 == 0
+
+
+def tt_round_applies(cfg, gate=False):
+    """The one-launch round of trees of 17..64 nodes."""
+    return (cfg.bf16 and 16 < cfg.T <= 64 and cfg.N <= 128 and cfg.P % 64 == 0 and (cfg.H * cfg.P // cfg.G) % 512 == 0
+            and not cfg.xbc and not gate)
+
+
+def route(cfg):
+    return "fused" if fused_applies(cfg) else ("one launch, 17-64 nodes" if tt_round_applies(cfg) else "two calls")
 
 
 class Step:
@@ -140,13 +153,14 @@ def check(step, out, units, state_in=None, window_in=None):
 
 
 # ----------------------------------------------------------------------------
-# the five workloads at full size (the 64-node stress trees take the two calls)
+# the five workloads at full size (the 64-node stress trees take the one-launch
+# round of the 17-64-node verify)
 # ----------------------------------------------------------------------------
 
 @pytest.mark.parametrize("cid,k", [(0, 1), (1, 4), (2, 4), (3, 6), (4, 3)])
 def test_commit_verify_full_size(cid, k):
     cfg = C.CONFIGS[cid]
-    log("commit_verify config %d %s (%s)" % (cid, cfg.name, "fused" if fused_applies(cfg) else "two calls"))
+    log("commit_verify config %d %s (%s)" % (cid, cfg.name, route(cfg)))
     step = Step(cfg)
     out = step.run()
     assert not torch.isnan(out[2]).any(), "NaN in y"
@@ -162,7 +176,7 @@ def test_commit_verify_full_size(cid, k):
 def test_commit_verify_small_random(spec):
     L, Bsz, T, H, P, N, G, W, bf16, silu, bias, tree = spec
     cfg = C.Config(110 + SMALL.index(spec), "small", L, Bsz, T, H, P, N, G, W, bf16, 0.5, tree, silu, bias)
-    log("commit_verify small %s (%s)" % (spec, "fused" if fused_applies(cfg) else "two calls"))
+    log("commit_verify small %s (%s)" % (spec, route(cfg)))
     step = Step(cfg)
     check(step, step.run(), [(l, b) for l in range(L) for b in range(Bsz)])
 
@@ -175,10 +189,12 @@ def _edge_cfg(**kw):
     return C.Config(130, "edge", 2, 6, 12, 4, 64, 128, 1, 4, True, 0.5, "forest").replace(**kw)
 
 
-@pytest.mark.parametrize("kw", [dict(), dict(T=24), dict(P=40, H=8)], ids=["fused", "T24", "P40"])
+@pytest.mark.parametrize("kw", [dict(), dict(T=24), dict(T=24, H=8), dict(P=40, H=8)],
+                         ids=["fused", "T24", "T24-one-launch", "P40"])
 @pytest.mark.parametrize("inplace", [False, True])
 def test_failed_commits_pass_state_through(kw, inplace):
     cfg = _edge_cfg(**kw)
+    log("failed commits %s (%s)" % (kw, route(cfg)))
     prev = C.make_inputs(cfg)
     prev.parent[1, 3] = 5                      # previous tree invalid (forward reference)
     prev.path_len[2] = cfg.T + 1               # path too long
@@ -197,8 +213,9 @@ def test_failed_commits_pass_state_through(kw, inplace):
           window_in=step.gp.window)
 
 
-def test_inplace_equals_out_of_place():
-    cfg = _edge_cfg()
+@pytest.mark.parametrize("kw", [dict(), dict(T=40, H=8)], ids=["fused", "one-launch-17-64"])
+def test_inplace_equals_out_of_place(kw):
+    cfg = _edge_cfg(**kw)
     step = Step(cfg)
     ref = step.run()
     s_in, w_in = step.gp.state.clone(), step.gp.window.clone()
@@ -209,9 +226,11 @@ def test_inplace_equals_out_of_place():
                            b.view(torch.int32) if b.dtype == torch.float32 else b)
 
 
-@pytest.mark.parametrize("kw", [dict(), dict(bf16=False, silu=True, conv_bias=True, N=64, W=3)])
+@pytest.mark.parametrize("kw", [dict(), dict(bf16=False, silu=True, conv_bias=True, N=64, W=3), dict(T=33, H=8),
+                                dict(T=64, H=8, N=64, W=2, silu=True, conv_bias=True, tree="chain_or_star")])
 def test_fused_agrees_with_separate_calls(kw):
     cfg = _edge_cfg(**kw)
+    log("one round against commit then verify %s (%s)" % (kw, route(cfg)))
     step = Step(cfg)
     s_f, w_f, y_f, cs_f, vs_f = step.run()
     gp, gn = step.gp, step.gn
@@ -240,12 +259,13 @@ def test_fifo_flag_takes_the_two_calls():
     assert_close(b[2].double().cpu().numpy(), a[2].double().cpu().numpy(), "y fifo vs fused")
 
 
-@pytest.mark.parametrize("T", [16, 20])
-def test_three_tree_loop(T):
+@pytest.mark.parametrize("T,H", [(16, 4), (20, 4), (40, 8)])
+def test_three_tree_loop(T, H):
     """Tree 1 -> (commit 1, verify 2) -> (commit 2, verify 3): the state
-    carried on the GPU in place through two fused steps equals the oracle's
+    carried on the GPU in place through two rounds equals the oracle's
     commit / verify chain."""
-    cfg = _edge_cfg(Bsz=4, T=T)
+    cfg = _edge_cfg(Bsz=4, T=T, H=H)
+    log("three-tree loop T=%d H=%d (%s)" % (T, H, route(cfg)))
     s1 = Step(cfg, next_cid=901)
     st, win = s1.gp.state.clone(), s1.gp.window.clone()
     s1.run(inplace=True, state=st, window=win)
@@ -283,7 +303,7 @@ def test_zero_sizes():
             assert (cs.cpu().numpy() == 0).all() and (vs.cpu().numpy() == 0).all()
 
 
-@pytest.mark.parametrize("kw", [dict(), dict(T=20)], ids=["fused", "two-calls"])
+@pytest.mark.parametrize("kw", [dict(), dict(T=20), dict(T=20, H=8)], ids=["fused", "two-calls", "one-launch-17-64"])
 def test_graph_replay_equals_eager(kw):
     """One round captured in a HIP graph (in place on the state and window)
     and replayed three times, with unrelated eager work and synchronisation
@@ -404,3 +424,50 @@ def test_fused_round_long_paths_every_width(W):
     assert fused_applies(cfg)
     out = step.run()
     check(step, out, [(l, b) for l in range(cfg.L) for b in range(cfg.Bsz)])
+
+
+@pytest.mark.parametrize("W", [1, 2, 3, 4])
+def test_tt_round_long_paths_every_width(W):
+    """The one-launch round of trees of 17-64 nodes along long accepted
+    paths: the previous tree is a 64-chain whose accepted paths run 0, 1, 3,
+    4, 5, 17, 63 and 64 nodes (four path positions per matrix-core product,
+    the last group partly past the path), the next tree a random forest;
+    conv widths 1-4, SiLU and a bias on the even widths, d_state 32 and
+    128, 8 and 16 blocks per workgroup."""
+    cfg = C.Config(270 + W, "tt-long-paths", 2, 8, 64, 8 if W % 2 else 16, 64, 32 if W % 2 else 128, 1, W, True,
+                   0.5, "chain", W % 2 == 0, W % 2 == 0)
+    assert tt_round_applies(cfg)
+    prev = C.make_inputs(cfg)
+    for b, n in enumerate([0, 1, 3, 4, 5, 17, 63, 64]):
+        prev.path[b, :] = -1
+        prev.path[b, :n] = np.arange(n, dtype=np.int32)
+        prev.path_len[b] = n
+    nxt = C.make_inputs(cfg.replace(cid=cfg.cid + 500, tree="forest"), skip=NEXT_ONLY)
+    log("one-launch round, 64-chain paths, W=%d" % W)
+    step = Step(cfg, prev=prev, nxt=nxt)
+    out = step.run()
+    check(step, out, [(l, b) for l in range(cfg.L) for b in range(cfg.Bsz)])
+
+
+# L, Bsz, T, H, P, N, G, W, silu, bias, tree
+TT_ROUND_SPECS = [
+    (1, 3, 17, 8, 64, 16, 1, 4, False, False, "forest"),
+    (1, 3, 32, 8, 64, 32, 1, 3, True, True, "forest"),
+    (2, 2, 33, 16, 64, 64, 2, 2, False, True, "forest"),
+    (1, 3, 48, 8, 128, 128, 1, 1, True, False, "forest"),       # two blocks per head
+    (1, 2, 49, 16, 64, 128, 1, 4, False, False, "chain_or_star"),
+    (1, 3, 64, 8, 64, 64, 1, 4, True, True, "forest"),
+]
+
+
+@pytest.mark.parametrize("spec", TT_ROUND_SPECS, ids=lambda s: "T%dH%dP%dN%dG%dW%d" % s[2:8])
+def test_tt_round_small(spec):
+    """Every tile count (17, 32, 33, 48, 49, 64 nodes), d_state 16-128, one
+    and two B/C groups, all units against the oracle."""
+    L, Bsz, T, H, P, N, G, W, silu, bias, tree = spec
+    cfg = C.Config(280 + TT_ROUND_SPECS.index(spec), "tt-round", L, Bsz, T, H, P, N, G, W, True, 0.5, tree, silu,
+                   bias)
+    assert tt_round_applies(cfg)
+    log("one-launch round %s" % (spec,))
+    step = Step(cfg)
+    check(step, step.run(), [(l, b) for l in range(L) for b in range(Bsz)])

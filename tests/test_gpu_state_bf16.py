@@ -46,6 +46,7 @@ VERIFY_SPECS = [
     (1, 2, 33, 4, 64, 128, 1, 4, False, False, "forest"),      # 17-64 nodes, fp32 inputs
     (1, 3, 20, 8, 16, 16, 1, 4, True, True, "forest"),         # heads of 16 channels
     (1, 2, 48, 8, 64, 128, 1, 4, True, False, "forest"),       # 8 one-head blocks: the role-split kernel
+    (1, 2, 64, 16, 64, 64, 1, 2, True, True, "chain_or_star"),  # 16 blocks; the round in one launch
     # bf16 products over pairs of column groups (up to 16 nodes): d_state
     # 32, 64 (heads of 32 channels) and 256 (a ring of four pieces)
     (1, 3, 12, 4, 64, 32, 1, 4, True, False, "forest"),
@@ -182,7 +183,9 @@ def check_round(case, s_out, w_out, y, cst, vst, units):
 @pytest.mark.parametrize("spec", VERIFY_SPECS, ids=lambda s: "T%dH%dP%dN%dG%d%s" % (s[2], s[3], s[4], s[5], s[6],
                                                                                     "bf" if s[8] else "f32"))
 def test_round_state_bf16(spec):
-    """The fused round (T <= 16) and its two-call form (17-64 nodes)."""
+    """The fused round (T <= 16), the one-launch round of the role-split
+    verify (17-64 nodes, 8 or 16 one-head blocks per B/C group) and the
+    two-call form (other 17-64-node shapes)."""
     cfg = cfg_of(spec, 90 + VERIFY_SPECS.index(spec))
     log("round with a bf16 state %s" % (spec,))
     case = GpuCase(cfg)
