@@ -35,6 +35,12 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
+// word 3 of a raw buffer resource on gfx9: 32-bit data format (untyped
+// accesses, range-checked against the record count, no swizzle)
+constexpr int kBufWord3 = 0x00020000;
+// s_waitcnt vmcnt(0), the other counters left alone (gfx9 encoding)
+constexpr int kWaitVm0 = 0x0F70;
+
 constexpr int kTtRows = 64;   // channels per block
 constexpr int kTtWaves = 4;
 constexpr int kTtThreads = kTtWaves * kWave;
@@ -1087,6 +1093,17 @@ __global__ void __launch_bounds__(kWsThreads) verify_tt_ws_kernel(CommitVerifyAr
   const TIn* xg = reinterpret_cast<const TIn*>(a.x) + unit * T * (int64_t)DI;
   const TIn* wg = reinterpret_cast<const TIn*>(a.window_in) + unit * (W - 1) * (int64_t)CH;
   const TIn* dtg = reinterpret_cast<const TIn*>(a.dt_raw) + unit * T * (int64_t)H;
+  // buffer resources over this unit's y rows and committed window: an offset
+  // past the range drops the store, so that stores of padded nodes or unused
+  // window rows need no branch (a branch around a store changes the count
+  // of outstanding memory operations from phase to phase, and the compiler
+  // then waits for all of them before the next block's state is used)
+  constexpr int kOutOfRange = 0x7FFFFFF0;
+  const __amdgpu_buffer_rsrc_t y_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(a.y + unit * T * (int64_t)DI, (short)0, T * DI * 4, kBufWord3);
+  const __amdgpu_buffer_rsrc_t wo_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      CM && W > 1 ? reinterpret_cast<TIn*>(a.window_out) + unit * (W - 1) * (int64_t)CH : nullptr, (short)0,
+      CM && W > 1 ? (W - 1) * CH * E : 0, kBufWord3);
   // each block's head: dt, S (fp64) and exp(S), wave = block, lane = node
   for (int bw = wave; bw < NBLK; bw += kWsWaves) {
     const int v = lane;
@@ -1130,10 +1147,15 @@ __global__ void __launch_bounds__(kWsThreads) verify_tt_ws_kernel(CommitVerifyAr
   // 3.. of the block's path buffer (the window right-aligned: element e of
   // (old window, path rows) sits at row 4 - W + e)
   constexpr int kPQ = CM ? ((3 + KT) * (kTtRows / 4) + kTtThreads - 1) / kTtThreads : 1;
-  RawQ pxr[kXQ];
-  RawQ ppr[kPQ];
-  uint32_t pwin[3] = {0u, 0u, 0u};
-  float pcw[4] = {0.f, 0.f, 0.f, 0.f}, pcb = 0.f;
+  // one block's prefetched inputs; two sets, so that a block's loads are
+  // issued two phases before its delivery
+  struct PRegs {
+    RawQ x[kXQ];
+    RawQ p[kPQ];
+    uint32_t win[3];
+    float cw[4], cb;
+  };
+  PRegs pra, prb;
   const int clen = CM ? s_misc[1] : 0;  // path length applied (0 when nothing is committed)
   const TIn* xpg = CM ? reinterpret_cast<const TIn*>(a.x_prev) + unit * T * (int64_t)DI : nullptr;
   // Every prefetch load is unconditional, from a clamped address where its
@@ -1176,7 +1198,7 @@ __global__ void __launch_bounds__(kWsThreads) verify_tt_ws_kernel(CommitVerifyAr
   }
   const float* cwb = a.prm.conv_w + ((int64_t)l * CH + cw0 + pch) * W;
   const float* cbb = a.prm.conv_b ? a.prm.conv_b + (int64_t)l * CH + cw0 + pch : cwb;
-  auto prefetch = [&](int blk) {
+  auto prefetch = [&](int blk, PRegs& R) {
     const int ptid = opaque_tid();  // < 256
     const int c0 = cw0 + blk * kTtRows, boff = blk * kTtRows;
 #pragma unroll
@@ -1184,25 +1206,25 @@ __global__ void __launch_bounds__(kWsThreads) verify_tt_ws_kernel(CommitVerifyAr
       const int qi = ptid + it * kTtThreads;
       const int v = qi / (kTtRows / 4), c4 = (qi % (kTtRows / 4)) * 4;
       const int vr = v < T ? v : T - 1;  // rows past T repeat row T - 1 (never a tap source)
-      pxr[it] = *reinterpret_cast<const RawQ*>(xg + (int64_t)vr * DI + c0 + c4);
+      R.x[it] = *reinterpret_cast<const RawQ*>(xg + (int64_t)vr * DI + c0 + c4);
     }
     if constexpr (CM) {
 #pragma unroll
-      for (int it = 0; it < kPQ; ++it) ppr[it] = *reinterpret_cast<const RawQ*>(psrc[it] + boff);
+      for (int it = 0; it < kPQ; ++it) R.p[it] = *reinterpret_cast<const RawQ*>(psrc[it] + boff);
     }
 #pragma unroll
     for (int r = 0; r < 3; ++r) {
       // bf16: the aligned dword holding the element (the rows start at even
       // elements), its half picked at delivery
       const TIn* src = wsrc[r] + boff;
-      pwin[r] = E == 2 ? *reinterpret_cast<const uint32_t*>(src - (pch & 1)) : raw_bits<TIn>(src);
+      R.win[r] = E == 2 ? *reinterpret_cast<const uint32_t*>(src - (pch & 1)) : raw_bits<TIn>(src);
     }
     const float* cwp = cwb + (int64_t)boff * W;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) pcw[t] = cwp[t < W ? W - 1 - t : 0];
-    pcb = (a.prm.conv_b ? cbb + boff : cwp)[0];
+    for (int t = 0; t < 4; ++t) R.cw[t] = cwp[t < W ? W - 1 - t : 0];
+    R.cb = (a.prm.conv_b ? cbb + boff : cwp)[0];
   };
-  auto deliver = [&](int blk) {
+  auto deliver = [&](int blk, PRegs& R) {
     const int ptid = opaque_tid();
     const int par = blk & 1;
     TIn* xw = s_xw(par);
@@ -1211,7 +1233,7 @@ __global__ void __launch_bounds__(kWsThreads) verify_tt_ws_kernel(CommitVerifyAr
     for (int it = 0; it < kXQ; ++it) {
       const int qi = ptid + it * kTtThreads;
       const int v = qi / (kTtRows / 4), c4 = (qi % (kTtRows / 4)) * 4;
-      if (qi < KT * (kTtRows / 4)) *reinterpret_cast<RawQ*>(xr + v * kTtRows + c4) = pxr[it];
+      if (qi < KT * (kTtRows / 4)) *reinterpret_cast<RawQ*>(xr + v * kTtRows + c4) = R.x[it];
     }
     if constexpr (CM) {
       TIn* pr = s_pr(par);
@@ -1220,34 +1242,39 @@ __global__ void __launch_bounds__(kWsThreads) verify_tt_ws_kernel(CommitVerifyAr
         const int qi = ptid + it * kTtThreads;
         const int rr = qi / (kTtRows / 4), c4 = (qi % (kTtRows / 4)) * 4;
         if ((rr >= 3 && rr < 3 + clen) || (rr < 3 && rr >= 4 - W))
-          *reinterpret_cast<RawQ*>(pr + rr * kTtRows + c4) = ppr[it];
+          *reinterpret_cast<RawQ*>(pr + rr * kTtRows + c4) = R.p[it];
       }
     }
     if (ptid < kTtRows) {
+      uint32_t win[3];
+#pragma unroll
+      for (int r = 0; r < 3; ++r) win[r] = E == 2 ? (R.win[r] >> (16 * (ptid & 1))) & 0xFFFFu : R.win[r];
 #pragma unroll
       for (int r = 0; r < 3; ++r)
-        if (E == 2) pwin[r] = (pwin[r] >> (16 * (ptid & 1))) & 0xFFFFu;
-#pragma unroll
-      for (int r = 0; r < 3; ++r)
-        if (r < W - 1) xw[(4 - W + r) * kTtRows + ptid] = from_bits<TIn>(pwin[r]);
+        if (r < W - 1) xw[(4 - W + r) * kTtRows + ptid] = from_bits<TIn>(win[r]);
 #pragma unroll
       for (int r = 0; r < 3; ++r)
         if (r < 4 - W) xw[r * kTtRows + ptid] = from_bits<TIn>(0u);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) s_cw(par)[t * kTtRows + ptid] = t < W ? pcw[t] : 0.0f;
-      s_cb(par)[ptid] = a.prm.conv_b ? pcb : 0.0f;
+      for (int t = 0; t < 4; ++t) s_cw(par)[t * kTtRows + ptid] = t < W ? R.cw[t] : 0.0f;
+      s_cb(par)[ptid] = a.prm.conv_b ? R.cb : 0.0f;
       if constexpr (CM) {  // the committed window leaves with its block
-        TIn* wo = reinterpret_cast<TIn*>(a.window_out) + unit * (W - 1) * (int64_t)CH + cw0 + blk * kTtRows + ptid;
+        // buffer stores: rows past W - 1 and the blocks past the last (the
+        // loop delivers one) fall outside the range and are dropped, so that
+        // every phase issues the same memory operations
+        const uint32_t c = cw0 + blk * kTtRows + ptid;
 #pragma unroll
         for (int r = 0; r < 3; ++r)
-          if (r < W - 1) wo[(int64_t)r * CH] = from_bits<TIn>(pwin[r]);
+          __builtin_amdgcn_raw_buffer_store_b16((uint16_t)win[r], wo_rsrc,
+                                                blk < NBLK ? (int)(((uint32_t)r * CH + c) * 2u) : kOutOfRange, 0, 0);
       }
     }
   };
   if (producer) {
-    prefetch(0);
-    deliver(0);
-    if (NBLK > 1) prefetch(1);
+    prefetch(0, pra);
+    deliver(0, pra);
+    prefetch(1, pra);  // (NBLK >= 8)
+    prefetch(2, prb);
   }
   // consumers with bf16 inputs and d_state <= 128: the C operands of every
   // node tile and column group pair stay in registers for all the
@@ -1302,9 +1329,13 @@ __global__ void __launch_bounds__(kWsThreads) verify_tt_ws_kernel(CommitVerifyAr
   // as well, the allocator gave the loads other registers, and the copy at
   // the end of every phase waited for them.
   if (producer) {
-    for (int ph = 0; ph <= NBLK; ++ph) {
+    // phase ph (< NBLK) delivers block ph + 1 from the set R and refills R
+    // with block ph + 3 (the last block again near the end, and a delivery
+    // past the last block: every phase issues the same memory operations);
+    // the two sets alternate by phase
+    auto pphase = [&](int ph, PRegs& R) {
       uint32_t nf_any = 0;  // (as in verify_tt_kernel)
-      if (ph < NBLK) {
+      {
         const int par = ph & 1;
         // ---- conv of block ph (lane = channel, wave = node quads) ----
         {
@@ -1374,18 +1405,22 @@ __global__ void __launch_bounds__(kWsThreads) verify_tt_ws_kernel(CommitVerifyAr
           }
         }
       }
-      if (ph + 1 < NBLK) deliver(ph + 1);
-      if (ph + 2 < NBLK) prefetch(ph + 2);
+      deliver(ph + 1, R);
+      prefetch(ph + 3 < NBLK ? ph + 3 : NBLK - 1, R);
       if (nf_any) s_nff[ph] = 1;  // (a plain flag: the reduction of __syncthreads_or
       __syncthreads();             // put its temporaries on registers with loads in flight)
+    };
+    for (int ph = 0; ph < NBLK; ph += 2) {  // (NBLK even)
+      pphase(ph, pra);
+      pphase(ph + 1, prb);
     }
+    __syncthreads();  // phase NBLK: the consumers' last path terms
   } else {
-    for (int ph = 0; ph <= NBLK; ++ph) {
-      // ---- C . h0 of block ph first (its state arrived a phase ago) ----
-      f32x4 acc[TT];
+    // ---- the commit and C . h0 of block ph (its state arrived a phase ago) ----
+    auto cstate = [&](int ph, f32x4 (&acc)[TT]) {
 #pragma unroll
       for (int ti = 0; ti < TT; ++ti) acc[ti] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (ph < NBLK) {
+      {
         const int ln = opaque_tid() & (kWave - 1), jj = ln & 15, kk = ln >> 4;
         const int c0 = cw0 + ph * kTtRows;
         // the next block's state, loaded unconditionally (the last block
@@ -1501,9 +1536,11 @@ __global__ void __launch_bounds__(kWsThreads) verify_tt_ws_kernel(CommitVerifyAr
           }
         }
       }
-      // ---- path terms and y of block ph - 1 ----
-      if (ph >= 1) {
-        const int pb = ph - 1, par = pb & 1;
+    };
+    // ---- path terms and y of block pb ----
+    auto cpath = [&](int pb) {
+      {
+        const int par = pb & 1;
         const int ln = opaque_tid() & (kWave - 1), jj = ln & 15, kk = ln >> 4;
         const int c0 = cw0 + pb * kTtRows;
         const int row = rw * 16 + jj;
@@ -1511,6 +1548,7 @@ __global__ void __launch_bounds__(kWsThreads) verify_tt_ws_kernel(CommitVerifyAr
         const float* xt = s_xt(par);
         const float* mm = s_m(par);
         float* yrow = a.y + unit * T * (int64_t)DI + c0 + row;
+        const uint32_t yoff = (uint32_t)(c0 + row) * 4u;  // bytes into the unit's y rows
         // column tile outermost: one x~ quad per tj serves every node tile
         // ti >= tj, and the TT accumulators are independent product chains
         f32x4 y[TT];
@@ -1535,19 +1573,41 @@ __global__ void __launch_bounds__(kWsThreads) verify_tt_ws_kernel(CommitVerifyAr
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int v = 16 * ti + 4 * kk + r;
-            if (v < T) yrow[(int64_t)v * DI] = tree_ok ? y[ti][r] : __builtin_nanf("");
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(tree_ok ? y[ti][r] : __builtin_nanf("")), y_rsrc,
+                                                  v < T ? (int)((uint32_t)v * DI * 4u + yoff) : kOutOfRange, 0, 0);
           }
         if (xt_nonfinite) {  // (rare) y_v not finite where v's root path holds a non-finite x~_u
           const uint64_t nfm = nonfinite_nodes(s_nf(par), row);
           for (int v = 4 * kk; v < T; v = (v & 3) == 3 ? v + 13 : v + 1)  // this lane's nodes 16 ti + 4 k + r
             if (s_anc[v] & nfm) yrow[(int64_t)v * DI] = __builtin_nanf("");
+          // (these stores stay out of the count the next phase's waits assume)
+          __builtin_amdgcn_s_waitcnt(kWaitVm0);
         }
       }
+    };
+    // phase 0: block 0's state part; phases 1 .. NBLK - 1: block ph's state
+    // part and block ph - 1's path terms; phase NBLK: the last path terms
+    // (every loop phase issues the same memory operations)
+    f32x4 acc[TT];
+    cstate(0, acc);
+    // as many (dropped) stores as a phase's path terms issue: the loop's
+    // waits for the state count them
+#pragma unroll
+    for (int i = 0; i < 4 * TT; ++i) __builtin_amdgcn_raw_buffer_store_b32(0u, y_rsrc, kOutOfRange - 64 * i, 0, 0);
+#pragma unroll
+    for (int ti = 0; ti < TT; ++ti) accp[ti] = acc[ti];
+    __syncthreads();
+    xt_nonfinite = s_nff[0] != 0;  // block ph's conv outputs, whose path terms come next
+    for (int ph = 1; ph < NBLK; ++ph) {
+      cstate(ph, acc);
+      cpath(ph - 1);
 #pragma unroll
       for (int ti = 0; ti < TT; ++ti) accp[ti] = acc[ti];
       __syncthreads();
-      xt_nonfinite = s_nff[ph] != 0;  // block ph's conv outputs, whose path terms come next
+      xt_nonfinite = s_nff[ph] != 0;
     }
+    cpath(NBLK - 1);
+    __syncthreads();
   }
 }
 
