@@ -92,6 +92,25 @@ __device__ __forceinline__ void split3(f32x4 p, f32x4 q, u32x4& t0, u32x4& t1, u
   }
 }
 
+// 4 x 4 transpose across the four lanes of a quad (lane index j & 3) and
+// the four elements of q: element t of lane s ends as element s of lane t.
+// Two butterfly stages: swap the off-diagonal 2 x 2 blocks between lanes
+// 2 apart, then the off-diagonal elements of each 2 x 2 block between
+// neighbouring lanes (DPP quad permutations)
+__device__ __forceinline__ float dpp_xor1(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));  // quad_perm [1,0,3,2]
+}
+__device__ __forceinline__ float dpp_xor2(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));  // quad_perm [2,3,0,1]
+}
+__device__ __forceinline__ f32x4 quad_transpose(f32x4 m, int j) {
+  const bool hi = (j & 2) != 0, lo = (j & 1) != 0;
+  const float x0 = dpp_xor2(m.x), x1 = dpp_xor2(m.y), x2 = dpp_xor2(m.z), x3 = dpp_xor2(m.w);
+  const float n0 = hi ? x2 : m.x, n1 = hi ? x3 : m.y, n2 = hi ? m.z : x0, n3 = hi ? m.w : x1;
+  const float y0 = dpp_xor1(n0), y1 = dpp_xor1(n1), y2 = dpp_xor1(n2), y3 = dpp_xor1(n3);
+  return f32x4{lo ? y1 : n0, lo ? n1 : y0, lo ? y3 : n2, lo ? n3 : y2};
+}
+
 template <typename TIn>
 __device__ __forceinline__ f32x4 load4(const TIn* p);
 template <>
@@ -1567,15 +1586,21 @@ __global__ void __launch_bounds__(kWsThreads) verify_tt_ws_kernel(CommitVerifyAr
           }
           asm volatile("" ::: "memory");  // one column tile's operands at a time
         }
-        // lane (c + 16 k) holds nodes 16 ti + 4 k + r of channel row
+        // lane (c + 16 k) holds nodes 16 ti + 4 k + r of channel row: a 4 x 4
+        // transpose within each lane quad (node r <-> channel c % 4) gives
+        // lane (4 m + s + 16 k) channels 4 m .. 4 m + 3 of node 16 ti + 4 k + s,
+        // one 16-byte store per node tile instead of four 4-byte ones
+        const int s = jj & 3;
+        const uint32_t yoff4 = (uint32_t)(c0 + rw * 16 + (jj & ~3)) * 4u;
 #pragma unroll
-        for (int ti = 0; ti < TT; ++ti)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int v = 16 * ti + 4 * kk + r;
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(tree_ok ? y[ti][r] : __builtin_nanf("")), y_rsrc,
-                                                  v < T ? (int)((uint32_t)v * DI * 4u + yoff) : kOutOfRange, 0, 0);
-          }
+        for (int ti = 0; ti < TT; ++ti) {
+          const f32x4 tq = quad_transpose(y[ti], jj);
+          const int v = 16 * ti + 4 * kk + s;
+          const u32x4 bits = tree_ok ? __builtin_bit_cast(u32x4, tq) : u32x4{0x7FC00000u, 0x7FC00000u, 0x7FC00000u,
+                                                                               0x7FC00000u};
+          __builtin_amdgcn_raw_buffer_store_b128(bits, y_rsrc, v < T ? (int)((uint32_t)v * DI * 4u + yoff4) : kOutOfRange,
+                                                 0, 0);
+        }
         if (xt_nonfinite) {  // (rare) y_v not finite where v's root path holds a non-finite x~_u
           const uint64_t nfm = nonfinite_nodes(s_nf(par), row);
           for (int v = 4 * kk; v < T; v = (v & 3) == 3 ? v + 13 : v + 1)  // this lane's nodes 16 ti + 4 k + r
@@ -1593,7 +1618,8 @@ __global__ void __launch_bounds__(kWsThreads) verify_tt_ws_kernel(CommitVerifyAr
     // as many (dropped) stores as a phase's path terms issue: the loop's
     // waits for the state count them
 #pragma unroll
-    for (int i = 0; i < 4 * TT; ++i) __builtin_amdgcn_raw_buffer_store_b32(0u, y_rsrc, kOutOfRange - 64 * i, 0, 0);
+    for (int i = 0; i < TT; ++i)
+      __builtin_amdgcn_raw_buffer_store_b128(u32x4{0u, 0u, 0u, 0u}, y_rsrc, kOutOfRange - 64 * i, 0, 0);
 #pragma unroll
     for (int ti = 0; ti < TT; ++ti) accp[ti] = acc[ti];
     __syncthreads();
