@@ -38,10 +38,17 @@ KERNELS = ("verify", "commit", "commit_verify")
 def verify_source(cfg):
     """The verify kernel a workload's shape dispatches to (plain flags)."""
     if cfg.T <= 16 and cfg.P % 16 == 0:
-        return CSRC + "verify_mfma.hip"
+        return CSRC + "commit_verify.hip"  # the round's kernel with nothing to commit
     if cfg.T <= 64 and cfg.P % 16 == 0 and (cfg.d_in // cfg.G) % 64 == 0:
         return CSRC + "verify_tt.hip"
     return CSRC + "verify.hip"
+
+
+def tt_round(cfg):
+    """Whether a workload's round of 17-64-node trees runs as one launch of
+    the role-split verify (else as commit, then verify)."""
+    return (cfg.bf16 and 16 < cfg.T <= 64 and cfg.N <= 128 and cfg.P % 64 == 0
+            and (cfg.d_in // cfg.G) % 512 == 0)
 
 
 def kernel_sources(kernel, cfg):
@@ -52,9 +59,36 @@ def kernel_sources(kernel, cfg):
         files = [CSRC + "commit.hip"]
     elif cfg.T <= 16 and cfg.P % 16 == 0:
         files = [CSRC + "commit_verify.hip"]
+    elif tt_round(cfg):
+        files = [CSRC + "verify_tt.hip"]
     else:  # the round runs as a commit followed by a verify
         files = [CSRC + "commit.hip", verify_source(cfg)]
     return files + [CSRC + "common.h"]
+
+
+def _last_template_arg(name):
+    head = name.split("(")[0]
+    return head[head.rfind(",") + 1:].strip(" >") if "<" in head else ""
+
+
+def kernel_family(name):
+    """Which call a dispatched kernel belongs to: verify, commit,
+    commit_verify (the round), copy (the plain coalesced copy probe), or
+    None.  The round's kernel with nothing to commit (last template argument
+    true) serves ssm_tree_verify on trees of at most 16 nodes; the
+    role-split verify with the commit (last argument true) is the round of
+    17-64-node trees."""
+    if "probe_kernel<1, 0, 0>" in name:
+        return "copy"
+    if "commit_verify_kernel<" in name:
+        return "verify" if _last_template_arg(name) == "true" else "commit_verify"
+    if "verify_tt_ws_kernel<" in name:
+        return "commit_verify" if _last_template_arg(name) == "true" else "verify"
+    if any(k in name for k in ("verify_mfma_kernel", "verify_tt_kernel", "verify_proj_kernel")):
+        return "verify"
+    if "::commit_kernel" in name:
+        return "commit"
+    return None
 
 
 def algorithmic_bytes(cfg, path_len):
@@ -106,11 +140,6 @@ def load_traffic(kernel, cfg):
 
 
 PROBE_BYTES = 4 << 30  # hbm_probe's buffer: the copy probe reads and writes this many bytes per dispatch
-KERNEL_MATCH = {"verify": ("verify_mfma_kernel", "verify_tt_kernel", "verify_tt_ws_kernel", "verify_proj_kernel"),
-                "commit": ("::commit_kernel",),
-                "commit_verify": ("commit_verify_kernel",),
-                # the coalesced plain copy probe (kind 1, layout 0, plain loads and stores, one tile per workgroup)
-                "copy": ("probe_kernel<1, 0, false>",)}
 
 
 def _pmc_per_dispatch(run_dir, counter):
@@ -127,9 +156,9 @@ def _pmc_per_dispatch(run_dir, counter):
             for row in csv.DictReader(fh):
                 if row["Counter_Name"] != counter:
                     continue
-                for fam, keys in KERNEL_MATCH.items():
-                    if any(k in row["Kernel_Name"] for k in keys):
-                        acc.setdefault(fam, []).append(float(row["Counter_Value"]))
+                fam = kernel_family(row["Kernel_Name"])
+                if fam:
+                    acc.setdefault(fam, []).append(float(row["Counter_Value"]))
     return {fam: sum(v) / len(v) for fam, v in acc.items()}
 
 
@@ -325,6 +354,76 @@ def rotated_rates(torch, m, C, cid, threads, min_bytes=1 << 30, reps=3):
            "verify": rate(vms, ab["verify"]), "round": rate(rms, rb),
            "note": "sets cycled so that no call finds its inputs in the last-level cache; not in the step"}
     del sets, prms
+    torch.cuda.empty_cache()
+    return out
+
+
+def stress_workload(torch, m, C, threads, reps=4):
+    """The batch-64 tree-64 stress workload (64-node trees, 10.7 GB of root
+    state, far past the last-level cache): the one-launch round in place,
+    verify alone, and the same round as the two calls (commit in place, then
+    verify), each timed with HIP events; inputs resident before timing."""
+    from testgen.device import upload
+    cfg = C.CONFIGS[4]
+    inp = C.make_inputs(cfg, nthreads=threads)
+    nx = C.make_inputs(cfg.replace(cid=cfg.cid + 500), nthreads=threads,
+                       skip=("state", "window", "A", "D", "dt_bias", "conv_w", "conv_b"))
+    g, g2 = upload(inp), upload(nx)
+    dims = m.make_dims(cfg.L, cfg.Bsz, cfg.T, cfg.H, cfg.P, cfg.N, cfg.G, cfg.W, cfg.bf16, cfg.silu)
+    prm = m.make_params(g.A, g.D, g.dt_bias, g.conv_w, g.conv_b)
+    y = torch.empty((cfg.L, cfg.Bsz, cfg.T, cfg.d_in), dtype=torch.float32, device="cuda")
+    st_c = torch.empty(cfg.Bsz, dtype=torch.int32, device="cuda")
+    st_v = torch.empty_like(st_c)
+    flip = [0]
+
+    def round_():
+        prev, nxt = (g, g2) if flip[0] % 2 == 0 else (g2, g)
+        flip[0] += 1
+        m.commit_verify(dims, prm, prev.parent, prev.path, prev.path_len, prev.x, prev.B, prev.dt_raw, g.window,
+                        g.state, g.window, g.state, nxt.parent, nxt.x, nxt.B, nxt.C, nxt.dt_raw, y, st_c, st_v)
+
+    def verify():
+        m.verify(dims, prm, g2.parent, g2.x, g2.B, g2.C, g2.dt_raw, g.window, g.state, y, st_v)
+
+    def two_calls():
+        prev, nxt = (g, g2) if flip[0] % 2 == 0 else (g2, g)
+        flip[0] += 1
+        m.commit(dims, prm, prev.parent, prev.path, prev.path_len, prev.x, prev.B, prev.dt_raw, g.window, g.state,
+                 g.window, g.state, st_c)
+        m.verify(dims, prm, nxt.parent, nxt.x, nxt.B, nxt.C, nxt.dt_raw, g.window, g.state, y, st_v)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        out = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            out.append(e0.elapsed_time(e1))
+        return out
+
+    rms, vms, tms = timed(round_), timed(verify), timed(two_calls)
+    if not (st_v.cpu() == 0).all() or not (st_c.cpu() == 0).all() or torch.isnan(y).any():
+        raise SystemExit("bench: bad status or NaN on the stress workload")
+    a1, a2 = algorithmic_bytes(cfg, inp.path_len), algorithmic_bytes(cfg, nx.path_len)
+    rb = (a1["commit_verify"] + a2["commit_verify"]) // 2
+    nl = cfg.L * cfg.Bsz * cfg.T
+
+    def rate(ms, nbytes):
+        a = sum(ms) / len(ms)
+        gbs = nbytes / (a * 1e-3) / 1e9
+        return {"ms": round(a, 4), "ms_min": round(min(ms), 4), "bytes": nbytes,
+                "node_layers_per_s": round(nl / (a * 1e-3), 1), "GBps": round(gbs, 1),
+                "frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+    out = {"workload": cfg.name, "round": dict(rate(rms, rb), kernel="verify_tt_ws_kernel (one launch)"),
+           "verify": dict(rate(vms, a2["verify"]), kernel="verify_tt_ws_kernel"),
+           "two_call_round": dict(rate(tms, rb), kernels="commit_kernel + verify_tt_ws_kernel"),
+           "note": "not in the step"}
+    del g, g2, y
     torch.cuda.empty_cache()
     return out
 
@@ -717,7 +816,7 @@ def main(argv=None):
     fifo_ms = timed(lambda: m.verify(dims_fifo, prm, g.parent, g.x, g.B, g.C, g.dt_raw, window, state, y, st_v),
                     reps=3)
 
-    per_layer = draft = opts = sbf = ceiling = None
+    per_layer = draft = opts = sbf = ceiling = stress = None
     small = {}
     if not args.no_extras:
         # practical ceilings of the same GPU, by the hand-written probes
@@ -726,6 +825,8 @@ def main(argv=None):
                                       (2, 0, 1, 0), (2, 1, 0, 0)])
         for cid in (1, 2):
             small[C.CONFIGS[cid].name] = rotated_rates(torch, m, C, cid, args.threads)
+        if args.config != 4:
+            stress = stress_workload(torch, m, C, args.threads)
         sbf = state_bf16_round(torch, m, cfg, g, g2, state, window, timed, (inp.path_len, inp2.path_len))
         per_layer = per_layer_round(torch, m, cfg, g, g2, state, window, y, st_c, st_v, timed)
         draft = draft_decode(torch, m, C, upload, args.threads, timed)
@@ -759,7 +860,7 @@ def main(argv=None):
     if vsrc == "verify_tt.hip" and cfg.bf16:
         engine, vpeak = "mfma bf16 (state split in 3 bf16 terms)", 2500.0
         xflops = 3 * 2 * cfg.L * cfg.Bsz * (16 * ((cfg.T + 15) // 16)) * cfg.H * cfg.P * cfg.N
-    elif vsrc in ("verify_tt.hip", "verify_mfma.hip"):
+    elif vsrc in ("verify_tt.hip", "commit_verify.hip"):
         engine, vpeak, xflops = "mfma fp32", 157.3, vflops
     else:
         engine, vpeak, xflops = "valu fp32", 78.6, vflops
@@ -777,7 +878,8 @@ def main(argv=None):
             "commit": dict(ms=round(avg(com_ms), 4), ms_min=round(min(com_ms), 4), bytes=ab["commit"],
                            roofline=roof("commit", ab["commit"], avg(com_ms)), note="not in the step"),
             "verify_fifo_walk": dict(ms=round(avg(fifo_ms), 4), bytes=ab["verify"],
-                                     note="SSM_TREE_VERIFY_FIFO, not in the step")}
+                                     note="SSM_TREE_VERIFY_FIFO: the page's FIFO walk kept as a correctness "
+                                          "reference of the walk; no performance claim; not in the step")}
     rec = {
         "metric": METRIC,
         "value": round(node_layers / (ms_per_step * 1e-3), 1),
@@ -804,6 +906,7 @@ def main(argv=None):
         "options_round": opts,
         "state_bf16_round": sbf,
         "small_workloads": small or None,
+        "stress_workload": stress,
         "ceiling": ceiling,
         "param_bytes_per_call": ab["params"],
         "verify_hbm_frac": kern["verify"]["roofline"]["frac"],
