@@ -84,7 +84,7 @@ def kernel_family(name):
         return "verify" if _last_template_arg(name) == "true" else "commit_verify"
     if "verify_tt_ws_kernel<" in name:
         return "commit_verify" if _last_template_arg(name) == "true" else "verify"
-    if any(k in name for k in ("verify_mfma_kernel", "verify_tt_kernel", "verify_proj_kernel")):
+    if any(k in name for k in ("verify_tt_kernel", "verify_proj_kernel")):
         return "verify"
     if "::commit_kernel" in name:
         return "commit"

@@ -18,7 +18,7 @@ LIB = os.path.join(HERE, "libssm_tree.so")
 # HBM ceiling probes for the measurement harness (not part of the ABI)
 PROBE_LIB = os.path.join(HERE, "libssm_tree_probe.so")
 PROBE_SOURCES = ["probe.hip"]
-SOURCES = ["api.hip", "verify.hip", "verify_mfma.hip", "verify_tt.hip", "verify_fifo.hip", "commit.hip", "commit_verify.hip",
+SOURCES = ["api.hip", "verify.hip", "verify_tt.hip", "verify_fifo.hip", "commit.hip", "commit_verify.hip",
            "plan.hip"]
 ARCH = "gfx950"
 

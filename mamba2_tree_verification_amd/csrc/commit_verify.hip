@@ -5,7 +5,7 @@
 // accepted path of the previous tree (SpecMamba page sec. 3.1: recompute
 // from the stored per-token dt, B and x), written once, and the next
 // tree's outputs are formed from the new state while it is still in
-// registers (the root projection of verify_mfma.hip:
+// registers (the root projection of verify.hip:
 //   y_v = a_v (C_v . h) + sum_{u on path(v)} M[v][u] x~_u).
 // Results equal ssm_tree_commit followed by ssm_tree_verify on the
 // committed state and window, up to fp32 rounding.  A sequence whose commit

@@ -26,8 +26,10 @@
 // is the only output.
 //
 // Trees of at most 16 nodes whose heads are a multiple of 16 channels wide
-// take the matrix-core kernel in verify_mfma.hip (same formula, both sums as
-// MFMA contractions); this file's VALU kernel serves every other shape.
+// take the round's kernel in commit_verify.hip with nothing to commit, and
+// trees of 17-64 nodes the matrix-core kernels of verify_tt.hip (same
+// formula, both sums as MFMA contractions); this file's VALU kernel serves
+// every other shape.
 //
 // Mapping.  A workgroup of NW waves owns one (layer, sequence) and NBLK
 // consecutive blocks of NW*R*64 channels (rows of the root state) inside one
@@ -677,13 +679,6 @@ int launch_in(const VerifyArgs& a, hipStream_t s) {
 
 }  // namespace
 
-bool mfma_verify_applies(const Dims& d);
-int launch_verify_mfma(const VerifyArgs& a, bool bf16, hipStream_t s);
-#ifndef SSMT_VERIFY_ONESHOT
-#define SSMT_VERIFY_ONESHOT 1
-#endif
-constexpr bool kVerifyOneshot = SSMT_VERIFY_ONESHOT != 0;
-
 int launch_verify_fifo(const VerifyArgs& a, bool bf16, hipStream_t s);
 
 // SSM_TREE_CONV_XBC and the gate: taken on the fused round's shapes, whose
@@ -698,18 +693,20 @@ int launch_verify_tt(const VerifyArgs& a, bool bf16, hipStream_t s);
 bool verify_options_supported(const Dims& d, bool gate, bool bf16) {
   if (d.sbf16)
     return d.T == 0 || (!d.fifo && !d.xbc && !gate &&
-                        (mfma_verify_applies(d) || (tt_verify_applies(d) && tt_verify_fits(d, bf16, false))));
+                        (commit_verify_fused_applies(d) || (tt_verify_applies(d) && tt_verify_fits(d, bf16, false))));
   // the options: trees of 1-16 nodes on the fused round's kernel, 17-64 on
   // the options' instantiation of verify_tt_kernel
   return (!d.xbc && !gate) ||
          (!d.fifo && (commit_verify_fused_applies(d) || (tt_verify_applies(d) && tt_verify_fits(d, bf16, true))));
 }
 
+// trees of 1-16 nodes: the round's kernel with nothing to commit (one
+// workgroup per 64 channels of a (layer, sequence))
 int launch_verify_oneshot(const VerifyArgs& a, bool bf16, hipStream_t s);
 
 int launch_verify(const VerifyArgs& a, bool bf16, hipStream_t s) {
   if (a.d.fifo) return launch_verify_fifo(a, bf16, s);
-  if (mfma_verify_applies(a.d)) return kVerifyOneshot ? launch_verify_oneshot(a, bf16, s) : launch_verify_mfma(a, bf16, s);
+  if (commit_verify_fused_applies(a.d)) return launch_verify_oneshot(a, bf16, s);
   if (tt_verify_applies(a.d)) {
     const int st = launch_verify_tt(a, bf16, s);
     // E_DIMS: its LDS does not fit this shape, nothing launched (the vector

@@ -20,7 +20,7 @@
 // order, so the results are identical.
 //
 // This is the reference form of the method on the GPU.  The root
-// projection (verify_mfma.hip, verify.hip) computes the same outputs
+// projection (verify.hip, verify_tt.hip, commit_verify.hip) computes the same outputs
 // without materialising child states and is the default.
 #include "common.h"
 

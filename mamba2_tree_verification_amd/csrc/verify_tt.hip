@@ -1,7 +1,7 @@
 // verify_tt.hip - ssm_tree_verify for trees of 17 to 64 nodes, on the gfx950
 // matrix cores.
 //
-// The root projection of verify_mfma.hip (SpecMamba page sec. 3.2
+// The root projection of verify.hip (SpecMamba page sec. 3.2
 // recurrence, unrolled along each root path):
 //   y_v[c] = a_v (C_v . h0[c]) + sum_{u on path(v)} M_h[v][u] x~_u[c],
 //   M_h[v][u] = exp(S_v - S_u) dt_u (C_v . B_u), plus D_h when u = v,
