@@ -209,10 +209,15 @@ int ssm_tree_commit(const ssm_tree_dims* dims, const ssm_tree_params* params, co
  *             is verified from them.
  * verify_status [Bsz] or NULL: as ssm_tree_verify's seq_status (next tree).
  * Outputs equal ssm_tree_commit followed by ssm_tree_verify up to fp32
- * rounding.  Trees of 1 to 16 nodes with a headdim that is a multiple of 16
- * take the fused kernel; other shapes, and dims.flags with
- * SSM_TREE_VERIFY_FIFO, copy state and window to the outputs (unless in
- * place), run ssm_tree_commit in place on them and then ssm_tree_verify.
+ * rounding.  One launch: trees of 1 to 16 nodes with a headdim that is a
+ * multiple of 16; trees of 17 to 64 nodes with bf16 inputs, d_state <= 128,
+ * a headdim that is a multiple of 64, (H*P/G) a multiple of 512 and neither
+ * SSM_TREE_CONV_XBC nor a gate (the accepted path is then committed in
+ * closed form, exp of fp64 prefix sums of dt*A weighting each path token:
+ * equal to the sequential replay up to fp32 rounding).  Other shapes, and
+ * dims.flags with SSM_TREE_VERIFY_FIFO, copy state and window to the
+ * outputs (unless in place), run ssm_tree_commit in place on them and then
+ * ssm_tree_verify.
  * Host-side errors as for the two calls; every output range is checked
  * against every input range before anything is enqueued.
  */

@@ -857,12 +857,26 @@ __global__ void __launch_bounds__(kTtThreads) verify_tt_kernel(VerifyArgs a, int
 // The same verify with the waves split by role, for blocks that lie in one
 // head (P a multiple of 64) and at least 8 blocks per workgroup.  Waves 0-3
 // (producers) run the vector work of block ph: the conv and M, then deliver
-// block ph + 1's inputs and prefetch block ph + 2's.  Waves 4-7 (consumers)
-// run the matrix work: C . h0 of block ph, then the path terms and y of
-// block ph - 1.  Conv outputs, M, the x rows and the conv parameters are
-// double-buffered by block parity, so one barrier per phase separates
-// writers from readers, and each SIMD holds one wave of each role whose
-// vector and matrix instructions overlap.
+// block ph + 1's inputs and issue block ph + 3's loads (two register sets).
+// Waves 4-7 (consumers) run the matrix work: C . h0 of block ph, then the
+// path terms and y of block ph - 1.  Conv outputs, M, the x rows and the
+// conv parameters are double-buffered by block parity, so one barrier per
+// phase separates writers from readers, and each SIMD holds one wave of each
+// role whose vector and matrix instructions overlap.  Every phase of a
+// role's loop issues the same memory operations (unconditional loads from
+// clamped addresses, stores past the range dropped by buffer resources),
+// so the compiler's waits count them and loads stay in flight across the
+// barrier.
+//
+// With CM the kernel is also the round of ssm_tree_commit_verify (SpecMamba
+// page sec. 3.1, the accepted path recomputed from the stored dt, B and x):
+// the previous tree's path is committed into each block's state before its
+// C . h0, in closed form on the matrix cores,
+//   h_new^T = exp(P_last) h^T + Bp^T W,  W[q][c] = exp(P_last - P_q) dt_q x~_q[c],
+// P_q the fp64 prefix sum of dt * A along the path (the producers form W
+// for the first 16 positions, the consumers for the rest), the state and
+// the committed window are written, and the next tree is verified from the
+// committed state.
 // ---------------------------------------------------------------------------
 
 namespace {
@@ -870,11 +884,16 @@ namespace {
 constexpr int kWsWaves = 8;
 constexpr int kWsThreads = kWsWaves * kWave;
 constexpr int kWsMaxBlk = 16;
+// the commit's first 16 path positions: their weighted conv outputs are
+// formed by the producers, [channel][position] with a padded stride (the 16
+// lanes that read one position read 16 channels on distinct banks)
+constexpr int kWqPos = 16;
+constexpr int kWqStride = kWqPos + 1;
 
 struct TtWsLds {
   int parent, anc, cidx, misc, C, cbt, X, Y, Mo, S2, Ah, dt, D, cw, cb, nf, nff, total, row, xbuf, ybuf, mbuf, cwbuf;
   // cm: the commit's own arrays (offset 0 when unused)
-  int pparent, path, Pr, wt, at;
+  int pparent, path, Pr, wt, at, Wq;
   __host__ __device__ TtWsLds(int N, int E, int TT, bool cm = false) {
     const int KT = 16 * TT, pair_bytes = 4 * 16 * kPairStride * pair_of(TT, 0);
     int o = 0;
@@ -902,13 +921,14 @@ struct TtWsLds {
     cb = o; o += 2 * 4 * kTtRows;            // [parity][channel]
     nf = o; o += 2 * kTtRows * kTtMaxT / 4;  // [parity][channel][node quad] codes of non-finite conv outputs
     nff = o; o += 4 * (kWsMaxBlk + 1);       // [phase] whether the block's conv outputs hold a non-finite value
-    pparent = path = Pr = wt = at = 0;
+    pparent = path = Pr = wt = at = Wq = 0;
     if (cm) {
       pparent = o; o += 4 * kTtMaxT;         // the committed tree's parent[]
       path = o; o += 4 * kTtMaxT;            // the accepted path
       Pr = o; o += 2 * ybuf;                 // [parity] old window rows and the path's x rows, raw
       wt = o; o += 4 * kWsMaxBlk * kTtMaxT;  // [block][path position] exp(P_last - P_q) dt_q
       at = o; o += 4 * kWsMaxBlk;            // [block] exp(P_last)
+      Wq = o; o += 2 * 4 * kTtRows * kWqStride;  // [parity][channel][position < 16] weight * x~ (producers)
       // the path's B rows (raw, zero past its length) take the C rows' place
       // once the matrix-core operands hold those
     }
@@ -951,6 +971,7 @@ __global__ void __launch_bounds__(kWsThreads) verify_tt_ws_kernel(CommitVerifyAr
   float* s_at = reinterpret_cast<float*>(smem + lo.at);
   auto s_pr = [&](int par) { return reinterpret_cast<TIn*>(smem + lo.Pr + par * lo.ybuf); };
   int32_t* s_nff = reinterpret_cast<int32_t*>(smem + lo.nff);
+  auto s_wq = [&](int par) { return reinterpret_cast<float*>(smem + lo.Wq + par * 4 * kTtRows * kWqStride); };
   uint64_t* s_anc = reinterpret_cast<uint64_t*>(smem + lo.anc);
   int32_t* s_cidx = reinterpret_cast<int32_t*>(smem + lo.cidx);
   int32_t* s_misc = reinterpret_cast<int32_t*>(smem + lo.misc);
@@ -1172,6 +1193,7 @@ __global__ void __launch_bounds__(kWsThreads) verify_tt_ws_kernel(CommitVerifyAr
     RawQ x[kXQ];
     RawQ p[kPQ];
     uint32_t win[3];
+    uint32_t q7[CM ? 7 : 1];  // the rows of this thread's channel that its 4 path positions tap
     float cw[4], cb;
   };
   PRegs pra, prb;
@@ -1188,18 +1210,24 @@ __global__ void __launch_bounds__(kWsThreads) verify_tt_ws_kernel(CommitVerifyAr
   // the path in LDS), so that a prefetch issues its loads without waiting on
   // LDS reads.  Each points at the row's element for channel offset 0 of
   // block 0 (plus the thread's channel within the block).
-  const TIn* psrc[kPQ];
+  // (as element offsets from x_prev's unit, or from the window's where bit
+  // it of pwin_rows is set: 32-bit offsets keep the registers down)
+  int psrc[kPQ];
+  uint32_t pwin_rows = 0;
   const TIn* wsrc[3];
   {
     const int ptid = opaque_tid();
 #pragma unroll
     for (int it = 0; it < kPQ; ++it) {
-      psrc[it] = xg + cw0;  // (unused rows)
+      psrc[it] = cw0;  // (unused rows: row 0 of the previous tree's x)
       if constexpr (CM) {
         const int qi = ptid + it * kTtThreads;
         const int rr = qi / (kTtRows / 4), c4 = (qi % (kTtRows / 4)) * 4;
-        if (rr >= 3 && rr < 3 + clen) psrc[it] = xpg + (int64_t)s_path[rr - 3] * DI + cw0 + c4;
-        if (rr < 3 && rr >= 4 - W) psrc[it] = wg + (int64_t)(rr - (4 - W)) * CH + cw0 + c4;
+        if (rr >= 3 && rr < 3 + clen) psrc[it] = s_path[rr - 3] * DI + cw0 + c4;
+        if (rr < 3 && rr >= 4 - W) {
+          psrc[it] = (rr - (4 - W)) * CH + cw0 + c4;
+          pwin_rows |= 1u << it;
+        }
       }
     }
 #pragma unroll
@@ -1211,6 +1239,26 @@ __global__ void __launch_bounds__(kWsThreads) verify_tt_ws_kernel(CommitVerifyAr
         if constexpr (CM) {  // the committed window: element clen + r of (old window, path rows)
           const int e = clen + r;
           wsrc[r] = e < W - 1 ? wg + (int64_t)e * CH + c : xpg + (int64_t)s_path[e - (W - 1)] * DI + c;
+        }
+      }
+    }
+  }
+  // the commit's first 16 path positions, producer thread (channel pch,
+  // positions 4 pg .. 4 pg + 3, pg = its wave): they tap element q + W - 1 - t
+  // of (old window, path rows), i.e. rows 4 pg .. 4 pg + 6 of the block's
+  // path buffer (row 4 - W + e holds element e)
+  int qsrc[CM ? 7 : 1];  // (offsets as psrc; window rows flagged by bit 8 + m of pwin_rows)
+  {
+    const int pg = opaque_tid() >> 6;
+#pragma unroll
+    for (int m = 0; m < (CM ? 7 : 1); ++m) {
+      qsrc[m] = cw0 + pch;  // (unused rows)
+      if constexpr (CM) {
+        const int rr = 4 * pg + m;
+        if (rr >= 3 && rr < 3 + clen) qsrc[m] = s_path[rr - 3] * DI + cw0 + pch;
+        if (rr < 3 && rr >= 4 - W) {
+          qsrc[m] = (rr - (4 - W)) * CH + cw0 + pch;
+          pwin_rows |= 1u << (8 + m);
         }
       }
     }
@@ -1229,7 +1277,13 @@ __global__ void __launch_bounds__(kWsThreads) verify_tt_ws_kernel(CommitVerifyAr
     }
     if constexpr (CM) {
 #pragma unroll
-      for (int it = 0; it < kPQ; ++it) R.p[it] = *reinterpret_cast<const RawQ*>(psrc[it] + boff);
+      for (int it = 0; it < kPQ; ++it)
+        R.p[it] = *reinterpret_cast<const RawQ*>(((pwin_rows >> it) & 1 ? wg : xpg) + psrc[it] + boff);
+      // (the aligned dword holding the element: the rows start at even elements)
+#pragma unroll
+      for (int m = 0; m < 7; ++m)
+        R.q7[m] = *reinterpret_cast<const uint32_t*>(((pwin_rows >> (8 + m)) & 1 ? wg : xpg) + qsrc[m] + boff -
+                                                     (pch & 1));
     }
 #pragma unroll
     for (int r = 0; r < 3; ++r) {
@@ -1255,6 +1309,26 @@ __global__ void __launch_bounds__(kWsThreads) verify_tt_ws_kernel(CommitVerifyAr
       if (qi < KT * (kTtRows / 4)) *reinterpret_cast<RawQ*>(xr + v * kTtRows + c4) = R.x[it];
     }
     if constexpr (CM) {
+      // the weighted conv outputs W[q][c] = exp(P_last - P_q) dt_q x~_q[c] of
+      // this thread's channel at positions 4 pg .. 4 pg + 3 (zero past the
+      // path; a delivery past the last block writes a buffer nobody reads)
+      {
+        const int pg = ptid >> 6, wb = blk < NBLK ? blk : NBLK - 1;
+        float xv[7];
+#pragma unroll
+        for (int m = 0; m < 7; ++m) xv[m] = __uint_as_float(((R.q7[m] >> (16 * (pch & 1))) & 0xFFFFu) << 16);
+        float* wq = s_wq(par) + pch * kWqStride;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int q = 4 * pg + i;
+          float z = fmaf(R.cw[0], xv[i + 3], a.prm.conv_b ? R.cb : 0.0f);
+#pragma unroll
+          for (int t = 1; t < 4; ++t)
+            if (t < W) z = fmaf(R.cw[t], xv[i + 3 - t], z);
+          const float xt = d.silu ? silu_fast(z) : z;
+          wq[q] = q < clen ? s_wt[wb * kTtMaxT + q] * xt : 0.0f;
+        }
+      }
       TIn* pr = s_pr(par);
 #pragma unroll
       for (int it = 0; it < kPQ; ++it) {
@@ -1483,12 +1557,17 @@ __global__ void __launch_bounds__(kWsThreads) verify_tt_ws_kernel(CommitVerifyAr
               } else {
                 bw[0] = *reinterpret_cast<const uint16_t*>(bq);
               }
-              float z = fmaf(cwv[0], load_in(pr, (3 + q) * kTtRows + ch), cbv);
+              float wv;
+              if (s4 < kWqPos) {  // formed by the producers
+                wv = s_wq(par)[ch * kWqStride + q];
+              } else {
+                float z = fmaf(cwv[0], load_in(pr, (3 + q) * kTtRows + ch), cbv);
 #pragma unroll
-              for (int t = 1; t < 4; ++t)
-                if (t < W) z = fmaf(cwv[t], load_in(pr, (3 + q - t) * kTtRows + ch), z);
-              const float xt = d.silu ? silu_fast(z) : z;
-              const float wv = q < clen ? s_wt[ph * kTtMaxT + q] * xt : 0.0f;
+                for (int t = 1; t < 4; ++t)
+                  if (t < W) z = fmaf(cwv[t], load_in(pr, (3 + q - t) * kTtRows + ch), z);
+                const float xt = d.silu ? silu_fast(z) : z;
+                wv = q < clen ? s_wt[ph * kTtMaxT + q] * xt : 0.0f;
+              }
 #pragma unroll
               for (int gg = 0; gg < NG; ++gg) {
                 const uint32_t w2 = bw[gg >> 1];
