@@ -997,7 +997,39 @@ __global__ void __launch_bounds__(kWsThreads) verify_tt_ws_kernel(CommitVerifyAr
 #pragma unroll
     for (int gg = 0; gg < NG; ++gg) hq[gg] = SQ::load(sin + 16 * gg);
   }
+  // ---- every wave's blocks (wave, wave + 8): the nodes' dt_raw (lane =
+  // node) and the head's parameters, issued at entry so that the head data
+  // below waits on no load ----
+  constexpr int kHB = (kWsMaxBlk + kWsWaves - 1) / kWsWaves;
+  uint32_t hdt[kHB], hdtp[kHB];
+  float hbias[kHB], hA[kHB], hD[kHB];
+  {
+    const TIn* dtg0 = reinterpret_cast<const TIn*>(a.dt_raw) + unit * T * (int64_t)H;
+#pragma unroll
+    for (int i = 0; i < kHB; ++i) {
+      const int bw = wave + kWsWaves * i;
+      const int h = (cw0 + (bw < NBLK ? bw : 0) * kTtRows) / P;
+      hdt[i] = raw_bits<TIn>(dtg0 + (int64_t)(lane < T ? lane : T - 1) * H + h);
+      hbias[i] = a.prm.dt_bias[(int64_t)l * H + h];
+      hA[i] = a.prm.A[(int64_t)l * H + h];
+      hD[i] = a.prm.D[(int64_t)l * H + h];
+      hdtp[i] = 0u;
+    }
+  }
 
+  const TIn* xg = reinterpret_cast<const TIn*>(a.x) + unit * T * (int64_t)DI;
+  const TIn* wg = reinterpret_cast<const TIn*>(a.window_in) + unit * (W - 1) * (int64_t)CH;
+  // buffer resources over this unit's y rows and committed window: an offset
+  // past the range drops the store, so that stores of padded nodes or unused
+  // window rows need no branch (a branch around a store changes the count
+  // of outstanding memory operations from phase to phase, and the compiler
+  // then waits for all of them before the next block's state is used)
+  constexpr int kOutOfRange = 0x7FFFFFF0;
+  const __amdgpu_buffer_rsrc_t y_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(a.y + unit * T * (int64_t)DI, (short)0, T * DI * 4, kBufWord3);
+  const __amdgpu_buffer_rsrc_t wo_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      CM && W > 1 ? reinterpret_cast<TIn*>(a.window_out) + unit * (W - 1) * (int64_t)CH : nullptr, (short)0,
+      CM && W > 1 ? (W - 1) * CH * E : 0, kBufWord3);
   // ---- tree prologue (all waves): parent[], C and B rows ----
   if (tid < kTtMaxT) s_parent[tid] = tid < T ? a.parent[(int64_t)b * T + tid] : 0;
   if (tid <= kWsMaxBlk) s_nff[tid] = 0;
@@ -1021,6 +1053,199 @@ __global__ void __launch_bounds__(kWsThreads) verify_tt_ws_kernel(CommitVerifyAr
     *reinterpret_cast<u32x4*>(s_B + v * rs + q * 16) = b4;
   }
   __syncthreads();
+  // ---- producers' per-block inputs, a block ahead in registers ----
+  constexpr int kXQ = (KT * (kTtRows / 4) + kTtThreads - 1) / kTtThreads;  // (256 producer threads)
+  // the commit: the old window rows and the path's x rows, rows 0..2 and
+  // 3.. of the block's path buffer (the window right-aligned: element e of
+  // (old window, path rows) sits at row 4 - W + e)
+  constexpr int kPQ = CM ? ((3 + KT) * (kTtRows / 4) + kTtThreads - 1) / kTtThreads : 1;
+  // one block's prefetched inputs; two sets, so that a block's loads are
+  // issued two phases before its delivery
+  struct PRegs {
+    RawQ x[kXQ];
+    RawQ p[kPQ];
+    uint32_t win[3];
+    uint32_t q7[CM ? 7 : 1];  // the rows of this thread's channel that its 4 path positions tap
+    float cw[4], cb;
+  };
+  PRegs pra, prb;
+  // path length applied (0 when nothing is committed): first the length as
+  // given, clamped, so that blocks 0 and 1 are fetched before the path is
+  // validated; a failed commit (rare) sets 0 and fetches them again
+  int clen = CM ? (s_misc[3] < 0 ? 0 : (s_misc[3] > T ? T : s_misc[3])) : 0;
+  auto spath = [&](int q) {  // a path node, clamped into the tree (an invalid path is refetched)
+    const int v = s_path[q];
+    return (v >= 0 && v < T) ? v : 0;
+  };
+  const TIn* xpg = CM ? reinterpret_cast<const TIn*>(a.x_prev) + unit * T * (int64_t)DI : nullptr;
+  // Every prefetch load is unconditional, from a clamped address where its
+  // value is not needed (selected away at delivery): a load under a branch
+  // makes the compiler wait for it where the branches join, which turned
+  // the one-phase lead into a wait inside the same phase.  Unused lanes of
+  // a load all read one address.
+  const int pch = opaque_tid() & (kTtRows - 1);  // the channel of the per-channel rows (all four waves)
+  // The sources of a thread's path and window rows are the same for every
+  // block but for the block's channel offset: resolved once here (through
+  // the path in LDS), so that a prefetch issues its loads without waiting on
+  // LDS reads.  Each points at the row's element for channel offset 0 of
+  // block 0 (plus the thread's channel within the block).
+  // (as element offsets from x_prev's unit, or from the window's where bit
+  // it of pwin_rows is set: 32-bit offsets keep the registers down)
+  int psrc[kPQ];
+  uint32_t pwin_rows = 0;
+  const TIn* wsrc[3];
+  int qsrc[CM ? 7 : 1];  // (offsets as psrc; window rows flagged by bit 8 + m of pwin_rows)
+  auto resolve_sources = [&]() {
+    pwin_rows = 0;
+    const int ptid = opaque_tid();
+#pragma unroll
+    for (int it = 0; it < kPQ; ++it) {
+      psrc[it] = cw0;  // (unused rows: row 0 of the previous tree's x)
+      if constexpr (CM) {
+        const int qi = ptid + it * kTtThreads;
+        const int rr = qi / (kTtRows / 4), c4 = (qi % (kTtRows / 4)) * 4;
+        if (rr >= 3 && rr < 3 + clen) psrc[it] = spath(rr - 3) * DI + cw0 + c4;
+        if (rr < 3 && rr >= 4 - W) {
+          psrc[it] = (rr - (4 - W)) * CH + cw0 + c4;
+          pwin_rows |= 1u << it;
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 3; ++r) {
+      const int c = cw0 + pch;
+      wsrc[r] = xg + c;  // (unused taps)
+      if (r < W - 1) {
+        wsrc[r] = wg + (int64_t)r * CH + c;
+        if constexpr (CM) {  // the committed window: element clen + r of (old window, path rows)
+          const int e = clen + r;
+          wsrc[r] = e < W - 1 ? wg + (int64_t)e * CH + c : xpg + (int64_t)spath(e - (W - 1)) * DI + c;
+        }
+      }
+    }
+    // the commit's first 16 path positions, producer thread (channel pch,
+    // positions 4 pg .. 4 pg + 3, pg = its wave): they tap element
+    // q + W - 1 - t of (old window, path rows), i.e. rows 4 pg .. 4 pg + 6 of
+    // the block's path buffer (row 4 - W + e holds element e)
+    const int pg = ptid >> 6;
+#pragma unroll
+    for (int m = 0; m < (CM ? 7 : 1); ++m) {
+      qsrc[m] = cw0 + pch;  // (unused rows)
+      if constexpr (CM) {
+        const int rr = 4 * pg + m;
+        if (rr >= 3 && rr < 3 + clen) qsrc[m] = spath(rr - 3) * DI + cw0 + pch;
+        if (rr < 3 && rr >= 4 - W) {
+          qsrc[m] = (rr - (4 - W)) * CH + cw0 + pch;
+          pwin_rows |= 1u << (8 + m);
+        }
+      }
+    }
+  };
+  resolve_sources();
+  const float* cwb = a.prm.conv_w + ((int64_t)l * CH + cw0 + pch) * W;
+  const float* cbb = a.prm.conv_b ? a.prm.conv_b + (int64_t)l * CH + cw0 + pch : cwb;
+  auto prefetch = [&](int blk, PRegs& R) {
+    const int ptid = opaque_tid();  // < 256
+    const int c0 = cw0 + blk * kTtRows, boff = blk * kTtRows;
+#pragma unroll
+    for (int it = 0; it < kXQ; ++it) {
+      const int qi = ptid + it * kTtThreads;
+      const int v = qi / (kTtRows / 4), c4 = (qi % (kTtRows / 4)) * 4;
+      const int vr = v < T ? v : T - 1;  // rows past T repeat row T - 1 (never a tap source)
+      R.x[it] = *reinterpret_cast<const RawQ*>(xg + (int64_t)vr * DI + c0 + c4);
+    }
+    if constexpr (CM) {
+#pragma unroll
+      for (int it = 0; it < kPQ; ++it)
+        R.p[it] = *reinterpret_cast<const RawQ*>(((pwin_rows >> it) & 1 ? wg : xpg) + psrc[it] + boff);
+      // (the aligned dword holding the element: the rows start at even elements)
+#pragma unroll
+      for (int m = 0; m < 7; ++m)
+        R.q7[m] = *reinterpret_cast<const uint32_t*>(((pwin_rows >> (8 + m)) & 1 ? wg : xpg) + qsrc[m] + boff -
+                                                     (pch & 1));
+    }
+#pragma unroll
+    for (int r = 0; r < 3; ++r) {
+      // bf16: the aligned dword holding the element (the rows start at even
+      // elements), its half picked at delivery
+      const TIn* src = wsrc[r] + boff;
+      R.win[r] = E == 2 ? *reinterpret_cast<const uint32_t*>(src - (pch & 1)) : raw_bits<TIn>(src);
+    }
+    const float* cwp = cwb + (int64_t)boff * W;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) R.cw[t] = cwp[t < W ? W - 1 - t : 0];
+    R.cb = (a.prm.conv_b ? cbb + boff : cwp)[0];
+  };
+  auto deliver = [&](int blk, PRegs& R) {
+    const int ptid = opaque_tid();
+    const int par = blk & 1;
+    TIn* xw = s_xw(par);
+    TIn* xr = xw + 3 * kTtRows;
+#pragma unroll
+    for (int it = 0; it < kXQ; ++it) {
+      const int qi = ptid + it * kTtThreads;
+      const int v = qi / (kTtRows / 4), c4 = (qi % (kTtRows / 4)) * 4;
+      if (qi < KT * (kTtRows / 4)) *reinterpret_cast<RawQ*>(xr + v * kTtRows + c4) = R.x[it];
+    }
+    if constexpr (CM) {
+      // the weighted conv outputs W[q][c] = exp(P_last - P_q) dt_q x~_q[c] of
+      // this thread's channel at positions 4 pg .. 4 pg + 3 (zero past the
+      // path; a delivery past the last block writes a buffer nobody reads)
+      {
+        const int pg = ptid >> 6, wb = blk < NBLK ? blk : NBLK - 1;
+        float xv[7];
+#pragma unroll
+        for (int m = 0; m < 7; ++m) xv[m] = __uint_as_float(((R.q7[m] >> (16 * (pch & 1))) & 0xFFFFu) << 16);
+        float* wq = s_wq(par) + pch * kWqStride;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int q = 4 * pg + i;
+          float z = fmaf(R.cw[0], xv[i + 3], a.prm.conv_b ? R.cb : 0.0f);
+#pragma unroll
+          for (int t = 1; t < 4; ++t)
+            if (t < W) z = fmaf(R.cw[t], xv[i + 3 - t], z);
+          const float xt = d.silu ? silu_fast(z) : z;
+          wq[q] = q < clen ? s_wt[wb * kTtMaxT + q] * xt : 0.0f;
+        }
+      }
+      TIn* pr = s_pr(par);
+#pragma unroll
+      for (int it = 0; it < kPQ; ++it) {
+        const int qi = ptid + it * kTtThreads;
+        const int rr = qi / (kTtRows / 4), c4 = (qi % (kTtRows / 4)) * 4;
+        if ((rr >= 3 && rr < 3 + clen) || (rr < 3 && rr >= 4 - W))
+          *reinterpret_cast<RawQ*>(pr + rr * kTtRows + c4) = R.p[it];
+      }
+    }
+    if (ptid < kTtRows) {
+      uint32_t win[3];
+#pragma unroll
+      for (int r = 0; r < 3; ++r) win[r] = E == 2 ? (R.win[r] >> (16 * (ptid & 1))) & 0xFFFFu : R.win[r];
+#pragma unroll
+      for (int r = 0; r < 3; ++r)
+        if (r < W - 1) xw[(4 - W + r) * kTtRows + ptid] = from_bits<TIn>(win[r]);
+#pragma unroll
+      for (int r = 0; r < 3; ++r)
+        if (r < 4 - W) xw[r * kTtRows + ptid] = from_bits<TIn>(0u);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) s_cw(par)[t * kTtRows + ptid] = t < W ? R.cw[t] : 0.0f;
+      s_cb(par)[ptid] = a.prm.conv_b ? R.cb : 0.0f;
+      if constexpr (CM) {  // the committed window leaves with its block
+        // buffer stores: rows past W - 1 and the blocks past the last (the
+        // loop delivers one) fall outside the range and are dropped, so that
+        // every phase issues the same memory operations
+        const uint32_t c = cw0 + blk * kTtRows + ptid;
+#pragma unroll
+        for (int r = 0; r < 3; ++r)
+          __builtin_amdgcn_raw_buffer_store_b16((uint16_t)win[r], wo_rsrc,
+                                                blk < NBLK ? (int)(((uint32_t)r * CH + c) * 2u) : kOutOfRange, 0, 0);
+      }
+    }
+  };
+  if (producer) {  // blocks 0 and 1 in flight through the rest of the prologue
+    prefetch(0, prb);
+    prefetch(1, pra);  // (NBLK >= 8)
+  }
   // the commit: the path's B rows, gathered before the path is validated
   // (a failed commit applies none of them), held until the C rows are dead
   constexpr int kBPT = CM ? (KT * kChunks + kWsThreads - 1) / kWsThreads : 1;
@@ -1028,6 +1253,18 @@ __global__ void __launch_bounds__(kWsThreads) verify_tt_ws_kernel(CommitVerifyAr
   if constexpr (CM) {
     const int len_raw = s_misc[3];
     const int lg = len_raw < 0 ? 0 : (len_raw > T ? T : len_raw);
+    {  // the path's dt_raw per block head (lane = path position; an invalid
+       // path is discarded with the commit)
+      const TIn* dtpg = reinterpret_cast<const TIn*>(a.dt_prev) + unit * T * (int64_t)H;
+      const int vp = lane < lg ? s_path[lane] : 0;
+      const int vs = (vp >= 0 && vp < T) ? vp : 0;
+#pragma unroll
+      for (int i = 0; i < kHB; ++i) {
+        const int bw = wave + kWsWaves * i;
+        const int h = (cw0 + (bw < NBLK ? bw : 0) * kTtRows) / P;
+        hdtp[i] = raw_bits<TIn>(dtpg + (int64_t)vs * H + h);
+      }
+    }
     const unsigned char* Bpg =
         reinterpret_cast<const unsigned char*>(a.B_prev) + ((unit * T) * G + g) * (int64_t)N * E;
 #pragma unroll
@@ -1129,34 +1366,32 @@ __global__ void __launch_bounds__(kWsThreads) verify_tt_ws_kernel(CommitVerifyAr
   }
   __syncthreads();  // the B rows are dead: their space holds the conv outputs
   const bool tree_ok = s_misc[0] != 0;
+  if (CM && s_misc[1] != clen) {  // the commit failed: nothing is applied
+    clen = s_misc[1];
+    resolve_sources();
+    if (producer) {
+      prefetch(0, prb);
+      prefetch(1, pra);
+    }
+  }
 
-  const TIn* xg = reinterpret_cast<const TIn*>(a.x) + unit * T * (int64_t)DI;
-  const TIn* wg = reinterpret_cast<const TIn*>(a.window_in) + unit * (W - 1) * (int64_t)CH;
-  const TIn* dtg = reinterpret_cast<const TIn*>(a.dt_raw) + unit * T * (int64_t)H;
-  // buffer resources over this unit's y rows and committed window: an offset
-  // past the range drops the store, so that stores of padded nodes or unused
-  // window rows need no branch (a branch around a store changes the count
-  // of outstanding memory operations from phase to phase, and the compiler
-  // then waits for all of them before the next block's state is used)
-  constexpr int kOutOfRange = 0x7FFFFFF0;
-  const __amdgpu_buffer_rsrc_t y_rsrc =
-      __builtin_amdgcn_make_buffer_rsrc(a.y + unit * T * (int64_t)DI, (short)0, T * DI * 4, kBufWord3);
-  const __amdgpu_buffer_rsrc_t wo_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      CM && W > 1 ? reinterpret_cast<TIn*>(a.window_out) + unit * (W - 1) * (int64_t)CH : nullptr, (short)0,
-      CM && W > 1 ? (W - 1) * CH * E : 0, kBufWord3);
-  // each block's head: dt, S (fp64) and exp(S), wave = block, lane = node
-  for (int bw = wave; bw < NBLK; bw += kWsWaves) {
+  // ---- each block's head: dt, S (fp64) and exp(S), wave = block, lane =
+  // node, from the registers loaded at entry ----
+  auto raw_f32 = [](uint32_t r) { return E == 2 ? __uint_as_float(r << 16) : __uint_as_float(r); };
+#pragma unroll
+  for (int i = 0; i < kHB; ++i) {
+    const int bw = wave + kWsWaves * i;
+    if (bw >= NBLK) break;
     const int v = lane;
-    const int h = (cw0 + bw * kTtRows) / P;
     float dtv = 0.0f;
-    if (v < T) dtv = softplus_hw(load_in(dtg, (int64_t)v * H + h) + a.prm.dt_bias[(int64_t)l * H + h]);
+    if (v < T) dtv = softplus_hw(raw_f32(hdt[i]) + hbias[i]);
     int up = v < T ? s_parent[v] : -1;
     up = (up >= 0 && up < v) ? up : -1;
-    const double s2 = root_path_sum((double)(dtv * a.prm.A[(int64_t)l * H + h]), up, v) * 1.4426950408889634;
+    const double s2 = root_path_sum((double)(dtv * hA[i]), up, v) * 1.4426950408889634;
     s_dt[bw * kTtMaxT + v] = dtv;
     s_S2[bw * kTtMaxT + v] = s2;
     s_Ah[bw * kTtMaxT + v] = __builtin_amdgcn_exp2f((float)s2);
-    if (v == 0) s_D[bw] = a.prm.D[(int64_t)l * H + h];
+    if (v == 0) s_D[bw] = hD[i];
     if constexpr (CM) {
       // the accepted path in closed form (lane = path position q):
       //   h_new = exp(P_last) h + sum_q exp(P_last - P_q) dt_q x~_q B_q,
@@ -1164,11 +1399,8 @@ __global__ void __launch_bounds__(kWsThreads) verify_tt_ws_kernel(CommitVerifyAr
       // the path's length leave P_last in lane 63)
       const int len = s_misc[1];
       float dtq = 0.0f;
-      if (v < len)
-        dtq = softplus_hw(load_in(reinterpret_cast<const TIn*>(a.dt_prev) + unit * T * (int64_t)H,
-                                  (int64_t)s_path[v] * H + h) +
-                          a.prm.dt_bias[(int64_t)l * H + h]);
-      double pq = (double)(dtq * a.prm.A[(int64_t)l * H + h]);
+      if (v < len) dtq = softplus_hw(raw_f32(hdtp[i]) + hbias[i]);
+      double pq = (double)(dtq * hA[i]);
 #pragma unroll
       for (int off = 1; off < kWave; off <<= 1) {
         const double o = __shfl_up(pq, off);
@@ -1181,192 +1413,10 @@ __global__ void __launch_bounds__(kWsThreads) verify_tt_ws_kernel(CommitVerifyAr
     }
   }
 
-  // ---- producers' per-block inputs, a block ahead in registers ----
-  constexpr int kXQ = (KT * (kTtRows / 4) + kTtThreads - 1) / kTtThreads;  // (256 producer threads)
-  // the commit: the old window rows and the path's x rows, rows 0..2 and
-  // 3.. of the block's path buffer (the window right-aligned: element e of
-  // (old window, path rows) sits at row 4 - W + e)
-  constexpr int kPQ = CM ? ((3 + KT) * (kTtRows / 4) + kTtThreads - 1) / kTtThreads : 1;
-  // one block's prefetched inputs; two sets, so that a block's loads are
-  // issued two phases before its delivery
-  struct PRegs {
-    RawQ x[kXQ];
-    RawQ p[kPQ];
-    uint32_t win[3];
-    uint32_t q7[CM ? 7 : 1];  // the rows of this thread's channel that its 4 path positions tap
-    float cw[4], cb;
-  };
-  PRegs pra, prb;
-  const int clen = CM ? s_misc[1] : 0;  // path length applied (0 when nothing is committed)
-  const TIn* xpg = CM ? reinterpret_cast<const TIn*>(a.x_prev) + unit * T * (int64_t)DI : nullptr;
-  // Every prefetch load is unconditional, from a clamped address where its
-  // value is not needed (selected away at delivery): a load under a branch
-  // makes the compiler wait for it where the branches join, which turned
-  // the one-phase lead into a wait inside the same phase.  Unused lanes of
-  // a load all read one address.
-  const int pch = opaque_tid() & (kTtRows - 1);  // the channel of the per-channel rows (all four waves)
-  // The sources of a thread's path and window rows are the same for every
-  // block but for the block's channel offset: resolved once here (through
-  // the path in LDS), so that a prefetch issues its loads without waiting on
-  // LDS reads.  Each points at the row's element for channel offset 0 of
-  // block 0 (plus the thread's channel within the block).
-  // (as element offsets from x_prev's unit, or from the window's where bit
-  // it of pwin_rows is set: 32-bit offsets keep the registers down)
-  int psrc[kPQ];
-  uint32_t pwin_rows = 0;
-  const TIn* wsrc[3];
-  {
-    const int ptid = opaque_tid();
-#pragma unroll
-    for (int it = 0; it < kPQ; ++it) {
-      psrc[it] = cw0;  // (unused rows: row 0 of the previous tree's x)
-      if constexpr (CM) {
-        const int qi = ptid + it * kTtThreads;
-        const int rr = qi / (kTtRows / 4), c4 = (qi % (kTtRows / 4)) * 4;
-        if (rr >= 3 && rr < 3 + clen) psrc[it] = s_path[rr - 3] * DI + cw0 + c4;
-        if (rr < 3 && rr >= 4 - W) {
-          psrc[it] = (rr - (4 - W)) * CH + cw0 + c4;
-          pwin_rows |= 1u << it;
-        }
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < 3; ++r) {
-      const int c = cw0 + pch;
-      wsrc[r] = xg + c;  // (unused taps)
-      if (r < W - 1) {
-        wsrc[r] = wg + (int64_t)r * CH + c;
-        if constexpr (CM) {  // the committed window: element clen + r of (old window, path rows)
-          const int e = clen + r;
-          wsrc[r] = e < W - 1 ? wg + (int64_t)e * CH + c : xpg + (int64_t)s_path[e - (W - 1)] * DI + c;
-        }
-      }
-    }
-  }
-  // the commit's first 16 path positions, producer thread (channel pch,
-  // positions 4 pg .. 4 pg + 3, pg = its wave): they tap element q + W - 1 - t
-  // of (old window, path rows), i.e. rows 4 pg .. 4 pg + 6 of the block's
-  // path buffer (row 4 - W + e holds element e)
-  int qsrc[CM ? 7 : 1];  // (offsets as psrc; window rows flagged by bit 8 + m of pwin_rows)
-  {
-    const int pg = opaque_tid() >> 6;
-#pragma unroll
-    for (int m = 0; m < (CM ? 7 : 1); ++m) {
-      qsrc[m] = cw0 + pch;  // (unused rows)
-      if constexpr (CM) {
-        const int rr = 4 * pg + m;
-        if (rr >= 3 && rr < 3 + clen) qsrc[m] = s_path[rr - 3] * DI + cw0 + pch;
-        if (rr < 3 && rr >= 4 - W) {
-          qsrc[m] = (rr - (4 - W)) * CH + cw0 + pch;
-          pwin_rows |= 1u << (8 + m);
-        }
-      }
-    }
-  }
-  const float* cwb = a.prm.conv_w + ((int64_t)l * CH + cw0 + pch) * W;
-  const float* cbb = a.prm.conv_b ? a.prm.conv_b + (int64_t)l * CH + cw0 + pch : cwb;
-  auto prefetch = [&](int blk, PRegs& R) {
-    const int ptid = opaque_tid();  // < 256
-    const int c0 = cw0 + blk * kTtRows, boff = blk * kTtRows;
-#pragma unroll
-    for (int it = 0; it < kXQ; ++it) {
-      const int qi = ptid + it * kTtThreads;
-      const int v = qi / (kTtRows / 4), c4 = (qi % (kTtRows / 4)) * 4;
-      const int vr = v < T ? v : T - 1;  // rows past T repeat row T - 1 (never a tap source)
-      R.x[it] = *reinterpret_cast<const RawQ*>(xg + (int64_t)vr * DI + c0 + c4);
-    }
-    if constexpr (CM) {
-#pragma unroll
-      for (int it = 0; it < kPQ; ++it)
-        R.p[it] = *reinterpret_cast<const RawQ*>(((pwin_rows >> it) & 1 ? wg : xpg) + psrc[it] + boff);
-      // (the aligned dword holding the element: the rows start at even elements)
-#pragma unroll
-      for (int m = 0; m < 7; ++m)
-        R.q7[m] = *reinterpret_cast<const uint32_t*>(((pwin_rows >> (8 + m)) & 1 ? wg : xpg) + qsrc[m] + boff -
-                                                     (pch & 1));
-    }
-#pragma unroll
-    for (int r = 0; r < 3; ++r) {
-      // bf16: the aligned dword holding the element (the rows start at even
-      // elements), its half picked at delivery
-      const TIn* src = wsrc[r] + boff;
-      R.win[r] = E == 2 ? *reinterpret_cast<const uint32_t*>(src - (pch & 1)) : raw_bits<TIn>(src);
-    }
-    const float* cwp = cwb + (int64_t)boff * W;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) R.cw[t] = cwp[t < W ? W - 1 - t : 0];
-    R.cb = (a.prm.conv_b ? cbb + boff : cwp)[0];
-  };
-  auto deliver = [&](int blk, PRegs& R) {
-    const int ptid = opaque_tid();
-    const int par = blk & 1;
-    TIn* xw = s_xw(par);
-    TIn* xr = xw + 3 * kTtRows;
-#pragma unroll
-    for (int it = 0; it < kXQ; ++it) {
-      const int qi = ptid + it * kTtThreads;
-      const int v = qi / (kTtRows / 4), c4 = (qi % (kTtRows / 4)) * 4;
-      if (qi < KT * (kTtRows / 4)) *reinterpret_cast<RawQ*>(xr + v * kTtRows + c4) = R.x[it];
-    }
-    if constexpr (CM) {
-      // the weighted conv outputs W[q][c] = exp(P_last - P_q) dt_q x~_q[c] of
-      // this thread's channel at positions 4 pg .. 4 pg + 3 (zero past the
-      // path; a delivery past the last block writes a buffer nobody reads)
-      {
-        const int pg = ptid >> 6, wb = blk < NBLK ? blk : NBLK - 1;
-        float xv[7];
-#pragma unroll
-        for (int m = 0; m < 7; ++m) xv[m] = __uint_as_float(((R.q7[m] >> (16 * (pch & 1))) & 0xFFFFu) << 16);
-        float* wq = s_wq(par) + pch * kWqStride;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int q = 4 * pg + i;
-          float z = fmaf(R.cw[0], xv[i + 3], a.prm.conv_b ? R.cb : 0.0f);
-#pragma unroll
-          for (int t = 1; t < 4; ++t)
-            if (t < W) z = fmaf(R.cw[t], xv[i + 3 - t], z);
-          const float xt = d.silu ? silu_fast(z) : z;
-          wq[q] = q < clen ? s_wt[wb * kTtMaxT + q] * xt : 0.0f;
-        }
-      }
-      TIn* pr = s_pr(par);
-#pragma unroll
-      for (int it = 0; it < kPQ; ++it) {
-        const int qi = ptid + it * kTtThreads;
-        const int rr = qi / (kTtRows / 4), c4 = (qi % (kTtRows / 4)) * 4;
-        if ((rr >= 3 && rr < 3 + clen) || (rr < 3 && rr >= 4 - W))
-          *reinterpret_cast<RawQ*>(pr + rr * kTtRows + c4) = R.p[it];
-      }
-    }
-    if (ptid < kTtRows) {
-      uint32_t win[3];
-#pragma unroll
-      for (int r = 0; r < 3; ++r) win[r] = E == 2 ? (R.win[r] >> (16 * (ptid & 1))) & 0xFFFFu : R.win[r];
-#pragma unroll
-      for (int r = 0; r < 3; ++r)
-        if (r < W - 1) xw[(4 - W + r) * kTtRows + ptid] = from_bits<TIn>(win[r]);
-#pragma unroll
-      for (int r = 0; r < 3; ++r)
-        if (r < 4 - W) xw[r * kTtRows + ptid] = from_bits<TIn>(0u);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) s_cw(par)[t * kTtRows + ptid] = t < W ? R.cw[t] : 0.0f;
-      s_cb(par)[ptid] = a.prm.conv_b ? R.cb : 0.0f;
-      if constexpr (CM) {  // the committed window leaves with its block
-        // buffer stores: rows past W - 1 and the blocks past the last (the
-        // loop delivers one) fall outside the range and are dropped, so that
-        // every phase issues the same memory operations
-        const uint32_t c = cw0 + blk * kTtRows + ptid;
-#pragma unroll
-        for (int r = 0; r < 3; ++r)
-          __builtin_amdgcn_raw_buffer_store_b16((uint16_t)win[r], wo_rsrc,
-                                                blk < NBLK ? (int)(((uint32_t)r * CH + c) * 2u) : kOutOfRange, 0, 0);
-      }
-    }
-  };
-  if (producer) {
-    prefetch(0, pra);
-    deliver(0, pra);
-    prefetch(1, pra);  // (NBLK >= 8)
+  // block 0 delivered (with the commit after the barrier below: its
+  // weighted path conv reads the head data of other waves)
+  if (!CM && producer) {
+    deliver(0, prb);
     prefetch(2, prb);
   }
   // consumers with bf16 inputs and d_state <= 128: the C operands of every
@@ -1394,6 +1444,10 @@ __global__ void __launch_bounds__(kWsThreads) verify_tt_ws_kernel(CommitVerifyAr
   for (int ti = 0; ti < TT; ++ti) accp[ti] = f32x4{0.f, 0.f, 0.f, 0.f};
   __syncthreads();
   if constexpr (CM) {
+    if (producer) {
+      deliver(0, prb);
+      prefetch(2, prb);
+    }
     // the C rows are dead: the path's B rows take their place, as
     // [position q][column j][group gg] (NG bf16 per (q, j)), so that the
     // lane that brings B_q[16 gg + j] for every gg reads them at once
