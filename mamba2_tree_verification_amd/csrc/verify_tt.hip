@@ -883,7 +883,8 @@ namespace {
 
 constexpr int kWsWaves = 8;
 constexpr int kWsThreads = kWsWaves * kWave;
-constexpr int kWsMaxBlk = 16;
+constexpr int kWsMaxBlk = 16;   // blocks per workgroup, the round
+constexpr int kWsMaxBlkV = 40;  // blocks per workgroup, verify alone (its per-block tables have room)
 // the commit's first 16 path positions: their weighted conv outputs are
 // formed by the producers, [channel][position] with a padded stride (the 16
 // lanes that read one position read 16 channels on distinct banks)
@@ -894,7 +895,7 @@ struct TtWsLds {
   int parent, anc, cidx, misc, C, cbt, X, Y, Mo, S2, Ah, dt, D, cw, cb, nf, nff, total, row, xbuf, ybuf, mbuf, cwbuf;
   // cm: the commit's own arrays (offset 0 when unused)
   int pparent, path, Pr, wt, at, Wq;
-  __host__ __device__ TtWsLds(int N, int E, int TT, bool cm = false) {
+  __host__ __device__ TtWsLds(int N, int E, int TT, bool cm, int nblk) {
     const int KT = 16 * TT, pair_bytes = 4 * 16 * kPairStride * pair_of(TT, 0);
     int o = 0;
     row = N * E + 16;
@@ -912,22 +913,22 @@ struct TtWsLds {
     Y = o; o += 2 * ybuf;
     mbuf = pair_bytes;
     Mo = o; o += 2 * mbuf;
-    S2 = o; o += 8 * kWsMaxBlk * kTtMaxT;   // [block][node] fp64
-    Ah = o; o += 4 * kWsMaxBlk * kTtMaxT;   // [block][node]
-    dt = o; o += 4 * kWsMaxBlk * kTtMaxT;   // [block][node]
-    D = o; o += 4 * kWsMaxBlk;
+    S2 = o; o += 8 * nblk * kTtMaxT;        // [block][node] fp64
+    Ah = o; o += 4 * nblk * kTtMaxT;        // [block][node]
+    dt = o; o += 4 * nblk * kTtMaxT;        // [block][node]
+    D = o; o += 4 * nblk;
     cwbuf = 4 * 4 * kTtRows;
     cw = o; o += 2 * cwbuf;                  // [parity][tap][channel]
     cb = o; o += 2 * 4 * kTtRows;            // [parity][channel]
     nf = o; o += 2 * kTtRows * kTtMaxT / 4;  // [parity][channel][node quad] codes of non-finite conv outputs
-    nff = o; o += 4 * (kWsMaxBlk + 1);       // [phase] whether the block's conv outputs hold a non-finite value
+    nff = o; o += 4 * (nblk + 1);            // [phase] whether the block's conv outputs hold a non-finite value
     pparent = path = Pr = wt = at = Wq = 0;
     if (cm) {
       pparent = o; o += 4 * kTtMaxT;         // the committed tree's parent[]
       path = o; o += 4 * kTtMaxT;            // the accepted path
       Pr = o; o += 2 * ybuf;                 // [parity] old window rows and the path's x rows, raw
-      wt = o; o += 4 * kWsMaxBlk * kTtMaxT;  // [block][path position] exp(P_last - P_q) dt_q
-      at = o; o += 4 * kWsMaxBlk;            // [block] exp(P_last)
+      wt = o; o += 4 * nblk * kTtMaxT;       // [block][path position] exp(P_last - P_q) dt_q
+      at = o; o += 4 * nblk;                 // [block] exp(P_last)
       Wq = o; o += 2 * 4 * kTtRows * kWqStride;  // [parity][channel][position < 16] weight * x~ (producers)
       // the path's B rows (raw, zero past its length) take the C rows' place
       // once the matrix-core operands hold those
@@ -963,7 +964,7 @@ __global__ void __launch_bounds__(kWsThreads) verify_tt_ws_kernel(CommitVerifyAr
   static_assert(!CM || (E == 2 && NG <= 8), "commit: bf16 inputs, d_state <= 128");
 
   extern __shared__ __align__(16) unsigned char smem[];
-  const TtWsLds lo(N, E, TT, CM);
+  const TtWsLds lo(N, E, TT, CM, NBLK);
   int32_t* s_parent = reinterpret_cast<int32_t*>(smem + lo.parent);
   int32_t* s_pparent = reinterpret_cast<int32_t*>(smem + lo.pparent);
   int32_t* s_path = reinterpret_cast<int32_t*>(smem + lo.path);
@@ -1000,7 +1001,7 @@ __global__ void __launch_bounds__(kWsThreads) verify_tt_ws_kernel(CommitVerifyAr
   // ---- every wave's blocks (wave, wave + 8): the nodes' dt_raw (lane =
   // node) and the head's parameters, issued at entry so that the head data
   // below waits on no load ----
-  constexpr int kHB = (kWsMaxBlk + kWsWaves - 1) / kWsWaves;
+  constexpr int kHB = ((CM ? kWsMaxBlk : kWsMaxBlkV) + kWsWaves - 1) / kWsWaves;
   uint32_t hdt[kHB], hdtp[kHB];
   float hbias[kHB], hA[kHB], hD[kHB];
   {
@@ -1032,7 +1033,7 @@ __global__ void __launch_bounds__(kWsThreads) verify_tt_ws_kernel(CommitVerifyAr
       CM && W > 1 ? (W - 1) * CH * E : 0, kBufWord3);
   // ---- tree prologue (all waves): parent[], C and B rows ----
   if (tid < kTtMaxT) s_parent[tid] = tid < T ? a.parent[(int64_t)b * T + tid] : 0;
-  if (tid <= kWsMaxBlk) s_nff[tid] = 0;
+  if (tid <= NBLK) s_nff[tid] = 0;
   if constexpr (CM) {
     if (tid < kTtMaxT) {
       s_pparent[tid] = tid < T ? a.parent_prev[(int64_t)b * T + tid] : 0;
@@ -1774,7 +1775,7 @@ namespace {
 
 template <typename TIn, typename TS, int NG, int TT, bool CM = false>
 int launch_ws_t(const CommitVerifyArgs& a, int nblk, hipStream_t s) {
-  const size_t lds = (size_t)TtWsLds(16 * NG, (int)sizeof(TIn), TT, CM).total;
+  const size_t lds = (size_t)TtWsLds(16 * NG, (int)sizeof(TIn), TT, CM, nblk).total;
   if (lds > 160 * 1024) return SSM_TREE_E_DIMS;
   if (allow_lds(verify_tt_ws_kernel<TIn, TS, NG, TT, CM>, lds) != hipSuccess) return SSM_TREE_E_HIP;
   dim3 grid(a.d.d_in / (nblk * kTtRows), a.d.Bsz, a.d.L);
@@ -1820,7 +1821,15 @@ int launch_tt_pick(const VerifyArgs& a, hipStream_t s) {
     if (a.d.xbc || a.z) return launch_tt_t<TIn, TS, NG, TT, true>(a, s);
   const int blocks = a.d.d_in / a.d.G / kTtRows;
   if (a.d.P % kTtRows == 0 && blocks % 8 == 0) {
-    const int st = launch_ws_t<TIn, TS, NG, TT>(ws_args(a), blocks % kWsMaxBlk == 0 ? kWsMaxBlk : 8, s);
+    // the most blocks per workgroup (the prologue's share of its time
+    // shrinks) that divide the group and whose tables fit the LDS
+    int nblk = 8;
+    for (int c = kWsMaxBlkV; c > 8; c -= 8)
+      if (blocks % c == 0 && TtWsLds(16 * NG, (int)sizeof(TIn), TT, false, c).total <= 160 * 1024) {
+        nblk = c;
+        break;
+      }
+    const int st = launch_ws_t<TIn, TS, NG, TT>(ws_args(a), nblk, s);
     if (st != SSM_TREE_E_DIMS) return st;  // E_DIMS: its LDS does not fit, nothing launched
   }
   return launch_tt_t<TIn, TS, NG, TT>(a, s);

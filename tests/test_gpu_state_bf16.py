@@ -47,6 +47,7 @@ VERIFY_SPECS = [
     (1, 3, 20, 8, 16, 16, 1, 4, True, True, "forest"),         # heads of 16 channels
     (1, 2, 48, 8, 64, 128, 1, 4, True, False, "forest"),       # 8 one-head blocks: the role-split kernel
     (1, 2, 64, 16, 64, 64, 1, 2, True, True, "chain_or_star"),  # 16 blocks; the round in one launch
+    (1, 2, 33, 40, 64, 64, 1, 4, True, False, "forest"),       # 40 blocks per workgroup in verify
     # bf16 products over pairs of column groups (up to 16 nodes): d_state
     # 32, 64 (heads of 32 channels) and 256 (a ring of four pieces)
     (1, 3, 12, 4, 64, 32, 1, 4, True, False, "forest"),
