@@ -883,7 +883,7 @@ namespace {
 
 constexpr int kWsWaves = 8;
 constexpr int kWsThreads = kWsWaves * kWave;
-constexpr int kWsMaxBlk = 16;   // blocks per workgroup, the round
+constexpr int kWsMaxBlk = 20;   // blocks per workgroup, the round (an even count)
 constexpr int kWsMaxBlkV = 40;  // blocks per workgroup, verify alone (its per-block tables have room)
 // the commit's first 16 path positions: their weighted conv outputs are
 // formed by the producers, [channel][position] with a padded stride (the 16
@@ -1860,7 +1860,15 @@ int launch_tt_in(const VerifyArgs& a, hipStream_t s) {
 template <typename TS, int NG>
 int launch_tt_round_g(const CommitVerifyArgs& a, hipStream_t s) {
   const int blocks = a.d.d_in / a.d.G / kTtRows;
-  const int nblk = blocks % kWsMaxBlk == 0 ? kWsMaxBlk : 8;
+  // the most blocks per workgroup (an even count dividing the group) whose
+  // tables fit the LDS next to the commit's buffers
+  const int TTs = a.d.T <= 32 ? 2 : (a.d.T <= 48 ? 3 : 4);
+  int nblk = 8;
+  for (int c = kWsMaxBlk; c > 8; c -= 2)
+    if (blocks % c == 0 && TtWsLds(16 * NG, 2, TTs, true, c).total <= 160 * 1024) {
+      nblk = c;
+      break;
+    }
   const int T = a.d.T;
   if (T <= 32) return launch_ws_t<bf16_t, TS, NG, 2, true>(a, nblk, s);
   if (T <= 48) return launch_ws_t<bf16_t, TS, NG, 3, true>(a, nblk, s);
