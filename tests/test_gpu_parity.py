@@ -79,7 +79,7 @@ SMALL = [
     (1, 2, 33, 8, 64, 64, 1, 3, False, False, True, "forest"),
     (1, 2, 24, 16, 64, 32, 2, 4, True, False, False, "forest"),
     # 40 and 24 one-head blocks per group: verify takes 40 and 24 blocks per
-    # workgroup (the round 8)
+    # workgroup, the one-launch round 20 and 12
     (1, 2, 40, 40, 64, 64, 1, 4, True, False, False, "forest"),
     (1, 2, 20, 24, 64, 32, 1, 3, True, True, True, "chain_or_star"),
 ]
