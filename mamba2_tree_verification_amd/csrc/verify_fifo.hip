@@ -143,20 +143,34 @@ __host__ __device__ inline int fifo_slots(int T, int E) {
 
 }  // namespace
 
+// The loads of one block of 32 channels that do not depend on the plan:
+// its x and window rows (raw words), its dt_raw values, its parameters and
+// its root state.  Issued a block ahead, they are in flight during the
+// previous block's walk.
 template <typename TIn, int NS>
-__global__ void __launch_bounds__(kFWaves * kWave, 2) verify_fifo_kernel(VerifyArgs a, int K) {
+struct FifoBlockLoads {
+  static constexpr int kXW = kFCh * (int)sizeof(TIn) / 4;  // words per x row
+  static constexpr int kXL = (kXW * (kMaxNodes + 3) + kFWaves * kWave - 1) / (kFWaves * kWave);
+  uint32_t xw[kXL];
+  float dtv, cw[4], cb, Ah, dtb, Dh;
+  float h[2 * NS];
+};
+
+template <typename TIn, int NS>
+__global__ void __launch_bounds__(kFWaves * kWave, NS * sizeof(TIn) <= 32 ? 2 : 1) verify_fifo_kernel(VerifyArgs a, int K, int NBK) {
   constexpr int E = 2 * NS;  // state values per lane (two channels)
   constexpr int EV = E >= 4 ? 4 : 2;  // values per LDS access
+  typedef FifoBlockLoads<TIn, NS> BL;
   const Dims d = a.d;
   const int T = d.T, N = d.N, P = d.P, H = d.H, W = d.W, DI = d.d_in, G = d.G;
+  const int T4 = (T + 3) & ~3;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int qp = lane >> 4, s = lane & 15;
   const int b = blockIdx.y, l = blockIdx.z;
   const int64_t unit = (int64_t)l * d.Bsz + b;
-  const int c0 = blockIdx.x * kFCh;
-  const int pair = wave * 4 + qp;  // channel pair within the workgroup
-  const int ca = c0 + 2 * pair;    // first channel of the pair (same head and group as ca + 1)
-  const int g = (c0 / P) / (H / G);
+  const int blk0 = blockIdx.x * NBK;  // first 32-channel block of this workgroup
+  const int pair = wave * 4 + qp;     // channel pair within a block
+  const int ch = tid % kFCh;          // the channel whose conv and y this thread forms
 
   extern __shared__ __align__(16) unsigned char smem[];
   const FifoLds lo(T, E, K);
@@ -171,70 +185,70 @@ __global__ void __launch_bounds__(kFWaves * kWave, 2) verify_fifo_kernel(VerifyA
   float* s_y = reinterpret_cast<float*>(smem + lo.y);
   uint8_t* s_path = reinterpret_cast<uint8_t*>(smem + lo.path);
   float* s_ring = reinterpret_cast<float*>(smem + lo.ring);
-
   uint32_t* s_xr = reinterpret_cast<uint32_t*>(smem + lo.xr);
   float* s_dt = reinterpret_cast<float*>(smem + lo.dt);
 
-  // ---- entry: every load that does not depend on the plan, the parent
-  // first (its wait counts the rest as still in flight) ----
-  const int pv = a.parent[(int64_t)b * T + (tid < T ? tid : T - 1)];
-  // heads of the workgroup's channels; their dt_raw rows go through LDS when
-  // one value per thread covers them
-  const int h_lo = c0 / P, nh = (c0 + kFCh - 1) / P - h_lo + 1;
-  const bool dt_lds = T * nh <= kFWaves * kWave;
   const TIn* dtr = reinterpret_cast<const TIn*>(a.dt_raw) + unit * T * H;
-  const int dti = tid < T * nh ? tid : T * nh - 1;
-  const float dtv = load_in(dtr, (int64_t)(dti / nh) * H + h_lo + dti % nh);
-  // x rows of the nodes and the window rows, 32 channels each, as raw words
-  // (unconditional loads from clamped indices; the surplus is not stored)
-  constexpr int kXW = kFCh * (int)sizeof(TIn) / 4;  // words per row
-  constexpr int kXL = (kXW * (kMaxNodes + 3) + kFWaves * kWave - 1) / (kFWaves * kWave);
-  const int xwords = kXW * (T + W - 1);
-  uint32_t xw[kXL];
-#pragma unroll
-  for (int k = 0; k < kXL; ++k) {
-    int w = tid + k * kFWaves * kWave;
-    w = w < xwords ? w : xwords - 1;
-    const int r = w / kXW, o = (w % kXW) * (4 / (int)sizeof(TIn));
-    const TIn* src = r < T ? reinterpret_cast<const TIn*>(a.x) + (unit * T + r) * (int64_t)DI + c0 + o
-                           : reinterpret_cast<const TIn*>(a.window) + (unit * (W - 1) + (r - T)) * (int64_t)DI + c0 + o;
-    xw[k] = *reinterpret_cast<const uint32_t*>(src);
-  }
-  // one channel's parameters per thread
-  const int ch = tid % kFCh, cc = c0 + ch, hh = cc / P;
-  const float* cwp = a.prm.conv_w + ((int64_t)l * DI + cc) * W;
-  float cw[4];
-#pragma unroll
-  for (int jj = 0; jj < 4; ++jj) cw[jj] = cwp[jj < W ? jj : 0];
-  const float cb = a.prm.conv_b ? a.prm.conv_b[(int64_t)l * DI + cc] : 0.0f;
-  const float Ah = a.prm.A[(int64_t)l * H + hh], dtb = a.prm.dt_bias[(int64_t)l * H + hh];
-  const float Dh = a.prm.D[(int64_t)l * H + hh];
-  // root state and the first four nodes' B and C segments
-  float hp[E];
-  const float* h0p = reinterpret_cast<const float*>(a.state) + (unit * DI + ca) * (int64_t)N + s * NS;
-  load_state_seg<NS>(h0p, hp);
-  load_state_seg<NS>(h0p + N, hp + NS);
-  const TIn* Bg = reinterpret_cast<const TIn*>(a.B) + (unit * T * G + g) * (int64_t)N + s * NS;
-  const TIn* Cg = reinterpret_cast<const TIn*>(a.C) + (unit * T * G + g) * (int64_t)N + s * NS;
-  // four register sets: node v's rows are loaded while node v - 4 is formed
-  SegRow<TIn, NS> b0, cr0, b1, cr1, b2, cr2, b3, cr3;
-  auto fetch = [&](int v, SegRow<TIn, NS>& br, SegRow<TIn, NS>& cr) {
-    v = v < T ? v : T - 1;  // past the end: the last row again (branch-free)
-    br.load(Bg + (int64_t)v * G * N);
-    cr.load(Cg + (int64_t)v * G * N);
+  const int xwords = BL::kXW * (T + W - 1);
+  // heads of block blk's channels; their dt_raw values go through LDS when
+  // one value per thread covers them
+  auto heads = [&](int blk, int& h_lo, int& nh) {
+    h_lo = blk * kFCh / P;
+    nh = (blk * kFCh + kFCh - 1) / P - h_lo + 1;
   };
-  fetch(0, b0, cr0);
-  fetch(1, b1, cr1);
-  fetch(2, b2, cr2);
-  fetch(3, b3, cr3);
+  // every load of block blk that does not depend on the plan (unconditional
+  // loads from clamped indices; the surplus is never used)
+  auto issue = [&](int blk, BL& L) __attribute__((always_inline)) {
+    const int c0 = blk * kFCh, cc = c0 + ch, hh = cc / P;
+    int h_lo, nh;
+    heads(blk, h_lo, nh);
+    const int dti = tid < T * nh ? tid : T * nh - 1;
+    L.dtv = load_in(dtr, (int64_t)(dti / nh) * H + h_lo + dti % nh);
+#pragma unroll
+    for (int k = 0; k < BL::kXL; ++k) {
+      int w = tid + k * kFWaves * kWave;
+      w = w < xwords ? w : xwords - 1;
+      const int r = w / BL::kXW, o = (w % BL::kXW) * (4 / (int)sizeof(TIn));
+      const TIn* src = r < T ? reinterpret_cast<const TIn*>(a.x) + (unit * T + r) * (int64_t)DI + c0 + o
+                             : reinterpret_cast<const TIn*>(a.window) + (unit * (W - 1) + (r - T)) * (int64_t)DI + c0 + o;
+      L.xw[k] = *reinterpret_cast<const uint32_t*>(src);
+    }
+    const float* cwp = a.prm.conv_w + ((int64_t)l * DI + cc) * W;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) L.cw[jj] = cwp[jj < W ? jj : 0];
+    L.cb = a.prm.conv_b ? a.prm.conv_b[(int64_t)l * DI + cc] : 0.0f;
+    L.Ah = a.prm.A[(int64_t)l * H + hh];
+    L.dtb = a.prm.dt_bias[(int64_t)l * H + hh];
+    L.Dh = a.prm.D[(int64_t)l * H + hh];
+    const float* h0p = reinterpret_cast<const float*>(a.state) + (unit * DI + c0 + 2 * pair) * (int64_t)N + s * NS;
+    load_state_seg<NS>(h0p, L.h);
+    load_state_seg<NS>(h0p + N, L.h + NS);
+  };
+  // B and C segments: node v's rows of block blk's group; four register
+  // sets, node v's rows loaded while node v - 4 is formed
+  auto group_rows = [&](int blk, const TIn*& Bg, const TIn*& Cg) {
+    const int g = (blk * kFCh / P) / (H / G);
+    Bg = reinterpret_cast<const TIn*>(a.B) + (unit * T * G + g) * (int64_t)N + s * NS;
+    Cg = reinterpret_cast<const TIn*>(a.C) + (unit * T * G + g) * (int64_t)N + s * NS;
+  };
+  SegRow<TIn, NS> b0, cr0, b1, cr1, b2, cr2, b3, cr3;
 
+  // ---- entry: the parent first (its wait counts the rest as in flight),
+  // then the first block's loads and rows ----
+  const int pv = a.parent[(int64_t)b * T + (tid < T ? tid : T - 1)];
+  BL L;
+  issue(blk0, L);
+  {
+    const TIn *Bg, *Cg;
+    group_rows(blk0, Bg, Cg);
+    b0.load(Bg); cr0.load(Cg);
+    b1.load(Bg + (int64_t)(T > 1 ? 1 : 0) * G * N); cr1.load(Cg + (int64_t)(T > 1 ? 1 : 0) * G * N);
+    b2.load(Bg + (int64_t)(T > 2 ? 2 : T - 1) * G * N); cr2.load(Cg + (int64_t)(T > 2 ? 2 : T - 1) * G * N);
+    b3.load(Bg + (int64_t)(T > 3 ? 3 : T - 1) * G * N); cr3.load(Cg + (int64_t)(T > 3 ? 3 : T - 1) * G * N);
+  }
   if (tid < T) s_parent[tid] = pv;
   if (tid < kMaxNodes) s_flag[tid] = 0;
   if (tid == 0) s_misc[1] = 0;
-  if (dt_lds && tid < T * nh) s_dt[tid] = dtv;
-#pragma unroll
-  for (int k = 0; k < kXL; ++k)
-    if (tid + k * kFWaves * kWave < xwords) s_xr[tid + k * kFWaves * kWave] = xw[k];
   __syncthreads();
   // BFS labelling check: parent[0] = -1, -1 <= parent[v] < v, non-decreasing
   if (tid < T) {
@@ -244,13 +258,15 @@ __global__ void __launch_bounds__(kFWaves * kWave, 2) verify_fifo_kernel(VerifyA
   __syncthreads();
   const bool valid = s_misc[1] == 0;
   if (blockIdx.x == 0 && l == 0 && tid == 0 && a.seq_status) a.seq_status[b] = valid ? SSM_TREE_OK : SSM_TREE_E_TREE;
-  float* yo = a.y + unit * T * DI + c0;
   if (!valid) {
-    for (int i = tid; i < T * kFCh; i += kFWaves * kWave) yo[(int64_t)(i / kFCh) * DI + i % kFCh] = __builtin_nanf("");
+    float* yo = a.y + unit * T * DI + blk0 * kFCh;
+    for (int i = tid; i < T * kFCh * NBK; i += kFWaves * kWave)
+      yo[(int64_t)(i / (kFCh * NBK)) * DI + i % (kFCh * NBK)] = __builtin_nanf("");
     return;
   }
 
-  // ---- plan: which nodes have children, conv input rows ----
+  // ---- plan, once for every block: which nodes have children, conv input
+  // rows, queue slots and peak occupancy ----
   if (tid < T) {
     const int v = tid, p = s_parent[v];
     if (p >= 0 && s_parent[v - 1] != p) s_flag[p] = 1;  // v is p's first child
@@ -262,7 +278,6 @@ __global__ void __launch_bounds__(kFWaves * kWave, 2) verify_fifo_kernel(VerifyA
     s_cidx[v] = packed;
   }
   __syncthreads();
-  // queue slots and peak occupancy (wave 0, one lane per node)
   if (wave == 0) {
     const int v = lane;
     const int p = v < T ? s_parent[v] : -1;
@@ -277,27 +292,8 @@ __global__ void __launch_bounds__(kFWaves * kWave, 2) verify_fifo_kernel(VerifyA
     if (v < T) s_word[v] = (p + 1) | ((internal && K > 0 ? rank % K + 1 : 0) << 8);
     // nodes T .. T4 - 1 pad the last group of four: children of the last
     // node's parent, never queued; what they form is never read
-    if (v >= T && v < ((T + 3) & ~3)) s_word[v] = s_parent[T - 1] + 1;
+    if (v >= T && v < T4) s_word[v] = s_parent[T - 1] + 1;
     if (v == 0) s_misc[0] = occ;
-  }
-  // per (node, channel): conv output, dt x~, exp(dt A); a thread keeps one
-  // channel's parameters and takes every eighth node
-  {
-    float* scf = reinterpret_cast<float*>(s_sc);
-    auto xrow = [&](int r) -> float {  // channel ch of row r (node, or T + window row)
-      if constexpr (sizeof(TIn) == 2)
-        return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(s_xr)[r * kFCh + ch] << 16);
-      return __uint_as_float(s_xr[r * kFCh + ch]);
-    };
-    for (int v = tid / kFCh; v < T; v += kFWaves * kWave / kFCh) {
-      float z = fmaf(cw[W - 1], xrow(v), cb);
-      const int codes = s_cidx[v];
-      for (int jj = 1; jj < W; ++jj) z = fmaf(cw[W - 1 - jj], xrow((codes >> (8 * (jj - 1))) & 255), z);
-      const float xt = d.silu ? silu_f32(z) : z;
-      const float dt = softplus_f32((dt_lds ? s_dt[v * nh + hh - h_lo] : load_in(dtr, (int64_t)v * H + hh)) + dtb);
-      s_xt[v * kFCh + ch] = xt;
-      *reinterpret_cast<float2*>(&scf[(v * kFCh / 2 + ch / 2) * 4 + (ch & 1) * 2]) = make_float2(expf(dt * Ah), dt * xt);
-    }
   }
   __syncthreads();
   const bool over = s_misc[0] > K;  // past the queue capacity: replay fallback
@@ -305,100 +301,167 @@ __global__ void __launch_bounds__(kFWaves * kWave, 2) verify_fifo_kernel(VerifyA
     build_paths(s_parent, T, s_depth, s_path);
     __syncthreads();
   }
-  const int word = lane < ((T + 3) & ~3) ? s_word[lane] : 0;
-
-  // ---- the walk (each wave on its own; no barriers) ----
-  // slot k of this lane: E values at s_ring + ((k * waves + wave) * E / EV + j) * 64 + lane, EV at a time
+  const int word = lane < T4 ? s_word[lane] : 0;
   auto slot_ptr = [&](int k, int j) { return s_ring + (((k * kFWaves + wave) * (E / EV) + j) * kWave + lane) * EV; };
-  int cur = -1;  // the parent whose state is in hp (-1: the root state)
-  auto step = [&](int v, SegRow<TIn, NS>& br, SegRow<TIn, NS>& cr) __attribute__((always_inline)) {
-    const int w = __builtin_amdgcn_readlane(word, v);
-    const int p = (w & 0xFF) - 1;
-    if (p != cur) {
-      if (!over) {
-        // the parent comes off the front of the queue
-        const int ps = ((__builtin_amdgcn_readlane(word, p) >> 8) & 0xFF) - 1;
+
+  for (int bi = 0; bi < NBK; ++bi) {
+    const int blk = blk0 + bi, c0 = blk * kFCh;
+    const int nblk = bi + 1 < NBK ? blk + 1 : blk;  // the block whose loads go out during this walk
+    int h_lo, nh;
+    heads(blk, h_lo, nh);
+    const bool dt_lds = T * nh <= kFWaves * kWave;
+    // this block's x rows and dt_raw values to LDS; its parameters and root
+    // state to registers (the previous block's y is out of LDS: barrier C)
+    if (dt_lds && tid < T * nh) s_dt[tid] = L.dtv;
+#pragma unroll
+    for (int k = 0; k < BL::kXL; ++k)
+      if (tid + k * kFWaves * kWave < xwords) s_xr[tid + k * kFWaves * kWave] = L.xw[k];
+    float cw[4];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) cw[jj] = L.cw[jj];
+    const float cb = L.cb, Ah = L.Ah, dtb = L.dtb, Dh = L.Dh;
+    float hp[E];
+#pragma unroll
+    for (int i = 0; i < E; ++i) hp[i] = L.h[i];
+    __syncthreads();  // A
+    // per (node, channel): conv output, dt x~, exp(dt A); a thread keeps one
+    // channel and takes every eighth node
+    {
+      float* scf = reinterpret_cast<float*>(s_sc);
+      const int hh = (c0 + ch) / P;
+      auto xrow = [&](int r) -> float {  // channel ch of row r (node, or T + window row)
+        if constexpr (sizeof(TIn) == 2)
+          return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(s_xr)[r * kFCh + ch] << 16);
+        return __uint_as_float(s_xr[r * kFCh + ch]);
+      };
+      for (int v = tid / kFCh; v < T; v += kFWaves * kWave / kFCh) {
+        float z = fmaf(cw[W - 1], xrow(v), cb);
+        const int codes = s_cidx[v];
+        for (int jj = 1; jj < W; ++jj) z = fmaf(cw[W - 1 - jj], xrow((codes >> (8 * (jj - 1))) & 255), z);
+        const float xt = d.silu ? silu_f32(z) : z;
+        const float dt =
+            softplus_f32((dt_lds ? s_dt[v * nh + hh - h_lo] : load_in(dtr, (int64_t)v * H + hh)) + dtb);
+        s_xt[v * kFCh + ch] = xt;
+        *reinterpret_cast<float2*>(&scf[(v * kFCh / 2 + ch / 2) * 4 + (ch & 1) * 2]) =
+            make_float2(expf(dt * Ah), dt * xt);
+      }
+    }
+    __syncthreads();  // B
+    issue(nblk, L);
+
+    // ---- the walk (each wave on its own; no barriers) ----
+    const TIn *Bg, *Cg, *Bn, *Cn;
+    group_rows(blk, Bg, Cg);
+    group_rows(nblk, Bn, Cn);
+    // rows of node v + 4: this block's (clamped to T - 1), or past T4 the
+    // next block's first four (so that its walk starts with them in place)
+    auto fetch = [&](int v, SegRow<TIn, NS>& br, SegRow<TIn, NS>& cr) __attribute__((always_inline)) {
+      const bool nx = v >= T4;
+      const int r = nx ? v - T4 : (v < T ? v : T - 1);
+      const int rr = r < T ? r : T - 1;
+      br.load((nx ? Bn : Bg) + (int64_t)rr * G * N);
+      cr.load((nx ? Cn : Cg) + (int64_t)rr * G * N);
+    };
+    int cur = -1;  // the parent whose state is in hp (-1: the root state)
+    auto step = [&](int v, SegRow<TIn, NS>& br, SegRow<TIn, NS>& cr) __attribute__((always_inline)) {
+      const int w = __builtin_amdgcn_readlane(word, v);
+      const int p = (w & 0xFF) - 1;
+      if (p != cur) {
+        if (!over) {
+          // the parent comes off the front of the queue
+          const int ps = ((__builtin_amdgcn_readlane(word, p) >> 8) & 0xFF) - 1;
+#pragma unroll
+          for (int j = 0; j < E / EV; ++j) {
+            if constexpr (EV == 4) {
+              const float4 t = *reinterpret_cast<const float4*>(slot_ptr(ps, j));
+              hp[4 * j] = t.x; hp[4 * j + 1] = t.y; hp[4 * j + 2] = t.z; hp[4 * j + 3] = t.w;
+            } else {
+              const float2 t = *reinterpret_cast<const float2*>(slot_ptr(ps, j));
+              hp[2 * j] = t.x; hp[2 * j + 1] = t.y;
+            }
+          }
+        } else {
+          // rebuild the parent's state from the root along its path
+          const float* h0p = reinterpret_cast<const float*>(a.state) + (unit * DI + c0 + 2 * pair) * (int64_t)N + s * NS;
+          load_state_seg<NS>(h0p, hp);
+          load_state_seg<NS>(h0p + N, hp + NS);
+          for (int k = 0; k < s_depth[p]; ++k) {
+            const int u = s_path[p * kMaxNodes + k];
+            const float4 su = s_sc[u * kFCh / 2 + pair];
+            SegRow<TIn, NS> bu;
+            bu.load(Bg + (int64_t)u * G * N);
+#pragma unroll
+            for (int i = 0; i < NS; ++i) {
+              hp[i] = fmaf(su.x, hp[i], su.y * bu.get(i));
+              hp[NS + i] = fmaf(su.z, hp[NS + i], su.w * bu.get(i));
+            }
+          }
+          __builtin_amdgcn_s_waitcnt(kFifoWaitVm0);  // no load of hp left in flight past this branch
+        }
+        cur = p;
+      }
+      const float4 sv = s_sc[v * kFCh / 2 + pair];
+      float hv[E];
+      float pa = 0.0f, pb = 0.0f;
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
+        const float bi_ = br.get(i), ci = cr.get(i);
+        hv[i] = fmaf(sv.x, hp[i], sv.y * bi_);
+        pa = fmaf(ci, hv[i], pa);
+        hv[NS + i] = fmaf(sv.z, hp[NS + i], sv.w * bi_);
+        pb = fmaf(ci, hv[NS + i], pb);
+      }
+      fetch(v + 4, br, cr);
+      // queue the child's state when it has children of its own
+      const int slot = ((w >> 8) & 0xFF) - 1;
+      if (!over && slot >= 0) {
 #pragma unroll
         for (int j = 0; j < E / EV; ++j) {
-          if constexpr (EV == 4) {
-            const float4 t = *reinterpret_cast<const float4*>(slot_ptr(ps, j));
-            hp[4 * j] = t.x; hp[4 * j + 1] = t.y; hp[4 * j + 2] = t.z; hp[4 * j + 3] = t.w;
-          } else {
-            const float2 t = *reinterpret_cast<const float2*>(slot_ptr(ps, j));
-            hp[2 * j] = t.x; hp[2 * j + 1] = t.y;
-          }
+          if constexpr (EV == 4)
+            *reinterpret_cast<float4*>(slot_ptr(slot, j)) =
+                make_float4(hv[4 * j], hv[4 * j + 1], hv[4 * j + 2], hv[4 * j + 3]);
+          else
+            *reinterpret_cast<float2*>(slot_ptr(slot, j)) = make_float2(hv[2 * j], hv[2 * j + 1]);
         }
-      } else {
-        // rebuild the parent's state from the root along its path
-        load_state_seg<NS>(h0p, hp);
-        load_state_seg<NS>(h0p + N, hp + NS);
-        for (int k = 0; k < s_depth[p]; ++k) {
-          const int u = s_path[p * kMaxNodes + k];
-          const float4 su = s_sc[u * kFCh / 2 + pair];
-          SegRow<TIn, NS> bu;
-          bu.load(Bg + (int64_t)u * G * N);
-#pragma unroll
-          for (int i = 0; i < NS; ++i) {
-            hp[i] = fmaf(su.x, hp[i], su.y * bu.get(i));
-            hp[NS + i] = fmaf(su.z, hp[NS + i], su.w * bu.get(i));
-          }
-        }
-        __builtin_amdgcn_s_waitcnt(kFifoWaitVm0);  // no load of hp left in flight past this branch
       }
-      cur = p;
+      pa = row16_sum(pa);
+      pb = row16_sum(pb);
+      if (s == 0) *reinterpret_cast<float2*>(&s_y[v * kFCh + 2 * pair]) = make_float2(pa, pb);
+    };
+    for (int v = 0; v < T; v += 4) {
+      step(v, b0, cr0);
+      step(v + 1, b1, cr1);
+      step(v + 2, b2, cr2);
+      step(v + 3, b3, cr3);
     }
-    const float4 sv = s_sc[v * kFCh / 2 + pair];
-    float hv[E];
-    float pa = 0.0f, pb = 0.0f;
-#pragma unroll
-    for (int i = 0; i < NS; ++i) {
-      const float bi = br.get(i), ci = cr.get(i);
-      hv[i] = fmaf(sv.x, hp[i], sv.y * bi);
-      pa = fmaf(ci, hv[i], pa);
-      hv[NS + i] = fmaf(sv.z, hp[NS + i], sv.w * bi);
-      pb = fmaf(ci, hv[NS + i], pb);
-    }
-    fetch(v + 4, br, cr);
-    // queue the child's state when it has children of its own
-    const int slot = ((w >> 8) & 0xFF) - 1;
-    if (!over && slot >= 0) {
-#pragma unroll
-      for (int j = 0; j < E / EV; ++j) {
-        if constexpr (EV == 4)
-          *reinterpret_cast<float4*>(slot_ptr(slot, j)) = make_float4(hv[4 * j], hv[4 * j + 1], hv[4 * j + 2], hv[4 * j + 3]);
-        else
-          *reinterpret_cast<float2*>(slot_ptr(slot, j)) = make_float2(hv[2 * j], hv[2 * j + 1]);
-      }
-    }
-    pa = row16_sum(pa);
-    pb = row16_sum(pb);
-    if (s == 0) *reinterpret_cast<float2*>(&s_y[v * kFCh + 2 * pair]) = make_float2(pa, pb);
-  };
-  // the root state and the first rows have landed long ago: wait for them
-  // here, so that the loop's waits count only its own prefetches
-  __builtin_amdgcn_s_waitcnt(kFifoWaitVm0);
-  for (int v = 0; v < T; v += 4) {
-    step(v, b0, cr0);
-    step(v + 1, b1, cr1);
-    step(v + 2, b2, cr2);
-    step(v + 3, b3, cr3);
-  }
-  __syncthreads();
+    __syncthreads();  // C
 
-  // ---- y = C . h + D x~, whole row segments ----
-  for (int i = tid; i < T * kFCh; i += kFWaves * kWave)  // channel i % 32 = ch
-    yo[(int64_t)(i / kFCh) * DI + ch] = fmaf(Dh, s_xt[i], s_y[i]);
+    // ---- y = C . h + D x~, whole row segments ----
+    float* yo = a.y + unit * T * DI + c0;
+    for (int i = tid; i < T * kFCh; i += kFWaves * kWave)  // channel i % 32 = ch
+      yo[(int64_t)(i / kFCh) * DI + ch] = fmaf(Dh, s_xt[i], s_y[i]);
+  }
 }
 
 namespace {
+
+// blocks of 32 channels per workgroup: up to four, dividing the blocks of
+// a (layer, sequence)
+int fifo_blocks_per_workgroup(int d_in) {
+  const int blocks = d_in / kFCh;
+  for (int c = 4; c > 1; --c)
+    if (blocks % c == 0) return c;
+  return 1;
+}
 
 template <typename TIn, int NS>
 int launch_fifo_t(const VerifyArgs& a, hipStream_t s) {
   const int K = fifo_slots(a.d.T, 2 * NS);
   const size_t lds = (size_t)FifoLds(a.d.T, 2 * NS, K).total;
   if (allow_lds(verify_fifo_kernel<TIn, NS>, lds) != hipSuccess) return SSM_TREE_E_HIP;
-  dim3 grid(a.d.d_in / kFCh, a.d.Bsz, a.d.L);
-  hipLaunchKernelGGL((verify_fifo_kernel<TIn, NS>), grid, dim3(kFWaves * kWave), lds, s, a, K);
+  const int nbk = fifo_blocks_per_workgroup(a.d.d_in);
+  dim3 grid(a.d.d_in / kFCh / nbk, a.d.Bsz, a.d.L);
+  hipLaunchKernelGGL((verify_fifo_kernel<TIn, NS>), grid, dim3(kFWaves * kWave), lds, s, a, K, nbk);
   return hipGetLastError() == hipSuccess ? SSM_TREE_OK : SSM_TREE_E_HIP;
 }
 

@@ -9,7 +9,8 @@
 
 Each runs on every kernel family: the <= 16-node verify and the fused
 round, the 17-64-node matrix-core verifies (one- and two-role), the
-vector-ALU verify (headdim 40, dense and deep trees) and the commit.
+vector-ALU verify (headdim 40, dense and deep trees), the commit, and the
+explicit FIFO walk.
 
 Where the oracle is finite the comparison is
 
@@ -181,8 +182,8 @@ def scales(cfg, inp, l, b, nxt=None):
     return y_s, s_s, yn_s
 
 
-def run_verify_commit(cfg, inp):
-    case = GpuCase(cfg, inp=inp)
+def run_verify(cfg, inp, fifo=False):
+    case = GpuCase(cfg, inp=inp, fifo=fifo)
     units = [(l, b) for l in range(cfg.L) for b in range(cfg.Bsz)]
     sc = {lb: scales(cfg, inp, *lb) for lb in units}
     y, st = case.verify()
@@ -191,6 +192,11 @@ def run_verify_commit(cfg, inp):
     for (l, b), (yr, rc, _) in ref.items():
         assert stn[b] == rc == 0, ("status", b, stn[b], rc)
         assert_match(y[l, b].double().cpu().numpy(), yr, "%s y[l=%d,b=%d]" % (cfg.name, l, b), sc[l, b][0])
+    return case, units, sc
+
+
+def run_verify_commit(cfg, inp):
+    case, units, sc = run_verify(cfg, inp)
     s_out, w_out, st2 = case.commit()
     ref = case.oracle_commit(units)
     stn = st2.cpu().numpy()
@@ -256,3 +262,18 @@ def test_edges_round(name, case):
     cfg, prev, nxt = _inputs(name, case, cid)
     log("edges round %s %s" % (name, case))
     run_round(cfg, prev, nxt)
+
+
+# the explicit FIFO walk (SSM_TREE_VERIFY_FIFO) at the same edges: trees of
+# 16 nodes (queue in LDS) and 40 nodes (queue, or the replay fallback), and
+# deep chains and stars
+FIFO_SHAPES = ["mfma16", "tt40", "valu40"]
+
+
+@pytest.mark.parametrize("case", CASES)
+@pytest.mark.parametrize("name", FIFO_SHAPES)
+def test_edges_fifo_verify(name, case):
+    cid = 700 + 10 * list(SHAPES).index(name) + CASES.index(case)
+    cfg, prev, _ = _inputs(name, case, cid)
+    log("edges fifo verify %s %s" % (name, case))
+    run_verify(cfg, prev, fifo=True)
