@@ -32,7 +32,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0
 METRIC = "verified tree-node-layers/sec (Mamba2-2.7B SSM, 16-node tree); % HBM peak"
 CSRC = "mamba2_tree_verification_amd/csrc/"
-KERNELS = ("verify", "commit", "commit_verify")
+KERNELS = ("verify", "commit", "commit_verify", "verify_fifo")
 
 
 def verify_source(cfg):
@@ -55,6 +55,8 @@ def kernel_sources(kernel, cfg):
     """Source files whose change invalidates a recorded traffic figure."""
     if kernel == "verify":
         files = [verify_source(cfg)]
+    elif kernel == "verify_fifo":
+        files = [CSRC + "verify_fifo.hip"]
     elif kernel == "commit":
         files = [CSRC + "commit.hip"]
     elif cfg.T <= 16 and cfg.P % 16 == 0:
@@ -73,8 +75,8 @@ def _last_template_arg(name):
 
 def kernel_family(name):
     """Which call a dispatched kernel belongs to: verify, commit,
-    commit_verify (the round), copy (the plain coalesced copy probe), or
-    None.  The round's kernel with nothing to commit (last template argument
+    commit_verify (the round), verify_fifo (the FIFO walk), copy (the plain
+    coalesced copy probe), or None.  The round's kernel with nothing to commit (last template argument
     true) serves ssm_tree_verify on trees of at most 16 nodes; the
     role-split verify with the commit (last argument true) is the round of
     17-64-node trees."""
@@ -88,6 +90,8 @@ def kernel_family(name):
         return "verify"
     if "::commit_kernel" in name:
         return "commit"
+    if "verify_fifo_kernel<" in name:
+        return "verify_fifo"
     return None
 
 
@@ -865,6 +869,14 @@ def main(argv=None):
     else:
         engine, vpeak, xflops = "valu fp32", 78.6, vflops
     vach = xflops / (avg(ver_ms) * 1e-3) / 1e12
+    # the FIFO walk forms every child state: per (state element, node) the
+    # update dA h_parent + (dt x~) B (a multiply and a fused multiply-add)
+    # and the term of C . h (a fused multiply-add), 5 flop, on the vector ALU
+    # without packed fp32 (78.6 TFLOP/s)
+    fflops = 5 * cfg.L * cfg.Bsz * cfg.T * cfg.H * cfg.P * cfg.N
+    fach = fflops / (avg(fifo_ms) * 1e-3) / 1e12
+    fcompute = {"engine": "valu fp32", "flops": fflops, "achieved": round(fach, 2), "peak": 78.6,
+                "unit": "TFLOP/s", "frac": round(fach / 78.6, 4)}
     vcompute = {"engine": engine, "flops": xflops, "achieved": round(vach, 2),
                 "peak": vpeak, "unit": "TFLOP/s", "frac": round(vach / vpeak, 4)}
 
@@ -878,8 +890,10 @@ def main(argv=None):
             "commit": dict(ms=round(avg(com_ms), 4), ms_min=round(min(com_ms), 4), bytes=ab["commit"],
                            roofline=roof("commit", ab["commit"], avg(com_ms)), note="not in the step"),
             "verify_fifo_walk": dict(ms=round(avg(fifo_ms), 4), bytes=ab["verify"],
-                                     note="SSM_TREE_VERIFY_FIFO: the page's FIFO walk kept as a correctness "
-                                          "reference of the walk; no performance claim; not in the step")}
+                                     roofline=roof("verify_fifo", ab["verify"], avg(fifo_ms)), compute=fcompute,
+                                     note="SSM_TREE_VERIFY_FIFO: the page's breadth-first walk with a FIFO of "
+                                          "live states, every child state formed on the vector ALU; not in the "
+                                          "step")}
     rec = {
         "metric": METRIC,
         "value": round(node_layers / (ms_per_step * 1e-3), 1),
