@@ -10,6 +10,11 @@ flag names), contiguity and element counts against the dims, raising
 ``ValueError`` before the library is called, pass ``data_ptr()`` and the
 current HIP stream, and raise ``SsmTreeError`` on a nonzero return.  Every step of the
 computation runs in the HIP kernels; there is no CPU fallback.
+
+Debug mode: with ``SSM_TREE_DEBUG=1`` in the environment the helpers also
+wait for the call to finish and raise ``SsmTreeError`` when a per-sequence
+status they were given is not OK (an invalid tree or accepted path), naming
+the first such sequence.  Without it, statuses are left to the caller.
 """
 from __future__ import annotations
 
@@ -212,6 +217,25 @@ def _check_call(dims: Dims, params: Params, items) -> None:
                 raise ValueError("params.%s: %d elements, the dims imply %d" % (name, n, want[size]))
 
 
+def _debug() -> bool:
+    return os.environ.get("SSM_TREE_DEBUG", "") not in ("", "0")
+
+
+def _check_statuses(where: str, statuses) -> None:
+    """Debug mode: wait for the call and raise on the first sequence whose
+    status is not OK."""
+    import torch
+    for name, t in statuses:
+        if t is None:
+            continue
+        if t.is_cuda:
+            torch.cuda.synchronize(t.device)
+        bad = (t.cpu() != OK).nonzero()
+        if len(bad):
+            i = int(bad[0])
+            raise SsmTreeError(int(t.cpu()[i]), "%s (%s of sequence %d)" % (where, name, i))
+
+
 def verify(dims: Dims, params: Params, parent, x, B, C, dt_raw, conv_window, state, y, seq_status=None,
            stream=None, z=None):
     """ssm_tree_verify; z (optional) gates y by silu(z)."""
@@ -224,6 +248,8 @@ def verify(dims: Dims, params: Params, parent, x, B, C, dt_raw, conv_window, sta
                          _ptr(conv_window), _ptr(state), _ptr(y), _ptr(seq_status), _stream(stream))
     if rc != OK:
         raise SsmTreeError(rc, "ssm_tree_verify")
+    if _debug():
+        _check_statuses("ssm_tree_verify", (("seq_status", seq_status),))
 
 
 def commit(dims: Dims, params: Params, parent, path, path_len, x, B, dt_raw, conv_window_in, state_in,
@@ -241,6 +267,8 @@ def commit(dims: Dims, params: Params, parent, path, path_len, x, B, dt_raw, con
                          _ptr(state_out), _ptr(seq_status), _stream(stream))
     if rc != OK:
         raise SsmTreeError(rc, "ssm_tree_commit")
+    if _debug():
+        _check_statuses("ssm_tree_commit", (("seq_status", seq_status),))
 
 
 def commit_verify(dims: Dims, params: Params, parent_prev, path, path_len, x_prev, B_prev, dt_raw_prev,
@@ -267,6 +295,8 @@ def commit_verify(dims: Dims, params: Params, parent_prev, path, path_len, x_pre
                                 _ptr(verify_status), _stream(stream))
     if rc != OK:
         raise SsmTreeError(rc, "ssm_tree_commit_verify")
+    if _debug():
+        _check_statuses("ssm_tree_commit_verify", (("commit_status", commit_status), ("verify_status", verify_status)))
 
 
 def plan(dims: Dims, parent, plan_out, stream=None):

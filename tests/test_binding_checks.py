@@ -1,7 +1,9 @@
 """The torch helpers refuse, before the library is called, tensors whose
 dtype or element count does not match the dims (CPU only: the device check
 is bypassed so that host tensors stand in for device ones, and every call
-here fails on a check before any pointer is used)."""
+here fails on a check before any pointer is used).  Debug mode
+(SSM_TREE_DEBUG=1) is checked with the entry points replaced by stubs that
+return OK."""
 import pytest
 
 torch = pytest.importorskip("torch")
@@ -141,3 +143,33 @@ def test_plan_sizes():
     with pytest.raises(ValueError, match="parent"):
         m.plan(d, torch.zeros(BSZ, T - 1, dtype=torch.int32),
                torch.zeros(BSZ * (m.PLAN_HEADER + T * m.PLAN_STRIDE), dtype=torch.int32))
+
+
+def _returns_ok(*a, **k):
+    return m.OK
+
+
+def test_debug_mode_raises_on_a_failed_sequence(monkeypatch):
+    """SSM_TREE_DEBUG=1: a call that returns OK but leaves a sequence's
+    status at E_TREE raises and names that sequence; without it the status is
+    left to the caller."""
+    monkeypatch.setattr(m, "ssm_tree_verify", _returns_ok)
+    monkeypatch.setattr(m, "ssm_tree_commit_verify", _returns_ok)
+    monkeypatch.setattr(m, "_stream", lambda s: 0)
+    t = inputs()
+    t["status"][1] = m.E_TREE
+    monkeypatch.delenv("SSM_TREE_DEBUG", raising=False)
+    call_verify(dims(), t)
+    monkeypatch.setenv("SSM_TREE_DEBUG", "1")
+    with pytest.raises(m.SsmTreeError, match="sequence 1") as e:
+        call_verify(dims(), t)
+    assert e.value.code == m.E_TREE
+    t["status"][1] = m.OK
+    call_verify(dims(), t)
+    # the round: either status names the sequence
+    st2 = torch.zeros(BSZ, dtype=torch.int32)
+    st2[2] = m.E_PATH
+    with pytest.raises(m.SsmTreeError, match="commit_status of sequence 2"):
+        m.commit_verify(dims(), params(t), t["parent"], t["path"], t["path_len"], t["x"], t["B"], t["dt_raw"],
+                        t["window"], t["state"], t["window"], t["state"], t["parent"], t["x"], t["B"], t["C"],
+                        t["dt_raw"], t["y"], st2, t["status"])
