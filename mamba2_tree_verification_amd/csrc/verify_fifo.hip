@@ -92,9 +92,11 @@ __device__ __forceinline__ void load_state_seg(const float* p, float* out) {
   }
 }
 
+// v from another lane of the row; with 0 (the identity of the sum) as the
+// old value the compiler folds the move into the add that takes it
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
 
 // sum over the 16 lanes of a DPP row; every lane of the row gets it
