@@ -61,6 +61,25 @@ def test_fifo_small_random(spec):
     check_verify(case, y, st, [(l, b) for l in range(L) for b in range(Bsz)])
 
 
+# instances the small set leaves out: float32 inputs at d_state 256 (the
+# widest lane segment), 32 and 64
+FIFO_F32 = [
+    # L, Bsz, T, H, P, N, G, W, bf16, silu, bias, tree
+    (1, 2, 24, 2, 64, 256, 1, 4, False, True, False, "forest"),
+    (2, 2, 16, 4, 32, 32, 2, 3, False, False, True, "forest"),
+    (1, 3, 40, 2, 64, 64, 1, 4, False, False, False, "chain_or_star"),
+]
+
+
+@pytest.mark.parametrize("spec", FIFO_F32, ids=lambda s: "T%dN%dP%d" % (s[2], s[5], s[4]))
+def test_fifo_float32_instances(spec):
+    L, Bsz, T, H, P, N, G, W, bf16, silu, bias, tree = spec
+    cfg = C.Config(60 + FIFO_F32.index(spec), "small", L, Bsz, T, H, P, N, G, W, bf16, 0.5, tree, silu, bias)
+    case = GpuCase(cfg, fifo=True)
+    y, st = case.verify()
+    check_verify(case, y, st, [(l, b) for l in range(L) for b in range(Bsz)])
+
+
 def _wide_tree(n_internal, fanout):
     """Root with n_internal internal children, each with `fanout` leaves:
     every internal child is queued before the first is expanded, so the
