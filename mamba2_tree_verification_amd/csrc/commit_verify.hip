@@ -3,7 +3,9 @@
 //
 // Per (layer, sequence): the root state is read once, advanced along the
 // accepted path of the previous tree (SpecMamba page sec. 3.1: recompute
-// from the stored per-token dt, B and x), written once, and the next
+// from the stored per-token dt, B and x; the replay in closed form, a
+// decayed state plus rank-4 updates on the matrix cores), written once,
+// and the next
 // tree's outputs are formed from the new state while it is still in
 // registers (the root projection of verify.hip:
 //   y_v = a_v (C_v . h) + sum_{u on path(v)} M[v][u] x~_u).
@@ -672,21 +674,37 @@ __global__ void __launch_bounds__(kCvWaves * kWave)
     f32x4 hq[NG];
 #pragma unroll
     for (int gg = 0; gg < NG; ++gg) hq[gg] = SQ::to_f32(hraw[gg]);
-    for (int q = 0; q < (VO ? 0 : len); ++q) {
-      const float dA = s_dAp[s_path[q] * 4 + hh];
-      const float cx = s_dtx[q * kCvRows + row];
-      const TIn* bp = reinterpret_cast<const TIn*>(s_Bp + q * rs);
-      const float* bpt = s_Bpt + q * N + 4 * k;
+    if (!VO && len > 0) {
+      // the replay along the path in closed form: with a_q = exp(dt_q A)
+      // and c_q = a_{q+1} ... a_{len-1},
+      //   h_new = (a_0 ... a_{len-1}) h + sum_q c_q (dt_q x~_q) B_q,
+      // the sum as rank-4 updates on the matrix cores: the state quads are
+      // the accumulator (lane j + 16 k, element t: row 4 k + t of the tile
+      // whose columns are channels), A = the path's B rows (lane j + 16 k
+      // brings B_{s4+k} at the column of row j), B = c_q dt_q x~_q of
+      // channel j.  Lane q < len forms c_q.
+      float cl = 1.0f;
+      for (int i = len - 1; i > lane; --i) cl *= s_dAp[s_path[i] * 4 + hh];
+      const float a_all = __shfl(cl, 0) * s_dAp[s_path[0] * 4 + hh];
 #pragma unroll
-      for (int gg = 0; gg < NG; ++gg) {
-        const f32x4 bq = xbc ? *reinterpret_cast<const f32x4*>(bpt + 16 * gg) : load4<TIn>(bp + colq(gg));
-        // scale in place, then one fused multiply-add: both steps write
-        // the state's own registers (no copy of the state per node)
-        hq[gg] *= dA;
-        hq[gg].x = fmaf(cx, bq.x, hq[gg].x);
-        hq[gg].y = fmaf(cx, bq.y, hq[gg].y);
-        hq[gg].z = fmaf(cx, bq.z, hq[gg].z);
-        hq[gg].w = fmaf(cx, bq.w, hq[gg].w);
+      for (int gg = 0; gg < NG; ++gg) hq[gg] *= a_all;
+      // column of tile row m in quad gg (the state quads' own columns)
+      auto colrow = [&](int gg, int m) {
+        return kWide ? 32 * (gg >> 1) + 8 * (m >> 2) + 4 * (gg & 1) + (m & 3) : 16 * gg + m;
+      };
+      for (int s4 = 0; s4 < len; s4 += 4) {
+        const int q = s4 + k;
+        const bool on = q < len;
+        const float cq = __shfl(cl, q);
+        const float wv = on ? cq * s_dtx[q * kCvRows + row] : 0.0f;
+        const TIn* bp = reinterpret_cast<const TIn*>(s_Bp + (on ? q : 0) * rs);
+        const float* bpt = s_Bpt + (on ? q : 0) * N;
+#pragma unroll
+        for (int gg = 0; gg < NG; ++gg) {
+          const int col = colrow(gg, j);
+          const float av = on ? (xbc ? bpt[col] : load_in(bp, col)) : 0.0f;
+          hq[gg] = mfma4(av, wv, hq[gg]);
+        }
       }
     }
     // the committed state as stored (a bfloat16 state is rounded): the
