@@ -813,9 +813,9 @@ def main(argv=None):
                 out.append(e0.elapsed_time(e1))
         return out
 
-    ver_ms = timed(lambda: m.verify(dims, prm, g.parent, g.x, g.B, g.C, g.dt_raw, window, state, y, st_v))
+    ver_ms = timed(lambda: m.verify(dims, prm, g.parent, g.x, g.B, g.C, g.dt_raw, window, state, y, st_v), reps=11)
     com_ms = timed(lambda: m.commit(dims, prm, g.parent, g.path, g.path_len, g.x, g.B, g.dt_raw, window, state,
-                                    window, state, st_c))
+                                    window, state, st_c), reps=11)
     dims_fifo = m.make_dims(cfg.L, cfg.Bsz, cfg.T, cfg.H, cfg.P, cfg.N, cfg.G, cfg.W, cfg.bf16, cfg.silu, fifo=True)
     fifo_ms = timed(lambda: m.verify(dims_fifo, prm, g.parent, g.x, g.B, g.C, g.dt_raw, window, state, y, st_v),
                     reps=3)
