@@ -331,7 +331,24 @@ __global__ void __launch_bounds__(kCvWaves * kWave)
   auto colq = [&](int gg) { return kWide ? 32 * (gg >> 1) + 8 * k + 4 * (gg & 1) : 16 * gg + 4 * k; };
   const TS* sin = reinterpret_cast<const TS*>(a.state_in) + (unit * DI + c0 + wave * 16 + j) * (int64_t)N;
   typename SQ::Raw hraw[NG];
-  if constexpr (kWide) {
+  // A float32 state moves in whole 128-byte lines: per pair of column groups
+  // p a wave loads its 16 rows with two instructions, lane (8 r + c) taking
+  // the 16-byte chunk c of columns 32 p .. 32 p + 31 of row r (and of row
+  // 8 + r), non-temporal (streamed past the caches) like commit_kernel's.
+  // The quads change to the operand layout through LDS before the commit.
+  // (Half a line per row per instruction, the operand layout, streams the
+  // state about a fifth slower in the round.  Verify only reads the state,
+  // and there the change of layout cost more than it saved.)
+  constexpr bool kCoal = sizeof(TS) == 4 && NG % 2 == 0 && !OPT && !VO;
+  const int lr = lane >> 3, lc = lane & 7;  // row within eight, chunk of the 128-byte line
+  const TS* sinw = reinterpret_cast<const TS*>(a.state_in) + (unit * DI + c0 + wave * 16) * (int64_t)N;
+  if constexpr (kCoal) {
+#pragma unroll
+    for (int pp = 0; pp < NG / 2; ++pp) {
+      hraw[2 * pp] = SQ::load_nt(sinw + lr * N + 32 * pp + 4 * lc);
+      hraw[2 * pp + 1] = SQ::load_nt(sinw + (8 + lr) * N + 32 * pp + 4 * lc);
+    }
+  } else if constexpr (kWide) {
 #pragma unroll
     for (int gp = 0; gp < NG / 2; ++gp) {
       const u32x4* src = reinterpret_cast<const u32x4*>(sin + colq(2 * gp));
@@ -672,8 +689,25 @@ __global__ void __launch_bounds__(kCvWaves * kWave)
     const int row = wave * 16 + j;
     const int hh = (c0 + wave * 16) / P - h_lo;  // the wave's head (P is a multiple of 16)
     f32x4 hq[NG];
+    // the wave's 1 KiB for the state's change of layout: the next tree's and
+    // the path's x rows are dead here (the y staging takes them back after a
+    // barrier), [row 0..15][16-byte chunk 0..3] of one column group
+    f32x4* s_tw = reinterpret_cast<f32x4*>(smem + lo.xn) + wave * 64;
+    if constexpr (kCoal) {
 #pragma unroll
-    for (int gg = 0; gg < NG; ++gg) hq[gg] = SQ::to_f32(hraw[gg]);
+      for (int gg = 0; gg < NG; ++gg) {
+        if ((lc >> 2) == (gg & 1)) {
+          s_tw[lr * 4 + (lc & 3)] = hraw[gg & ~1];
+          s_tw[(8 + lr) * 4 + (lc & 3)] = hraw[gg | 1];
+        }
+        wave_sync();
+        hq[gg] = s_tw[j * 4 + k];
+        wave_sync();
+      }
+    } else {
+#pragma unroll
+      for (int gg = 0; gg < NG; ++gg) hq[gg] = SQ::to_f32(hraw[gg]);
+    }
     if (!VO && len > 0) {
       // the replay along the path in closed form: with a_q = exp(dt_q A)
       // and c_q = a_{q+1} ... a_{len-1},
@@ -716,7 +750,26 @@ __global__ void __launch_bounds__(kCvWaves * kWave)
     }
     if (!VO && (!OPT || a.state_out)) {
       TS* so = reinterpret_cast<TS*>(a.state_out) + (unit * DI + c0 + row) * (int64_t)N;
-      if constexpr (kWide) {
+      if constexpr (kCoal) {
+        // back to whole lines through the same LDS, non-temporal
+        TS* sow = reinterpret_cast<TS*>(a.state_out) + (unit * DI + c0 + wave * 16) * (int64_t)N;
+#pragma unroll
+        for (int pp = 0; pp < NG / 2; ++pp) {
+          f32x4 oa = f32x4{0.f, 0.f, 0.f, 0.f}, ob = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int hs = 0; hs < 2; ++hs) {
+            s_tw[j * 4 + k] = hq[2 * pp + hs];
+            wave_sync();
+            if ((lc >> 2) == hs) {
+              oa = s_tw[lr * 4 + (lc & 3)];
+              ob = s_tw[(8 + lr) * 4 + (lc & 3)];
+            }
+            wave_sync();
+          }
+          SQ::store_nt(sow + lr * N + 32 * pp + 4 * lc, oa);
+          SQ::store_nt(sow + (8 + lr) * N + 32 * pp + 4 * lc, ob);
+        }
+      } else if constexpr (kWide) {
 #pragma unroll
         for (int gp = 0; gp < NG / 2; ++gp)
           *reinterpret_cast<u32x4*>(so + colq(2 * gp)) =
@@ -890,6 +943,7 @@ __global__ void __launch_bounds__(kCvWaves * kWave)
       }
     }
     const bool tree_ok = s_misc[2] != 0;
+    if constexpr (kCoal) __syncthreads();  // every wave is done with its layout buffer
     // lane (c + 16 k) holds nodes 4 k + r of channel row
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
