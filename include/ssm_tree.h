@@ -75,7 +75,13 @@ extern "C" {
  * up to 64 at 64 nodes, 128 up to 48 nodes, 256 up to 32 nodes); not with
  * SSM_TREE_VERIFY_FIFO; and by
  * ssm_tree_commit for every supported shape.  Other combinations return
- * SSM_TREE_E_DIMS before anything is enqueued. */
+ * SSM_TREE_E_DIMS before anything is enqueued.
+ * On trees of 1 to 16 nodes ssm_tree_verify and ssm_tree_commit_verify
+ * first convolve each sequence's B and C rows once, into a workspace of
+ * L*Bsz*G*T*3*N float32 values that the library takes in stream order
+ * from a memory pool of its own on the stream's device and releases, in
+ * stream order, after the kernels that read it (SSM_TREE_E_HIP if that
+ * allocation fails). */
 #define SSM_TREE_CONV_XBC 4
 /* ssm_tree_verify computes every child state explicitly, walking the tree
  * breadth-first with a FIFO of live states (SpecMamba page sec. 3.2), instead

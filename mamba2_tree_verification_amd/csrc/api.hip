@@ -3,6 +3,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "common.h"
 
 namespace ssmt {
@@ -14,6 +16,7 @@ bool verify_options_supported(const Dims& d, bool gate, bool bf16);
 bool commit_options_supported(const Dims& d);
 bool commit_verify_options_supported(const Dims& d, bool gate);
 int launch_commit_verify(const CommitVerifyArgs& a, bool bf16, hipStream_t s);
+size_t bc_workspace_bytes(const Dims& d);
 bool tt_round_applies(const Dims& d, bool bf16, bool gate);
 int launch_tt_round(const CommitVerifyArgs& a, hipStream_t s);
 hipError_t launch_plan(const int32_t* parent, int Bsz, int T, int W, int32_t* out, hipStream_t s);
@@ -43,6 +46,53 @@ Range range_of(const void* p, int64_t bytes) {
 bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.hi > a.lo && b.hi > b.lo; }
 
 bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+// The convolved B and C rows of the xBC conv (trees of up to 16 nodes) live
+// in a workspace taken in stream order from a memory pool of the library's
+// own, one per device: it is allocated on the caller's stream before the
+// kernels and released after them, so calls on different streams never
+// share one, and the pool keeps its memory for the next call instead of
+// returning it to the device at each synchronisation.
+constexpr int kMaxDevices = 64;
+
+hipMemPool_t workspace_pool(hipStream_t s) {
+  int dev = -1;
+  if ((s ? hipStreamGetDevice(s, &dev) : hipGetDevice(&dev)) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return nullptr;
+  static std::mutex m;
+  static hipMemPool_t pools[kMaxDevices] = {};
+  std::lock_guard<std::mutex> lock(m);
+  if (!pools[dev]) {
+    hipMemPoolProps p;
+    memset(&p, 0, sizeof(p));
+    p.allocType = hipMemAllocationTypePinned;
+    p.location.type = hipMemLocationTypeDevice;
+    p.location.id = dev;
+    hipMemPool_t pool = nullptr;
+    if (hipMemPoolCreate(&pool, &p) != hipSuccess) return nullptr;
+    uint64_t keep = UINT64_MAX;
+    if (hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep) != hipSuccess) {
+      hipMemPoolDestroy(pool);
+      return nullptr;
+    }
+    pools[dev] = pool;
+  }
+  return pools[dev];
+}
+
+// the fused round's kernels, with the xBC conv's workspace when it needs one
+int run_fused(CommitVerifyArgs& a, bool bf16, hipStream_t s) {
+  const size_t bytes = bc_workspace_bytes(a.d);
+  if (!bytes) return launch_commit_verify(a, bf16, s);
+  hipMemPool_t pool = workspace_pool(s);
+  void* ws = nullptr;
+  if (!pool || hipMallocFromPoolAsync(&ws, bytes, pool, s) != hipSuccess) return SSM_TREE_E_HIP;
+  a.bcw = static_cast<float*>(ws);
+  const int st = launch_commit_verify(a, bf16, s);
+  // released in stream order, after the kernels that read it
+  if (hipFreeAsync(ws, s) != hipSuccess && st == SSM_TREE_OK) return SSM_TREE_E_HIP;
+  return st;
+}
 
 int check_dims(const ssm_tree_dims* dm, Dims* out) {
   if (!dm) return SSM_TREE_E_NULL;
@@ -158,7 +208,7 @@ int ssm_tree_verify(const ssm_tree_dims* dims, const ssm_tree_params* params, co
     a.z = z;
     a.y = y;
     a.verify_status = seq_status;
-    return launch_commit_verify(a, dims->in_dtype == SSM_TREE_BF16, s);
+    return run_fused(a, dims->in_dtype == SSM_TREE_BF16, s);
   }
   VerifyArgs a;
   a.d = d;
@@ -301,6 +351,7 @@ int ssm_tree_commit_verify(const ssm_tree_dims* dims, const ssm_tree_params* par
   hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
   const bool bf16 = dims->in_dtype == SSM_TREE_BF16;
   CommitVerifyArgs a;
+  memset(&a, 0, sizeof(a));
   a.d = d;
   a.prm = Params{params->A, params->D, params->dt_bias, params->conv_w, params->conv_b};
   a.parent_prev = parent_prev;
@@ -323,7 +374,7 @@ int ssm_tree_commit_verify(const ssm_tree_dims* dims, const ssm_tree_params* par
   a.y = y;
   a.commit_status = commit_status;
   a.verify_status = verify_status;
-  if (fused) return launch_commit_verify(a, bf16, s);
+  if (fused) return run_fused(a, bf16, s);
   // trees of 17-64 nodes: one launch where the role-split verify applies
   // (E_DIMS from it: nothing was launched)
   if (kTtRound && tt_round_applies(d, bf16, z != nullptr)) {

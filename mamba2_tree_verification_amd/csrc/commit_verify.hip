@@ -50,6 +50,7 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kCvRows = 64;   // channels per workgroup
 constexpr int kCvWaves = 4;
 constexpr int kCvT = 16;      // node capacity
+constexpr int kBcThreads = 256;  // bc_conv_kernel
 constexpr int kRowPad = 16;   // bytes of padding per staged B / C row (LDS banks)
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -104,7 +105,7 @@ struct CvLds {
   int pparent, path, parent, misc, anc, cidx, dAp, dtp, dt, S, Sd, av, Mt, D, cbt, cw, cb, win, xn, xp, ys, C, B, dtx,
       Bp, xt, total, row;
   // the options' own arrays (offset 0 when unused)
-  int z, cwbc, cbbc, winbc, Cp, Bpt;
+  int z, Bpt;
   // vo: verify only (nothing committed: no previous tree's rows)
   __host__ __device__ CvLds(int N, int E, int P, bool xbc = false, bool gate = false, bool vo = false) {
     int o = 0;
@@ -138,17 +139,16 @@ struct CvLds {
     o += kCvT * row > 4 * kCvT * kCvRows ? kCvT * row : 4 * kCvT * kCvRows;
     Bp = o; o += vo ? 0 : kCvT * row;         // previous tree B rows of the path nodes (raw, padded)
     xt = o; o += 4 * kCvRows * kCvT;          // next tree conv outputs, MFMA B-operand layout
-    z = cwbc = cbbc = winbc = Cp = Bpt = 0;
+    z = Bpt = 0;
     if (gate) { z = o; o += kCvT * kCvRows * E; }          // gate input rows (raw)
     if (xbc) {
-      dtx = o; o += 4 * kCvT * kCvRows;       // the raw B rows stay live: dt * x~ gets its own space
-      cwbc = o; o += 4 * 4 * 2 * N;           // conv weights of the group's B then C channels, by taps back
-      cbbc = o; o += 4 * 2 * N;               // their bias
-      winbc = o; o += align16(3 * 2 * N * E); // old window rows of those channels (raw)
-      Cp = o; o += kCvT * row;                // previous tree C rows of the path nodes (raw, padded)
-      Bpt = o; o += 4 * kCvT * N;             // convolved B rows of the path nodes, fp32
-      // (the next tree's convolved B and C rows are formed in registers by
-      // the lanes that take them, from the raw rows, which stay live)
+      // The raw B and C rows of both trees are not read (the next tree's
+      // convolved rows go from the workspace to the registers of the lanes
+      // that take them): dt * x~ takes the C rows' place, and the path's
+      // convolved B rows (fp32, from the workspace) follow it over the B
+      // and Bp rows, which always have room for them.
+      dtx = C;
+      Bpt = C + 4 * kCvT * kCvRows;
     }
     total = o;
   }
@@ -171,10 +171,11 @@ __device__ __forceinline__ bool finite4(f32x4 v) {
 // VO: verify only (ssm_tree_verify): no previous tree, nothing committed,
 // no state or window written.
 // (verify only with bf16 inputs holds 7 waves per SIMD: its LDS leaves room
-// for 7 workgroups per CU)
+// for 7 workgroups per CU; the options' instance with bf16 inputs and
+// d_state 128 is held to 6, which its registers allow without spilling)
 template <typename TIn, typename TS, int NG, bool OPT, bool VO>
 __global__ void __launch_bounds__(kCvWaves * kWave)
-    __attribute__((amdgpu_waves_per_eu(VO && sizeof(TIn) == 2 && NG <= 8 ? 7 : 1))) commit_verify_kernel(CommitVerifyArgs a) {
+    __attribute__((amdgpu_waves_per_eu(VO && sizeof(TIn) == 2 && NG <= 8 ? 7 : (OPT && sizeof(TIn) == 2 && NG == 8 ? 6 : 1)))) commit_verify_kernel(CommitVerifyArgs a) {
   typedef StateQuad<TS> SQ;
   constexpr int N = 16 * NG;
   constexpr int E = (int)sizeof(TIn);
@@ -225,11 +226,11 @@ __global__ void __launch_bounds__(kCvWaves * kWave)
   float* s_xt = reinterpret_cast<float*>(smem + lo.xt);
   const int rs = lo.row;
   TIn* s_z = reinterpret_cast<TIn*>(smem + lo.z);
-  float* s_cwbc = reinterpret_cast<float*>(smem + lo.cwbc);
-  float* s_cbbc = reinterpret_cast<float*>(smem + lo.cbbc);
-  TIn* s_winbc = reinterpret_cast<TIn*>(smem + lo.winbc);
-  unsigned char* s_Cp = smem + lo.Cp;
   float* s_Bpt = reinterpret_cast<float*>(smem + lo.Bpt);
+  // SSM_TREE_CONV_XBC: the group's convolved rows, [T][2 N] of the next tree
+  // (B then C) and [T][N] of the path, formed ahead of this kernel
+  const float* bcw_n = xbc ? a.bcw + (unit * G + g) * (int64_t)T * 3 * N : nullptr;
+  const float* bcw_p = xbc ? bcw_n + (int64_t)T * 2 * N : nullptr;
 
   // ======== trip 1: everything that does not depend on the path ========
 
@@ -257,7 +258,7 @@ __global__ void __launch_bounds__(kCvWaves * kWave)
 #pragma unroll
   for (int it = 0; it < kCPT; ++it) {
     const int ci = tid + it * kCvWaves * kWave, v = ci / kChunks, q = ci % kChunks;
-    if (v < T) {
+    if (v < T && !xbc) {
       rc[it] = *reinterpret_cast<const u32x4*>(Cg + (int64_t)v * G * N * E + q * 16);
       rb[it] = *reinterpret_cast<const u32x4*>(Bg + (int64_t)v * G * N * E + q * 16);
     }
@@ -291,33 +292,11 @@ __global__ void __launch_bounds__(kCvWaves * kWave)
       if (jj < W) r_cw[jj] = cw[jj];
     if (a.prm.conv_b) r_cb = a.prm.conv_b[(int64_t)l * CH + c0 + lane];
   }
-  // the options: gate rows; the group's B and C conv weights, bias and old
-  // window rows (thread i < 2 N owns channel i: B channels, then C)
+  // the options: gate rows
   RawQ rz{};
-  constexpr int kBcPT = (2 * N + kCvWaves * kWave - 1) / (kCvWaves * kWave);
-  float o_cw[kBcPT][4], o_cb[kBcPT];
-  TIn o_win[kBcPT][3];
   if constexpr (OPT) {
     if (gate && xv < T)
       rz = *reinterpret_cast<const RawQ*>(reinterpret_cast<const TIn*>(a.z) + (unit * T + xv) * DI + c0 + xq);
-    if (xbc) {
-#pragma unroll
-      for (int it = 0; it < kBcPT; ++it) {
-        const int i = tid + it * kCvWaves * kWave;
-        if (i < 2 * N) {
-          const int ch = DI + (i < N ? g * N + i : G * N + g * N + i - N);
-          const float* cw = a.prm.conv_w + ((int64_t)l * CH + ch) * W;
-          // by taps back: o_cw[jj] weighs the input jj steps before the token
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) o_cw[it][jj] = jj < W ? cw[W - 1 - jj] : 0.0f;
-          o_cb[it] = a.prm.conv_b ? a.prm.conv_b[(int64_t)l * CH + ch] : 0.0f;
-          const TIn* wsrc = reinterpret_cast<const TIn*>(a.window_in) + unit * (W - 1) * (int64_t)CH + ch;
-#pragma unroll
-          for (int r = 0; r < 3; ++r)
-            if (r < W - 1) o_win[it][r] = wsrc[(int64_t)r * CH];
-        }
-      }
-    }
   }
 
   // the state last: the small rows above reach LDS while it is still in flight
@@ -375,7 +354,7 @@ __global__ void __launch_bounds__(kCvWaves * kWave)
 #pragma unroll
   for (int it = 0; it < kCPT; ++it) {
     const int ci = tid + it * kCvWaves * kWave, v = ci / kChunks, q = ci % kChunks;
-    if (v < T) {
+    if (v < T && !xbc) {
       *reinterpret_cast<u32x4*>(s_C + v * rs + q * 16) = rc[it];
       *reinterpret_cast<u32x4*>(s_B + v * rs + q * 16) = rb[it];
     }
@@ -402,20 +381,6 @@ __global__ void __launch_bounds__(kCvWaves * kWave)
   }
   if constexpr (OPT) {
     if (gate && xv < T) *reinterpret_cast<RawQ*>(s_z + xv * kCvRows + xq) = rz;
-    if (xbc) {
-#pragma unroll
-      for (int it = 0; it < kBcPT; ++it) {
-        const int i = tid + it * kCvWaves * kWave;
-        if (i < 2 * N) {
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) s_cwbc[i * 4 + jj] = o_cw[it][jj];
-          s_cbbc[i] = o_cb[it];
-#pragma unroll
-          for (int r = 0; r < 3; ++r)
-            if (r < W - 1) s_winbc[r * 2 * N + i] = o_win[it][r];
-        }
-      }
-    }
   }
   __syncthreads();
 
@@ -428,17 +393,26 @@ __global__ void __launch_bounds__(kCvWaves * kWave)
     const int vs = (v >= 0 && v < T) ? v : 0;  // an invalid path is discarded below
     rxp = *reinterpret_cast<const RawQ*>(reinterpret_cast<const TIn*>(a.x_prev) + (unit * T + vs) * DI + c0 + xq);
   }
-  u32x4 rbp[kCPT], rcp[kCPT];
+  u32x4 rbp[kCPT];
   const unsigned char* Bpg = reinterpret_cast<const unsigned char*>(a.B_prev) + ((unit * T) * G + g) * (int64_t)N * E;
-  const unsigned char* Cpg = reinterpret_cast<const unsigned char*>(a.C_prev) + ((unit * T) * G + g) * (int64_t)N * E;
 #pragma unroll
   for (int it = 0; it < kCPT; ++it) {
     const int ci = tid + it * kCvWaves * kWave, q = ci / kChunks, ch = ci % kChunks;
-    if (q < lg) {
+    if (q < lg && !xbc) {
       const int v = s_path[q];
       const int vs = (v >= 0 && v < T) ? v : 0;
       rbp[it] = *reinterpret_cast<const u32x4*>(Bpg + (int64_t)vs * G * N * E + ch * 16);
-      if (xbc) rcp[it] = *reinterpret_cast<const u32x4*>(Cpg + (int64_t)vs * G * N * E + ch * 16);
+    }
+  }
+  // with the xBC conv: the path's convolved B rows (positions past a failed
+  // commit's length 0 are loaded but never read)
+  constexpr int kQPT = (kCvT * N / 4 + kCvWaves * kWave - 1) / (kCvWaves * kWave);
+  f32x4 rbq[OPT ? kQPT : 1];
+  if constexpr (OPT) {
+#pragma unroll
+    for (int it = 0; it < kQPT; ++it) {
+      const int ci = tid + it * kCvWaves * kWave;
+      if (xbc && ci < lg * (N / 4)) rbq[it] = *reinterpret_cast<const f32x4*>(bcw_p + 4 * ci);
     }
   }
 
@@ -575,9 +549,13 @@ __global__ void __launch_bounds__(kCvWaves * kWave)
 #pragma unroll
   for (int it = 0; it < kCPT; ++it) {
     const int ci = tid + it * kCvWaves * kWave, q = ci / kChunks, ch = ci % kChunks;
-    if (q < lg) {
-      *reinterpret_cast<u32x4*>(s_Bp + q * rs + ch * 16) = rbp[it];
-      if (xbc) *reinterpret_cast<u32x4*>(s_Cp + q * rs + ch * 16) = rcp[it];
+    if (q < lg && !xbc) *reinterpret_cast<u32x4*>(s_Bp + q * rs + ch * 16) = rbp[it];
+  }
+  if constexpr (OPT) {
+#pragma unroll
+    for (int it = 0; it < kQPT; ++it) {
+      const int ci = tid + it * kCvWaves * kWave;
+      if (xbc && ci < lg * (N / 4)) *reinterpret_cast<f32x4*>(s_Bpt + 4 * ci) = rbq[it];
     }
   }
   __syncthreads();
@@ -663,24 +641,6 @@ __global__ void __launch_bounds__(kCvWaves * kWave)
     }
     // MFMA B-operand layout: channel row lane, quad v / 4 swizzled
     s_xt[lane * kCvT + 4 * ((v >> 2) ^ ((lane >> 2) & 3)) + (v & 3)] = xt;
-  }
-  if constexpr (OPT) {
-    if (xbc) {
-      // the xBC conv of the group's B channels over the path's nodes, along
-      // (old window rows, path rows); the next tree's B and C rows are
-      // convolved where the products take them
-      for (int i = tid; i < len * N; i += kCvWaves * kWave) {
-        const int k = i / N, n = i % N;
-        float acc = s_cbbc[n];
-        for (int j = 0; j < W; ++j) {  // the input j steps back
-          const int e = k + W - 1 - j;
-          const float u = e < W - 1 ? load_in(s_winbc, e * 2 * N + n)
-                                    : load_in(reinterpret_cast<const TIn*>(s_Bp + (e - (W - 1)) * rs), n);
-          acc = fmaf(s_cwbc[n * 4 + j], u, acc);
-        }
-        s_Bpt[k * N + n] = d.silu ? silu_fast(acc) : acc;
-      }
-    }
   }
   __syncthreads();
 
@@ -784,35 +744,9 @@ __global__ void __launch_bounds__(kCvWaves * kWave)
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
     const bool live = j < T;
     f32x4 cbx = f32x4{0.f, 0.f, 0.f, 0.f};  // with the xBC conv: C_v . B_u, formed below
-    // with the xBC conv, the raw rows that tap jj (steps back) of node j
-    // reads: the node itself, an ancestor, or past the root a row of the
-    // committed window (old window rows, then the path's rows)
-    const unsigned char* tb[4] = {s_B + j * rs, s_B, s_B, s_B};
-    const unsigned char* tc[4] = {s_C + j * rs, s_C, s_C, s_C};
-    if constexpr (OPT) {
-      if (xbc) {
-        const int codes = s_cidx[j];
-#pragma unroll
-        for (int jj = 1; jj < 4; ++jj) {
-          if (jj < W) {
-            const int code = (codes >> (8 * (jj - 1))) & 255;
-            if (code < T) {
-              tb[jj] = s_B + code * rs;
-              tc[jj] = s_C + code * rs;
-            } else {
-              const int e = len + code - T;
-              if (e < W - 1) {
-                tb[jj] = reinterpret_cast<const unsigned char*>(s_winbc) + e * 2 * N * E;
-                tc[jj] = tb[jj] + N * E;
-              } else {
-                tb[jj] = s_Bp + (e - (W - 1)) * rs;
-                tc[jj] = s_Cp + (e - (W - 1)) * rs;
-              }
-            }
-          }
-        }
-      }
-    }
+    // with the xBC conv, node j's convolved B and C rows (node 0's for the
+    // lanes past the tree, whose products are zeroed)
+    const float* bcj = OPT && xbc ? bcw_n + (live ? j : 0) * 2 * N : nullptr;
     // bf16 C rows and a bf16 state are exact bf16 operands: one 16x16x32
     // product per pair of column groups (lane j + 16 k feeds columns
     // 16 gg + 4 k .. + 3 of both groups, the same slots in C and in h)
@@ -837,35 +771,8 @@ __global__ void __launch_bounds__(kCvWaves * kWave)
           if (xbc) {
             // the convolved B and C values of node j, columns n0 .. n0 + 3
             const int n0 = 16 * gg + 4 * k;
-            f32x4 ab = *reinterpret_cast<const f32x4*>(s_cbbc + n0);
-            f32x4 ac = *reinterpret_cast<const f32x4*>(s_cbbc + N + n0);
-            f32x4 wb[4], wc[4];
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-              wb[t] = *reinterpret_cast<const f32x4*>(s_cwbc + (n0 + t) * 4);
-              wc[t] = *reinterpret_cast<const f32x4*>(s_cwbc + (N + n0 + t) * 4);
-            }
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-              if (jj < W) {
-                const f32x4 ub = load4<TIn>(reinterpret_cast<const TIn*>(tb[jj]) + n0);
-                const f32x4 uc = load4<TIn>(reinterpret_cast<const TIn*>(tc[jj]) + n0);
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                  ab[t] = fmaf(wb[t][jj], ub[t], ab[t]);
-                  ac[t] = fmaf(wc[t][jj], uc[t], ac[t]);
-                }
-              }
-            }
-            if (d.silu) {
-#pragma unroll
-              for (int t = 0; t < 4; ++t) {
-                ab[t] = silu_fast(ab[t]);
-                ac[t] = silu_fast(ac[t]);
-              }
-            }
-            cq = ac;
-            bxq = ab;
+            bxq = *reinterpret_cast<const f32x4*>(bcj + n0);
+            cq = *reinterpret_cast<const f32x4*>(bcj + N + n0);
           } else {
             cq = load4<TIn>(reinterpret_cast<const TIn*>(s_C + j * rs) + colq(gg));
           }
@@ -962,6 +869,124 @@ __global__ void __launch_bounds__(kCvWaves * kWave)
   }
 }
 
+// ---------------------------------------------------------------------------
+// SSM_TREE_CONV_XBC: the convolved B and C rows, once per sequence and group
+// ---------------------------------------------------------------------------
+//
+// Every workgroup of a (layer, sequence) needs the same convolved B and C
+// rows of its group (the conv of SSM layers that pass x, B and C through
+// conv1d together, Mamba2).  They are formed here once, in fp32, into the
+// workspace the round then reads:
+//   next tree [T][2N]: node v's B channels (columns 0..N-1) and C channels
+//             (N..2N-1) convolved over v's taps: v itself, its ancestors,
+//             and past the root the rows of the committed window (the old
+//             window's rows, then the accepted path's rows);
+//   path      [T][N]: the accepted path's B channels convolved along (old
+//             window rows, path rows), positions q < len.
+// SiLU follows when set.  The commit length follows the round's own checks
+// (0 when the previous tree or the path is not valid, or with nothing to
+// commit), so the window taps agree with what the round commits.  One
+// workgroup per (group, sequence, layer); each thread owns channels.
+template <typename TIn>
+__global__ void __launch_bounds__(kBcThreads) bc_conv_kernel(CommitVerifyArgs a) {
+  const Dims d = a.d;
+  const int T = d.T, W = d.W, N = d.N, G = d.G, DI = d.d_in, CH = d.CH, GN = G * N;
+  const int g = blockIdx.x, b = blockIdx.y, l = blockIdx.z;
+  const int64_t unit = (int64_t)l * d.Bsz + b;
+  const int tid = threadIdx.x;
+  __shared__ int32_t s_parent[kCvT], s_pparent[kCvT], s_path[kCvT], s_code[kCvT][3], s_len;
+  const bool commit = a.path_len != nullptr;
+  if (tid < T) {
+    s_parent[tid] = a.parent[(int64_t)b * T + tid];
+    s_pparent[tid] = commit ? a.parent_prev[(int64_t)b * T + tid] : -1;
+    s_path[tid] = commit ? a.path[(int64_t)b * T + tid] : 0;
+  }
+  __syncthreads();
+  const bool prev_ok = !commit || tree_is_valid(s_pparent, T);
+  if (tid == 0) {
+    const int len_raw = commit ? a.path_len[b] : 0;
+    bool ok = prev_ok && len_raw >= 0 && len_raw <= T;
+    for (int q = 0; ok && q < len_raw; ++q) {
+      const int v = s_path[q];
+      ok = v >= 0 && v < T && s_pparent[v] == (q == 0 ? -1 : s_path[q - 1]);
+    }
+    s_len = ok ? len_raw : 0;
+  }
+  if (tid < T) {
+    // taps 1..3 of node tid: an ancestor, or past the root T + the row of
+    // the committed window counted from its oldest (a walk that stays in
+    // range on an invalid tree, whose outputs the round discards)
+    int u = tid, depth = 0, an[3] = {-1, -1, -1};
+    for (int s = 0; s < kCvT && u >= 0; ++s) {
+      ++depth;
+      const int p = s_parent[u];
+      u = (p >= 0 && p < u) ? p : -1;
+      if (s < 3) an[s] = u;
+    }
+#pragma unroll
+    for (int jj = 1; jj < 4; ++jj) s_code[tid][jj - 1] = an[jj - 1] >= 0 ? an[jj - 1] : T + (W - 2) - (jj - depth);
+  }
+  __syncthreads();
+  const int len = s_len;
+  const TIn* win = reinterpret_cast<const TIn*>(a.window_in) + unit * (W - 1) * (int64_t)CH + DI;
+  float* out_n = a.bcw + (unit * G + g) * (int64_t)T * 3 * N;
+  float* out_p = out_n + (int64_t)T * 2 * N;
+  // column c < 2 N: B channel c (c < N) or C channel c - N of group g
+  for (int c = tid; c < 2 * N; c += kBcThreads) {
+    const bool isB = c < N;
+    const int n = isB ? c : c - N;
+    const int wch = isB ? g * N + n : GN + g * N + n;  // among the window's B, C channels
+    const float* cw = a.prm.conv_w + ((int64_t)l * CH + DI + wch) * W;
+    float w[4];  // by taps back: w[jj] weighs the input jj steps before the token
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) w[jj] = jj < W ? cw[W - 1 - jj] : 0.0f;
+    const float bias = a.prm.conv_b ? a.prm.conv_b[(int64_t)l * CH + DI + wch] : 0.0f;
+    const TIn* rows = reinterpret_cast<const TIn*>(isB ? a.B : a.C) + (unit * T * G + g) * (int64_t)N + n;
+    const TIn* prow = reinterpret_cast<const TIn*>(isB ? a.B_prev : a.C_prev) + (unit * T * G + g) * (int64_t)N + n;
+    // element e of (old window rows, path rows): the committed window's rows
+    // are elements len .. len + W - 2
+    auto elem = [&](int e) {
+      return e < W - 1 ? load_in(win, (int64_t)e * CH + wch) : load_in(prow, (int64_t)s_path[e - (W - 1)] * GN);
+    };
+    for (int v = 0; v < T; ++v) {
+      float acc = fmaf(w[0], load_in(rows, (int64_t)v * GN), bias);
+#pragma unroll
+      for (int jj = 1; jj < 4; ++jj) {
+        if (jj < W) {
+          const int code = s_code[v][jj - 1];
+          acc = fmaf(w[jj], code < T ? load_in(rows, (int64_t)code * GN) : elem(len + code - T), acc);
+        }
+      }
+      out_n[(int64_t)v * 2 * N + c] = d.silu ? silu_fast(acc) : acc;
+    }
+    if (isB) {
+      for (int q = 0; q < len; ++q) {
+        float acc = bias;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          if (jj < W) acc = fmaf(w[jj], elem(q + W - 1 - jj), acc);
+        out_p[(int64_t)q * N + n] = d.silu ? silu_fast(acc) : acc;
+      }
+    }
+  }
+}
+
+// bytes of the convolved rows a round with SSM_TREE_CONV_XBC on trees of up
+// to 16 nodes needs (0 otherwise)
+size_t bc_workspace_bytes(const Dims& d) {
+  if (!d.xbc || d.T < 1 || d.T > kCvT) return 0;
+  return (size_t)d.L * d.Bsz * d.G * d.T * 3 * d.N * sizeof(float);
+}
+
+hipError_t launch_bc_conv(const CommitVerifyArgs& a, bool bf16, hipStream_t s) {
+  dim3 grid(a.d.G, a.d.Bsz, a.d.L);
+  if (bf16)
+    hipLaunchKernelGGL((bc_conv_kernel<bf16_t>), grid, dim3(kBcThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((bc_conv_kernel<float>), grid, dim3(kBcThreads), 0, s, a);
+  return hipGetLastError();
+}
+
 namespace {
 
 template <typename TIn, typename TS, int NG, bool OPT, bool VO = false>
@@ -969,6 +994,10 @@ int launch_cv_o(const CommitVerifyArgs& a, hipStream_t s) {
   const size_t lds =
       (size_t)CvLds(16 * NG, (int)sizeof(TIn), a.d.P, OPT && a.d.xbc, OPT && a.z != nullptr, VO).total;
   if (allow_lds(commit_verify_kernel<TIn, TS, NG, OPT, VO>, lds) != hipSuccess) return SSM_TREE_E_HIP;
+  if (OPT && a.d.xbc) {  // the convolved B and C rows first
+    if (!a.bcw) return SSM_TREE_E_NULL;
+    if (launch_bc_conv(a, sizeof(TIn) == 2, s) != hipSuccess) return SSM_TREE_E_HIP;
+  }
   dim3 grid(a.d.d_in / kCvRows, a.d.Bsz, a.d.L);
   hipLaunchKernelGGL((commit_verify_kernel<TIn, TS, NG, OPT, VO>), grid, dim3(kCvWaves * kWave), lds, s, a);
   if (hipGetLastError() != hipSuccess) return SSM_TREE_E_HIP;

@@ -191,6 +191,10 @@ struct CommitVerifyArgs {
   float* y;
   int32_t* commit_status;
   int32_t* verify_status;
+  // SSM_TREE_CONV_XBC on trees of up to 16 nodes: the convolved B and C rows,
+  // [L][Bsz][G] blocks of [T][2N] (next tree, B then C) and [T][N] (the
+  // accepted path's B), float32, written by bc_conv_kernel ahead of the round
+  float* bcw;
 };
 
 // Allow a kernel more than the default 64 KiB of dynamic LDS (gfx950 has
