@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define SSM_TREE_ABI_VERSION 3
+#define SSM_TREE_ABI_VERSION 4
 
 /* input element types for x, B, C, dt_raw and the conv window */
 #define SSM_TREE_F32 0
@@ -111,6 +111,7 @@ extern "C" {
 #define SSM_TREE_E_ALIAS (-5)  /* an output overlaps an input (other than an allowed exact in-place) */
 #define SSM_TREE_E_HIP (-6)    /* a HIP launch failed */
 #define SSM_TREE_E_FLAGS (-7)  /* unknown bits in dims.flags */
+#define SSM_TREE_E_SCRATCH (-8) /* ssm_tree_commit_verify_noalloc: the call needs more than its fixed scratch */
 #define SSM_TREE_E_TREE (-10)  /* seq_status: parent[] is not a BFS labelling */
 #define SSM_TREE_E_PATH (-11)  /* seq_status: path is not a root-to-node path of the tree */
 
@@ -233,6 +234,32 @@ int ssm_tree_commit_verify(const ssm_tree_dims* dims, const ssm_tree_params* par
                            const void* state_in, void* conv_window_out, void* state_out, const int32_t* parent,
                            const void* x, const void* B, const void* C, const void* dt_raw, const void* z,
                            float* y, int32_t* commit_status, int32_t* verify_status, void* hip_stream);
+
+/*
+ * ssm_tree_commit_verify_noalloc: ssm_tree_commit_verify for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  Same arguments, outputs, status
+ * codes and kernels; it calls no allocating routine.
+ * The one scratch buffer a round uses, the convolved B and C rows of
+ * SSM_TREE_CONV_XBC on trees of 1 to 16 nodes (L*Bsz*G*T*3*N float32
+ * values), is here a fixed device array of 32 MiB that the library holds on
+ * each device it runs on until the process ends, instead of the stream-
+ * ordered pool allocation ssm_tree_commit_verify makes.  A call that needs
+ * more returns SSM_TREE_E_SCRATCH before anything is enqueued.  Every call
+ * on one device shares that array, which keeps the last call's contents
+ * (nothing needs clearing: a round writes each value it reads first), so
+ * calls that overlap on one device (other streams, other threads) race:
+ * the caller serialises them.  Calls that need no scratch (no
+ * SSM_TREE_CONV_XBC, or more than 16 nodes) behave exactly as
+ * ssm_tree_commit_verify.
+ */
+int ssm_tree_commit_verify_noalloc(const ssm_tree_dims* dims, const ssm_tree_params* params,
+                                   const int32_t* parent_prev, const int32_t* path, const int32_t* path_len,
+                                   const void* x_prev, const void* B_prev, const void* C_prev,
+                                   const void* dt_raw_prev, const void* conv_window_in, const void* state_in,
+                                   void* conv_window_out, void* state_out, const int32_t* parent, const void* x,
+                                   const void* B, const void* C, const void* dt_raw, const void* z, float* y,
+                                   int32_t* commit_status, int32_t* verify_status, void* hip_stream);
 
 /*
  * ssm_tree_plan: the tree plan the kernels derive from parent[] (SpecMamba

@@ -1,7 +1,8 @@
 """Python binding of libssm_tree.so (argument marshalling only).
 
 The functions ``ssm_tree_verify``, ``ssm_tree_commit``,
-``ssm_tree_commit_verify``, ``ssm_tree_plan``, ``ssm_tree_status_string`` and
+``ssm_tree_commit_verify``, ``ssm_tree_commit_verify_noalloc``,
+``ssm_tree_plan``, ``ssm_tree_status_string`` and
 ``ssm_tree_abi_version`` mirror the C ABI in ``include/ssm_tree.h`` one to
 one and take raw device addresses.  The ``verify`` / ``commit`` /
 ``commit_verify`` / ``plan`` helpers accept torch tensors on the GPU,
@@ -25,13 +26,13 @@ import threading
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libssm_tree.so")
 
-SSM_TREE_ABI_VERSION = 3
+SSM_TREE_ABI_VERSION = 4
 SSM_TREE_F32, SSM_TREE_BF16 = 0, 1
 SSM_TREE_CONV_SILU = 1
 SSM_TREE_VERIFY_FIFO = 2
 SSM_TREE_CONV_XBC = 4
 SSM_TREE_STATE_BF16 = 8
-OK, E_NULL, E_ALIGN, E_DIMS, E_DTYPE, E_ALIAS, E_HIP, E_FLAGS = 0, -1, -2, -3, -4, -5, -6, -7
+OK, E_NULL, E_ALIGN, E_DIMS, E_DTYPE, E_ALIAS, E_HIP, E_FLAGS, E_SCRATCH = 0, -1, -2, -3, -4, -5, -6, -7, -8
 E_TREE, E_PATH = -10, -11
 PLAN_HEADER, PLAN_STRIDE, PLAN_UNUSED = 4, 8, -32768
 
@@ -75,6 +76,8 @@ def load():
         L.ssm_tree_commit.restype = i
         L.ssm_tree_commit_verify.argtypes = [p] * 23
         L.ssm_tree_commit_verify.restype = i
+        L.ssm_tree_commit_verify_noalloc.argtypes = [p] * 23
+        L.ssm_tree_commit_verify_noalloc.restype = i
         L.ssm_tree_plan.argtypes = [p] * 4
         L.ssm_tree_plan.restype = i
         L.ssm_tree_status_string.argtypes = [i]
@@ -110,6 +113,15 @@ def ssm_tree_commit_verify(dims: Dims, params: Params, parent_prev, path, path_l
                                          x_prev, B_prev, C_prev, dt_raw_prev, conv_window_in, state_in,
                                          conv_window_out, state_out, parent, x, B, C, dt_raw, z, y, commit_status,
                                          verify_status, hip_stream)
+
+
+def ssm_tree_commit_verify_noalloc(dims: Dims, params: Params, parent_prev, path, path_len, x_prev, B_prev, C_prev,
+                                   dt_raw_prev, conv_window_in, state_in, conv_window_out, state_out, parent, x, B,
+                                   C, dt_raw, z, y, commit_status, verify_status, hip_stream) -> int:
+    return load().ssm_tree_commit_verify_noalloc(ctypes.byref(dims), ctypes.byref(params), parent_prev, path,
+                                                 path_len, x_prev, B_prev, C_prev, dt_raw_prev, conv_window_in,
+                                                 state_in, conv_window_out, state_out, parent, x, B, C, dt_raw, z, y,
+                                                 commit_status, verify_status, hip_stream)
 
 
 def ssm_tree_plan(dims: Dims, parent, plan_out, hip_stream) -> int:
@@ -273,9 +285,11 @@ def commit(dims: Dims, params: Params, parent, path, path_len, x, B, dt_raw, con
 
 def commit_verify(dims: Dims, params: Params, parent_prev, path, path_len, x_prev, B_prev, dt_raw_prev,
                   conv_window_in, state_in, conv_window_out, state_out, parent, x, B, C, dt_raw, y,
-                  commit_status=None, verify_status=None, stream=None, C_prev=None, z=None):
+                  commit_status=None, verify_status=None, stream=None, C_prev=None, z=None, noalloc=False):
     """ssm_tree_commit_verify; C_prev is needed only with the xBC conv, z
-    (optional) gates the next tree's y by silu(z)."""
+    (optional) gates the next tree's y by silu(z); noalloc calls
+    ssm_tree_commit_verify_noalloc instead (no allocation; its fixed scratch
+    is shared by every such call on the device)."""
     sk = _state_kind(dims)
     _check_call(dims, params, (("parent_prev", parent_prev, "int32", "tree"), ("path", path, "int32", "tree"),
                                ("path_len", path_len, "int32", "seq"), ("x_prev", x_prev, "in", "tok"),
@@ -288,13 +302,14 @@ def commit_verify(dims: Dims, params: Params, parent_prev, path, path_len, x_pre
                                ("dt_raw", dt_raw, "in", "dt"), ("z", z, "in", "tok"), ("y", y, "float32", "tok"),
                                ("commit_status", commit_status, "int32", "seq"),
                                ("verify_status", verify_status, "int32", "seq")))
-    rc = ssm_tree_commit_verify(dims, params, _ptr(parent_prev), _ptr(path), _ptr(path_len), _ptr(x_prev),
+    fn = ssm_tree_commit_verify_noalloc if noalloc else ssm_tree_commit_verify
+    rc = fn(dims, params, _ptr(parent_prev), _ptr(path), _ptr(path_len), _ptr(x_prev),
                                 _ptr(B_prev), _ptr(C_prev), _ptr(dt_raw_prev), _ptr(conv_window_in),
                                 _ptr(state_in), _ptr(conv_window_out), _ptr(state_out), _ptr(parent), _ptr(x),
                                 _ptr(B), _ptr(C), _ptr(dt_raw), _ptr(z), _ptr(y), _ptr(commit_status),
                                 _ptr(verify_status), _stream(stream))
     if rc != OK:
-        raise SsmTreeError(rc, "ssm_tree_commit_verify")
+        raise SsmTreeError(rc, "ssm_tree_commit_verify_noalloc" if noalloc else "ssm_tree_commit_verify")
     if _debug():
         _check_statuses("ssm_tree_commit_verify", (("commit_status", commit_status), ("verify_status", verify_status)))
 

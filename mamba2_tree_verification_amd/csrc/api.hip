@@ -80,10 +80,47 @@ hipMemPool_t workspace_pool(hipStream_t s) {
   return pools[dev];
 }
 
+// The allocation-free round (ssm_tree_commit_verify_noalloc) keeps the xBC
+// workspace in this fixed device array instead: one copy per device, held
+// until the process ends and shared by every such call on that device.
+// Nothing in it needs clearing: a round writes every value it reads first.
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+__device__ __align__(256) static float scratch[kScratchBytes / sizeof(float)];
+
+// scratch's device address on the stream's device, looked up once per device
+// with that device current (the host-side name is not a device address)
+float* scratch_address(hipStream_t s) {
+  int dev = -1;
+  if ((s ? hipStreamGetDevice(s, &dev) : hipGetDevice(&dev)) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return nullptr;
+  static std::mutex m;
+  static float* addr[kMaxDevices] = {};
+  std::lock_guard<std::mutex> lock(m);
+  if (!addr[dev]) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return nullptr;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return nullptr;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev && hipSetDevice(cur) != hipSuccess) return nullptr;
+    if (e != hipSuccess || !p) return nullptr;
+    addr[dev] = static_cast<float*>(p);
+  }
+  return addr[dev];
+}
+
 // the fused round's kernels, with the xBC conv's workspace when it needs one
-int run_fused(CommitVerifyArgs& a, bool bf16, hipStream_t s) {
+// (noalloc: the fixed array, never an allocation)
+int run_fused(CommitVerifyArgs& a, bool bf16, hipStream_t s, bool noalloc = false) {
   const size_t bytes = bc_workspace_bytes(a.d);
   if (!bytes) return launch_commit_verify(a, bf16, s);
+  if (noalloc) {
+    if (bytes > kScratchBytes) return SSM_TREE_E_SCRATCH;
+    float* p = scratch_address(s);
+    if (!p) return SSM_TREE_E_HIP;
+    a.bcw = p;
+    return launch_commit_verify(a, bf16, s);
+  }
   hipMemPool_t pool = workspace_pool(s);
   void* ws = nullptr;
   if (!pool || hipMallocFromPoolAsync(&ws, bytes, pool, s) != hipSuccess) return SSM_TREE_E_HIP;
@@ -141,6 +178,7 @@ const char* ssm_tree_status_string(int status) {
     case SSM_TREE_E_ALIAS: return "an output overlaps an input";
     case SSM_TREE_E_HIP: return "HIP kernel launch failed";
     case SSM_TREE_E_FLAGS: return "unknown flag bits";
+    case SSM_TREE_E_SCRATCH: return "the call needs more scratch memory than the allocation-free entry point holds";
     case SSM_TREE_E_TREE: return "parent[] is not a BFS-ordered tree";
     case SSM_TREE_E_PATH: return "path is not a root-to-node path of the tree";
     default: return "unknown status";
@@ -288,12 +326,13 @@ int ssm_tree_commit(const ssm_tree_dims* dims, const ssm_tree_params* params, co
   return launch_commit(a, dims->in_dtype == SSM_TREE_BF16, s) == hipSuccess ? SSM_TREE_OK : SSM_TREE_E_HIP;
 }
 
-int ssm_tree_commit_verify(const ssm_tree_dims* dims, const ssm_tree_params* params, const int32_t* parent_prev,
-                           const int32_t* path, const int32_t* path_len, const void* x_prev, const void* B_prev,
-                           const void* C_prev, const void* dt_raw_prev, const void* conv_window_in,
-                           const void* state_in, void* conv_window_out, void* state_out, const int32_t* parent,
-                           const void* x, const void* B, const void* C, const void* dt_raw, const void* z,
-                           float* y, int32_t* commit_status, int32_t* verify_status, void* hip_stream) {
+static int commit_verify_impl(const ssm_tree_dims* dims, const ssm_tree_params* params, const int32_t* parent_prev,
+                              const int32_t* path, const int32_t* path_len, const void* x_prev, const void* B_prev,
+                              const void* C_prev, const void* dt_raw_prev, const void* conv_window_in,
+                              const void* state_in, void* conv_window_out, void* state_out, const int32_t* parent,
+                              const void* x, const void* B, const void* C, const void* dt_raw, const void* z,
+                              float* y, int32_t* commit_status, int32_t* verify_status, void* hip_stream,
+                              bool noalloc) {
   Dims d;
   int st = check_dims(dims, &d);
   if (st) return st;
@@ -374,7 +413,9 @@ int ssm_tree_commit_verify(const ssm_tree_dims* dims, const ssm_tree_params* par
   a.y = y;
   a.commit_status = commit_status;
   a.verify_status = verify_status;
-  if (fused) return run_fused(a, bf16, s);
+  if (fused) return run_fused(a, bf16, s, noalloc);
+  // (no other path of the round uses scratch memory: the two calls below
+  // never reach the xBC workspace, which only the fused shapes take)
   // trees of 17-64 nodes: one launch where the role-split verify applies
   // (E_DIMS from it: nothing was launched)
   if (kTtRound && tt_round_applies(d, bf16, z != nullptr)) {
@@ -396,6 +437,29 @@ int ssm_tree_commit_verify(const ssm_tree_dims* dims, const ssm_tree_params* par
   if (st) return st;
   return ssm_tree_verify(dims, params, parent, x, B, C, dt_raw, z, conv_window_out, state_out, y, verify_status,
                          hip_stream);
+}
+
+int ssm_tree_commit_verify(const ssm_tree_dims* dims, const ssm_tree_params* params, const int32_t* parent_prev,
+                           const int32_t* path, const int32_t* path_len, const void* x_prev, const void* B_prev,
+                           const void* C_prev, const void* dt_raw_prev, const void* conv_window_in,
+                           const void* state_in, void* conv_window_out, void* state_out, const int32_t* parent,
+                           const void* x, const void* B, const void* C, const void* dt_raw, const void* z,
+                           float* y, int32_t* commit_status, int32_t* verify_status, void* hip_stream) {
+  return commit_verify_impl(dims, params, parent_prev, path, path_len, x_prev, B_prev, C_prev, dt_raw_prev,
+                            conv_window_in, state_in, conv_window_out, state_out, parent, x, B, C, dt_raw, z, y,
+                            commit_status, verify_status, hip_stream, false);
+}
+
+int ssm_tree_commit_verify_noalloc(const ssm_tree_dims* dims, const ssm_tree_params* params,
+                                   const int32_t* parent_prev, const int32_t* path, const int32_t* path_len,
+                                   const void* x_prev, const void* B_prev, const void* C_prev,
+                                   const void* dt_raw_prev, const void* conv_window_in, const void* state_in,
+                                   void* conv_window_out, void* state_out, const int32_t* parent, const void* x,
+                                   const void* B, const void* C, const void* dt_raw, const void* z, float* y,
+                                   int32_t* commit_status, int32_t* verify_status, void* hip_stream) {
+  return commit_verify_impl(dims, params, parent_prev, path, path_len, x_prev, B_prev, C_prev, dt_raw_prev,
+                            conv_window_in, state_in, conv_window_out, state_out, parent, x, B, C, dt_raw, z, y,
+                            commit_status, verify_status, hip_stream, true);
 }
 
 int ssm_tree_plan(const ssm_tree_dims* dims, const int32_t* parent, int32_t* plan_out, void* hip_stream) {

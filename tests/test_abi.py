@@ -22,7 +22,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(["ssm_tree_verify", "ssm_tree_commit", "ssm_tree_commit_verify",
-                                           "ssm_tree_plan", "ssm_tree_status_string", "ssm_tree_abi_version"])
+                                           "ssm_tree_commit_verify_noalloc", "ssm_tree_plan",
+                                           "ssm_tree_status_string", "ssm_tree_abi_version"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -38,7 +39,8 @@ def test_header_constants_match_binding():
     assert consts["SSM_TREE_ABI_VERSION"] == m.SSM_TREE_ABI_VERSION
     assert consts["SSM_TREE_BF16"] == m.SSM_TREE_BF16 and consts["SSM_TREE_F32"] == m.SSM_TREE_F32
     for k, v in dict(OK=m.OK, E_NULL=m.E_NULL, E_ALIGN=m.E_ALIGN, E_DIMS=m.E_DIMS, E_DTYPE=m.E_DTYPE,
-                     E_ALIAS=m.E_ALIAS, E_HIP=m.E_HIP, E_FLAGS=m.E_FLAGS, E_TREE=m.E_TREE, E_PATH=m.E_PATH).items():
+                     E_ALIAS=m.E_ALIAS, E_HIP=m.E_HIP, E_FLAGS=m.E_FLAGS, E_SCRATCH=m.E_SCRATCH, E_TREE=m.E_TREE,
+                     E_PATH=m.E_PATH).items():
         assert consts["SSM_TREE_" + k] == v, k
     assert consts["SSM_TREE_PLAN_HEADER"] == m.PLAN_HEADER and consts["SSM_TREE_PLAN_STRIDE"] == m.PLAN_STRIDE
     assert consts["SSM_TREE_PLAN_UNUSED"] == m.PLAN_UNUSED
@@ -49,8 +51,8 @@ def test_header_constants_match_binding():
 
 
 def test_status_strings():
-    for code in (m.OK, m.E_NULL, m.E_ALIGN, m.E_DIMS, m.E_DTYPE, m.E_ALIAS, m.E_HIP, m.E_FLAGS, m.E_TREE,
-                 m.E_PATH):
+    for code in (m.OK, m.E_NULL, m.E_ALIGN, m.E_DIMS, m.E_DTYPE, m.E_ALIAS, m.E_HIP, m.E_FLAGS, m.E_SCRATCH,
+                 m.E_TREE, m.E_PATH):
         s = m.ssm_tree_status_string(code)
         assert s and s != "unknown status"
     assert m.ssm_tree_status_string(-999) == "unknown status"
@@ -149,35 +151,38 @@ def call_commit_verify(dims, params, **kw):
              dt_prev=fake(15), win_in=fake(6), state_in=fake(7), win_out=fake(16), state_out=fake(17),
              parent=fake(18), x=fake(2), B=fake(3), C=fake(4), dt_raw=fake(5), z=None, y=fake(8), cst=fake(9),
              vst=fake(19))
+    noalloc = kw.pop("noalloc", False)
     a.update(kw)
-    return m.ssm_tree_commit_verify(dims, params, a["pparent"], a["path"], a["plen"], a["x_prev"], a["B_prev"],
-                                    a["C_prev"], a["dt_prev"], a["win_in"], a["state_in"], a["win_out"],
-                                    a["state_out"], a["parent"], a["x"], a["B"], a["C"], a["dt_raw"], a["z"],
-                                    a["y"], a["cst"], a["vst"], None)
+    fn = m.ssm_tree_commit_verify_noalloc if noalloc else m.ssm_tree_commit_verify
+    return fn(dims, params, a["pparent"], a["path"], a["plen"], a["x_prev"], a["B_prev"], a["C_prev"], a["dt_prev"],
+              a["win_in"], a["state_in"], a["win_out"], a["state_out"], a["parent"], a["x"], a["B"], a["C"],
+              a["dt_raw"], a["z"], a["y"], a["cst"], a["vst"], None)
 
 
+@pytest.mark.parametrize("noalloc", [False, True], ids=["alloc", "noalloc"])
 @pytest.mark.parametrize("dkw", [dict(), dict(T=40), dict(H=8, P=40, N=16)])
-def test_commit_verify_host_checks(dkw):
+def test_commit_verify_host_checks(dkw, noalloc):
+    """(ssm_tree_commit_verify_noalloc makes the same checks)"""
     # the same checks whichever way the call would run (fused kernel, or the two calls)
     d, p = good_dims(**dkw), good_params()
     for k in ("pparent", "path", "plen", "x_prev", "B_prev", "dt_prev", "state_in", "state_out", "parent", "x",
               "B", "C", "dt_raw", "y", "win_in", "win_out"):
-        assert call_commit_verify(d, p, **{k: None}) == m.E_NULL, k
+        assert call_commit_verify(d, p, **{k: None}, noalloc=noalloc) == m.E_NULL, k
     for k in ("pparent", "x_prev", "state_out", "C", "y", "cst", "vst", "win_out"):
-        assert call_commit_verify(d, p, **{k: fake(30, 8)}) == m.E_ALIGN, k
-    assert call_commit_verify(d, p, state_out=fake(7, 4096)) == m.E_ALIAS      # partial overlap with state_in
-    assert call_commit_verify(d, p, win_out=fake(6, 2048)) == m.E_ALIAS        # partial overlap with window_in
-    assert call_commit_verify(d, p, y=fake(7)) == m.E_ALIAS                    # y over state_in
-    assert call_commit_verify(d, p, y=fake(6)) == m.E_ALIAS                    # y over window_in
-    assert call_commit_verify(d, p, y=fake(17)) == m.E_ALIAS                   # y over state_out
-    assert call_commit_verify(d, p, state_out=fake(13)) == m.E_ALIAS           # over x_prev
-    assert call_commit_verify(d, p, win_out=fake(4)) == m.E_ALIAS              # over C
-    assert call_commit_verify(d, p, cst=fake(19)) == m.E_ALIAS                 # the two status arrays
-    assert call_commit_verify(d, p, vst=fake(1)) == m.E_ALIAS                  # status over parent_prev
-    assert call_commit_verify(d, good_params(A=None)) == m.E_NULL
+        assert call_commit_verify(d, p, **{k: fake(30, 8)}, noalloc=noalloc) == m.E_ALIGN, k
+    assert call_commit_verify(d, p, state_out=fake(7, 4096), noalloc=noalloc) == m.E_ALIAS      # partial overlap with state_in
+    assert call_commit_verify(d, p, win_out=fake(6, 2048), noalloc=noalloc) == m.E_ALIAS        # partial overlap with window_in
+    assert call_commit_verify(d, p, y=fake(7), noalloc=noalloc) == m.E_ALIAS                    # y over state_in
+    assert call_commit_verify(d, p, y=fake(6), noalloc=noalloc) == m.E_ALIAS                    # y over window_in
+    assert call_commit_verify(d, p, y=fake(17), noalloc=noalloc) == m.E_ALIAS                   # y over state_out
+    assert call_commit_verify(d, p, state_out=fake(13), noalloc=noalloc) == m.E_ALIAS           # over x_prev
+    assert call_commit_verify(d, p, win_out=fake(4), noalloc=noalloc) == m.E_ALIAS              # over C
+    assert call_commit_verify(d, p, cst=fake(19), noalloc=noalloc) == m.E_ALIAS                 # the two status arrays
+    assert call_commit_verify(d, p, vst=fake(1), noalloc=noalloc) == m.E_ALIAS                  # status over parent_prev
+    assert call_commit_verify(d, good_params(A=None), noalloc=noalloc) == m.E_NULL
     bad = good_dims(**dkw)
     bad.flags = 16  # the first unassigned bit
-    assert call_commit_verify(bad, p) == m.E_FLAGS
+    assert call_commit_verify(bad, p, noalloc=noalloc) == m.E_FLAGS
 
 
 def test_plan_host_checks():
