@@ -78,7 +78,7 @@ extern "C" {
  * SSM_TREE_E_DIMS before anything is enqueued.
  * On trees of 1 to 16 nodes ssm_tree_verify and ssm_tree_commit_verify
  * first convolve each sequence's B and C rows once, into a workspace of
- * L*Bsz*G*T*3*N float32 values that the library takes in stream order
+ * L*Bsz*G*(T*3*N + 256) float32 values that the library takes in stream order
  * from a memory pool of its own on the stream's device and releases, in
  * stream order, after the kernels that read it (SSM_TREE_E_HIP if that
  * allocation fails). */
@@ -241,8 +241,8 @@ int ssm_tree_commit_verify(const ssm_tree_dims* dims, const ssm_tree_params* par
  * loops, harnesses that forbid hipMalloc).  Same arguments, outputs, status
  * codes and kernels; it calls no allocating routine.
  * The one scratch buffer a round uses, the convolved B and C rows of
- * SSM_TREE_CONV_XBC on trees of 1 to 16 nodes (L*Bsz*G*T*3*N float32
- * values), is here a fixed device array of 32 MiB that the library holds on
+ * SSM_TREE_CONV_XBC on trees of 1 to 16 nodes (L*Bsz*G*(T*3*N + 256)
+ * float32 values), is here a fixed device array of 32 MiB that the library holds on
  * each device it runs on until the process ends, instead of the stream-
  * ordered pool allocation ssm_tree_commit_verify makes.  A call that needs
  * more returns SSM_TREE_E_SCRATCH before anything is enqueued.  Every call

@@ -50,7 +50,12 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kCvRows = 64;   // channels per workgroup
 constexpr int kCvWaves = 4;
 constexpr int kCvT = 16;      // node capacity
-constexpr int kBcThreads = 256;  // bc_conv_kernel
+constexpr int kBcThreads = 256;  // bc_conv_kernel (one thread per entry of the 16 x 16 C . B table)
+constexpr int kBcMaxN = 256;     // d_state bound of its LDS rows
+static_assert(kBcThreads == kCvT * kCvT, "C . B table mapping");
+// floats of one (sequence, group) block of the xBC workspace: the next
+// tree's convolved B and C rows, the path's B rows, the C . B table
+__host__ __device__ constexpr int bc_block_floats(int T, int N) { return T * 3 * N + kCvT * kCvT; }
 constexpr int kRowPad = 16;   // bytes of padding per staged B / C row (LDS banks)
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -124,7 +129,7 @@ struct CvLds {
     av = o; o += 4 * 4 * kCvT;                // next tree: a_v = exp(S_v) per head and node
     Mt = o; o += 4 * slab_heads(P) * kCvT * kCvT;  // next tree: exp(S_v - S_u) dt_u, u on v's root path, else 0
     D = o; o += 16;
-    cbt = o; o += xbc ? 0 : 4 * kCvT * kCvT;  // next tree: C_v . B_u (with the xBC conv each wave forms it itself)
+    cbt = o; o += xbc ? 0 : 4 * kCvT * kCvT;  // next tree: C_v . B_u (with the xBC conv, in the workspace)
     cw = o; o += 4 * 4 * kCvRows;             // conv weights per channel, tap order of the parameters
     cb = o; o += 4 * kCvRows;                 // conv bias per channel
     win = o; o += align16(3 * kCvRows * E);   // old window rows (raw)
@@ -229,8 +234,9 @@ __global__ void __launch_bounds__(kCvWaves * kWave)
   float* s_Bpt = reinterpret_cast<float*>(smem + lo.Bpt);
   // SSM_TREE_CONV_XBC: the group's convolved rows, [T][2 N] of the next tree
   // (B then C) and [T][N] of the path, formed ahead of this kernel
-  const float* bcw_n = xbc ? a.bcw + (unit * G + g) * (int64_t)T * 3 * N : nullptr;
+  const float* bcw_n = xbc ? a.bcw + (unit * G + g) * (int64_t)bc_block_floats(T, N) : nullptr;
   const float* bcw_p = xbc ? bcw_n + (int64_t)T * 2 * N : nullptr;
+  const float* bcw_cb = xbc ? bcw_p + (int64_t)T * N : nullptr;
 
   // ======== trip 1: everything that does not depend on the path ========
 
@@ -446,7 +452,7 @@ __global__ void __launch_bounds__(kCvWaves * kWave)
     }
   } else if (wave == 1 && !xbc) {
     // C_v . B_u of the next tree: lane (u + 16 q) ends with CB[4 q + r][u]
-    // (with the xBC conv each wave forms it later from the convolved rows)
+    // (with the xBC conv the table is in the workspace)
     f32x4 cbm = f32x4{0.f, 0.f, 0.f, 0.f};
     const bool live = j < T;
     if constexpr (E == 2) {
@@ -743,10 +749,12 @@ __global__ void __launch_bounds__(kCvWaves * kWave)
     // C . h on the matrix cores: lane (c + 16 q) ends with (C_{4q+r} . h_c)
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
     const bool live = j < T;
-    f32x4 cbx = f32x4{0.f, 0.f, 0.f, 0.f};  // with the xBC conv: C_v . B_u, formed below
-    // with the xBC conv, node j's convolved B and C rows (node 0's for the
-    // lanes past the tree, whose products are zeroed)
-    const float* bcj = OPT && xbc ? bcw_n + (live ? j : 0) * 2 * N : nullptr;
+    // with the xBC conv, node j's convolved C row (node 0's for the lanes
+    // past the tree, whose products are zeroed), and the C . B table
+    // (C_v . B_u at [v][u]) in the workspace instead of LDS
+    const float* ccj = OPT && xbc ? bcw_n + (live ? j : 0) * 2 * N + N : nullptr;
+    const float* cbt = OPT && xbc ? bcw_cb : s_cbt;
+    const f32x4 cbr = *reinterpret_cast<const f32x4*>(cbt + j * kCvT + 4 * k);
     // bf16 C rows and a bf16 state are exact bf16 operands: one 16x16x32
     // product per pair of column groups (lane j + 16 k feeds columns
     // 16 gg + 4 k .. + 3 of both groups, the same slots in C and in h)
@@ -766,13 +774,11 @@ __global__ void __launch_bounds__(kCvWaves * kWave)
     } else {
 #pragma unroll
       for (int gg = 0; gg < NG; ++gg) {
-        f32x4 cq, bxq = f32x4{0.f, 0.f, 0.f, 0.f};
+        f32x4 cq;
         if constexpr (OPT) {
           if (xbc) {
-            // the convolved B and C values of node j, columns n0 .. n0 + 3
-            const int n0 = 16 * gg + 4 * k;
-            bxq = *reinterpret_cast<const f32x4*>(bcj + n0);
-            cq = *reinterpret_cast<const f32x4*>(bcj + N + n0);
+            // the convolved C values of node j, columns 16 gg + 4 k .. + 3
+            cq = *reinterpret_cast<const f32x4*>(ccj + 16 * gg + 4 * k);
           } else {
             cq = load4<TIn>(reinterpret_cast<const TIn*>(s_C + j * rs) + colq(gg));
           }
@@ -784,26 +790,12 @@ __global__ void __launch_bounds__(kCvWaves * kWave)
         acc = mfma4(cq.y, hq[gg].y, acc);
         acc = mfma4(cq.z, hq[gg].z, acc);
         acc = mfma4(cq.w, hq[gg].w, acc);
-        if constexpr (OPT) {
-          if (xbc) {
-            // B rows as the A operand and C rows as the B operand: lane
-            // (i + 16 k) ends with (B_{4k+t} . C_i) = CB[i][4 k + t], the
-            // layout the path terms read, with no transpose
-            f32x4 bq = bxq;
-            if (!live) bq = f32x4{0.f, 0.f, 0.f, 0.f};
-            cbx = mfma4(bq.x, cq.x, cbx);
-            cbx = mfma4(bq.y, cq.y, cbx);
-            cbx = mfma4(bq.z, cq.z, cbx);
-            cbx = mfma4(bq.w, cq.w, cbx);
-          }
-        }
       }
     }
     // then the path terms M[v][u] x~_u, with the diagonal D
     const int i = j;
     const f32x4 mq = *reinterpret_cast<const f32x4*>(s_Mt + (hh * kCvT + i) * kCvT + 4 * k);
     const f32x4 aq = *reinterpret_cast<const f32x4*>(s_a + hh * kCvT + 4 * k);
-    const f32x4 cbr = xbc ? cbx : *reinterpret_cast<const f32x4*>(s_cbt + i * kCvT + 4 * k);
     const int ancm = s_anc[i];
     const float Dh = s_D[hh];
     f32x4 mop, y;
@@ -831,15 +823,7 @@ __global__ void __launch_bounds__(kCvWaves * kWave)
         const float* mrow = s_Mt + (hh * kCvT + v) * kCvT;
         float yy = y[t];
         for (int u = 0; u < kCvT; ++u) {
-          // C_v . B_u: lane v + 16 (u / 4), element u % 4 of cbx, or the table
-          float cb = 0.0f;
-          if (xbc) {
-            const f32x4 cq4 = cbx;
-            const float e = (u & 3) == 0 ? cq4.x : (u & 3) == 1 ? cq4.y : (u & 3) == 2 ? cq4.z : cq4.w;
-            cb = __shfl(e, v + 16 * (u >> 2));
-          } else {
-            cb = s_cbt[v * kCvT + u];
-          }
+          const float cb = cbt[v * kCvT + u];  // C_v . B_u
           if ((av >> u) & 1) {
             const float mv = mrow[u] * cb;
             const float xu = s_xt[row * kCvT + 4 * ((u >> 2) ^ ((row >> 2) & 3)) + (u & 3)];
@@ -882,7 +866,9 @@ __global__ void __launch_bounds__(kCvWaves * kWave)
 //             and past the root the rows of the committed window (the old
 //             window's rows, then the accepted path's rows);
 //   path      [T][N]: the accepted path's B channels convolved along (old
-//             window rows, path rows), positions q < len.
+//             window rows, path rows), positions q < len;
+//   C.B       [16][16]: C_v . B_u of the next tree's convolved rows (zero
+//             past T), which every wave of the round would otherwise form.
 // SiLU follows when set.  The commit length follows the round's own checks
 // (0 when the previous tree or the path is not valid, or with nothing to
 // commit), so the window taps agree with what the round commits.  One
@@ -895,6 +881,10 @@ __global__ void __launch_bounds__(kBcThreads) bc_conv_kernel(CommitVerifyArgs a)
   const int64_t unit = (int64_t)l * d.Bsz + b;
   const int tid = threadIdx.x;
   __shared__ int32_t s_parent[kCvT], s_pparent[kCvT], s_path[kCvT], s_code[kCvT][3], s_len;
+  // the next tree's convolved rows, [node][column] with an odd stride (the
+  // C . B dots below read 16 rows at one column on distinct banks)
+  constexpr int kRs = 2 * kBcMaxN + 1;
+  __shared__ float s_rows[kCvT * kRs];
   const bool commit = a.path_len != nullptr;
   if (tid < T) {
     s_parent[tid] = a.parent[(int64_t)b * T + tid];
@@ -929,8 +919,9 @@ __global__ void __launch_bounds__(kBcThreads) bc_conv_kernel(CommitVerifyArgs a)
   __syncthreads();
   const int len = s_len;
   const TIn* win = reinterpret_cast<const TIn*>(a.window_in) + unit * (W - 1) * (int64_t)CH + DI;
-  float* out_n = a.bcw + (unit * G + g) * (int64_t)T * 3 * N;
+  float* out_n = a.bcw + (unit * G + g) * (int64_t)bc_block_floats(T, N);
   float* out_p = out_n + (int64_t)T * 2 * N;
+  float* out_cb = out_p + (int64_t)T * N;
   // column c < 2 N: B channel c (c < N) or C channel c - N of group g
   for (int c = tid; c < 2 * N; c += kBcThreads) {
     const bool isB = c < N;
@@ -948,6 +939,8 @@ __global__ void __launch_bounds__(kBcThreads) bc_conv_kernel(CommitVerifyArgs a)
     auto elem = [&](int e) {
       return e < W - 1 ? load_in(win, (int64_t)e * CH + wch) : load_in(prow, (int64_t)s_path[e - (W - 1)] * GN);
     };
+    // (results go to LDS first: no global store between the nodes' loads)
+#pragma unroll 4
     for (int v = 0; v < T; ++v) {
       float acc = fmaf(w[0], load_in(rows, (int64_t)v * GN), bias);
 #pragma unroll
@@ -957,7 +950,7 @@ __global__ void __launch_bounds__(kBcThreads) bc_conv_kernel(CommitVerifyArgs a)
           acc = fmaf(w[jj], code < T ? load_in(rows, (int64_t)code * GN) : elem(len + code - T), acc);
         }
       }
-      out_n[(int64_t)v * 2 * N + c] = d.silu ? silu_fast(acc) : acc;
+      s_rows[v * kRs + c] = d.silu ? silu_fast(acc) : acc;
     }
     if (isB) {
       for (int q = 0; q < len; ++q) {
@@ -969,13 +962,26 @@ __global__ void __launch_bounds__(kBcThreads) bc_conv_kernel(CommitVerifyArgs a)
       }
     }
   }
+  __syncthreads();
+  for (int i = tid; i < T * 2 * N; i += kBcThreads) out_n[i] = s_rows[(i / (2 * N)) * kRs + i % (2 * N)];
+  // C_v . B_u, thread (v, u) of the 16 x 16 table (zero past the tree)
+  {
+    const int v = tid / kCvT, u = tid % kCvT;
+    float acc = 0.0f;
+    if (v < T && u < T) {
+      const float* cv = s_rows + v * kRs + N;
+      const float* bu = s_rows + u * kRs;
+      for (int n = 0; n < N; ++n) acc = fmaf(cv[n], bu[n], acc);
+    }
+    out_cb[tid] = acc;
+  }
 }
 
 // bytes of the convolved rows a round with SSM_TREE_CONV_XBC on trees of up
 // to 16 nodes needs (0 otherwise)
 size_t bc_workspace_bytes(const Dims& d) {
   if (!d.xbc || d.T < 1 || d.T > kCvT) return 0;
-  return (size_t)d.L * d.Bsz * d.G * d.T * 3 * d.N * sizeof(float);
+  return (size_t)d.L * d.Bsz * d.G * bc_block_floats(d.T, d.N) * sizeof(float);
 }
 
 hipError_t launch_bc_conv(const CommitVerifyArgs& a, bool bf16, hipStream_t s) {

@@ -51,7 +51,7 @@ def _run(step, noalloc):
 
 
 def _workspace_bytes(cfg):
-    return cfg.L * cfg.Bsz * cfg.G * cfg.T * 3 * cfg.N * 4 if cfg.xbc and cfg.T <= 16 else 0
+    return cfg.L * cfg.Bsz * cfg.G * (cfg.T * 3 * cfg.N + 256) * 4 if cfg.xbc and cfg.T <= 16 else 0
 
 
 def _same(a, b, what):
@@ -88,7 +88,7 @@ def test_noalloc_matches_the_allocating_round():
 
 def test_noalloc_full_size_round():
     """The 2.7B batch-16 tree-16 round with SiLU, the xBC conv and the gate
-    (25.2 MB of convolved rows in the 32 MiB array), then the small
+    (26.2 MB of convolved rows in the 32 MiB array), then the small
     workload's round over the same array."""
     big = C.CONFIGS[3].replace(cid=890, silu=True, xbc=True, gate=True)
     small = C.CONFIGS[0].replace(cid=891, silu=True, xbc=True, gate=True)
@@ -100,7 +100,7 @@ def test_noalloc_full_size_round():
 
 
 def test_noalloc_refuses_a_call_beyond_its_scratch():
-    # 32 x 32 sequences of 16-node trees, d_state 256: 50.3 MB of convolved
+    # 32 x 32 sequences of 16-node trees, d_state 256: 51.4 MB of convolved
     # rows, more than the array holds; refused before anything is enqueued
     L, Bsz, T, H, P, N, G, W = 32, 32, 16, 1, 64, 256, 1, 4
     cfg = C.Config(892, "noalloc-big", L, Bsz, T, H, P, N, G, W, True, 0.5, "forest", True, False, True, False)
