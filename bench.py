@@ -397,7 +397,8 @@ def stress_workload(torch, m, C, threads, reps=4):
         m.verify(dims, prm, nxt.parent, nxt.x, nxt.B, nxt.C, nxt.dt_raw, g.window, g.state, y, st_v)
 
     def timed(fn):
-        fn()
+        for _ in range(WARM_EXTRA // 2):  # the ramp to the steady rate (10 calls of 64-node trees)
+            fn()
         torch.cuda.synchronize()
         out = []
         for _ in range(reps):
@@ -544,6 +545,11 @@ def draft_decode(torch, m, C, upload, threads, timed, steps=15):
             "note": "one-node ssm_tree_commit_verify per draft token (all layers in one call); not in the step"}
 
 
+# untimed rounds before an extra round is timed: a fresh process or workload
+# takes about 20 rounds to reach its steady rate
+WARM_EXTRA = 20
+
+
 def options_round(torch, m, C, cfg, g, g2, state, timed, threads, path_lens):
     """The same decode round with the Mamba2-convention options: SiLU over
     the conv of x, B and C (SSM_TREE_CONV_XBC) and the output gate
@@ -570,6 +576,8 @@ def options_round(torch, m, C, cfg, g, g2, state, timed, threads, path_lens):
                         z=zs[(k[0] + 1) % 2])
         k[0] += 1
 
+    for _ in range(WARM_EXTRA):  # a fresh workload's ramp to its steady rate, as for the step
+        step()
     ms = timed(step, reps=9)
     torch.cuda.synchronize()
     if not (cst.cpu() == 0).all() or not (vst.cpu() == 0).all() or torch.isnan(y).any():
@@ -612,6 +620,8 @@ def state_bf16_round(torch, m, cfg, g, g2, state, window, timed, path_lens):
         k[0] += 1
 
     try:
+        for _ in range(WARM_EXTRA):
+            step()
         ms = timed(step, reps=9)
     except m.SsmTreeError as e:  # shapes no kernel takes with a bf16 state
         return {"skipped": str(e)}
@@ -801,7 +811,9 @@ def main(argv=None):
     # calls (verify from the state, then the in-place commit), and the page's
     # own form of verification (explicit FIFO walk, every child state
     # materialised)
-    def timed(fn, reps=5):
+    def timed(fn, reps=5, warm=0):
+        for _ in range(warm):  # the ramp of a call not yet run in this process
+            fn()
         out = []
         for k in range(reps):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -813,9 +825,10 @@ def main(argv=None):
                 out.append(e0.elapsed_time(e1))
         return out
 
-    ver_ms = timed(lambda: m.verify(dims, prm, g.parent, g.x, g.B, g.C, g.dt_raw, window, state, y, st_v), reps=11)
+    ver_ms = timed(lambda: m.verify(dims, prm, g.parent, g.x, g.B, g.C, g.dt_raw, window, state, y, st_v), reps=11,
+                   warm=WARM_EXTRA // 2)
     com_ms = timed(lambda: m.commit(dims, prm, g.parent, g.path, g.path_len, g.x, g.B, g.dt_raw, window, state,
-                                    window, state, st_c), reps=11)
+                                    window, state, st_c), reps=11, warm=WARM_EXTRA // 2)
     dims_fifo = m.make_dims(cfg.L, cfg.Bsz, cfg.T, cfg.H, cfg.P, cfg.N, cfg.G, cfg.W, cfg.bf16, cfg.silu, fifo=True)
     fifo_ms = timed(lambda: m.verify(dims_fifo, prm, g.parent, g.x, g.B, g.C, g.dt_raw, window, state, y, st_v),
                     reps=3)
