@@ -324,7 +324,7 @@ __global__ void __launch_bounds__(kCvWaves * kWave)
   // (Half a line per row per instruction, the operand layout, streams the
   // state about a fifth slower in the round.  Verify only reads the state,
   // and there the change of layout cost more than it saved.)
-  constexpr bool kCoal = sizeof(TS) == 4 && NG % 2 == 0 && !OPT && !VO;
+  constexpr bool kCoal = sizeof(TS) == 4 && NG % 2 == 0 && !VO;
   const int lr = lane >> 3, lc = lane & 7;  // row within eight, chunk of the 128-byte line
   const TS* sinw = reinterpret_cast<const TS*>(a.state_in) + (unit * DI + c0 + wave * 16) * (int64_t)N;
   if constexpr (kCoal) {
