@@ -7,7 +7,7 @@ status arrays) must equal the allocating entry point's bit for bit, on calls
 in a row that reuse the array (the second smaller than the first, with the
 array still holding the first call's rows), with and without the options;
 a call that needs more than the array holds is refused before anything is
-enqueued.  Both entry points are called through the C ABI (the binding's
+enqueued; and a round captured in a HIP graph replays to the eager results.  Both entry points are called through the C ABI (the binding's
 ctypes functions).
 """
 import os
@@ -125,3 +125,44 @@ def test_noalloc_refuses_a_call_beyond_its_scratch():
     assert e.value.code == m.E_SCRATCH
     torch.cuda.synchronize()
     assert bool((state == 3.0).all()) and bool((y == 5.0).all())  # nothing ran
+
+
+def test_noalloc_graph_replay_with_options():
+    """The allocation-free round with the options (its fixed array in use)
+    captured in a HIP graph and replayed three times, with unrelated eager
+    work between replays, equals three eager rounds of
+    ssm_tree_commit_verify bit for bit after every replay."""
+    cfg = C.Config(893, "noalloc-graph", 2, 3, 12, 4, 64, 128, 1, 4, True, 0.5, "forest", True, True, True, True)
+    step = Step(cfg)
+    s0, w0 = step.gp.state.clone(), step.gp.window.clone()
+    st, win = s0.clone(), w0.clone()
+    y = torch.empty((cfg.L, cfg.Bsz, cfg.T, cfg.d_in), dtype=torch.float32, device="cuda")
+    eager = []
+    for _ in range(3):
+        out = step.run(inplace=True, state=st, window=win, y=y)
+        eager.append([t.clone() for t in out])
+    st.copy_(s0)
+    win.copy_(w0)
+    y.fill_(0.0)
+    _run(step, noalloc=True)  # an eager call first: the array's address is looked up there, not under capture
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    gp, gn = step.gp, step.gn
+    cst = torch.empty((cfg.Bsz,), dtype=torch.int32, device="cuda")
+    vst = torch.empty_like(cst)
+    log("noalloc round captured in a graph: %s" % cfg.name)
+    with torch.cuda.graph(graph, stream=side):
+        m.commit_verify(step.dims, step.prm, gp.parent, gp.path, gp.path_len, gp.x, gp.B, gp.dt_raw, win, st, win,
+                        st, gn.parent, gn.x, gn.B, gn.C, gn.dt_raw, y, cst, vst, C_prev=gp.C, z=gn.z, noalloc=True)
+    torch.cuda.synchronize()
+    assert torch.equal(st, s0), "capture must not execute the round"
+    for r in range(3):
+        graph.replay()
+        torch.cuda.synchronize()
+        for got, ref in zip((st, win, y, cst, vst), eager[r]):
+            assert torch.equal(got.view(torch.int32) if got.dtype == torch.float32 else got,
+                               ref.view(torch.int32) if ref.dtype == torch.float32 else ref), ("replay", r)
+        junk = torch.randn(1 << 20, device="cuda")  # unrelated eager work between replays
+        assert torch.isfinite(junk.sum())
+        torch.cuda.synchronize()
