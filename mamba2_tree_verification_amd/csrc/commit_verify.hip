@@ -145,7 +145,7 @@ struct CvLds {
     Bp = o; o += vo ? 0 : kCvT * row;         // previous tree B rows of the path nodes (raw, padded)
     xt = o; o += 4 * kCvRows * kCvT;          // next tree conv outputs, MFMA B-operand layout
     z = Bpt = 0;
-    if (gate) { z = o; o += kCvT * kCvRows * E; }          // gate input rows (raw)
+    if (gate && !xbc) { z = o; o += kCvT * kCvRows * E; }  // gate input rows (raw)
     if (xbc) {
       // The raw B and C rows of both trees are not read (the next tree's
       // convolved rows go from the workspace to the registers of the lanes
@@ -154,6 +154,9 @@ struct CvLds {
       // and Bp rows, which always have room for them.
       dtx = C;
       Bpt = C + 4 * kCvT * kCvRows;
+      // the gate rows arrive after the commit, over the same space (dead by
+      // then; it is never smaller than 4 KiB)
+      if (gate) z = C;
     }
     total = o;
   }
@@ -301,7 +304,7 @@ __global__ void __launch_bounds__(kCvWaves * kWave)
   // the options: gate rows
   RawQ rz{};
   if constexpr (OPT) {
-    if (gate && xv < T)
+    if (gate && !xbc && xv < T)
       rz = *reinterpret_cast<const RawQ*>(reinterpret_cast<const TIn*>(a.z) + (unit * T + xv) * DI + c0 + xq);
   }
 
@@ -386,7 +389,7 @@ __global__ void __launch_bounds__(kCvWaves * kWave)
     s_cb[lane] = r_cb;
   }
   if constexpr (OPT) {
-    if (gate && xv < T) *reinterpret_cast<RawQ*>(s_z + xv * kCvRows + xq) = rz;
+    if (gate && !xbc && xv < T) *reinterpret_cast<RawQ*>(s_z + xv * kCvRows + xq) = rz;
   }
   __syncthreads();
 
@@ -746,6 +749,15 @@ __global__ void __launch_bounds__(kCvWaves * kWave)
       }
     }
 
+    // with the xBC conv the gate rows are loaded now, under the products,
+    // and staged after the commit's arrays are done with (thread (v, q) as
+    // in trip 1)
+    const int zv = tid >> 4, zq = (tid & 15) * 4;  // (= xv, xq)
+    RawQ rzl{};
+    if constexpr (OPT) {
+      if (xbc && gate && zv < T)
+        rzl = *reinterpret_cast<const RawQ*>(reinterpret_cast<const TIn*>(a.z) + (unit * T + zv) * DI + c0 + zq);
+    }
     // C . h on the matrix cores: lane (c + 16 q) ends with (C_{4q+r} . h_c)
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
     const bool live = j < T;
@@ -835,6 +847,13 @@ __global__ void __launch_bounds__(kCvWaves * kWave)
     }
     const bool tree_ok = s_misc[2] != 0;
     if constexpr (kCoal) __syncthreads();  // every wave is done with its layout buffer
+    if constexpr (OPT) {
+      if (xbc && gate) {
+        if constexpr (!kCoal) __syncthreads();  // every wave is done with dt * x~ and the path rows
+        if (zv < T) *reinterpret_cast<RawQ*>(s_z + zv * kCvRows + zq) = rzl;
+        __syncthreads();
+      }
+    }
     // lane (c + 16 k) holds nodes 4 k + r of channel row
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
