@@ -271,3 +271,48 @@ def test_unsupported_option_combinations_refused():
         step.run(inplace=True, state=s_in, window=step.gp.window.clone())
     assert e.value.code == m.E_DIMS
     assert torch.equal(s_in, step.gp.state)
+
+
+# ----------------------------------------------------------------------------
+# the xBC conv on seeded random shapes of 1-16 nodes (the fused round and
+# verify, whose convolved B/C rows and C . B table come from the workspace)
+# ----------------------------------------------------------------------------
+
+def _random_xbc_shapes(n, seed):
+    """(T, H, P, N, G, W, bf16, silu, conv_b, gate): headdims that are
+    multiples of 16, H*P/G a multiple of 64 (every other draw with the most
+    groups the heads allow), every d_state, conv widths 1-4, both input
+    types and every option combination."""
+    rng = np.random.default_rng(seed)
+    hp = [(4, 16), (2, 32), (4, 48), (1, 64), (2, 64), (1, 128), (8, 16), (6, 32), (4, 32)]
+    hp_groups = [(8, 16), (6, 32), (4, 32), (2, 64), (4, 64)]  # head shapes that allow G > 1
+    out = []
+    while len(out) < n:
+        pick = hp_groups if len(out) % 2 else hp
+        H, P = pick[int(rng.integers(len(pick)))]
+        gs = [g for g in (1, 2, 3, 4, 6, 8) if H % g == 0 and (H * P // g) % 64 == 0]
+        G = int(gs[-1]) if len(out) % 2 else int(rng.choice(gs))  # every other draw: the most groups
+        N = int(rng.choice([16, 32, 64, 128, 256]))
+        T = int(rng.integers(1, 17))
+        W = int(rng.integers(1, 5))
+        bf16, silu, cb, gate = (bool(rng.integers(2)) for _ in range(4))
+        out.append((T, H, P, N, G, W, bf16, silu, cb, gate))
+    return out
+
+
+RANDOM_XBC = _random_xbc_shapes(12, 2026)
+
+
+@pytest.mark.parametrize("k", range(len(RANDOM_XBC)), ids=lambda k: "T%dH%dP%dN%dG%dW%d" % RANDOM_XBC[k][:6])
+def test_xbc_random_shapes(k):
+    """The round and verify alone with the xBC conv against the oracle on
+    every (layer, sequence) unit."""
+    T, H, P, N, G, W, bf16, silu, cb, gate = RANDOM_XBC[k]
+    cfg = C.Config(950 + k, "xbc-random", 2, 3, T, H, P, N, G, W, bf16, 0.5, "forest", silu, cb, True, gate)
+    log("random xBC shape %d: %s" % (k, RANDOM_XBC[k]))
+    units = [(l, b) for l in range(cfg.L) for b in range(cfg.Bsz)]
+    step = Step(cfg)
+    check(step, step.run(), units)
+    case = GpuCase(cfg)
+    y, st = case.verify()
+    check_verify(case, y, st, units)
