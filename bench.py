@@ -893,7 +893,9 @@ def main(argv=None):
     vcompute = {"engine": engine, "flops": xflops, "achieved": round(vach, 2),
                 "peak": vpeak, "unit": "TFLOP/s", "frac": round(vach / vpeak, 4)}
 
-    kern = {"commit_verify": dict(ms=round(avg(cv_ms), 4), ms_min=round(min(cv_ms), 4), bytes=cvb,
+    kern = {"commit_verify": dict(ms=round(avg(cv_ms), 4), ms_min=round(min(cv_ms), 4),
+                                  ms_median=round(sorted(cv_ms)[len(cv_ms) // 2], 4),
+                                  ms_max=round(max(cv_ms), 4), bytes=cvb,
                                   node_layers_per_s=round(node_layers / (avg(cv_ms) * 1e-3), 1),
                                   roofline=roof("commit_verify", cvb, avg(cv_ms))),
             "verify": dict(ms=round(avg(ver_ms), 4), ms_min=round(min(ver_ms), 4), bytes=ab["verify"],
