@@ -69,6 +69,8 @@ CASES = [
     ((9, 2, 64, 64, 2, 3, True, False, False, True, False), 2, 3),  # then a smaller one
     ((12, 4, 32, 32, 1, 4, False, True, True, True, True), 2, 2),   # fp32 inputs
     ((16, 4, 64, 128, 1, 4, True, True, False, False, False), 2, 4),  # no options: no scratch used
+    ((20, 4, 64, 128, 1, 4, True, True, False, True, True), 2, 3),  # options past 16 nodes: the two calls
+    ((40, 8, 64, 128, 1, 4, True, True, False, False, False), 2, 2),  # the one-launch 17-64-node round
 ]
 
 
