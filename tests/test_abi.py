@@ -267,3 +267,15 @@ def test_state_bf16_host_checks():
     assert call_commit(sb(), p, state_out=fake(7, 393200)) == m.E_ALIAS
     assert call_commit_verify(sb(), p, state_out=fake(7, 393200)) == m.E_ALIAS
     assert call_commit(good_dims(), p, state_out=fake(7, 600000)) == m.E_ALIAS
+
+
+def test_noalloc_refuses_a_call_beyond_its_scratch_before_any_hip_call():
+    """ssm_tree_commit_verify_noalloc: 32 x 32 sequences of 16-node trees at
+    d_state 256 with the xBC conv need 51.4 MB of convolved rows, more than
+    its 32 MiB array; the call is refused after the argument checks and
+    before any HIP call (so it runs here without a GPU)."""
+    d = good_dims(L=32, Bsz=32, T=16, H=1, P=64, N=256)
+    d.flags |= m.SSM_TREE_CONV_XBC
+    assert call_commit_verify(d, good_params(), noalloc=True) == m.E_SCRATCH
+    # the argument checks still come first
+    assert call_commit_verify(d, good_params(), noalloc=True, y=None) == m.E_NULL
